@@ -1,0 +1,161 @@
+"""fp64 CPU oracle for the selective scan and its decode step.
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, by ``__graft_entry__.smoke()``
+and by the CPU-baseline leg of ``bench.py``.  The HIP library never imports,
+links or calls it, and it shares no code with the HIP path.
+
+Every function follows the definitions in "Mamba and selective state spaces"
+(zerotofrontier.app/ssm/mamba): the S6 definition box in "The selective
+state-space model", the two rules of "The discretization the code actually
+uses", the SiLU gate of "The Mamba block" and the step of "Decoding with a
+constant-size cache".  The C source states each formula beside its code.
+
+Inputs are converted to float64 here (bf16 and fp32 values convert exactly);
+outputs stay float64.
+
+Parity status: every function below is pinned by ``tests/test_oracle_pins.py``
+against the pages' worked numbers, closed forms (LTI convolution, first-order
+IIR filter), a brute-force mixing-matrix evaluation and invariants.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+ZOH = 0
+EULER = 1
+_MODES = {"zoh": ZOH, "euler": EULER, ZOH: ZOH, EULER: EULER}
+
+_lib = None
+_dp = ctypes.POINTER(ctypes.c_double)
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = os.environ.get("SSM_ORACLE_LIB")  # a planted-mistake copy, in the mutation tests
+    if path is None:
+        path = _build.LIB
+        if not os.path.exists(path):
+            _build.build()
+    lib = ctypes.CDLL(path)
+    lib.oracle_softplus.restype = ctypes.c_double
+    lib.oracle_softplus.argtypes = [ctypes.c_double]
+    lib.oracle_sigmoid.restype = ctypes.c_double
+    lib.oracle_sigmoid.argtypes = [ctypes.c_double]
+    lib.oracle_discretize.restype = None
+    lib.oracle_discretize.argtypes = [ctypes.c_double, ctypes.c_double, ctypes.c_double,
+                                      ctypes.c_int, _dp, _dp]
+    lib.oracle_combine.restype = None
+    lib.oracle_combine.argtypes = [ctypes.c_double] * 4 + [_dp, _dp]
+    lib.oracle_scan_fwd.restype = None
+    lib.oracle_scan_fwd.argtypes = [ctypes.c_void_p] * 9 + [ctypes.c_int, ctypes.c_int,
+                                                            ctypes.c_void_p, ctypes.c_void_p] + \
+        [ctypes.c_int64] * 4 + [ctypes.c_int]
+    lib.oracle_step.restype = None
+    lib.oracle_step.argtypes = [ctypes.c_void_p] * 9 + [ctypes.c_int, ctypes.c_int,
+                                                        ctypes.c_void_p] + [ctypes.c_int64] * 3
+    _lib = lib
+    return lib
+
+
+def _f64(a):
+    if a is None:
+        return None
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def softplus(v: float) -> float:
+    """log(1 + e^v), overflow-safe."""
+    return _load().oracle_softplus(float(v))
+
+
+def sigmoid(v: float) -> float:
+    return _load().oracle_sigmoid(float(v))
+
+
+def discretize(delta: float, a: float, b: float, dt_mode="zoh"):
+    """(abar, bbar) for one (channel, state) pair under ZOH or exponential-Euler."""
+    ab = ctypes.c_double()
+    bb = ctypes.c_double()
+    _load().oracle_discretize(float(delta), float(a), float(b), _MODES[dt_mode],
+                              ctypes.byref(ab), ctypes.byref(bb))
+    return ab.value, bb.value
+
+
+def combine(first, then):
+    """Apply the affine step `first` = (a1, b1) and then `then` = (a2, b2)."""
+    a = ctypes.c_double()
+    b = ctypes.c_double()
+    _load().oracle_combine(float(first[0]), float(first[1]), float(then[0]), float(then[1]),
+                           ctypes.byref(a), ctypes.byref(b))
+    return a.value, b.value
+
+
+def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True,
+             dt_mode="zoh", h0=None, nthreads=None):
+    """Sequential fp64 selective scan.
+
+    u, delta, z: (batch, L, dim); B, C: (batch, L, N); A: (dim, N); D, delta_bias: (dim,);
+    h0: optional (batch, dim, N) initial state (zero when omitted).
+    Returns (y (batch, L, dim), last_state (batch, dim, N)), both float64.
+    """
+    u = _f64(u)
+    delta = _f64(delta)
+    A = _f64(A)
+    B = _f64(B)
+    C = _f64(C)
+    D = _f64(D)
+    z = _f64(z)
+    delta_bias = _f64(delta_bias)
+    h0 = _f64(h0)
+    batch, L, dim = u.shape
+    N = A.shape[1]
+    assert delta.shape == u.shape and A.shape == (dim, N)
+    assert B.shape == (batch, L, N) and C.shape == (batch, L, N)
+    assert D is None or D.shape == (dim,)
+    assert z is None or z.shape == u.shape
+    assert delta_bias is None or delta_bias.shape == (dim,)
+    assert h0 is None or h0.shape == (batch, dim, N)
+    y = np.empty((batch, L, dim), dtype=np.float64)
+    last = np.empty((batch, dim, N), dtype=np.float64)
+    if nthreads is None:
+        nthreads = os.cpu_count() or 1
+    _load().oracle_scan_fwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                            _ptr(delta_bias), _ptr(h0), int(bool(softplus)), _MODES[dt_mode],
+                            _ptr(y), _ptr(last), batch, L, dim, N, int(nthreads))
+    return y, last
+
+
+def step(state, u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True,
+         dt_mode="zoh"):
+    """One fp64 decode step.
+
+    state: (batch, dim, N) -- not modified; the updated state is returned.
+    u, delta, z: (batch, dim); B, C: (batch, N).
+    Returns (y (batch, dim), new_state (batch, dim, N)).
+    """
+    st = np.array(state, dtype=np.float64, copy=True, order="C")
+    u = _f64(u)
+    delta = _f64(delta)
+    A = _f64(A)
+    B = _f64(B)
+    C = _f64(C)
+    D = _f64(D)
+    z = _f64(z)
+    delta_bias = _f64(delta_bias)
+    batch, dim = u.shape
+    N = A.shape[1]
+    assert st.shape == (batch, dim, N) and B.shape == (batch, N) and C.shape == (batch, N)
+    y = np.empty((batch, dim), dtype=np.float64)
+    _load().oracle_step(_ptr(st), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                        _ptr(z), _ptr(delta_bias), int(bool(softplus)), _MODES[dt_mode],
+                        _ptr(y), batch, dim, N)
+    return y, st

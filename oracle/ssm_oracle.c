@@ -1,0 +1,200 @@
+/*
+ * ssm_oracle.c -- fp64 CPU oracle for the selective scan and its decode step.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may include, link or
+ * call this file; only the test-suite, the smoke check and the CPU-baseline leg
+ * of the benchmark use it.  It shares no source with the HIP library.
+ *
+ * It is the plain definition, run sequentially in double precision:
+ *
+ *   "Mamba and selective state spaces" (zerotofrontier.app/ssm/mamba),
+ *   section "The selective state-space model", the S6 definition box:
+ *     Delta_t = softplus(raw_t + b_Delta), H_0 = 0,
+ *     h_{t,cn} = abar_{t,cn} h_{t-1,cn} + bbar_{t,cn} x_t^(c),
+ *     y_t^(c) = sum_n C_{t,n} h_{t,cn} + D_c x_t^(c).
+ *   Same page, "The discretization the code actually uses":
+ *     abar = exp(Delta*lambda) for both rules;
+ *     zero-order hold:    bbar = (exp(Delta*lambda) - 1)/lambda * B
+ *     exponential-Euler:  bbar = Delta * B
+ *   "Mamba, annotated" (that-mathevs.github.io), "Discretization (equation 4)":
+ *     the scalar ZOH form (e^{Delta A} - 1)/A * B.
+ *   "The Mamba block" section of the first page: the output is gated by SiLU(z),
+ *     SiLU(v) = v * sigma(v), applied to the S6 output (which includes D x).
+ *   "Decoding with a constant-size cache": one step updates the state entrywise,
+ *     reads it and gates it.
+ *
+ * Readings where the pages leave a step open (each is listed in the design doc):
+ *   - the bias is added once, inside the softplus; softplus may be switched off,
+ *     in which case Delta = raw + bias as given;
+ *   - A = 0 under ZOH takes the limit bbar = Delta * B;
+ *   - the gate multiplies (C.h + D x);
+ *   - the state is read after it is written for the same token.
+ *
+ * Layouts (row-major, dense):
+ *   u, delta, z, y : (batch, L, dim)      B, C : (batch, L, N)
+ *   A : (dim, N)     D, delta_bias : (dim)
+ *   state / h0 / last_state : (batch, dim, N)
+ * Optional pointers (D, z, delta_bias, h0, last_state) may be NULL.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+#define ORACLE_DT_ZOH 0
+#define ORACLE_DT_EULER 1
+
+/* softplus(v) = log(1 + e^v), written so that neither branch overflows
+ * (finite for v = +-1000, as the warm-up exercise on the first page asks). */
+double oracle_softplus(double v) {
+  if (v > 0.0) return v + log1p(exp(-v));
+  return log1p(exp(v));
+}
+
+/* logistic sigmoid, stable for both signs */
+double oracle_sigmoid(double v) {
+  if (v >= 0.0) return 1.0 / (1.0 + exp(-v));
+  double e = exp(v);
+  return e / (1.0 + e);
+}
+
+/* The step size from the raw projection: bias inside, softplus once. */
+static double step_size(double raw, double bias, int softplus) {
+  double v = raw + bias;
+  return softplus ? oracle_softplus(v) : v;
+}
+
+/* Discretize one (channel, state) pair: abar = exp(delta*a).
+ * ZOH:   bbar = (exp(delta*a) - 1) / a * b   (expm1 keeps small delta*a exact;
+ *        a = 0 takes the limit delta*b).
+ * EULER: bbar = delta * b. */
+void oracle_discretize(double delta, double a, double b, int dt_mode,
+                       double* abar, double* bbar) {
+  double kappa = delta * a;
+  *abar = exp(kappa);
+  if (dt_mode == ORACLE_DT_ZOH) {
+    *bbar = (a != 0.0) ? expm1(kappa) / a * b : delta * b;
+  } else {
+    *bbar = delta * b;
+  }
+}
+
+/* The associative combine of two affine steps h -> a h + b, applying `first`
+ * and then `then`: (a1, b1) . (a2, b2) = (a1 a2, a2 b1 + b2).
+ * ("Selection breaks the convolution" on the first page; "The scan, in one
+ * equation" on the second.)  The sequential scan below does not need it; it
+ * is here so that the tests can check it and use it to compose segments. */
+void oracle_combine(double a1, double b1, double a2, double b2,
+                    double* a_out, double* b_out) {
+  *a_out = a1 * a2;
+  *b_out = a2 * b1 + b2;
+}
+
+typedef struct {
+  const double *u, *delta, *A, *B, *C, *D, *z, *bias, *h0;
+  double *y, *last_state;
+  int64_t batch, L, dim, N;
+  int softplus, dt_mode;
+  int64_t row_begin, row_end; /* rows are (b, c) pairs, b-major */
+} scan_job;
+
+/* One (batch, channel) row of the scan, over all t. */
+static void scan_row(const scan_job* j, int64_t b, int64_t c) {
+  const int64_t L = j->L, dim = j->dim, N = j->N;
+  double h[64];
+  double* hp = h;
+  double* heap = NULL;
+  if (N > 64) {
+    heap = (double*)malloc(sizeof(double) * (size_t)N);
+    hp = heap;
+  }
+  for (int64_t n = 0; n < N; ++n)
+    hp[n] = j->h0 ? j->h0[(b * dim + c) * N + n] : 0.0;
+  const double bias = j->bias ? j->bias[c] : 0.0;
+  const double dskip = j->D ? j->D[c] : 0.0;
+  for (int64_t t = 0; t < L; ++t) {
+    const int64_t xi = (b * L + t) * dim + c;
+    const double x = j->u[xi];
+    const double dt = step_size(j->delta[xi], bias, j->softplus);
+    const double* Bt = j->B + (b * L + t) * N;
+    const double* Ct = j->C + (b * L + t) * N;
+    double acc = 0.0;
+    for (int64_t n = 0; n < N; ++n) {
+      double abar, bbar;
+      oracle_discretize(dt, j->A[c * N + n], Bt[n], j->dt_mode, &abar, &bbar);
+      hp[n] = abar * hp[n] + bbar * x; /* write the token first ... */
+      acc += Ct[n] * hp[n];            /* ... then read the state */
+    }
+    double out = acc + dskip * x;
+    if (j->z) {
+      const double zz = j->z[xi];
+      out *= zz * oracle_sigmoid(zz);
+    }
+    j->y[xi] = out;
+  }
+  if (j->last_state)
+    for (int64_t n = 0; n < N; ++n) j->last_state[(b * dim + c) * N + n] = hp[n];
+  free(heap);
+}
+
+static void* scan_worker(void* arg) {
+  const scan_job* j = (const scan_job*)arg;
+  for (int64_t r = j->row_begin; r < j->row_end; ++r) scan_row(j, r / j->dim, r % j->dim);
+  return NULL;
+}
+
+/* The full scan.  Rows (b, c) are independent and are split over `nthreads`
+ * host threads; each row is computed exactly as written above. */
+void oracle_scan_fwd(const double* u, const double* delta, const double* A,
+                     const double* B, const double* C, const double* D,
+                     const double* z, const double* delta_bias, const double* h0,
+                     int softplus, int dt_mode, double* y, double* last_state,
+                     int64_t batch, int64_t L, int64_t dim, int64_t N, int nthreads) {
+  const int64_t rows = batch * dim;
+  if (rows <= 0) return;
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > rows) nthreads = (int)rows;
+  scan_job* jobs = (scan_job*)calloc((size_t)nthreads, sizeof(scan_job));
+  pthread_t* tids = (pthread_t*)calloc((size_t)nthreads, sizeof(pthread_t));
+  for (int i = 0; i < nthreads; ++i) {
+    scan_job* j = &jobs[i];
+    j->u = u; j->delta = delta; j->A = A; j->B = B; j->C = C; j->D = D; j->z = z;
+    j->bias = delta_bias; j->h0 = h0; j->y = y; j->last_state = last_state;
+    j->batch = batch; j->L = L; j->dim = dim; j->N = N;
+    j->softplus = softplus; j->dt_mode = dt_mode;
+    j->row_begin = rows * i / nthreads;
+    j->row_end = rows * (i + 1) / nthreads;
+  }
+  for (int i = 1; i < nthreads; ++i) pthread_create(&tids[i], NULL, scan_worker, &jobs[i]);
+  scan_worker(&jobs[0]);
+  for (int i = 1; i < nthreads; ++i) pthread_join(tids[i], NULL);
+  free(jobs);
+  free(tids);
+}
+
+/* One decode step: the same body as the scan for a single token, with the
+ * state read from and written back to `state` (batch, dim, N).
+ * u, delta, z, y : (batch, dim); B, C : (batch, N). */
+void oracle_step(double* state, const double* u, const double* delta, const double* A,
+                 const double* B, const double* C, const double* D, const double* z,
+                 const double* delta_bias, int softplus, int dt_mode, double* y,
+                 int64_t batch, int64_t dim, int64_t N) {
+  for (int64_t b = 0; b < batch; ++b) {
+    for (int64_t c = 0; c < dim; ++c) {
+      const int64_t xi = b * dim + c;
+      const double x = u[xi];
+      const double dt = step_size(delta[xi], delta_bias ? delta_bias[c] : 0.0, softplus);
+      double* h = state + xi * N;
+      double acc = 0.0;
+      for (int64_t n = 0; n < N; ++n) {
+        double abar, bbar;
+        oracle_discretize(dt, A[c * N + n], B[b * N + n], dt_mode, &abar, &bbar);
+        h[n] = abar * h[n] + bbar * x;
+        acc += C[b * N + n] * h[n];
+      }
+      double out = acc + (D ? D[c] : 0.0) * x;
+      if (z) out *= z[xi] * oracle_sigmoid(z[xi]);
+      y[xi] = out;
+    }
+  }
+}

@@ -1,0 +1,53 @@
+"""The pins must fail when a plausible mistake is planted in the oracle.
+
+Each case copies the oracle's C source to a temporary directory, applies one
+textual mutation, compiles it with gcc and runs the pin suite against that
+library in a child process.  Nothing here touches a GPU.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "ssm_oracle.c")
+
+MUTATIONS = {
+    "read_before_write": (
+        "      hp[n] = abar * hp[n] + bbar * x; /* write the token first ... */\n"
+        "      acc += Ct[n] * hp[n];            /* ... then read the state */",
+        "      acc += Ct[n] * hp[n];\n      hp[n] = abar * hp[n] + bbar * x;"),
+    "dropped_skip": ("double out = acc + dskip * x;", "double out = acc;"),
+    "bias_twice": ("double v = raw + bias;", "double v = raw + 2.0 * bias;"),
+    "softplus_twice": ("return softplus ? oracle_softplus(v) : v;",
+                       "return softplus ? oracle_softplus(oracle_softplus(v)) : v;"),
+    "zoh_as_euler": ("*bbar = (a != 0.0) ? expm1(kappa) / a * b : delta * b;", "*bbar = delta * b;"),
+    "euler_as_zoh": ("    *bbar = delta * b;\n  }", "    *bbar = expm1(kappa) / a * b;\n  }"),
+    "combine_transposed": ("*b_out = a2 * b1 + b2;", "*b_out = a1 * b2 + b1;"),
+    "A_transposed": ("j->A[c * N + n]", "j->A[(n * dim + c) % (dim * N)]"),
+    "B_C_swapped": ("acc += Ct[n] * hp[n];", "acc += Bt[n] * hp[n];"),
+    "gate_before_skip": ("    double out = acc + dskip * x;\n    if (j->z) {\n      const double zz = j->z[xi];\n      out *= zz * oracle_sigmoid(zz);\n    }",
+                         "    double out = acc;\n    if (j->z) {\n      const double zz = j->z[xi];\n      out *= zz * oracle_sigmoid(zz);\n    }\n    out += dskip * x;"),
+    "decay_sign": ("  *abar = exp(kappa);", "  *abar = exp(-kappa);"),
+    "sigmoid_sign": ("if (v >= 0.0) return 1.0 / (1.0 + exp(-v));", "if (v >= 0.0) return 1.0 / (1.0 + exp(v));"),
+    "step_drops_state": ("        h[n] = abar * h[n] + bbar * x;", "        h[n] = bbar * x;"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(name, tmp_path):
+    old, new = MUTATIONS[name]
+    src = open(SRC).read()
+    assert src.count(old) >= 1, f"mutation anchor for {name} not found"
+    mutated = src.replace(old, new)
+    csrc = tmp_path / "mut.c"
+    lib = tmp_path / "libmut.so"
+    csrc.write_text(mutated)
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-o", str(lib), str(csrc),
+                    "-lm", "-pthread"], check=True)
+    env = dict(os.environ, SSM_ORACLE_LIB=str(lib))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0, f"mutation {name} survived the pins:\n{r.stdout[-2000:]}"
