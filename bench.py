@@ -1,0 +1,271 @@
+#!/usr/bin/env python3
+"""Benchmark of the MI355X selective scan: one JSON line on stdout.
+
+A step is one fused selective-scan forward (ssm_scan_fwd) over the
+Mamba-130M-shaped layer: batch 8, L 2048, D 1536 (d_model 768 x expand 2),
+N 16, bf16 inputs and output, fp32 state, SiLU(z) gate, D skip, dt bias with
+softplus, zero-order-hold discretization.  Inputs are resident in HBM before
+the timed region; three independent input sets (203 MB each) rotate from step
+to step so that the 256 MB Infinity Cache cannot serve a step from the previous
+one.  `value` is algorithmic bytes per step / measured step time.
+
+Also reported, outside `value`: the same scan under the exponential-Euler rule,
+the decode step (ssm_step) on its workload (batch 256, D 5120, N 16,
+1000 consecutive tokens), the kernel roofline for the dominant kernel, and the
+fp64 CPU oracle timed on the host.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+METRIC = "selective-scan fwd achieved HBM GB/s (% of peak) and B·L·D elems/s; decode tok/s"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def scan_bytes(b, L, D, N, io_bytes, gate):
+    """Algorithmic bytes of one scan: every input read once, y and the final
+    state written once (u, raw delta, [z], y: b L D; B, C: b L N; A: D N fp32;
+    D, bias: D fp32 each; last_state: b D N fp32)."""
+    streamed = 3 if gate else 2
+    return (streamed + 1) * b * L * D * io_bytes + 2 * b * L * N * io_bytes + 4 * D * N + 8 * D \
+        + 4 * b * D * N
+
+
+def step_bytes(b, D, N, io_bytes, gate):
+    """Algorithmic bytes of one decode step: state read + written (fp32), u, raw
+    delta, [z] read and y written (b D), B, C (b N), A (D N), D and bias (D)."""
+    streamed = 3 if gate else 2
+    return 8 * b * D * N + (streamed + 1) * b * D * io_bytes + 2 * b * N * io_bytes + 4 * D * N + 8 * D
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "selective_state_space_66_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel_key):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = data.get(kernel_key)
+    if not ent or ent.get("source_hash") != kernel_source_hash():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def to_dev(x, io, dev):
+    import torch
+    if x is None:
+        return None
+    if io == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(dev)
+
+
+def upload_scan(inp, dev):
+    io = inp["io"]
+    return dict(u=to_dev(inp["u"], io, dev), delta=to_dev(inp["delta"], io, dev),
+                A=to_dev(inp["A"], "f32", dev), B=to_dev(inp["B"], io, dev),
+                C=to_dev(inp["C"], io, dev), D=to_dev(inp["D"], "f32", dev),
+                z=to_dev(inp["z"], io, dev), delta_bias=to_dev(inp["delta_bias"], "f32", dev))
+
+
+def time_scan(sets, steps, warmup, dt_mode):
+    """Run warmup + timed steps rotating over the input sets.  Returns
+    (wall ms per step, mean per-launch kernel ms from HIP events)."""
+    import torch
+    import selective_state_space_66_amd as ssm
+    outs = [(torch.empty_like(s["u"]), torch.empty(s["u"].shape[0], s["u"].shape[2], s["A"].shape[1],
+                                                    dtype=torch.float32, device=s["u"].device))
+            for s in sets]
+
+    def launch(i):
+        s = sets[i % len(sets)]
+        y, last = outs[i % len(sets)]
+        ssm.scan_fwd(s["u"], s["delta"], s["A"], s["B"], s["C"], D=s["D"], z=s["z"],
+                     delta_bias=s["delta_bias"], softplus=True, dt_mode=dt_mode, y=y,
+                     last_state=last)
+
+    for i in range(warmup):
+        launch(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record()
+        launch(warmup + i)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    kern = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    return wall, kern
+
+
+def time_decode(cfg, nsteps, dev, npool=8):
+    """ssm_step over nsteps consecutive tokens on the full state; the token inputs
+    cycle through `npool` distinct seeded token batches resident in HBM."""
+    import torch
+    import selective_state_space_66_amd as ssm
+    import workloads as W
+    A, D, bias = W.channel_params(cfg.seed, cfg.dim, cfg.N)
+    Ad, Dd, bd = to_dev(A, "f32", dev), to_dev(D, "f32", dev), to_dev(bias, "f32", dev)
+    state = to_dev(W.step_state0(cfg), "f32", dev)
+    pool = []
+    for s in range(npool):
+        inp = W.step_inputs(cfg, s)
+        pool.append({k: to_dev(inp[k], cfg.io, dev) for k in ("u", "delta", "B", "C", "z")})
+    ys = [torch.empty_like(p["u"]) for p in pool]
+
+    def one(i):
+        p = pool[i % npool]
+        ssm.step(state, p["u"], p["delta"], Ad, p["B"], p["C"], D=Dd, z=p["z"], delta_bias=bd,
+                 y=ys[i % npool])
+
+    for i in range(20):
+        one(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for i in range(nsteps):
+        one(i)
+    e1.record()
+    torch.cuda.synchronize()
+    wall_s = time.perf_counter() - t0
+    return wall_s, e0.elapsed_time(e1) / nsteps
+
+
+def cpu_baseline(cfg, inp, threads):
+    """The fp64 oracle, as it stands, on the same workload on the host cores."""
+    import oracle
+    import workloads as W
+    f = lambda k: W.as_f64(inp[k], cfg.io)
+    args = [f("u"), f("delta"), inp["A"], f("B"), f("C")]
+    t0 = time.perf_counter()
+    oracle.scan_fwd(*args, D=inp["D"], z=f("z"), delta_bias=inp["delta_bias"], softplus=True,
+                    dt_mode="zoh", nthreads=threads)
+    return time.perf_counter() - t0
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--decode-steps", type=int, default=1000)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the scan shards by batch or channel with no communication; see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import selective_state_space_66_amd as ssm
+    import workloads as W
+    ssm.load_library()  # fail loudly if the HIP library is missing
+    dev = torch.device("cuda:0")
+
+    cfg = W.SCAN_CONFIGS["mamba130m"]
+    log(f"[bench] generating inputs for {cfg}")
+    inp0 = W.scan_inputs(cfg)
+    sets = [upload_scan(inp0, dev)]
+    for k in (1, 2):  # two more independent sets (other seeds) for cache rotation
+        other = W.ScanConfig(cfg.name, cfg.batch, cfg.L, cfg.dim, cfg.N, cfg.io, cfg.gate,
+                             cfg.seed + 100 * k)
+        sets.append(upload_scan(W.scan_inputs(other), dev))
+    nbytes = scan_bytes(cfg.batch, cfg.L, cfg.dim, cfg.N, 2, cfg.gate)
+    elems = cfg.batch * cfg.L * cfg.dim
+
+    log("[bench] timing ZOH scan")
+    wall_ms, kern_ms = time_scan(sets, args.steps, args.warmup, "zoh")
+    log(f"[bench] zoh: wall {wall_ms:.4f} ms/step, kernel {kern_ms:.4f} ms")
+    log("[bench] timing exponential-Euler scan")
+    e_wall, e_kern = time_scan(sets, args.steps, args.warmup, "euler")
+    log(f"[bench] euler: wall {e_wall:.4f} ms/step, kernel {e_kern:.4f} ms")
+
+    dcfg = W.STEP_CONFIGS["decode"]
+    log("[bench] timing decode steps")
+    d_wall_s, d_kern_ms = time_decode(dcfg, args.decode_steps, dev)
+    d_bytes = step_bytes(dcfg.batch, dcfg.dim, dcfg.N, 2, dcfg.gate)
+    del sets
+    torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu:
+        threads = min(16, os.cpu_count() or 1)
+        log(f"[bench] timing the fp64 oracle on {threads} host threads (whole workload)")
+        cpu_s = cpu_baseline(cfg, inp0, threads)
+        cpu = {"value": round(nbytes / cpu_s / 1e9, 4), "unit": "GB/s", "cores": threads,
+               "kind": "oracle",
+               "sample": f"the whole workload ({cfg.batch}x{cfg.L}x{cfg.dim}, N {cfg.N}, ZOH, "
+                         f"gate): {cpu_s:.2f} s wall, {elems / cpu_s:.4g} elems/s"}
+        log(f"[bench] oracle: {cpu_s:.2f} s")
+
+    gbs = nbytes / (wall_ms * 1e-3) / 1e9
+    achieved = nbytes / (kern_ms * 1e-3) / 1e9
+    traffic = measured_traffic("scan_fwd_mamba130m_zoh")
+    out = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "mamba130m-layer selective scan fwd: batch 8, L 2048, D 1536, N 16, "
+                               "bf16 io, fp32 state, silu(z) gate, D skip, softplus(delta+bias), ZOH",
+                   "batch": cfg.batch, "seq_len": cfg.L, "dim": cfg.dim, "d_state": cfg.N,
+                   "io_dtype": "bf16", "dt_mode": "zoh", "parallelism": "none (1 GPU)"},
+        "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+        "elems_per_s": float(f"{elems / (wall_ms * 1e-3):.4g}"),
+        "updates_per_s": float(f"{elems * cfg.N / (wall_ms * 1e-3):.4g}"),
+        "algorithmic_bytes_per_step": nbytes,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "kernel": "scan_fwd_kernel (ZOH, bf16, gate)",
+                     "kernel_ms": round(kern_ms, 5)},
+        "cpu_baseline": cpu,
+        "euler": {"ms_per_step": round(e_wall, 5), "GB/s": round(nbytes / (e_wall * 1e-3) / 1e9, 2),
+                  "kernel_ms": round(e_kern, 5)},
+        "decode": {"workload": "ssm_step: batch 256, D 5120, N 16, bf16 io, fp32 state, gate, ZOH",
+                   "steps": args.decode_steps,
+                   "tok_per_s": round(dcfg.batch * args.decode_steps / d_wall_s, 1),
+                   "us_per_step": round(d_kern_ms * 1e3, 3),
+                   "GB/s": round(d_bytes / (d_kern_ms * 1e-3) / 1e9, 2)},
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

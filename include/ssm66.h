@@ -1,0 +1,113 @@
+/*
+ * ssm66.h -- C ABI of the MI355X (gfx950) selective-scan library.
+ *
+ * Two operations, both defined on "Mamba and selective state spaces"
+ * (zerotofrontier.app/ssm/mamba):
+ *
+ *   ssm_scan_fwd : the selective state-space layer (S6) over whole sequences --
+ *                  section "The selective state-space model", the S6 definition
+ *                  box (Delta_t = softplus(raw_t + b_Delta); abar = exp(Delta A);
+ *                  h_t = abar h_{t-1} + bbar x_t; y_t = C_t . h_t + D x_t), with
+ *                  the two input-weight rules of "The discretization the code
+ *                  actually uses" (zero-order hold, and the exponential-Euler
+ *                  rule bbar = Delta B) and the SiLU(z) gate of "The Mamba
+ *                  block".  Prefill keeps only the final state ("Decoding with
+ *                  a constant-size cache"), returned in last_state.
+ *   ssm_step     : one token of that layer against a state cache, updated in
+ *                  place ("Decoding with a constant-size cache").
+ *
+ * Conventions shared by both calls
+ *   - Every pointer is caller-owned DEVICE memory (HBM).  The library keeps no
+ *     pointer after the call returns and allocates nothing.
+ *   - Tensors are dense and row-major:
+ *       u, delta, z, y    : (batch, seqlen, dim)   [ssm_step: (batch, dim)]
+ *       B, C              : (batch, seqlen, dstate) [ssm_step: (batch, dstate)]
+ *       A                 : (dim, dstate)            float32
+ *       D, delta_bias     : (dim)                    float32
+ *       last_state, state : (batch, dim, dstate)     float32
+ *     u, delta, B, C, z and y share one I/O dtype (io_dtype: SSM_F32 or
+ *     SSM_BF16); A, D, delta_bias and the states are float32 in every mode.
+ *   - D, z, delta_bias and last_state may be NULL (no skip, no gate, zero bias,
+ *     final state not returned).
+ *   - softplus != 0 applies Delta = softplus(delta + bias); softplus == 0 uses
+ *     Delta = delta + bias as given.  The bias is added exactly once.
+ *   - dt_mode selects the input weight: SSM_DT_ZOH, bbar = (exp(Delta A) - 1)/A B
+ *     (limit Delta B at A = 0), or SSM_DT_EULER, bbar = Delta B.
+ *   - The gate multiplies the whole S6 output: y = (C.h + D u) * z * sigmoid(z).
+ *   - 1 <= dstate <= 16; batch, seqlen, dim >= 0.  Zero batch or dim is a no-op;
+ *     seqlen == 0 writes zeros to last_state.
+ *   - Pointers must be aligned to their element size.  y must not overlap an
+ *     input; in ssm_step, y must not overlap state.
+ *   - Values are not checked: negative Delta, A >= 0, NaN and Inf are computed
+ *     as written.
+ *   - stream is a hipStream_t (NULL = the default stream).  Calls only enqueue
+ *     work and return; nothing is synchronised.  On any error status nothing
+ *     has been enqueued, except SSM_ERR_HIP, which reports a failed launch.
+ *     Faults inside a kernel surface at the caller's next synchronisation.
+ *   - Thread-safe: no mutable global state.
+ */
+#ifndef SSM66_H
+#define SSM66_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSM_ABI_VERSION 1
+
+/* status codes */
+#define SSM_OK 0
+#define SSM_ERR_NULL 1        /* a required pointer is NULL */
+#define SSM_ERR_SHAPE 2       /* negative size, dstate outside [1, 16], or size overflow */
+#define SSM_ERR_DTYPE 3       /* io_dtype is not SSM_F32 or SSM_BF16 */
+#define SSM_ERR_FLAG 4        /* softplus not 0/1, or dt_mode unknown */
+#define SSM_ERR_ALIGN 5       /* a pointer is not aligned to its element size */
+#define SSM_ERR_UNSUPPORTED 6 /* a size the kernels do not handle (e.g. > 2^31 rows) */
+#define SSM_ERR_HIP 7         /* the HIP runtime rejected the launch */
+
+/* io dtypes */
+#define SSM_F32 0
+#define SSM_BF16 1
+
+/* discretization rules */
+#define SSM_DT_ZOH 0
+#define SSM_DT_EULER 1
+
+/*
+ * The selective scan over whole sequences.
+ *
+ * y[b,t,c] = gate(z[b,t,c]) * (sum_n C[b,t,n] h_t[b,c,n] + D[c] u[b,t,c]),
+ * h_t[b,c,n] = exp(Delta A[c,n]) h_{t-1}[b,c,n] + bbar(Delta, A[c,n], B[b,t,n]) u[b,t,c],
+ * Delta = softplus?(delta[b,t,c] + delta_bias[c]), h_{-1} = 0.
+ * last_state (optional) receives h after the last token.
+ * Returns SSM_OK or an error status (see above).
+ */
+int ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                 const float* D, const void* z, const float* delta_bias, int softplus,
+                 int dt_mode, void* y, float* last_state, int64_t batch, int64_t seqlen,
+                 int64_t dim, int64_t dstate, int io_dtype, void* stream);
+
+/*
+ * One decode step against the state cache `state` (batch, dim, dstate),
+ * updated in place: the same body as one token of ssm_scan_fwd.
+ * u, delta, z, y: (batch, dim); B, C: (batch, dstate).
+ * Returns SSM_OK or an error status.
+ */
+int ssm_step(float* state, const void* u, const void* delta, const float* A, const void* B,
+             const void* C, const float* D, const void* z, const float* delta_bias, int softplus,
+             int dt_mode, void* y, int64_t batch, int64_t dim, int64_t dstate, int io_dtype,
+             void* stream);
+
+/* A static, human-readable string for a status code. */
+const char* ssm_status_string(int status);
+
+/* SSM_ABI_VERSION of the built library. */
+int ssm_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSM66_H */

@@ -1,0 +1,168 @@
+"""MI355X (gfx950) selective scan: Python binding of the C ABI in include/ssm66.h.
+
+This module only marshals arguments: it checks tensor device, dtype, shape and
+contiguity, allocates outputs with torch and passes raw device pointers and the
+current HIP stream to the library.  Every step of the computation runs in the
+library's HIP kernels.  There is no CPU or PyTorch fallback: if the library is
+missing, every call raises.
+
+    y, last_state = scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
+                             softplus=True, dt_mode="zoh")
+    y = step(state, u, delta, A, B, C, D=None, z=None, delta_bias=None,
+             softplus=True, dt_mode="zoh")     # state updated in place
+"""
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libssm66_hip.so")
+
+SSM_F32, SSM_BF16 = 0, 1
+SSM_DT_ZOH, SSM_DT_EULER = 0, 1
+_MODES = {"zoh": SSM_DT_ZOH, "euler": SSM_DT_EULER}
+
+_lib = None
+
+
+class SsmError(RuntimeError):
+    def __init__(self, status, where):
+        super().__init__(f"{where}: status {status} ({status_string(status)})")
+        self.status = status
+
+
+def load_library():
+    """Load the built HIP library (build it with selective_state_space_66_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"HIP library not built: {LIB_PATH} is missing "
+                          "(run `python -m selective_state_space_66_amd.build`)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i64, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.ssm_scan_fwd.restype = ci
+    lib.ssm_scan_fwd.argtypes = [vp] * 8 + [ci, ci, vp, vp, i64, i64, i64, i64, ci, vp]
+    lib.ssm_step.restype = ci
+    lib.ssm_step.argtypes = [vp] * 9 + [ci, ci, vp, i64, i64, i64, ci, vp]
+    lib.ssm_status_string.restype = ctypes.c_char_p
+    lib.ssm_status_string.argtypes = [ci]
+    lib.ssm_abi_version.restype = ci
+    lib.ssm_abi_version.argtypes = []
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().ssm_status_string(int(status)).decode()
+
+
+def abi_version() -> int:
+    return load_library().ssm_abi_version()
+
+
+def _io_code(t):
+    import torch
+    if t.dtype == torch.float32:
+        return SSM_F32
+    if t.dtype == torch.bfloat16:
+        return SSM_BF16
+    raise TypeError(f"io tensors must be float32 or bfloat16, got {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(t, name, shape, dtype, device):
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name}: expected device {device}, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+
+
+def _stream(device):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True, dt_mode="zoh",
+             y=None, last_state=None, return_last_state=True):
+    """Selective scan over whole sequences on the GPU.
+
+    u, delta, z: (batch, L, dim); B, C: (batch, L, N) -- all float32 or all bfloat16.
+    A: (dim, N) float32; D, delta_bias: (dim,) float32.
+    Returns (y, last_state): y like u; last_state (batch, dim, N) float32 (None if not requested).
+    """
+    import torch
+    lib = load_library()
+    if u.dim() != 3:
+        raise ValueError("u must be (batch, L, dim)")
+    batch, L, dim = u.shape
+    N = A.shape[-1]
+    dev = u.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on the GPU")
+    io = u.dtype
+    _io_code(u)
+    _check(u, "u", (batch, L, dim), io, dev)
+    _check(delta, "delta", (batch, L, dim), io, dev)
+    _check(A, "A", (dim, N), torch.float32, dev)
+    _check(B, "B", (batch, L, N), io, dev)
+    _check(C, "C", (batch, L, N), io, dev)
+    _check(D, "D", (dim,), torch.float32, dev)
+    _check(z, "z", (batch, L, dim), io, dev)
+    _check(delta_bias, "delta_bias", (dim,), torch.float32, dev)
+    if y is None:
+        y = torch.empty_like(u)
+    _check(y, "y", (batch, L, dim), io, dev)
+    if last_state is None and return_last_state:
+        last_state = torch.empty((batch, dim, N), dtype=torch.float32, device=dev)
+    _check(last_state, "last_state", (batch, dim, N), torch.float32, dev)
+    st = lib.ssm_scan_fwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                          _ptr(delta_bias), int(bool(softplus)), _MODES[dt_mode], _ptr(y),
+                          _ptr(last_state), batch, L, dim, N, _io_code(u), _stream(dev))
+    if st != 0:
+        raise SsmError(st, "ssm_scan_fwd")
+    return y, last_state
+
+
+def step(state, u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True,
+         dt_mode="zoh", y=None):
+    """One decode step on the GPU; `state` (batch, dim, N) float32 is updated in place.
+
+    u, delta, z: (batch, dim); B, C: (batch, N) -- float32 or bfloat16. Returns y like u.
+    """
+    import torch
+    lib = load_library()
+    if u.dim() != 2:
+        raise ValueError("u must be (batch, dim)")
+    batch, dim = u.shape
+    N = A.shape[-1]
+    dev = u.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on the GPU")
+    io = u.dtype
+    _io_code(u)
+    _check(state, "state", (batch, dim, N), torch.float32, dev)
+    _check(u, "u", (batch, dim), io, dev)
+    _check(delta, "delta", (batch, dim), io, dev)
+    _check(A, "A", (dim, N), torch.float32, dev)
+    _check(B, "B", (batch, N), io, dev)
+    _check(C, "C", (batch, N), io, dev)
+    _check(D, "D", (dim,), torch.float32, dev)
+    _check(z, "z", (batch, dim), io, dev)
+    _check(delta_bias, "delta_bias", (dim,), torch.float32, dev)
+    if y is None:
+        y = torch.empty_like(u)
+    _check(y, "y", (batch, dim), io, dev)
+    st = lib.ssm_step(_ptr(state), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                      _ptr(z), _ptr(delta_bias), int(bool(softplus)), _MODES[dt_mode], _ptr(y),
+                      batch, dim, N, _io_code(u), _stream(dev))
+    if st != 0:
+        raise SsmError(st, "ssm_step")
+    return y

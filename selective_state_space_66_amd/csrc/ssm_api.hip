@@ -1,0 +1,133 @@
+// ssm_api.hip -- the C ABI declared in include/ssm66.h.
+//
+// Argument validation runs before any HIP call, so an invalid call returns its
+// status without touching a device and with nothing enqueued.  A valid call
+// chooses a kernel instance and enqueues one launch on the caller's stream.
+#include <stdint.h>
+#include <stdlib.h>
+
+#include "../../include/ssm66.h"
+#include "ssm_launch.h"
+
+namespace {
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// a * b * c without int64 overflow; false on overflow
+bool mul3(int64_t a, int64_t b, int64_t c, int64_t* out) {
+  __int128 r = (__int128)a * b * c;
+  if (r > INT64_MAX) return false;
+  *out = (int64_t)r;
+  return true;
+}
+
+int check_common(int64_t batch, int64_t len, int64_t dim, int64_t dstate, int io_dtype,
+                 int softplus, int dt_mode) {
+  if (batch < 0 || len < 0 || dim < 0) return SSM_ERR_SHAPE;
+  if (dstate < 1 || dstate > 16) return SSM_ERR_SHAPE;
+  if (io_dtype != SSM_F32 && io_dtype != SSM_BF16) return SSM_ERR_DTYPE;
+  if (softplus != 0 && softplus != 1) return SSM_ERR_FLAG;
+  if (dt_mode != SSM_DT_ZOH && dt_mode != SSM_DT_EULER) return SSM_ERR_FLAG;
+  int64_t tmp;
+  if (!mul3(batch, len, dim, &tmp) || !mul3(batch, len, dstate, &tmp) ||
+      !mul3(batch, dim, dstate, &tmp) || !mul3(dim, dstate, 4, &tmp))
+    return SSM_ERR_SHAPE;
+  return SSM_OK;
+}
+
+// states per wave for the scan: the largest of 4, 2, 1 that divides dstate and
+// keeps the B and C rows aligned for vector scalar loads.  An override
+// (SSM66_SCAN_G = 1, 2 or 4) exists for tuning experiments.
+int pick_scan_g(int64_t dstate, const void* B, const void* C, size_t esize, int64_t blocks) {
+  int forced = 0;
+  if (const char* e = getenv("SSM66_SCAN_G")) forced = atoi(e);
+  const int cands[3] = {4, 2, 1};
+  for (int g : cands) {
+    if (dstate % g) continue;
+    if (!aligned(B, esize * g) || !aligned(C, esize * g)) continue;
+    if (forced && g != forced) continue;
+    (void)blocks;
+    return g;
+  }
+  return 1;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ssm_abi_version(void) { return SSM_ABI_VERSION; }
+
+const char* ssm_status_string(int status) {
+  switch (status) {
+    case SSM_OK: return "ok";
+    case SSM_ERR_NULL: return "a required pointer is NULL";
+    case SSM_ERR_SHAPE: return "invalid shape (negative size, dstate outside [1,16], or overflow)";
+    case SSM_ERR_DTYPE: return "unknown io dtype";
+    case SSM_ERR_FLAG: return "invalid softplus flag or dt_mode";
+    case SSM_ERR_ALIGN: return "pointer not aligned to its element size";
+    case SSM_ERR_UNSUPPORTED: return "size not supported by the kernels";
+    case SSM_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                 const float* D, const void* z, const float* delta_bias, int softplus,
+                 int dt_mode, void* y, float* last_state, int64_t batch, int64_t seqlen,
+                 int64_t dim, int64_t dstate, int io_dtype, void* stream) {
+  int st = check_common(batch, seqlen, dim, dstate, io_dtype, softplus, dt_mode);
+  if (st != SSM_OK) return st;
+  const bool has_tokens = batch > 0 && seqlen > 0 && dim > 0;
+  const bool has_rows = batch > 0 && dim > 0;
+  if (!has_rows) return SSM_OK;
+  if (!A) return SSM_ERR_NULL;
+  if (has_tokens && (!u || !delta || !B || !C || !y)) return SSM_ERR_NULL;
+  const size_t es = io_dtype == SSM_BF16 ? 2 : 4;
+  const void* io_ptrs[6] = {u, delta, B, C, z, y};
+  for (const void* q : io_ptrs)
+    if (q && !aligned(q, es)) return SSM_ERR_ALIGN;
+  const void* f32_ptrs[4] = {A, D, delta_bias, last_state};
+  for (const void* q : f32_ptrs)
+    if (q && !aligned(q, 4)) return SSM_ERR_ALIGN;
+  if (batch > 65535 || (dim + 63) / 64 > 0x7fffffff) return SSM_ERR_UNSUPPORTED;
+
+  ssm66::ScanParams p;
+  p.u = u; p.delta = delta; p.A = A; p.B = B; p.C = C; p.D = D; p.z = z;
+  p.delta_bias = delta_bias; p.y = y; p.last_state = last_state;
+  p.batch = batch; p.L = seqlen; p.dim = dim; p.N = dstate; p.softplus = softplus;
+  const int G = pick_scan_g(dstate, B, C, es, batch * ((dim + 63) / 64));
+  hipError_t e = ssm66::launch_scan_fwd(p, io_dtype, G, dt_mode == SSM_DT_ZOH, z != nullptr,
+                                        (hipStream_t)stream);
+  return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
+int ssm_step(float* state, const void* u, const void* delta, const float* A, const void* B,
+             const void* C, const float* D, const void* z, const float* delta_bias, int softplus,
+             int dt_mode, void* y, int64_t batch, int64_t dim, int64_t dstate, int io_dtype,
+             void* stream) {
+  int st = check_common(batch, 1, dim, dstate, io_dtype, softplus, dt_mode);
+  if (st != SSM_OK) return st;
+  if (batch == 0 || dim == 0) return SSM_OK;
+  if (!state || !u || !delta || !A || !B || !C || !y) return SSM_ERR_NULL;
+  const size_t es = io_dtype == SSM_BF16 ? 2 : 4;
+  const void* io_ptrs[6] = {u, delta, B, C, z, y};
+  for (const void* q : io_ptrs)
+    if (q && !aligned(q, es)) return SSM_ERR_ALIGN;
+  const void* f32_ptrs[4] = {state, A, D, delta_bias};
+  for (const void* q : f32_ptrs)
+    if (q && !aligned(q, 4)) return SSM_ERR_ALIGN;
+  int64_t threads;
+  if (!mul3(batch, dim, 4, &threads) || (threads + 255) / 256 > 0x7fffffff)
+    return SSM_ERR_UNSUPPORTED;
+
+  ssm66::StepParams p;
+  p.state = state; p.u = u; p.delta = delta; p.A = A; p.B = B; p.C = C; p.D = D; p.z = z;
+  p.delta_bias = delta_bias; p.y = y; p.batch = batch; p.dim = dim; p.N = dstate;
+  p.softplus = softplus;
+  hipError_t e = ssm66::launch_step(p, io_dtype, dt_mode == SSM_DT_ZOH, z != nullptr,
+                                    (hipStream_t)stream);
+  return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,45 @@
+// ssm_launch.h -- internal interface between the C-ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssm66 {
+
+struct ScanParams {
+  const void* u;
+  const void* delta;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* D;           // nullable
+  const void* z;            // nullable
+  const float* delta_bias;  // nullable
+  void* y;
+  float* last_state;  // nullable
+  int64_t batch, L, dim, N;
+  int softplus;
+};
+
+struct StepParams {
+  float* state;
+  const void* u;
+  const void* delta;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* D;
+  const void* z;
+  const float* delta_bias;
+  void* y;
+  int64_t batch, dim, N;
+  int softplus;
+};
+
+// G = states per wave (1, 2 or 4); G must divide N and B, C must be aligned to
+// G elements.
+hipError_t launch_scan_fwd(const ScanParams& p, int io_dtype, int G, bool zoh, bool gate,
+                           hipStream_t stream);
+hipError_t launch_step(const StepParams& p, int io_dtype, bool zoh, bool gate, hipStream_t stream);
+
+}  // namespace ssm66

@@ -1,0 +1,111 @@
+"""The C-ABI library loads, exports every function include/ssm66.h declares, and
+rejects invalid arguments before touching a device.  No compute call is made
+here (no GPU is needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import selective_state_space_66_amd as ssm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssm66.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(ssm_\w+)\s*\(", src, flags=re.M)))
+
+
+def _header_constants():
+    src = open(HEADER).read()
+    return {k: int(v) for k, v in re.findall(r"#define\s+(SSM_\w+)\s+(\d+)", src)}
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ssm.LIB_PATH):
+        from selective_state_space_66_amd import build
+        build.build()
+    return ssm.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared_functions()
+    assert set(names) == {"ssm_scan_fwd", "ssm_step", "ssm_status_string", "ssm_abi_version"}
+    raw = ctypes.CDLL(ssm.LIB_PATH)
+    for n in names:
+        assert hasattr(raw, n), f"{n} not exported"
+
+
+def test_abi_version_and_strings(lib):
+    consts = _header_constants()
+    assert ssm.abi_version() == consts["SSM_ABI_VERSION"]
+    for k, v in consts.items():
+        if k.startswith("SSM_ERR") or k == "SSM_OK":
+            s = ssm.status_string(v)
+            assert s and s != "unknown status"
+    assert ssm.status_string(12345) == "unknown status"
+
+
+# a fake, well-aligned, never-dereferenced device address
+FAKE = ctypes.c_void_p(0x10000)
+MISALIGNED = ctypes.c_void_p(0x10001)
+
+
+def _scan(lib, **kw):
+    a = dict(u=FAKE, delta=FAKE, A=FAKE, B=FAKE, C=FAKE, D=None, z=None, bias=None, softplus=1,
+             dt_mode=0, y=FAKE, last=None, batch=2, L=8, dim=64, N=16, io=1, stream=None)
+    a.update(kw)
+    return lib.ssm_scan_fwd(a["u"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], a["bias"],
+                            a["softplus"], a["dt_mode"], a["y"], a["last"], a["batch"], a["L"],
+                            a["dim"], a["N"], a["io"], a["stream"])
+
+
+def _step(lib, **kw):
+    a = dict(state=FAKE, u=FAKE, delta=FAKE, A=FAKE, B=FAKE, C=FAKE, D=None, z=None, bias=None,
+             softplus=1, dt_mode=0, y=FAKE, batch=2, dim=64, N=16, io=1, stream=None)
+    a.update(kw)
+    return lib.ssm_step(a["state"], a["u"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"],
+                        a["bias"], a["softplus"], a["dt_mode"], a["y"], a["batch"], a["dim"],
+                        a["N"], a["io"], a["stream"])
+
+
+@pytest.mark.parametrize("call", [_scan, _step])
+def test_invalid_arguments_are_rejected(lib, call):
+    c = _header_constants()
+    assert call(lib, N=0) == c["SSM_ERR_SHAPE"]
+    assert call(lib, N=17) == c["SSM_ERR_SHAPE"]
+    assert call(lib, batch=-1) == c["SSM_ERR_SHAPE"]
+    assert call(lib, dim=-3) == c["SSM_ERR_SHAPE"]
+    assert call(lib, io=2) == c["SSM_ERR_DTYPE"]
+    assert call(lib, softplus=2) == c["SSM_ERR_FLAG"]
+    assert call(lib, dt_mode=7) == c["SSM_ERR_FLAG"]
+    assert call(lib, u=None) == c["SSM_ERR_NULL"]
+    assert call(lib, A=None) == c["SSM_ERR_NULL"]
+    assert call(lib, y=None) == c["SSM_ERR_NULL"]
+    assert call(lib, u=MISALIGNED) == c["SSM_ERR_ALIGN"]
+    assert call(lib, A=MISALIGNED) == c["SSM_ERR_ALIGN"]
+    assert call(lib, D=MISALIGNED) == c["SSM_ERR_ALIGN"]
+    assert call(lib, batch=1 << 40, dim=1 << 40) == c["SSM_ERR_SHAPE"]
+    # empty work is a no-op and never reaches the device
+    assert call(lib, batch=0) == c["SSM_OK"]
+    assert call(lib, dim=0) == c["SSM_OK"]
+
+
+def test_scan_specific_checks(lib):
+    c = _header_constants()
+    assert _scan(lib, L=-1) == c["SSM_ERR_SHAPE"]
+    assert _scan(lib, last=MISALIGNED) == c["SSM_ERR_ALIGN"]
+    assert _scan(lib, batch=70000) == c["SSM_ERR_UNSUPPORTED"]
+    assert _step(lib, state=None) == c["SSM_ERR_NULL"]
+    assert _step(lib, state=MISALIGNED) == c["SSM_ERR_ALIGN"]
+
+
+def test_python_binding_rejects_cpu_tensors(lib):
+    import torch
+    u = torch.zeros(1, 4, 8)
+    with pytest.raises(ValueError):
+        ssm.scan_fwd(u, u, torch.zeros(8, 16), torch.zeros(1, 4, 16), torch.zeros(1, 4, 16))

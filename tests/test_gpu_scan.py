@@ -1,0 +1,180 @@
+"""GPU parity of ssm_scan_fwd against the fp64 oracle.
+
+Tolerances: fp32 I/O, max |y - y_ref| <= 1e-4 (1 + |y_ref|) elementwise, and the
+same for the final state; bf16 I/O with fp32 state, relative RMS error <= 1e-2
+on y and on the final state.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from gpu_helpers import (DEV, assert_close, f64, max_scaled_err, scan_gpu, scan_ref, to_dev,
+                         to_host64)
+import oracle
+import selective_state_space_66_amd as ssm
+
+pytestmark = pytest.mark.gpu
+
+
+def _cfg(batch, L, dim, N, io, gate, seed=21):
+    return W.ScanConfig(f"t{batch}x{L}x{dim}x{N}", batch, L, dim, N, io, gate, seed)
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("mode", ["zoh", "euler"])
+@pytest.mark.parametrize("gate", [True, False])
+def test_ragged_tiles_and_chunks(io, mode, gate):
+    # 3 channel tiles (last one 2 wide), 4 token chunks (last one 4 long)
+    inp = W.scan_inputs(_cfg(2, 100, 130, 16, io, gate))
+    y, last = scan_gpu(inp, mode)
+    yr, lr = scan_ref(inp, mode)
+    assert_close(to_host64(y), yr, io, "y")
+    assert_close(to_host64(last), lr, io, "last_state")
+
+
+@pytest.mark.parametrize("N", [1, 2, 3, 4, 5, 8, 12, 16])
+@pytest.mark.parametrize("mode", ["zoh", "euler"])
+def test_state_sizes(N, mode):
+    inp = W.scan_inputs(_cfg(2, 70, 96, N, "f32", True, seed=N))
+    y, last = scan_gpu(inp, mode)
+    yr, lr = scan_ref(inp, mode)
+    assert last.shape == (2, 96, N)
+    assert_close(to_host64(y), yr, "f32", "y")
+    assert_close(to_host64(last), lr, "f32", "last_state")
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("mode", ["zoh", "euler"])
+def test_optional_inputs_absent(io, mode):
+    inp = W.scan_inputs(_cfg(1, 64, 64, 16, io, False, seed=5))
+    y, last = scan_gpu(inp, mode, use_D=False, use_bias=False)
+    yr, lr = scan_ref(inp, mode, use_D=False, use_bias=False)
+    assert_close(to_host64(y), yr, io, "y")
+    assert_close(to_host64(last), lr, io, "last_state")
+
+
+@pytest.mark.parametrize("mode", ["zoh", "euler"])
+def test_softplus_off(mode):
+    inp = W.scan_inputs(_cfg(2, 80, 70, 16, "f32", True, seed=6))
+    # Delta = raw + bias given directly: keep it positive and modest
+    inp["delta"] = (np.abs(inp["delta"]) * 0.05).astype(np.float32)
+    inp["delta_bias"] = np.abs(inp["delta_bias"]) * 0.001
+    y, last = scan_gpu(inp, mode, softplus=False)
+    yr, lr = scan_ref(inp, mode, softplus=False)
+    assert_close(to_host64(y), yr, "f32", "y")
+    assert_close(to_host64(last), lr, "f32", "last_state")
+
+
+def test_zoh_small_and_zero_A():
+    """Channels with |A| < 1/2 or A = 0 take the careful ZOH form (limit Delta B at A = 0)."""
+    inp = W.scan_inputs(_cfg(2, 90, 192, 16, "f32", True, seed=7))
+    A = inp["A"].copy()
+    A[3, 5] = 0.0          # first tile: one zero entry
+    A[70, :] = -0.01       # second tile: a slow channel
+    A[150, 2] = 0.3        # third tile: an unstable, small positive rate
+    inp["A"] = A
+    for mode in ("zoh", "euler"):
+        y, last = scan_gpu(inp, mode)
+        yr, lr = scan_ref(inp, mode)
+        assert_close(to_host64(y), yr, "f32", f"y {mode}")
+        assert_close(to_host64(last), lr, "f32", f"last_state {mode}")
+
+
+def test_extreme_step_sizes_finite():
+    """softplus of +-1000 stays finite; Delta = 0 tokens leave the state alone."""
+    inp = W.scan_inputs(_cfg(1, 64, 64, 16, "f32", True, seed=8))
+    d = inp["delta"].copy()
+    d[0, ::7, :] = 1000.0
+    d[0, 3::11, :] = -1000.0
+    inp["delta"] = d
+    for mode in ("zoh", "euler"):
+        y, last = scan_gpu(inp, mode)
+        yr, lr = scan_ref(inp, mode)
+        assert np.all(np.isfinite(to_host64(y)))
+        assert_close(to_host64(y), yr, "f32", f"y {mode}")
+        assert_close(to_host64(last), lr, "f32", f"last {mode}")
+
+
+def test_empty_sizes():
+    A = torch.full((8, 16), -1.0, device=DEV)
+    u = torch.zeros((2, 0, 8), device=DEV)
+    B = torch.zeros((2, 0, 16), device=DEV)
+    last = torch.full((2, 8, 16), 7.0, device=DEV)
+    y, last = ssm.scan_fwd(u, u, A, B, B, last_state=last)
+    torch.cuda.synchronize()
+    assert y.shape == (2, 0, 8) and torch.all(last == 0)
+    u0 = torch.zeros((0, 5, 8), device=DEV)
+    B0 = torch.zeros((0, 5, 16), device=DEV)
+    y0, l0 = ssm.scan_fwd(u0, u0, A, B0, B0)
+    assert y0.shape == (0, 5, 8) and l0.shape == (0, 8, 16)
+    Az = torch.zeros((0, 16), device=DEV)
+    uz = torch.zeros((3, 5, 0), device=DEV)
+    Bz = torch.zeros((3, 5, 16), device=DEV)
+    yz, lz = ssm.scan_fwd(uz, uz, Az, Bz, Bz)
+    torch.cuda.synchronize()
+    assert yz.shape == (3, 5, 0)
+
+
+def test_deterministic():
+    inp = W.scan_inputs(_cfg(2, 96, 200, 16, "bf16", True, seed=9))
+    y1, l1 = scan_gpu(inp)
+    y2, l2 = scan_gpu(inp)
+    assert torch.equal(y1, y2) and torch.equal(l1, l2)
+
+
+def test_causality_on_gpu():
+    inp = W.scan_inputs(_cfg(1, 80, 64, 16, "f32", True, seed=10))
+    y1, _ = scan_gpu(inp)
+    inp2 = dict(inp)
+    inp2["u"] = inp["u"].copy()
+    inp2["u"][0, 50, :] += 1.0
+    y2, _ = scan_gpu(inp2)
+    assert torch.equal(y1[:, :50], y2[:, :50])
+    assert not torch.equal(y1[:, 50], y2[:, 50])
+
+
+# ------------------------------------------------------------ the workloads
+
+
+def test_tiny_config_full():
+    cfg = W.SCAN_CONFIGS["tiny"]
+    inp = W.scan_inputs(cfg)
+    for mode in ("zoh", "euler"):
+        y, last = scan_gpu(inp, mode)
+        yr, lr = scan_ref(inp, mode)
+        assert_close(to_host64(y), yr, "f32", f"y {mode}")
+        assert_close(to_host64(last), lr, "f32", f"last {mode}")
+
+
+def _sample_channels(dim, seed, k=12):
+    rng = np.random.default_rng(seed)
+    ch = {0, 1, 63, 64, dim // 2, dim - 65, dim - 1}
+    ch.update(int(c) for c in rng.choice(dim, size=k, replace=False))
+    return np.array(sorted(ch), dtype=np.int64)
+
+
+@pytest.mark.parametrize("name", ["mamba130m", "mamba1p4b", "longseq"])
+def test_full_size_sampled(name):
+    """Full-size launch (the benchmark's configuration); the oracle checks a sample
+    of channels over every batch entry and token, plus their final states."""
+    cfg = W.SCAN_CONFIGS[name]
+    print(f"[{name}] generating inputs", flush=True)
+    inp = W.scan_inputs(cfg)
+    ch = _sample_channels(cfg.dim, cfg.seed, k=6 if name == "longseq" else 12)
+    for mode in ("zoh", "euler"):
+        print(f"[{name}] launch {mode}", flush=True)
+        y, last = scan_gpu(inp, mode)
+        chd = torch.from_numpy(ch).to(DEV)
+        ys = to_host64(y.index_select(2, chd))
+        ls = to_host64(last.index_select(1, chd))
+        del y, last
+        sub = W.scan_inputs(cfg, channels=ch)
+        for k in ("u", "delta", "z"):
+            if sub[k] is not None:
+                assert np.array_equal(sub[k], inp[k][:, :, ch])
+        yr, lr = scan_ref(sub, mode)
+        e1 = assert_close(ys, yr, "bf16", f"{name} y {mode}")
+        e2 = assert_close(ls, lr, "bf16", f"{name} last_state {mode}")
+        print(f"[{name}] {mode}: rel-rms y {e1:.2e}, last_state {e2:.2e}", flush=True)
+        torch.cuda.empty_cache()

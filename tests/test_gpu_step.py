@@ -1,0 +1,143 @@
+"""GPU parity of ssm_step (the decode step) against the fp64 oracle, and the
+scan/step consistency properties on the GPU."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import selective_state_space_66_amd as ssm
+import workloads as W
+from gpu_helpers import DEV, assert_close, f64, scan_gpu, scan_ref, to_dev, to_host64
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_steps_gpu(cfg, nsteps, check_at, channels, mode="zoh"):
+    """Run nsteps GPU steps on the full state; return the sampled y at check_at
+    and the sampled final state."""
+    A, D, bias = W.channel_params(cfg.seed, cfg.dim, cfg.N)
+    st = to_dev(W.step_state0(cfg), "f32")
+    Ad, Dd, bd = to_dev(A, "f32"), to_dev(D, "f32"), to_dev(bias, "f32")
+    chd = torch.from_numpy(channels).to(DEV)
+    got = {}
+    for s in range(nsteps):
+        inp = W.step_inputs(cfg, s)
+        y = ssm.step(st, to_dev(inp["u"], cfg.io), to_dev(inp["delta"], cfg.io), Ad,
+                     to_dev(inp["B"], cfg.io), to_dev(inp["C"], cfg.io), D=Dd,
+                     z=to_dev(inp["z"], cfg.io), delta_bias=bd, dt_mode=mode)
+        if (s + 1) in check_at:
+            got[s + 1] = to_host64(y.index_select(1, chd))
+    return got, to_host64(st.index_select(1, chd))
+
+
+def _run_steps_ref(cfg, nsteps, check_at, channels, mode="zoh"):
+    A, D, bias = W.channel_params(cfg.seed, cfg.dim, cfg.N, channels)
+    st = W.step_state0(cfg, channels).astype(np.float64)
+    out = {}
+    for s in range(nsteps):
+        inp = W.step_inputs(cfg, s, channels)
+        y, st = oracle.step(st, f64(inp["u"], cfg.io), f64(inp["delta"], cfg.io), A,
+                            f64(inp["B"], cfg.io), f64(inp["C"], cfg.io), D=D,
+                            z=f64(inp["z"], cfg.io), delta_bias=bias, dt_mode=mode)
+        if (s + 1) in check_at:
+            out[s + 1] = y
+    return out, st
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("mode", ["zoh", "euler"])
+@pytest.mark.parametrize("N", [16, 5])
+def test_steps_small(io, mode, N):
+    cfg = W.StepConfig("s", 3, 70, N, io, True, 31, 20)
+    ch = np.arange(70)
+    got, gst = _run_steps_gpu(cfg, 20, set(range(1, 21)), ch, mode)
+    ref, rst = _run_steps_ref(cfg, 20, set(range(1, 21)), ch, mode)
+    for s in ref:
+        assert_close(got[s], ref[s], io, f"y step {s}")
+    assert_close(gst, rst, io, "state")
+
+
+def test_step_without_optional_inputs():
+    cfg = W.StepConfig("s", 2, 64, 16, "f32", False, 32, 5)
+    A, _, _ = W.channel_params(cfg.seed, cfg.dim, cfg.N)
+    st0 = W.step_state0(cfg)
+    inp = W.step_inputs(cfg, 0)
+    st = to_dev(st0, "f32")
+    y = ssm.step(st, to_dev(inp["u"], "f32"), to_dev(inp["delta"], "f32"), to_dev(A, "f32"),
+                 to_dev(inp["B"], "f32"), to_dev(inp["C"], "f32"), softplus=True)
+    torch.cuda.synchronize()
+    yr, sr = oracle.step(st0, inp["u"], inp["delta"], A, inp["B"], inp["C"], softplus=True)
+    assert_close(to_host64(y), yr, "f32", "y")
+    assert_close(to_host64(st), sr, "f32", "state")
+
+
+@pytest.mark.parametrize("mode", ["zoh", "euler"])
+def test_scan_equals_steps_on_gpu(mode):
+    """Token-by-token decoding reproduces the scan at every step."""
+    cfg = W.ScanConfig("c", 2, 48, 130, 16, "f32", True, 33)
+    inp = W.scan_inputs(cfg)
+    y, last = scan_gpu(inp, mode)
+    yh = to_host64(y)
+    st = torch.zeros((2, 130, 16), device=DEV)
+    Ad, Dd, bd = to_dev(inp["A"], "f32"), to_dev(inp["D"], "f32"), to_dev(inp["delta_bias"], "f32")
+    for t in range(48):
+        yt = ssm.step(st, to_dev(inp["u"][:, t], "f32"), to_dev(inp["delta"][:, t], "f32"), Ad,
+                      to_dev(inp["B"][:, t], "f32"), to_dev(inp["C"][:, t], "f32"), D=Dd,
+                      z=to_dev(inp["z"][:, t], "f32"), delta_bias=bd, dt_mode=mode)
+        assert_close(to_host64(yt), yh[:, t], "f32", f"step {t}")
+    assert_close(to_host64(st), to_host64(last), "f32", "state")
+
+
+@pytest.mark.parametrize("mode", ["zoh", "euler"])
+def test_prefill_then_decode_on_gpu(mode):
+    """Prefill keeps only the final state; decoding the rest from it matches the
+    oracle's full scan."""
+    cfg = W.ScanConfig("p", 2, 60, 96, 16, "bf16", True, 34)
+    inp = W.scan_inputs(cfg)
+    L1 = 37
+    head = {k: (v[:, :L1] if (k in ("u", "delta", "z", "B", "C") and v is not None) else v)
+            for k, v in inp.items()}
+    _, st = scan_gpu(head, mode)
+    yr, lr = scan_ref(inp, mode)
+    Ad, Dd, bd = to_dev(inp["A"], "f32"), to_dev(inp["D"], "f32"), to_dev(inp["delta_bias"], "f32")
+    ys = []
+    for t in range(L1, 60):
+        ys.append(to_host64(ssm.step(
+            st, to_dev(inp["u"][:, t], "bf16"), to_dev(inp["delta"][:, t], "bf16"), Ad,
+            to_dev(inp["B"][:, t], "bf16"), to_dev(inp["C"][:, t], "bf16"), D=Dd,
+            z=to_dev(inp["z"][:, t], "bf16"), delta_bias=bd, dt_mode=mode)))
+    assert_close(np.stack(ys, axis=1), yr[:, L1:], "bf16", "decoded y")
+    assert_close(to_host64(st), lr, "bf16", "final state")
+
+
+def _sample(dim, seed):
+    rng = np.random.default_rng(seed)
+    return np.array(sorted({0, 63, 64, dim - 1, *rng.choice(dim, 8, replace=False).tolist()}),
+                    dtype=np.int64)
+
+
+def test_decode_config_full_size():
+    """The decode workload at full size (256 x 5120, N = 16) for 100 steps."""
+    cfg = W.STEP_CONFIGS["decode"]
+    ch = _sample(cfg.dim, 4)
+    checks = {1, 10, 100}
+    print("[decode] full size, 100 steps", flush=True)
+    got, gst = _run_steps_gpu(cfg, 100, checks, ch)
+    ref, rst = _run_steps_ref(cfg, 100, checks, ch)
+    for s in sorted(checks):
+        assert_close(got[s], ref[s], "bf16", f"y step {s}")
+    assert_close(gst, rst, "bf16", "state")
+
+
+def test_decode_thousand_steps():
+    """1000 consecutive steps (the decode workload's length) on 16 of its 256 sequences."""
+    full = W.STEP_CONFIGS["decode"]
+    cfg = W.StepConfig("decode16", 16, full.dim, full.N, full.io, True, full.seed, 1000)
+    ch = _sample(cfg.dim, 5)
+    checks = {1, 10, 100, 1000}
+    print("[decode] 16 sequences, 1000 steps", flush=True)
+    got, gst = _run_steps_gpu(cfg, 1000, checks, ch)
+    ref, rst = _run_steps_ref(cfg, 1000, checks, ch)
+    for s in sorted(checks):
+        assert_close(got[s], ref[s], "bf16", f"y step {s}")
+    assert_close(gst, rst, "bf16", "state")

@@ -3,7 +3,7 @@
 Serves both the HIP path and the oracle; holds none of the scan's arithmetic.
 
 Values are counter-based: element i of stream s under seed k is a pure function
-of (k, s, i) (SplitMix64 of the stream position, then Box-Muller), so any
+of (k, s, i) (SplitMix64 of the stream position, then Box-Muller in float32), so any
 subset of channels of a full-size workload can be regenerated without drawing
 the rest.  That is what lets the oracle check sampled channels of the largest
 shapes.
@@ -47,21 +47,59 @@ def _key(seed: int, stream: int) -> np.uint64:
     return k[0]
 
 
-def uniform(seed: int, stream: int, idx: np.ndarray) -> np.ndarray:
-    """U(0,1) (open interval) in float64 at integer positions idx."""
+def _hash(seed: int, stream: int, idx: np.ndarray) -> np.ndarray:
+    """SplitMix64 of stream position idx: a uint64 per element."""
     idx = np.asarray(idx, dtype=np.uint64)
     with np.errstate(over="ignore"):
-        h = _mix(_key(seed, stream) + (idx + np.uint64(1)) * _GOLDEN)
+        return _mix(_key(seed, stream) + (idx + np.uint64(1)) * _GOLDEN)
+
+
+def uniform(seed: int, stream: int, idx: np.ndarray) -> np.ndarray:
+    """U(0,1) (open interval) in float64 at integer positions idx (53-bit)."""
+    h = _hash(seed, stream, idx)
     return ((h >> np.uint64(11)).astype(np.float64) + 0.5) * (1.0 / 9007199254740992.0)
 
 
+def _normal_block(seed, stream, idx, std):
+    # one hash per value: 24 bits for the radius, 24 for the angle (Box-Muller,
+    # cosine branch) -- tails reach about 5.9 standard deviations
+    h = _hash(seed, stream, idx)
+    u1 = ((h >> np.uint64(40)).astype(np.float32) + np.float32(0.5)) * np.float32(2.0 ** -24)
+    u2 = ((h & np.uint64(0xFFFFFF)).astype(np.float32) + np.float32(0.5)) * np.float32(2.0 ** -24)
+    z = np.sqrt(np.float32(-2.0) * np.log(u1)) * np.cos(np.float32(2.0 * np.pi) * u2)
+    if std != 1.0:
+        z = z * np.float32(std)
+    return z.astype(np.float32, copy=False)
+
+
+_POOL = None
+
+
+def _pool():
+    global _POOL
+    if _POOL is None:
+        import concurrent.futures
+        import os
+        n = min(16, os.cpu_count() or 1)
+        _POOL = concurrent.futures.ThreadPoolExecutor(max_workers=n)
+    return _POOL
+
+
 def normal(seed: int, stream: int, idx: np.ndarray, std: float = 1.0) -> np.ndarray:
-    """N(0, std^2) as float32 at integer positions idx (Box-Muller, cosine branch)."""
-    idx = np.asarray(idx, dtype=np.uint64)
-    u1 = uniform(seed, stream, idx * np.uint64(2))
-    u2 = uniform(seed, stream, idx * np.uint64(2) + np.uint64(1))
-    z = np.sqrt(-2.0 * np.log(u1)) * np.cos(2.0 * np.pi * u2)
-    return (z * std).astype(np.float32)
+    """N(0, std^2) as float32 at integer positions idx."""
+    idx = np.asarray(idx)
+    flat = idx.reshape(-1)
+    n = flat.size
+    blk = 1 << 21
+    if n <= blk:
+        return _normal_block(seed, stream, flat, std).reshape(idx.shape)
+    out = np.empty(n, dtype=np.float32)
+
+    def work(s0):
+        out[s0:s0 + blk] = _normal_block(seed, stream, flat[s0:s0 + blk], std)
+
+    list(_pool().map(work, range(0, n, blk)))
+    return out.reshape(idx.shape)
 
 
 def to_bf16_bits(x: np.ndarray) -> np.ndarray:
