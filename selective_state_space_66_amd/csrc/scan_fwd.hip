@@ -7,32 +7,34 @@
 // with bbar from "The discretization the code actually uses" (ZOH, or the
 // exponential-Euler rule Delta B), reading the state after writing it.
 // Inputs are read once, y is written once and the state never leaves the
-// chip, the fusion argued for in "Why the scan must be fused".
+// chip -- the fusion argued for in "Why the scan must be fused".
 //
-// Work decomposition (one block = one batch row x 64 channels):
-//   * lane  = channel.  B_t and C_t are shared by all channels, so within a
-//     wave they are uniform: they arrive by scalar loads into SGPRs and cost
-//     no vector bandwidth or LDS traffic.
-//   * wave  = a group of G of the 16 state entries; the block has P = 16/G
-//     waves.  Each lane keeps its G states in VGPRs for the whole sequence.
-//   * time  = sequential inside the lane, in chunks of TC tokens.  Per chunk,
-//     each wave prepares TC/P tokens: it reads u, raw delta and z (coalesced,
-//     128 B per row for bf16), computes Delta, Delta*u, D*u and silu(z) once
-//     per (token, channel) and stages them in LDS.  After a barrier every wave
-//     runs the recurrence over the whole chunk for its states and writes its
-//     partial readout sum_n C_n h_n to LDS; after a second barrier each wave
-//     reduces the P partials for its tokens, applies the skip and the gate and
-//     stores y.  Raw loads for the next chunk are issued before the recurrence
-//     so that they land while it runs.  The state carries from chunk to chunk
-//     in registers.
+// Work decomposition.  A block owns one batch entry and CW consecutive
+// channels; its CW x NG threads are (channel, state group) pairs, each group
+// holding G of the (padded) NPAD = G NG state entries of its channel in VGPRs
+// for the whole sequence.  Tokens run sequentially in chunks of TC:
+//   prep      each thread reads u, raw delta and z for TC/NG tokens of its
+//             channel, computes Delta and Delta*u (or u) once per (token,
+//             channel) and stages them in LDS; D*u and silu(z) stay in its
+//             registers for the epilogue.  B and C rows of the chunk are
+//             staged in LDS as fp32, interleaved so that one 16-byte read
+//             gives a group its B and C for a token.  Raw loads of the next
+//             chunk are then issued, to land while the recurrence runs.
+//   recurrence (after a barrier) every thread runs its G states over the TC
+//             tokens: per update one v_exp_f32 and 4 (Euler) or 6 (ZOH)
+//             VALU ops; everything it reads comes from LDS, so waits are
+//             in-order and loads pipeline.  It writes one partial readout
+//             per token to LDS.
+//   epilogue  (after a second barrier) each thread sums the NG partials of
+//             its TC/NG tokens, adds D*u, applies the gate and stores y.
+// The state carries from chunk to chunk in registers; after the last chunk it
+// is written to last_state.
 //
-// Per state update the recurrence costs 1 exp + 4 VALU ops (exponential-Euler:
-// Delta*A, Delta*u*B, fma state, fma readout) or 1 exp + 6 (zero-order hold).
-// ZOH fast path: the lane keeps g = A h, for which
+// ZOH fast path: the thread keeps g = A h, for which
 //   g_t = abar (g_{t-1} + u B) - u B,
-// the exact ZOH update multiplied through by A, with no division and no
-// cancellation for |A| >= 1/2; the readout uses C/A.  A wave whose channels
-// hold any |A| < 1/2 (or A = 0) instead runs the careful path, h-form with
+// the exact ZOH update multiplied through by A: no division, no (abar - 1)
+// cancellation; the readout uses C / A.  A wave whose channels hold any
+// |A| < 1/2 (or A = 0) runs the careful form instead, h-form with
 // bbar = Delta B phi(Delta A), phi(k) = (e^k - 1)/k, accurate for every A.
 #include "ssm_device.h"
 #include "ssm_launch.h"
@@ -58,88 +60,127 @@ __device__ __forceinline__ typename RawT<IO>::type load_raw(const IO* __restrict
 
 enum class Path { kEuler, kZohFast, kZohCareful };
 
-template <int TC, int P>
-struct Smem {
-  float2 dd[TC][64];  // (Delta, x): x = Delta*u (Euler) or u (ZOH)
-  float2 ep[TC][64];  // (D*u, silu(z) or 1)
-  float part[P][TC][64];
+// Static shape of one kernel instance.
+template <int G_, int NG_>
+struct Shape {
+  static constexpr int G = G_;                   // states per thread
+  static constexpr int NG = NG_;                 // state groups per channel
+  static constexpr int NPAD = G * NG;            // padded state count
+  static constexpr int CW = NG >= 4 ? 16 : 64 / NG;  // channels per block
+  static constexpr int THREADS = CW * NG;
+  static constexpr int TC = NG == 8 ? 48 : 32;   // tokens per chunk
+  static constexpr int RPT = TC / NG;            // tokens each thread prepares and finishes
+  static constexpr int BCN = TC * NPAD;          // B (and C) elements per chunk
+  static constexpr int BCPT = (BCN + THREADS - 1) / THREADS;
+  static constexpr int PSTRIDE = TC * CW + 16;   // partial-readout row stride (bank offset)
+  static_assert(TC % NG == 0, "tokens of a chunk must split evenly over the groups");
+  static_assert(THREADS % 64 == 0, "whole waves");
 };
 
-// The recurrence over `nt` tokens of one chunk for the G states of this lane.
-template <typename IO, int G, int TC, int P, Path PATH, bool FULL>
-__device__ __forceinline__ void run_chunk(Smem<TC, P>& sm, float (&st)[G], const float (&Ap)[G],
-                                          const float (&Aa)[G], const float (&CA)[G],
-                                          const IO* __restrict__ Bp, const IO* __restrict__ Cp,
-                                          int64_t N, int nt, int w, int lane) {
-  constexpr int kUnroll = FULL ? 8 : 1;
-  const int n_end = FULL ? TC : nt;
-#pragma unroll kUnroll
-  for (int t = 0; t < n_end; ++t) {
-    const float2 dd = sm.dd[t][lane];
-    float Bv[G], Cv[G];
-    load_uniform<G>(Bp + t * N, Bv);
-    load_uniform<G>(Cp + t * N, Cv);
-    float acc = 0.0f;
-#pragma unroll
-    for (int k = 0; k < G; ++k) {
-      const float bk = Bv[k];
-      const float ck = Cv[k];
-      const float a = exp2_hw(dd.x * Ap[k]);  // abar = exp(Delta A)
-      if constexpr (PATH == Path::kEuler) {
-        st[k] = fmaf(a, st[k], dd.y * bk);  // h = abar h + (Delta u) B
-        acc = fmaf(ck, st[k], acc);
-      } else if constexpr (PATH == Path::kZohFast) {
-        const float ub = dd.y * bk;          // u B
-        st[k] = fmaf(a, st[k] + ub, -ub);    // g = abar (g + uB) - uB,  g = A h
-        acc = fmaf(ck * CA[k], st[k], acc);  // C h = (C / A) g
-      } else {
-        const float kap = dd.x * Aa[k];      // Delta A
-        const float bbar = dd.x * bk * zoh_phi(kap, a);
-        st[k] = fmaf(a, st[k], bbar * dd.y);  // h = abar h + bbar u
-        acc = fmaf(ck, st[k], acc);
-      }
-    }
-    sm.part[w][t][lane] = acc;
+template <class S>
+struct Smem {
+  float2 dd[S::TC][S::CW];              // (Delta, x): x = Delta*u (Euler) or u (ZOH)
+  float bc[S::TC][S::NG][2 * S::G];     // per token and group: G values of B, then of C
+  float part[S::NG][S::PSTRIDE];        // partial readouts, [group][token * CW + channel]
+};
+
+// Read 2G consecutive floats (the group's B and C) from LDS.
+template <int G>
+__device__ __forceinline__ void read_bc(const float* p, float (&b)[G], float (&c)[G]) {
+  if constexpr (G == 1) {
+    const float2 v = *(const float2*)p;
+    b[0] = v.x; c[0] = v.y;
+  } else if constexpr (G == 2) {
+    const float4 v = *(const float4*)p;
+    b[0] = v.x; b[1] = v.y; c[0] = v.z; c[1] = v.w;
+  } else {
+    static_assert(G == 4, "G is 1, 2 or 4");
+    const float4 v0 = *(const float4*)p;
+    const float4 v1 = *(const float4*)(p + 4);
+    b[0] = v0.x; b[1] = v0.y; b[2] = v0.z; b[3] = v0.w;
+    c[0] = v1.x; c[1] = v1.y; c[2] = v1.z; c[3] = v1.w;
   }
 }
 
-// Pointers are separate __restrict__ arguments: that is what lets the compiler
-// prove no store of the kernel clobbers B and C, and serve their wave-uniform
-// reads with scalar loads.
-template <typename IO, int G, int TC, bool ZOH, bool GATE>
-__global__ __launch_bounds__(64 * (16 / G)) void scan_fwd_kernel(
+// The recurrence over the tokens of one chunk for the G states of this thread.
+template <class S, Path PATH, bool FULL>
+__device__ __forceinline__ void run_chunk(Smem<S>& sm, float (&st)[S::G], const float (&Ap)[S::G],
+                                          const float (&Aa)[S::G], const float (&CA)[S::G],
+                                          int nt, int cl, int g) {
+  constexpr int G = S::G;
+  constexpr int kUnroll = FULL ? 8 : 1;
+  const int n_end = FULL ? S::TC : nt;
+  float* part = &sm.part[g][cl];
+#pragma unroll kUnroll
+  for (int t = 0; t < n_end; ++t) {
+    const float2 dd = sm.dd[t][cl];
+    float Bv[G], Cv[G];
+    read_bc<G>(&sm.bc[t][g][0], Bv, Cv);
+    float acc = 0.0f;
+#pragma unroll
+    for (int k = 0; k < G; ++k) {
+      const float a = exp2_hw(dd.x * Ap[k]);  // abar = exp(Delta A)
+      if constexpr (PATH == Path::kEuler) {
+        st[k] = fmaf(a, st[k], dd.y * Bv[k]);  // h = abar h + (Delta u) B
+        acc = fmaf(Cv[k], st[k], acc);
+      } else if constexpr (PATH == Path::kZohFast) {
+        const float ub = dd.y * Bv[k];          // u B
+        st[k] = fmaf(a, st[k] + ub, -ub);       // g = abar (g + uB) - uB,  g = A h
+        acc = fmaf(Cv[k] * CA[k], st[k], acc);  // C h = (C / A) g
+      } else {
+        const float kap = dd.x * Aa[k];         // Delta A
+        const float bbar = dd.x * Bv[k] * zoh_phi(kap, a);
+        st[k] = fmaf(a, st[k], bbar * dd.y);    // h = abar h + bbar u
+        acc = fmaf(Cv[k], st[k], acc);
+      }
+    }
+    part[t * S::CW] = acc;
+  }
+}
+
+// Pointers are separate __restrict__ arguments; y and last_state must not
+// overlap any input.
+template <typename IO, int G, int NG, bool ZOH, bool GATE>
+__global__ __launch_bounds__((Shape<G, NG>::THREADS)) void scan_fwd_kernel(
     const IO* __restrict__ u, const IO* __restrict__ dr, const float* __restrict__ Am,
     const IO* __restrict__ Bm, const IO* __restrict__ Cm, const float* __restrict__ Dm,
     const IO* __restrict__ zz, const float* __restrict__ bias_v, IO* __restrict__ y,
     float* __restrict__ last_state, const int64_t L, const int64_t dim, const int64_t N,
-    const int softplus) {
-  constexpr int P = 16 / G;
-  constexpr int RPW = TC / P;  // tokens each wave prepares and finishes per chunk
-  static_assert(TC % P == 0, "chunk must split evenly over the waves");
+    const int64_t ntiles, const int softplus) {
+  using S = Shape<G, NG>;
+  constexpr int CW = S::CW, TC = S::TC, RPT = S::RPT, NPAD = S::NPAD;
   using Raw = typename RawT<IO>::type;
 
-  __shared__ Smem<TC, P> sm;
+  __shared__ Smem<S> sm;
 
-  const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t c = (int64_t)blockIdx.x * 64 + lane;
-  const int64_t b = blockIdx.y;
+  // XCD-aware order: consecutive blocks go round-robin to the 8 XCDs, so give
+  // each XCD a contiguous run of tiles -- neighbouring tiles share 128-byte
+  // lines of u, raw delta, z and y, and then share that XCD's L2.
+  const int64_t nblk = (int64_t)gridDim.x;
+  const int64_t bid = blockIdx.x;
+  const int64_t logical = (nblk % 8 == 0) ? (bid % 8) * (nblk / 8) + bid / 8 : bid;
+  const int64_t b = logical / ntiles;
+  const int64_t tile = logical - b * ntiles;
+
+  const int tid = threadIdx.x;
+  const int cl = tid % CW;  // channel within the tile
+  const int g = tid / CW;   // state group
+  const int64_t c = tile * CW + cl;
   const bool cvalid = c < dim;
-  const int n0 = w * G;
-  // G divides N (the host guarantees it): a wave holds G real states or none
-  const int nvalid = (n0 < N) ? G : 0;
+  const int n0 = g * G;
+  const int ngroups = (int)((N + G - 1) / G);  // groups holding real states
 
-  // per-lane channel constants
+  // per-thread channel constants
   float Ap[G], Aa[G], CA[G];
   bool small_a = false;
 #pragma unroll
   for (int k = 0; k < G; ++k) {
-    float a = 0.0f;
-    if (k < nvalid && cvalid) a = Am[c * N + n0 + k];
+    const bool real = cvalid && (n0 + k) < N;
+    const float a = real ? Am[c * N + n0 + k] : 0.0f;
     Ap[k] = a * kLog2e;
     Aa[k] = a;
     CA[k] = (a != 0.0f) ? 1.0f / a : 0.0f;
-    if (k < nvalid && cvalid && !(fabsf(a) >= 0.5f)) small_a = true;
+    if (real && !(fabsf(a) >= 0.5f)) small_a = true;
   }
   const float bias = (cvalid && bias_v) ? bias_v[c] : 0.0f;
   const float dskip = (cvalid && Dm) ? Dm[c] : 0.0f;
@@ -153,74 +194,81 @@ __global__ __launch_bounds__(64 * (16 / G)) void scan_fwd_kernel(
   const int64_t nchunks = (L + TC - 1) / TC;
   const int64_t row0 = b * L;  // first token row of this batch entry
 
-  Raw ru[RPW], rd[RPW], rz[RPW];
+  Raw ru[RPT], rd[RPT], rz[RPT], rb[S::BCPT], rc[S::BCPT];
   auto prefetch = [&](int64_t t0) {
 #pragma unroll
-    for (int i = 0; i < RPW; ++i) {
-      const int64_t t = t0 + w + P * i;
+    for (int i = 0; i < RPT; ++i) {
+      const int64_t t = t0 + g + NG * i;
       const bool ok = cvalid && t < L;
       const int64_t idx = (row0 + t) * dim + c;
       ru[i] = ok ? load_raw(u + idx) : (Raw)0;
       rd[i] = ok ? load_raw(dr + idx) : (Raw)0;
       if constexpr (GATE) rz[i] = ok ? load_raw(zz + idx) : (Raw)0;
     }
+#pragma unroll
+    for (int i = 0; i < S::BCPT; ++i) {
+      const int e = tid + S::THREADS * i;
+      const int tt = e / NPAD, n = e % NPAD;
+      const bool ok = e < S::BCN && n < N && (t0 + tt) < L;
+      const int64_t idx = (row0 + t0 + tt) * N + n;
+      rb[i] = ok ? load_raw(Bm + idx) : (Raw)0;
+      rc[i] = ok ? load_raw(Cm + idx) : (Raw)0;
+    }
   };
 
+  float du[RPT], gz[RPT];
   if (nchunks > 0) prefetch(0);
   for (int64_t ck = 0; ck < nchunks; ++ck) {
     const int64_t t0 = ck * TC;
-    // ---- prepare this wave's tokens of the chunk
+    // ---- prep: this thread's tokens of the chunk, and its share of B and C
 #pragma unroll
-    for (int i = 0; i < RPW; ++i) {
-      const int r = w + P * i;
+    for (int i = 0; i < RPT; ++i) {
+      const int r = g + NG * i;
       const bool ok = cvalid && (t0 + r) < L;
-      const float x = raw_to_f32(ru[i]);
+      const float x = ok ? raw_to_f32(ru[i]) : 0.0f;
       const float v = raw_to_f32(rd[i]) + bias;
       float dlt = softplus ? softplus_f(v) : v;
       dlt = ok ? dlt : 0.0f;  // padding tokens leave the state unchanged
-      sm.dd[r][lane] = make_float2(dlt, ZOH ? (ok ? x : 0.0f) : dlt * x);
-      float g = 1.0f;
-      if constexpr (GATE) g = silu_f(raw_to_f32(rz[i]));
-      sm.ep[r][lane] = make_float2(dskip * x, g);
+      sm.dd[r][cl] = make_float2(dlt, ZOH ? x : dlt * x);
+      du[i] = dskip * x;
+      gz[i] = 1.0f;
+      if constexpr (GATE) gz[i] = silu_f(raw_to_f32(rz[i]));
+    }
+#pragma unroll
+    for (int i = 0; i < S::BCPT; ++i) {
+      const int e = tid + S::THREADS * i;
+      if (e < S::BCN) {
+        const int tt = e / NPAD, n = e % NPAD;
+        sm.bc[tt][n / G][n % G] = raw_to_f32(rb[i]);
+        sm.bc[tt][n / G][G + n % G] = raw_to_f32(rc[i]);
+      }
     }
     if (ck + 1 < nchunks) prefetch(t0 + TC);
     __syncthreads();
 
-    // ---- the recurrence for this wave's states over the chunk
-    if (nvalid > 0) {
-      const IO* __restrict__ Bp = Bm + (row0 + t0) * N + n0;
-      const IO* __restrict__ Cp = Cm + (row0 + t0) * N + n0;
-      const int nt = (int)(L - t0 < TC ? L - t0 : TC);
-      if constexpr (!ZOH) {
-        if (nt == TC)
-          run_chunk<IO, G, TC, P, Path::kEuler, true>(sm, st, Ap, Aa, CA, Bp, Cp, N, nt, w, lane);
-        else
-          run_chunk<IO, G, TC, P, Path::kEuler, false>(sm, st, Ap, Aa, CA, Bp, Cp, N, nt, w, lane);
-      } else if (!careful) {
-        if (nt == TC)
-          run_chunk<IO, G, TC, P, Path::kZohFast, true>(sm, st, Ap, Aa, CA, Bp, Cp, N, nt, w, lane);
-        else
-          run_chunk<IO, G, TC, P, Path::kZohFast, false>(sm, st, Ap, Aa, CA, Bp, Cp, N, nt, w, lane);
-      } else {
-        if (nt == TC)
-          run_chunk<IO, G, TC, P, Path::kZohCareful, true>(sm, st, Ap, Aa, CA, Bp, Cp, N, nt, w, lane);
-        else
-          run_chunk<IO, G, TC, P, Path::kZohCareful, false>(sm, st, Ap, Aa, CA, Bp, Cp, N, nt, w, lane);
-      }
+    // ---- the recurrence for this thread's states over the chunk
+    const int nt = (int)(L - t0 < TC ? L - t0 : TC);
+    if constexpr (!ZOH) {
+      if (nt == TC) run_chunk<S, Path::kEuler, true>(sm, st, Ap, Aa, CA, nt, cl, g);
+      else run_chunk<S, Path::kEuler, false>(sm, st, Ap, Aa, CA, nt, cl, g);
+    } else if (!careful) {
+      if (nt == TC) run_chunk<S, Path::kZohFast, true>(sm, st, Ap, Aa, CA, nt, cl, g);
+      else run_chunk<S, Path::kZohFast, false>(sm, st, Ap, Aa, CA, nt, cl, g);
+    } else {
+      if (nt == TC) run_chunk<S, Path::kZohCareful, true>(sm, st, Ap, Aa, CA, nt, cl, g);
+      else run_chunk<S, Path::kZohCareful, false>(sm, st, Ap, Aa, CA, nt, cl, g);
     }
     __syncthreads();
 
-    // ---- finish this wave's tokens: reduce the partial readouts, skip, gate, store
-    const int nwaves = (int)((N + G - 1) / G);
+    // ---- epilogue: reduce the partial readouts, skip, gate, store
 #pragma unroll
-    for (int i = 0; i < RPW; ++i) {
-      const int r = w + P * i;
+    for (int i = 0; i < RPT; ++i) {
+      const int r = g + NG * i;
       const int64_t t = t0 + r;
       if (cvalid && t < L) {
-        float s = sm.part[0][r][lane];
-        for (int j = 1; j < nwaves; ++j) s += sm.part[j][r][lane];
-        const float2 ep = sm.ep[r][lane];
-        store_io(y + (row0 + t) * dim + c, (s + ep.x) * ep.y);
+        float s = sm.part[0][r * CW + cl];
+        for (int j = 1; j < ngroups; ++j) s += sm.part[j][r * CW + cl];
+        store_io(y + (row0 + t) * dim + c, (s + du[i]) * gz[i]);
       }
     }
   }
@@ -229,7 +277,7 @@ __global__ __launch_bounds__(64 * (16 / G)) void scan_fwd_kernel(
   if (cvalid && last_state) {
 #pragma unroll
     for (int k = 0; k < G; ++k) {
-      if (k < nvalid) {
+      if (n0 + k < N) {
         const float h = (ZOH && !careful) ? st[k] * CA[k] : st[k];
         last_state[(b * dim + c) * N + n0 + k] = h;
       }
@@ -237,39 +285,41 @@ __global__ __launch_bounds__(64 * (16 / G)) void scan_fwd_kernel(
   }
 }
 
-template <typename IO, int G, int TC, bool ZOH, bool GATE>
+template <typename IO, int G, int NG, bool ZOH, bool GATE>
 hipError_t launch_one(const ScanParams& p, hipStream_t stream) {
-  const dim3 grid((unsigned)((p.dim + 63) / 64), (unsigned)p.batch);
-  const dim3 block(64 * (16 / G));
-  hipLaunchKernelGGL((scan_fwd_kernel<IO, G, TC, ZOH, GATE>), grid, block, 0, stream,
-                     (const IO*)p.u, (const IO*)p.delta, p.A, (const IO*)p.B, (const IO*)p.C,
-                     p.D, (const IO*)p.z, p.delta_bias, (IO*)p.y, p.last_state, p.L, p.dim, p.N,
-                     p.softplus);
+  using S = Shape<G, NG>;
+  const int64_t ntiles = (p.dim + S::CW - 1) / S::CW;
+  const int64_t nblk = ntiles * p.batch;
+  if (nblk > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((scan_fwd_kernel<IO, G, NG, ZOH, GATE>), dim3((unsigned)nblk),
+                     dim3(S::THREADS), 0, stream, (const IO*)p.u, (const IO*)p.delta, p.A,
+                     (const IO*)p.B, (const IO*)p.C, p.D, (const IO*)p.z, p.delta_bias, (IO*)p.y,
+                     p.last_state, p.L, p.dim, p.N, ntiles, p.softplus);
   return hipGetLastError();
 }
 
-template <typename IO, int G, int TC>
+template <typename IO, int G, int NG>
 hipError_t launch_modes(const ScanParams& p, bool zoh, bool gate, hipStream_t stream) {
-  if (zoh) return gate ? launch_one<IO, G, TC, true, true>(p, stream) : launch_one<IO, G, TC, true, false>(p, stream);
-  return gate ? launch_one<IO, G, TC, false, true>(p, stream) : launch_one<IO, G, TC, false, false>(p, stream);
+  if (zoh) return gate ? launch_one<IO, G, NG, true, true>(p, stream) : launch_one<IO, G, NG, true, false>(p, stream);
+  return gate ? launch_one<IO, G, NG, false, true>(p, stream) : launch_one<IO, G, NG, false, false>(p, stream);
 }
 
 template <typename IO>
-hipError_t launch_io(const ScanParams& p, int G, bool zoh, bool gate, hipStream_t stream) {
-  switch (G) {
-    case 1: return launch_modes<IO, 1, 16>(p, zoh, gate, stream);
-    case 2: return launch_modes<IO, 2, 32>(p, zoh, gate, stream);
-    case 4: return launch_modes<IO, 4, 32>(p, zoh, gate, stream);
-    default: return hipErrorInvalidValue;
-  }
+hipError_t launch_io(const ScanParams& p, int G, int NG, bool zoh, bool gate, hipStream_t stream) {
+  if (G == 4 && NG == 4) return launch_modes<IO, 4, 4>(p, zoh, gate, stream);
+  if (G == 2 && NG == 8) return launch_modes<IO, 2, 8>(p, zoh, gate, stream);
+  if (G == 1 && NG == 16) return launch_modes<IO, 1, 16>(p, zoh, gate, stream);
+  if (G == 4 && NG == 2) return launch_modes<IO, 4, 2>(p, zoh, gate, stream);
+  if (G == 4 && NG == 1) return launch_modes<IO, 4, 1>(p, zoh, gate, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-hipError_t launch_scan_fwd(const ScanParams& p, int io_dtype, int G, bool zoh, bool gate,
+hipError_t launch_scan_fwd(const ScanParams& p, int io_dtype, int G, int NG, bool zoh, bool gate,
                            hipStream_t stream) {
-  if (io_dtype == 1) return launch_io<bf16_bits>(p, G, zoh, gate, stream);
-  return launch_io<float>(p, G, zoh, gate, stream);
+  if (io_dtype == 1) return launch_io<bf16_bits>(p, G, NG, zoh, gate, stream);
+  return launch_io<float>(p, G, NG, zoh, gate, stream);
 }
 
 }  // namespace ssm66

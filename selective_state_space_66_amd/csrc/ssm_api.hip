@@ -35,21 +35,22 @@ int check_common(int64_t batch, int64_t len, int64_t dim, int64_t dstate, int io
   return SSM_OK;
 }
 
-// states per wave for the scan: the largest of 4, 2, 1 that divides dstate and
-// keeps the B and C rows aligned for vector scalar loads.  An override
-// (SSM66_SCAN_G = 1, 2 or 4) exists for tuning experiments.
-int pick_scan_g(int64_t dstate, const void* B, const void* C, size_t esize, int64_t blocks) {
-  int forced = 0;
-  if (const char* e = getenv("SSM66_SCAN_G")) forced = atoi(e);
-  const int cands[3] = {4, 2, 1};
-  for (int g : cands) {
-    if (dstate % g) continue;
-    if (!aligned(B, esize * g) || !aligned(C, esize * g)) continue;
-    if (forced && g != forced) continue;
-    (void)blocks;
-    return g;
+// Kernel shape for the scan: G states per thread, NG groups per channel
+// (G * NG >= dstate).  Up to 8 states one group shape covers them; for 9..16
+// the choice trades per-thread work against the number of waves: a wave is
+// 16 channels x 4 groups (64 lanes), so b * dim * NG / 64 waves share the
+// 1024 SIMDs.  SSM66_SCAN_G (1, 2 or 4) forces G for 9..16 states (tuning).
+void pick_scan_shape(int64_t dstate, int64_t rows, int* G, int* NG) {
+  if (dstate <= 4) { *G = 4; *NG = 1; return; }
+  if (dstate <= 8) { *G = 4; *NG = 2; return; }
+  int g = 0;
+  if (const char* e = getenv("SSM66_SCAN_G")) g = atoi(e);
+  if (g != 1 && g != 2 && g != 4) {
+    const int64_t waves4 = rows * 4 / 64;  // waves with G = 4
+    g = waves4 >= 2048 ? 4 : (waves4 >= 512 ? 2 : 1);
   }
-  return 1;
+  *G = g;
+  *NG = 16 / g;
 }
 
 }  // namespace
@@ -90,14 +91,15 @@ int ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B
   const void* f32_ptrs[4] = {A, D, delta_bias, last_state};
   for (const void* q : f32_ptrs)
     if (q && !aligned(q, 4)) return SSM_ERR_ALIGN;
-  if (batch > 65535 || (dim + 63) / 64 > 0x7fffffff) return SSM_ERR_UNSUPPORTED;
+  if (batch * ((dim + 15) / 16) > 0x7fffffff) return SSM_ERR_UNSUPPORTED;
 
   ssm66::ScanParams p;
   p.u = u; p.delta = delta; p.A = A; p.B = B; p.C = C; p.D = D; p.z = z;
   p.delta_bias = delta_bias; p.y = y; p.last_state = last_state;
   p.batch = batch; p.L = seqlen; p.dim = dim; p.N = dstate; p.softplus = softplus;
-  const int G = pick_scan_g(dstate, B, C, es, batch * ((dim + 63) / 64));
-  hipError_t e = ssm66::launch_scan_fwd(p, io_dtype, G, dt_mode == SSM_DT_ZOH, z != nullptr,
+  int G, NG;
+  pick_scan_shape(dstate, batch * dim, &G, &NG);
+  hipError_t e = ssm66::launch_scan_fwd(p, io_dtype, G, NG, dt_mode == SSM_DT_ZOH, z != nullptr,
                                         (hipStream_t)stream);
   return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }

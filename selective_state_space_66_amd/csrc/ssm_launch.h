@@ -36,9 +36,9 @@ struct StepParams {
   int softplus;
 };
 
-// G = states per wave (1, 2 or 4); G must divide N and B, C must be aligned to
-// G elements.
-hipError_t launch_scan_fwd(const ScanParams& p, int io_dtype, int G, bool zoh, bool gate,
+// G = states per thread, NG = state groups per channel, G * NG >= N.
+// Supported (G, NG): (4, 4), (2, 8), (1, 16), (4, 2), (4, 1).
+hipError_t launch_scan_fwd(const ScanParams& p, int io_dtype, int G, int NG, bool zoh, bool gate,
                            hipStream_t stream);
 hipError_t launch_step(const StepParams& p, int io_dtype, bool zoh, bool gate, hipStream_t stream);
 

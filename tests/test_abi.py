@@ -99,7 +99,7 @@ def test_scan_specific_checks(lib):
     c = _header_constants()
     assert _scan(lib, L=-1) == c["SSM_ERR_SHAPE"]
     assert _scan(lib, last=MISALIGNED) == c["SSM_ERR_ALIGN"]
-    assert _scan(lib, batch=70000) == c["SSM_ERR_UNSUPPORTED"]
+    assert _scan(lib, batch=1 << 20, dim=1 << 20, L=1) == c["SSM_ERR_UNSUPPORTED"]  # > 2^31 blocks
     assert _step(lib, state=None) == c["SSM_ERR_NULL"]
     assert _step(lib, state=MISALIGNED) == c["SSM_ERR_ALIGN"]
 
