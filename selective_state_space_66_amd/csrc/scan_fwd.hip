@@ -66,15 +66,20 @@ struct Shape {
   static constexpr int G = G_;                   // states per thread
   static constexpr int NG = NG_;                 // state groups per channel
   static constexpr int NPAD = G * NG;            // padded state count
-  static constexpr int CW = NG >= 4 ? 16 : 64 / NG;  // channels per block
+  static constexpr int CW = 16;                  // channels per block
   static constexpr int THREADS = CW * NG;
-  static constexpr int TC = NG == 8 ? 48 : 32;   // tokens per chunk
+  static constexpr int TC = NG == 8 ? 64 : 32;   // tokens per chunk
   static constexpr int RPT = TC / NG;            // tokens each thread prepares and finishes
   static constexpr int BCN = TC * NPAD;          // B (and C) elements per chunk
   static constexpr int BCPT = (BCN + THREADS - 1) / THREADS;
   static constexpr int PSTRIDE = TC * CW + 16;   // partial-readout row stride (bank offset)
   static_assert(TC % NG == 0, "tokens of a chunk must split evenly over the groups");
   static_assert(THREADS % 64 == 0, "whole waves");
+  // each thread stages EPT consecutive B (and C) elements of a chunk; with a
+  // dense layout (N == NPAD) they are whole groups inside one token
+  static constexpr int EPT = BCN / THREADS;
+  static_assert(BCN % THREADS == 0 && NPAD % EPT == 0 && EPT % G == 0,
+                "a thread stages whole groups of one token");
 };
 
 template <class S>
@@ -102,44 +107,73 @@ __device__ __forceinline__ void read_bc(const float* p, float (&b)[G], float (&c
   }
 }
 
+// One state update for G states at one token; returns the partial readout.
+template <int G, Path PATH>
+__device__ __forceinline__ float update(float (&st)[G], const float (&Ap)[G], const float (&Aa)[G],
+                                        const float (&CA)[G], float2 dd, const float (&Bv)[G],
+                                        const float (&Cv)[G]) {
+  float acc = 0.0f;
+#pragma unroll
+  for (int k = 0; k < G; ++k) {
+    const float a = exp2_hw(dd.x * Ap[k]);  // abar = exp(Delta A)
+    if constexpr (PATH == Path::kEuler) {
+      st[k] = fmaf(a, st[k], dd.y * Bv[k]);  // h = abar h + (Delta u) B
+      acc = fmaf(Cv[k], st[k], acc);
+    } else if constexpr (PATH == Path::kZohFast) {
+      const float ub = dd.y * Bv[k];          // u B
+      st[k] = fmaf(a, st[k] + ub, -ub);       // g = abar (g + uB) - uB,  g = A h
+      acc = fmaf(Cv[k] * CA[k], st[k], acc);  // C h = (C / A) g
+    } else {
+      const float kap = dd.x * Aa[k];         // Delta A
+      const float bbar = dd.x * Bv[k] * zoh_phi(kap, a);
+      st[k] = fmaf(a, st[k], bbar * dd.y);    // h = abar h + bbar u
+      acc = fmaf(Cv[k], st[k], acc);
+    }
+  }
+  return acc;
+}
+
 // The recurrence over the tokens of one chunk for the G states of this thread.
+// Full chunks go in batches of U tokens: all LDS reads of a batch are issued
+// before its arithmetic, so their latency overlaps, and its U partial readouts
+// are written after it.
 template <class S, Path PATH, bool FULL>
 __device__ __forceinline__ void run_chunk(Smem<S>& sm, float (&st)[S::G], const float (&Ap)[S::G],
                                           const float (&Aa)[S::G], const float (&CA)[S::G],
                                           int nt, int cl, int g) {
   constexpr int G = S::G;
-  constexpr int kUnroll = FULL ? 8 : 1;
-  const int n_end = FULL ? S::TC : nt;
   float* part = &sm.part[g][cl];
-#pragma unroll kUnroll
-  for (int t = 0; t < n_end; ++t) {
-    const float2 dd = sm.dd[t][cl];
-    float Bv[G], Cv[G];
-    read_bc<G>(&sm.bc[t][g][0], Bv, Cv);
-    float acc = 0.0f;
+  if constexpr (FULL) {
+    constexpr int U = G >= 4 ? 4 : 8;
+    static_assert(S::TC % U == 0, "whole batches");
+    for (int t0 = 0; t0 < S::TC; t0 += U) {
+      float2 dd[U];
+      float Bv[U][G], Cv[U][G];
 #pragma unroll
-    for (int k = 0; k < G; ++k) {
-      const float a = exp2_hw(dd.x * Ap[k]);  // abar = exp(Delta A)
-      if constexpr (PATH == Path::kEuler) {
-        st[k] = fmaf(a, st[k], dd.y * Bv[k]);  // h = abar h + (Delta u) B
-        acc = fmaf(Cv[k], st[k], acc);
-      } else if constexpr (PATH == Path::kZohFast) {
-        const float ub = dd.y * Bv[k];          // u B
-        st[k] = fmaf(a, st[k] + ub, -ub);       // g = abar (g + uB) - uB,  g = A h
-        acc = fmaf(Cv[k] * CA[k], st[k], acc);  // C h = (C / A) g
-      } else {
-        const float kap = dd.x * Aa[k];         // Delta A
-        const float bbar = dd.x * Bv[k] * zoh_phi(kap, a);
-        st[k] = fmaf(a, st[k], bbar * dd.y);    // h = abar h + bbar u
-        acc = fmaf(Cv[k], st[k], acc);
+      for (int j = 0; j < U; ++j) {
+        dd[j] = sm.dd[t0 + j][cl];
+        read_bc<G>(&sm.bc[t0 + j][g][0], Bv[j], Cv[j]);
       }
+      // keep the batch's reads ahead of its arithmetic (the scheduler would
+      // otherwise interleave them one token at a time and expose LDS latency)
+      __builtin_amdgcn_sched_barrier(0);
+      float acc[U];
+#pragma unroll
+      for (int j = 0; j < U; ++j) acc[j] = update<G, PATH>(st, Ap, Aa, CA, dd[j], Bv[j], Cv[j]);
+#pragma unroll
+      for (int j = 0; j < U; ++j) part[(t0 + j) * S::CW] = acc[j];
     }
-    part[t * S::CW] = acc;
+  } else {
+    for (int t = 0; t < nt; ++t) {
+      float Bv[G], Cv[G];
+      read_bc<G>(&sm.bc[t][g][0], Bv, Cv);
+      part[t * S::CW] = update<G, PATH>(st, Ap, Aa, CA, sm.dd[t][cl], Bv, Cv);
+    }
   }
 }
 
 // Pointers are separate __restrict__ arguments; y and last_state must not
-// overlap any input.
+// overlap any input.  The host guarantees NG * dim < 2^31 (32-bit lane offsets).
 template <typename IO, int G, int NG, bool ZOH, bool GATE>
 __global__ __launch_bounds__((Shape<G, NG>::THREADS)) void scan_fwd_kernel(
     const IO* __restrict__ u, const IO* __restrict__ dr, const float* __restrict__ Am,
@@ -148,7 +182,7 @@ __global__ __launch_bounds__((Shape<G, NG>::THREADS)) void scan_fwd_kernel(
     float* __restrict__ last_state, const int64_t L, const int64_t dim, const int64_t N,
     const int64_t ntiles, const int softplus) {
   using S = Shape<G, NG>;
-  constexpr int CW = S::CW, TC = S::TC, RPT = S::RPT, NPAD = S::NPAD;
+  constexpr int CW = S::CW, TC = S::TC, RPT = S::RPT, NPAD = S::NPAD, THREADS = S::THREADS;
   using Raw = typename RawT<IO>::type;
 
   __shared__ Smem<S> sm;
@@ -167,8 +201,14 @@ __global__ __launch_bounds__((Shape<G, NG>::THREADS)) void scan_fwd_kernel(
   const int g = tid / CW;   // state group
   const int64_t c = tile * CW + cl;
   const bool cvalid = c < dim;
+  const bool tile_full = (tile + 1) * CW <= dim;  // block-uniform
+  const int64_t cc = cvalid ? c : dim - 1;        // loads of padding lanes stay in bounds
+  // offset of (token g, channel cc) from a chunk's first token row; token
+  // g + NG i sits i * NG * dim elements further (a uniform step)
+  const uint32_t lane_off = (uint32_t)(g * dim + cc);
   const int n0 = g * G;
   const int ngroups = (int)((N + G - 1) / G);  // groups holding real states
+  const bool dense_bc = (N == NPAD);           // B, C rows are exactly NPAD wide
 
   // per-thread channel constants
   float Ap[G], Aa[G], CA[G];
@@ -194,53 +234,137 @@ __global__ __launch_bounds__((Shape<G, NG>::THREADS)) void scan_fwd_kernel(
   const int64_t nchunks = (L + TC - 1) / TC;
   const int64_t row0 = b * L;  // first token row of this batch entry
 
-  Raw ru[RPT], rd[RPT], rz[RPT], rb[S::BCPT], rc[S::BCPT];
+  // ---- raw prefetch of one chunk: u, raw delta, z for this thread's tokens,
+  // and its share of the chunk's B and C rows (as 32-bit words)
+  constexpr int BCW = S::EPT * (int)sizeof(IO) / 4;  // 32-bit words per thread
+  Raw ru[RPT], rd[RPT], rz[RPT];
+  uint32_t rb[BCW], rc[BCW];
   auto prefetch = [&](int64_t t0) {
+    const bool full = t0 + TC <= L;  // uniform
+    if (full) {
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-      const int64_t t = t0 + g + NG * i;
-      const bool ok = cvalid && t < L;
-      const int64_t idx = (row0 + t) * dim + c;
-      ru[i] = ok ? load_raw(u + idx) : (Raw)0;
-      rd[i] = ok ? load_raw(dr + idx) : (Raw)0;
-      if constexpr (GATE) rz[i] = ok ? load_raw(zz + idx) : (Raw)0;
-    }
+      for (int i = 0; i < RPT; ++i) {
+        const int64_t rowi = (row0 + t0 + NG * i) * dim;  // uniform
+        ru[i] = load_raw(u + rowi + lane_off);
+        rd[i] = load_raw(dr + rowi + lane_off);
+        if constexpr (GATE) rz[i] = load_raw(zz + rowi + lane_off);
+      }
+    } else {
 #pragma unroll
-    for (int i = 0; i < S::BCPT; ++i) {
-      const int e = tid + S::THREADS * i;
-      const int tt = e / NPAD, n = e % NPAD;
-      const bool ok = e < S::BCN && n < N && (t0 + tt) < L;
-      const int64_t idx = (row0 + t0 + tt) * N + n;
-      rb[i] = ok ? load_raw(Bm + idx) : (Raw)0;
-      rc[i] = ok ? load_raw(Cm + idx) : (Raw)0;
+      for (int i = 0; i < RPT; ++i) {
+        int64_t t = t0 + g + NG * i;
+        t = t < L ? t : L - 1;
+        const int64_t idx = (row0 + t) * dim + cc;
+        ru[i] = load_raw(u + idx);
+        rd[i] = load_raw(dr + idx);
+        if constexpr (GATE) rz[i] = load_raw(zz + idx);
+      }
     }
+    // B and C: the chunk's rows are TC * N contiguous elements; words past the
+    // last token (or past the tensor) are clamped to its last word
+    const int64_t e0 = (row0 + t0) * N;                        // first element
+    const int64_t ewords = ((row0 + (full ? t0 + TC : L)) * N * (int64_t)sizeof(IO) + 3) / 4;
+    const uint32_t* bw = (const uint32_t*)Bm;
+    const uint32_t* cw = (const uint32_t*)Cm;
+    const int64_t w0 = e0 * (int64_t)sizeof(IO) / 4;
+    if (dense_bc && full) {
+#pragma unroll
+      for (int i = 0; i < BCW; ++i) {
+        rb[i] = bw[w0 + tid * BCW + i];
+        rc[i] = cw[w0 + tid * BCW + i];
+      }
+    } else if (dense_bc) {
+#pragma unroll
+      for (int i = 0; i < BCW; ++i) {
+        int64_t w = w0 + tid * BCW + i;
+        w = w < ewords ? w : ewords - 1;
+        rb[i] = bw[w];
+        rc[i] = cw[w];
+      }
+    } else {
+      // general layout: element by element (dstate below the padded width)
+#pragma unroll
+      for (int i = 0; i < BCW; ++i) {
+        rb[i] = 0u;
+        rc[i] = 0u;
+      }
+#pragma unroll
+      for (int i = 0; i < S::EPT; ++i) {
+        const int e = tid * S::EPT + i;  // element of the padded chunk
+        const int tt = e / NPAD, n = e % NPAD;
+        if (e < S::BCN && n < N && t0 + tt < L) {
+          const int64_t idx = (row0 + t0 + tt) * N + n;
+          uint32_t vb, vc;
+          if constexpr (sizeof(IO) == 2) {
+            vb = ((const uint16_t*)Bm)[idx];
+            vc = ((const uint16_t*)Cm)[idx];
+          } else {
+            vb = __float_as_uint(((const float*)Bm)[idx]);
+            vc = __float_as_uint(((const float*)Cm)[idx]);
+          }
+          const int sh = (sizeof(IO) == 2) ? 16 * (i & 1) : 0;
+          rb[i / (4 / sizeof(IO))] |= vb << sh;
+          rc[i / (4 / sizeof(IO))] |= vc << sh;
+        }
+      }
+    }
+  };
+
+  // element j (0..NPAD*TC) of the staged B or C word array, as fp32
+  auto word_elem = [&](const uint32_t (&w)[BCW], int j) -> float {
+    if constexpr (sizeof(IO) == 2)
+      return __uint_as_float((j & 1) ? (w[j >> 1] & 0xffff0000u) : (w[j >> 1] << 16));
+    else
+      return __uint_as_float(w[j]);
   };
 
   float du[RPT], gz[RPT];
   if (nchunks > 0) prefetch(0);
   for (int64_t ck = 0; ck < nchunks; ++ck) {
     const int64_t t0 = ck * TC;
-    // ---- prep: this thread's tokens of the chunk, and its share of B and C
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) {
+    const bool full = t0 + TC <= L;  // block-uniform
+    // ---- prep: this thread's tokens of the chunk.  Padding lanes (channel
+    // past dim) compute on clamped copies; nothing of theirs is ever stored.
+    // In the last, partial chunk, tokens past L get Delta = 0 and x = 0 so the
+    // final state is left as it was after token L - 1.
+    auto prep_token = [&](int i, bool live) {
       const int r = g + NG * i;
-      const bool ok = cvalid && (t0 + r) < L;
-      const float x = ok ? raw_to_f32(ru[i]) : 0.0f;
+      float x = raw_to_f32(ru[i]);
       const float v = raw_to_f32(rd[i]) + bias;
-      float dlt = softplus ? softplus_f(v) : v;
-      dlt = ok ? dlt : 0.0f;  // padding tokens leave the state unchanged
+      const float sp = softplus_f(v);
+      float dlt = softplus ? sp : v;
+      if (!live) {
+        dlt = 0.0f;
+        x = 0.0f;
+      }
       sm.dd[r][cl] = make_float2(dlt, ZOH ? x : dlt * x);
       du[i] = dskip * x;
       gz[i] = 1.0f;
       if constexpr (GATE) gz[i] = silu_f(raw_to_f32(rz[i]));
-    }
+    };
+    if (full) {
 #pragma unroll
-    for (int i = 0; i < S::BCPT; ++i) {
-      const int e = tid + S::THREADS * i;
-      if (e < S::BCN) {
-        const int tt = e / NPAD, n = e % NPAD;
-        sm.bc[tt][n / G][n % G] = raw_to_f32(rb[i]);
-        sm.bc[tt][n / G][G + n % G] = raw_to_f32(rc[i]);
+      for (int i = 0; i < RPT; ++i) prep_token(i, true);
+    } else {
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) prep_token(i, (t0 + g + NG * i) < L);
+    }
+    // ---- stage B and C: this thread's EPT elements are states
+    // [ns, ns + EPT) of token tt of the chunk, i.e. whole groups; each group
+    // gets its G values of B and then of C.  Tokens past L are zeroed.
+    {
+      constexpr int EPT = S::EPT;
+      const int tt = (tid * EPT) / NPAD;
+      const int ns = (tid * EPT) % NPAD;
+      const bool live = full || (t0 + tt) < L;
+#pragma unroll
+      for (int q = 0; q < EPT / G; ++q) {
+        float* dst = &sm.bc[tt][ns / G + q][0];
+#pragma unroll
+        for (int k = 0; k < G; ++k) {
+          dst[k] = live ? word_elem(rb, q * G + k) : 0.0f;
+          dst[G + k] = live ? word_elem(rc, q * G + k) : 0.0f;
+        }
       }
     }
     if (ck + 1 < nchunks) prefetch(t0 + TC);
@@ -261,14 +385,28 @@ __global__ __launch_bounds__((Shape<G, NG>::THREADS)) void scan_fwd_kernel(
     __syncthreads();
 
     // ---- epilogue: reduce the partial readouts, skip, gate, store
+    if (full && tile_full) {
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-      const int r = g + NG * i;
-      const int64_t t = t0 + r;
-      if (cvalid && t < L) {
+      for (int i = 0; i < RPT; ++i) {
+        const int r = g + NG * i;
         float s = sm.part[0][r * CW + cl];
-        for (int j = 1; j < ngroups; ++j) s += sm.part[j][r * CW + cl];
-        store_io(y + (row0 + t) * dim + c, (s + du[i]) * gz[i]);
+#pragma unroll
+        for (int j = 1; j < NG; ++j)
+          if (j < ngroups) s += sm.part[j][r * CW + cl];
+        store_io(y + (row0 + t0 + NG * i) * dim + lane_off, (s + du[i]) * gz[i]);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) {
+        const int r = g + NG * i;
+        const int64_t t = t0 + r;
+        if (cvalid && t < L) {
+          float s = sm.part[0][r * CW + cl];
+#pragma unroll
+          for (int j = 1; j < NG; ++j)
+            if (j < ngroups) s += sm.part[j][r * CW + cl];
+          store_io(y + (row0 + t) * dim + c, (s + du[i]) * gz[i]);
+        }
       }
     }
   }
@@ -309,8 +447,8 @@ hipError_t launch_io(const ScanParams& p, int G, int NG, bool zoh, bool gate, hi
   if (G == 4 && NG == 4) return launch_modes<IO, 4, 4>(p, zoh, gate, stream);
   if (G == 2 && NG == 8) return launch_modes<IO, 2, 8>(p, zoh, gate, stream);
   if (G == 1 && NG == 16) return launch_modes<IO, 1, 16>(p, zoh, gate, stream);
-  if (G == 4 && NG == 2) return launch_modes<IO, 4, 2>(p, zoh, gate, stream);
-  if (G == 4 && NG == 1) return launch_modes<IO, 4, 1>(p, zoh, gate, stream);
+  if (G == 2 && NG == 4) return launch_modes<IO, 2, 4>(p, zoh, gate, stream);
+  if (G == 1 && NG == 4) return launch_modes<IO, 1, 4>(p, zoh, gate, stream);
   return hipErrorInvalidValue;
 }
 

@@ -41,8 +41,8 @@ int check_common(int64_t batch, int64_t len, int64_t dim, int64_t dstate, int io
 // 16 channels x 4 groups (64 lanes), so b * dim * NG / 64 waves share the
 // 1024 SIMDs.  SSM66_SCAN_G (1, 2 or 4) forces G for 9..16 states (tuning).
 void pick_scan_shape(int64_t dstate, int64_t rows, int* G, int* NG) {
-  if (dstate <= 4) { *G = 4; *NG = 1; return; }
-  if (dstate <= 8) { *G = 4; *NG = 2; return; }
+  if (dstate <= 4) { *G = 1; *NG = 4; return; }
+  if (dstate <= 8) { *G = 2; *NG = 4; return; }
   int g = 0;
   if (const char* e = getenv("SSM66_SCAN_G")) g = atoi(e);
   if (g != 1 && g != 2 && g != 4) {
@@ -91,7 +91,8 @@ int ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B
   const void* f32_ptrs[4] = {A, D, delta_bias, last_state};
   for (const void* q : f32_ptrs)
     if (q && !aligned(q, 4)) return SSM_ERR_ALIGN;
-  if (batch * ((dim + 15) / 16) > 0x7fffffff) return SSM_ERR_UNSUPPORTED;
+  // grid size, and 32-bit lane offsets within a chunk (16 groups x dim)
+  if (batch * ((dim + 15) / 16) > 0x7fffffff || 16 * dim > 0x7fffffff) return SSM_ERR_UNSUPPORTED;
 
   ssm66::ScanParams p;
   p.u = u; p.delta = delta; p.A = A; p.B = B; p.C = C; p.D = D; p.z = z;

@@ -37,7 +37,7 @@ struct StepParams {
 };
 
 // G = states per thread, NG = state groups per channel, G * NG >= N.
-// Supported (G, NG): (4, 4), (2, 8), (1, 16), (4, 2), (4, 1).
+// Supported (G, NG): (4, 4), (2, 8), (1, 16) for up to 16 states, (2, 4) and (1, 4).
 hipError_t launch_scan_fwd(const ScanParams& p, int io_dtype, int G, int NG, bool zoh, bool gate,
                            hipStream_t stream);
 hipError_t launch_step(const StepParams& p, int io_dtype, bool zoh, bool gate, hipStream_t stream);
