@@ -15,6 +15,12 @@ the decode step (ssm_step) on its workload (batch 256, D 5120, N 16,
 fp64 CPU oracle timed on the host.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu]
+
+For profilers (rocprofv3) a reduced mode runs a few launches of one kernel on
+one input set and prints no JSON:
+    python bench.py --only scan [--dt-mode zoh|euler] [--launches 3]
+    python bench.py --only decode [--launches 3]
+    python bench.py --only copy     # a plain 256 MiB device copy, for counter calibration
 """
 import argparse
 import hashlib
@@ -171,6 +177,31 @@ def cpu_baseline(cfg, inp, threads):
     return time.perf_counter() - t0
 
 
+def profile_only(what, launches, dt_mode):
+    """A few launches of one kernel for an external profiler (no timing, no JSON)."""
+    import torch
+    import selective_state_space_66_amd as ssm
+    import workloads as W
+    dev = torch.device("cuda:0")
+    if what == "copy":
+        x = torch.ones(128 * 1024 * 1024, dtype=torch.bfloat16, device=dev)
+        y = torch.empty_like(x)
+        for _ in range(launches):
+            y.copy_(x)
+    elif what == "scan":
+        cfg = W.SCAN_CONFIGS["mamba130m"]
+        s = upload_scan(W.scan_inputs(cfg), dev)
+        y = torch.empty_like(s["u"])
+        last = torch.empty(cfg.batch, cfg.dim, cfg.N, device=dev)
+        for _ in range(launches):
+            ssm.scan_fwd(s["u"], s["delta"], s["A"], s["B"], s["C"], D=s["D"], z=s["z"],
+                         delta_bias=s["delta_bias"], dt_mode=dt_mode, y=y, last_state=last)
+    elif what == "decode":
+        time_decode(W.STEP_CONFIGS["decode"], launches, dev, npool=2)
+    torch.cuda.synchronize()
+    log(f"[bench] profile-only {what}: {launches} launches done")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -178,6 +209,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--decode-steps", type=int, default=1000)
+    ap.add_argument("--only", choices=["scan", "decode", "copy"], default=None,
+                    help="profiling mode: a few launches of one kernel, no JSON")
+    ap.add_argument("--launches", type=int, default=3)
+    ap.add_argument("--dt-mode", choices=["zoh", "euler"], default="zoh")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -189,6 +224,9 @@ def main():
     import selective_state_space_66_amd as ssm
     import workloads as W
     ssm.load_library()  # fail loudly if the HIP library is missing
+    if args.only:
+        profile_only(args.only, args.launches, args.dt_mode)
+        return
     dev = torch.device("cuda:0")
 
     cfg = W.SCAN_CONFIGS["mamba130m"]
