@@ -144,24 +144,37 @@ __device__ __forceinline__ void run_chunk(Smem<S>& sm, float (&st)[S::G], const 
   constexpr int G = S::G;
   float* part = &sm.part[g][cl];
   if constexpr (FULL) {
-    constexpr int U = G >= 4 ? 4 : 8;
+    // batches of U tokens, software-pipelined: the LDS reads of batch j + 1 are
+    // issued before the arithmetic of batch j (LDS returns in order, so the
+    // waits for batch j do not cover batch j + 1's reads)
+    constexpr int U = G >= 4 ? 2 : 4;
+    constexpr int NB = S::TC / U;
     static_assert(S::TC % U == 0, "whole batches");
-    for (int t0 = 0; t0 < S::TC; t0 += U) {
-      float2 dd[U];
-      float Bv[U][G], Cv[U][G];
+    float2 dd[2][U];
+    float Bv[2][U][G], Cv[2][U][G];
 #pragma unroll
-      for (int j = 0; j < U; ++j) {
-        dd[j] = sm.dd[t0 + j][cl];
-        read_bc<G>(&sm.bc[t0 + j][g][0], Bv[j], Cv[j]);
+    for (int j = 0; j < U; ++j) {
+      dd[0][j] = sm.dd[j][cl];
+      read_bc<G>(&sm.bc[j][g][0], Bv[0][j], Cv[0][j]);
+    }
+#pragma unroll
+    for (int bt = 0; bt < NB; ++bt) {
+      const int cur = bt & 1, nxt = cur ^ 1;
+      if (bt + 1 < NB) {
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+          const int t = (bt + 1) * U + j;
+          dd[nxt][j] = sm.dd[t][cl];
+          read_bc<G>(&sm.bc[t][g][0], Bv[nxt][j], Cv[nxt][j]);
+        }
       }
-      // keep the batch's reads ahead of its arithmetic (the scheduler would
-      // otherwise interleave them one token at a time and expose LDS latency)
       __builtin_amdgcn_sched_barrier(0);
       float acc[U];
 #pragma unroll
-      for (int j = 0; j < U; ++j) acc[j] = update<G, PATH>(st, Ap, Aa, CA, dd[j], Bv[j], Cv[j]);
+      for (int j = 0; j < U; ++j)
+        acc[j] = update<G, PATH>(st, Ap, Aa, CA, dd[cur][j], Bv[cur][j], Cv[cur][j]);
 #pragma unroll
-      for (int j = 0; j < U; ++j) part[(t0 + j) * S::CW] = acc[j];
+      for (int j = 0; j < U; ++j) part[(bt * U + j) * S::CW] = acc[j];
     }
   } else {
     for (int t = 0; t < nt; ++t) {
@@ -182,7 +195,7 @@ __global__ __launch_bounds__((Shape<G, NG>::THREADS)) void scan_fwd_kernel(
     float* __restrict__ last_state, const int64_t L, const int64_t dim, const int64_t N,
     const int64_t ntiles, const int softplus) {
   using S = Shape<G, NG>;
-  constexpr int CW = S::CW, TC = S::TC, RPT = S::RPT, NPAD = S::NPAD, THREADS = S::THREADS;
+  constexpr int CW = S::CW, TC = S::TC, RPT = S::RPT, NPAD = S::NPAD;
   using Raw = typename RawT<IO>::type;
 
   __shared__ Smem<S> sm;

@@ -35,18 +35,20 @@ int check_common(int64_t batch, int64_t len, int64_t dim, int64_t dstate, int io
   return SSM_OK;
 }
 
-// Kernel shape for the scan: G states per thread, NG groups per channel
+// Scan kernel shape: G states per thread, NG state groups per channel
 // (G * NG >= dstate).  Up to 8 states one group shape covers them; for 9..16
 // the choice trades per-thread work against the number of waves: a wave is
-// 16 channels x 4 groups (64 lanes), so b * dim * NG / 64 waves share the
-// 1024 SIMDs.  SSM66_SCAN_G (1, 2 or 4) forces G for 9..16 states (tuning).
-void pick_scan_shape(int64_t dstate, int64_t rows, int* G, int* NG) {
+// 16 channels x 4 groups (64 lanes), so b * dim * NG / 64 waves share the 1024
+// SIMDs.  SSM66_SCAN_KERNEL = "lds1", "lds2" or "lds4" forces G for 9..16
+// states (tuning, and tests that cover every instance).
+void pick_scan_shape(int64_t batch, int64_t dim, int64_t dstate, int* G, int* NG) {
   if (dstate <= 4) { *G = 1; *NG = 4; return; }
   if (dstate <= 8) { *G = 2; *NG = 4; return; }
   int g = 0;
-  if (const char* e = getenv("SSM66_SCAN_G")) g = atoi(e);
+  if (const char* e = getenv("SSM66_SCAN_KERNEL"))
+    if (e[0] == 'l' && e[1] == 'd' && e[2] == 's') g = atoi(e + 3);
   if (g != 1 && g != 2 && g != 4) {
-    const int64_t waves4 = rows * 4 / 64;  // waves with G = 4
+    const int64_t waves4 = batch * dim * 4 / 64;  // waves with G = 4
     g = waves4 >= 2048 ? 4 : (waves4 >= 512 ? 2 : 1);
   }
   *G = g;
@@ -99,9 +101,9 @@ int ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B
   p.delta_bias = delta_bias; p.y = y; p.last_state = last_state;
   p.batch = batch; p.L = seqlen; p.dim = dim; p.N = dstate; p.softplus = softplus;
   int G, NG;
-  pick_scan_shape(dstate, batch * dim, &G, &NG);
-  hipError_t e = ssm66::launch_scan_fwd(p, io_dtype, G, NG, dt_mode == SSM_DT_ZOH, z != nullptr,
-                                        (hipStream_t)stream);
+  pick_scan_shape(batch, dim, dstate, &G, &NG);
+  const hipError_t e = ssm66::launch_scan_fwd(p, io_dtype, G, NG, dt_mode == SSM_DT_ZOH,
+                                              z != nullptr, (hipStream_t)stream);
   return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 

@@ -30,15 +30,16 @@ __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2
 __device__ __forceinline__ float log2_hw(float x) { return __builtin_amdgcn_logf(x); }
 __device__ __forceinline__ float rcp_hw(float x) { return __builtin_amdgcn_rcpf(x); }
 
-// softplus(v) = log(1 + e^v).  w = 1 + e^v is rounded; (w - 1) - e^v is that
-// rounding error, exactly, and removing it keeps small step sizes accurate in
-// absolute terms.  Above v = 20 the result is v to within 2e-9 relative.
+// softplus(v) = log(1 + e^v) = max(v, 0) + log(1 + e^-|v|): the exponential
+// is at most 1, so nothing overflows and no threshold is needed.  w = 1 + e is
+// rounded; r = (w - 1) - e is that rounding error, exactly (Sterbenz), and
+// log(1 + e) = log(w) - r / w ~ log(w) - r keeps small step sizes accurate in
+// relative terms, not only to 6e-8 absolute.
 __device__ __forceinline__ float softplus_f(float v) {
-  const float e = exp2_hw(v * kLog2e);
+  const float e = exp2_hw(-fabsf(v) * kLog2e);
   const float w = 1.0f + e;
   const float r = (w - 1.0f) - e;
-  const float s = fmaf(log2_hw(w), kLn2, -r);
-  return v > 20.0f ? v : s;
+  return fmaf(log2_hw(w), kLn2, fmaxf(v, 0.0f) - r);
 }
 
 // SiLU(z) = z * sigmoid(z) = z / (1 + e^-z); z -> -inf gives -0, not NaN.
