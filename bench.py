@@ -35,6 +35,16 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+# ALU roofline of the scan.  Per state update the method does 2 multiplies and
+# 2 FMAs (6 flops: Delta A, (Delta u) B, the state FMA, the readout FMA) and one
+# exponential.  MI355X issues 256 CU x 4 SIMD x 16 lanes x 2.4 GHz = 39.3e12
+# non-packed fp32 lane instructions per second (packed fp32 is not used), and
+# v_exp_f32 takes two issue slots (half rate): 4 + 2 = 6 slots for 6 flops, so
+# the mix peaks at 39.3 TFLOP/s, i.e. 6.55e12 state updates per second.
+VALU_LANE_OPS = 256 * 4 * 16 * 2.4e9
+FLOPS_PER_UPDATE = 6
+SLOTS_PER_UPDATE = 6
+ALU_PEAK_TFLOPS = VALU_LANE_OPS / SLOTS_PER_UPDATE * FLOPS_PER_UPDATE / 1e12
 METRIC = "selective-scan fwd achieved HBM GB/s (% of peak) and B·L·D elems/s; decode tok/s"
 
 
@@ -267,6 +277,8 @@ def main():
 
     gbs = nbytes / (wall_ms * 1e-3) / 1e9
     achieved = nbytes / (kern_ms * 1e-3) / 1e9
+    updates = elems * cfg.N
+    tflops = FLOPS_PER_UPDATE * updates / (kern_ms * 1e-3) / 1e12
     traffic = measured_traffic("scan_fwd_mamba130m_zoh")
     out = {
         "metric": METRIC,
@@ -289,13 +301,19 @@ def main():
         "elems_per_s": float(f"{elems / (wall_ms * 1e-3):.4g}"),
         "updates_per_s": float(f"{elems * cfg.N / (wall_ms * 1e-3):.4g}"),
         "algorithmic_bytes_per_step": nbytes,
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+        "roofline": {"bound": "alu", "achieved": round(tflops, 3), "peak": round(ALU_PEAK_TFLOPS, 2),
+                     "unit": "TFLOP/s", "frac": round(tflops / ALU_PEAK_TFLOPS, 4),
                      "traffic": traffic, "kernel": "scan_fwd_kernel (ZOH, bf16, gate)",
-                     "kernel_ms": round(kern_ms, 5)},
+                     "kernel_ms": round(kern_ms, 5),
+                     "per_launch": {"updates": updates, "flops": FLOPS_PER_UPDATE * updates,
+                                    "algorithmic_bytes": nbytes},
+                     "hbm": {"achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": round(achieved / HBM_PEAK_GBS, 4)}},
         "cpu_baseline": cpu,
         "euler": {"ms_per_step": round(e_wall, 5), "GB/s": round(nbytes / (e_wall * 1e-3) / 1e9, 2),
-                  "kernel_ms": round(e_kern, 5)},
+                  "kernel_ms": round(e_kern, 5),
+                  "alu_frac": round(FLOPS_PER_UPDATE * updates / (e_kern * 1e-3) / 1e12
+                                    / ALU_PEAK_TFLOPS, 4)},
         "decode": {"workload": "ssm_step: batch 256, D 5120, N 16, bf16 io, fp32 state, gate, ZOH",
                    "steps": args.decode_steps,
                    "tok_per_s": round(dcfg.batch * args.decode_steps / d_wall_s, 1),
