@@ -15,7 +15,11 @@ outputs stay float64.
 
 Parity status: every function below is pinned by ``tests/test_oracle_pins.py``
 against the pages' worked numbers, closed forms (LTI convolution, first-order
-IIR filter), a brute-force mixing-matrix evaluation and invariants.
+IIR filter), a brute-force mixing-matrix evaluation and invariants.  The
+initial state, the sequence lengths and the document resets of ``scan_fwd`` are
+pinned against independent routes to the same result: scanning the truncated
+or split sequence, and the first page's remark that one very large step resets
+the state.
 """
 import ctypes
 import os
@@ -54,6 +58,10 @@ def _load():
     lib.oracle_scan_fwd.restype = None
     lib.oracle_scan_fwd.argtypes = [ctypes.c_void_p] * 9 + [ctypes.c_int, ctypes.c_int,
                                                             ctypes.c_void_p, ctypes.c_void_p] + \
+        [ctypes.c_int64] * 4 + [ctypes.c_int]
+    lib.oracle_scan_fwd_ex.restype = None
+    lib.oracle_scan_fwd_ex.argtypes = [ctypes.c_void_p] * 11 + [ctypes.c_int, ctypes.c_int,
+                                                               ctypes.c_void_p, ctypes.c_void_p] + \
         [ctypes.c_int64] * 4 + [ctypes.c_int]
     lib.oracle_step.restype = None
     lib.oracle_step.argtypes = [ctypes.c_void_p] * 9 + [ctypes.c_int, ctypes.c_int,
@@ -100,11 +108,13 @@ def combine(first, then):
 
 
 def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True,
-             dt_mode="zoh", h0=None, nthreads=None):
+             dt_mode="zoh", h0=None, seq_lens=None, reset=None, nthreads=None):
     """Sequential fp64 selective scan.
 
     u, delta, z: (batch, L, dim); B, C: (batch, L, N); A: (dim, N); D, delta_bias: (dim,);
-    h0: optional (batch, dim, N) initial state (zero when omitted).
+    h0: optional (batch, dim, N) initial state (zero when omitted);
+    seq_lens: optional (batch,) real lengths (tokens past them are padding: y = 0,
+    state kept); reset: optional (batch, L) flags, state zeroed before a flagged token.
     Returns (y (batch, L, dim), last_state (batch, dim, N)), both float64.
     """
     u = _f64(u)
@@ -124,13 +134,26 @@ def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True,
     assert z is None or z.shape == u.shape
     assert delta_bias is None or delta_bias.shape == (dim,)
     assert h0 is None or h0.shape == (batch, dim, N)
+    if seq_lens is not None:
+        seq_lens = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int64))
+        assert seq_lens.shape == (batch,)
+    if reset is not None:
+        reset = np.ascontiguousarray(np.asarray(reset) != 0, dtype=np.uint8)
+        assert reset.shape == (batch, L)
     y = np.empty((batch, L, dim), dtype=np.float64)
     last = np.empty((batch, dim, N), dtype=np.float64)
     if nthreads is None:
         nthreads = os.cpu_count() or 1
-    _load().oracle_scan_fwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+    lib = _load()
+    if seq_lens is None and reset is None:
+        lib.oracle_scan_fwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
                             _ptr(delta_bias), _ptr(h0), int(bool(softplus)), _MODES[dt_mode],
                             _ptr(y), _ptr(last), batch, L, dim, N, int(nthreads))
+    else:
+        lib.oracle_scan_fwd_ex(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                               _ptr(delta_bias), _ptr(h0), _ptr(seq_lens), _ptr(reset),
+                               int(bool(softplus)), _MODES[dt_mode], _ptr(y), _ptr(last),
+                               batch, L, dim, N, int(nthreads))
     return y, last
 
 

@@ -30,11 +30,26 @@
  *   - the gate multiplies (C.h + D x);
  *   - the state is read after it is written for the same token.
  *
+ * Sequences that do not start from zero or do not fill the batch (the
+ * extended scan, oracle_scan_fwd_ex):
+ *   - h0 is the state before the first token (the prefill of "Decoding with a
+ *     constant-size cache" keeps only the final state; a later chunk of the
+ *     same prompt starts from it);
+ *   - seq_lens[b] real tokens, then padding: padded tokens produce y = 0 and
+ *     leave the state alone, so last_state is the state after the last real
+ *     token ("Where Mamba implementations go wrong": padding is not masked out
+ *     of the state by itself; here it is kept out explicitly);
+ *   - reset[b, t] != 0 marks a document start: the state is zeroed before
+ *     token t is written ("What each parameter does": at a document break the
+ *     state should forget everything; a very large Delta does it inside the
+ *     layer, the flag does it outright).
+ *
  * Layouts (row-major, dense):
  *   u, delta, z, y : (batch, L, dim)      B, C : (batch, L, N)
  *   A : (dim, N)     D, delta_bias : (dim)
  *   state / h0 / last_state : (batch, dim, N)
- * Optional pointers (D, z, delta_bias, h0, last_state) may be NULL.
+ *   seq_lens : (batch)                    reset : (batch, L)
+ * Optional pointers (D, z, delta_bias, h0, seq_lens, reset, last_state) may be NULL.
  */
 #include <math.h>
 #include <pthread.h>
@@ -92,6 +107,8 @@ void oracle_combine(double a1, double b1, double a2, double b2,
 
 typedef struct {
   const double *u, *delta, *A, *B, *C, *D, *z, *bias, *h0;
+  const int64_t* seq_lens;
+  const uint8_t* reset;
   double *y, *last_state;
   int64_t batch, L, dim, N;
   int softplus, dt_mode;
@@ -112,8 +129,17 @@ static void scan_row(const scan_job* j, int64_t b, int64_t c) {
     hp[n] = j->h0 ? j->h0[(b * dim + c) * N + n] : 0.0;
   const double bias = j->bias ? j->bias[c] : 0.0;
   const double dskip = j->D ? j->D[c] : 0.0;
+  int64_t len = j->seq_lens ? j->seq_lens[b] : L; /* real tokens of this sequence */
+  if (len < 0) len = 0;
+  if (len > L) len = L;
   for (int64_t t = 0; t < L; ++t) {
     const int64_t xi = (b * L + t) * dim + c;
+    if (t >= len) { /* padding: no output, state kept */
+      j->y[xi] = 0.0;
+      continue;
+    }
+    if (j->reset && j->reset[b * L + t]) /* a document starts at t */
+      for (int64_t n = 0; n < N; ++n) hp[n] = 0.0;
     const double x = j->u[xi];
     const double dt = step_size(j->delta[xi], bias, j->softplus);
     const double* Bt = j->B + (b * L + t) * N;
@@ -145,11 +171,12 @@ static void* scan_worker(void* arg) {
 
 /* The full scan.  Rows (b, c) are independent and are split over `nthreads`
  * host threads; each row is computed exactly as written above. */
-void oracle_scan_fwd(const double* u, const double* delta, const double* A,
-                     const double* B, const double* C, const double* D,
-                     const double* z, const double* delta_bias, const double* h0,
-                     int softplus, int dt_mode, double* y, double* last_state,
-                     int64_t batch, int64_t L, int64_t dim, int64_t N, int nthreads) {
+void oracle_scan_fwd_ex(const double* u, const double* delta, const double* A,
+                        const double* B, const double* C, const double* D,
+                        const double* z, const double* delta_bias, const double* h0,
+                        const int64_t* seq_lens, const uint8_t* reset,
+                        int softplus, int dt_mode, double* y, double* last_state,
+                        int64_t batch, int64_t L, int64_t dim, int64_t N, int nthreads) {
   const int64_t rows = batch * dim;
   if (rows <= 0) return;
   if (nthreads < 1) nthreads = 1;
@@ -160,6 +187,7 @@ void oracle_scan_fwd(const double* u, const double* delta, const double* A,
     scan_job* j = &jobs[i];
     j->u = u; j->delta = delta; j->A = A; j->B = B; j->C = C; j->D = D; j->z = z;
     j->bias = delta_bias; j->h0 = h0; j->y = y; j->last_state = last_state;
+    j->seq_lens = seq_lens; j->reset = reset;
     j->batch = batch; j->L = L; j->dim = dim; j->N = N;
     j->softplus = softplus; j->dt_mode = dt_mode;
     j->row_begin = rows * i / nthreads;
@@ -170,6 +198,16 @@ void oracle_scan_fwd(const double* u, const double* delta, const double* A,
   for (int i = 1; i < nthreads; ++i) pthread_join(tids[i], NULL);
   free(jobs);
   free(tids);
+}
+
+/* Every sequence full length, no document breaks. */
+void oracle_scan_fwd(const double* u, const double* delta, const double* A,
+                     const double* B, const double* C, const double* D,
+                     const double* z, const double* delta_bias, const double* h0,
+                     int softplus, int dt_mode, double* y, double* last_state,
+                     int64_t batch, int64_t L, int64_t dim, int64_t N, int nthreads) {
+  oracle_scan_fwd_ex(u, delta, A, B, C, D, z, delta_bias, h0, NULL, NULL, softplus, dt_mode, y,
+                     last_state, batch, L, dim, N, nthreads);
 }
 
 /* One decode step: the same body as the scan for a single token, with the

@@ -32,6 +32,14 @@ MUTATIONS = {
     "decay_sign": ("  *abar = exp(kappa);", "  *abar = exp(-kappa);"),
     "sigmoid_sign": ("if (v >= 0.0) return 1.0 / (1.0 + exp(-v));", "if (v >= 0.0) return 1.0 / (1.0 + exp(v));"),
     "step_drops_state": ("        h[n] = abar * h[n] + bbar * x;", "        h[n] = bbar * x;"),
+    "padding_off_by_one": ("    if (t >= len) { /* padding: no output, state kept */",
+                           "    if (t > len) { /* padding: no output, state kept */"),
+    "padding_updates_state": ("      j->y[xi] = 0.0;\n      continue;", "      j->y[xi] = 0.0;"),
+    "reset_ignored": ("    if (j->reset && j->reset[b * L + t]) /* a document starts at t */",
+                      "    if (0) /* a document starts at t */"),
+    "reset_one_token_late": ("    if (j->reset && j->reset[b * L + t]) /* a document starts at t */",
+                             "    if (j->reset && t > 0 && j->reset[b * L + t - 1])"),
+    "h0_ignored": ("    hp[n] = j->h0 ? j->h0[(b * dim + c) * N + n] : 0.0;", "    hp[n] = 0.0;"),
 }
 
 

@@ -410,3 +410,96 @@ def test_empty_sequence():
     p = _rand_problem(L=0)
     y, last = oracle.scan_fwd(**p)
     assert y.shape == (2, 0, 5) and np.all(last == 0.0)
+
+
+# ------------------------------------------- initial state, lengths, resets
+
+
+def _one(p, b):
+    """Batch entry b of a problem dict, as a batch of one."""
+    return {k: (v[b:b + 1] if (k in ("u", "delta", "z", "B", "C") and v is not None) else v)
+            for k, v in p.items()}
+
+
+@pytest.mark.parametrize("mode", ["zoh", "euler"])
+def test_seq_lens_equal_truncation(mode):
+    """A sequence of length l followed by padding gives, on its l real tokens,
+    exactly the scan of those tokens alone; padded positions output 0 and the
+    final state is the state after token l - 1."""
+    p = _rand_problem(batch=4, L=30)
+    h0 = RNG.normal(size=(4, 5, 16))
+    lens = [30, 17, 1, 0]
+    y, last = oracle.scan_fwd(**p, dt_mode=mode, h0=h0, seq_lens=lens)
+    for b, l in enumerate(lens):
+        yb, lb = oracle.scan_fwd(**_cut(_one(p, b), 0, l), dt_mode=mode, h0=h0[b:b + 1])
+        np.testing.assert_array_equal(y[b, :l], yb[0])
+        assert np.all(y[b, l:] == 0.0)
+        np.testing.assert_array_equal(last[b], lb[0])
+    # lengths outside [0, L] are clamped
+    y2, last2 = oracle.scan_fwd(**p, dt_mode=mode, h0=h0, seq_lens=[99, 17, 1, -5])
+    np.testing.assert_array_equal(y2, y)
+    np.testing.assert_array_equal(last2, last)
+
+
+@pytest.mark.parametrize("mode", ["zoh", "euler"])
+def test_reset_equals_separate_documents(mode):
+    """Two documents packed into one sequence with a reset at the break give
+    exactly the two documents scanned separately, the second from zero."""
+    p = _rand_problem(batch=2, L=40)
+    h0 = RNG.normal(size=(2, 5, 16))
+    reset = np.zeros((2, 40), dtype=bool)
+    reset[0, 13] = True
+    reset[1, 29] = True
+    y, last = oracle.scan_fwd(**p, dt_mode=mode, h0=h0, reset=reset)
+    for b, cut in ((0, 13), (1, 29)):
+        one = _one(p, b)
+        ya, _ = oracle.scan_fwd(**_cut(one, 0, cut), dt_mode=mode, h0=h0[b:b + 1])
+        yb, lb = oracle.scan_fwd(**_cut(one, cut, 40), dt_mode=mode)
+        np.testing.assert_array_equal(y[b, :cut], ya[0])
+        np.testing.assert_array_equal(y[b, cut:], yb[0])
+        np.testing.assert_array_equal(last[b], lb[0])
+
+
+def test_reset_at_start_discards_h0():
+    p = _rand_problem(batch=2, L=12)
+    reset = np.zeros((2, 12), dtype=bool)
+    reset[:, 0] = True
+    y, last = oracle.scan_fwd(**p, h0=RNG.normal(size=(2, 5, 16)), reset=reset)
+    y0, last0 = oracle.scan_fwd(**p)
+    np.testing.assert_array_equal(y, y0)
+    np.testing.assert_array_equal(last, last0)
+
+
+def test_left_padding_with_reset():
+    """Left padding (garbage before the real tokens) with a reset at the first
+    real token gives the unpadded scan on the real tokens."""
+    p = _rand_problem(batch=1, L=25)
+    pad = 9
+    reset = np.zeros((1, 25), dtype=bool)
+    reset[0, pad] = True
+    y, last = oracle.scan_fwd(**p, reset=reset)
+    yr, lr = oracle.scan_fwd(**_cut(p, pad, 25))
+    np.testing.assert_array_equal(y[:, pad:], yr)
+    np.testing.assert_array_equal(last, lr)
+
+
+def test_large_step_resets_like_the_flag():
+    """"One token with a large Delta" resets the state ("What each parameter
+    does" on the first page): under ZOH a step of 1e4 makes abar = exp(Delta A)
+    underflow to 0, so the scan equals the scan with a reset flag at that token
+    (same Delta), and nothing before it reaches the outputs after it."""
+    p = _rand_problem(batch=1, L=30)
+    p["delta_bias"] = np.zeros(5)
+    p["delta"] = np.abs(p["delta"]) * 0.1
+    p["delta"][0, 11, :] = 1e4
+    y, last = oracle.scan_fwd(**p, softplus=False)
+    reset = np.zeros((1, 30), dtype=bool)
+    reset[0, 11] = True
+    yf, lf = oracle.scan_fwd(**p, softplus=False, reset=reset)
+    np.testing.assert_array_equal(y, yf)
+    np.testing.assert_array_equal(last, lf)
+    q = dict(p)
+    q["u"] = p["u"].copy()
+    q["u"][0, :11] += RNG.normal(size=(11, 5))
+    y2, _ = oracle.scan_fwd(**q, softplus=False)
+    np.testing.assert_array_equal(y2[:, 11:], y[:, 11:])
