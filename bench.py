@@ -109,21 +109,23 @@ def upload_scan(inp, dev):
                 z=to_dev(inp["z"], io, dev), delta_bias=to_dev(inp["delta_bias"], "f32", dev))
 
 
-def time_scan(sets, steps, warmup, dt_mode):
+def time_scan(sets, steps, warmup, dt_mode, extras=None):
     """Run warmup + timed steps rotating over the input sets.  Returns
-    (wall ms per step, mean per-launch kernel ms from HIP events)."""
+    (wall ms per step, mean per-launch kernel ms from HIP events).  `extras`
+    (h0, seq_lens, reset) selects the extended scan."""
     import torch
     import selective_state_space_66_amd as ssm
     outs = [(torch.empty_like(s["u"]), torch.empty(s["u"].shape[0], s["u"].shape[2], s["A"].shape[1],
                                                     dtype=torch.float32, device=s["u"].device))
             for s in sets]
+    ex = extras or {}
 
     def launch(i):
         s = sets[i % len(sets)]
         y, last = outs[i % len(sets)]
         ssm.scan_fwd(s["u"], s["delta"], s["A"], s["B"], s["C"], D=s["D"], z=s["z"],
                      delta_bias=s["delta_bias"], softplus=True, dt_mode=dt_mode, y=y,
-                     last_state=last)
+                     last_state=last, **ex)
 
     for i in range(warmup):
         launch(i)
@@ -257,6 +259,21 @@ def main():
     e_wall, e_kern = time_scan(sets, args.steps, args.warmup, "euler")
     log(f"[bench] euler: wall {e_wall:.4f} ms/step, kernel {e_kern:.4f} ms")
 
+    # the extended scan: chunked prefill from an initial state, ragged lengths
+    # and packed documents (a reset every 512 tokens)
+    rng = np.random.default_rng(11)
+    lens = [cfg.L, cfg.L - 48, cfg.L // 2 + 1, cfg.L, 1000, cfg.L, 1537, cfg.L]
+    reset = np.zeros((cfg.batch, cfg.L), dtype=np.uint8)
+    reset[:, 512::512] = 1
+    extras = {"h0": torch.from_numpy(rng.normal(size=(cfg.batch, cfg.dim, cfg.N)).astype(np.float32)).to(dev),
+              "seq_lens": torch.tensor(lens, dtype=torch.int32, device=dev),
+              "reset": torch.from_numpy(reset).to(dev)}
+    log("[bench] timing the extended scan (h0, lengths, resets)")
+    x_wall, x_kern = time_scan(sets, args.steps, args.warmup, "zoh", extras)
+    x_bytes = nbytes + 4 * cfg.batch * cfg.dim * cfg.N + cfg.batch * cfg.L + 4 * cfg.batch
+    x_updates = sum(lens) * cfg.dim * cfg.N
+    log(f"[bench] extended: wall {x_wall:.4f} ms/step, kernel {x_kern:.4f} ms")
+
     dcfg = W.STEP_CONFIGS["decode"]
     log("[bench] timing decode steps")
     d_wall_s, d_kern_ms = time_decode(dcfg, args.decode_steps, dev)
@@ -314,6 +331,12 @@ def main():
                   "kernel_ms": round(e_kern, 5),
                   "alu_frac": round(FLOPS_PER_UPDATE * updates / (e_kern * 1e-3) / 1e12
                                     / ALU_PEAK_TFLOPS, 4)},
+        "scan_ex": {"workload": "ssm_scan_fwd_ex on the same layer, ZOH: h0 given, lengths "
+                                f"{lens}, a document start every 512 tokens",
+                    "kernel_ms": round(x_kern, 5),
+                    "GB/s": round(x_bytes / (x_kern * 1e-3) / 1e9, 2),
+                    "alu_frac": round(FLOPS_PER_UPDATE * x_updates / (x_kern * 1e-3) / 1e12
+                                      / ALU_PEAK_TFLOPS, 4)},
         "decode": {"workload": "ssm_step: batch 256, D 5120, N 16, bf16 io, fp32 state, gate, ZOH",
                    "steps": args.decode_steps,
                    "tok_per_s": round(dcfg.batch * args.decode_steps / d_wall_s, 1),

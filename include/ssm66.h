@@ -1,7 +1,7 @@
 /*
  * ssm66.h -- C ABI of the MI355X (gfx950) selective-scan library.
  *
- * Two operations, both defined on "Mamba and selective state spaces"
+ * Three entry points, all defined on "Mamba and selective state spaces"
  * (zerotofrontier.app/ssm/mamba):
  *
  *   ssm_scan_fwd : the selective state-space layer (S6) over whole sequences --
@@ -13,10 +13,18 @@
  *                  rule bbar = Delta B) and the SiLU(z) gate of "The Mamba
  *                  block".  Prefill keeps only the final state ("Decoding with
  *                  a constant-size cache"), returned in last_state.
+ *   ssm_scan_fwd_ex : the same scan for sequences that do not start from zero
+ *                  or do not fill the batch: an initial state (a later chunk
+ *                  of a prefill starts from the state the earlier chunk
+ *                  returned), per-sequence lengths with padding after them
+ *                  (padding must be kept out of the state: "Where Mamba
+ *                  implementations go wrong"), and document starts where the
+ *                  state is forgotten ("What each parameter does": packed
+ *                  documents should not see each other).
  *   ssm_step     : one token of that layer against a state cache, updated in
  *                  place ("Decoding with a constant-size cache").
  *
- * Conventions shared by both calls
+ * Conventions shared by all calls
  *   - Every pointer is caller-owned DEVICE memory (HBM).  The library keeps no
  *     pointer after the call returns and allocates nothing.
  *   - Tensors are dense and row-major:
@@ -35,7 +43,7 @@
  *     (limit Delta B at A = 0), or SSM_DT_EULER, bbar = Delta B.
  *   - The gate multiplies the whole S6 output: y = (C.h + D u) * z * sigmoid(z).
  *   - 1 <= dstate <= 16; batch, seqlen, dim >= 0.  Zero batch or dim is a no-op;
- *     seqlen == 0 writes zeros to last_state.
+ *     seqlen == 0 writes the initial state (zero, or h0) to last_state.
  *   - Pointers must be aligned to their element size.  y must not overlap an
  *     input; in ssm_step, y must not overlap state.
  *   - Values are not checked: negative Delta, A >= 0, NaN and Inf are computed
@@ -55,7 +63,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 1
+#define SSM_ABI_VERSION 2
 
 /* status codes */
 #define SSM_OK 0
@@ -88,6 +96,29 @@ int ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B
                  const float* D, const void* z, const float* delta_bias, int softplus,
                  int dt_mode, void* y, float* last_state, int64_t batch, int64_t seqlen,
                  int64_t dim, int64_t dstate, int io_dtype, void* stream);
+
+/*
+ * ssm_scan_fwd with three optional extras (any of them may be NULL; with all
+ * three NULL it is ssm_scan_fwd):
+ *   h0        (batch, dim, dstate) float32: the state before token 0
+ *             (instead of zero).  last_state may be the same buffer as h0
+ *             (the state is then advanced in place); no other overlap.
+ *   seq_lens  (batch) int32: sequence b has seq_lens[b] real tokens followed
+ *             by padding (values are clamped to [0, seqlen]).  Padded tokens
+ *             do not touch the state, whatever their inputs hold (NaN
+ *             included), and their y is 0; last_state is the state after the
+ *             last real token.
+ *   reset     (batch, seqlen) uint8: nonzero at t means a new document starts
+ *             at token t: the state is set to zero before token t is written.
+ *             Left padding is a reset at the first real token.
+ * seq_lens must be 4-byte aligned; reset has no alignment requirement.
+ * Returns SSM_OK or an error status.
+ */
+int ssm_scan_fwd_ex(const void* u, const void* delta, const float* A, const void* B,
+                    const void* C, const float* D, const void* z, const float* delta_bias,
+                    int softplus, int dt_mode, const float* h0, const int32_t* seq_lens,
+                    const uint8_t* reset, void* y, float* last_state, int64_t batch,
+                    int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype, void* stream);
 
 /*
  * One decode step against the state cache `state` (batch, dim, dstate),

@@ -7,7 +7,8 @@ library's HIP kernels.  There is no CPU or PyTorch fallback: if the library is
 missing, every call raises.
 
     y, last_state = scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
-                             softplus=True, dt_mode="zoh")
+                             softplus=True, dt_mode="zoh",
+                             h0=None, seq_lens=None, reset=None)
     y = step(state, u, delta, A, B, C, D=None, z=None, delta_bias=None,
              softplus=True, dt_mode="zoh")     # state updated in place
 """
@@ -41,6 +42,8 @@ def load_library():
     vp, i64, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     lib.ssm_scan_fwd.restype = ci
     lib.ssm_scan_fwd.argtypes = [vp] * 8 + [ci, ci, vp, vp, i64, i64, i64, i64, ci, vp]
+    lib.ssm_scan_fwd_ex.restype = ci
+    lib.ssm_scan_fwd_ex.argtypes = [vp] * 8 + [ci, ci] + [vp] * 5 + [i64, i64, i64, i64, ci, vp]
     lib.ssm_step.restype = ci
     lib.ssm_step.argtypes = [vp] * 9 + [ci, ci, vp, i64, i64, i64, ci, vp]
     lib.ssm_status_string.restype = ctypes.c_char_p
@@ -91,11 +94,14 @@ def _stream(device):
 
 
 def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True, dt_mode="zoh",
-             y=None, last_state=None, return_last_state=True):
+             y=None, last_state=None, return_last_state=True, h0=None, seq_lens=None, reset=None):
     """Selective scan over whole sequences on the GPU.
 
     u, delta, z: (batch, L, dim); B, C: (batch, L, N) -- all float32 or all bfloat16.
     A: (dim, N) float32; D, delta_bias: (dim,) float32.
+    h0: optional (batch, dim, N) float32 initial state (last_state may be h0: in place);
+    seq_lens: optional (batch,) int32 real lengths (padding after them: y = 0, state kept);
+    reset: optional (batch, L) bool or uint8, state zeroed before each flagged token.
     Returns (y, last_state): y like u; last_state (batch, dim, N) float32 (None if not requested).
     """
     import torch
@@ -123,11 +129,24 @@ def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True, 
     if last_state is None and return_last_state:
         last_state = torch.empty((batch, dim, N), dtype=torch.float32, device=dev)
     _check(last_state, "last_state", (batch, dim, N), torch.float32, dev)
-    st = lib.ssm_scan_fwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
-                          _ptr(delta_bias), int(bool(softplus)), _MODES[dt_mode], _ptr(y),
-                          _ptr(last_state), batch, L, dim, N, _io_code(u), _stream(dev))
+    if h0 is None and seq_lens is None and reset is None:
+        st = lib.ssm_scan_fwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                              _ptr(delta_bias), int(bool(softplus)), _MODES[dt_mode], _ptr(y),
+                              _ptr(last_state), batch, L, dim, N, _io_code(u), _stream(dev))
+        if st != 0:
+            raise SsmError(st, "ssm_scan_fwd")
+        return y, last_state
+    _check(h0, "h0", (batch, dim, N), torch.float32, dev)
+    _check(seq_lens, "seq_lens", (batch,), torch.int32, dev)
+    if reset is not None and reset.dtype == torch.bool:
+        reset = reset.view(torch.uint8)
+    _check(reset, "reset", (batch, L), torch.uint8, dev)
+    st = lib.ssm_scan_fwd_ex(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                             _ptr(delta_bias), int(bool(softplus)), _MODES[dt_mode], _ptr(h0),
+                             _ptr(seq_lens), _ptr(reset), _ptr(y), _ptr(last_state), batch, L,
+                             dim, N, _io_code(u), _stream(dev))
     if st != 0:
-        raise SsmError(st, "ssm_scan_fwd")
+        raise SsmError(st, "ssm_scan_fwd_ex")
     return y, last_state
 
 

@@ -30,12 +30,21 @@
 // The state carries from chunk to chunk in registers; after the last chunk it
 // is written to last_state.
 //
+// Sequences that do not start from zero or do not fill the batch: h0 (if
+// given) is the state before the first token; seq_lens[b] (if given) real
+// tokens are followed by padding, which gets Delta = 0 and x = 0 (the state is
+// kept) and y = 0; reset[b, t] != 0 (if given) zeroes the state before token
+// t.  Resets are block-uniform (a block owns one batch entry), so a chunk
+// holding none runs the ordinary batched recurrence.
+//
 // ZOH fast path: the thread keeps g = A h, for which
 //   g_t = abar (g_{t-1} + u B) - u B,
 // the exact ZOH update multiplied through by A: no division, no (abar - 1)
 // cancellation; the readout uses C / A.  A wave whose channels hold any
 // |A| < 1/2 (or A = 0) runs the careful form instead, h-form with
 // bbar = Delta B phi(Delta A), phi(k) = (e^k - 1)/k, accurate for every A.
+#include <type_traits>
+
 #include "ssm_device.h"
 #include "ssm_launch.h"
 
@@ -59,6 +68,8 @@ __device__ __forceinline__ typename RawT<IO>::type load_raw(const IO* __restrict
 }
 
 enum class Path { kEuler, kZohFast, kZohCareful };
+template <Path P>
+using PathTag = std::integral_constant<Path, P>;
 
 // Static shape of one kernel instance.
 template <int G_, int NG_>
@@ -87,6 +98,7 @@ struct Smem {
   float2 dd[S::TC][S::CW];              // (Delta, x): x = Delta*u (Euler) or u (ZOH)
   float bc[S::TC][S::NG][2 * S::G];     // per token and group: G values of B, then of C
   float part[S::NG][S::PSTRIDE];        // partial readouts, [group][token * CW + channel]
+  int rst[S::TC];                       // document starts within the chunk (reset flags)
 };
 
 // Read 2G consecutive floats (the group's B and C) from LDS.
@@ -137,7 +149,7 @@ __device__ __forceinline__ float update(float (&st)[G], const float (&Ap)[G], co
 // Full chunks go in batches of U tokens: all LDS reads of a batch are issued
 // before its arithmetic, so their latency overlaps, and its U partial readouts
 // are written after it.
-template <class S, Path PATH, bool FULL>
+template <class S, Path PATH, bool FULL, bool RST = false>
 __device__ __forceinline__ void run_chunk(Smem<S>& sm, float (&st)[S::G], const float (&Ap)[S::G],
                                           const float (&Aa)[S::G], const float (&CA)[S::G],
                                           int nt, int cl, int g) {
@@ -178,6 +190,12 @@ __device__ __forceinline__ void run_chunk(Smem<S>& sm, float (&st)[S::G], const 
     }
   } else {
     for (int t = 0; t < nt; ++t) {
+      if constexpr (RST) {
+        if (sm.rst[t]) {  // a document starts here: forget the state
+#pragma unroll
+          for (int k = 0; k < G; ++k) st[k] = 0.0f;
+        }
+      }
       float Bv[G], Cv[G];
       read_bc<G>(&sm.bc[t][g][0], Bv, Cv);
       part[t * S::CW] = update<G, PATH>(st, Ap, Aa, CA, sm.dd[t][cl], Bv, Cv);
@@ -185,14 +203,17 @@ __device__ __forceinline__ void run_chunk(Smem<S>& sm, float (&st)[S::G], const 
   }
 }
 
-// Pointers are separate __restrict__ arguments; y and last_state must not
-// overlap any input.  The host guarantees NG * dim < 2^31 (32-bit lane offsets).
+// Pointers are separate __restrict__ arguments; y must not overlap any input,
+// and last_state none but h0 (each thread reads its h0 entries before it
+// writes the same entries of last_state).  The host guarantees
+// NG * dim < 2^31 (32-bit lane offsets).
 template <typename IO, int G, int NG, bool ZOH, bool GATE>
 __global__ __launch_bounds__((Shape<G, NG>::THREADS)) void scan_fwd_kernel(
     const IO* __restrict__ u, const IO* __restrict__ dr, const float* __restrict__ Am,
     const IO* __restrict__ Bm, const IO* __restrict__ Cm, const float* __restrict__ Dm,
-    const IO* __restrict__ zz, const float* __restrict__ bias_v, IO* __restrict__ y,
-    float* __restrict__ last_state, const int64_t L, const int64_t dim, const int64_t N,
+    const IO* __restrict__ zz, const float* __restrict__ bias_v, const float* h0,
+    const int32_t* __restrict__ seq_lens, const uint8_t* __restrict__ reset,
+    IO* __restrict__ y, float* last_state, const int64_t L, const int64_t dim, const int64_t N,
     const int64_t ntiles, const int softplus) {
   using S = Shape<G, NG>;
   constexpr int CW = S::CW, TC = S::TC, RPT = S::RPT, NPAD = S::NPAD;
@@ -242,10 +263,19 @@ __global__ __launch_bounds__((Shape<G, NG>::THREADS)) void scan_fwd_kernel(
 
   float st[G];
 #pragma unroll
-  for (int k = 0; k < G; ++k) st[k] = 0.0f;
+  for (int k = 0; k < G; ++k) {
+    float h = 0.0f;
+    if (h0 && cvalid && (n0 + k) < N) h = h0[(b * dim + c) * N + n0 + k];
+    st[k] = (ZOH && !careful) ? Aa[k] * h : h;  // the fast ZOH path keeps g = A h
+  }
 
   const int64_t nchunks = (L + TC - 1) / TC;
   const int64_t row0 = b * L;  // first token row of this batch entry
+  int64_t Leff = L;            // real tokens of this sequence; the rest is padding
+  if (seq_lens) {
+    const int64_t sl = seq_lens[b];
+    Leff = sl < 0 ? 0 : (sl < L ? sl : L);
+  }
 
   // ---- raw prefetch of one chunk: u, raw delta, z for this thread's tokens,
   // and its share of the chunk's B and C rows (as 32-bit words)
@@ -335,11 +365,12 @@ __global__ __launch_bounds__((Shape<G, NG>::THREADS)) void scan_fwd_kernel(
   if (nchunks > 0) prefetch(0);
   for (int64_t ck = 0; ck < nchunks; ++ck) {
     const int64_t t0 = ck * TC;
-    const bool full = t0 + TC <= L;  // block-uniform
+    const bool full = t0 + TC <= Leff;  // every token of the chunk is real (block-uniform)
     // ---- prep: this thread's tokens of the chunk.  Padding lanes (channel
     // past dim) compute on clamped copies; nothing of theirs is ever stored.
-    // In the last, partial chunk, tokens past L get Delta = 0 and x = 0 so the
-    // final state is left as it was after token L - 1.
+    // Tokens past the sequence (padding, or past L in the last chunk) get
+    // Delta = 0 and x = 0, so the state is left as it was after the last real
+    // token whatever the padded inputs hold.
     auto prep_token = [&](int i, bool live) {
       const int r = g + NG * i;
       float x = raw_to_f32(ru[i]);
@@ -360,7 +391,7 @@ __global__ __launch_bounds__((Shape<G, NG>::THREADS)) void scan_fwd_kernel(
       for (int i = 0; i < RPT; ++i) prep_token(i, true);
     } else {
 #pragma unroll
-      for (int i = 0; i < RPT; ++i) prep_token(i, (t0 + g + NG * i) < L);
+      for (int i = 0; i < RPT; ++i) prep_token(i, (t0 + g + NG * i) < Leff);
     }
     // ---- stage B and C: this thread's EPT elements are states
     // [ns, ns + EPT) of token tt of the chunk, i.e. whole groups; each group
@@ -369,7 +400,7 @@ __global__ __launch_bounds__((Shape<G, NG>::THREADS)) void scan_fwd_kernel(
       constexpr int EPT = S::EPT;
       const int tt = (tid * EPT) / NPAD;
       const int ns = (tid * EPT) % NPAD;
-      const bool live = full || (t0 + tt) < L;
+      const bool live = full || (t0 + tt) < Leff;
 #pragma unroll
       for (int q = 0; q < EPT / G; ++q) {
         float* dst = &sm.bc[tt][ns / G + q][0];
@@ -380,20 +411,39 @@ __global__ __launch_bounds__((Shape<G, NG>::THREADS)) void scan_fwd_kernel(
         }
       }
     }
-    if (ck + 1 < nchunks) prefetch(t0 + TC);
-    __syncthreads();
-
-    // ---- the recurrence for this thread's states over the chunk
-    const int nt = (int)(L - t0 < TC ? L - t0 : TC);
-    if constexpr (!ZOH) {
-      if (nt == TC) run_chunk<S, Path::kEuler, true>(sm, st, Ap, Aa, CA, nt, cl, g);
-      else run_chunk<S, Path::kEuler, false>(sm, st, Ap, Aa, CA, nt, cl, g);
-    } else if (!careful) {
-      if (nt == TC) run_chunk<S, Path::kZohFast, true>(sm, st, Ap, Aa, CA, nt, cl, g);
-      else run_chunk<S, Path::kZohFast, false>(sm, st, Ap, Aa, CA, nt, cl, g);
+    // document starts of this chunk: one flag per token, block-uniform
+    bool chunk_resets = false;
+    if (reset) {
+      int mine = 0;
+      if (cl == 0) {
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+          const int r = g + NG * i;
+          const int f = (t0 + r < Leff) ? (int)reset[row0 + t0 + r] : 0;
+          sm.rst[r] = f;
+          mine |= f;
+        }
+      }
+      if (ck + 1 < nchunks) prefetch(t0 + TC);
+      chunk_resets = __syncthreads_or(mine) != 0;
     } else {
-      if (nt == TC) run_chunk<S, Path::kZohCareful, true>(sm, st, Ap, Aa, CA, nt, cl, g);
-      else run_chunk<S, Path::kZohCareful, false>(sm, st, Ap, Aa, CA, nt, cl, g);
+      if (ck + 1 < nchunks) prefetch(t0 + TC);
+      __syncthreads();
+    }
+
+    // ---- the recurrence for this thread's states over the chunk's real tokens
+    const int64_t nreal = Leff - t0;
+    const int nt = (int)(nreal < 0 ? 0 : (nreal < TC ? nreal : TC));
+    auto run = [&](auto path_tag) {
+      constexpr Path PATH = decltype(path_tag)::value;
+      if (nt == TC && !chunk_resets) run_chunk<S, PATH, true>(sm, st, Ap, Aa, CA, nt, cl, g);
+      else if (chunk_resets) run_chunk<S, PATH, false, true>(sm, st, Ap, Aa, CA, nt, cl, g);
+      else run_chunk<S, PATH, false>(sm, st, Ap, Aa, CA, nt, cl, g);
+    };
+    if (nt > 0) {
+      if constexpr (!ZOH) run(PathTag<Path::kEuler>());
+      else if (!careful) run(PathTag<Path::kZohFast>());
+      else run(PathTag<Path::kZohCareful>());
     }
     __syncthreads();
 
@@ -414,11 +464,15 @@ __global__ __launch_bounds__((Shape<G, NG>::THREADS)) void scan_fwd_kernel(
         const int r = g + NG * i;
         const int64_t t = t0 + r;
         if (cvalid && t < L) {
-          float s = sm.part[0][r * CW + cl];
+          float out = 0.0f;  // padding outputs 0
+          if (t < Leff) {
+            float s = sm.part[0][r * CW + cl];
 #pragma unroll
-          for (int j = 1; j < NG; ++j)
-            if (j < ngroups) s += sm.part[j][r * CW + cl];
-          store_io(y + (row0 + t) * dim + c, (s + du[i]) * gz[i]);
+            for (int j = 1; j < NG; ++j)
+              if (j < ngroups) s += sm.part[j][r * CW + cl];
+            out = (s + du[i]) * gz[i];
+          }
+          store_io(y + (row0 + t) * dim + c, out);
         }
       }
     }
@@ -444,8 +498,9 @@ hipError_t launch_one(const ScanParams& p, hipStream_t stream) {
   if (nblk > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL((scan_fwd_kernel<IO, G, NG, ZOH, GATE>), dim3((unsigned)nblk),
                      dim3(S::THREADS), 0, stream, (const IO*)p.u, (const IO*)p.delta, p.A,
-                     (const IO*)p.B, (const IO*)p.C, p.D, (const IO*)p.z, p.delta_bias, (IO*)p.y,
-                     p.last_state, p.L, p.dim, p.N, ntiles, p.softplus);
+                     (const IO*)p.B, (const IO*)p.C, p.D, (const IO*)p.z, p.delta_bias, p.h0,
+                     p.seq_lens, p.reset, (IO*)p.y, p.last_state, p.L, p.dim, p.N, ntiles,
+                     p.softplus);
   return hipGetLastError();
 }
 

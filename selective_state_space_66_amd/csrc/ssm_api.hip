@@ -75,10 +75,11 @@ const char* ssm_status_string(int status) {
   }
 }
 
-int ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
-                 const float* D, const void* z, const float* delta_bias, int softplus,
-                 int dt_mode, void* y, float* last_state, int64_t batch, int64_t seqlen,
-                 int64_t dim, int64_t dstate, int io_dtype, void* stream) {
+int ssm_scan_fwd_ex(const void* u, const void* delta, const float* A, const void* B,
+                    const void* C, const float* D, const void* z, const float* delta_bias,
+                    int softplus, int dt_mode, const float* h0, const int32_t* seq_lens,
+                    const uint8_t* reset, void* y, float* last_state, int64_t batch,
+                    int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype, void* stream) {
   int st = check_common(batch, seqlen, dim, dstate, io_dtype, softplus, dt_mode);
   if (st != SSM_OK) return st;
   const bool has_tokens = batch > 0 && seqlen > 0 && dim > 0;
@@ -90,7 +91,7 @@ int ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B
   const void* io_ptrs[6] = {u, delta, B, C, z, y};
   for (const void* q : io_ptrs)
     if (q && !aligned(q, es)) return SSM_ERR_ALIGN;
-  const void* f32_ptrs[4] = {A, D, delta_bias, last_state};
+  const void* f32_ptrs[6] = {A, D, delta_bias, last_state, h0, seq_lens};
   for (const void* q : f32_ptrs)
     if (q && !aligned(q, 4)) return SSM_ERR_ALIGN;
   // grid size, and 32-bit lane offsets within a chunk (16 groups x dim)
@@ -98,13 +99,22 @@ int ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B
 
   ssm66::ScanParams p;
   p.u = u; p.delta = delta; p.A = A; p.B = B; p.C = C; p.D = D; p.z = z;
-  p.delta_bias = delta_bias; p.y = y; p.last_state = last_state;
+  p.delta_bias = delta_bias; p.h0 = h0; p.seq_lens = seq_lens; p.reset = reset;
+  p.y = y; p.last_state = last_state;
   p.batch = batch; p.L = seqlen; p.dim = dim; p.N = dstate; p.softplus = softplus;
   int G, NG;
   pick_scan_shape(batch, dim, dstate, &G, &NG);
   const hipError_t e = ssm66::launch_scan_fwd(p, io_dtype, G, NG, dt_mode == SSM_DT_ZOH,
                                               z != nullptr, (hipStream_t)stream);
   return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
+int ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                 const float* D, const void* z, const float* delta_bias, int softplus,
+                 int dt_mode, void* y, float* last_state, int64_t batch, int64_t seqlen,
+                 int64_t dim, int64_t dstate, int io_dtype, void* stream) {
+  return ssm_scan_fwd_ex(u, delta, A, B, C, D, z, delta_bias, softplus, dt_mode, nullptr, nullptr,
+                         nullptr, y, last_state, batch, seqlen, dim, dstate, io_dtype, stream);
 }
 
 int ssm_step(float* state, const void* u, const void* delta, const float* A, const void* B,

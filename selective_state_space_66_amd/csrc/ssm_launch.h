@@ -15,8 +15,11 @@ struct ScanParams {
   const float* D;           // nullable
   const void* z;            // nullable
   const float* delta_bias;  // nullable
+  const float* h0;          // nullable: initial state (batch, dim, N)
+  const int32_t* seq_lens;  // nullable: real tokens per sequence (batch)
+  const uint8_t* reset;     // nullable: document starts (batch, L)
   void* y;
-  float* last_state;  // nullable
+  float* last_state;  // nullable; may be the same buffer as h0
   int64_t batch, L, dim, N;
   int softplus;
 };

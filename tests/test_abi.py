@@ -34,7 +34,8 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared_functions()
-    assert set(names) == {"ssm_scan_fwd", "ssm_step", "ssm_status_string", "ssm_abi_version"}
+    assert set(names) == {"ssm_scan_fwd", "ssm_scan_fwd_ex", "ssm_step", "ssm_status_string",
+                          "ssm_abi_version"}
     raw = ctypes.CDLL(ssm.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), f"{n} not exported"
@@ -64,6 +65,17 @@ def _scan(lib, **kw):
                             a["dim"], a["N"], a["io"], a["stream"])
 
 
+def _scan_ex(lib, **kw):
+    a = dict(u=FAKE, delta=FAKE, A=FAKE, B=FAKE, C=FAKE, D=None, z=None, bias=None, softplus=1,
+             dt_mode=0, h0=None, seq_lens=None, reset=None, y=FAKE, last=None, batch=2, L=8,
+             dim=64, N=16, io=1, stream=None)
+    a.update(kw)
+    return lib.ssm_scan_fwd_ex(a["u"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"],
+                               a["bias"], a["softplus"], a["dt_mode"], a["h0"], a["seq_lens"],
+                               a["reset"], a["y"], a["last"], a["batch"], a["L"], a["dim"], a["N"],
+                               a["io"], a["stream"])
+
+
 def _step(lib, **kw):
     a = dict(state=FAKE, u=FAKE, delta=FAKE, A=FAKE, B=FAKE, C=FAKE, D=None, z=None, bias=None,
              softplus=1, dt_mode=0, y=FAKE, batch=2, dim=64, N=16, io=1, stream=None)
@@ -73,7 +85,7 @@ def _step(lib, **kw):
                         a["N"], a["io"], a["stream"])
 
 
-@pytest.mark.parametrize("call", [_scan, _step])
+@pytest.mark.parametrize("call", [_scan, _scan_ex, _step])
 def test_invalid_arguments_are_rejected(lib, call):
     c = _header_constants()
     assert call(lib, N=0) == c["SSM_ERR_SHAPE"]
@@ -100,6 +112,10 @@ def test_scan_specific_checks(lib):
     assert _scan(lib, L=-1) == c["SSM_ERR_SHAPE"]
     assert _scan(lib, last=MISALIGNED) == c["SSM_ERR_ALIGN"]
     assert _scan(lib, batch=1 << 20, dim=1 << 20, L=1) == c["SSM_ERR_UNSUPPORTED"]  # > 2^31 blocks
+    assert _scan_ex(lib, h0=MISALIGNED) == c["SSM_ERR_ALIGN"]
+    assert _scan_ex(lib, seq_lens=ctypes.c_void_p(0x10002)) == c["SSM_ERR_ALIGN"]
+    assert _scan_ex(lib, L=-1) == c["SSM_ERR_SHAPE"]
+    assert _scan_ex(lib, batch=1 << 20, dim=1 << 20, L=1) == c["SSM_ERR_UNSUPPORTED"]
     assert _step(lib, state=None) == c["SSM_ERR_NULL"]
     assert _step(lib, state=MISALIGNED) == c["SSM_ERR_ALIGN"]
 
