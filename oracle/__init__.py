@@ -66,6 +66,12 @@ def _load():
     lib.oracle_step.restype = None
     lib.oracle_step.argtypes = [ctypes.c_void_p] * 9 + [ctypes.c_int, ctypes.c_int,
                                                         ctypes.c_void_p] + [ctypes.c_int64] * 3
+    lib.oracle_conv1d_fwd.restype = None
+    lib.oracle_conv1d_fwd.argtypes = [ctypes.c_void_p] * 6 + [ctypes.c_int, ctypes.c_void_p,
+                                                              ctypes.c_void_p] + [ctypes.c_int64] * 4
+    lib.oracle_conv1d_step.restype = None
+    lib.oracle_conv1d_step.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int, ctypes.c_void_p] + \
+        [ctypes.c_int64] * 3
     _lib = lib
     return lib
 
@@ -182,3 +188,52 @@ def step(state, u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=Tru
                         _ptr(z), _ptr(delta_bias), int(bool(softplus)), _MODES[dt_mode],
                         _ptr(y), batch, dim, N)
     return y, st
+
+
+def conv1d_fwd(x, weight, bias=None, silu=True, state_in=None, seq_lens=None, reset=None):
+    """The block's causal depthwise convolution (+ SiLU) over whole sequences, fp64.
+
+    x: (batch, L, dim); weight: (dim, k), weight[c, i] multiplies the input i
+    steps back; bias: (dim,); state_in: optional (batch, k - 1, dim) window of
+    earlier inputs, oldest first; seq_lens (batch,), reset (batch, L) as in
+    scan_fwd.  Returns (out (batch, L, dim), state_out (batch, k - 1, dim)).
+    """
+    x = _f64(x)
+    w = _f64(weight)
+    bias = _f64(bias)
+    state_in = _f64(state_in)
+    batch, L, dim = x.shape
+    k = w.shape[1]
+    assert w.shape == (dim, k) and k >= 1
+    assert bias is None or bias.shape == (dim,)
+    assert state_in is None or state_in.shape == (batch, k - 1, dim)
+    if seq_lens is not None:
+        seq_lens = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int64))
+        assert seq_lens.shape == (batch,)
+    if reset is not None:
+        reset = np.ascontiguousarray(np.asarray(reset) != 0, dtype=np.uint8)
+        assert reset.shape == (batch, L)
+    out = np.empty((batch, L, dim), dtype=np.float64)
+    st = np.empty((batch, k - 1, dim), dtype=np.float64)
+    _load().oracle_conv1d_fwd(_ptr(x), _ptr(w), _ptr(bias), _ptr(state_in), _ptr(seq_lens),
+                              _ptr(reset), int(bool(silu)), _ptr(out), _ptr(st), batch, L, dim, k)
+    return out, st
+
+
+def conv1d_step(window, x, weight, bias=None, silu=True):
+    """One decoding step of the convolution, fp64.
+
+    window: (batch, k - 1, dim), oldest first -- not modified; x: (batch, dim).
+    Returns (out (batch, dim), new_window).
+    """
+    win = np.array(window, dtype=np.float64, copy=True, order="C")
+    x = _f64(x)
+    w = _f64(weight)
+    bias = _f64(bias)
+    batch, dim = x.shape
+    k = w.shape[1]
+    assert win.shape == (batch, k - 1, dim) and w.shape == (dim, k)
+    out = np.empty((batch, dim), dtype=np.float64)
+    _load().oracle_conv1d_step(_ptr(win), _ptr(x), _ptr(w), _ptr(bias), int(bool(silu)),
+                               _ptr(out), batch, dim, k)
+    return out, win

@@ -236,3 +236,80 @@ void oracle_step(double* state, const double* u, const double* delta, const doub
     }
   }
 }
+
+/* ------------------------------------------------------------------------
+ * The short causal depthwise convolution in front of the scan, "The Mamba
+ * block" on the first page:
+ *   x_t = SiLU( sum_{i=0}^{k-1} w_i (.) xt_{t-i} + b_conv ),  xt_s = 0 before
+ *   the sequence,
+ * each channel with its own k weights ("It is depthwise").  w is stored
+ * (dim, k) with w[c*k + i] multiplying the input i steps back.
+ *
+ * Decoding ("Decoding with a constant-size cache"; "One decoding step with
+ * conv and state caches") keeps the last k - 1 INPUTS of the convolution,
+ * oldest first, per sequence: window (batch, k - 1, dim).  "Where Mamba
+ * implementations go wrong" stresses that the window holds inputs, not
+ * outputs, and shifts every step.
+ *
+ * The prefill form takes the same optional extras as the scan: state_in (the
+ * window carried in from an earlier chunk, zeros when NULL), seq_lens
+ * (padding after each length: output 0; state_out holds the last k - 1 real
+ * inputs) and reset (a document starting at t sees zeros before t).
+ * state_out receives the window after the last real token.
+ * ------------------------------------------------------------------------ */
+
+static double act(double v, int silu) { return silu ? v * oracle_sigmoid(v) : v; }
+
+void oracle_conv1d_fwd(const double* x, const double* w, const double* bias,
+                       const double* state_in, const int64_t* seq_lens, const uint8_t* reset,
+                       int silu, double* out, double* state_out, int64_t batch, int64_t L,
+                       int64_t dim, int64_t k) {
+  for (int64_t b = 0; b < batch; ++b) {
+    int64_t len = seq_lens ? seq_lens[b] : L;
+    if (len < 0) len = 0;
+    if (len > L) len = L;
+    for (int64_t c = 0; c < dim; ++c) {
+      /* the input at position s (s may be negative: the carried-in window),
+       * for a document that starts at `start` (inputs before it are zero) */
+#define XT(s, start)                                                                   \
+  (((s) < (start)) ? 0.0                                                               \
+   : ((s) >= 0)    ? x[(b * L + (s)) * dim + c]                                        \
+   : (state_in && (s) >= -(k - 1)) ? state_in[(b * (k - 1) + (k - 1 + (s))) * dim + c] \
+                                   : 0.0)
+      int64_t start = -(k - 1); /* no document break yet: the window counts */
+      for (int64_t t = 0; t < L; ++t) {
+        const int64_t oi = (b * L + t) * dim + c;
+        if (t >= len) {
+          out[oi] = 0.0;
+          continue;
+        }
+        if (reset && reset[b * L + t]) start = t;
+        double pre = bias ? bias[c] : 0.0;
+        for (int64_t i = 0; i < k; ++i) pre += w[c * k + i] * XT(t - i, start);
+        out[oi] = act(pre, silu);
+      }
+      if (state_out)
+        for (int64_t j = 0; j < k - 1; ++j) {
+          const int64_t s = len - (k - 1) + j; /* oldest first */
+          state_out[(b * (k - 1) + j) * dim + c] = XT(s, start);
+        }
+#undef XT
+    }
+  }
+}
+
+/* One decoding step: append x to the window, convolve, shift. */
+void oracle_conv1d_step(double* window, const double* x, const double* w, const double* bias,
+                        int silu, double* out, int64_t batch, int64_t dim, int64_t k) {
+  for (int64_t b = 0; b < batch; ++b) {
+    for (int64_t c = 0; c < dim; ++c) {
+      double* win = window + b * (k - 1) * dim + c; /* win[j * dim], j = 0 oldest */
+      const double xt = x[b * dim + c];
+      double pre = (bias ? bias[c] : 0.0) + w[c * k] * xt;
+      for (int64_t i = 1; i < k; ++i) pre += w[c * k + i] * win[(k - 1 - i) * dim];
+      out[b * dim + c] = act(pre, silu);
+      for (int64_t j = 0; j + 1 < k - 1; ++j) win[j * dim] = win[(j + 1) * dim];
+      if (k > 1) win[(k - 2) * dim] = xt;
+    }
+  }
+}

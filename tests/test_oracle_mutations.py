@@ -40,6 +40,16 @@ MUTATIONS = {
     "reset_one_token_late": ("    if (j->reset && j->reset[b * L + t]) /* a document starts at t */",
                              "    if (j->reset && t > 0 && j->reset[b * L + t - 1])"),
     "h0_ignored": ("    hp[n] = j->h0 ? j->h0[(b * dim + c) * N + n] : 0.0;", "    hp[n] = 0.0;"),
+    "conv_taps_reversed": ("for (int64_t i = 0; i < k; ++i) pre += w[c * k + i] * XT(t - i, start);",
+                           "for (int64_t i = 0; i < k; ++i) pre += w[c * k + (k - 1 - i)] * XT(t - i, start);"),
+    "conv_not_causal": ("for (int64_t i = 0; i < k; ++i) pre += w[c * k + i] * XT(t - i, start);",
+                        "for (int64_t i = 0; i < k; ++i) pre += w[c * k + i] * XT(t - i + 1, start);"),
+    "conv_window_holds_outputs": ("      if (k > 1) win[(k - 2) * dim] = xt;",
+                                  "      if (k > 1) win[(k - 2) * dim] = out[b * dim + c];"),
+    "conv_window_newest_first": ("          const int64_t s = len - (k - 1) + j; /* oldest first */",
+                                 "          const int64_t s = len - 1 - j;"),
+    "conv_reset_ignored": ("        if (reset && reset[b * L + t]) start = t;", "        (void)reset;"),
+    "conv_bias_dropped": ("        double pre = bias ? bias[c] : 0.0;", "        double pre = 0.0;"),
 }
 
 
@@ -56,6 +66,7 @@ def test_planted_mistake_is_caught(name, tmp_path):
                     "-lm", "-pthread"], check=True)
     env = dict(os.environ, SSM_ORACLE_LIB=str(lib))
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py"),
+                        os.path.join(ROOT, "tests", "test_oracle_conv_pins.py")],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
     assert r.returncode != 0, f"mutation {name} survived the pins:\n{r.stdout[-2000:]}"

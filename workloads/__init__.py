@@ -252,3 +252,61 @@ def as_f64(x: Optional[np.ndarray], io: str) -> Optional[np.ndarray]:
     if io == "bf16" and x.dtype == np.uint16:
         return bf16_bits_to_f32(x).astype(np.float64)
     return np.asarray(x, dtype=np.float64)
+
+
+# ------------------------------------------------- the block's convolution
+
+S_CONV_W, S_CONV_B, S_CONV_X, S_CONV_WIN = range(21, 25)
+
+
+@dataclass(frozen=True)
+class ConvConfig:
+    name: str
+    batch: int
+    L: int          # 0 for the decoding workload (one token per step)
+    dim: int
+    k: int
+    io: str
+    seed: int
+    steps: int = 0  # decoding steps
+
+
+CONV_CONFIGS: Dict[str, ConvConfig] = {
+    # the convolution in front of the Mamba-130M-shaped scan layer
+    "conv130m": ConvConfig("conv130m", 8, 2048, 1536, 4, "bf16", 5),
+    "conv_tiny": ConvConfig("conv_tiny", 2, 100, 70, 4, "f32", 6),
+    # one decoding step of the convolution at the decode workload's width
+    "conv_decode": ConvConfig("conv_decode", 256, 0, 5120, 4, "bf16", 7, steps=100),
+}
+
+
+def conv_params(seed: int, dim: int, k: int):
+    """Depthwise weights (dim, k) and bias (dim,), U(-1/sqrt(k), 1/sqrt(k)) float32
+    (the usual fan-in bound of a convolution with k taps per channel)."""
+    bound = 1.0 / np.sqrt(k)
+    w = (2.0 * uniform(seed, S_CONV_W, np.arange(dim * k)) - 1.0) * bound
+    b = (2.0 * uniform(seed, S_CONV_B, np.arange(dim)) - 1.0) * bound
+    return w.reshape(dim, k).astype(np.float32), b.astype(np.float32)
+
+
+def conv_inputs(cfg: ConvConfig, channels: Optional[Sequence[int]] = None) -> dict:
+    """x (batch, L, len(channels)) in the io dtype (bf16 bits or fp32) ~ N(0, 1),
+    and the weights and bias of those channels."""
+    ch = np.arange(cfg.dim) if channels is None else np.asarray(channels, dtype=np.int64)
+    w, b = conv_params(cfg.seed, cfg.dim, cfg.k)
+    idx = (np.arange(cfg.batch * cfg.L, dtype=np.int64)[:, None] * cfg.dim + ch[None, :])
+    x = _io(normal(cfg.seed, S_CONV_X, idx), cfg.io).reshape(cfg.batch, cfg.L, len(ch))
+    return dict(x=x, w=w[ch], bias=b[ch], io=cfg.io, channels=ch)
+
+
+def conv_window0(cfg: ConvConfig) -> np.ndarray:
+    """A decoding window (batch, k - 1, dim) of earlier inputs ~ N(0, 1), io dtype."""
+    n = cfg.batch * (cfg.k - 1) * cfg.dim
+    return _io(normal(cfg.seed, S_CONV_WIN, np.arange(n)), cfg.io).reshape(
+        cfg.batch, cfg.k - 1, cfg.dim)
+
+
+def conv_step_inputs(cfg: ConvConfig, step: int) -> np.ndarray:
+    """The token (batch, dim) of decoding step `step`, io dtype."""
+    idx = np.arange(cfg.batch * cfg.dim, dtype=np.int64) + (step + 1) * cfg.batch * cfg.dim
+    return _io(normal(cfg.seed, S_CONV_X, idx), cfg.io).reshape(cfg.batch, cfg.dim)
