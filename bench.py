@@ -10,9 +10,10 @@ to step so that the 256 MB Infinity Cache cannot serve a step from the previous
 one.  `value` is algorithmic bytes per step / measured step time.
 
 Also reported, outside `value`: the same scan under the exponential-Euler rule,
-the decode step (ssm_step) on its workload (batch 256, D 5120, N 16,
-1000 consecutive tokens), the kernel roofline for the dominant kernel, and the
-fp64 CPU oracle timed on the host.
+the extended scan (initial state, lengths, document resets), the block's
+convolution (sequence and decoding step), the decode step (ssm_step) on its
+workload (batch 256, D 5120, N 16, 1000 consecutive tokens), the kernel
+roofline for the dominant kernel, and the fp64 CPU oracle timed on the host.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu]
 
@@ -20,6 +21,7 @@ For profilers (rocprofv3) a reduced mode runs a few launches of one kernel on
 one input set and prints no JSON:
     python bench.py --only scan [--dt-mode zoh|euler] [--launches 3]
     python bench.py --only decode [--launches 3]
+    python bench.py --only conv [--launches 3]
     python bench.py --only copy     # a plain 256 MiB device copy, for counter calibration
 """
 import argparse
@@ -177,6 +179,75 @@ def time_decode(cfg, nsteps, dev, npool=8):
     return wall_s, e0.elapsed_time(e1) / nsteps
 
 
+def conv_bytes(b, L, D, k, io_bytes):
+    """Algorithmic bytes of the sequence convolution: x read and out written once,
+    the decoding window written, weights and bias read."""
+    return 2 * b * L * D * io_bytes + b * (k - 1) * D * io_bytes + 4 * D * k + 4 * D
+
+
+def time_conv(dev, steps, warmup, nsets=4):
+    """The block's convolution on the Mamba-130M layer's input (bf16, k = 4),
+    rotating `nsets` input sets (4 x 100 MB of x and out > the 256 MB Infinity
+    Cache); and its decoding step on the decode workload's width (the window
+    stays cache-resident across steps, as in a real decoding loop)."""
+    import torch
+    import selective_state_space_66_amd as ssm
+    import workloads as W
+    cfg = W.CONV_CONFIGS["conv130m"]
+    sets = []
+    for k in range(nsets):
+        c = W.ConvConfig(cfg.name, cfg.batch, cfg.L, cfg.dim, cfg.k, cfg.io, cfg.seed + 100 * k)
+        inp = W.conv_inputs(c)
+        sets.append((to_dev(inp["x"], cfg.io, dev), to_dev(inp["w"], "f32", dev),
+                     to_dev(inp["bias"], "f32", dev)))
+    outs = [(torch.empty_like(x), torch.empty((cfg.batch, cfg.k - 1, cfg.dim), dtype=x.dtype,
+                                              device=dev)) for x, _, _ in sets]
+
+    def launch(i):
+        x, w, b = sets[i % nsets]
+        o, win = outs[i % nsets]
+        ssm.conv1d_fwd(x, w, bias=b, out=o, window_out=win)
+
+    for i in range(warmup):
+        launch(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record()
+        launch(warmup + i)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    fwd_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+    dcfg = W.CONV_CONFIGS["conv_decode"]
+    w, b = W.conv_params(dcfg.seed, dcfg.dim, dcfg.k)
+    wd, bd = to_dev(w, "f32", dev), to_dev(b, "f32", dev)
+    win = to_dev(W.conv_window0(dcfg), dcfg.io, dev)
+    toks = [to_dev(W.conv_step_inputs(dcfg, s), dcfg.io, dev) for s in range(8)]
+    o = torch.empty_like(toks[0])
+    for i in range(20):
+        ssm.conv1d_step(win, toks[i % 8], wd, bias=bd, out=o)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(dcfg.steps):
+        ssm.conv1d_step(win, toks[i % 8], wd, bias=bd, out=o)
+    e1.record()
+    torch.cuda.synchronize()
+    step_us = e0.elapsed_time(e1) / dcfg.steps * 1e3
+    fwd_b = conv_bytes(cfg.batch, cfg.L, cfg.dim, cfg.k, 2)
+    step_b = 8 * dcfg.batch * dcfg.dim * 2 + 4 * dcfg.dim * (dcfg.k + 1)
+    return {"workload": f"ssm_conv1d_fwd: batch {cfg.batch}, L {cfg.L}, D {cfg.dim}, k {cfg.k}, "
+                        "bf16, SiLU",
+            "kernel_ms": round(fwd_ms, 5),
+            "GB/s": round(fwd_b / (fwd_ms * 1e-3) / 1e9, 2),
+            "hbm_frac": round(fwd_b / (fwd_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "step": {"workload": f"ssm_conv1d_step: batch {dcfg.batch}, D {dcfg.dim}, k {dcfg.k}, "
+                                 "bf16, SiLU", "us_per_step": round(step_us, 3),
+                     "GB/s": round(step_b / (step_us * 1e-6) / 1e9, 2)}}
+
+
 def cpu_baseline(cfg, inp, threads):
     """The fp64 oracle, as it stands, on the same workload on the host cores."""
     import oracle
@@ -210,6 +281,13 @@ def profile_only(what, launches, dt_mode):
                          delta_bias=s["delta_bias"], dt_mode=dt_mode, y=y, last_state=last)
     elif what == "decode":
         time_decode(W.STEP_CONFIGS["decode"], launches, dev, npool=2)
+    elif what == "conv":
+        cfg = W.CONV_CONFIGS["conv130m"]
+        inp = W.conv_inputs(cfg)
+        x = to_dev(inp["x"], cfg.io, dev)
+        w, b = to_dev(inp["w"], "f32", dev), to_dev(inp["bias"], "f32", dev)
+        for _ in range(launches):
+            ssm.conv1d_fwd(x, w, bias=b)
     torch.cuda.synchronize()
     log(f"[bench] profile-only {what}: {launches} launches done")
 
@@ -221,7 +299,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--decode-steps", type=int, default=1000)
-    ap.add_argument("--only", choices=["scan", "decode", "copy"], default=None,
+    ap.add_argument("--only", choices=["scan", "decode", "conv", "copy"], default=None,
                     help="profiling mode: a few launches of one kernel, no JSON")
     ap.add_argument("--launches", type=int, default=3)
     ap.add_argument("--dt-mode", choices=["zoh", "euler"], default="zoh")
@@ -274,12 +352,16 @@ def main():
     x_updates = sum(lens) * cfg.dim * cfg.N
     log(f"[bench] extended: wall {x_wall:.4f} ms/step, kernel {x_kern:.4f} ms")
 
+    log("[bench] timing the convolution")
+    del sets
+    torch.cuda.empty_cache()
+    conv = time_conv(dev, args.steps, args.warmup)
+    log(f"[bench] conv: {conv['kernel_ms']:.4f} ms, step {conv['step']['us_per_step']:.2f} us")
+
     dcfg = W.STEP_CONFIGS["decode"]
     log("[bench] timing decode steps")
     d_wall_s, d_kern_ms = time_decode(dcfg, args.decode_steps, dev)
     d_bytes = step_bytes(dcfg.batch, dcfg.dim, dcfg.N, 2, dcfg.gate)
-    del sets
-    torch.cuda.empty_cache()
 
     cpu = None
     if not args.no_cpu:
@@ -337,6 +419,7 @@ def main():
                     "GB/s": round(x_bytes / (x_kern * 1e-3) / 1e9, 2),
                     "alu_frac": round(FLOPS_PER_UPDATE * x_updates / (x_kern * 1e-3) / 1e12
                                       / ALU_PEAK_TFLOPS, 4)},
+        "conv": conv,
         "decode": {"workload": "ssm_step: batch 256, D 5120, N 16, bf16 io, fp32 state, gate, ZOH",
                    "steps": args.decode_steps,
                    "tok_per_s": round(dcfg.batch * args.decode_steps / d_wall_s, 1),

@@ -1,7 +1,7 @@
 /*
  * ssm66.h -- C ABI of the MI355X (gfx950) selective-scan library.
  *
- * Three entry points, all defined on "Mamba and selective state spaces"
+ * Five entry points, all defined on "Mamba and selective state spaces"
  * (zerotofrontier.app/ssm/mamba):
  *
  *   ssm_scan_fwd : the selective state-space layer (S6) over whole sequences --
@@ -23,6 +23,10 @@
  *                  documents should not see each other).
  *   ssm_step     : one token of that layer against a state cache, updated in
  *                  place ("Decoding with a constant-size cache").
+ *   ssm_conv1d_fwd, ssm_conv1d_step : the short causal depthwise convolution
+ *                  (+ SiLU) that feeds the scan in "The Mamba block", over
+ *                  whole sequences and as one decoding step with its window of
+ *                  the last k - 1 inputs.
  *
  * Conventions shared by all calls
  *   - Every pointer is caller-owned DEVICE memory (HBM).  The library keeps no
@@ -63,12 +67,13 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 2
+#define SSM_ABI_VERSION 3
 
 /* status codes */
 #define SSM_OK 0
 #define SSM_ERR_NULL 1        /* a required pointer is NULL */
-#define SSM_ERR_SHAPE 2       /* negative size, dstate outside [1, 16], or size overflow */
+#define SSM_ERR_SHAPE 2       /* negative size, dstate outside [1, 16], width outside
+                                 [1, 4], or size overflow */
 #define SSM_ERR_DTYPE 3       /* io_dtype is not SSM_F32 or SSM_BF16 */
 #define SSM_ERR_FLAG 4        /* softplus not 0/1, or dt_mode unknown */
 #define SSM_ERR_ALIGN 5       /* a pointer is not aligned to its element size */
@@ -130,6 +135,44 @@ int ssm_step(float* state, const void* u, const void* delta, const float* A, con
              const void* C, const float* D, const void* z, const float* delta_bias, int softplus,
              int dt_mode, void* y, int64_t batch, int64_t dim, int64_t dstate, int io_dtype,
              void* stream);
+
+/*
+ * The block's causal depthwise convolution over whole sequences ("The Mamba
+ * block": x_t = SiLU(sum_{i<k} w_i * xt_{t-i} + b_conv), inputs before the
+ * sequence are zero, each channel has its own k taps).
+ *   x, out      : (batch, seqlen, dim), io dtype
+ *   weight      : (dim, width) float32; weight[c * width + i] multiplies the
+ *                 input i steps back (i = 0 is the current token)
+ *   bias        : (dim) float32, or NULL
+ *   silu        : 1 applies SiLU to the sum, 0 returns the sum
+ *   window_in   : (batch, width - 1, dim) io dtype, oldest first: the inputs
+ *                 before token 0 (a later chunk of a prefill), or NULL (zeros)
+ *   seq_lens    : (batch) int32 or NULL; tokens past a length output 0
+ *   reset       : (batch, seqlen) uint8 or NULL; a document starting at t sees
+ *                 zeros before t
+ *   window_out  : (batch, width - 1, dim) io dtype, or NULL: the last width - 1
+ *                 real inputs, oldest first (zeros before a document start) --
+ *                 the decoding window after a prefill ("Decoding with a
+ *                 constant-size cache").  Must not overlap window_in.
+ * 1 <= width <= 4.  The io pointers must be aligned to their element size;
+ * weight, bias and seq_lens to 4 bytes.  Returns SSM_OK or an error status.
+ */
+int ssm_conv1d_fwd(const void* x, const float* weight, const float* bias, int silu,
+                   const void* window_in, const int32_t* seq_lens, const uint8_t* reset,
+                   void* out, void* window_out, int64_t batch, int64_t seqlen, int64_t dim,
+                   int64_t width, int io_dtype, void* stream);
+
+/*
+ * One decoding step of the convolution: out = SiLU?(w_0 x + sum_{i>=1} w_i
+ * window[width - 1 - i] + b); then window (batch, width - 1, dim), oldest
+ * first, drops its oldest input and appends x, in place (the window holds
+ * inputs, not outputs: "Where Mamba implementations go wrong").
+ * x, out: (batch, dim) io dtype; weight, bias as for ssm_conv1d_fwd.
+ * Returns SSM_OK or an error status.
+ */
+int ssm_conv1d_step(void* window, const void* x, const float* weight, const float* bias,
+                    int silu, void* out, int64_t batch, int64_t dim, int64_t width, int io_dtype,
+                    void* stream);
 
 /* A static, human-readable string for a status code. */
 const char* ssm_status_string(int status);

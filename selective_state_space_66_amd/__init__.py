@@ -11,6 +11,9 @@ missing, every call raises.
                              h0=None, seq_lens=None, reset=None)
     y = step(state, u, delta, A, B, C, D=None, z=None, delta_bias=None,
              softplus=True, dt_mode="zoh")     # state updated in place
+    out, window = conv1d_fwd(x, weight, bias=None, silu=True, window_in=None,
+                             seq_lens=None, reset=None)
+    out = conv1d_step(window, x, weight, bias=None, silu=True)   # window updated in place
 """
 import ctypes
 import os
@@ -44,6 +47,10 @@ def load_library():
     lib.ssm_scan_fwd.argtypes = [vp] * 8 + [ci, ci, vp, vp, i64, i64, i64, i64, ci, vp]
     lib.ssm_scan_fwd_ex.restype = ci
     lib.ssm_scan_fwd_ex.argtypes = [vp] * 8 + [ci, ci] + [vp] * 5 + [i64, i64, i64, i64, ci, vp]
+    lib.ssm_conv1d_fwd.restype = ci
+    lib.ssm_conv1d_fwd.argtypes = [vp] * 3 + [ci] + [vp] * 5 + [i64] * 4 + [ci, vp]
+    lib.ssm_conv1d_step.restype = ci
+    lib.ssm_conv1d_step.argtypes = [vp] * 4 + [ci, vp] + [i64] * 3 + [ci, vp]
     lib.ssm_step.restype = ci
     lib.ssm_step.argtypes = [vp] * 9 + [ci, ci, vp, i64, i64, i64, ci, vp]
     lib.ssm_status_string.restype = ctypes.c_char_p
@@ -185,3 +192,74 @@ def step(state, u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=Tru
     if st != 0:
         raise SsmError(st, "ssm_step")
     return y
+
+
+def conv1d_fwd(x, weight, bias=None, silu=True, window_in=None, seq_lens=None, reset=None,
+               out=None, window_out=None, return_window=True):
+    """The block's causal depthwise convolution (+ SiLU) over whole sequences on the GPU.
+
+    x: (batch, L, dim) float32 or bfloat16; weight: (dim, k) float32, weight[c, i]
+    multiplies the input i steps back (1 <= k <= 4); bias: (dim,) float32;
+    window_in: optional (batch, k - 1, dim) earlier inputs, oldest first;
+    seq_lens: optional (batch,) int32; reset: optional (batch, L) bool or uint8.
+    Returns (out like x, window (batch, k - 1, dim) like x, or None if not requested).
+    """
+    import torch
+    lib = load_library()
+    if x.dim() != 3:
+        raise ValueError("x must be (batch, L, dim)")
+    batch, L, dim = x.shape
+    k = weight.shape[-1]
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on the GPU")
+    io = x.dtype
+    _io_code(x)
+    _check(x, "x", (batch, L, dim), io, dev)
+    _check(weight, "weight", (dim, k), torch.float32, dev)
+    _check(bias, "bias", (dim,), torch.float32, dev)
+    _check(window_in, "window_in", (batch, k - 1, dim), io, dev)
+    _check(seq_lens, "seq_lens", (batch,), torch.int32, dev)
+    if reset is not None and reset.dtype == torch.bool:
+        reset = reset.view(torch.uint8)
+    _check(reset, "reset", (batch, L), torch.uint8, dev)
+    if out is None:
+        out = torch.empty_like(x)
+    _check(out, "out", (batch, L, dim), io, dev)
+    if window_out is None and return_window:
+        window_out = torch.empty((batch, k - 1, dim), dtype=io, device=dev)
+    _check(window_out, "window_out", (batch, k - 1, dim), io, dev)
+    st = lib.ssm_conv1d_fwd(_ptr(x), _ptr(weight), _ptr(bias), int(bool(silu)), _ptr(window_in),
+                            _ptr(seq_lens), _ptr(reset), _ptr(out), _ptr(window_out), batch, L,
+                            dim, k, _io_code(x), _stream(dev))
+    if st != 0:
+        raise SsmError(st, "ssm_conv1d_fwd")
+    return out, window_out
+
+
+def conv1d_step(window, x, weight, bias=None, silu=True, out=None):
+    """One decoding step of the convolution on the GPU; `window` (batch, k - 1, dim),
+    oldest first, is shifted in place.  x: (batch, dim). Returns out like x."""
+    import torch
+    lib = load_library()
+    if x.dim() != 2:
+        raise ValueError("x must be (batch, dim)")
+    batch, dim = x.shape
+    k = weight.shape[-1]
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on the GPU")
+    io = x.dtype
+    _io_code(x)
+    _check(window, "window", (batch, k - 1, dim), io, dev)
+    _check(x, "x", (batch, dim), io, dev)
+    _check(weight, "weight", (dim, k), torch.float32, dev)
+    _check(bias, "bias", (dim,), torch.float32, dev)
+    if out is None:
+        out = torch.empty_like(x)
+    _check(out, "out", (batch, dim), io, dev)
+    st = lib.ssm_conv1d_step(_ptr(window), _ptr(x), _ptr(weight), _ptr(bias), int(bool(silu)),
+                             _ptr(out), batch, dim, k, _io_code(x), _stream(dev))
+    if st != 0:
+        raise SsmError(st, "ssm_conv1d_step")
+    return out

@@ -145,4 +145,68 @@ int ssm_step(float* state, const void* u, const void* delta, const float* A, con
   return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 
+int ssm_conv1d_fwd(const void* x, const float* weight, const float* bias, int silu,
+                   const void* window_in, const int32_t* seq_lens, const uint8_t* reset,
+                   void* out, void* window_out, int64_t batch, int64_t seqlen, int64_t dim,
+                   int64_t width, int io_dtype, void* stream) {
+  if (batch < 0 || seqlen < 0 || dim < 0) return SSM_ERR_SHAPE;
+  if (width < 1 || width > 4) return SSM_ERR_SHAPE;
+  if (io_dtype != SSM_F32 && io_dtype != SSM_BF16) return SSM_ERR_DTYPE;
+  if (silu != 0 && silu != 1) return SSM_ERR_FLAG;
+  int64_t tmp;
+  if (!mul3(batch, seqlen, dim, &tmp) || !mul3(batch, width, dim, &tmp)) return SSM_ERR_SHAPE;
+  if (batch == 0 || dim == 0) return SSM_OK;
+  if (!weight) return SSM_ERR_NULL;
+  if (seqlen > 0 && (!x || !out)) return SSM_ERR_NULL;
+  const size_t es = io_dtype == SSM_BF16 ? 2 : 4;
+  const void* io_ptrs[4] = {x, out, window_in, window_out};
+  for (const void* q : io_ptrs)
+    if (q && !aligned(q, es)) return SSM_ERR_ALIGN;
+  const void* f32_ptrs[3] = {weight, bias, seq_lens};
+  for (const void* q : f32_ptrs)
+    if (q && !aligned(q, 4)) return SSM_ERR_ALIGN;
+  // grid: channel vectors in x, 64-token runs in y, batch in z
+  if ((seqlen + 63) / 64 > 65535 || batch > 65535 || dim / 64 + 1 > 0x7fffffff)
+    return SSM_ERR_UNSUPPORTED;
+  bool vec4 = dim % 4 == 0;
+  for (const void* q : io_ptrs)
+    if (q && !aligned(q, 4 * es)) vec4 = false;
+
+  ssm66::ConvParams p;
+  p.x = x; p.w = weight; p.bias = bias; p.state_in = window_in; p.seq_lens = seq_lens;
+  p.reset = reset; p.out = out; p.state_out = window_out;
+  p.batch = batch; p.L = seqlen; p.dim = dim; p.k = width; p.silu = silu;
+  const hipError_t e = ssm66::launch_conv1d(p, io_dtype, vec4, false, (hipStream_t)stream);
+  return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
+int ssm_conv1d_step(void* window, const void* x, const float* weight, const float* bias,
+                    int silu, void* out, int64_t batch, int64_t dim, int64_t width, int io_dtype,
+                    void* stream) {
+  if (batch < 0 || dim < 0) return SSM_ERR_SHAPE;
+  if (width < 1 || width > 4) return SSM_ERR_SHAPE;
+  if (io_dtype != SSM_F32 && io_dtype != SSM_BF16) return SSM_ERR_DTYPE;
+  if (silu != 0 && silu != 1) return SSM_ERR_FLAG;
+  int64_t tmp;
+  if (!mul3(batch, width, dim, &tmp)) return SSM_ERR_SHAPE;
+  if (batch == 0 || dim == 0) return SSM_OK;
+  if (!weight || !x || !out || (width > 1 && !window)) return SSM_ERR_NULL;
+  const size_t es = io_dtype == SSM_BF16 ? 2 : 4;
+  const void* io_ptrs[3] = {x, out, window};
+  for (const void* q : io_ptrs)
+    if (q && !aligned(q, es)) return SSM_ERR_ALIGN;
+  if (!aligned(weight, 4) || (bias && !aligned(bias, 4))) return SSM_ERR_ALIGN;
+  if ((batch * dim + 255) / 256 > 0x7fffffff) return SSM_ERR_UNSUPPORTED;
+  bool vec4 = dim % 4 == 0;
+  for (const void* q : io_ptrs)
+    if (q && !aligned(q, 4 * es)) vec4 = false;
+
+  ssm66::ConvParams p;
+  p.x = x; p.w = weight; p.bias = bias; p.state_in = nullptr; p.seq_lens = nullptr;
+  p.reset = nullptr; p.out = out; p.state_out = window;
+  p.batch = batch; p.L = 1; p.dim = dim; p.k = width; p.silu = silu;
+  const hipError_t e = ssm66::launch_conv1d(p, io_dtype, vec4, true, (hipStream_t)stream);
+  return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
 }  // extern "C"

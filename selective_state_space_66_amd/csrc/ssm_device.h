@@ -26,6 +26,13 @@ __device__ __forceinline__ void store_io(bf16_bits* p, float v) {
   *p = __builtin_bit_cast(uint16_t, (__bf16)v);
 }
 
+// two floats -> two bf16 (round to nearest even) in one word, a in the low half
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const uint32_t lo = __builtin_bit_cast(uint16_t, (__bf16)a);
+  const uint32_t hi = __builtin_bit_cast(uint16_t, (__bf16)b);
+  return lo | (hi << 16);
+}
+
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float log2_hw(float x) { return __builtin_amdgcn_logf(x); }
 __device__ __forceinline__ float rcp_hw(float x) { return __builtin_amdgcn_rcpf(x); }
@@ -54,41 +61,6 @@ __device__ __forceinline__ float zoh_phi(float k, float ek) {
                                                         1.0f / 120.0f), 1.0f / 24.0f), 1.0f / 6.0f),
                                0.5f), 1.0f);
   return fabsf(k) < 0.5f ? s : (ek - 1.0f) / k;
-}
-
-// Load G consecutive io values from a wave-uniform address.  When the address
-// is uniform and the pointer is a __restrict__ kernel argument (so no store of
-// the kernel can clobber it), the compiler serves this with one scalar load
-// (s_load_dwordxN) into SGPRs.  p must be aligned to G elements.
-template <int bytes> struct UVec;
-template <> struct UVec<2> { using type = uint16_t; };
-template <> struct UVec<4> { using type = uint32_t; };
-template <> struct UVec<8> { using type = uint2; };
-template <> struct UVec<16> { using type = uint4; };
-
-template <int G, typename IO>
-__device__ __forceinline__ void load_uniform(const IO* __restrict__ p, float (&v)[G]) {
-  constexpr int bytes = G * (int)sizeof(IO);
-  static_assert(bytes <= 16, "at most 16 bytes per uniform load");
-  using V = typename UVec<bytes>::type;
-  const V raw = *(const V*)p;
-  uint32_t w[(bytes + 3) / 4];
-  if constexpr (bytes == 2)
-    w[0] = (uint32_t)raw;
-  else
-    __builtin_memcpy(w, &raw, bytes);
-  if constexpr (sizeof(IO) == 4) {
-#pragma unroll
-    for (int k = 0; k < G; ++k) v[k] = __uint_as_float(w[k]);
-  } else if constexpr (G == 1) {
-    v[0] = __uint_as_float(w[0] << 16);
-  } else {
-#pragma unroll
-    for (int k = 0; k < G / 2; ++k) {
-      v[2 * k] = __uint_as_float(w[k] << 16);
-      v[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
-    }
-  }
 }
 
 }  // namespace ssm66

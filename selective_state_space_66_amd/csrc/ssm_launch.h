@@ -39,10 +39,27 @@ struct StepParams {
   int softplus;
 };
 
+struct ConvParams {
+  const void* x;            // (batch, L, dim) io dtype; (batch, dim) for a step
+  const float* w;           // (dim, k): w[c * k + i] multiplies the input i steps back
+  const float* bias;        // nullable (dim)
+  const void* state_in;     // nullable window before the sequence (batch, k - 1, dim)
+  const int32_t* seq_lens;  // nullable (batch)
+  const uint8_t* reset;     // nullable (batch, L)
+  void* out;
+  void* state_out;          // nullable window after the last real token; a step's window (in/out)
+  int64_t batch, L, dim, k;
+  int silu;
+};
+
 // G = states per thread, NG = state groups per channel, G * NG >= N.
 // Supported (G, NG): (4, 4), (2, 8), (1, 16) for up to 16 states, (2, 4) and (1, 4).
 hipError_t launch_scan_fwd(const ScanParams& p, int io_dtype, int G, int NG, bool zoh, bool gate,
                            hipStream_t stream);
+// step = false: the sequence kernel; true: one decoding step.  vec4: dim is a
+// multiple of 4 and the io pointers are aligned to 4 elements.
+hipError_t launch_conv1d(const ConvParams& p, int io_dtype, bool vec4, bool step,
+                         hipStream_t stream);
 hipError_t launch_step(const StepParams& p, int io_dtype, bool zoh, bool gate, hipStream_t stream);
 
 }  // namespace ssm66

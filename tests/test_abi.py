@@ -34,8 +34,8 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared_functions()
-    assert set(names) == {"ssm_scan_fwd", "ssm_scan_fwd_ex", "ssm_step", "ssm_status_string",
-                          "ssm_abi_version"}
+    assert set(names) == {"ssm_scan_fwd", "ssm_scan_fwd_ex", "ssm_step", "ssm_conv1d_fwd",
+                          "ssm_conv1d_step", "ssm_status_string", "ssm_abi_version"}
     raw = ctypes.CDLL(ssm.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), f"{n} not exported"
@@ -125,3 +125,48 @@ def test_python_binding_rejects_cpu_tensors(lib):
     u = torch.zeros(1, 4, 8)
     with pytest.raises(ValueError):
         ssm.scan_fwd(u, u, torch.zeros(8, 16), torch.zeros(1, 4, 16), torch.zeros(1, 4, 16))
+
+
+def _conv(lib, **kw):
+    a = dict(x=FAKE, w=FAKE, bias=None, silu=1, win_in=None, seq_lens=None, reset=None, out=FAKE,
+             win_out=None, batch=2, L=8, dim=64, k=4, io=1, stream=None)
+    a.update(kw)
+    return lib.ssm_conv1d_fwd(a["x"], a["w"], a["bias"], a["silu"], a["win_in"], a["seq_lens"],
+                              a["reset"], a["out"], a["win_out"], a["batch"], a["L"], a["dim"],
+                              a["k"], a["io"], a["stream"])
+
+
+def _conv_step(lib, **kw):
+    a = dict(win=FAKE, x=FAKE, w=FAKE, bias=None, silu=1, out=FAKE, batch=2, dim=64, k=4, io=1,
+             stream=None)
+    a.update(kw)
+    return lib.ssm_conv1d_step(a["win"], a["x"], a["w"], a["bias"], a["silu"], a["out"],
+                               a["batch"], a["dim"], a["k"], a["io"], a["stream"])
+
+
+@pytest.mark.parametrize("call", [_conv, _conv_step])
+def test_conv_invalid_arguments_are_rejected(lib, call):
+    c = _header_constants()
+    assert call(lib, k=0) == c["SSM_ERR_SHAPE"]
+    assert call(lib, k=5) == c["SSM_ERR_SHAPE"]
+    assert call(lib, batch=-1) == c["SSM_ERR_SHAPE"]
+    assert call(lib, dim=-1) == c["SSM_ERR_SHAPE"]
+    assert call(lib, io=3) == c["SSM_ERR_DTYPE"]
+    assert call(lib, silu=2) == c["SSM_ERR_FLAG"]
+    assert call(lib, w=None) == c["SSM_ERR_NULL"]
+    assert call(lib, x=None) == c["SSM_ERR_NULL"]
+    assert call(lib, out=None) == c["SSM_ERR_NULL"]
+    assert call(lib, x=MISALIGNED) == c["SSM_ERR_ALIGN"]
+    assert call(lib, w=MISALIGNED) == c["SSM_ERR_ALIGN"]
+    assert call(lib, batch=0) == c["SSM_OK"]
+    assert call(lib, dim=0) == c["SSM_OK"]
+
+
+def test_conv_specific_checks(lib):
+    c = _header_constants()
+    assert _conv(lib, L=-1) == c["SSM_ERR_SHAPE"]
+    assert _conv(lib, win_out=MISALIGNED) == c["SSM_ERR_ALIGN"]
+    assert _conv(lib, seq_lens=ctypes.c_void_p(0x10002)) == c["SSM_ERR_ALIGN"]
+    assert _conv(lib, batch=70000) == c["SSM_ERR_UNSUPPORTED"]
+    assert _conv(lib, L=64 * 65536) == c["SSM_ERR_UNSUPPORTED"]
+    assert _conv_step(lib, win=None) == c["SSM_ERR_NULL"]
