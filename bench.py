@@ -243,6 +243,8 @@ def time_conv(dev, steps, warmup, nsets=4):
             "kernel_ms": round(fwd_ms, 5),
             "GB/s": round(fwd_b / (fwd_ms * 1e-3) / 1e9, 2),
             "hbm_frac": round(fwd_b / (fwd_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "algorithmic_bytes": fwd_b,
+            "traffic": measured_traffic("conv1d_fwd_conv130m"),
             "step": {"workload": f"ssm_conv1d_step: batch {dcfg.batch}, D {dcfg.dim}, k {dcfg.k}, "
                                  "bf16, SiLU", "us_per_step": round(step_us, 3),
                      "GB/s": round(step_b / (step_us * 1e-6) / 1e9, 2)}}

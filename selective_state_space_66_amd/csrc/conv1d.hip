@@ -9,13 +9,14 @@
 // window holds inputs, not outputs: "Where Mamba implementations go wrong").
 //
 // Both kernels move each input once and each output once; they are bound by
-// HBM.  A thread owns VEC consecutive channels (one 8-byte bf16 or 16-byte
-// fp32 access per token when VEC = 4) and, in the sequence kernel, a run of T
+// HBM.  A thread owns VEC = 4 consecutive channels (one 8-byte bf16 or 16-byte
+// fp32 access per token) and, in the sequence kernel, a run of T
 // tokens: it keeps the last K - 1 inputs of its channels in registers as a
 // sliding window and reads the K - 1 inputs before its run once more (the
-// halo, K - 1 of T + K - 1 loads).  A wave covers 64 * VEC consecutive
-// channels of one token row, so every access is a contiguous 512- or
-// 1024-byte segment.
+// halo, mostly served by L2: the neighbouring run read those rows).  A wave
+// covers 256 consecutive channels of one token row, so every access is a
+// contiguous 512- or 1024-byte segment.  All loads of a thread are issued
+// before the first is used.
 #include "ssm_device.h"
 #include "ssm_launch.h"
 
@@ -23,20 +24,26 @@ namespace ssm66 {
 
 namespace {
 
-constexpr int kConvT = 16;       // tokens per thread (sequence kernel)
+constexpr int kConvT = 8;        // tokens per thread (sequence kernel)
 constexpr int kConvWaves = 4;    // waves per block, along the tokens
 
+// VEC consecutive io elements: Raw is what one access moves (kept raw in
+// registers until used: a bf16 word holds two values), unpack turns it into
+// fp32, store rounds fp32 back (bf16: nearest even).
 template <typename IO, int VEC>
 struct VecIO;
 template <>
 struct VecIO<float, 1> {
-  static __device__ __forceinline__ void load(const float* p, float (&v)[1]) { v[0] = *p; }
+  using Raw = float;
+  static __device__ __forceinline__ Raw load_raw(const float* p) { return *p; }
+  static __device__ __forceinline__ void unpack(Raw r, float (&v)[1]) { v[0] = r; }
   static __device__ __forceinline__ void store(float* p, const float (&v)[1]) { *p = v[0]; }
 };
 template <>
 struct VecIO<float, 4> {
-  static __device__ __forceinline__ void load(const float* p, float (&v)[4]) {
-    const float4 q = *(const float4*)p;
+  using Raw = float4;
+  static __device__ __forceinline__ Raw load_raw(const float* p) { return *(const float4*)p; }
+  static __device__ __forceinline__ void unpack(Raw q, float (&v)[4]) {
     v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
   }
   static __device__ __forceinline__ void store(float* p, const float (&v)[4]) {
@@ -45,8 +52,10 @@ struct VecIO<float, 4> {
 };
 template <>
 struct VecIO<bf16_bits, 1> {
-  static __device__ __forceinline__ void load(const bf16_bits* p, float (&v)[1]) {
-    v[0] = to_f32(*p);
+  using Raw = uint32_t;
+  static __device__ __forceinline__ Raw load_raw(const bf16_bits* p) { return *p; }
+  static __device__ __forceinline__ void unpack(Raw r, float (&v)[1]) {
+    v[0] = __uint_as_float(r << 16);
   }
   static __device__ __forceinline__ void store(bf16_bits* p, const float (&v)[1]) {
     store_io(p, v[0]);
@@ -54,8 +63,9 @@ struct VecIO<bf16_bits, 1> {
 };
 template <>
 struct VecIO<bf16_bits, 4> {
-  static __device__ __forceinline__ void load(const bf16_bits* p, float (&v)[4]) {
-    const uint2 q = *(const uint2*)p;
+  using Raw = uint2;
+  static __device__ __forceinline__ Raw load_raw(const bf16_bits* p) { return *(const uint2*)p; }
+  static __device__ __forceinline__ void unpack(Raw q, float (&v)[4]) {
     v[0] = __uint_as_float(q.x << 16);
     v[1] = __uint_as_float(q.x & 0xffff0000u);
     v[2] = __uint_as_float(q.y << 16);
@@ -68,6 +78,10 @@ struct VecIO<bf16_bits, 4> {
     *(uint2*)p = q;
   }
 };
+template <typename IO, int VEC>
+__device__ __forceinline__ void vload(const IO* p, float (&v)[VEC]) {
+  VecIO<IO, VEC>::unpack(VecIO<IO, VEC>::load_raw(p), v);
+}
 
 __device__ __forceinline__ float conv_act(float v, bool silu) { return silu ? silu_f(v) : v; }
 
@@ -91,16 +105,57 @@ __global__ __launch_bounds__(64 * kConvWaves) void conv1d_fwd_kernel(
     len = sl < 0 ? 0 : (sl < L ? sl : L);
   }
 
+  // optional inputs are read through a valid stand-in pointer and masked, so
+  // that no load sits behind a branch (a branch around a load makes the
+  // compiler wait for it on the spot)
+  const float* bias_src = bias ? bias : w;
   float wt[VEC][K], bs[VEC];
 #pragma unroll
   for (int v = 0; v < VEC; ++v) {
 #pragma unroll
     for (int i = 0; i < K; ++i) wt[v][i] = w[(c0 + v) * K + i];
-    bs[v] = bias ? bias[c0 + v] : 0.0f;
+    const float bv = bias_src[c0 + v];
+    bs[v] = bias ? bv : 0.0f;
+  }
+
+  // ---- every load first, unconditionally, through addresses clamped into the
+  // tensors (values of padded or out-of-range positions are then masked), so
+  // that all of them are in flight together
+  if (L == 0) {  // no tokens: the window carries over (thread t0 == 0 only)
+    float win[K > 1 ? K - 1 : 1][VEC];
+#pragma unroll
+    for (int j = 0; j < K - 1; ++j) {
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) win[j][v] = 0.0f;
+      if (state_in) vload<IO, VEC>(state_in + (b * (K - 1) + j) * dim + c0, win[j]);
+      if (state_out) V::store(state_out + (b * (K - 1) + j) * dim + c0, win[j]);
+    }
+    return;
+  }
+  auto row = [&](int64_t t) -> int64_t { return t < 0 ? 0 : (t < L ? t : L - 1); };
+  // reset flags: x holds at least batch * L bytes, so it stands in when reset is NULL
+  const uint8_t* rsrc = reset ? reset : (const uint8_t*)x;
+  const int rmask = reset ? 0xff : 0;
+  typename V::Raw xh[K > 1 ? K - 1 : 1];  // xh[q - 1]: the input at t0 - q
+  int rh[K > 1 ? K - 1 : 1];
+#pragma unroll
+  for (int q = 1; q < K; ++q) {
+    const int64_t s = t0 - q;
+    const IO* src = x + (b * L + row(s)) * dim + c0;
+    if (s < 0 && state_in) src = state_in + (b * (K - 1) + (K - 1 + s)) * dim + c0;
+    xh[q - 1] = V::load_raw(src);
+    rh[q - 1] = (int)rsrc[b * L + row(s)] & rmask;
+  }
+  typename V::Raw xr[kConvT];
+  int rf[kConvT];
+#pragma unroll
+  for (int i = 0; i < kConvT; ++i) {
+    xr[i] = V::load_raw(x + (b * L + row(t0 + i)) * dim + c0);
+    rf[i] = (int)rsrc[b * L + row(t0 + i)] & rmask;
   }
 
   // ---- the window before t0: replay inputs t0 - (K - 1) .. t0 - 1 (negative
-  // positions come from state_in), clearing at document starts
+  // positions from state_in, or zero), clearing at document starts
   float win[K > 1 ? K - 1 : 1][VEC];
 #pragma unroll
   for (int j = 0; j < K - 1; ++j)
@@ -110,28 +165,17 @@ __global__ __launch_bounds__(64 * kConvWaves) void conv1d_fwd_kernel(
   for (int q = K - 1; q >= 1; --q) {
     const int64_t s = t0 - q;
     // positions at or past len occur only when len < t0 (all outputs zero)
-    const bool use = s < 0 || s < len;
-    float in[VEC];
-#pragma unroll
-    for (int v = 0; v < VEC; ++v) in[v] = 0.0f;
-    if (s >= 0 && use) {
-      if (reset && reset[b * L + s]) {
-#pragma unroll
-        for (int j = 0; j < K - 1; ++j)
-#pragma unroll
-          for (int v = 0; v < VEC; ++v) win[j][v] = 0.0f;
-      }
-      V::load(x + (b * L + s) * dim + c0, in);
-    } else if (s < 0 && state_in) {
-      V::load(state_in + (b * (K - 1) + (K - 1 + s)) * dim + c0, in);
-    }
-    if (use) {
+    if (s < 0 || s < len) {
+      const bool clear = s >= 0 && rh[q - 1] != 0;
+      const bool zero = s < 0 && !state_in;
+      float xv[VEC];
+      V::unpack(xh[q - 1], xv);
 #pragma unroll
       for (int j = K - 2; j >= 1; --j)
 #pragma unroll
-        for (int v = 0; v < VEC; ++v) win[j][v] = win[j - 1][v];
+        for (int v = 0; v < VEC; ++v) win[j][v] = clear ? 0.0f : win[j - 1][v];
 #pragma unroll
-      for (int v = 0; v < VEC; ++v) win[0][v] = in[v];
+      for (int v = 0; v < VEC; ++v) win[0][v] = zero ? 0.0f : xv[v];
     }
   }
 
@@ -147,47 +191,36 @@ __global__ __launch_bounds__(64 * kConvWaves) void conv1d_fwd_kernel(
   };
   if (len == 0 && t0 == 0) write_state();
 
-  // ---- this thread's tokens: all loads first, then the sliding window
+  // ---- this thread's tokens, through the sliding window
   const int nt = (int)(L - t0 < kConvT ? L - t0 : kConvT);
-  float xin[kConvT][VEC];
-#pragma unroll
-  for (int i = 0; i < kConvT; ++i) {
-    if (i < nt && t0 + i < len) V::load(x + (b * L + t0 + i) * dim + c0, xin[i]);
-  }
-  const bool has_reset = reset != nullptr;
 #pragma unroll
   for (int i = 0; i < kConvT; ++i) {
     if (i < nt) {
-    const int64_t t = t0 + i;
-    float o[VEC];
-    if (t >= len) {
-#pragma unroll
-      for (int v = 0; v < VEC; ++v) o[v] = 0.0f;  // padding outputs 0
-    } else {
-      if (has_reset && reset[b * L + t]) {
-#pragma unroll
-        for (int j = 0; j < K - 1; ++j)
-#pragma unroll
-          for (int v = 0; v < VEC; ++v) win[j][v] = 0.0f;
-      }
+      const int64_t t = t0 + i;
+      const bool live = t < len;
+      const bool clear = live && rf[i] != 0;  // a document starts at t
+      float xin[VEC];
+      V::unpack(xr[i], xin);
+      float o[VEC];
 #pragma unroll
       for (int v = 0; v < VEC; ++v) {
-        float acc = fmaf(wt[v][0], xin[i][v], bs[v]);
+        float acc = fmaf(wt[v][0], xin[v], bs[v]);
 #pragma unroll
-        for (int j = 1; j < K; ++j) acc = fmaf(wt[v][j], win[j - 1][v], acc);
-        o[v] = conv_act(acc, silu);
+        for (int j = 1; j < K; ++j) acc = fmaf(wt[v][j], clear ? 0.0f : win[j - 1][v], acc);
+        o[v] = live ? conv_act(acc, silu) : 0.0f;  // padding outputs 0
       }
+      if (live) {
 #pragma unroll
-      for (int j = K - 2; j >= 1; --j)
+        for (int j = K - 2; j >= 1; --j)
 #pragma unroll
-        for (int v = 0; v < VEC; ++v) win[j][v] = win[j - 1][v];
-      if constexpr (K > 1) {
+          for (int v = 0; v < VEC; ++v) win[j][v] = clear ? 0.0f : win[j - 1][v];
+        if constexpr (K > 1) {
 #pragma unroll
-        for (int v = 0; v < VEC; ++v) win[0][v] = xin[i][v];
+          for (int v = 0; v < VEC; ++v) win[0][v] = xin[v];
+        }
+        if (t == len - 1) write_state();
       }
-      if (t == len - 1) write_state();
-    }
-    V::store(out + (b * L + t) * dim + c0, o);
+      V::store(out + (b * L + t) * dim + c0, o);
     }
   }
 }
@@ -205,9 +238,9 @@ __global__ __launch_bounds__(256) void conv1d_step_kernel(
   const int64_t b = gid / nvec;
   const int64_t c0 = (gid - b * nvec) * VEC;
   float xt[VEC], win[K > 1 ? K - 1 : 1][VEC];  // win[j]: j = 0 oldest
-  V::load(x + b * dim + c0, xt);
+  vload<IO, VEC>(x + b * dim + c0, xt);
 #pragma unroll
-  for (int j = 0; j < K - 1; ++j) V::load(window + (b * (K - 1) + j) * dim + c0, win[j]);
+  for (int j = 0; j < K - 1; ++j) vload<IO, VEC>(window + (b * (K - 1) + j) * dim + c0, win[j]);
   float o[VEC];
 #pragma unroll
   for (int v = 0; v < VEC; ++v) {
@@ -256,6 +289,11 @@ hipError_t by_width(const ConvParams& p, bool step, hipStream_t stream) {
   }
 }
 
+// Four channels per thread where the channels and pointers allow (8-byte bf16
+// or 16-byte fp32 accesses); else one.  Measured on the Mamba-130M layer's
+// convolution: 8 tokens x 4 channels per thread, 4 waves per block, beats 16
+// or 32 tokens (fewer waves in flight) and 16-byte bf16 accesses (more
+// registers, half the occupancy).
 template <typename IO>
 hipError_t by_vec(const ConvParams& p, bool vec4, bool step, hipStream_t stream) {
   return vec4 ? by_width<IO, 4>(p, step, stream) : by_width<IO, 1>(p, step, stream);
