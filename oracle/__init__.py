@@ -19,7 +19,9 @@ IIR filter), a brute-force mixing-matrix evaluation and invariants.  The
 initial state, the sequence lengths and the document resets of ``scan_fwd`` are
 pinned against independent routes to the same result: scanning the truncated
 or split sequence, and the first page's remark that one very large step resets
-the state.
+the state.  The backward pass (``scan_bwd``) is pinned by central finite
+differences of the forward; the convolution by numpy.convolve and the impulse
+response.
 """
 import ctypes
 import os
@@ -66,6 +68,9 @@ def _load():
     lib.oracle_step.restype = None
     lib.oracle_step.argtypes = [ctypes.c_void_p] * 9 + [ctypes.c_int, ctypes.c_int,
                                                         ctypes.c_void_p] + [ctypes.c_int64] * 3
+    lib.oracle_scan_bwd.restype = None
+    lib.oracle_scan_bwd.argtypes = [ctypes.c_void_p] * 9 + [ctypes.c_int, ctypes.c_int] + \
+        [ctypes.c_void_p] * 11 + [ctypes.c_int64] * 4
     lib.oracle_conv1d_fwd.restype = None
     lib.oracle_conv1d_fwd.argtypes = [ctypes.c_void_p] * 6 + [ctypes.c_int, ctypes.c_void_p,
                                                               ctypes.c_void_p] + [ctypes.c_int64] * 4
@@ -237,3 +242,33 @@ def conv1d_step(window, x, weight, bias=None, silu=True):
     _load().oracle_conv1d_step(_ptr(win), _ptr(x), _ptr(w), _ptr(bias), int(bool(silu)),
                                _ptr(out), batch, dim, k)
     return out, win
+
+
+def scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, softplus=True,
+             dt_mode="zoh", h0=None, dlast=None):
+    """Gradients of the fp64 scan: given dy (batch, L, dim) and optionally dlast
+    (batch, dim, N), the gradient of last_state, returns a dict with du, ddelta
+    (of the raw delta), dA, dB, dC and, where their inputs are given, dD, dz,
+    ddelta_bias and dh0 -- all float64.  Every state is kept (small cases only).
+    """
+    u, delta, A, B, C = _f64(u), _f64(delta), _f64(A), _f64(B), _f64(C)
+    dy, D, z, delta_bias, h0, dlast = _f64(dy), _f64(D), _f64(z), _f64(delta_bias), _f64(h0), \
+        _f64(dlast)
+    batch, L, dim = u.shape
+    N = A.shape[1]
+    assert dy.shape == u.shape and B.shape == (batch, L, N) and C.shape == (batch, L, N)
+    assert dlast is None or dlast.shape == (batch, dim, N)
+    assert h0 is None or h0.shape == (batch, dim, N)
+    out = dict(du=np.empty_like(u), ddelta=np.empty_like(u), dA=np.empty((dim, N)),
+               dB=np.empty((batch, L, N)), dC=np.empty((batch, L, N)))
+    out["dD"] = np.empty(dim) if D is not None else None
+    out["dz"] = np.empty_like(u) if z is not None else None
+    out["ddelta_bias"] = np.empty(dim) if delta_bias is not None else None
+    out["dh0"] = np.empty((batch, dim, N)) if h0 is not None else None
+    _load().oracle_scan_bwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                            _ptr(delta_bias), _ptr(h0), int(bool(softplus)), _MODES[dt_mode],
+                            _ptr(dy), _ptr(dlast), _ptr(out["du"]), _ptr(out["ddelta"]),
+                            _ptr(out["dA"]), _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dD"]),
+                            _ptr(out["dz"]), _ptr(out["ddelta_bias"]), _ptr(out["dh0"]),
+                            batch, L, dim, N)
+    return out

@@ -313,3 +313,139 @@ void oracle_conv1d_step(double* window, const double* x, const double* w, const 
     }
   }
 }
+
+/* ------------------------------------------------------------------------
+ * Backward pass of the scan.
+ *
+ * The pages fix what it must compute, not how: gradients of the forward
+ * above, with the states recomputed from the inputs rather than stored ("Why
+ * the scan must be fused": the backward pass reloads x, Delta, B, C and
+ * recomputes the states; "the backward pass of a linear recurrence is itself
+ * a linear recurrence run in reverse").  This oracle keeps every state (it is
+ * only run on small cases) and runs that reverse recurrence in the plainest
+ * form, derived here by the chain rule:
+ *
+ *   forward:  h_t = abar_t h_{t-1} + bbar_t u_t,   s_t = C_t . h_t + D u_t,
+ *             y_t = s_t * silu(z_t) (or s_t),      abar = exp(Delta A),
+ *             bbar = Delta B phi(Delta A) (ZOH, phi(k) = (e^k - 1)/k) or Delta B
+ *   given dy (and the gradient dlast of last_state = h_{L-1}):
+ *     ds_t = dy_t silu(z_t),   dz_t = dy_t s_t silu'(z_t)
+ *     g_t  = ds_t C_t + abar_{t+1} g_{t+1},  g_{L-1} = ds_{L-1} C_{L-1} + dlast
+ *            (g_t = dLoss/dh_t through every later use of h_t)
+ *     dabar = g_t h_{t-1},  dbbar = g_t u_t
+ *     dC_tn = sum_c ds_t h_tn,   du_t = sum_n g_tn bbar_tn + ds_t D
+ *     dD    = sum_t ds_t u_t
+ *     through kappa = Delta A (abar and phi depend on A and Delta only via
+ *     kappa, and bbar carries one more factor Delta B):
+ *       dDelta_t = sum_n [dabar A abar + dbbar B (phi + kappa phi')]
+ *                = sum_n [dabar A abar + dbbar abar B]        (ZOH)
+ *                = sum_n [dabar A abar + dbbar B]             (Euler)
+ *       dA_n     = sum_t [dabar Delta abar + dbbar B Delta^2 phi'(kappa)]  (ZOH)
+ *                = sum_t  dabar Delta abar                                 (Euler)
+ *       dB_tn    = sum_c dbbar Delta phi (ZOH) or dbbar Delta (Euler)
+ *     draw_t = dDelta_t sigma(v_t) with softplus (the derivative of softplus),
+ *              dDelta_t without;  dbias = sum_t draw_t
+ *     dh0 = abar_0 g_0.
+ * phi' is taken from its series below |kappa| = 0.1 and from
+ * (kappa e^kappa - expm1(kappa)) / kappa^2 above it.
+ * ------------------------------------------------------------------------ */
+
+static double phi_prime(double k) {
+  if (fabs(k) < 0.1) {
+    /* sum_{j>=1} j k^{j-1} / (j+1)! */
+    double term_f = 1.0, s = 0.0, kp = 1.0;
+    for (int j = 1; j <= 12; ++j) {
+      term_f *= (double)(j + 1); /* (j+1)! */
+      s += (double)j * kp / term_f;
+      kp *= k;
+    }
+    return s;
+  }
+  return (k * exp(k) - expm1(k)) / (k * k);
+}
+
+void oracle_scan_bwd(const double* u, const double* delta, const double* A, const double* B,
+                     const double* C, const double* D, const double* z,
+                     const double* delta_bias, const double* h0, int softplus, int dt_mode,
+                     const double* dy, const double* dlast, double* du, double* ddelta,
+                     double* dA, double* dB, double* dC, double* dD, double* dz,
+                     double* ddelta_bias, double* dh0, int64_t batch, int64_t L, int64_t dim,
+                     int64_t N) {
+  /* outputs accumulated over channels or over (batch, time) start at zero */
+  for (int64_t i = 0; i < dim * N; ++i) dA[i] = 0.0;
+  for (int64_t i = 0; i < batch * L * N; ++i) dB[i] = dC[i] = 0.0;
+  for (int64_t c = 0; c < dim; ++c) {
+    if (dD) dD[c] = 0.0;
+    if (ddelta_bias) ddelta_bias[c] = 0.0;
+  }
+  double* hs = (double*)malloc(sizeof(double) * (size_t)((L + 1) * N)); /* h_{-1} .. h_{L-1} */
+  double* g = (double*)malloc(sizeof(double) * (size_t)N);
+  for (int64_t b = 0; b < batch; ++b) {
+    for (int64_t c = 0; c < dim; ++c) {
+      const double bias = delta_bias ? delta_bias[c] : 0.0;
+      const double dskip = D ? D[c] : 0.0;
+      /* forward, keeping every state: hs[(t + 1) * N + n] = h_t */
+      for (int64_t n = 0; n < N; ++n) hs[n] = h0 ? h0[(b * dim + c) * N + n] : 0.0;
+      for (int64_t t = 0; t < L; ++t) {
+        const int64_t xi = (b * L + t) * dim + c;
+        const double dt = step_size(delta[xi], bias, softplus);
+        for (int64_t n = 0; n < N; ++n) {
+          double abar, bbar;
+          oracle_discretize(dt, A[c * N + n], B[(b * L + t) * N + n], dt_mode, &abar, &bbar);
+          hs[(t + 1) * N + n] = abar * hs[t * N + n] + bbar * u[xi];
+        }
+      }
+      /* reverse */
+      for (int64_t n = 0; n < N; ++n) g[n] = dlast ? dlast[(b * dim + c) * N + n] : 0.0;
+      for (int64_t t = L - 1; t >= 0; --t) {
+        const int64_t xi = (b * L + t) * dim + c;
+        const double x = u[xi];
+        const double v = delta[xi] + bias;
+        const double dt = softplus ? oracle_softplus(v) : v;
+        const double* Bt = B + (b * L + t) * N;
+        const double* Ct = C + (b * L + t) * N;
+        const double* ht = hs + (t + 1) * N;
+        const double* hp = hs + t * N;
+        double s = dskip * x;
+        for (int64_t n = 0; n < N; ++n) s += Ct[n] * ht[n];
+        double ds = dy[xi];
+        if (z) {
+          const double zz = z[xi], sg = oracle_sigmoid(zz);
+          ds = dy[xi] * zz * sg;
+          if (dz) dz[xi] = dy[xi] * s * sg * (1.0 + zz * (1.0 - sg));
+        }
+        double ddt = 0.0, dx = ds * dskip;
+        for (int64_t n = 0; n < N; ++n) {
+          const double a = A[c * N + n], kap = dt * a;
+          double abar, bbar;
+          oracle_discretize(dt, a, Bt[n], dt_mode, &abar, &bbar);
+          g[n] += ds * Ct[n];
+          dC[(b * L + t) * N + n] += ds * ht[n];
+          const double dabar = g[n] * hp[n];
+          const double dbbar = g[n] * x;
+          dx += g[n] * bbar;
+          if (dt_mode == ORACLE_DT_ZOH) {
+            const double phi = (a != 0.0) ? expm1(kap) / kap : 1.0;
+            ddt += dabar * a * abar + dbbar * abar * Bt[n];
+            dA[c * N + n] += dabar * dt * abar + dbbar * Bt[n] * dt * dt * phi_prime(kap);
+            dB[(b * L + t) * N + n] += dbbar * dt * phi;
+          } else {
+            ddt += dabar * a * abar + dbbar * Bt[n];
+            dA[c * N + n] += dabar * dt * abar;
+            dB[(b * L + t) * N + n] += dbbar * dt;
+          }
+          g[n] *= abar; /* carry to t - 1 */
+        }
+        du[xi] = dx;
+        if (dD) dD[c] += ds * x;
+        const double dv = softplus ? ddt * oracle_sigmoid(v) : ddt;
+        ddelta[xi] = dv;
+        if (ddelta_bias) ddelta_bias[c] += dv;
+      }
+      if (dh0)
+        for (int64_t n = 0; n < N; ++n) dh0[(b * dim + c) * N + n] = g[n];
+    }
+  }
+  free(hs);
+  free(g);
+}

@@ -50,6 +50,18 @@ MUTATIONS = {
                                  "          const int64_t s = len - 1 - j;"),
     "conv_reset_ignored": ("        if (reset && reset[b * L + t]) start = t;", "        (void)reset;"),
     "conv_bias_dropped": ("        double pre = bias ? bias[c] : 0.0;", "        double pre = 0.0;"),
+    "bwd_no_carry": ("          g[n] *= abar; /* carry to t - 1 */", "          (void)0;"),
+    "bwd_softplus_derivative": ("        const double dv = softplus ? ddt * oracle_sigmoid(v) : ddt;",
+                                "        const double dv = softplus ? ddt * oracle_sigmoid(-v) : ddt;"),
+    "bwd_zoh_ddelta_as_euler": ("            ddt += dabar * a * abar + dbbar * abar * Bt[n];",
+                                "            ddt += dabar * a * abar + dbbar * Bt[n];"),
+    "bwd_dA_drops_phi_prime": ("            dA[c * N + n] += dabar * dt * abar + dbbar * Bt[n] * dt * dt * phi_prime(kap);",
+                               "            dA[c * N + n] += dabar * dt * abar;"),
+    "bwd_dC_uses_old_state": ("          dC[(b * L + t) * N + n] += ds * ht[n];",
+                              "          dC[(b * L + t) * N + n] += ds * hp[n];"),
+    "bwd_silu_derivative": ("          if (dz) dz[xi] = dy[xi] * s * sg * (1.0 + zz * (1.0 - sg));",
+                            "          if (dz) dz[xi] = dy[xi] * s * sg;"),
+    "bwd_phi_prime_series": ("      s += (double)j * kp / term_f;", "      s += kp / term_f;"),
 }
 
 
@@ -67,6 +79,7 @@ def test_planted_mistake_is_caught(name, tmp_path):
     env = dict(os.environ, SSM_ORACLE_LIB=str(lib))
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
                         os.path.join(ROOT, "tests", "test_oracle_pins.py"),
-                        os.path.join(ROOT, "tests", "test_oracle_conv_pins.py")],
+                        os.path.join(ROOT, "tests", "test_oracle_conv_pins.py"),
+                        os.path.join(ROOT, "tests", "test_oracle_bwd_pins.py")],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
     assert r.returncode != 0, f"mutation {name} survived the pins:\n{r.stdout[-2000:]}"
