@@ -179,6 +179,36 @@ def time_decode(cfg, nsteps, dev, npool=8):
     return wall_s, e0.elapsed_time(e1) / nsteps
 
 
+def time_bwd(sets, steps, warmup, dev):
+    """ssm_scan_bwd on the Mamba-130M layer (ZOH, gate, D, bias), rotating the
+    input sets, one dy per set; one workspace reused."""
+    import torch
+    import selective_state_space_66_amd as ssm
+    s0 = sets[0]
+    batch, L, dim = s0["u"].shape
+    N = s0["A"].shape[1]
+    ws = torch.empty(ssm.scan_bwd_workspace_size(batch, L, dim, N), dtype=torch.uint8, device=dev)
+    gen = torch.Generator(device="cpu").manual_seed(12)
+    dys = [torch.randn((batch, L, dim), generator=gen).to(torch.bfloat16).to(dev) for _ in sets]
+
+    def launch(i):
+        s = sets[i % len(sets)]
+        ssm.scan_bwd(s["u"], s["delta"], s["A"], s["B"], s["C"], dys[i % len(sets)], D=s["D"],
+                     z=s["z"], delta_bias=s["delta_bias"], workspace=ws)
+
+    for i in range(warmup):
+        launch(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record()
+        launch(warmup + i)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in ev])), ws.numel()
+
+
 def conv_bytes(b, L, D, k, io_bytes):
     """Algorithmic bytes of the sequence convolution: x read and out written once,
     the decoding window written, weights and bias read."""
@@ -354,6 +384,10 @@ def main():
     x_updates = sum(lens) * cfg.dim * cfg.N
     log(f"[bench] extended: wall {x_wall:.4f} ms/step, kernel {x_kern:.4f} ms")
 
+    log("[bench] timing the backward pass")
+    b_ms, b_ws = time_bwd(sets, max(5, args.steps // 5), 2, dev)
+    log(f"[bench] backward: {b_ms:.4f} ms per call (workspace {b_ws / 1e6:.1f} MB)")
+
     log("[bench] timing the convolution")
     del sets
     torch.cuda.empty_cache()
@@ -421,6 +455,11 @@ def main():
                     "GB/s": round(x_bytes / (x_kern * 1e-3) / 1e9, 2),
                     "alu_frac": round(FLOPS_PER_UPDATE * x_updates / (x_kern * 1e-3) / 1e12
                                       / ALU_PEAK_TFLOPS, 4)},
+        "bwd": {"workload": "ssm_scan_bwd on the same layer, ZOH, gate, D, bias: du, d delta, dz, "
+                            "dA, dB, dC, dD, d bias (states recomputed from the inputs)",
+                "ms": round(b_ms, 4), "x_forward": round(b_ms / kern_ms, 2),
+                "updates_per_s": float(f"{elems * cfg.N / (b_ms * 1e-3):.4g}"),
+                "workspace_MB": round(b_ws / 1e6, 1)},
         "conv": conv,
         "decode": {"workload": "ssm_step: batch 256, D 5120, N 16, bf16 io, fp32 state, gate, ZOH",
                    "steps": args.decode_steps,

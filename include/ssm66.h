@@ -1,7 +1,7 @@
 /*
  * ssm66.h -- C ABI of the MI355X (gfx950) selective-scan library.
  *
- * Five entry points, all defined on "Mamba and selective state spaces"
+ * Six operations, all defined on "Mamba and selective state spaces"
  * (zerotofrontier.app/ssm/mamba):
  *
  *   ssm_scan_fwd : the selective state-space layer (S6) over whole sequences --
@@ -21,6 +21,11 @@
  *                  implementations go wrong"), and document starts where the
  *                  state is forgotten ("What each parameter does": packed
  *                  documents should not see each other).
+ *   ssm_scan_bwd : gradients of ssm_scan_fwd (with h0 and the gradient of
+ *                  last_state), recomputing the states from the inputs instead
+ *                  of storing them ("Why the scan must be fused": the backward
+ *                  pass reloads x, Delta, B, C and recomputes the states; the
+ *                  backward of a linear recurrence is a reverse recurrence).
  *   ssm_step     : one token of that layer against a state cache, updated in
  *                  place ("Decoding with a constant-size cache").
  *   ssm_conv1d_fwd, ssm_conv1d_step : the short causal depthwise convolution
@@ -61,13 +66,14 @@
 #ifndef SSM66_H
 #define SSM66_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 3
+#define SSM_ABI_VERSION 4
 
 /* status codes */
 #define SSM_OK 0
@@ -124,6 +130,40 @@ int ssm_scan_fwd_ex(const void* u, const void* delta, const float* A, const void
                     int softplus, int dt_mode, const float* h0, const int32_t* seq_lens,
                     const uint8_t* reset, void* y, float* last_state, int64_t batch,
                     int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype, void* stream);
+
+/*
+ * Bytes of device workspace ssm_scan_bwd needs for these sizes (0 for invalid
+ * sizes): per-chunk state checkpoints (batch x ceil(seqlen/16) x dim x dstate
+ * floats) and the partial sums that are added in a fixed order at the end.
+ */
+size_t ssm_scan_bwd_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate);
+
+/*
+ * Backward pass of ssm_scan_fwd / ssm_scan_fwd_ex without lengths or resets.
+ * Inputs: the forward's inputs (u, delta, A, B, C, D, z, delta_bias, softplus,
+ * dt_mode, h0 -- D, z, delta_bias, h0 nullable), dy (batch, seqlen, dim) io
+ * dtype, and dlast_state (batch, dim, dstate) float32, the gradient of
+ * last_state (NULL = zero).
+ * Outputs (overwritten, not accumulated into):
+ *   du, ddelta (gradient of the RAW delta), dz : (batch, seqlen, dim) io dtype
+ *     (dz is required when z is given and ignored otherwise);
+ *   dB, dC : (batch, seqlen, dstate) io dtype;
+ *   dA : (dim, dstate) float32;  dD, ddelta_bias : (dim) float32, or NULL;
+ *   dh0 : (batch, dim, dstate) float32, or NULL.
+ * workspace: device memory of at least ssm_scan_bwd_workspace_size(...) bytes,
+ * 256-byte aligned, owned by the caller, contents not needed before or after.
+ * Sums over channels (dB, dC) and over batch entries (dA, dD, ddelta_bias) are
+ * added in a fixed order: repeated calls give identical bits.  Calls that share
+ * a workspace must not overlap.  Returns SSM_OK or an error status
+ * (SSM_ERR_SHAPE also when workspace_bytes is too small).
+ */
+int ssm_scan_bwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                 const float* D, const void* z, const float* delta_bias, int softplus,
+                 int dt_mode, const float* h0, const void* dy, const float* dlast_state,
+                 void* du, void* ddelta, float* dA, void* dB, void* dC, float* dD, void* dz,
+                 float* ddelta_bias, float* dh0, void* workspace, size_t workspace_bytes,
+                 int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype,
+                 void* stream);
 
 /*
  * One decode step against the state cache `state` (batch, dim, dstate),

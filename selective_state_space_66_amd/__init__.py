@@ -11,6 +11,8 @@ missing, every call raises.
                              h0=None, seq_lens=None, reset=None)
     y = step(state, u, delta, A, B, C, D=None, z=None, delta_bias=None,
              softplus=True, dt_mode="zoh")     # state updated in place
+    grads = scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None,
+                     softplus=True, dt_mode="zoh", h0=None, dlast=None)
     out, window = conv1d_fwd(x, weight, bias=None, silu=True, window_in=None,
                              seq_lens=None, reset=None)
     out = conv1d_step(window, x, weight, bias=None, silu=True)   # window updated in place
@@ -47,6 +49,11 @@ def load_library():
     lib.ssm_scan_fwd.argtypes = [vp] * 8 + [ci, ci, vp, vp, i64, i64, i64, i64, ci, vp]
     lib.ssm_scan_fwd_ex.restype = ci
     lib.ssm_scan_fwd_ex.argtypes = [vp] * 8 + [ci, ci] + [vp] * 5 + [i64, i64, i64, i64, ci, vp]
+    lib.ssm_scan_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.ssm_scan_bwd_workspace_size.argtypes = [i64] * 4
+    lib.ssm_scan_bwd.restype = ci
+    lib.ssm_scan_bwd.argtypes = [vp] * 8 + [ci, ci] + [vp] * 13 + [ctypes.c_size_t] + \
+        [i64] * 4 + [ci, vp]
     lib.ssm_conv1d_fwd.restype = ci
     lib.ssm_conv1d_fwd.argtypes = [vp] * 3 + [ci] + [vp] * 5 + [i64] * 4 + [ci, vp]
     lib.ssm_conv1d_step.restype = ci
@@ -263,3 +270,60 @@ def conv1d_step(window, x, weight, bias=None, silu=True, out=None):
     if st != 0:
         raise SsmError(st, "ssm_conv1d_step")
     return out
+
+
+def scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, softplus=True,
+             dt_mode="zoh", h0=None, dlast=None, workspace=None):
+    """Gradients of scan_fwd on the GPU (states recomputed, not stored).
+
+    dy: like u; dlast: optional (batch, dim, N) float32, the gradient of last_state.
+    Returns a dict: du, ddelta (of the raw delta), dB, dC (io dtype), dA (float32),
+    and, where their inputs were given, dz (io dtype), dD, ddelta_bias, dh0 (float32).
+    workspace: optional uint8 device tensor of at least scan_bwd_workspace_size() bytes.
+    """
+    import torch
+    lib = load_library()
+    batch, L, dim = u.shape
+    N = A.shape[-1]
+    dev = u.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on the GPU")
+    io = u.dtype
+    _io_code(u)
+    for t, name, shape in ((u, "u", (batch, L, dim)), (delta, "delta", (batch, L, dim)),
+                           (B, "B", (batch, L, N)), (C, "C", (batch, L, N)),
+                           (dy, "dy", (batch, L, dim)), (z, "z", (batch, L, dim))):
+        _check(t, name, shape, io, dev)
+    _check(A, "A", (dim, N), torch.float32, dev)
+    _check(D, "D", (dim,), torch.float32, dev)
+    _check(delta_bias, "delta_bias", (dim,), torch.float32, dev)
+    _check(h0, "h0", (batch, dim, N), torch.float32, dev)
+    _check(dlast, "dlast", (batch, dim, N), torch.float32, dev)
+    need = scan_bwd_workspace_size(batch, L, dim, N)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    if workspace.numel() < need:
+        raise ValueError(f"workspace: need {need} bytes, got {workspace.numel()}")
+    f32 = dict(dtype=torch.float32, device=dev)
+    g = dict(du=torch.empty_like(u), ddelta=torch.empty_like(u),
+             dB=torch.empty((batch, L, N), dtype=io, device=dev),
+             dC=torch.empty((batch, L, N), dtype=io, device=dev),
+             dA=torch.empty((dim, N), **f32),
+             dz=torch.empty_like(u) if z is not None else None,
+             dD=torch.empty((dim,), **f32) if D is not None else None,
+             ddelta_bias=torch.empty((dim,), **f32) if delta_bias is not None else None,
+             dh0=torch.empty((batch, dim, N), **f32) if h0 is not None else None)
+    st = lib.ssm_scan_bwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                          _ptr(delta_bias), int(bool(softplus)), _MODES[dt_mode], _ptr(h0),
+                          _ptr(dy), _ptr(dlast), _ptr(g["du"]), _ptr(g["ddelta"]), _ptr(g["dA"]),
+                          _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dD"]), _ptr(g["dz"]),
+                          _ptr(g["ddelta_bias"]), _ptr(g["dh0"]), _ptr(workspace),
+                          workspace.numel(), batch, L, dim, N, _io_code(u), _stream(dev))
+    if st != 0:
+        raise SsmError(st, "ssm_scan_bwd")
+    return g
+
+
+def scan_bwd_workspace_size(batch, L, dim, N):
+    """Bytes of workspace ssm_scan_bwd needs for these sizes."""
+    return int(load_library().ssm_scan_bwd_workspace_size(batch, L, dim, N))

@@ -1,0 +1,497 @@
+// scan_bwd.hip -- backward pass of the fused selective scan for gfx950.
+//
+// Gradients of the scan in scan_fwd.hip with respect to u, the raw delta, A,
+// B, C, D, z, the delta bias and h0, given dy and the gradient of last_state.
+// "Mamba and selective state spaces" (zerotofrontier.app/ssm/mamba), "Why the
+// scan must be fused": the backward pass stores no states; it reloads the
+// inputs, recomputes the states on chip, and runs the reverse recurrence
+// (the backward pass of a linear recurrence is a linear recurrence run
+// backwards).  With ds_t = dy_t silu(z_t) and the adjoint
+//   g_t = ds_t C_t + abar_{t+1} g_{t+1}   (g = dLoss/dh_t),
+// the per-update gradients are dabar = g h_{t-1} and dbbar = g u_t, and
+// Delta and A are reached through kappa = Delta A (ZOH bbar = Delta B phi(kappa),
+// phi(k) = (e^k - 1)/k; exponential-Euler bbar = Delta B).
+//
+// Decomposition (as the forward): a block owns one batch entry and 16
+// channels, its threads are (channel, state group) pairs holding G states.
+// Pass 1 runs the states forward through the whole sequence and writes the
+// state at every chunk start (TC = 16 tokens) to the workspace.  Pass 2 walks
+// the chunks backwards: it recomputes the chunk's states, abar and phi from
+// its checkpoint into registers (and the pre-gate output s, for dz), then runs
+// the adjoint backwards through the chunk.  Sums over the states of one
+// (token, channel) -- dDelta, du, s -- go through LDS across the state groups;
+// sums over the channels of one (token, state) -- dB, dC -- go through LDS
+// across the block's channels and leave as one partial per channel tile.  A
+// second kernel adds the partials (channel tiles for dB, dC; batch entries for
+// dA, dD, d bias) in a fixed order: the result does not depend on timing.
+#include <type_traits>
+
+#include "ssm_device.h"
+#include "ssm_launch.h"
+
+namespace ssm66 {
+
+namespace {
+
+template <int G_, int NG_>
+struct BShape {
+  static constexpr int G = G_;
+  static constexpr int NG = NG_;
+  static constexpr int NPAD = G * NG;
+  static constexpr int CW = 16;                 // channels per block
+  static constexpr int THREADS = CW * NG;
+  static constexpr int TC = 16;                 // tokens per chunk (states kept in registers)
+  static constexpr int RPT = TC / NG;           // tokens each thread prepares and finishes
+  static constexpr int HALF = 8;                // tokens per dB / dC reduction round
+  static constexpr int BCN = TC * NPAD;         // B (and C) elements of a chunk
+  static constexpr int PST = TC * CW + 16;      // partial row stride
+  static_assert(TC % NG == 0 && TC % HALF == 0, "chunk shape");
+  static_assert(THREADS % 64 == 0, "whole waves");
+};
+
+template <class S>
+struct BSmem {
+  float4 dd[S::TC][S::CW];                  // (Delta, u, ds, -) per token and channel
+  float bc[S::TC][S::NG][2 * S::G];         // B then C of each group, per token
+  float part[2][S::NG][S::PST];             // per-group partial sums per (token, channel)
+  float red[2][S::HALF][S::NPAD][S::CW + 1];  // dB, dC contributions per (token, state, channel)
+  float chan[2][S::NG][S::CW];              // dD, d bias per (group, channel), at the end
+};
+
+// phi(k) = (e^k - 1)/k and phi'(k), from a = e^k: Horner on the series below
+// |k| = 1/2 (both at once), the closed forms (a - 1)/k and (a - phi)/k above.
+__device__ __forceinline__ void phi_and_prime(float k, float a, float& phi, float& dphi) {
+  constexpr float c0 = 1.0f, c1 = 1.0f / 2.0f, c2 = 1.0f / 6.0f, c3 = 1.0f / 24.0f,
+                  c4 = 1.0f / 120.0f, c5 = 1.0f / 720.0f, c6 = 1.0f / 5040.0f,
+                  c7 = 1.0f / 40320.0f, c8 = 1.0f / 362880.0f;
+  float p = c8, d = 0.0f;
+  d = fmaf(d, k, p); p = fmaf(p, k, c7);
+  d = fmaf(d, k, p); p = fmaf(p, k, c6);
+  d = fmaf(d, k, p); p = fmaf(p, k, c5);
+  d = fmaf(d, k, p); p = fmaf(p, k, c4);
+  d = fmaf(d, k, p); p = fmaf(p, k, c3);
+  d = fmaf(d, k, p); p = fmaf(p, k, c2);
+  d = fmaf(d, k, p); p = fmaf(p, k, c1);
+  d = fmaf(d, k, p); p = fmaf(p, k, c0);
+  const float r = 1.0f / k;
+  const float pl = (a - 1.0f) * r;
+  const float dl = (a - pl) * r;
+  const bool small = fabsf(k) < 0.5f;
+  phi = small ? p : pl;
+  dphi = small ? d : dl;
+}
+
+struct BwdArgs {
+  const void *u, *delta, *B, *C, *z, *dy;
+  const float *A, *D, *bias, *h0, *dlast;
+  void *du, *ddelta, *dz;
+  float* dh0;
+  float* ckpt;    // (batch, nchunks, dim, N)
+  float* pbc;     // (ntiles, 2, batch, L, N)
+  float* pA;      // (batch, dim, N)
+  float* pDb;     // (2, batch, dim)
+  int64_t batch, L, dim, N, ntiles, nchunks;
+  int softplus, want_dz;
+};
+
+template <typename IO, int G, int NG, bool ZOH, bool GATE>
+__global__ __launch_bounds__((BShape<G, NG>::THREADS)) void scan_bwd_kernel(const BwdArgs p) {
+  using S = BShape<G, NG>;
+  constexpr int CW = S::CW, TC = S::TC, RPT = S::RPT, NPAD = S::NPAD, HALF = S::HALF;
+  __shared__ BSmem<S> sm;
+
+  const IO* __restrict__ u = (const IO*)p.u;
+  const IO* __restrict__ dr = (const IO*)p.delta;
+  const IO* __restrict__ Bm = (const IO*)p.B;
+  const IO* __restrict__ Cm = (const IO*)p.C;
+  const IO* __restrict__ zz = (const IO*)p.z;
+  const IO* __restrict__ dyp = (const IO*)p.dy;
+  const int64_t L = p.L, dim = p.dim, N = p.N;
+
+  const int64_t nblk = (int64_t)gridDim.x;
+  const int64_t bid = blockIdx.x;
+  const int64_t logical = (nblk % 8 == 0) ? (bid % 8) * (nblk / 8) + bid / 8 : bid;
+  const int64_t b = logical / p.ntiles;
+  const int64_t tile = logical - b * p.ntiles;
+  const int tid = threadIdx.x;
+  const int cl = tid % CW, g = tid / CW;
+  const int64_t c = tile * CW + cl;
+  const bool cvalid = c < dim;
+  const int64_t cc = cvalid ? c : dim - 1;
+  const int n0 = g * G;
+  const int64_t row0 = b * L;
+
+  float Aa[G], Ap[G];
+#pragma unroll
+  for (int k = 0; k < G; ++k) {
+    const bool real = cvalid && (n0 + k) < N;
+    Aa[k] = real ? p.A[c * N + n0 + k] : 0.0f;
+    Ap[k] = Aa[k] * kLog2e;
+  }
+  const float bias = p.bias ? p.bias[cc] : 0.0f;
+  const float dskip = p.D ? p.D[cc] : 0.0f;
+
+  // ---- stage one chunk: (Delta, u, ds) per (token, channel), B and C per
+  // (token, state); the epilogue values of this thread's tokens stay in
+  // registers.  Tokens past L get zeros.
+  float e_dy[RPT], e_sv[RPT], e_gz[RPT], e_dg[RPT], e_u[RPT], e_ds[RPT];
+  auto stage = [&](int64_t t0, bool bwd) {
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const int r = g + NG * i;
+      const int64_t t = t0 + r;
+      const bool live = t < L;
+      const int64_t idx = (row0 + (live ? t : L - 1)) * dim + cc;
+      const float x = live ? to_f32(u[idx]) : 0.0f;
+      const float v = to_f32(dr[idx]) + bias;
+      const float dl = live ? (p.softplus ? softplus_f(v) : v) : 0.0f;
+      float ds = 0.0f;
+      if (bwd) {
+        const float dyv = live ? to_f32(dyp[idx]) : 0.0f;
+        float gz = 1.0f, dg = 0.0f;
+        if constexpr (GATE) {
+          const float zv = to_f32(zz[idx]);
+          const float sg = rcp_hw(1.0f + exp2_hw(-zv * kLog2e));  // sigma(z)
+          gz = zv * sg;                                          // silu(z)
+          dg = sg * fmaf(zv, 1.0f - sg, 1.0f);                   // silu'(z)
+        }
+        ds = dyv * gz;
+        e_dy[i] = dyv;
+        e_gz[i] = gz;
+        e_dg[i] = dg;
+        e_u[i] = x;
+        e_ds[i] = ds;
+        // d softplus / dv = sigma(v)
+        e_sv[i] = p.softplus ? rcp_hw(1.0f + exp2_hw(-v * kLog2e)) : 1.0f;
+      }
+      sm.dd[r][cl] = make_float4(dl, x, ds, 0.0f);
+    }
+    // B and C: every thread stages whole groups of one token
+    for (int e = tid; e < TC * NG; e += S::THREADS) {
+      const int tt = e / NG, gg = e % NG;
+      const int64_t t = t0 + tt;
+#pragma unroll
+      for (int k = 0; k < G; ++k) {
+        const int n = gg * G + k;
+        const bool ok = t < L && n < N;
+        const int64_t bi = (row0 + (t < L ? t : L - 1)) * N + (n < N ? n : N - 1);
+        sm.bc[tt][gg][k] = ok ? to_f32(Bm[bi]) : 0.0f;
+        sm.bc[tt][gg][G + k] = ok ? to_f32(Cm[bi]) : 0.0f;
+      }
+    }
+  };
+
+  auto update_state = [&](float& h, float a, float bw, float dl, float x, float Bv) {
+    // h = abar h + bbar u, bbar = Delta B phi (ZOH; bw = phi) or Delta B (Euler)
+    h = fmaf(a, h, (ZOH ? dl * bw : dl) * Bv * x);
+  };
+
+  // ---- pass 1: the states forward, one checkpoint per chunk start
+  float h[G];
+#pragma unroll
+  for (int k = 0; k < G; ++k)
+    h[k] = (p.h0 && cvalid && n0 + k < N) ? p.h0[(b * dim + c) * N + n0 + k] : 0.0f;
+  for (int64_t ck = 0; ck < p.nchunks; ++ck) {
+    const int64_t t0 = ck * TC;
+    if (cvalid) {
+#pragma unroll
+      for (int k = 0; k < G; ++k)
+        if (n0 + k < N) p.ckpt[((b * p.nchunks + ck) * dim + c) * N + n0 + k] = h[k];
+    }
+    stage(t0, false);
+    __syncthreads();
+    const int nt = (int)(L - t0 < TC ? L - t0 : TC);
+    for (int t = 0; t < nt; ++t) {
+      const float4 d4 = sm.dd[t][cl];
+#pragma unroll
+      for (int k = 0; k < G; ++k) {
+        const float kap = d4.x * Aa[k];
+        const float a = exp2_hw(d4.x * Ap[k]);
+        float phi = 1.0f, dphi;
+        if constexpr (ZOH) phi_and_prime(kap, a, phi, dphi);
+        update_state(h[k], a, phi, d4.x, d4.y, sm.bc[t][g][k]);
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- pass 2: the chunks backwards
+  float gad[G], dA[G];
+#pragma unroll
+  for (int k = 0; k < G; ++k) {
+    gad[k] = (p.dlast && cvalid && n0 + k < N) ? p.dlast[(b * dim + c) * N + n0 + k] : 0.0f;
+    dA[k] = 0.0f;
+  }
+  float accD = 0.0f, accB = 0.0f;  // this thread's tokens: sum ds u, sum d(raw delta)
+  for (int64_t ck = p.nchunks - 1; ck >= 0; --ck) {
+    const int64_t t0 = ck * TC;
+    const int nt = (int)(L - t0 < TC ? L - t0 : TC);
+    stage(t0, true);
+    float hst[G];
+#pragma unroll
+    for (int k = 0; k < G; ++k)
+      hst[k] = (cvalid && n0 + k < N) ? p.ckpt[((b * p.nchunks + ck) * dim + c) * N + n0 + k] : 0.0f;
+    __syncthreads();
+
+    // recompute: states, abar and phi of the chunk; partial pre-gate readout
+    float hs[TC][G], as[TC][G], ps[TC][G];
+#pragma unroll
+    for (int k = 0; k < G; ++k) h[k] = hst[k];
+#pragma unroll
+    for (int t = 0; t < TC; ++t) {
+      if (t < nt) {
+        const float4 d4 = sm.dd[t][cl];
+        float acc = 0.0f;
+#pragma unroll
+        for (int k = 0; k < G; ++k) {
+          const float a = exp2_hw(d4.x * Ap[k]);
+          float phi = 1.0f, dphi;
+          if constexpr (ZOH) phi_and_prime(d4.x * Aa[k], a, phi, dphi);
+          update_state(h[k], a, phi, d4.x, d4.y, sm.bc[t][g][k]);
+          hs[t][k] = h[k];
+          as[t][k] = a;
+          ps[t][k] = phi;
+          acc = fmaf(sm.bc[t][g][G + k], h[k], acc);
+        }
+        sm.part[0][g][t * CW + cl] = acc;
+      }
+    }
+    __syncthreads();
+    // dz = dy s silu'(z), s = C.h + D u (this thread's tokens)
+    if constexpr (GATE) {
+      if (p.want_dz) {
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+          const int r = g + NG * i;
+          const int64_t t = t0 + r;
+          if (cvalid && r < nt) {
+            float s = fmaf(dskip, e_u[i], 0.0f);
+            for (int j = 0; j < NG; ++j) s += sm.part[0][j][r * CW + cl];
+            store_io((IO*)p.dz + (row0 + t) * dim + c, e_dy[i] * s * e_dg[i]);
+          }
+        }
+      }
+    }
+    __syncthreads();
+
+    // the adjoint backwards through the chunk, in two rounds of HALF tokens
+#pragma unroll
+    for (int half = TC / HALF - 1; half >= 0; --half) {
+#pragma unroll
+      for (int tt = HALF - 1; tt >= 0; --tt) {
+        const int t = half * HALF + tt;
+        if (t < nt) {
+          const float4 d4 = sm.dd[t][cl];
+          const float dl = d4.x, x = d4.y, ds = d4.z;
+          float ddt = 0.0f, dx = 0.0f;
+#pragma unroll
+          for (int k = 0; k < G; ++k) {
+            const float Bv = sm.bc[t][g][k], Cv = sm.bc[t][g][G + k];
+            const float a = as[t][k];
+            const float hp = t > 0 ? hs[t > 0 ? t - 1 : 0][k] : hst[k];
+            gad[k] = fmaf(ds, Cv, gad[k]);               // g_t
+            const float da = gad[k] * hp;                // d abar
+            const float db = gad[k] * x;                 // d bbar
+            float dBc;
+            if constexpr (ZOH) {
+              float phi, dphi;
+              phi_and_prime(dl * Aa[k], a, phi, dphi);
+              ddt = fmaf(da * Aa[k] + db * Bv, a, ddt);  // (da A + db B) abar
+              dA[k] = fmaf(da * dl, a, fmaf(db * Bv * dl * dl, dphi, dA[k]));
+              dBc = db * dl * ps[t][k];
+              dx = fmaf(gad[k], dl * Bv * ps[t][k], dx);
+            } else {
+              ddt = fmaf(da * Aa[k], a, fmaf(db, Bv, ddt));
+              dA[k] = fmaf(da * dl, a, dA[k]);
+              dBc = db * dl;
+              dx = fmaf(gad[k], dl * Bv, dx);
+            }
+            sm.red[0][tt][n0 + k][cl] = cvalid ? dBc : 0.0f;
+            sm.red[1][tt][n0 + k][cl] = cvalid ? ds * hs[t][k] : 0.0f;
+            gad[k] *= a;                                 // carry to t - 1
+          }
+          sm.part[0][g][t * CW + cl] = ddt;
+          sm.part[1][g][t * CW + cl] = dx;
+        }
+      }
+      __syncthreads();
+      // dB, dC of these HALF tokens: sum over the block's channels
+      for (int e = tid; e < 2 * HALF * NPAD; e += S::THREADS) {
+        const int which = e / (HALF * NPAD);
+        const int rem = e - which * HALF * NPAD;
+        const int tt = rem / NPAD, n = rem % NPAD;
+        const int t = half * HALF + tt;
+        if (t < nt && n < N) {
+          float s = 0.0f;
+#pragma unroll
+          for (int q = 0; q < CW; ++q) s += sm.red[which][tt][n][q];
+          p.pbc[(((tile * 2 + which) * p.batch + b) * L + t0 + t) * N + n] = s;
+        }
+      }
+      __syncthreads();
+    }
+
+    // epilogue: d(raw delta), du; sums for dD and d bias
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const int r = g + NG * i;
+      const int64_t t = t0 + r;
+      if (r < nt) {
+        float ddt = 0.0f, dx = e_ds[i] * dskip;
+        for (int j = 0; j < NG; ++j) {
+          ddt += sm.part[0][j][r * CW + cl];
+          dx += sm.part[1][j][r * CW + cl];
+        }
+        const float dv = ddt * e_sv[i];
+        accB += dv;
+        accD = fmaf(e_ds[i], e_u[i], accD);
+        if (cvalid) {
+          store_io((IO*)p.ddelta + (row0 + t) * dim + c, dv);
+          store_io((IO*)p.du + (row0 + t) * dim + c, dx);
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- per-block results: dh0 (the carried adjoint is abar_0 g_0), dA,
+  // dD and d bias partials for this batch entry
+  if (cvalid) {
+#pragma unroll
+    for (int k = 0; k < G; ++k) {
+      if (n0 + k < N) {
+        if (p.dh0) p.dh0[(b * dim + c) * N + n0 + k] = gad[k];
+        p.pA[(b * dim + c) * N + n0 + k] = dA[k];
+      }
+    }
+  }
+  sm.chan[0][g][cl] = accD;
+  sm.chan[1][g][cl] = accB;
+  __syncthreads();
+  if (g == 0 && cvalid) {
+    float sD = 0.0f, sB = 0.0f;
+    for (int j = 0; j < NG; ++j) {
+      sD += sm.chan[0][j][cl];
+      sB += sm.chan[1][j][cl];
+    }
+    p.pDb[b * dim + c] = sD;
+    p.pDb[(p.batch + b) * dim + c] = sB;
+  }
+}
+
+// dB, dC: add the channel tiles' partials in tile order, round to the io dtype.
+template <typename IO>
+__global__ __launch_bounds__(256) void bwd_finalize_bc(const float* __restrict__ pbc,
+                                                       IO* __restrict__ dB, IO* __restrict__ dC,
+                                                       const int64_t ntiles, const int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  float sb = 0.0f, sc = 0.0f;
+  for (int64_t tl = 0; tl < ntiles; ++tl) {
+    sb += pbc[(tl * 2 + 0) * n + i];
+    sc += pbc[(tl * 2 + 1) * n + i];
+  }
+  store_io(dB + i, sb);
+  store_io(dC + i, sc);
+}
+
+// dA (dim * N), dD and d bias (dim): add the batch entries' partials in order.
+__global__ __launch_bounds__(256) void bwd_finalize_params(
+    const float* __restrict__ pA, const float* __restrict__ pDb, float* __restrict__ dA,
+    float* __restrict__ dD, float* __restrict__ dbias, const int64_t batch, const int64_t dim,
+    const int64_t N) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < dim * N) {
+    float s = 0.0f;
+    for (int64_t b = 0; b < batch; ++b) s += pA[b * dim * N + i];
+    dA[i] = s;
+  }
+  if (i < dim) {
+    float sD = 0.0f, sB = 0.0f;
+    for (int64_t b = 0; b < batch; ++b) {
+      sD += pDb[b * dim + i];
+      sB += pDb[(batch + b) * dim + i];
+    }
+    if (dD) dD[i] = sD;
+    if (dbias) dbias[i] = sB;
+  }
+}
+
+template <typename IO, int G, int NG, bool ZOH, bool GATE>
+hipError_t bwd_launch_one(const BwdArgs& a, hipStream_t stream) {
+  using S = BShape<G, NG>;
+  const int64_t nblk = a.ntiles * a.batch;
+  if (nblk > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((scan_bwd_kernel<IO, G, NG, ZOH, GATE>), dim3((unsigned)nblk),
+                     dim3(S::THREADS), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <typename IO, int G, int NG>
+hipError_t bwd_modes(const BwdArgs& a, bool zoh, bool gate, hipStream_t stream) {
+  if (zoh) return gate ? bwd_launch_one<IO, G, NG, true, true>(a, stream)
+                       : bwd_launch_one<IO, G, NG, true, false>(a, stream);
+  return gate ? bwd_launch_one<IO, G, NG, false, true>(a, stream)
+              : bwd_launch_one<IO, G, NG, false, false>(a, stream);
+}
+
+template <typename IO>
+hipError_t bwd_io(const ScanBwdParams& q, bool zoh, bool gate, hipStream_t stream) {
+  BwdArgs a;
+  a.u = q.u; a.delta = q.delta; a.B = q.B; a.C = q.C; a.z = q.z; a.dy = q.dy;
+  a.A = q.A; a.D = q.D; a.bias = q.delta_bias; a.h0 = q.h0; a.dlast = q.dlast;
+  a.du = q.du; a.ddelta = q.ddelta; a.dz = q.dz; a.dh0 = q.dh0;
+  a.batch = q.batch; a.L = q.L; a.dim = q.dim; a.N = q.N;
+  a.ntiles = (q.dim + 15) / 16;
+  a.nchunks = (q.L + 15) / 16;
+  a.softplus = q.softplus;
+  a.want_dz = q.dz != nullptr;
+  // workspace: checkpoints, dB/dC partials, dA partials, dD/dbias partials
+  char* w = (char*)q.workspace;
+  a.ckpt = (float*)w;
+  w += scan_bwd_ckpt_bytes(q.batch, q.L, q.dim, q.N);
+  a.pbc = (float*)w;
+  w += (size_t)a.ntiles * 2 * q.batch * q.L * q.N * sizeof(float);
+  a.pA = (float*)w;
+  w += (size_t)q.batch * q.dim * q.N * sizeof(float);
+  a.pDb = (float*)w;
+  hipError_t e;
+  if (q.N <= 4) e = bwd_modes<IO, 1, 4>(a, zoh, gate, stream);
+  else if (q.N <= 8) e = bwd_modes<IO, 2, 4>(a, zoh, gate, stream);
+  else e = bwd_modes<IO, 2, 8>(a, zoh, gate, stream);
+  if (e != hipSuccess) return e;
+  const int64_t nbc = q.batch * q.L * q.N;
+  if (nbc > 0) {
+    hipLaunchKernelGGL((bwd_finalize_bc<IO>), dim3((unsigned)((nbc + 255) / 256)), dim3(256), 0,
+                       stream, a.pbc, (IO*)q.dB, (IO*)q.dC, a.ntiles, nbc);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int64_t np = q.dim * q.N;
+  hipLaunchKernelGGL(bwd_finalize_params, dim3((unsigned)((np + 255) / 256)), dim3(256), 0, stream,
+                     a.pA, a.pDb, q.dA, q.dD, q.ddelta_bias, q.batch, q.dim, q.N);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t scan_bwd_ckpt_bytes(int64_t batch, int64_t L, int64_t dim, int64_t N) {
+  // 256-byte aligned sections
+  const size_t raw = (size_t)batch * ((L + 15) / 16) * dim * N * sizeof(float);
+  return (raw + 255) / 256 * 256;
+}
+
+size_t scan_bwd_workspace_bytes(int64_t batch, int64_t L, int64_t dim, int64_t N) {
+  auto al = [](size_t x) { return (x + 255) / 256 * 256; };
+  const size_t ntiles = (size_t)((dim + 15) / 16);
+  return scan_bwd_ckpt_bytes(batch, L, dim, N) + al(ntiles * 2 * batch * L * N * sizeof(float)) +
+         al((size_t)batch * dim * N * sizeof(float)) + al((size_t)2 * batch * dim * sizeof(float));
+}
+
+hipError_t launch_scan_bwd(const ScanBwdParams& q, int io_dtype, bool zoh, bool gate,
+                           hipStream_t stream) {
+  if (io_dtype == 1) return bwd_io<bf16_bits>(q, zoh, gate, stream);
+  return bwd_io<float>(q, zoh, gate, stream);
+}
+
+}  // namespace ssm66

@@ -145,6 +145,52 @@ int ssm_step(float* state, const void* u, const void* delta, const float* A, con
   return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 
+size_t ssm_scan_bwd_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate) {
+  if (check_common(batch, seqlen, dim, dstate, SSM_F32, 0, SSM_DT_ZOH) != SSM_OK) return 0;
+  return ssm66::scan_bwd_workspace_bytes(batch, seqlen, dim, dstate);
+}
+
+int ssm_scan_bwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                 const float* D, const void* z, const float* delta_bias, int softplus,
+                 int dt_mode, const float* h0, const void* dy, const float* dlast_state,
+                 void* du, void* ddelta, float* dA, void* dB, void* dC, float* dD, void* dz,
+                 float* ddelta_bias, float* dh0, void* workspace, size_t workspace_bytes,
+                 int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype,
+                 void* stream) {
+  int st = check_common(batch, seqlen, dim, dstate, io_dtype, softplus, dt_mode);
+  if (st != SSM_OK) return st;
+  if (batch == 0 || dim == 0) return SSM_OK;
+  if (!A || !dA) return SSM_ERR_NULL;
+  const bool has_tokens = seqlen > 0;
+  if (has_tokens && (!u || !delta || !B || !C || !dy || !du || !ddelta || !dB || !dC))
+    return SSM_ERR_NULL;
+  if (z && !dz) return SSM_ERR_NULL;  // the gate's gradient is part of the result
+  if (!workspace) return SSM_ERR_NULL;
+  if (workspace_bytes < ssm66::scan_bwd_workspace_bytes(batch, seqlen, dim, dstate))
+    return SSM_ERR_SHAPE;
+  const size_t es = io_dtype == SSM_BF16 ? 2 : 4;
+  const void* io_ptrs[11] = {u, delta, B, C, z, dy, du, ddelta, dB, dC, dz};
+  for (const void* q : io_ptrs)
+    if (q && !aligned(q, es)) return SSM_ERR_ALIGN;
+  const void* f32_ptrs[10] = {A, D, delta_bias, h0, dlast_state, dA, dD, ddelta_bias, dh0,
+                              workspace};
+  for (const void* q : f32_ptrs)
+    if (q && !aligned(q, 4)) return SSM_ERR_ALIGN;
+  if (!aligned(workspace, 256)) return SSM_ERR_ALIGN;
+  if (batch * ((dim + 15) / 16) > 0x7fffffff) return SSM_ERR_UNSUPPORTED;
+
+  ssm66::ScanBwdParams p;
+  p.u = u; p.delta = delta; p.B = B; p.C = C; p.z = z; p.dy = dy;
+  p.A = A; p.D = D; p.delta_bias = delta_bias; p.h0 = h0; p.dlast = dlast_state;
+  p.du = du; p.ddelta = ddelta; p.dB = dB; p.dC = dC; p.dz = dz;
+  p.dA = dA; p.dD = dD; p.ddelta_bias = ddelta_bias; p.dh0 = dh0;
+  p.workspace = workspace;
+  p.batch = batch; p.L = seqlen; p.dim = dim; p.N = dstate; p.softplus = softplus;
+  const hipError_t e = ssm66::launch_scan_bwd(p, io_dtype, dt_mode == SSM_DT_ZOH, z != nullptr,
+                                              (hipStream_t)stream);
+  return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
 int ssm_conv1d_fwd(const void* x, const float* weight, const float* bias, int silu,
                    const void* window_in, const int32_t* seq_lens, const uint8_t* reset,
                    void* out, void* window_out, int64_t batch, int64_t seqlen, int64_t dim,

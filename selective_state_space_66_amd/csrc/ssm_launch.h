@@ -39,6 +39,16 @@ struct StepParams {
   int softplus;
 };
 
+struct ScanBwdParams {
+  const void *u, *delta, *B, *C, *z, *dy;     // io dtype; z nullable
+  const float *A, *D, *delta_bias, *h0, *dlast;  // D, delta_bias, h0, dlast nullable
+  void *du, *ddelta, *dB, *dC, *dz;           // io dtype; dz nullable
+  float *dA, *dD, *ddelta_bias, *dh0;          // dD, ddelta_bias, dh0 nullable
+  void* workspace;                             // scan_bwd_workspace_bytes(...) bytes
+  int64_t batch, L, dim, N;
+  int softplus;
+};
+
 struct ConvParams {
   const void* x;            // (batch, L, dim) io dtype; (batch, dim) for a step
   const float* w;           // (dim, k): w[c * k + i] multiplies the input i steps back
@@ -60,6 +70,10 @@ hipError_t launch_scan_fwd(const ScanParams& p, int io_dtype, int G, int NG, boo
 // multiple of 4 and the io pointers are aligned to 4 elements.
 hipError_t launch_conv1d(const ConvParams& p, int io_dtype, bool vec4, bool step,
                          hipStream_t stream);
+size_t scan_bwd_ckpt_bytes(int64_t batch, int64_t L, int64_t dim, int64_t N);
+size_t scan_bwd_workspace_bytes(int64_t batch, int64_t L, int64_t dim, int64_t N);
+hipError_t launch_scan_bwd(const ScanBwdParams& p, int io_dtype, bool zoh, bool gate,
+                           hipStream_t stream);
 hipError_t launch_step(const StepParams& p, int io_dtype, bool zoh, bool gate, hipStream_t stream);
 
 }  // namespace ssm66

@@ -34,7 +34,8 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared_functions()
-    assert set(names) == {"ssm_scan_fwd", "ssm_scan_fwd_ex", "ssm_step", "ssm_conv1d_fwd",
+    assert set(names) == {"ssm_scan_fwd", "ssm_scan_fwd_ex", "ssm_scan_bwd",
+                          "ssm_scan_bwd_workspace_size", "ssm_step", "ssm_conv1d_fwd",
                           "ssm_conv1d_step", "ssm_status_string", "ssm_abi_version"}
     raw = ctypes.CDLL(ssm.LIB_PATH)
     for n in names:
@@ -170,3 +171,40 @@ def test_conv_specific_checks(lib):
     assert _conv(lib, batch=70000) == c["SSM_ERR_UNSUPPORTED"]
     assert _conv(lib, L=64 * 65536) == c["SSM_ERR_UNSUPPORTED"]
     assert _conv_step(lib, win=None) == c["SSM_ERR_NULL"]
+
+
+def _bwd(lib, **kw):
+    a = dict(u=FAKE, delta=FAKE, A=FAKE, B=FAKE, C=FAKE, D=None, z=None, bias=None, softplus=1,
+             dt_mode=0, h0=None, dy=FAKE, dlast=None, du=FAKE, ddelta=FAKE, dA=FAKE, dB=FAKE,
+             dC=FAKE, dD=None, dz=None, dbias=None, dh0=None, ws=ctypes.c_void_p(0x100000),
+             wsb=1 << 40, batch=2, L=8, dim=64, N=16, io=1, stream=None)
+    a.update(kw)
+    return lib.ssm_scan_bwd(a["u"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], a["bias"],
+                            a["softplus"], a["dt_mode"], a["h0"], a["dy"], a["dlast"], a["du"],
+                            a["ddelta"], a["dA"], a["dB"], a["dC"], a["dD"], a["dz"], a["dbias"],
+                            a["dh0"], a["ws"], a["wsb"], a["batch"], a["L"], a["dim"], a["N"],
+                            a["io"], a["stream"])
+
+
+def test_bwd_invalid_arguments_are_rejected(lib):
+    c = _header_constants()
+    assert _bwd(lib, N=0) == c["SSM_ERR_SHAPE"]
+    assert _bwd(lib, N=17) == c["SSM_ERR_SHAPE"]
+    assert _bwd(lib, io=5) == c["SSM_ERR_DTYPE"]
+    assert _bwd(lib, dt_mode=3) == c["SSM_ERR_FLAG"]
+    assert _bwd(lib, dy=None) == c["SSM_ERR_NULL"]
+    assert _bwd(lib, dA=None) == c["SSM_ERR_NULL"]
+    assert _bwd(lib, z=FAKE, dz=None) == c["SSM_ERR_NULL"]
+    assert _bwd(lib, ws=None) == c["SSM_ERR_NULL"]
+    assert _bwd(lib, wsb=16) == c["SSM_ERR_SHAPE"]
+    assert _bwd(lib, ws=ctypes.c_void_p(0x100040)) == c["SSM_ERR_ALIGN"]
+    assert _bwd(lib, du=MISALIGNED) == c["SSM_ERR_ALIGN"]
+    assert _bwd(lib, batch=0) == c["SSM_OK"]
+    assert _bwd(lib, batch=1 << 20, dim=1 << 20, L=1, wsb=1 << 62) == c["SSM_ERR_UNSUPPORTED"]
+
+
+def test_bwd_workspace_size(lib):
+    f = lib.ssm_scan_bwd_workspace_size
+    assert f(2, 40, 70, 16) >= 4 * 2 * 3 * 70 * 16  # three 16-token checkpoints per row
+    assert f(-1, 4, 4, 4) == 0 and f(1, 4, 4, 17) == 0
+    assert f(8, 2048, 1536, 16) > f(8, 1024, 1536, 16)
