@@ -60,7 +60,7 @@ __device__ __forceinline__ float zoh_phi(float k, float ek) {
   const float s = fmaf(k, fmaf(k, fmaf(k, fmaf(k, fmaf(k, fmaf(k, 1.0f / 5040.0f, 1.0f / 720.0f),
                                                         1.0f / 120.0f), 1.0f / 24.0f), 1.0f / 6.0f),
                                0.5f), 1.0f);
-  return fabsf(k) < 0.5f ? s : (ek - 1.0f) / k;
+  return fabsf(k) < 0.5f ? s : (ek - 1.0f) * rcp_hw(k);
 }
 
 }  // namespace ssm66
