@@ -71,6 +71,10 @@ def _load():
     lib.oracle_scan_bwd.restype = None
     lib.oracle_scan_bwd.argtypes = [ctypes.c_void_p] * 9 + [ctypes.c_int, ctypes.c_int] + \
         [ctypes.c_void_p] * 11 + [ctypes.c_int64] * 4
+    lib.oracle_ssd_fwd.restype = None
+    lib.oracle_ssd_fwd.argtypes = [ctypes.c_void_p] * 9 + [ctypes.c_int, ctypes.c_int,
+                                                           ctypes.c_void_p, ctypes.c_void_p] + \
+        [ctypes.c_int64] * 5
     lib.oracle_conv1d_fwd.restype = None
     lib.oracle_conv1d_fwd.argtypes = [ctypes.c_void_p] * 6 + [ctypes.c_int, ctypes.c_void_p,
                                                               ctypes.c_void_p] + [ctypes.c_int64] * 4
@@ -272,3 +276,28 @@ def scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, softplus=Tr
                             _ptr(out["dz"]), _ptr(out["ddelta_bias"]), _ptr(out["dh0"]),
                             batch, L, dim, N)
     return out
+
+
+def ssd_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, softplus=True, dt_mode="euler",
+            h0=None):
+    """Mamba-2 / SSD layer, fp64: one scalar decay A[h] and one step size per
+    (token, head); B, C shared by all heads.
+
+    x, z: (batch, L, nheads, P); dt: (batch, L, nheads); A, D, dt_bias: (nheads,);
+    B, C: (batch, L, N); h0: optional (batch, nheads, P, N).
+    Returns (y (batch, L, nheads, P), last_state (batch, nheads, P, N)).
+    """
+    x, dt, A, B, C = _f64(x), _f64(dt), _f64(A), _f64(B), _f64(C)
+    D, z, dt_bias, h0 = _f64(D), _f64(z), _f64(dt_bias), _f64(h0)
+    batch, L, nheads, P = x.shape
+    N = B.shape[2]
+    assert dt.shape == (batch, L, nheads) and A.shape == (nheads,)
+    assert B.shape == (batch, L, N) and C.shape == (batch, L, N)
+    assert z is None or z.shape == x.shape
+    assert h0 is None or h0.shape == (batch, nheads, P, N)
+    y = np.empty_like(x)
+    last = np.empty((batch, nheads, P, N))
+    _load().oracle_ssd_fwd(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                           _ptr(dt_bias), _ptr(h0), int(bool(softplus)), _MODES[dt_mode],
+                           _ptr(y), _ptr(last), batch, L, nheads, P, N)
+    return y, last

@@ -449,3 +449,62 @@ void oracle_scan_bwd(const double* u, const double* delta, const double* A, cons
   free(hs);
   free(g);
 }
+
+/* ------------------------------------------------------------------------
+ * Mamba-2 / SSD: one scalar decay per head.  "Mamba and selective state
+ * spaces", the section on what Mamba cannot do yet: Mamba-2 gives each head, a
+ * group of P channels, a single scalar decay, so most of the work becomes
+ * matrix products and N can grow to 64..256.  "State-space models & Mamba"
+ * (llm-tutorial.darvinyi.com, ch. 12), "The Mamba CUDA kernel": with A a scalar
+ * per channel group the recurrence is h_t = alpha_t h_{t-1} + Bbar_t x_t and the
+ * whole layer is a structured (1-semiseparable) masked matmul.
+ *
+ * The plain recurrence, per batch entry b, head hd, head channel p, state n:
+ *   Delta_t = softplus(dt_raw[b,t,hd] + dt_bias[hd])   (or without softplus)
+ *   alpha_t = exp(Delta_t A[hd])
+ *   w_t     = Delta_t (exponential-Euler) or Delta_t phi(Delta_t A[hd]) (ZOH)
+ *   h_t[p,n] = alpha_t h_{t-1}[p,n] + w_t B[b,t,n] x[b,t,hd,p]
+ *   y[b,t,hd,p] = (sum_n C[b,t,n] h_t[p,n] + D[hd] x) * silu(z)?
+ * B and C are shared by all heads (one group).  Layouts:
+ *   x, z, y : (batch, L, nheads * P)   dt_raw : (batch, L, nheads)
+ *   A, D, dt_bias : (nheads)           B, C : (batch, L, N)
+ *   h0 / last_state : (batch, nheads * P, N)
+ * ------------------------------------------------------------------------ */
+void oracle_ssd_fwd(const double* x, const double* dt_raw, const double* A, const double* B,
+                    const double* C, const double* D, const double* z, const double* dt_bias,
+                    const double* h0, int softplus, int dt_mode, double* y, double* last_state,
+                    int64_t batch, int64_t L, int64_t nheads, int64_t P, int64_t N) {
+  const int64_t dim = nheads * P;
+  double* h = (double*)malloc(sizeof(double) * (size_t)N);
+  for (int64_t b = 0; b < batch; ++b) {
+    for (int64_t hd = 0; hd < nheads; ++hd) {
+      const double a = A[hd];
+      for (int64_t p = 0; p < P; ++p) {
+        const int64_t c = hd * P + p;
+        for (int64_t n = 0; n < N; ++n) h[n] = h0 ? h0[(b * dim + c) * N + n] : 0.0;
+        for (int64_t t = 0; t < L; ++t) {
+          const double dt = step_size(dt_raw[(b * L + t) * nheads + hd],
+                                      dt_bias ? dt_bias[hd] : 0.0, softplus);
+          const double kap = dt * a;
+          const double alpha = exp(kap);
+          const double w = (dt_mode == ORACLE_DT_ZOH)
+                               ? ((a != 0.0) ? expm1(kap) / a : dt)  /* Delta phi(Delta A) */
+                               : dt;
+          const int64_t xi = (b * L + t) * dim + c;
+          const double xv = x[xi];
+          double acc = 0.0;
+          for (int64_t n = 0; n < N; ++n) {
+            h[n] = alpha * h[n] + w * B[(b * L + t) * N + n] * xv;
+            acc += C[(b * L + t) * N + n] * h[n];
+          }
+          double out = acc + (D ? D[hd] : 0.0) * xv;
+          if (z) out *= z[xi] * oracle_sigmoid(z[xi]);
+          y[xi] = out;
+        }
+        if (last_state)
+          for (int64_t n = 0; n < N; ++n) last_state[(b * dim + c) * N + n] = h[n];
+      }
+    }
+  }
+  free(h);
+}

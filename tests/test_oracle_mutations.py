@@ -62,6 +62,11 @@ MUTATIONS = {
     "bwd_silu_derivative": ("          if (dz) dz[xi] = dy[xi] * s * sg * (1.0 + zz * (1.0 - sg));",
                             "          if (dz) dz[xi] = dy[xi] * s * sg;"),
     "bwd_phi_prime_series": ("      s += (double)j * kp / term_f;", "      s += kp / term_f;"),
+    "ssd_wrong_head_decay": ("      const double a = A[hd];", "      const double a = A[0];"),
+    "ssd_weight_missing": ("            h[n] = alpha * h[n] + w * B[(b * L + t) * N + n] * xv;",
+                           "            h[n] = alpha * h[n] + B[(b * L + t) * N + n] * xv;"),
+    "ssd_dt_per_channel": ("          const double dt = step_size(dt_raw[(b * L + t) * nheads + hd],",
+                           "          const double dt = step_size(dt_raw[(b * L + t) * nheads + (hd + p) % nheads],"),
 }
 
 
@@ -80,6 +85,7 @@ def test_planted_mistake_is_caught(name, tmp_path):
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
                         os.path.join(ROOT, "tests", "test_oracle_pins.py"),
                         os.path.join(ROOT, "tests", "test_oracle_conv_pins.py"),
-                        os.path.join(ROOT, "tests", "test_oracle_bwd_pins.py")],
+                        os.path.join(ROOT, "tests", "test_oracle_bwd_pins.py"),
+                        os.path.join(ROOT, "tests", "test_oracle_ssd_pins.py")],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
     assert r.returncode != 0, f"mutation {name} survived the pins:\n{r.stdout[-2000:]}"

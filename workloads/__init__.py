@@ -310,3 +310,60 @@ def conv_step_inputs(cfg: ConvConfig, step: int) -> np.ndarray:
     """The token (batch, dim) of decoding step `step`, io dtype."""
     idx = np.arange(cfg.batch * cfg.dim, dtype=np.int64) + (step + 1) * cfg.batch * cfg.dim
     return _io(normal(cfg.seed, S_CONV_X, idx), cfg.io).reshape(cfg.batch, cfg.dim)
+
+
+# ----------------------------------------------- Mamba-2 / SSD (scalar decay)
+
+S_SSD_A, S_SSD_DT, S_SSD_D, S_SSD_X, S_SSD_DTR, S_SSD_B, S_SSD_C, S_SSD_Z = range(31, 39)
+
+
+@dataclass(frozen=True)
+class SSDConfig:
+    name: str
+    batch: int
+    L: int
+    nheads: int
+    P: int          # channels per head
+    N: int          # state size
+    io: str
+    gate: bool
+    seed: int
+
+
+SSD_CONFIGS: Dict[str, SSDConfig] = {
+    "ssd_tiny": SSDConfig("ssd_tiny", 2, 150, 3, 16, 32, "f32", True, 8),
+    # a Mamba-2-130M-shaped layer: d_model 768, expand 2 -> 1536 = 24 heads x 64, N 128
+    "ssd130m": SSDConfig("ssd130m", 8, 2048, 24, 64, 128, "bf16", True, 9),
+}
+
+
+def ssd_head_params(seed: int, nheads: int):
+    """A (nheads,) = -U[1, 16], D ~ N(0, 1), dt_bias = softplus^-1(dt) with dt
+    log-uniform in [1e-3, 1e-1] (the step-size range of the scan's workloads)."""
+    h = np.arange(nheads)
+    A = -(1.0 + 15.0 * uniform(seed, S_SSD_A, h)).astype(np.float32)
+    lo, hi = np.log(1e-3), np.log(1e-1)
+    dt = np.exp(lo + (hi - lo) * uniform(seed, S_SSD_DT, h))
+    dt_bias = np.log(np.expm1(dt)).astype(np.float32)
+    D = normal(seed, S_SSD_D, h)
+    return A, D, dt_bias
+
+
+def ssd_inputs(cfg: SSDConfig, heads: Optional[Sequence[int]] = None) -> dict:
+    """x, z (batch, L, len(heads), P) and dt (batch, L, len(heads)) in the io dtype
+    (dt raw in fp32 always -- it is one value per token and head), B, C
+    (batch, L, N) ~ N(0, 1) in the io dtype, head parameters in fp32.  With
+    `heads`, only those heads are generated (B and C whole)."""
+    b, L, H, P, N = cfg.batch, cfg.L, cfg.nheads, cfg.P, cfg.N
+    hs = np.arange(H) if heads is None else np.asarray(heads, dtype=np.int64)
+    A, D, dt_bias = ssd_head_params(cfg.seed, H)
+    tok = np.arange(b * L, dtype=np.int64)
+    xi = ((tok[:, None, None] * H + hs[None, :, None]) * P + np.arange(P)[None, None, :])
+    x = _io(normal(cfg.seed, S_SSD_X, xi), cfg.io).reshape(b, L, len(hs), P)
+    z = _io(normal(cfg.seed, S_SSD_Z, xi), cfg.io).reshape(b, L, len(hs), P) if cfg.gate else None
+    dt = normal(cfg.seed, S_SSD_DTR, tok[:, None] * H + hs[None, :]).reshape(b, L, len(hs))
+    bc = np.arange(b * L * N, dtype=np.int64).reshape(b, L, N)
+    Bm = _io(normal(cfg.seed, S_SSD_B, bc), cfg.io)
+    Cm = _io(normal(cfg.seed, S_SSD_C, bc), cfg.io)
+    return dict(x=x, z=z, dt=dt.astype(np.float32), A=A[hs], D=D[hs], dt_bias=dt_bias[hs],
+                B=Bm, C=Cm, io=cfg.io, heads=hs)
