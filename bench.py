@@ -10,8 +10,9 @@ to step so that the 256 MB Infinity Cache cannot serve a step from the previous
 one.  `value` is algorithmic bytes per step / measured step time.
 
 Also reported, outside `value`: the same scan under the exponential-Euler rule,
-the extended scan (initial state, lengths, document resets), the block's
-convolution (sequence and decoding step), the decode step (ssm_step) on its
+the extended scan (initial state, lengths, document resets), the backward pass,
+the block's convolution (sequence and decoding step), the Mamba-2 / SSD layer
+on the matrix cores, the decode step (ssm_step) on its
 workload (batch 256, D 5120, N 16, 1000 consecutive tokens), the kernel
 roofline for the dominant kernel, and the fp64 CPU oracle timed on the host.
 
@@ -22,6 +23,7 @@ one input set and prints no JSON:
     python bench.py --only scan [--dt-mode zoh|euler] [--launches 3]
     python bench.py --only decode [--launches 3]
     python bench.py --only conv [--launches 3]
+    python bench.py --only ssd [--launches 3]
     python bench.py --only copy     # a plain 256 MiB device copy, for counter calibration
 """
 import argparse
@@ -209,6 +211,73 @@ def time_bwd(sets, steps, warmup, dev):
     return float(np.mean([a.elapsed_time(b) for a, b in ev])), ws.numel()
 
 
+def ssd_bytes(b, L, H, P, N, gate):
+    """Algorithmic bytes of the SSD layer (bf16 io): x, [z] read and y written
+    once, B and C read once, dt (fp32) read once, A, D, dt_bias, and the final
+    state written (fp32)."""
+    return (3 if gate else 2) * b * L * H * P * 2 + 2 * b * L * N * 2 + 4 * b * L * H + 12 * H \
+        + 4 * b * H * P * N
+
+
+def ssd_mfma_flops(b, L, H, N):
+    """MFMA work of the chunked SSD kernel (64-token chunks, 64 channels per
+    head): the causal tiles of C B^T, C H^T, the masked scores times x, and the
+    state update, as 16x16x32 products of 16384 flops."""
+    chunks = b * H * ((L + 63) // 64)
+    per_chunk = 10 * (N // 32) + 16 * (N // 32) + 24 + (4 * N // 16) * 2
+    return chunks * per_chunk * 16384
+
+
+def time_ssd(dev, steps, warmup, nsets=3):
+    """The Mamba-2 / SSD layer (ssm_ssd_fwd) on the Mamba-2-130M shape, rotating
+    input sets (3 x ~160 MB > the 256 MB Infinity Cache)."""
+    import torch
+    import selective_state_space_66_amd as ssm
+    import workloads as W
+    cfg = W.SSD_CONFIGS["ssd130m"]
+    sets = []
+    for k in range(nsets):
+        c = W.SSDConfig(cfg.name, cfg.batch, cfg.L, cfg.nheads, cfg.P, cfg.N, cfg.io, cfg.gate,
+                        cfg.seed + 100 * k)
+        inp = W.ssd_inputs(c)
+        sets.append({kk: to_dev(inp[kk], "f32" if kk in ("dt", "A", "D", "dt_bias") else "bf16", dev)
+                     for kk in ("x", "z", "dt", "A", "D", "dt_bias", "B", "C")})
+    out = {}
+    for mode in ("euler", "zoh"):
+        ys = [(torch.empty_like(s["x"]), torch.empty((cfg.batch, cfg.nheads, cfg.P, cfg.N),
+                                                     dtype=torch.float32, device=dev)) for s in sets]
+
+        def launch(i):
+            s = sets[i % nsets]
+            y, last = ys[i % nsets]
+            ssm.ssd_fwd(s["x"], s["dt"], s["A"], s["B"], s["C"], D=s["D"], z=s["z"],
+                        dt_bias=s["dt_bias"], dt_mode=mode, y=y, last_state=last)
+
+        for i in range(warmup):
+            launch(i)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        for i in range(steps):
+            ev[i][0].record()
+            launch(warmup + i)
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        out[mode] = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    nb = ssd_bytes(cfg.batch, cfg.L, cfg.nheads, cfg.P, cfg.N, cfg.gate)
+    fl = ssd_mfma_flops(cfg.batch, cfg.L, cfg.nheads, cfg.N)
+    ms = out["euler"]
+    return {"workload": f"ssm_ssd_fwd: batch {cfg.batch}, L {cfg.L}, {cfg.nheads} heads x {cfg.P}, "
+                        f"N {cfg.N}, bf16, gate, D (Mamba-2-130M shape)",
+            "kernel_ms": round(ms, 5), "zoh_kernel_ms": round(out["zoh"], 5),
+            "roofline": {"bound": "hbm", "achieved": round(nb / (ms * 1e-3) / 1e9, 2),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                         "algorithmic_bytes": nb},
+            "mfma": {"achieved_TFLOPs": round(fl / (ms * 1e-3) / 1e12, 2), "peak_TFLOPs": 2500.0,
+                     "flops": fl}}
+
+
 def conv_bytes(b, L, D, k, io_bytes):
     """Algorithmic bytes of the sequence convolution: x read and out written once,
     the decoding window written, weights and bias read."""
@@ -313,6 +382,14 @@ def profile_only(what, launches, dt_mode):
                          delta_bias=s["delta_bias"], dt_mode=dt_mode, y=y, last_state=last)
     elif what == "decode":
         time_decode(W.STEP_CONFIGS["decode"], launches, dev, npool=2)
+    elif what == "ssd":
+        cfg = W.SSD_CONFIGS["ssd130m"]
+        inp = W.ssd_inputs(cfg)
+        t = {k: to_dev(inp[k], "f32" if k in ("dt", "A", "D", "dt_bias") else "bf16", dev)
+             for k in ("x", "z", "dt", "A", "D", "dt_bias", "B", "C")}
+        for _ in range(launches):
+            ssm.ssd_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
+                        dt_bias=t["dt_bias"])
     elif what == "conv":
         cfg = W.CONV_CONFIGS["conv130m"]
         inp = W.conv_inputs(cfg)
@@ -331,7 +408,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--decode-steps", type=int, default=1000)
-    ap.add_argument("--only", choices=["scan", "decode", "conv", "copy"], default=None,
+    ap.add_argument("--only", choices=["scan", "decode", "conv", "ssd", "copy"], default=None,
                     help="profiling mode: a few launches of one kernel, no JSON")
     ap.add_argument("--launches", type=int, default=3)
     ap.add_argument("--dt-mode", choices=["zoh", "euler"], default="zoh")
@@ -392,6 +469,10 @@ def main():
     del sets
     torch.cuda.empty_cache()
     conv = time_conv(dev, args.steps, args.warmup)
+    log("[bench] timing the Mamba-2 / SSD layer")
+    torch.cuda.empty_cache()
+    ssd = time_ssd(dev, args.steps, args.warmup)
+    log(f"[bench] ssd: {ssd['kernel_ms']:.4f} ms")
     log(f"[bench] conv: {conv['kernel_ms']:.4f} ms, step {conv['step']['us_per_step']:.2f} us")
 
     dcfg = W.STEP_CONFIGS["decode"]
@@ -461,6 +542,7 @@ def main():
                 "updates_per_s": float(f"{elems * cfg.N / (b_ms * 1e-3):.4g}"),
                 "workspace_MB": round(b_ws / 1e6, 1)},
         "conv": conv,
+        "ssd": ssd,
         "decode": {"workload": "ssm_step: batch 256, D 5120, N 16, bf16 io, fp32 state, gate, ZOH",
                    "steps": args.decode_steps,
                    "tok_per_s": round(dcfg.batch * args.decode_steps / d_wall_s, 1),

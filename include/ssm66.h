@@ -1,7 +1,7 @@
 /*
  * ssm66.h -- C ABI of the MI355X (gfx950) selective-scan library.
  *
- * Six operations, all defined on "Mamba and selective state spaces"
+ * Seven operations, defined on "Mamba and selective state spaces"
  * (zerotofrontier.app/ssm/mamba):
  *
  *   ssm_scan_fwd : the selective state-space layer (S6) over whole sequences --
@@ -28,6 +28,10 @@
  *                  backward of a linear recurrence is a reverse recurrence).
  *   ssm_step     : one token of that layer against a state cache, updated in
  *                  place ("Decoding with a constant-size cache").
+ *   ssm_ssd_fwd  : the Mamba-2 / SSD layer, one scalar decay per head, as a
+ *                  chunked masked matmul on the matrix cores (the first page on
+ *                  what Mamba cannot do yet; "The Mamba CUDA kernel" on
+ *                  "State-space models & Mamba", llm-tutorial.darvinyi.com).
  *   ssm_conv1d_fwd, ssm_conv1d_step : the short causal depthwise convolution
  *                  (+ SiLU) that feeds the scan in "The Mamba block", over
  *                  whole sequences and as one decoding step with its window of
@@ -73,7 +77,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 4
+#define SSM_ABI_VERSION 5
 
 /* status codes */
 #define SSM_OK 0
@@ -175,6 +179,28 @@ int ssm_step(float* state, const void* u, const void* delta, const float* A, con
              const void* C, const float* D, const void* z, const float* delta_bias, int softplus,
              int dt_mode, void* y, int64_t batch, int64_t dim, int64_t dstate, int io_dtype,
              void* stream);
+
+/*
+ * The Mamba-2 / SSD layer: the S6 recurrence with one scalar decay A[h] and
+ * one step size per (token, head) for each head of `headdim` channels, and B,
+ * C shared by all heads:
+ *   Delta = softplus?(dt[b,t,h] + dt_bias[h]),  alpha = exp(Delta A[h]),
+ *   w = Delta (SSM_DT_EULER) or Delta (exp(Delta A) - 1)/(Delta A) (SSM_DT_ZOH),
+ *   h_t[p,n] = alpha h_{t-1}[p,n] + w B[b,t,n] x[b,t,h,p],
+ *   y[b,t,h,p] = (sum_n C[b,t,n] h_t[p,n] + D[h] x[b,t,h,p]) * silu(z)?
+ * Layouts: x, z, y (batch, seqlen, nheads * headdim) io dtype; dt
+ * (batch, seqlen, nheads) float32; A, D, dt_bias (nheads) float32; B, C
+ * (batch, seqlen, dstate) io dtype; h0, last_state (batch, nheads * headdim,
+ * dstate) float32 (the scan's state layout).  D, z, dt_bias, h0, last_state
+ * may be NULL.  The kernel runs on the matrix cores with bf16 operands and
+ * fp32 accumulation and state: io_dtype must be SSM_BF16, headdim 64 and
+ * dstate 64 or 128 (else SSM_ERR_UNSUPPORTED); x, z, y, B, C must be 16-byte
+ * aligned.  Returns SSM_OK or an error status.
+ */
+int ssm_ssd_fwd(const void* x, const float* dt, const float* A, const void* B, const void* C,
+                const float* D, const void* z, const float* dt_bias, int softplus, int dt_mode,
+                const float* h0, void* y, float* last_state, int64_t batch, int64_t seqlen,
+                int64_t nheads, int64_t headdim, int64_t dstate, int io_dtype, void* stream);
 
 /*
  * The block's causal depthwise convolution over whole sequences ("The Mamba

@@ -13,6 +13,8 @@ missing, every call raises.
              softplus=True, dt_mode="zoh")     # state updated in place
     grads = scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None,
                      softplus=True, dt_mode="zoh", h0=None, dlast=None)
+    y, last_state = ssd_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, softplus=True,
+                            dt_mode="euler", h0=None)          # Mamba-2 / SSD
     out, window = conv1d_fwd(x, weight, bias=None, silu=True, window_in=None,
                              seq_lens=None, reset=None)
     out = conv1d_step(window, x, weight, bias=None, silu=True)   # window updated in place
@@ -54,6 +56,8 @@ def load_library():
     lib.ssm_scan_bwd.restype = ci
     lib.ssm_scan_bwd.argtypes = [vp] * 8 + [ci, ci] + [vp] * 13 + [ctypes.c_size_t] + \
         [i64] * 4 + [ci, vp]
+    lib.ssm_ssd_fwd.restype = ci
+    lib.ssm_ssd_fwd.argtypes = [vp] * 8 + [ci, ci, vp, vp, vp] + [i64] * 5 + [ci, vp]
     lib.ssm_conv1d_fwd.restype = ci
     lib.ssm_conv1d_fwd.argtypes = [vp] * 3 + [ci] + [vp] * 5 + [i64] * 4 + [ci, vp]
     lib.ssm_conv1d_step.restype = ci
@@ -327,3 +331,46 @@ def scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, softplus=Tr
 def scan_bwd_workspace_size(batch, L, dim, N):
     """Bytes of workspace ssm_scan_bwd needs for these sizes."""
     return int(load_library().ssm_scan_bwd_workspace_size(batch, L, dim, N))
+
+
+def ssd_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, softplus=True, dt_mode="euler",
+            h0=None, y=None, last_state=None, return_last_state=True):
+    """Mamba-2 / SSD layer on the GPU's matrix cores (one scalar decay per head).
+
+    x, z: (batch, L, nheads, headdim) bfloat16; dt: (batch, L, nheads) float32;
+    A, D, dt_bias: (nheads,) float32; B, C: (batch, L, N) bfloat16;
+    h0: optional (batch, nheads, headdim, N) float32.  headdim 64, N 64 or 128.
+    Returns (y like x, last_state (batch, nheads, headdim, N) float32 or None).
+    """
+    import torch
+    lib = load_library()
+    if x.dim() != 4:
+        raise ValueError("x must be (batch, L, nheads, headdim)")
+    batch, L, H, P = x.shape
+    N = B.shape[-1]
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on the GPU")
+    io = x.dtype
+    _io_code(x)
+    _check(x, "x", (batch, L, H, P), io, dev)
+    _check(z, "z", (batch, L, H, P), io, dev)
+    _check(dt, "dt", (batch, L, H), torch.float32, dev)
+    _check(A, "A", (H,), torch.float32, dev)
+    _check(D, "D", (H,), torch.float32, dev)
+    _check(dt_bias, "dt_bias", (H,), torch.float32, dev)
+    _check(B, "B", (batch, L, N), io, dev)
+    _check(C, "C", (batch, L, N), io, dev)
+    _check(h0, "h0", (batch, H, P, N), torch.float32, dev)
+    if y is None:
+        y = torch.empty_like(x)
+    _check(y, "y", (batch, L, H, P), io, dev)
+    if last_state is None and return_last_state:
+        last_state = torch.empty((batch, H, P, N), dtype=torch.float32, device=dev)
+    _check(last_state, "last_state", (batch, H, P, N), torch.float32, dev)
+    st = lib.ssm_ssd_fwd(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                         _ptr(dt_bias), int(bool(softplus)), _MODES[dt_mode], _ptr(h0), _ptr(y),
+                         _ptr(last_state), batch, L, H, P, N, _io_code(x), _stream(dev))
+    if st != 0:
+        raise SsmError(st, "ssm_ssd_fwd")
+    return y, last_state

@@ -191,6 +191,42 @@ int ssm_scan_bwd(const void* u, const void* delta, const float* A, const void* B
   return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 
+int ssm_ssd_fwd(const void* x, const float* dt, const float* A, const void* B, const void* C,
+                const float* D, const void* z, const float* dt_bias, int softplus, int dt_mode,
+                const float* h0, void* y, float* last_state, int64_t batch, int64_t seqlen,
+                int64_t nheads, int64_t headdim, int64_t dstate, int io_dtype, void* stream) {
+  if (batch < 0 || seqlen < 0 || nheads < 0 || headdim < 1 || dstate < 1) return SSM_ERR_SHAPE;
+  if (io_dtype != SSM_F32 && io_dtype != SSM_BF16) return SSM_ERR_DTYPE;
+  if (softplus != 0 && softplus != 1) return SSM_ERR_FLAG;
+  if (dt_mode != SSM_DT_ZOH && dt_mode != SSM_DT_EULER) return SSM_ERR_FLAG;
+  int64_t tmp;
+  if (!mul3(batch, seqlen, nheads * headdim, &tmp) || !mul3(batch, seqlen, dstate, &tmp) ||
+      !mul3(batch, nheads * headdim, dstate, &tmp))
+    return SSM_ERR_SHAPE;
+  if (batch == 0 || nheads == 0) return SSM_OK;
+  if (!A) return SSM_ERR_NULL;
+  if (seqlen > 0 && (!x || !dt || !B || !C || !y)) return SSM_ERR_NULL;
+  // the MFMA kernel: bf16 operands, 64 channels per head, 64 or 128 states
+  if (io_dtype != SSM_BF16 || headdim != 64 || (dstate != 64 && dstate != 128))
+    return SSM_ERR_UNSUPPORTED;
+  const void* v16[5] = {x, z, y, B, C};
+  for (const void* q : v16)
+    if (q && !aligned(q, 16)) return SSM_ERR_ALIGN;
+  const void* f32_ptrs[7] = {dt, A, D, dt_bias, h0, last_state, nullptr};
+  for (const void* q : f32_ptrs)
+    if (q && !aligned(q, 4)) return SSM_ERR_ALIGN;
+  if (batch * nheads > 0x7fffffff) return SSM_ERR_UNSUPPORTED;
+
+  ssm66::SSDParams p;
+  p.x = x; p.B = B; p.C = C; p.z = z; p.dt = dt; p.A = A; p.D = D; p.dt_bias = dt_bias;
+  p.h0 = h0; p.y = y; p.last_state = last_state;
+  p.batch = batch; p.L = seqlen; p.nheads = nheads; p.P = headdim; p.N = dstate;
+  p.softplus = softplus;
+  const hipError_t e = ssm66::launch_ssd_fwd(p, dt_mode == SSM_DT_ZOH, z != nullptr,
+                                             (hipStream_t)stream);
+  return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
 int ssm_conv1d_fwd(const void* x, const float* weight, const float* bias, int silu,
                    const void* window_in, const int32_t* seq_lens, const uint8_t* reset,
                    void* out, void* window_out, int64_t batch, int64_t seqlen, int64_t dim,

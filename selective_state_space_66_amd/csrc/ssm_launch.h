@@ -49,6 +49,15 @@ struct ScanBwdParams {
   int softplus;
 };
 
+struct SSDParams {
+  const void *x, *B, *C, *z;  // bf16; z nullable
+  const float *dt, *A, *D, *dt_bias, *h0;  // D, dt_bias, h0 nullable
+  void* y;
+  float* last_state;  // nullable
+  int64_t batch, L, nheads, P, N;
+  int softplus;
+};
+
 struct ConvParams {
   const void* x;            // (batch, L, dim) io dtype; (batch, dim) for a step
   const float* w;           // (dim, k): w[c * k + i] multiplies the input i steps back
@@ -74,6 +83,8 @@ size_t scan_bwd_ckpt_bytes(int64_t batch, int64_t L, int64_t dim, int64_t N);
 size_t scan_bwd_workspace_bytes(int64_t batch, int64_t L, int64_t dim, int64_t N);
 hipError_t launch_scan_bwd(const ScanBwdParams& p, int io_dtype, bool zoh, bool gate,
                            hipStream_t stream);
+// P == 64, N in {64, 128}, bf16 io; 16-byte aligned x, z, y, B, C.
+hipError_t launch_ssd_fwd(const SSDParams& p, bool zoh, bool gate, hipStream_t stream);
 hipError_t launch_step(const StepParams& p, int io_dtype, bool zoh, bool gate, hipStream_t stream);
 
 }  // namespace ssm66

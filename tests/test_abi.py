@@ -35,8 +35,9 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = _declared_functions()
     assert set(names) == {"ssm_scan_fwd", "ssm_scan_fwd_ex", "ssm_scan_bwd",
-                          "ssm_scan_bwd_workspace_size", "ssm_step", "ssm_conv1d_fwd",
-                          "ssm_conv1d_step", "ssm_status_string", "ssm_abi_version"}
+                          "ssm_scan_bwd_workspace_size", "ssm_step", "ssm_ssd_fwd",
+                          "ssm_conv1d_fwd", "ssm_conv1d_step", "ssm_status_string",
+                          "ssm_abi_version"}
     raw = ctypes.CDLL(ssm.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), f"{n} not exported"
@@ -208,3 +209,33 @@ def test_bwd_workspace_size(lib):
     assert f(2, 40, 70, 16) >= 4 * 2 * 3 * 70 * 16  # three 16-token checkpoints per row
     assert f(-1, 4, 4, 4) == 0 and f(1, 4, 4, 17) == 0
     assert f(8, 2048, 1536, 16) > f(8, 1024, 1536, 16)
+
+
+ALIGN16 = ctypes.c_void_p(0x10000)
+OFF8 = ctypes.c_void_p(0x10008)
+
+
+def _ssd(lib, **kw):
+    a = dict(x=ALIGN16, dt=FAKE, A=FAKE, B=ALIGN16, C=ALIGN16, D=None, z=None, bias=None,
+             softplus=1, dt_mode=1, h0=None, y=ALIGN16, last=None, batch=2, L=8, H=4, P=64,
+             N=128, io=1, stream=None)
+    a.update(kw)
+    return lib.ssm_ssd_fwd(a["x"], a["dt"], a["A"], a["B"], a["C"], a["D"], a["z"], a["bias"],
+                           a["softplus"], a["dt_mode"], a["h0"], a["y"], a["last"], a["batch"],
+                           a["L"], a["H"], a["P"], a["N"], a["io"], a["stream"])
+
+
+def test_ssd_invalid_arguments_are_rejected(lib):
+    c = _header_constants()
+    assert _ssd(lib, batch=-1) == c["SSM_ERR_SHAPE"]
+    assert _ssd(lib, P=0) == c["SSM_ERR_SHAPE"]
+    assert _ssd(lib, io=4) == c["SSM_ERR_DTYPE"]
+    assert _ssd(lib, dt_mode=9) == c["SSM_ERR_FLAG"]
+    assert _ssd(lib, x=None) == c["SSM_ERR_NULL"]
+    assert _ssd(lib, dt=None) == c["SSM_ERR_NULL"]
+    assert _ssd(lib, io=0) == c["SSM_ERR_UNSUPPORTED"]   # fp32 operands: not on this kernel
+    assert _ssd(lib, P=32) == c["SSM_ERR_UNSUPPORTED"]
+    assert _ssd(lib, N=96) == c["SSM_ERR_UNSUPPORTED"]
+    assert _ssd(lib, x=OFF8) == c["SSM_ERR_ALIGN"]        # 16-byte vectors
+    assert _ssd(lib, B=OFF8) == c["SSM_ERR_ALIGN"]
+    assert _ssd(lib, batch=0) == c["SSM_OK"]

@@ -331,7 +331,7 @@ class SSDConfig:
 
 
 SSD_CONFIGS: Dict[str, SSDConfig] = {
-    "ssd_tiny": SSDConfig("ssd_tiny", 2, 150, 3, 16, 32, "f32", True, 8),
+    "ssd_tiny": SSDConfig("ssd_tiny", 2, 150, 3, 64, 64, "bf16", True, 8),
     # a Mamba-2-130M-shaped layer: d_model 768, expand 2 -> 1536 = 24 heads x 64, N 128
     "ssd130m": SSDConfig("ssd130m", 8, 2048, 24, 64, 128, "bf16", True, 9),
 }
