@@ -216,7 +216,7 @@ __global__ __launch_bounds__((BShape<G, NG>::THREADS)) void scan_bwd_kernel(cons
         if (n0 + k < N) p.ckpt[((b * p.nchunks + ck) * dim + c) * N + n0 + k] = h[k];
     }
     stage(t0, false);
-    __syncthreads();
+    lds_barrier();
     const int nt = (int)(L - t0 < TC ? L - t0 : TC);
     for (int t = 0; t < nt; ++t) {
       const float4 d4 = sm.dd[t][cl];
@@ -229,7 +229,7 @@ __global__ __launch_bounds__((BShape<G, NG>::THREADS)) void scan_bwd_kernel(cons
         update_state(h[k], a, phi, d4.x, d4.y, sm.bc[t][g][k]);
       }
     }
-    __syncthreads();
+    lds_barrier();
   }
 
   // ---- pass 2: the chunks backwards
@@ -248,7 +248,7 @@ __global__ __launch_bounds__((BShape<G, NG>::THREADS)) void scan_bwd_kernel(cons
 #pragma unroll
     for (int k = 0; k < G; ++k)
       hst[k] = (cvalid && n0 + k < N) ? p.ckpt[((b * p.nchunks + ck) * dim + c) * N + n0 + k] : 0.0f;
-    __syncthreads();
+    lds_barrier();
 
     // recompute: states, abar and phi of the chunk; partial pre-gate readout
     float hs[TC][G], as[TC][G], ps[TC][G];
@@ -273,7 +273,7 @@ __global__ __launch_bounds__((BShape<G, NG>::THREADS)) void scan_bwd_kernel(cons
         sm.part[0][g][t * CW + cl] = acc;
       }
     }
-    __syncthreads();
+    lds_barrier();
     // dz = dy s silu'(z), s = C.h + D u (this thread's tokens)
     if constexpr (GATE) {
       if (p.want_dz) {
@@ -289,7 +289,7 @@ __global__ __launch_bounds__((BShape<G, NG>::THREADS)) void scan_bwd_kernel(cons
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
 
     // the adjoint backwards through the chunk, in two rounds of HALF tokens
 #pragma unroll
@@ -330,7 +330,7 @@ __global__ __launch_bounds__((BShape<G, NG>::THREADS)) void scan_bwd_kernel(cons
           sm.part[1][g][t * CW + cl] = dx;
         }
       }
-      __syncthreads();
+      lds_barrier();
       // dB, dC of these HALF tokens: sum over the block's channels
       for (int e = tid; e < 2 * HALF * NPAD; e += S::THREADS) {
         const int which = e / (HALF * NPAD);
@@ -344,7 +344,7 @@ __global__ __launch_bounds__((BShape<G, NG>::THREADS)) void scan_bwd_kernel(cons
           p.pbc[(((tile * 2 + which) * p.batch + b) * L + t0 + t) * N + n] = s;
         }
       }
-      __syncthreads();
+      lds_barrier();
     }
 
     // epilogue: d(raw delta), du; sums for dD and d bias
@@ -367,7 +367,7 @@ __global__ __launch_bounds__((BShape<G, NG>::THREADS)) void scan_bwd_kernel(cons
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
   }
 
   // ---- per-block results: dh0 (the carried adjoint is abar_0 g_0), dA,
@@ -383,7 +383,7 @@ __global__ __launch_bounds__((BShape<G, NG>::THREADS)) void scan_bwd_kernel(cons
   }
   sm.chan[0][g][cl] = accD;
   sm.chan[1][g][cl] = accB;
-  __syncthreads();
+  lds_barrier();
   if (g == 0 && cvalid) {
     float sD = 0.0f, sB = 0.0f;
     for (int j = 0; j < NG; ++j) {

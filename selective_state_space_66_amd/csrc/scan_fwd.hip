@@ -428,7 +428,7 @@ __global__ __launch_bounds__((Shape<G, NG>::THREADS)) void scan_fwd_kernel(
       chunk_resets = __syncthreads_or(mine) != 0;
     } else {
       if (ck + 1 < nchunks) prefetch(t0 + TC);
-      __syncthreads();
+      lds_barrier();
     }
 
     // ---- the recurrence for this thread's states over the chunk's real tokens
@@ -445,7 +445,7 @@ __global__ __launch_bounds__((Shape<G, NG>::THREADS)) void scan_fwd_kernel(
       else if (!careful) run(PathTag<Path::kZohFast>());
       else run(PathTag<Path::kZohCareful>());
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- epilogue: reduce the partial readouts, skip, gate, store
     if (full && tile_full) {

@@ -197,7 +197,7 @@ __global__ __launch_bounds__(256) void ssd_fwd_kernel(const SSDArgs p) {
       sm.eend[s] = exp2_hw((cend - cum) * kLog2e) * wt;
       sm.et[s] = exp2_hw(cum * kLog2e);
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- masked scores S = (C B^T) * L for rows 16 w .. 16 w + 15
 #pragma unroll
@@ -219,7 +219,7 @@ __global__ __launch_bounds__(256) void ssd_fwd_kernel(const SSDArgs p) {
         sm.Ss[t][s] = to_bf(val);
       }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- Y = exp(cum_t) (C H_in^T) + S X, rows 16 w .., columns 16 pt ..
     f32x4 Y[4];
@@ -285,7 +285,7 @@ __global__ __launch_bounds__(256) void ssd_fwd_kernel(const SSDArgs p) {
         Hacc[nt] = mfma16(a, bb, Hacc[nt]);
       }
     }
-    __syncthreads();  // every wave is done with Hs, Bs, Bt, Cs, Xt, Ss of this chunk
+    lds_barrier();  // every wave is done with Hs, Bs, Bt, Cs, Xt, Ss of this chunk
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll

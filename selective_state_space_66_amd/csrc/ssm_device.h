@@ -33,6 +33,19 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return lo | (hi << 16);
 }
 
+// Barrier for data exchanged through LDS only.  __syncthreads() also fences
+// global memory at workgroup scope, which makes every wave wait for all of its
+// outstanding global loads (vmcnt(0)) -- including loads issued ahead of time
+// for the next chunk.  Here each wave waits for its own LDS operations
+// (lgkmcnt(0); vmcnt and expcnt left alone), then meets the others; the signal
+// fence stops the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float log2_hw(float x) { return __builtin_amdgcn_logf(x); }
 __device__ __forceinline__ float rcp_hw(float x) { return __builtin_amdgcn_rcpf(x); }
