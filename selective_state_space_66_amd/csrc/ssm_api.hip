@@ -215,7 +215,7 @@ int ssm_ssd_fwd(const void* x, const float* dt, const float* A, const void* B, c
   const void* f32_ptrs[7] = {dt, A, D, dt_bias, h0, last_state, nullptr};
   for (const void* q : f32_ptrs)
     if (q && !aligned(q, 4)) return SSM_ERR_ALIGN;
-  if (batch * nheads > 0x7fffffff) return SSM_ERR_UNSUPPORTED;
+  if (batch * nheads > 0x7fffffff / 4) return SSM_ERR_UNSUPPORTED;  // 4 blocks per head
 
   ssm66::SSDParams p;
   p.x = x; p.B = B; p.C = C; p.z = z; p.dt = dt; p.A = A; p.D = D; p.dt_bias = dt_bias;
