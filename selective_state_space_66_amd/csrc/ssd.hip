@@ -88,7 +88,7 @@ __device__ __forceinline__ bf16x8 tr_frag(const __bf16* base, int lane) {
 // banks.  Xs rows are 32 bytes, so the 16 lanes of a transposing read (4 rows
 // x 4 column quads) cover the 32 banks once.
 template <int N>
-struct SSDSmem {
+struct alignas(16) SSDSmem {
   static constexpr int BS = N + 8;
   static constexpr int SS = kQ + 8;
   __bf16 Bs[kQ][BS];            // B rows of the chunk (n contiguous)
