@@ -83,6 +83,15 @@ __device__ __forceinline__ bf16x8 tr_frag(const __bf16* base, int lane) {
   return __builtin_bit_cast(bf16x8, v);
 }
 
+// Per-token constants of one chunk, from its step sizes.
+struct ChunkConsts {
+  float cuml[kQ];   // running sum of Delta A in the chunk, times log2 e
+  float wv[kQ];     // input weight w_s
+  float fw[kQ];     // exp(cum* - cum_s) w_s, cum* = cum at the end of s's 16-block
+  float eend[kQ];   // exp(cum_Q - cum_s) w_s
+  float et[kQ];     // exp(cum_t)
+};
+
 // Row strides (bf16 elements).  Bs and Hs rows are read 16 bytes per lane,
 // rows l % 16: a stride of 4 dwords mod 32 puts 8 consecutive rows on distinct
 // banks.  Xs rows are 32 bytes, so the 16 lanes of a transposing read (4 rows
@@ -95,10 +104,7 @@ struct alignas(16) SSDSmem {
   __bf16 Xs[kQ][kPS];           // this block's x columns (p contiguous)
   __bf16 Ss[kQ][SS];            // masked scores S[t][s] (s contiguous)
   __bf16 Hs[2][kPS][BS];        // the state entering the chunk, bf16, double-buffered
-  float cuml[kQ];               // running sum of Delta A in the chunk, times log2 e
-  float wv[kQ];                 // input weight w_s
-  float eend[kQ];               // exp(cum_Q - cum_s) w_s
-  float et[kQ];                 // exp(cum_t)
+  ChunkConsts cc[2];            // per-token constants, double-buffered by chunk parity
 };
 
 struct SSDArgs {
@@ -109,6 +115,76 @@ struct SSDArgs {
   int64_t batch, L, nheads;
   int softplus;
 };
+
+// Inclusive prefix sum over the 64 lanes of a wave with DPP: shifts of 1, 2,
+// 4 and 8 lanes inside each row of 16 (lanes shifted in from outside the row
+// add 0), then the last lane of row 0 and 2 added to rows 1 and 3, and lane 31
+// added to rows 2 and 3.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_or_zero(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWS, 0xf, true));
+}
+__device__ __forceinline__ float wave_inclusive_sum(float v) {
+  v += dpp_or_zero<0x111, 0xf>(v);  // row_shr:1
+  v += dpp_or_zero<0x112, 0xf>(v);  // row_shr:2
+  v += dpp_or_zero<0x114, 0xf>(v);  // row_shr:4
+  v += dpp_or_zero<0x118, 0xf>(v);  // row_shr:8
+  v += dpp_or_zero<0x142, 0xa>(v);  // row_bcast:15 into rows 1, 3
+  v += dpp_or_zero<0x143, 0xc>(v);  // row_bcast:31 into rows 2, 3
+  return v;
+}
+
+__device__ __forceinline__ float lane_value(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
+// The scores of token block W (waves are specialised on it: all branches on
+// it are uniform): S^T tiles D[s][t] = sum_n B[s][n] C[t][n] for the s
+// blocks sb <= W, the tiles' MFMA chains interleaved, then masked and
+// weighted to S[t][s] = D exp(cum_t - cum_s) w_s (s <= t).  Below the diagonal
+// block the decay factors through the end of block sb, cum*:
+// exp(cum_t - cum*) exp(cum* - cum_s) w_s, both factors at most 1, the second
+// one per token (fw) -- one exponential per lane and tile.  On the diagonal
+// block it is taken directly.  Lane value i is s = 16 sb + 4 lk + i,
+// t = 16 W + lr.
+template <int W, int N, class Sm>
+__device__ __forceinline__ void chunk_scores(Sm& sm, const ChunkConsts& kc, const u32x4 (&cC)[N / 32],
+                                             int lr, int lk) {
+  f32x4 g[W + 1];
+#pragma unroll
+  for (int sb = 0; sb <= W; ++sb) g[sb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int k = 0; k < N / 32; ++k)
+#pragma unroll
+    for (int sb = 0; sb <= W; ++sb)
+      g[sb] = mfma16(*(const bf16x8*)&sm.Bs[16 * sb + lr][32 * k + 8 * lk], as_bf16x8(cC[k]), g[sb]);
+  const float ct = kc.cuml[16 * W + lr];
+#pragma unroll
+  for (int sb = 0; sb <= W; ++sb) {
+    float v[4];
+    if (sb < W) {
+      const float gt = exp2_hw(ct - kc.cuml[16 * sb + 15]);
+      const float4 fw = *(const float4*)&kc.fw[16 * sb + 4 * lk];
+      v[0] = g[sb][0] * fw.x * gt;
+      v[1] = g[sb][1] * fw.y * gt;
+      v[2] = g[sb][2] * fw.z * gt;
+      v[3] = g[sb][3] * fw.w * gt;
+    } else {
+      const float4 cs = *(const float4*)&kc.cuml[16 * sb + 4 * lk];
+      const float4 ws = *(const float4*)&kc.wv[16 * sb + 4 * lk];
+      const float csv[4] = {cs.x, cs.y, cs.z, cs.w}, wsv[4] = {ws.x, ws.y, ws.z, ws.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float e = exp2_hw(fminf(ct - csv[i], 0.0f));  // s > t is masked below
+        v[i] = (4 * lk + i <= lr) ? g[sb][i] * e * wsv[i] : 0.0f;
+      }
+    }
+    *(u32x2*)&sm.Ss[16 * W + lr][16 * sb + 4 * lk] =
+        u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+  }
+  if constexpr (W % 2 == 0)  // the tile past the diagonal that the 32-wide k-steps of S X read
+    *(u32x2*)&sm.Ss[16 * W + lr][16 * (W + 1) + 4 * lk] = u32x2{0u, 0u};
+}
 
 template <int N, bool ZOH, bool GATE>
 __global__ __launch_bounds__(256, 3) void ssd_fwd_kernel(const SSDArgs p) {
@@ -129,8 +205,9 @@ __global__ __launch_bounds__(256, 3) void ssd_fwd_kernel(const SSDArgs p) {
   const int q = (int)(logical - bh * kSlices);
   const int64_t b = bh / H, h = bh - b * H;
   const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6;   // wave w: token block 16 w .. 16 w + 15
-  const int lr = lane & 15, lk = lane >> 4;  // MFMA row / k-group of this lane
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave: token block 16 w ..
+  const int lr = lane & 15, lk = lane >> 4;                // MFMA row / k-group of this lane
   const float A = p.A[h];
   const float Dh = p.D ? p.D[h] : 0.0f;
   const float bias = p.dt_bias ? p.dt_bias[h] : 0.0f;
@@ -152,151 +229,140 @@ __global__ __launch_bounds__(256, 3) void ssd_fwd_kernel(const SSDArgs p) {
         u32x2{pack_bf16x2(Hacc[j][0], Hacc[j][1]), pack_bf16x2(Hacc[j][2], Hacc[j][3])};
   }
 
-  // ---- global reads of one chunk into registers; rows past L are clamped to
-  // the last row (finite data that the zero weights of padding tokens cancel).
-  // Issued for the next chunk before this chunk's products.
+  // ---- global reads of one chunk into registers, addressed as a uniform
+  // chunk base plus 32-bit byte offsets; rows past L are clamped to the last
+  // row (finite data that the zero weights of padding tokens cancel).  Issued
+  // for the next chunk before this chunk's products.
   u32x4 rB[RB], rC[NK];
   u32x2 rX, rZ = u32x2{0u, 0u};
   float rdt;
+  const int tz = 16 * w + lr;   // token of this lane's C row, z and output
+  const int tx = tid >> 2;      // token of this thread's x piece
   auto load_chunk = [&](int64_t t0) {
-    const int64_t last = L - 1;
+    const int lim = (int)(L - 1 - t0 < kQ - 1 ? L - 1 - t0 : kQ - 1);  // last row of the chunk
+    const char* Bc = (const char*)(p.B + (b * L + t0) * N);
+    const char* Cc = (const char*)(p.C + (b * L + t0) * N);
+    const char* Xc = (const char*)(p.x + (b * L + t0) * HP + ch0);
+    const char* Zc = (const char*)(p.z + (b * L + t0) * HP + ch0);
+    const char* Dc = (const char*)(p.dt + (b * L + t0) * H + h);
+    {  // first, so that waiting for it does not wait for the rest
+      const uint32_t rd = (uint32_t)(lane < lim ? lane : lim);
+      rdt = *(const float*)(Dc + rd * (uint32_t)H * 4u);
+    }
 #pragma unroll
     for (int r = 0; r < RB; ++r) {
       const int e = tid + 256 * r;
       const int s = e / (N / 8), c8 = (e % (N / 8)) * 8;
-      const int64_t row = b * L + (t0 + s < L ? t0 + s : last);
-      rB[r] = *(const u32x4*)(p.B + row * N + c8);
+      const uint32_t off = (uint32_t)((s < lim ? s : lim) * N + c8) * 2u;
+      rB[r] = *(const u32x4*)(Bc + off);
     }
-    {  // C rows of this wave's token block; z of this lane's output
-      const int64_t t = t0 + 16 * w + lr;
-      const int64_t row = b * L + (t < L ? t : last);
+    const uint32_t rz = (uint32_t)(tz < lim ? tz : lim);
+    const uint32_t offc = (rz * N + 8 * lk) * 2u;
 #pragma unroll
-      for (int k = 0; k < NK; ++k) rC[k] = *(const u32x4*)(p.C + row * N + 32 * k + 8 * lk);
-      if constexpr (GATE) rZ = *(const u32x2*)(p.z + row * HP + ch0 + 4 * lk);
-    }
-    {  // x: token tid / 4, channels 4 (tid % 4) ..
-      const int64_t t = t0 + (tid >> 2);
-      const int64_t row = b * L + (t < L ? t : last);
-      rX = *(const u32x2*)(p.x + row * HP + ch0 + 4 * (tid & 3));
-    }
-    {
-      const int64_t t = t0 + lane;
-      rdt = p.dt[(b * L + (t < L ? t : last)) * H + h];
-    }
+    for (int k = 0; k < NK; ++k) rC[k] = *(const u32x4*)(Cc + offc + 64 * k);
+    if constexpr (GATE) rZ = *(const u32x2*)(Zc + (rz * (uint32_t)HP + 4 * lk) * 2u);
+    const uint32_t rx = (uint32_t)(tx < lim ? tx : lim);
+    rX = *(const u32x2*)(Xc + (rx * (uint32_t)HP + 4 * (tid & 3)) * 2u);
   };
 
+  // ---- step sizes, decays and weights of a chunk (wave 0, lane = token)
+  auto chunk_consts = [&](ChunkConsts& kc, float raw, int nlive) {
+    const float v = raw + bias;
+    float dl = p.softplus ? softplus_f(v) : v;
+    if (lane >= nlive) dl = 0.0f;  // padding: no decay, no input
+    const float a = dl * A;
+    float wt = dl;
+    if constexpr (ZOH) wt = dl * zoh_phi(a, exp2_hw(a * kLog2e));
+    const float c = wave_inclusive_sum(a * kLog2e);  // running sum, log2 units
+    const float cb0 = lane_value(c, 15), cb1 = lane_value(c, 31), cb2 = lane_value(c, 47);
+    const float cend = lane_value(c, 63);
+    const float cblk = lane < 16 ? cb0 : (lane < 32 ? cb1 : (lane < 48 ? cb2 : cend));
+    kc.cuml[lane] = c;
+    kc.wv[lane] = wt;
+    kc.fw[lane] = exp2_hw(cblk - c) * wt;
+    kc.eend[lane] = exp2_hw(cend - c) * wt;
+    kc.et[lane] = exp2_hw(c);
+  };
+
+  // Per chunk, three phases between LDS barriers:
+  //   A: stage B and x; issue the next chunk's reads; Y^T starts with
+  //      H_in C^T (the state from the previous chunk) and the gate's silu;
+  //   B: the scores S (needs all of B); Y^T scaled by exp(cum_t);
+  //   C: Y^T += x^T S^T, epilogue and store; the state update; wave 0 forms
+  //      the next chunk's per-token constants.
   const int64_t nchunks = (L + kQ - 1) / kQ;
-  if (nchunks > 0) load_chunk(0);
+  if (nchunks > 0) {
+    load_chunk(0);
+    if (w == 0) chunk_consts(sm.cc[0], rdt, (int)(L < kQ ? L : kQ));
+  }
   for (int64_t ck = 0; ck < nchunks; ++ck) {
     const int64_t t0 = ck * kQ;
     const int nlive = (int)(L - t0 < kQ ? L - t0 : kQ);
-    const int cur = (int)(ck & 1);
+    const int cur = (int)(ck & 1), nxt = cur ^ 1;
+    const ChunkConsts& kc = sm.cc[cur];
 
-    // ---- stage B rows and the x columns (x rows past L as zeros)
+    // ---- A: stage B rows and the x columns (x rows past L as zeros)
 #pragma unroll
     for (int r = 0; r < RB; ++r) {
       const int e = tid + 256 * r;
       *(u32x4*)&sm.Bs[e / (N / 8)][(e % (N / 8)) * 8] = rB[r];
     }
-    *(u32x2*)&sm.Xs[tid >> 2][4 * (tid & 3)] = (tid >> 2) < nlive ? rX : u32x2{0u, 0u};
+    *(u32x2*)&sm.Xs[tx][4 * (tid & 3)] = tx < nlive ? rX : u32x2{0u, 0u};
     u32x4 cC[NK];
 #pragma unroll
     for (int k = 0; k < NK; ++k) cC[k] = rC[k];
-    const u32x2 cZ = rZ;
-    const float raw = rdt;
+    float gz[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+    if constexpr (GATE) {
+      gz[0] = lo_bf(rZ.x);
+      gz[1] = hi_bf(rZ.x);
+      gz[2] = lo_bf(rZ.y);
+      gz[3] = hi_bf(rZ.y);
+    }
     if (ck + 1 < nchunks) load_chunk(t0 + kQ);
-
-    // ---- step sizes, decays and weights of the chunk (wave 0, lane = token)
-    if (w == 0) {
-      const float v = raw + bias;
-      float dl = p.softplus ? softplus_f(v) : v;
-      if (lane >= nlive) dl = 0.0f;  // padding: no decay, no input
-      const float a = dl * A;
-      float wt = dl;
-      if constexpr (ZOH) wt = dl * zoh_phi(a, exp2_hw(a * kLog2e));
-      float c = a * kLog2e;  // inclusive running sum, log2 units
+    // Y^T for token block w: D[p][t] = sum_n H[p][n] C[t][n] first; lane value
+    // i is p = 4 lk + i, t = 16 w + lr
+    f32x4 y = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float o = __shfl_up(c, off, 64);
-        if (lane >= off) c += o;
-      }
-      const float cend = __shfl(c, 63, 64);
-      sm.cuml[lane] = c;
-      sm.wv[lane] = wt;
-      sm.eend[lane] = exp2_hw(cend - c) * wt;
-      sm.et[lane] = exp2_hw(c);
+    for (int k = 0; k < NK; ++k)
+      y = mfma16(*(const bf16x8*)&sm.Hs[cur][lr][32 * k + 8 * lk], as_bf16x8(cC[k]), y);
+    if constexpr (GATE) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) gz[i] = silu_f(gz[i]);
     }
     lds_barrier();
 
-    // ---- scores of this wave's token block t = 16 w .. : S^T tiles
-    // D[s][t] = sum_n B[s][n] C[t][n], masked to S[t][s] = D exp(cum_t - cum_s) w_s
-    // (s <= t); lane value i is s = 16 sb + 4 lk + i, t = 16 w + lr
-    {
-      const float ct = sm.cuml[16 * w + lr];
-#pragma unroll
-      for (int sb = 0; sb < 4; ++sb) {
-        if (sb <= w) {
-          f32x4 g = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-          for (int k = 0; k < NK; ++k)
-            g = mfma16(*(const bf16x8*)&sm.Bs[16 * sb + lr][32 * k + 8 * lk], as_bf16x8(cC[k]), g);
-          const float4 cs = *(const float4*)&sm.cuml[16 * sb + 4 * lk];
-          const float4 ws = *(const float4*)&sm.wv[16 * sb + 4 * lk];
-          const float csv[4] = {cs.x, cs.y, cs.z, cs.w}, wsv[4] = {ws.x, ws.y, ws.z, ws.w};
-          float v[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const bool keep = sb < w || 4 * lk + i <= lr;  // s <= t
-            v[i] = keep ? g[i] * exp2_hw(ct - csv[i]) * wsv[i] : 0.0f;
-          }
-          *(u32x2*)&sm.Ss[16 * w + lr][16 * sb + 4 * lk] =
-              u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-        } else if (sb == w + 1 && (w & 1) == 0) {
-          // the tile past the diagonal that the 32-wide k-steps of S X read
-          *(u32x2*)&sm.Ss[16 * w + lr][16 * sb + 4 * lk] = u32x2{0u, 0u};
-        }
-      }
+    // ---- B: scores of this wave's token block
+    switch (w) {
+      case 0: chunk_scores<0, N>(sm, kc, cC, lr, lk); break;
+      case 1: chunk_scores<1, N>(sm, kc, cC, lr, lk); break;
+      case 2: chunk_scores<2, N>(sm, kc, cC, lr, lk); break;
+      default: chunk_scores<3, N>(sm, kc, cC, lr, lk); break;
     }
-    lds_barrier();
-
-    // ---- Y^T for token block w: D[p][t] = exp(cum_t) sum_n H[p][n] C[t][n]
-    //      + sum_s x[s][p] S[t][s]; lane value i is p = 4 lk + i, t = 16 w + lr
     {
-      f32x4 y = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int k = 0; k < NK; ++k)
-        y = mfma16(*(const bf16x8*)&sm.Hs[cur][lr][32 * k + 8 * lk], as_bf16x8(cC[k]), y);
-      const float e = sm.et[16 * w + lr];
+      const float e = kc.et[tz];
 #pragma unroll
       for (int i = 0; i < 4; ++i) y[i] *= e;
-#pragma unroll
-      for (int s0 = 0; s0 < kQ; s0 += 32) {
-        if (s0 <= 16 * w + 15) {  // scores past the diagonal block are zero
-          const bf16x8 xa = tr_frag<kPS>(&sm.Xs[s0][0], lane);
-          y = mfma16(xa, *(const bf16x8*)&sm.Ss[16 * w + lr][s0 + 8 * lk], y);
-        }
-      }
-      // ---- epilogue: skip, gate, store 4 channels of token t
-      const int t = 16 * w + lr;
-      if (t < nlive) {
-        const u32x2 xv = *(const u32x2*)&sm.Xs[t][4 * lk];
-        float o[4] = {fmaf(Dh, lo_bf(xv.x), y[0]), fmaf(Dh, hi_bf(xv.x), y[1]),
-                      fmaf(Dh, lo_bf(xv.y), y[2]), fmaf(Dh, hi_bf(xv.y), y[3])};
-        if constexpr (GATE) {
-          o[0] *= silu_f(lo_bf(cZ.x));
-          o[1] *= silu_f(hi_bf(cZ.x));
-          o[2] *= silu_f(lo_bf(cZ.y));
-          o[3] *= silu_f(hi_bf(cZ.y));
-        }
-        *(u32x2*)(p.y + (b * L + t0 + t) * HP + ch0 + 4 * lk) =
-            u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
-      }
+    }
+    lds_barrier();
+
+    // ---- C: Y^T += sum_s x[s][p] S[t][s]; skip, gate, store 4 channels of token tz
+    y = mfma16(tr_frag<kPS>(&sm.Xs[0][0], lane), *(const bf16x8*)&sm.Ss[tz][8 * lk], y);
+    if (w >= 2)  // scores of s >= 32: zero for the first two token blocks
+      y = mfma16(tr_frag<kPS>(&sm.Xs[32][0], lane), *(const bf16x8*)&sm.Ss[tz][32 + 8 * lk], y);
+    if (tz < nlive) {
+      const u32x2 xv = *(const u32x2*)&sm.Xs[tz][4 * lk];
+      const float o0 = fmaf(Dh, lo_bf(xv.x), y[0]) * gz[0];
+      const float o1 = fmaf(Dh, hi_bf(xv.x), y[1]) * gz[1];
+      const float o2 = fmaf(Dh, lo_bf(xv.y), y[2]) * gz[2];
+      const float o3 = fmaf(Dh, hi_bf(xv.y), y[3]) * gz[3];
+      char* Yc = (char*)(p.y + (b * L + t0) * HP + ch0);
+      *(u32x2*)(Yc + ((uint32_t)tz * (uint32_t)HP + 4 * lk) * 2u) =
+          u32x2{pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)};
     }
 
-    // ---- state update, H^T tiles: D[n][p] = exp(cum_Q) H^T[n][p]
-    //      + sum_s B[s][n] (eend_s x[s][p])
+    // state update, H^T tiles: D[n][p] = exp(cum_Q) H^T[n][p] + sum_s B[s][n] (eend_s x[s][p])
     {
-      const float etot = exp2_hw(sm.cuml[kQ - 1]);
+      const float etot = exp2_hw(kc.cuml[kQ - 1]);
 #pragma unroll
       for (int j = 0; j < NTW; ++j)
 #pragma unroll
@@ -304,8 +370,8 @@ __global__ __launch_bounds__(256, 3) void ssd_fwd_kernel(const SSDArgs p) {
 #pragma unroll
       for (int s0 = 0; s0 < kQ; s0 += 32) {
         const bf16x8 xt = tr_frag<kPS>(&sm.Xs[s0][0], lane);  // x[s0 + 8 lk + j][lr]
-        const float4 e0 = *(const float4*)&sm.eend[s0 + 8 * lk];
-        const float4 e1 = *(const float4*)&sm.eend[s0 + 8 * lk + 4];
+        const float4 e0 = *(const float4*)&kc.eend[s0 + 8 * lk];
+        const float4 e1 = *(const float4*)&kc.eend[s0 + 8 * lk + 4];
         const float ev[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
         bf16x8 xw;
 #pragma unroll
@@ -316,13 +382,16 @@ __global__ __launch_bounds__(256, 3) void ssd_fwd_kernel(const SSDArgs p) {
           Hacc[j] = mfma16(bt, xw, Hacc[j]);
         }
       }
-      const int nxt = cur ^ 1;  // last read in the previous chunk, before its barriers
+      // Hs[nxt] was last read in the previous chunk, before its barriers
 #pragma unroll
       for (int j = 0; j < NTW; ++j)
         *(u32x2*)&sm.Hs[nxt][lr][16 * (w + kWaves * j) + 4 * lk] =
             u32x2{pack_bf16x2(Hacc[j][0], Hacc[j][1]), pack_bf16x2(Hacc[j][2], Hacc[j][3])};
     }
-    lds_barrier();  // every wave is done with Bs, Xs, Ss and the chunk's constants
+    // the next chunk's constants (its step sizes arrived with this chunk's prefetch)
+    if (w == 0 && ck + 1 < nchunks)
+      chunk_consts(sm.cc[nxt], rdt, (int)(L - t0 - kQ < kQ ? L - t0 - kQ : kQ));
+    lds_barrier();  // every wave is done with Bs, Xs, Ss and this chunk's constants
   }
 
   if (p.last_state) {
