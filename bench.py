@@ -72,10 +72,22 @@ def step_bytes(b, D, N, io_bytes, gate):
     return 8 * b * D * N + (streamed + 1) * b * D * io_bytes + 2 * b * N * io_bytes + 4 * D * N + 8 * D
 
 
-def kernel_source_hash():
+# The sources each measured kernel is built from: its own file, plus the shared
+# device and launch headers and the C-ABI file that picks its launch shape.
+KERNEL_SOURCES = {
+    "scan_fwd_mamba130m_zoh": ["scan_fwd.hip"],
+    "step_decode_zoh": ["step.hip"],
+    "conv1d_fwd_conv130m": ["conv1d.hip"],
+    "ssd_fwd_ssd130m": ["ssd.hip"],
+}
+COMMON_SOURCES = ["ssm_device.h", "ssm_launch.h", "ssm_api.hip"]
+
+
+def kernel_source_hash(kernel_key):
+    """Hash of the sources the kernel `kernel_key` is built from."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "selective_state_space_66_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in sorted(KERNEL_SOURCES[kernel_key] + COMMON_SOURCES):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
@@ -83,7 +95,7 @@ def kernel_source_hash():
 
 def measured_traffic(kernel_key):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel source; else None."""
+    was taken on the kernel's current sources; else None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as f:
@@ -91,7 +103,7 @@ def measured_traffic(kernel_key):
     except (OSError, ValueError):
         return None
     ent = data.get(kernel_key)
-    if not ent or ent.get("source_hash") != kernel_source_hash():
+    if not ent or ent.get("source_hash") != kernel_source_hash(kernel_key):
         return None
     return ent.get("bytes_per_launch")
 
@@ -273,7 +285,7 @@ def time_ssd(dev, steps, warmup, nsets=3):
             "roofline": {"bound": "hbm", "achieved": round(nb / (ms * 1e-3) / 1e9, 2),
                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                         "algorithmic_bytes": nb},
+                         "algorithmic_bytes": nb, "traffic": measured_traffic("ssd_fwd_ssd130m")},
             "mfma": {"achieved_TFLOPs": round(fl / (ms * 1e-3) / 1e12, 2), "peak_TFLOPs": 2500.0,
                      "flops": fl}}
 
@@ -547,7 +559,8 @@ def main():
                    "steps": args.decode_steps,
                    "tok_per_s": round(dcfg.batch * args.decode_steps / d_wall_s, 1),
                    "us_per_step": round(d_kern_ms * 1e3, 3),
-                   "GB/s": round(d_bytes / (d_kern_ms * 1e-3) / 1e9, 2)},
+                   "GB/s": round(d_bytes / (d_kern_ms * 1e-3) / 1e9, 2),
+                   "algorithmic_bytes": d_bytes, "traffic": measured_traffic("step_decode_zoh")},
     }
     print(json.dumps(out), flush=True)
 
