@@ -138,36 +138,70 @@ __global__ __launch_bounds__((BShape<G, NG>::THREADS)) void scan_bwd_kernel(cons
   const int n0 = g * G;
   const int64_t row0 = b * L;
 
-  float Aa[G], Ap[G];
+  float Aa[G], Ap[G], CA[G];
+  bool small_a = false;
 #pragma unroll
   for (int k = 0; k < G; ++k) {
     const bool real = cvalid && (n0 + k) < N;
     Aa[k] = real ? p.A[c * N + n0 + k] : 0.0f;
     Ap[k] = Aa[k] * kLog2e;
+    CA[k] = Aa[k] != 0.0f ? 1.0f / Aa[k] : 0.0f;
+    if (real && !(fabsf(Aa[k]) >= 0.5f)) small_a = true;
   }
+  // pass 1 under ZOH keeps g = A h, as the forward's fast form, unless a lane
+  // of the wave has a small |A| (wave-uniform choice)
+  const bool fast = ZOH && !__any(small_a);
   const float bias = p.bias ? p.bias[cc] : 0.0f;
   const float dskip = p.D ? p.D[cc] : 0.0f;
 
-  // ---- stage one chunk: (Delta, u, ds) per (token, channel), B and C per
-  // (token, state); the epilogue values of this thread's tokens stay in
-  // registers.  Tokens past L get zeros.
+  // ---- raw inputs of one chunk, read into registers a chunk ahead through
+  // addresses clamped into the tensors (no branch around a load): u, raw
+  // Delta (and dy, z in pass 2) of this thread's tokens, and the B (and C)
+  // values of one (token, state group) -- TC * NG of them, one per thread.
+  static_assert(TC * NG == S::THREADS, "one (token, group) of B and C per thread");
+  const int btt = tid / NG, bgg = tid % NG;
+  IO ru[RPT], rdl[RPT], rdy[RPT], rz[RPT], rb[G], rc[G];
+  auto load_raw = [&](int64_t t0, bool bwd) {
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const int64_t t = t0 + g + NG * i;
+      const int64_t idx = (row0 + (t < L ? t : L - 1)) * dim + cc;
+      ru[i] = u[idx];
+      rdl[i] = dr[idx];
+      if (bwd) {
+        rdy[i] = dyp[idx];
+        if constexpr (GATE) rz[i] = zz[idx];
+      }
+    }
+    const int64_t t = t0 + btt;
+    const int64_t base = (row0 + (t < L ? t : L - 1)) * N;
+#pragma unroll
+    for (int k = 0; k < G; ++k) {
+      const int n = bgg * G + k;
+      const int64_t bi = base + (n < N ? n : N - 1);
+      rb[k] = Bm[bi];
+      if (bwd) rc[k] = Cm[bi];
+    }
+  };
+
+  // ---- stage one chunk from the raw registers: (Delta, u, ds) per (token,
+  // channel), B and C per (token, state); the epilogue values of this
+  // thread's tokens stay in registers.  Tokens past L get zeros.
   float e_dy[RPT], e_sv[RPT], e_gz[RPT], e_dg[RPT], e_u[RPT], e_ds[RPT];
   auto stage = [&](int64_t t0, bool bwd) {
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
       const int r = g + NG * i;
-      const int64_t t = t0 + r;
-      const bool live = t < L;
-      const int64_t idx = (row0 + (live ? t : L - 1)) * dim + cc;
-      const float x = live ? to_f32(u[idx]) : 0.0f;
-      const float v = to_f32(dr[idx]) + bias;
+      const bool live = t0 + r < L;
+      const float x = live ? to_f32(ru[i]) : 0.0f;
+      const float v = to_f32(rdl[i]) + bias;
       const float dl = live ? (p.softplus ? softplus_f(v) : v) : 0.0f;
       float ds = 0.0f;
       if (bwd) {
-        const float dyv = live ? to_f32(dyp[idx]) : 0.0f;
+        const float dyv = live ? to_f32(rdy[i]) : 0.0f;
         float gz = 1.0f, dg = 0.0f;
         if constexpr (GATE) {
-          const float zv = to_f32(zz[idx]);
+          const float zv = to_f32(rz[i]);
           const float sg = rcp_hw(1.0f + exp2_hw(-zv * kLog2e));  // sigma(z)
           gz = zv * sg;                                          // silu(z)
           dg = sg * fmaf(zv, 1.0f - sg, 1.0f);                   // silu'(z)
@@ -183,18 +217,12 @@ __global__ __launch_bounds__((BShape<G, NG>::THREADS)) void scan_bwd_kernel(cons
       }
       sm.dd[r][cl] = make_float4(dl, x, ds, 0.0f);
     }
-    // B and C: every thread stages whole groups of one token
-    for (int e = tid; e < TC * NG; e += S::THREADS) {
-      const int tt = e / NG, gg = e % NG;
-      const int64_t t = t0 + tt;
+    const bool live = t0 + btt < L;
 #pragma unroll
-      for (int k = 0; k < G; ++k) {
-        const int n = gg * G + k;
-        const bool ok = t < L && n < N;
-        const int64_t bi = (row0 + (t < L ? t : L - 1)) * N + (n < N ? n : N - 1);
-        sm.bc[tt][gg][k] = ok ? to_f32(Bm[bi]) : 0.0f;
-        sm.bc[tt][gg][G + k] = ok ? to_f32(Cm[bi]) : 0.0f;
-      }
+    for (int k = 0; k < G; ++k) {
+      const bool ok = live && bgg * G + k < N;
+      sm.bc[btt][bgg][k] = ok ? to_f32(rb[k]) : 0.0f;
+      if (bwd) sm.bc[btt][bgg][G + k] = ok ? to_f32(rc[k]) : 0.0f;
     }
   };
 
@@ -203,31 +231,56 @@ __global__ __launch_bounds__((BShape<G, NG>::THREADS)) void scan_bwd_kernel(cons
     h = fmaf(a, h, (ZOH ? dl * bw : dl) * Bv * x);
   };
 
-  // ---- pass 1: the states forward, one checkpoint per chunk start
+  // ---- pass 1: the states forward, one checkpoint per chunk start.  Under
+  // ZOH's fast form h holds g = A h: g = abar (g + u B) - u B exactly, and the
+  // checkpoint is g / A.
   float h[G];
 #pragma unroll
-  for (int k = 0; k < G; ++k)
+  for (int k = 0; k < G; ++k) {
     h[k] = (p.h0 && cvalid && n0 + k < N) ? p.h0[(b * dim + c) * N + n0 + k] : 0.0f;
+    if (fast) h[k] *= Aa[k];
+  }
+  auto p1_tokens = [&](auto full_tag, auto fast_tag, int nt) {
+    constexpr bool FULL = decltype(full_tag)::value, FAST = decltype(fast_tag)::value;
+#pragma unroll
+    for (int t = 0; t < TC; ++t) {
+      if (FULL || t < nt) {
+        const float4 d4 = sm.dd[t][cl];
+#pragma unroll
+        for (int k = 0; k < G; ++k) {
+          const float Bv = sm.bc[t][g][k];
+          const float a = exp2_hw(d4.x * Ap[k]);
+          if constexpr (FAST) {
+            const float ub = d4.y * Bv;
+            h[k] = fmaf(a, h[k] + ub, -ub);
+          } else {
+            float phi = 1.0f, dphi;
+            if constexpr (ZOH) phi_and_prime(d4.x * Aa[k], a, phi, dphi);
+            update_state(h[k], a, phi, d4.x, d4.y, Bv);
+          }
+        }
+      }
+    }
+  };
+  if (p.nchunks > 0) load_raw(0, false);
   for (int64_t ck = 0; ck < p.nchunks; ++ck) {
     const int64_t t0 = ck * TC;
     if (cvalid) {
 #pragma unroll
       for (int k = 0; k < G; ++k)
-        if (n0 + k < N) p.ckpt[((b * p.nchunks + ck) * dim + c) * N + n0 + k] = h[k];
+        if (n0 + k < N)
+          p.ckpt[((b * p.nchunks + ck) * dim + c) * N + n0 + k] = fast ? h[k] * CA[k] : h[k];
     }
     stage(t0, false);
+    if (ck + 1 < p.nchunks) load_raw(t0 + TC, false);
     lds_barrier();
     const int nt = (int)(L - t0 < TC ? L - t0 : TC);
-    for (int t = 0; t < nt; ++t) {
-      const float4 d4 = sm.dd[t][cl];
-#pragma unroll
-      for (int k = 0; k < G; ++k) {
-        const float kap = d4.x * Aa[k];
-        const float a = exp2_hw(d4.x * Ap[k]);
-        float phi = 1.0f, dphi;
-        if constexpr (ZOH) phi_and_prime(kap, a, phi, dphi);
-        update_state(h[k], a, phi, d4.x, d4.y, sm.bc[t][g][k]);
-      }
+    if (nt == TC) {
+      if (fast) p1_tokens(std::true_type(), std::true_type(), nt);
+      else p1_tokens(std::true_type(), std::false_type(), nt);
+    } else {
+      if (fast) p1_tokens(std::false_type(), std::true_type(), nt);
+      else p1_tokens(std::false_type(), std::false_type(), nt);
     }
     lds_barrier();
   }
@@ -240,14 +293,28 @@ __global__ __launch_bounds__((BShape<G, NG>::THREADS)) void scan_bwd_kernel(cons
     dA[k] = 0.0f;
   }
   float accD = 0.0f, accB = 0.0f;  // this thread's tokens: sum ds u, sum d(raw delta)
+  // the chunk's checkpoint is read with its inputs, a chunk ahead
+  float hnext[G];
+  auto load_ckpt = [&](int64_t ck) {
+#pragma unroll
+    for (int k = 0; k < G; ++k)
+      hnext[k] = p.ckpt[((b * p.nchunks + ck) * dim + cc) * N + (n0 + k < N ? n0 + k : N - 1)];
+  };
+  if (p.nchunks > 0) {
+    load_raw((p.nchunks - 1) * TC, true);
+    load_ckpt(p.nchunks - 1);
+  }
   for (int64_t ck = p.nchunks - 1; ck >= 0; --ck) {
     const int64_t t0 = ck * TC;
     const int nt = (int)(L - t0 < TC ? L - t0 : TC);
     stage(t0, true);
     float hst[G];
 #pragma unroll
-    for (int k = 0; k < G; ++k)
-      hst[k] = (cvalid && n0 + k < N) ? p.ckpt[((b * p.nchunks + ck) * dim + c) * N + n0 + k] : 0.0f;
+    for (int k = 0; k < G; ++k) hst[k] = (cvalid && n0 + k < N) ? hnext[k] : 0.0f;
+    if (ck > 0) {
+      load_raw(t0 - TC, true);
+      load_ckpt(ck - 1);
+    }
     lds_barrier();
 
     // recompute: states, abar and phi of the chunk; partial pre-gate readout
