@@ -318,28 +318,35 @@ __global__ __launch_bounds__((BShape<G, NG>::THREADS)) void scan_bwd_kernel(cons
     lds_barrier();
 
     // recompute: states, abar and phi of the chunk; partial pre-gate readout
+    // (for dz).  Full chunks run unguarded.
     float hs[TC][G], as[TC][G], ps[TC][G];
 #pragma unroll
     for (int k = 0; k < G; ++k) h[k] = hst[k];
+    const bool want_s = GATE && p.want_dz;
+    auto recompute = [&](auto full_tag) {
+      constexpr bool FULL = decltype(full_tag)::value;
 #pragma unroll
-    for (int t = 0; t < TC; ++t) {
-      if (t < nt) {
-        const float4 d4 = sm.dd[t][cl];
-        float acc = 0.0f;
+      for (int t = 0; t < TC; ++t) {
+        if (FULL || t < nt) {
+          const float4 d4 = sm.dd[t][cl];
+          float acc = 0.0f;
 #pragma unroll
-        for (int k = 0; k < G; ++k) {
-          const float a = exp2_hw(d4.x * Ap[k]);
-          float phi = 1.0f, dphi;
-          if constexpr (ZOH) phi_and_prime(d4.x * Aa[k], a, phi, dphi);
-          update_state(h[k], a, phi, d4.x, d4.y, sm.bc[t][g][k]);
-          hs[t][k] = h[k];
-          as[t][k] = a;
-          ps[t][k] = phi;
-          acc = fmaf(sm.bc[t][g][G + k], h[k], acc);
+          for (int k = 0; k < G; ++k) {
+            const float a = exp2_hw(d4.x * Ap[k]);
+            float phi = 1.0f, dphi;
+            if constexpr (ZOH) phi_and_prime(d4.x * Aa[k], a, phi, dphi);
+            update_state(h[k], a, phi, d4.x, d4.y, sm.bc[t][g][k]);
+            hs[t][k] = h[k];
+            as[t][k] = a;
+            ps[t][k] = phi;
+            acc = fmaf(sm.bc[t][g][G + k], h[k], acc);
+          }
+          if (want_s) sm.part[0][g][t * CW + cl] = acc;
         }
-        sm.part[0][g][t * CW + cl] = acc;
       }
-    }
+    };
+    if (nt == TC) recompute(std::true_type());
+    else recompute(std::false_type());
     lds_barrier();
     // dz = dy s silu'(z), s = C.h + D u (this thread's tokens)
     if constexpr (GATE) {
@@ -361,42 +368,47 @@ __global__ __launch_bounds__((BShape<G, NG>::THREADS)) void scan_bwd_kernel(cons
     // the adjoint backwards through the chunk, in two rounds of HALF tokens
 #pragma unroll
     for (int half = TC / HALF - 1; half >= 0; --half) {
+      auto reverse = [&](auto full_tag) {
+        constexpr bool FULL = decltype(full_tag)::value;
 #pragma unroll
-      for (int tt = HALF - 1; tt >= 0; --tt) {
-        const int t = half * HALF + tt;
-        if (t < nt) {
-          const float4 d4 = sm.dd[t][cl];
-          const float dl = d4.x, x = d4.y, ds = d4.z;
-          float ddt = 0.0f, dx = 0.0f;
+        for (int tt = HALF - 1; tt >= 0; --tt) {
+          const int t = half * HALF + tt;
+          if (FULL || t < nt) {
+            const float4 d4 = sm.dd[t][cl];
+            const float dl = d4.x, x = d4.y, ds = d4.z;
+            float ddt = 0.0f, dx = 0.0f;
 #pragma unroll
-          for (int k = 0; k < G; ++k) {
-            const float Bv = sm.bc[t][g][k], Cv = sm.bc[t][g][G + k];
-            const float a = as[t][k];
-            const float hp = t > 0 ? hs[t > 0 ? t - 1 : 0][k] : hst[k];
-            gad[k] = fmaf(ds, Cv, gad[k]);               // g_t
-            const float da = gad[k] * hp;                // d abar
-            const float db = gad[k] * x;                 // d bbar
-            float dBc;
-            if constexpr (ZOH) {
-              const float dphi = phi_prime(dl * Aa[k], a, ps[t][k]);
-              ddt = fmaf(da * Aa[k] + db * Bv, a, ddt);  // (da A + db B) abar
-              dA[k] = fmaf(da * dl, a, fmaf(db * Bv * dl * dl, dphi, dA[k]));
-              dBc = db * dl * ps[t][k];
-              dx = fmaf(gad[k], dl * Bv * ps[t][k], dx);
-            } else {
-              ddt = fmaf(da * Aa[k], a, fmaf(db, Bv, ddt));
-              dA[k] = fmaf(da * dl, a, dA[k]);
-              dBc = db * dl;
-              dx = fmaf(gad[k], dl * Bv, dx);
+            for (int k = 0; k < G; ++k) {
+              const float Bv = sm.bc[t][g][k], Cv = sm.bc[t][g][G + k];
+              const float a = as[t][k];
+              const float hp = t > 0 ? hs[t > 0 ? t - 1 : 0][k] : hst[k];
+              gad[k] = fmaf(ds, Cv, gad[k]);               // g_t
+              const float da = gad[k] * hp;                // d abar
+              const float db = gad[k] * x;                 // d bbar
+              float dBc;
+              if constexpr (ZOH) {
+                const float dphi = phi_prime(dl * Aa[k], a, ps[t][k]);
+                ddt = fmaf(da * Aa[k] + db * Bv, a, ddt);  // (da A + db B) abar
+                dA[k] = fmaf(da * dl, a, fmaf(db * Bv * dl * dl, dphi, dA[k]));
+                dBc = db * dl * ps[t][k];
+                dx = fmaf(gad[k], dl * Bv * ps[t][k], dx);
+              } else {
+                ddt = fmaf(da * Aa[k], a, fmaf(db, Bv, ddt));
+                dA[k] = fmaf(da * dl, a, dA[k]);
+                dBc = db * dl;
+                dx = fmaf(gad[k], dl * Bv, dx);
+              }
+              sm.red[0][tt][n0 + k][cl] = cvalid ? dBc : 0.0f;
+              sm.red[1][tt][n0 + k][cl] = cvalid ? ds * hs[t][k] : 0.0f;
+              gad[k] *= a;                                 // carry to t - 1
             }
-            sm.red[0][tt][n0 + k][cl] = cvalid ? dBc : 0.0f;
-            sm.red[1][tt][n0 + k][cl] = cvalid ? ds * hs[t][k] : 0.0f;
-            gad[k] *= a;                                 // carry to t - 1
+            sm.part[0][g][t * CW + cl] = ddt;
+            sm.part[1][g][t * CW + cl] = dx;
           }
-          sm.part[0][g][t * CW + cl] = ddt;
-          sm.part[1][g][t * CW + cl] = dx;
         }
-      }
+      };
+      if (nt == TC) reverse(std::true_type());
+      else reverse(std::false_type());
       lds_barrier();
       // dB, dC of these HALF tokens: sum over the block's channels
       for (int e = tid; e < 2 * HALF * NPAD; e += S::THREADS) {
