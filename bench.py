@@ -159,6 +159,42 @@ def time_scan(sets, steps, warmup, dt_mode, extras=None):
     return wall, kern
 
 
+def time_narrow(dev, steps, warmup):
+    """The scan where (batch x channel) rows are few, so the sequential kernel
+    leaves most of the GPU idle: the Mamba-130M layer at batch 1 (1 x 2048 x
+    1536) and a long narrow sequence (1 x 65536 x 128), bf16, gate, ZOH.  Timed
+    with the library's own choice (the time-parallel scan) and with the
+    sequential kernel forced, for comparison."""
+    import workloads as W
+    out = {}
+    shapes = (("mamba130m_batch1", (1, 2048, 1536)), ("long_narrow", (1, 65536, 128)))
+    for name, (b, L, D) in shapes:
+        cfg = W.ScanConfig(name, b, L, D, 16, "bf16", True, 7)
+        sets = [upload_scan(W.scan_inputs(cfg), dev)]
+        res = {}
+        old = os.environ.get("SSM66_SCAN_KERNEL")
+        for label, env in (("auto", None), ("sequential", "lds1")):
+            if env is None:
+                os.environ.pop("SSM66_SCAN_KERNEL", None)
+            else:
+                os.environ["SSM66_SCAN_KERNEL"] = env
+            res[label] = time_scan(sets, steps, warmup, "zoh")[1]
+        if old is None:
+            os.environ.pop("SSM66_SCAN_KERNEL", None)
+        else:
+            os.environ["SSM66_SCAN_KERNEL"] = old
+        upd = b * L * D * 16
+        out[name] = {"workload": f"ssm_scan_fwd: batch {b}, L {L}, D {D}, N 16, bf16, gate, ZOH",
+                     "kernel": "scan_tpar_kernel (lanes hold tokens)",
+                     "kernel_ms": round(res["auto"], 5),
+                     "sequential_kernel_ms": round(res["sequential"], 5),
+                     "speedup": round(res["sequential"] / res["auto"], 2),
+                     "alu_frac": round(FLOPS_PER_UPDATE * upd / (res["auto"] * 1e-3) / 1e12
+                                       / ALU_PEAK_TFLOPS, 4)}
+        del sets
+    return out
+
+
 def time_decode(cfg, nsteps, dev, npool=8):
     """ssm_step over nsteps consecutive tokens on the full state; the token inputs
     cycle through `npool` distinct seeded token batches resident in HBM."""
@@ -486,6 +522,11 @@ def main():
     ssd = time_ssd(dev, args.steps, args.warmup)
     log(f"[bench] ssd: {ssd['kernel_ms']:.4f} ms")
     log(f"[bench] conv: {conv['kernel_ms']:.4f} ms, step {conv['step']['us_per_step']:.2f} us")
+    log("[bench] timing the scan on few, narrow rows")
+    torch.cuda.empty_cache()
+    narrow = time_narrow(dev, args.steps, args.warmup)
+    log("[bench] narrow: " + ", ".join(f"{k} {v['kernel_ms']:.4f} ms (sequential {v['sequential_kernel_ms']:.4f})"
+                                       for k, v in narrow.items()))
 
     dcfg = W.STEP_CONFIGS["decode"]
     log("[bench] timing decode steps")
@@ -555,6 +596,7 @@ def main():
                 "workspace_MB": round(b_ws / 1e6, 1)},
         "conv": conv,
         "ssd": ssd,
+        "time_parallel": narrow,
         "decode": {"workload": "ssm_step: batch 256, D 5120, N 16, bf16 io, fp32 state, gate, ZOH",
                    "steps": args.decode_steps,
                    "tok_per_s": round(dcfg.batch * args.decode_steps / d_wall_s, 1),

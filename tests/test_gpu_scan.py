@@ -134,7 +134,8 @@ def test_long_sequence_fp32(mode):
     assert_close(to_host64(last), lr, "f32", "last_state")
 
 
-KERNELS = ["lds1", "lds2", "lds4"]
+# sequential kernels with G = 1, 2, 4 states per thread, and the time-parallel one
+KERNELS = ["lds1", "lds2", "lds4", "tpar"]
 
 
 @pytest.mark.parametrize("kernel", KERNELS)
@@ -167,6 +168,35 @@ def test_each_kernel_short_sequences(kernel, L, monkeypatch):
     yr, lr = scan_ref(inp, "zoh")
     assert_close(to_host64(y), yr, "f32", "y")
     assert_close(to_host64(last), lr, "f32", "last_state")
+
+
+@pytest.mark.parametrize("N", [1, 5, 8, 16])
+@pytest.mark.parametrize("mode", ["zoh", "euler"])
+def test_time_parallel_state_sizes_and_chunks(N, mode, monkeypatch):
+    """The time-parallel kernel (lanes hold tokens, pairs combined by a wave
+    scan, waves through LDS, a carry between 256-token chunks): state sizes
+    below 16 (element loads), four chunks with a ragged last one, a zero and a
+    slow channel (the careful ZOH form beside the g form)."""
+    monkeypatch.setenv("SSM66_SCAN_KERNEL", "tpar")
+    inp = W.scan_inputs(_cfg(2, 777, 5, N, "f32", True, seed=40 + N))
+    A = inp["A"].copy()
+    A[1, 0] = 0.0
+    A[3, :] = -0.2
+    inp["A"] = A
+    y, last = scan_gpu(inp, mode)
+    yr, lr = scan_ref(inp, mode)
+    assert_close(to_host64(y), yr, "f32", "y")
+    assert_close(to_host64(last), lr, "f32", "last_state")
+
+
+def test_time_parallel_chosen_for_narrow_long_rows():
+    """Few (batch, channel) rows and a long sequence: the automatic choice is
+    the time-parallel kernel; bf16, gate, ZOH against the oracle."""
+    inp = W.scan_inputs(_cfg(1, 3000, 96, 16, "bf16", True, seed=47))
+    y, last = scan_gpu(inp, "zoh")
+    yr, lr = scan_ref(inp, "zoh")
+    assert_close(to_host64(y), yr, "bf16", "y")
+    assert_close(to_host64(last), lr, "bf16", "last_state")
 
 
 def test_empty_sizes():

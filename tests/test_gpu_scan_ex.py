@@ -11,7 +11,8 @@ import selective_state_space_66_amd as ssm
 
 pytestmark = pytest.mark.gpu
 
-KERNELS = ["lds1", "lds2", "lds4"]
+# sequential kernels with G = 1, 2, 4 states per thread, and the time-parallel one
+KERNELS = ["lds1", "lds2", "lds4", "tpar"]
 BF16_NAN = np.uint16(0x7FC0)
 
 
