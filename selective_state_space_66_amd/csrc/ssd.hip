@@ -92,19 +92,35 @@ struct ChunkConsts {
   float et[kQ];     // exp(cum_t)
 };
 
+// The K = 16 MFMA (v_mfma_f32_16x16x16_bf16): lane l holds A[l%16][4(l/16)+j]
+// and B[4(l/16)+j][l%16], j = 0..3; D as for K = 32.
+__device__ __forceinline__ f32x4 mfma16k16(i16x4 a, i16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+// The K = 16 operand fragment "row r = l % 16, k = 4 (l / 16) + j" of a
+// matrix stored k-major in LDS: one transposing read, lane (g, kk, qq)
+// addressing row 4 g + kk, columns 4 qq .. 4 qq + 3.
+template <int STRIDE>
+__device__ __forceinline__ i16x4 tr_frag4(const __bf16* base, int lane) {
+  const int g = lane >> 4, kk = (lane & 15) >> 2, qq = lane & 3;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4*)(void*)(base + (4 * g + kk) * STRIDE + 4 * qq));
+}
+
 // Row strides (bf16 elements).  Bs and Hs rows are read 16 bytes per lane,
 // rows l % 16: a stride of 4 dwords mod 32 puts 8 consecutive rows on distinct
 // banks.  Xs rows are 32 bytes, so the 16 lanes of a transposing read (4 rows
-// x 4 column quads) cover the 32 banks once.
+// x 4 column quads) cover the 32 banks once.  Everything a chunk reads is
+// double-buffered by chunk parity, so staging the next chunk does not wait for
+// the current one: one barrier per chunk.
 template <int N>
 struct alignas(16) SSDSmem {
   static constexpr int BS = N + 8;
-  static constexpr int SS = kQ + 8;
-  __bf16 Bs[kQ][BS];            // B rows of the chunk (n contiguous)
-  __bf16 Xs[kQ][kPS];           // this block's x columns (p contiguous)
-  __bf16 Ss[kQ][SS];            // masked scores S[t][s] (s contiguous)
-  __bf16 Hs[2][kPS][BS];        // the state entering the chunk, bf16, double-buffered
-  ChunkConsts cc[2];            // per-token constants, double-buffered by chunk parity
+  __bf16 Bs[2][kQ][BS];         // B rows of a chunk (n contiguous)
+  __bf16 Xs[2][kQ][kPS];        // this block's x columns (p contiguous)
+  __bf16 Hs[2][kPS][BS];        // the state entering a chunk, bf16
+  ChunkConsts cc[2];            // per-token constants
 };
 
 struct SSDArgs {
@@ -138,18 +154,20 @@ __device__ __forceinline__ float lane_value(float v, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }
 
-// The scores of token block W (waves are specialised on it: all branches on
-// it are uniform): S^T tiles D[s][t] = sum_n B[s][n] C[t][n] for the s
-// blocks sb <= W, the tiles' MFMA chains interleaved, then masked and
-// weighted to S[t][s] = D exp(cum_t - cum_s) w_s (s <= t).  Below the diagonal
-// block the decay factors through the end of block sb, cum*:
+// The scores of token block W and their product with x (waves are specialised
+// on W: all branches on it are uniform).  S^T tiles D[s][t] = sum_n B[s][n]
+// C[t][n] for the s blocks sb <= W (the tiles' MFMA chains interleaved) are
+// masked and weighted to S[t][s] = D exp(cum_t - cum_s) w_s (s <= t).  Below
+// the diagonal block the decay factors through the end of block sb, cum*:
 // exp(cum_t - cum*) exp(cum* - cum_s) w_s, both factors at most 1, the second
-// one per token (fw) -- one exponential per lane and tile.  On the diagonal
-// block it is taken directly.  Lane value i is s = 16 sb + 4 lk + i,
-// t = 16 W + lr.
+// one per token (fw) -- one exponential per lane and tile; on the diagonal
+// block it is taken directly.  A tile's lane values (s = 16 sb + 4 lk + i,
+// t = 16 W + lr) are, rounded to bf16, exactly the B operand of the K = 16
+// MFMA (4 consecutive k per lane), so Y^T += x^T S^T takes them from registers.
 template <int W, int N, class Sm>
-__device__ __forceinline__ void chunk_scores(Sm& sm, const ChunkConsts& kc, const u32x4 (&cC)[N / 32],
-                                             int lr, int lk) {
+__device__ __forceinline__ void scores_times_x(const Sm& sm, int cur, const ChunkConsts& kc,
+                                               const u32x4 (&cC)[N / 32], int lane, f32x4& y) {
+  const int lr = lane & 15, lk = lane >> 4;
   f32x4 g[W + 1];
 #pragma unroll
   for (int sb = 0; sb <= W; ++sb) g[sb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -157,7 +175,8 @@ __device__ __forceinline__ void chunk_scores(Sm& sm, const ChunkConsts& kc, cons
   for (int k = 0; k < N / 32; ++k)
 #pragma unroll
     for (int sb = 0; sb <= W; ++sb)
-      g[sb] = mfma16(*(const bf16x8*)&sm.Bs[16 * sb + lr][32 * k + 8 * lk], as_bf16x8(cC[k]), g[sb]);
+      g[sb] = mfma16(*(const bf16x8*)&sm.Bs[cur][16 * sb + lr][32 * k + 8 * lk], as_bf16x8(cC[k]),
+                     g[sb]);
   const float ct = kc.cuml[16 * W + lr];
 #pragma unroll
   for (int sb = 0; sb <= W; ++sb) {
@@ -179,11 +198,9 @@ __device__ __forceinline__ void chunk_scores(Sm& sm, const ChunkConsts& kc, cons
         v[i] = (4 * lk + i <= lr) ? g[sb][i] * e * wsv[i] : 0.0f;
       }
     }
-    *(u32x2*)&sm.Ss[16 * W + lr][16 * sb + 4 * lk] =
-        u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+    const i16x4 sf = __builtin_bit_cast(i16x4, u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])});
+    y = mfma16k16(tr_frag4<kPS>(&sm.Xs[cur][16 * sb][0], lane), sf, y);
   }
-  if constexpr (W % 2 == 0)  // the tile past the diagonal that the 32-wide k-steps of S X read
-    *(u32x2*)&sm.Ss[16 * W + lr][16 * (W + 1) + 4 * lk] = u32x2{0u, 0u};
 }
 
 template <int N, bool ZOH, bool GATE>
@@ -232,7 +249,7 @@ __global__ __launch_bounds__(256, 3) void ssd_fwd_kernel(const SSDArgs p) {
   // ---- global reads of one chunk into registers, addressed as a uniform
   // chunk base plus 32-bit byte offsets; rows past L are clamped to the last
   // row (finite data that the zero weights of padding tokens cancel).  Issued
-  // for the next chunk before this chunk's products.
+  // two chunks ahead of use, one chunk ahead of staging.
   u32x4 rB[RB], rC[NK];
   u32x2 rX, rZ = u32x2{0u, 0u};
   float rdt;
@@ -284,73 +301,65 @@ __global__ __launch_bounds__(256, 3) void ssd_fwd_kernel(const SSDArgs p) {
     kc.et[lane] = exp2_hw(c);
   };
 
-  // Per chunk, three phases between LDS barriers:
-  //   A: stage B and x; issue the next chunk's reads; Y^T starts with
-  //      H_in C^T (the state from the previous chunk) and the gate's silu;
-  //   B: the scores S (needs all of B); Y^T scaled by exp(cum_t);
-  //   C: Y^T += x^T S^T, epilogue and store; the state update; wave 0 forms
-  //      the next chunk's per-token constants.
+  // ---- stage a chunk from the registers: B rows, the x columns (rows past
+  // L as zeros), this wave's C fragment and gate, the chunk's constants
+  u32x4 cC[NK];
+  float gz[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+  auto stage = [&](int buf, int64_t t0) {
+    const int nlive = (int)(L - t0 < kQ ? L - t0 : kQ);
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+      const int e = tid + 256 * r;
+      *(u32x4*)&sm.Bs[buf][e / (N / 8)][(e % (N / 8)) * 8] = rB[r];
+    }
+    *(u32x2*)&sm.Xs[buf][tx][4 * (tid & 3)] = tx < nlive ? rX : u32x2{0u, 0u};
+#pragma unroll
+    for (int k = 0; k < NK; ++k) cC[k] = rC[k];
+    if constexpr (GATE) {
+      gz[0] = silu_f(lo_bf(rZ.x));
+      gz[1] = silu_f(hi_bf(rZ.x));
+      gz[2] = silu_f(lo_bf(rZ.y));
+      gz[3] = silu_f(hi_bf(rZ.y));
+    }
+    if (w == 0) chunk_consts(sm.cc[buf], rdt, nlive);
+  };
+
+  // Per chunk, after the barrier that publishes its staging: Y^T from the
+  // state, the scores times x, the epilogue, the state update; then the next
+  // chunk is staged into the other buffers and the one after it is read.
   const int64_t nchunks = (L + kQ - 1) / kQ;
   if (nchunks > 0) {
     load_chunk(0);
-    if (w == 0) chunk_consts(sm.cc[0], rdt, (int)(L < kQ ? L : kQ));
+    stage(0, 0);
+    if (nchunks > 1) load_chunk(kQ);
   }
+  lds_barrier();
   for (int64_t ck = 0; ck < nchunks; ++ck) {
     const int64_t t0 = ck * kQ;
     const int nlive = (int)(L - t0 < kQ ? L - t0 : kQ);
     const int cur = (int)(ck & 1), nxt = cur ^ 1;
     const ChunkConsts& kc = sm.cc[cur];
 
-    // ---- A: stage B rows and the x columns (x rows past L as zeros)
-#pragma unroll
-    for (int r = 0; r < RB; ++r) {
-      const int e = tid + 256 * r;
-      *(u32x4*)&sm.Bs[e / (N / 8)][(e % (N / 8)) * 8] = rB[r];
-    }
-    *(u32x2*)&sm.Xs[tx][4 * (tid & 3)] = tx < nlive ? rX : u32x2{0u, 0u};
-    u32x4 cC[NK];
-#pragma unroll
-    for (int k = 0; k < NK; ++k) cC[k] = rC[k];
-    float gz[4] = {1.0f, 1.0f, 1.0f, 1.0f};
-    if constexpr (GATE) {
-      gz[0] = lo_bf(rZ.x);
-      gz[1] = hi_bf(rZ.x);
-      gz[2] = lo_bf(rZ.y);
-      gz[3] = hi_bf(rZ.y);
-    }
-    if (ck + 1 < nchunks) load_chunk(t0 + kQ);
-    // Y^T for token block w: D[p][t] = sum_n H[p][n] C[t][n] first; lane value
-    // i is p = 4 lk + i, t = 16 w + lr
+    // ---- Y^T for token block w: D[p][t] = exp(cum_t) sum_n H[p][n] C[t][n]
+    //      + sum_s x[s][p] S[t][s]; lane value i is p = 4 lk + i, t = 16 w + lr
     f32x4 y = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int k = 0; k < NK; ++k)
       y = mfma16(*(const bf16x8*)&sm.Hs[cur][lr][32 * k + 8 * lk], as_bf16x8(cC[k]), y);
-    if constexpr (GATE) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) gz[i] = silu_f(gz[i]);
-    }
-    lds_barrier();
-
-    // ---- B: scores of this wave's token block
-    switch (w) {
-      case 0: chunk_scores<0, N>(sm, kc, cC, lr, lk); break;
-      case 1: chunk_scores<1, N>(sm, kc, cC, lr, lk); break;
-      case 2: chunk_scores<2, N>(sm, kc, cC, lr, lk); break;
-      default: chunk_scores<3, N>(sm, kc, cC, lr, lk); break;
-    }
     {
       const float e = kc.et[tz];
 #pragma unroll
       for (int i = 0; i < 4; ++i) y[i] *= e;
     }
-    lds_barrier();
-
-    // ---- C: Y^T += sum_s x[s][p] S[t][s]; skip, gate, store 4 channels of token tz
-    y = mfma16(tr_frag<kPS>(&sm.Xs[0][0], lane), *(const bf16x8*)&sm.Ss[tz][8 * lk], y);
-    if (w >= 2)  // scores of s >= 32: zero for the first two token blocks
-      y = mfma16(tr_frag<kPS>(&sm.Xs[32][0], lane), *(const bf16x8*)&sm.Ss[tz][32 + 8 * lk], y);
+    switch (w) {
+      case 0: scores_times_x<0, N>(sm, cur, kc, cC, lane, y); break;
+      case 1: scores_times_x<1, N>(sm, cur, kc, cC, lane, y); break;
+      case 2: scores_times_x<2, N>(sm, cur, kc, cC, lane, y); break;
+      default: scores_times_x<3, N>(sm, cur, kc, cC, lane, y); break;
+    }
+    // ---- epilogue: skip, gate, store 4 channels of token tz
     if (tz < nlive) {
-      const u32x2 xv = *(const u32x2*)&sm.Xs[tz][4 * lk];
+      const u32x2 xv = *(const u32x2*)&sm.Xs[cur][tz][4 * lk];
       const float o0 = fmaf(Dh, lo_bf(xv.x), y[0]) * gz[0];
       const float o1 = fmaf(Dh, hi_bf(xv.x), y[1]) * gz[1];
       const float o2 = fmaf(Dh, lo_bf(xv.y), y[2]) * gz[2];
@@ -360,7 +369,8 @@ __global__ __launch_bounds__(256, 3) void ssd_fwd_kernel(const SSDArgs p) {
           u32x2{pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)};
     }
 
-    // state update, H^T tiles: D[n][p] = exp(cum_Q) H^T[n][p] + sum_s B[s][n] (eend_s x[s][p])
+    // ---- state update, H^T tiles: D[n][p] = exp(cum_Q) H^T[n][p]
+    //      + sum_s B[s][n] (eend_s x[s][p])
     {
       const float etot = exp2_hw(kc.cuml[kQ - 1]);
 #pragma unroll
@@ -369,7 +379,7 @@ __global__ __launch_bounds__(256, 3) void ssd_fwd_kernel(const SSDArgs p) {
         for (int i = 0; i < 4; ++i) Hacc[j][i] *= etot;
 #pragma unroll
       for (int s0 = 0; s0 < kQ; s0 += 32) {
-        const bf16x8 xt = tr_frag<kPS>(&sm.Xs[s0][0], lane);  // x[s0 + 8 lk + j][lr]
+        const bf16x8 xt = tr_frag<kPS>(&sm.Xs[cur][s0][0], lane);  // x[s0 + 8 lk + j][lr]
         const float4 e0 = *(const float4*)&kc.eend[s0 + 8 * lk];
         const float4 e1 = *(const float4*)&kc.eend[s0 + 8 * lk + 4];
         const float ev[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
@@ -378,20 +388,24 @@ __global__ __launch_bounds__(256, 3) void ssd_fwd_kernel(const SSDArgs p) {
         for (int j = 0; j < 8; ++j) xw[j] = (__bf16)((float)xt[j] * ev[j]);
 #pragma unroll
         for (int j = 0; j < NTW; ++j) {
-          const bf16x8 bt = tr_frag<Sm::BS>(&sm.Bs[s0][16 * (w + kWaves * j)], lane);
+          const bf16x8 bt = tr_frag<Sm::BS>(&sm.Bs[cur][s0][16 * (w + kWaves * j)], lane);
           Hacc[j] = mfma16(bt, xw, Hacc[j]);
         }
       }
-      // Hs[nxt] was last read in the previous chunk, before its barriers
+      // Hs[nxt] was last read in the previous chunk, before this chunk's barrier
 #pragma unroll
       for (int j = 0; j < NTW; ++j)
         *(u32x2*)&sm.Hs[nxt][lr][16 * (w + kWaves * j) + 4 * lk] =
             u32x2{pack_bf16x2(Hacc[j][0], Hacc[j][1]), pack_bf16x2(Hacc[j][2], Hacc[j][3])};
     }
-    // the next chunk's constants (its step sizes arrived with this chunk's prefetch)
-    if (w == 0 && ck + 1 < nchunks)
-      chunk_consts(sm.cc[nxt], rdt, (int)(L - t0 - kQ < kQ ? L - t0 - kQ : kQ));
-    lds_barrier();  // every wave is done with Bs, Xs, Ss and this chunk's constants
+
+    // ---- the next chunk into the other buffers (last read in the previous
+    // chunk), and the reads of the one after it
+    if (ck + 1 < nchunks) {
+      stage(nxt, t0 + kQ);
+      if (ck + 2 < nchunks) load_chunk(t0 + 2 * kQ);
+    }
+    lds_barrier();
   }
 
   if (p.last_state) {
