@@ -105,6 +105,14 @@ extern "C" {
  * h_t[b,c,n] = exp(Delta A[c,n]) h_{t-1}[b,c,n] + bbar(Delta, A[c,n], B[b,t,n]) u[b,t,c],
  * Delta = softplus?(delta[b,t,c] + delta_bias[c]), h_{-1} = 0.
  * last_state (optional) receives h after the last token.
+ * Two kernels compute it ("Mamba and selective state spaces",
+ * "Selection breaks the convolution": the recurrence is an associative scan):
+ * lanes holding (channel, state group) and running through time, and, for at
+ * most 3072 (batch x channel) rows and 128 or more tokens, lanes holding
+ * tokens with the steps composed by a parallel scan.  Both give the same
+ * result up to fp32 rounding.  The environment variable SSM66_SCAN_KERNEL
+ * (read at each call) forces one: "tpar" the time-parallel kernel, "lds1",
+ * "lds2" or "lds4" the sequential one with 1, 2 or 4 states per lane.
  * Returns SSM_OK or an error status (see above).
  */
 int ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
