@@ -161,13 +161,15 @@ def time_scan(sets, steps, warmup, dt_mode, extras=None):
 
 def time_narrow(dev, steps, warmup):
     """The scan where (batch x channel) rows are few, so the sequential kernel
-    leaves most of the GPU idle: the Mamba-130M layer at batch 1 (1 x 2048 x
-    1536) and a long narrow sequence (1 x 65536 x 128), bf16, gate, ZOH.  Timed
+    leaves most of the GPU idle: the pages' speed-benchmark shape (batch 1,
+    L 2048, D 1024, N 16), the Mamba-130M layer at batch 1 (1 x 2048 x 1536)
+    and a long narrow sequence (1 x 65536 x 128), bf16, gate, ZOH.  Timed
     with the library's own choice (the time-parallel scan) and with the
     sequential kernel forced, for comparison."""
     import workloads as W
     out = {}
-    shapes = (("mamba130m_batch1", (1, 2048, 1536)), ("long_narrow", (1, 65536, 128)))
+    shapes = (("paper_speed_benchmark", (1, 2048, 1024)), ("mamba130m_batch1", (1, 2048, 1536)),
+              ("long_narrow", (1, 65536, 128)))
     for name, (b, L, D) in shapes:
         cfg = W.ScanConfig(name, b, L, D, 16, "bf16", True, 7)
         sets = [upload_scan(W.scan_inputs(cfg), dev)]
