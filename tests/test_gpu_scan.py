@@ -281,3 +281,26 @@ def test_full_size_sampled(name):
         e2 = assert_close(ls, lr, "bf16", f"{name} last_state {mode}")
         print(f"[{name}] {mode}: rel-rms y {e1:.2e}, last_state {e2:.2e}", flush=True)
         torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("shape", [(1, 2048, 1024), (1, 2048, 1536), (1, 65536, 128)])
+def test_full_size_time_parallel_sampled(shape):
+    """The benchmark's time-parallel shapes at full size, with the library's own
+    kernel choice (the time-parallel scan for these few rows): sampled channels
+    over every token, and their final states, against the oracle."""
+    b, L, dim = shape
+    cfg = W.ScanConfig(f"narrow{b}x{L}x{dim}", b, L, dim, 16, "bf16", True, 7)
+    inp = W.scan_inputs(cfg)
+    ch = _sample_channels(dim, 7, k=6)
+    for mode in ("zoh", "euler"):
+        print(f"[{cfg.name}] launch {mode}", flush=True)
+        y, last = scan_gpu(inp, mode)
+        chd = torch.from_numpy(ch).to(DEV)
+        ys = to_host64(y.index_select(2, chd))
+        ls = to_host64(last.index_select(1, chd))
+        del y, last
+        sub = W.scan_inputs(cfg, channels=ch)
+        yr, lr = scan_ref(sub, mode)
+        e1 = assert_close(ys, yr, "bf16", f"{cfg.name} y {mode}")
+        e2 = assert_close(ls, lr, "bf16", f"{cfg.name} last_state {mode}")
+        print(f"[{cfg.name}] {mode}: rel-rms y {e1:.2e}, last_state {e2:.2e}", flush=True)
