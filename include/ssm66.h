@@ -26,6 +26,9 @@
  *                  of storing them ("Why the scan must be fused": the backward
  *                  pass reloads x, Delta, B, C and recomputes the states; the
  *                  backward of a linear recurrence is a reverse recurrence).
+ *                  For training, ssm_scan_fwd_ckpt also keeps the state every
+ *                  16 tokens, and ssm_scan_bwd_ex recomputes from those
+ *                  checkpoints instead of from the start of the sequence.
  *   ssm_step     : one token of that layer against a state cache, updated in
  *                  place ("Decoding with a constant-size cache").
  *   ssm_ssd_fwd  : the Mamba-2 / SSD layer, one scalar decay per head, as a
@@ -77,7 +80,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 5
+#define SSM_ABI_VERSION 6
 
 /* status codes */
 #define SSM_OK 0
@@ -176,6 +179,43 @@ int ssm_scan_bwd(const void* u, const void* delta, const float* A, const void* B
                  float* ddelta_bias, float* dh0, void* workspace, size_t workspace_bytes,
                  int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype,
                  void* stream);
+
+/*
+ * Bytes of the training forward's checkpoints for these sizes (0 for invalid
+ * sizes): the state before every 16th token, (batch, ceil(seqlen/16), dim,
+ * dstate) float32, rounded up to 256 bytes.
+ */
+size_t ssm_scan_ckpt_size(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate);
+
+/*
+ * The training forward: ssm_scan_fwd with an initial state (h0, nullable, as
+ * in ssm_scan_fwd_ex) that also writes the state before tokens 0, 16, 32, ...
+ * of every sequence to ckpt (device memory of ssm_scan_ckpt_size(...) bytes,
+ * float32, 4-byte aligned, owned by the caller; required when seqlen > 0):
+ * the checkpoints the backward pass would otherwise rebuild with a forward
+ * sweep ("Why the scan must be fused": only chunk boundaries are kept, the
+ * states in between are recomputed).  y and last_state are the same as
+ * ssm_scan_fwd_ex's.  Returns SSM_OK or an error status.
+ */
+int ssm_scan_fwd_ckpt(const void* u, const void* delta, const float* A, const void* B,
+                      const void* C, const float* D, const void* z, const float* delta_bias,
+                      int softplus, int dt_mode, const float* h0, void* y, float* last_state,
+                      float* ckpt, int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                      int io_dtype, void* stream);
+
+/*
+ * ssm_scan_bwd with the forward's checkpoints: ckpt (nullable) is what
+ * ssm_scan_fwd_ckpt wrote for the same inputs and h0; with it the backward
+ * skips its own forward sweep (the checkpoint part of the workspace is then
+ * unused).  NULL makes it ssm_scan_bwd.  Returns SSM_OK or an error status.
+ */
+int ssm_scan_bwd_ex(const void* u, const void* delta, const float* A, const void* B,
+                    const void* C, const float* D, const void* z, const float* delta_bias,
+                    int softplus, int dt_mode, const float* h0, const void* dy,
+                    const float* dlast_state, void* du, void* ddelta, float* dA, void* dB,
+                    void* dC, float* dD, void* dz, float* ddelta_bias, float* dh0,
+                    const float* ckpt, void* workspace, size_t workspace_bytes, int64_t batch,
+                    int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype, void* stream);
 
 /*
  * One decode step against the state cache `state` (batch, dim, dstate),

@@ -53,6 +53,13 @@ def load_library():
     lib.ssm_scan_fwd_ex.argtypes = [vp] * 8 + [ci, ci] + [vp] * 5 + [i64, i64, i64, i64, ci, vp]
     lib.ssm_scan_bwd_workspace_size.restype = ctypes.c_size_t
     lib.ssm_scan_bwd_workspace_size.argtypes = [i64] * 4
+    lib.ssm_scan_ckpt_size.restype = ctypes.c_size_t
+    lib.ssm_scan_ckpt_size.argtypes = [i64] * 4
+    lib.ssm_scan_fwd_ckpt.restype = ci
+    lib.ssm_scan_fwd_ckpt.argtypes = [vp] * 8 + [ci, ci] + [vp] * 4 + [i64] * 4 + [ci, vp]
+    lib.ssm_scan_bwd_ex.restype = ci
+    lib.ssm_scan_bwd_ex.argtypes = [vp] * 8 + [ci, ci] + [vp] * 14 + [ctypes.c_size_t] + \
+        [i64] * 4 + [ci, vp]
     lib.ssm_scan_bwd.restype = ci
     lib.ssm_scan_bwd.argtypes = [vp] * 8 + [ci, ci] + [vp] * 13 + [ctypes.c_size_t] + \
         [i64] * 4 + [ci, vp]
@@ -277,13 +284,15 @@ def conv1d_step(window, x, weight, bias=None, silu=True, out=None):
 
 
 def scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, softplus=True,
-             dt_mode="zoh", h0=None, dlast=None, workspace=None):
+             dt_mode="zoh", h0=None, dlast=None, workspace=None, ckpt=None):
     """Gradients of scan_fwd on the GPU (states recomputed, not stored).
 
     dy: like u; dlast: optional (batch, dim, N) float32, the gradient of last_state.
     Returns a dict: du, ddelta (of the raw delta), dB, dC (io dtype), dA (float32),
     and, where their inputs were given, dz (io dtype), dD, ddelta_bias, dh0 (float32).
     workspace: optional uint8 device tensor of at least scan_bwd_workspace_size() bytes.
+    ckpt: optional checkpoints from scan_fwd_train on the same inputs and h0; the
+    states are then recomputed from them, without a forward sweep.
     """
     import torch
     lib = load_library()
@@ -303,6 +312,7 @@ def scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, softplus=Tr
     _check(delta_bias, "delta_bias", (dim,), torch.float32, dev)
     _check(h0, "h0", (batch, dim, N), torch.float32, dev)
     _check(dlast, "dlast", (batch, dim, N), torch.float32, dev)
+    _check(ckpt, "ckpt", (batch, (L + 15) // 16, dim, N), torch.float32, dev)
     need = scan_bwd_workspace_size(batch, L, dim, N)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
@@ -317,15 +327,65 @@ def scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, softplus=Tr
              dD=torch.empty((dim,), **f32) if D is not None else None,
              ddelta_bias=torch.empty((dim,), **f32) if delta_bias is not None else None,
              dh0=torch.empty((batch, dim, N), **f32) if h0 is not None else None)
-    st = lib.ssm_scan_bwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
-                          _ptr(delta_bias), int(bool(softplus)), _MODES[dt_mode], _ptr(h0),
-                          _ptr(dy), _ptr(dlast), _ptr(g["du"]), _ptr(g["ddelta"]), _ptr(g["dA"]),
-                          _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dD"]), _ptr(g["dz"]),
-                          _ptr(g["ddelta_bias"]), _ptr(g["dh0"]), _ptr(workspace),
-                          workspace.numel(), batch, L, dim, N, _io_code(u), _stream(dev))
+    st = lib.ssm_scan_bwd_ex(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                             _ptr(delta_bias), int(bool(softplus)), _MODES[dt_mode], _ptr(h0),
+                             _ptr(dy), _ptr(dlast), _ptr(g["du"]), _ptr(g["ddelta"]),
+                             _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dD"]),
+                             _ptr(g["dz"]), _ptr(g["ddelta_bias"]), _ptr(g["dh0"]), _ptr(ckpt),
+                             _ptr(workspace), workspace.numel(), batch, L, dim, N, _io_code(u),
+                             _stream(dev))
     if st != 0:
-        raise SsmError(st, "ssm_scan_bwd")
+        raise SsmError(st, "ssm_scan_bwd_ex")
     return g
+
+
+def scan_ckpt_size(batch, L, dim, N):
+    """Bytes of the training forward's checkpoints for these sizes."""
+    return int(load_library().ssm_scan_ckpt_size(batch, L, dim, N))
+
+
+def scan_fwd_train(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True,
+                   dt_mode="zoh", h0=None, y=None, last_state=None, ckpt=None):
+    """The training forward: scan_fwd (with an optional h0) that also keeps the
+    state before every 16th token for scan_bwd.
+
+    Returns (y, last_state, ckpt); ckpt is (batch, ceil(L/16), dim, N) float32.
+    """
+    import torch
+    lib = load_library()
+    if u.dim() != 3:
+        raise ValueError("u must be (batch, L, dim)")
+    batch, L, dim = u.shape
+    N = A.shape[-1]
+    dev = u.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on the GPU")
+    io = u.dtype
+    _io_code(u)
+    for t, name, shape in ((u, "u", (batch, L, dim)), (delta, "delta", (batch, L, dim)),
+                           (B, "B", (batch, L, N)), (C, "C", (batch, L, N)),
+                           (z, "z", (batch, L, dim))):
+        _check(t, name, shape, io, dev)
+    _check(A, "A", (dim, N), torch.float32, dev)
+    _check(D, "D", (dim,), torch.float32, dev)
+    _check(delta_bias, "delta_bias", (dim,), torch.float32, dev)
+    _check(h0, "h0", (batch, dim, N), torch.float32, dev)
+    if y is None:
+        y = torch.empty_like(u)
+    _check(y, "y", (batch, L, dim), io, dev)
+    if last_state is None:
+        last_state = torch.empty((batch, dim, N), dtype=torch.float32, device=dev)
+    _check(last_state, "last_state", (batch, dim, N), torch.float32, dev)
+    if ckpt is None:
+        ckpt = torch.empty((batch, (L + 15) // 16, dim, N), dtype=torch.float32, device=dev)
+    _check(ckpt, "ckpt", (batch, (L + 15) // 16, dim, N), torch.float32, dev)
+    st = lib.ssm_scan_fwd_ckpt(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                               _ptr(delta_bias), int(bool(softplus)), _MODES[dt_mode], _ptr(h0),
+                               _ptr(y), _ptr(last_state), _ptr(ckpt), batch, L, dim, N,
+                               _io_code(u), _stream(dev))
+    if st != 0:
+        raise SsmError(st, "ssm_scan_fwd_ckpt")
+    return y, last_state, ckpt
 
 
 def scan_bwd_workspace_size(batch, L, dim, N):

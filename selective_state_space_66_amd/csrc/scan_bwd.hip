@@ -104,6 +104,7 @@ struct BwdArgs {
   void *du, *ddelta, *dz;
   float* dh0;
   float* ckpt;    // (batch, nchunks, dim, N)
+  int have_ckpt;  // ckpt was written by the forward: no pass 1
   float* pbc;     // (ntiles, 2, batch, L, N)
   float* pA;      // (batch, dim, N)
   float* pDb;     // (2, batch, dim)
@@ -262,8 +263,9 @@ __global__ __launch_bounds__((BShape<G, NG>::THREADS)) void scan_bwd_kernel(cons
       }
     }
   };
-  if (p.nchunks > 0) load_raw(0, false);
-  for (int64_t ck = 0; ck < p.nchunks; ++ck) {
+  const int64_t p1_chunks = p.have_ckpt ? 0 : p.nchunks;
+  if (p1_chunks > 0) load_raw(0, false);
+  for (int64_t ck = 0; ck < p1_chunks; ++ck) {
     const int64_t t0 = ck * TC;
     if (cvalid) {
 #pragma unroll
@@ -543,7 +545,8 @@ hipError_t bwd_io(const ScanBwdParams& q, bool zoh, bool gate, hipStream_t strea
   a.want_dz = q.dz != nullptr;
   // workspace: checkpoints, dB/dC partials, dA partials, dD/dbias partials
   char* w = (char*)q.workspace;
-  a.ckpt = (float*)w;
+  a.ckpt = q.ckpt ? (float*)q.ckpt : (float*)w;
+  a.have_ckpt = q.ckpt != nullptr;
   w += scan_bwd_ckpt_bytes(q.batch, q.L, q.dim, q.N);
   a.pbc = (float*)w;
   w += (size_t)a.ntiles * 2 * q.batch * q.L * q.N * sizeof(float);

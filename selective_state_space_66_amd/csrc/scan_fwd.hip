@@ -149,10 +149,12 @@ __device__ __forceinline__ float update(float (&st)[G], const float (&Ap)[G], co
 // Full chunks go in batches of U tokens: all LDS reads of a batch are issued
 // before its arithmetic, so their latency overlaps, and its U partial readouts
 // are written after it.
-template <class S, Path PATH, bool FULL, bool RST = false>
+// CKPT (the training forward): ckpt(t) writes the state before chunk token t
+// when t is a multiple of 16 (chunks start at multiples of 16).
+template <class S, Path PATH, bool FULL, bool RST = false, bool CKPT = false, class Ckpt>
 __device__ __forceinline__ void run_chunk(Smem<S>& sm, float (&st)[S::G], const float (&Ap)[S::G],
                                           const float (&Aa)[S::G], const float (&CA)[S::G],
-                                          int nt, int cl, int g) {
+                                          int nt, int cl, int g, Ckpt&& ckpt) {
   constexpr int G = S::G;
   float* part = &sm.part[g][cl];
   if constexpr (FULL) {
@@ -172,6 +174,9 @@ __device__ __forceinline__ void run_chunk(Smem<S>& sm, float (&st)[S::G], const 
 #pragma unroll
     for (int bt = 0; bt < NB; ++bt) {
       const int cur = bt & 1, nxt = cur ^ 1;
+      if constexpr (CKPT) {
+        if ((bt * U) % 16 == 0) ckpt(bt * U);
+      }
       if (bt + 1 < NB) {
 #pragma unroll
         for (int j = 0; j < U; ++j) {
@@ -190,6 +195,9 @@ __device__ __forceinline__ void run_chunk(Smem<S>& sm, float (&st)[S::G], const 
     }
   } else {
     for (int t = 0; t < nt; ++t) {
+      if constexpr (CKPT) {
+        if (t % 16 == 0) ckpt(t);
+      }
       if constexpr (RST) {
         if (sm.rst[t]) {  // a document starts here: forget the state
 #pragma unroll
@@ -206,15 +214,17 @@ __device__ __forceinline__ void run_chunk(Smem<S>& sm, float (&st)[S::G], const 
 // Pointers are separate __restrict__ arguments; y must not overlap any input,
 // and last_state none but h0 (each thread reads its h0 entries before it
 // writes the same entries of last_state).  The host guarantees
-// NG * dim < 2^31 (32-bit lane offsets).
-template <typename IO, int G, int NG, bool ZOH, bool GATE>
+// NG * dim < 2^31 (32-bit lane offsets).  CKPT: also write the state before
+// every 16th token to ckpt (batch, ceil(L / 16), dim, N), the checkpoints the
+// backward pass would otherwise recompute.
+template <typename IO, int G, int NG, bool ZOH, bool GATE, bool CKPT>
 __global__ __launch_bounds__((Shape<G, NG>::THREADS)) void scan_fwd_kernel(
     const IO* __restrict__ u, const IO* __restrict__ dr, const float* __restrict__ Am,
     const IO* __restrict__ Bm, const IO* __restrict__ Cm, const float* __restrict__ Dm,
     const IO* __restrict__ zz, const float* __restrict__ bias_v, const float* h0,
     const int32_t* __restrict__ seq_lens, const uint8_t* __restrict__ reset,
-    IO* __restrict__ y, float* last_state, const int64_t L, const int64_t dim, const int64_t N,
-    const int64_t ntiles, const int softplus) {
+    IO* __restrict__ y, float* last_state, float* __restrict__ ckpt, const int64_t L,
+    const int64_t dim, const int64_t N, const int64_t ntiles, const int softplus) {
   using S = Shape<G, NG>;
   constexpr int CW = S::CW, TC = S::TC, RPT = S::RPT, NPAD = S::NPAD;
   using Raw = typename RawT<IO>::type;
@@ -270,6 +280,7 @@ __global__ __launch_bounds__((Shape<G, NG>::THREADS)) void scan_fwd_kernel(
   }
 
   const int64_t nchunks = (L + TC - 1) / TC;
+  const int64_t nck = (L + 15) / 16;  // checkpoints per sequence (CKPT)
   const int64_t row0 = b * L;  // first token row of this batch entry
   int64_t Leff = L;            // real tokens of this sequence; the rest is padding
   if (seq_lens) {
@@ -434,11 +445,23 @@ __global__ __launch_bounds__((Shape<G, NG>::THREADS)) void scan_fwd_kernel(
     // ---- the recurrence for this thread's states over the chunk's real tokens
     const int64_t nreal = Leff - t0;
     const int nt = (int)(nreal < 0 ? 0 : (nreal < TC ? nreal : TC));
+    // the state before chunk token t, in h units, to its checkpoint
+    auto write_ckpt = [&](int t) {
+      if (cvalid) {
+        float* dst = ckpt + ((b * nck + (t0 + t) / 16) * dim + c) * N + n0;
+#pragma unroll
+        for (int k = 0; k < G; ++k)
+          if (n0 + k < N) dst[k] = (ZOH && !careful) ? st[k] * CA[k] : st[k];
+      }
+    };
     auto run = [&](auto path_tag) {
       constexpr Path PATH = decltype(path_tag)::value;
-      if (nt == TC && !chunk_resets) run_chunk<S, PATH, true>(sm, st, Ap, Aa, CA, nt, cl, g);
-      else if (chunk_resets) run_chunk<S, PATH, false, true>(sm, st, Ap, Aa, CA, nt, cl, g);
-      else run_chunk<S, PATH, false>(sm, st, Ap, Aa, CA, nt, cl, g);
+      if (nt == TC && !chunk_resets)
+        run_chunk<S, PATH, true, false, CKPT>(sm, st, Ap, Aa, CA, nt, cl, g, write_ckpt);
+      else if (chunk_resets)
+        run_chunk<S, PATH, false, true, CKPT>(sm, st, Ap, Aa, CA, nt, cl, g, write_ckpt);
+      else
+        run_chunk<S, PATH, false, false, CKPT>(sm, st, Ap, Aa, CA, nt, cl, g, write_ckpt);
     };
     if (nt > 0) {
       if constexpr (!ZOH) run(PathTag<Path::kEuler>());
@@ -496,11 +519,12 @@ hipError_t launch_one(const ScanParams& p, hipStream_t stream) {
   const int64_t ntiles = (p.dim + S::CW - 1) / S::CW;
   const int64_t nblk = ntiles * p.batch;
   if (nblk > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((scan_fwd_kernel<IO, G, NG, ZOH, GATE>), dim3((unsigned)nblk),
-                     dim3(S::THREADS), 0, stream, (const IO*)p.u, (const IO*)p.delta, p.A,
-                     (const IO*)p.B, (const IO*)p.C, p.D, (const IO*)p.z, p.delta_bias, p.h0,
-                     p.seq_lens, p.reset, (IO*)p.y, p.last_state, p.L, p.dim, p.N, ntiles,
-                     p.softplus);
+  auto kern = p.ckpt ? scan_fwd_kernel<IO, G, NG, ZOH, GATE, true>
+                     : scan_fwd_kernel<IO, G, NG, ZOH, GATE, false>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(S::THREADS), 0, stream, (const IO*)p.u,
+                     (const IO*)p.delta, p.A, (const IO*)p.B, (const IO*)p.C, p.D,
+                     (const IO*)p.z, p.delta_bias, p.h0, p.seq_lens, p.reset, (IO*)p.y,
+                     p.last_state, p.ckpt, p.L, p.dim, p.N, ntiles, p.softplus);
   return hipGetLastError();
 }
 

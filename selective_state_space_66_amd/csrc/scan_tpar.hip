@@ -78,15 +78,16 @@ __device__ __forceinline__ float lane_bcast(float v, int l) {
 // Pointers are separate __restrict__ arguments; y must not overlap any input,
 // and last_state none but h0 (read before the first chunk, written after the
 // last).
-// NF: N == 16, whose B and C rows are read as 16-byte vectors.
-template <typename IO, bool ZOH, bool GATE, bool NF>
+// NF: N == 16, whose B and C rows are read as 16-byte vectors.  CKPT: also
+// write the state before every 16th token to ckpt (batch, ceil(L / 16), dim, N).
+template <typename IO, bool ZOH, bool GATE, bool NF, bool CKPT>
 __global__ __launch_bounds__(64 * kTW) void scan_tpar_kernel(
     const IO* __restrict__ u, const IO* __restrict__ dr, const float* __restrict__ Am,
     const IO* __restrict__ Bm, const IO* __restrict__ Cm, const float* __restrict__ Dm,
     const IO* __restrict__ zz, const float* __restrict__ bias_v, const float* h0,
     const int32_t* __restrict__ seq_lens, const uint8_t* __restrict__ reset,
-    IO* __restrict__ y, float* last_state, const int64_t L, const int64_t dim, const int N,
-    const int softplus) {
+    IO* __restrict__ y, float* last_state, float* __restrict__ ckpt, const int64_t L,
+    const int64_t dim, const int N, const int softplus) {
   __shared__ float2 tot[2][kTW][kNMax];  // per chunk parity, wave, state: the wave's total pair
   __shared__ float cst[2][kNMax];        // per state: A log2(e); readout factor (1/A for the g form)
 
@@ -114,9 +115,11 @@ __global__ __launch_bounds__(64 * kTW) void scan_tpar_kernel(
   const float dskip = Dm ? Dm[c] : 0.0f;
   // the carry into the chunk, state n = lane (lanes < N), in g units where fast
   float carry = 0.0f;
+  const int64_t nck = (L + 15) / 16;  // checkpoints per sequence (CKPT)
   if (lane < N) {
     const float hv = h0 ? h0[(b * dim + c) * N + lane] : 0.0f;
     carry = fast_l ? a_l * hv : hv;
+    if (CKPT && w == 0 && L > 0) ckpt[(b * nck * dim + c) * N + lane] = hv;
   }
   int64_t Leff = L;
   if (seq_lens) {
@@ -249,12 +252,17 @@ __global__ __launch_bounds__(64 * kTW) void scan_tpar_kernel(
     }
 
     // (3) the states of this lane's token and the readout
+    // the lane of the last token of a 16-token group writes the checkpoint of
+    // the next group (the state before its first token), in h units
+    const bool wck = CKPT && (t % 16 == 15) && t + 1 < L;
+    float* ckp = ckpt + ((b * nck + (wck ? (t + 1) / 16 : 0)) * dim + c) * N;
     float acc = 0.0f;
 #pragma unroll
     for (int n = 0; n < kNMax; ++n) {
       if (NF || n < N) {
         const float h = fmaf(pa[n], lane_bcast(cin, n), pb[n]);
         acc = fmaf(Cv[n] * cst[1][n] + (ZOH ? 0.0f : Cv[n]), h, acc);
+        if (wck) ckp[n] = ZOH ? h * cst[1][n] : h;  // g / A where g is carried
       }
     }
     if (t < L) store_io(y + (b * L + t0) * dim + c + (uint32_t)tl0 * (uint32_t)dim,
@@ -269,10 +277,14 @@ template <typename IO, bool ZOH, bool GATE>
 hipError_t tpar_launch(const ScanParams& p, hipStream_t stream) {
   const int64_t nblk = p.batch * p.dim;
   if (nblk > 0x7fffffff || kTT * p.dim >= 0x7fffffff) return hipErrorInvalidValue;
-  auto kern = p.N == kNMax ? scan_tpar_kernel<IO, ZOH, GATE, true> : scan_tpar_kernel<IO, ZOH, GATE, false>;
-  hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(64 * kTW), 0, stream, (const IO*)p.u, (const IO*)p.delta, p.A, (const IO*)p.B,
-                     (const IO*)p.C, p.D, (const IO*)p.z, p.delta_bias, p.h0, p.seq_lens, p.reset,
-                     (IO*)p.y, p.last_state, p.L, p.dim, (int)p.N, p.softplus);
+  auto kern = p.N == kNMax ? (p.ckpt ? scan_tpar_kernel<IO, ZOH, GATE, true, true>
+                                     : scan_tpar_kernel<IO, ZOH, GATE, true, false>)
+                           : (p.ckpt ? scan_tpar_kernel<IO, ZOH, GATE, false, true>
+                                     : scan_tpar_kernel<IO, ZOH, GATE, false, false>);
+  hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(64 * kTW), 0, stream, (const IO*)p.u,
+                     (const IO*)p.delta, p.A, (const IO*)p.B, (const IO*)p.C, p.D,
+                     (const IO*)p.z, p.delta_bias, p.h0, p.seq_lens, p.reset, (IO*)p.y,
+                     p.last_state, p.ckpt, p.L, p.dim, (int)p.N, p.softplus);
   return hipGetLastError();
 }
 

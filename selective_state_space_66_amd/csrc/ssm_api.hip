@@ -95,10 +95,10 @@ const char* ssm_status_string(int status) {
   }
 }
 
-int ssm_scan_fwd_ex(const void* u, const void* delta, const float* A, const void* B,
+static int scan_fwd_impl(const void* u, const void* delta, const float* A, const void* B,
                     const void* C, const float* D, const void* z, const float* delta_bias,
                     int softplus, int dt_mode, const float* h0, const int32_t* seq_lens,
-                    const uint8_t* reset, void* y, float* last_state, int64_t batch,
+                    const uint8_t* reset, void* y, float* last_state, float* ckpt, int64_t batch,
                     int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype, void* stream) {
   int st = check_common(batch, seqlen, dim, dstate, io_dtype, softplus, dt_mode);
   if (st != SSM_OK) return st;
@@ -107,6 +107,7 @@ int ssm_scan_fwd_ex(const void* u, const void* delta, const float* A, const void
   if (!has_rows) return SSM_OK;
   if (!A) return SSM_ERR_NULL;
   if (has_tokens && (!u || !delta || !B || !C || !y)) return SSM_ERR_NULL;
+  if (ckpt && !aligned(ckpt, 4)) return SSM_ERR_ALIGN;
   const size_t es = io_dtype == SSM_BF16 ? 2 : 4;
   const void* io_ptrs[6] = {u, delta, B, C, z, y};
   for (const void* q : io_ptrs)
@@ -120,7 +121,7 @@ int ssm_scan_fwd_ex(const void* u, const void* delta, const float* A, const void
   ssm66::ScanParams p;
   p.u = u; p.delta = delta; p.A = A; p.B = B; p.C = C; p.D = D; p.z = z;
   p.delta_bias = delta_bias; p.h0 = h0; p.seq_lens = seq_lens; p.reset = reset;
-  p.y = y; p.last_state = last_state;
+  p.y = y; p.last_state = last_state; p.ckpt = has_tokens ? ckpt : nullptr;
   p.batch = batch; p.L = seqlen; p.dim = dim; p.N = dstate; p.softplus = softplus;
   hipError_t e;
   if (has_tokens && use_time_parallel(batch, dim, seqlen)) {
@@ -133,6 +134,30 @@ int ssm_scan_fwd_ex(const void* u, const void* delta, const float* A, const void
                                (hipStream_t)stream);
   }
   return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
+int ssm_scan_fwd_ex(const void* u, const void* delta, const float* A, const void* B,
+                    const void* C, const float* D, const void* z, const float* delta_bias,
+                    int softplus, int dt_mode, const float* h0, const int32_t* seq_lens,
+                    const uint8_t* reset, void* y, float* last_state, int64_t batch,
+                    int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype, void* stream) {
+  return scan_fwd_impl(u, delta, A, B, C, D, z, delta_bias, softplus, dt_mode, h0, seq_lens, reset,
+                       y, last_state, nullptr, batch, seqlen, dim, dstate, io_dtype, stream);
+}
+
+size_t ssm_scan_ckpt_size(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate) {
+  if (check_common(batch, seqlen, dim, dstate, SSM_F32, 0, SSM_DT_ZOH) != SSM_OK) return 0;
+  return ssm66::scan_bwd_ckpt_bytes(batch, seqlen, dim, dstate);
+}
+
+int ssm_scan_fwd_ckpt(const void* u, const void* delta, const float* A, const void* B,
+                      const void* C, const float* D, const void* z, const float* delta_bias,
+                      int softplus, int dt_mode, const float* h0, void* y, float* last_state,
+                      float* ckpt, int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                      int io_dtype, void* stream) {
+  if (seqlen > 0 && batch > 0 && dim > 0 && !ckpt) return SSM_ERR_NULL;
+  return scan_fwd_impl(u, delta, A, B, C, D, z, delta_bias, softplus, dt_mode, h0, nullptr,
+                       nullptr, y, last_state, ckpt, batch, seqlen, dim, dstate, io_dtype, stream);
 }
 
 int ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
@@ -176,13 +201,13 @@ size_t ssm_scan_bwd_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, i
   return ssm66::scan_bwd_workspace_bytes(batch, seqlen, dim, dstate);
 }
 
-int ssm_scan_bwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
-                 const float* D, const void* z, const float* delta_bias, int softplus,
-                 int dt_mode, const float* h0, const void* dy, const float* dlast_state,
-                 void* du, void* ddelta, float* dA, void* dB, void* dC, float* dD, void* dz,
-                 float* ddelta_bias, float* dh0, void* workspace, size_t workspace_bytes,
-                 int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype,
-                 void* stream) {
+int ssm_scan_bwd_ex(const void* u, const void* delta, const float* A, const void* B,
+                    const void* C, const float* D, const void* z, const float* delta_bias,
+                    int softplus, int dt_mode, const float* h0, const void* dy,
+                    const float* dlast_state, void* du, void* ddelta, float* dA, void* dB,
+                    void* dC, float* dD, void* dz, float* ddelta_bias, float* dh0,
+                    const float* ckpt, void* workspace, size_t workspace_bytes, int64_t batch,
+                    int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype, void* stream) {
   int st = check_common(batch, seqlen, dim, dstate, io_dtype, softplus, dt_mode);
   if (st != SSM_OK) return st;
   if (batch == 0 || dim == 0) return SSM_OK;
@@ -198,8 +223,8 @@ int ssm_scan_bwd(const void* u, const void* delta, const float* A, const void* B
   const void* io_ptrs[11] = {u, delta, B, C, z, dy, du, ddelta, dB, dC, dz};
   for (const void* q : io_ptrs)
     if (q && !aligned(q, es)) return SSM_ERR_ALIGN;
-  const void* f32_ptrs[10] = {A, D, delta_bias, h0, dlast_state, dA, dD, ddelta_bias, dh0,
-                              workspace};
+  const void* f32_ptrs[11] = {A, D, delta_bias, h0, dlast_state, dA, dD, ddelta_bias, dh0,
+                              ckpt, workspace};
   for (const void* q : f32_ptrs)
     if (q && !aligned(q, 4)) return SSM_ERR_ALIGN;
   if (!aligned(workspace, 256)) return SSM_ERR_ALIGN;
@@ -211,10 +236,23 @@ int ssm_scan_bwd(const void* u, const void* delta, const float* A, const void* B
   p.du = du; p.ddelta = ddelta; p.dB = dB; p.dC = dC; p.dz = dz;
   p.dA = dA; p.dD = dD; p.ddelta_bias = ddelta_bias; p.dh0 = dh0;
   p.workspace = workspace;
+  p.ckpt = ckpt;
   p.batch = batch; p.L = seqlen; p.dim = dim; p.N = dstate; p.softplus = softplus;
   const hipError_t e = ssm66::launch_scan_bwd(p, io_dtype, dt_mode == SSM_DT_ZOH, z != nullptr,
                                               (hipStream_t)stream);
   return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
+int ssm_scan_bwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                 const float* D, const void* z, const float* delta_bias, int softplus,
+                 int dt_mode, const float* h0, const void* dy, const float* dlast_state,
+                 void* du, void* ddelta, float* dA, void* dB, void* dC, float* dD, void* dz,
+                 float* ddelta_bias, float* dh0, void* workspace, size_t workspace_bytes,
+                 int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype,
+                 void* stream) {
+  return ssm_scan_bwd_ex(u, delta, A, B, C, D, z, delta_bias, softplus, dt_mode, h0, dy,
+                         dlast_state, du, ddelta, dA, dB, dC, dD, dz, ddelta_bias, dh0, nullptr,
+                         workspace, workspace_bytes, batch, seqlen, dim, dstate, io_dtype, stream);
 }
 
 int ssm_ssd_fwd(const void* x, const float* dt, const float* A, const void* B, const void* C,

@@ -20,6 +20,7 @@ struct ScanParams {
   const uint8_t* reset;     // nullable: document starts (batch, L)
   void* y;
   float* last_state;  // nullable; may be the same buffer as h0
+  float* ckpt;        // nullable: the state before every 16th token (batch, ceil(L/16), dim, N)
   int64_t batch, L, dim, N;
   int softplus;
 };
@@ -45,6 +46,7 @@ struct ScanBwdParams {
   void *du, *ddelta, *dB, *dC, *dz;           // io dtype; dz nullable
   float *dA, *dD, *ddelta_bias, *dh0;          // dD, ddelta_bias, dh0 nullable
   void* workspace;                             // scan_bwd_workspace_bytes(...) bytes
+  const float* ckpt;                           // nullable: checkpoints written by the forward
   int64_t batch, L, dim, N;
   int softplus;
 };

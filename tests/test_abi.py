@@ -34,7 +34,8 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared_functions()
-    assert set(names) == {"ssm_scan_fwd", "ssm_scan_fwd_ex", "ssm_scan_bwd",
+    assert set(names) == {"ssm_scan_fwd", "ssm_scan_fwd_ex", "ssm_scan_fwd_ckpt",
+                          "ssm_scan_ckpt_size", "ssm_scan_bwd", "ssm_scan_bwd_ex",
                           "ssm_scan_bwd_workspace_size", "ssm_step", "ssm_ssd_fwd",
                           "ssm_conv1d_fwd", "ssm_conv1d_step", "ssm_status_string",
                           "ssm_abi_version"}
@@ -209,6 +210,50 @@ def test_bwd_workspace_size(lib):
     assert f(2, 40, 70, 16) >= 4 * 2 * 3 * 70 * 16  # three 16-token checkpoints per row
     assert f(-1, 4, 4, 4) == 0 and f(1, 4, 4, 17) == 0
     assert f(8, 2048, 1536, 16) > f(8, 1024, 1536, 16)
+
+
+def _bwd_ex(lib, ckpt, **kw):
+    a = dict(u=FAKE, delta=FAKE, A=FAKE, B=FAKE, C=FAKE, D=None, z=None, bias=None, softplus=1,
+             dt_mode=0, h0=None, dy=FAKE, dlast=None, du=FAKE, ddelta=FAKE, dA=FAKE, dB=FAKE,
+             dC=FAKE, dD=None, dz=None, dbias=None, dh0=None, ws=ctypes.c_void_p(0x100000),
+             wsb=1 << 40, batch=2, L=8, dim=64, N=16, io=1, stream=None)
+    a.update(kw)
+    return lib.ssm_scan_bwd_ex(a["u"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"],
+                               a["bias"], a["softplus"], a["dt_mode"], a["h0"], a["dy"],
+                               a["dlast"], a["du"], a["ddelta"], a["dA"], a["dB"], a["dC"],
+                               a["dD"], a["dz"], a["dbias"], a["dh0"], ckpt, a["ws"], a["wsb"],
+                               a["batch"], a["L"], a["dim"], a["N"], a["io"], a["stream"])
+
+
+def _fwd_ckpt(lib, **kw):
+    a = dict(u=FAKE, delta=FAKE, A=FAKE, B=FAKE, C=FAKE, D=None, z=None, bias=None, softplus=1,
+             dt_mode=0, h0=None, y=FAKE, last=None, ckpt=FAKE, batch=2, L=40, dim=64, N=16,
+             io=1, stream=None)
+    a.update(kw)
+    return lib.ssm_scan_fwd_ckpt(a["u"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"],
+                                 a["bias"], a["softplus"], a["dt_mode"], a["h0"], a["y"], a["last"],
+                                 a["ckpt"], a["batch"], a["L"], a["dim"], a["N"], a["io"],
+                                 a["stream"])
+
+
+def test_training_entry_points_reject_invalid_arguments(lib):
+    c = _header_constants()
+    assert _fwd_ckpt(lib, ckpt=None) == c["SSM_ERR_NULL"]   # checkpoints are the point
+    assert _fwd_ckpt(lib, ckpt=MISALIGNED) == c["SSM_ERR_ALIGN"]
+    assert _fwd_ckpt(lib, N=17) == c["SSM_ERR_SHAPE"]
+    assert _fwd_ckpt(lib, io=3) == c["SSM_ERR_DTYPE"]
+    assert _fwd_ckpt(lib, u=None) == c["SSM_ERR_NULL"]
+    assert _fwd_ckpt(lib, batch=0) == c["SSM_OK"]           # nothing to do, nothing launched
+    assert _bwd_ex(lib, MISALIGNED) == c["SSM_ERR_ALIGN"]
+    assert _bwd_ex(lib, FAKE, dy=None) == c["SSM_ERR_NULL"]
+    assert _bwd_ex(lib, FAKE, batch=0) == c["SSM_OK"]
+
+
+def test_ckpt_size(lib):
+    f = lib.ssm_scan_ckpt_size
+    assert f(2, 40, 70, 16) == (2 * 3 * 70 * 16 * 4 + 255) // 256 * 256  # states before 0, 16, 32
+    assert f(1, 16, 8, 16) == 8 * 16 * 4 and f(1, 17, 8, 16) == 2 * 8 * 16 * 4
+    assert f(-1, 4, 4, 4) == 0 and f(1, 4, 4, 17) == 0
 
 
 ALIGN16 = ctypes.c_void_p(0x10000)

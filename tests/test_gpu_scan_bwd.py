@@ -188,3 +188,97 @@ def test_bwd_full_size_sampled():
         _compare(got, r, "bf16", f"full {mode}")
         del g
         torch.cuda.empty_cache()
+
+
+# ------------------------------------------------- the training forward's checkpoints
+
+@pytest.mark.parametrize("kernel", ["lds1", "lds2", "lds4", "tpar"])
+@pytest.mark.parametrize("mode", ["zoh", "euler"])
+def test_train_forward_checkpoints(kernel, mode, monkeypatch):
+    """scan_fwd_train gives scan_fwd's y and last_state bit for bit, and its
+    checkpoint j is the state before token 16 j: the oracle's final state of
+    the sequence cut there (j = 0: h0).  A ragged channel tile, a ragged last
+    chunk, a zero and a slow channel (both ZOH forms)."""
+    monkeypatch.setenv("SSM66_SCAN_KERNEL", kernel)
+    inp = W.scan_inputs(_cfg(2, 99, 34, 16, "f32", True, seed=110))
+    A = inp["A"].copy()
+    A[5, 2] = 0.0
+    A[9, :] = -0.2
+    inp["A"] = A
+    h0 = np.random.default_rng(111).normal(size=(2, 34, 16)).astype(np.float32)
+    args = (to_dev(inp["u"], "f32"), to_dev(inp["delta"], "f32"), to_dev(inp["A"], "f32"),
+            to_dev(inp["B"], "f32"), to_dev(inp["C"], "f32"))
+    kw = dict(D=to_dev(inp["D"], "f32"), z=to_dev(inp["z"], "f32"),
+              delta_bias=to_dev(inp["delta_bias"], "f32"), dt_mode=mode, h0=to_dev(h0, "f32"))
+    y, last, ck = ssm.scan_fwd_train(*args, **kw)
+    y2, last2 = ssm.scan_fwd(*args, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2) and torch.equal(last, last2)
+    ckh = to_host64(ck)
+    assert ckh.shape == (2, 7, 34, 16)
+    for j in range(7):
+        t = 16 * j
+        sub = dict(inp)
+        for k in ("u", "delta", "z"):
+            sub[k] = inp[k][:, :t]
+        for k in ("B", "C"):
+            sub[k] = inp[k][:, :t]
+        _, lr = oracle.scan_fwd(sub["u"], sub["delta"], sub["A"], sub["B"], sub["C"], D=sub["D"],
+                                z=sub["z"], delta_bias=sub["delta_bias"], dt_mode=mode,
+                                h0=h0.astype(np.float64))
+        err = np.abs(ckh[:, j] - lr) / (1.0 + np.abs(lr))
+        assert err.max() <= 1e-4, f"checkpoint {j}: {err.max():.2e}"
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("mode", ["zoh", "euler"])
+def test_bwd_from_forward_checkpoints(io, mode):
+    """ssm_scan_bwd_ex with the training forward's checkpoints (no forward
+    sweep in the backward) against the oracle's backward."""
+    inp = W.scan_inputs(_cfg(2, 99, 34, 16, io, True, seed=112))
+    dy = _dy((2, 99, 34), io, 113)
+    rng = np.random.default_rng(114)
+    h0 = rng.normal(size=(2, 34, 16)).astype(np.float32)
+    dlast = rng.normal(size=(2, 34, 16)).astype(np.float32)
+    args = (to_dev(inp["u"], io), to_dev(inp["delta"], io), to_dev(inp["A"], "f32"),
+            to_dev(inp["B"], io), to_dev(inp["C"], io))
+    kw = dict(D=to_dev(inp["D"], "f32"), z=to_dev(inp["z"], io),
+              delta_bias=to_dev(inp["delta_bias"], "f32"), dt_mode=mode, h0=to_dev(h0, "f32"))
+    _, _, ck = ssm.scan_fwd_train(*args, **kw)
+    g = ssm.scan_bwd(*args, to_dev(dy, io), dlast=to_dev(dlast, "f32"), ckpt=ck, **kw)
+    torch.cuda.synchronize()
+    r = oracle.scan_bwd(f64(inp["u"], io), f64(inp["delta"], io), inp["A"], f64(inp["B"], io),
+                        f64(inp["C"], io), f64(dy, io), D=inp["D"], z=f64(inp["z"], io),
+                        delta_bias=inp["delta_bias"], dt_mode=mode, h0=h0.astype(np.float64),
+                        dlast=dlast.astype(np.float64))
+    _compare(g, r, io, f"from checkpoints {io} {mode}")
+
+
+def test_bwd_from_forward_checkpoints_full_size_sampled():
+    """The Mamba-130M layer, training forward then backward from its
+    checkpoints (the launch configuration bench.py times): dy on sampled
+    channels only, against the oracle's backward on those channels."""
+    cfg = W.SCAN_CONFIGS["mamba130m"]
+    inp = W.scan_inputs(cfg)
+    ch = np.array([0, 1, 17, 600, 1535])
+    dy = np.zeros((cfg.batch, cfg.L, cfg.dim), dtype=np.uint16)
+    dsub = _dy((cfg.batch, cfg.L, len(ch)), "bf16", 115)
+    dy[:, :, ch] = dsub
+    sub = W.scan_inputs(cfg, channels=ch)
+    chd = torch.from_numpy(ch).to(DEV)
+    args = (to_dev(inp["u"], "bf16"), to_dev(inp["delta"], "bf16"), to_dev(inp["A"], "f32"),
+            to_dev(inp["B"], "bf16"), to_dev(inp["C"], "bf16"))
+    kw = dict(D=to_dev(inp["D"], "f32"), z=to_dev(inp["z"], "bf16"),
+              delta_bias=to_dev(inp["delta_bias"], "f32"), dt_mode="zoh")
+    _, _, ck = ssm.scan_fwd_train(*args, **kw)
+    g = ssm.scan_bwd(*args, to_dev(dy, "bf16"), ckpt=ck, **kw)
+    torch.cuda.synchronize()
+    r = oracle.scan_bwd(f64(sub["u"], "bf16"), f64(sub["delta"], "bf16"), sub["A"],
+                        f64(sub["B"], "bf16"), f64(sub["C"], "bf16"), f64(dsub, "bf16"),
+                        D=sub["D"], z=f64(sub["z"], "bf16"), delta_bias=sub["delta_bias"],
+                        dt_mode="zoh")
+    got = {"du": g["du"].index_select(2, chd), "ddelta": g["ddelta"].index_select(2, chd),
+           "dz": g["dz"].index_select(2, chd), "dA": g["dA"].index_select(0, chd),
+           "dD": g["dD"].index_select(0, chd), "ddelta_bias": g["ddelta_bias"].index_select(0, chd),
+           "dB": g["dB"], "dC": g["dC"], "dh0": None}
+    _compare(got, r, "bf16", "full from checkpoints")
