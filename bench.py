@@ -261,6 +261,48 @@ def time_bwd(sets, steps, warmup, dev):
     return float(np.mean([a.elapsed_time(b) for a, b in ev])), ws.numel()
 
 
+def time_train(sets, steps, warmup, dev):
+    """The training path on the same layer: ssm_scan_fwd_ckpt (the forward that
+    keeps the state every 16 tokens) and ssm_scan_bwd_ex from those checkpoints,
+    rotating the input sets; returns (forward ms, backward ms) per launch."""
+    import torch
+    import selective_state_space_66_amd as ssm
+    s0 = sets[0]
+    batch, L, dim = s0["u"].shape
+    N = s0["A"].shape[1]
+    ws = torch.empty(ssm.scan_bwd_workspace_size(batch, L, dim, N), dtype=torch.uint8, device=dev)
+    gen = torch.Generator(device="cpu").manual_seed(13)
+    dys = [torch.randn((batch, L, dim), generator=gen).to(torch.bfloat16).to(dev) for _ in sets]
+    outs = [ssm.scan_fwd_train(s["u"], s["delta"], s["A"], s["B"], s["C"], D=s["D"], z=s["z"],
+                               delta_bias=s["delta_bias"]) for s in sets]
+
+    def fwd(i):
+        s, (y, last, ck) = sets[i % len(sets)], outs[i % len(sets)]
+        ssm.scan_fwd_train(s["u"], s["delta"], s["A"], s["B"], s["C"], D=s["D"], z=s["z"],
+                           delta_bias=s["delta_bias"], y=y, last_state=last, ckpt=ck)
+
+    def bwd(i):
+        s, (_, _, ck) = sets[i % len(sets)], outs[i % len(sets)]
+        ssm.scan_bwd(s["u"], s["delta"], s["A"], s["B"], s["C"], dys[i % len(sets)], D=s["D"],
+                     z=s["z"], delta_bias=s["delta_bias"], workspace=ws, ckpt=ck)
+
+    res = []
+    for launch in (fwd, bwd):
+        for i in range(warmup):
+            launch(i)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        for i in range(steps):
+            ev[i][0].record()
+            launch(warmup + i)
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        res.append(float(np.mean([a.elapsed_time(b) for a, b in ev])))
+    del outs, ws
+    return res[0], res[1]
+
+
 def ssd_bytes(b, L, H, P, N, gate):
     """Algorithmic bytes of the SSD layer (bf16 io): x, [z] read and y written
     once, B and C read once, dt (fp32) read once, A, D, dt_bias, and the final
@@ -513,6 +555,7 @@ def main():
 
     log("[bench] timing the backward pass")
     b_ms, b_ws = time_bwd(sets, max(5, args.steps // 5), 2, dev)
+    tf_ms, tb_ms = time_train(sets, max(5, args.steps // 5), 2, dev)
     log(f"[bench] backward: {b_ms:.4f} ms per call (workspace {b_ws / 1e6:.1f} MB)")
 
     log("[bench] timing the convolution")
@@ -595,7 +638,12 @@ def main():
                             "dA, dB, dC, dD, d bias (states recomputed from the inputs)",
                 "ms": round(b_ms, 4), "x_forward": round(b_ms / kern_ms, 2),
                 "updates_per_s": float(f"{elems * cfg.N / (b_ms * 1e-3):.4g}"),
-                "workspace_MB": round(b_ws / 1e6, 1)},
+                "workspace_MB": round(b_ws / 1e6, 1),
+                "training": {"workload": "ssm_scan_fwd_ckpt (keeps the state every 16 tokens) then "
+                                         "ssm_scan_bwd_ex from those checkpoints, same layer",
+                             "forward_ms": round(tf_ms, 4), "backward_ms": round(tb_ms, 4),
+                             "step_ms": round(tf_ms + tb_ms, 4),
+                             "step_ms_without_checkpoints": round(kern_ms + b_ms, 4)}},
         "conv": conv,
         "ssd": ssd,
         "time_parallel": narrow,
