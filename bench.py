@@ -24,6 +24,8 @@ one input set and prints no JSON:
     python bench.py --only decode [--launches 3]
     python bench.py --only conv [--launches 3]
     python bench.py --only ssd [--launches 3]
+    python bench.py --only bwd [--dt-mode zoh|euler] [--launches 3]   # the backward, Mamba-130M layer
+    python bench.py --only tpar [--launches 3]   # the time-parallel scan, Mamba-130M layer at batch 1
     python bench.py --only copy     # a plain 256 MiB device copy, for counter calibration
 """
 import argparse
@@ -472,6 +474,24 @@ def profile_only(what, launches, dt_mode):
         for _ in range(launches):
             ssm.scan_fwd(s["u"], s["delta"], s["A"], s["B"], s["C"], D=s["D"], z=s["z"],
                          delta_bias=s["delta_bias"], dt_mode=dt_mode, y=y, last_state=last)
+    elif what == "bwd":
+        cfg = W.SCAN_CONFIGS["mamba130m"]
+        s = upload_scan(W.scan_inputs(cfg), dev)
+        ws = torch.empty(ssm.scan_bwd_workspace_size(cfg.batch, cfg.L, cfg.dim, cfg.N),
+                         dtype=torch.uint8, device=dev)
+        gen = torch.Generator(device="cpu").manual_seed(12)
+        dy = torch.randn((cfg.batch, cfg.L, cfg.dim), generator=gen).to(torch.bfloat16).to(dev)
+        for _ in range(launches):
+            ssm.scan_bwd(s["u"], s["delta"], s["A"], s["B"], s["C"], dy, D=s["D"], z=s["z"],
+                         delta_bias=s["delta_bias"], dt_mode=dt_mode, workspace=ws)
+    elif what == "tpar":
+        cfg = W.ScanConfig("mamba130m_batch1", 1, 2048, 1536, 16, "bf16", True, 7)
+        s = upload_scan(W.scan_inputs(cfg), dev)
+        y = torch.empty_like(s["u"])
+        last = torch.empty(cfg.batch, cfg.dim, cfg.N, device=dev)
+        for _ in range(launches):
+            ssm.scan_fwd(s["u"], s["delta"], s["A"], s["B"], s["C"], D=s["D"], z=s["z"],
+                         delta_bias=s["delta_bias"], dt_mode=dt_mode, y=y, last_state=last)
     elif what == "decode":
         time_decode(W.STEP_CONFIGS["decode"], launches, dev, npool=2)
     elif what == "ssd":
@@ -500,7 +520,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--decode-steps", type=int, default=1000)
-    ap.add_argument("--only", choices=["scan", "decode", "conv", "ssd", "copy"], default=None,
+    ap.add_argument("--only", choices=["scan", "bwd", "tpar", "decode", "conv", "ssd", "copy"],
+                    default=None,
                     help="profiling mode: a few launches of one kernel, no JSON")
     ap.add_argument("--launches", type=int, default=3)
     ap.add_argument("--dt-mode", choices=["zoh", "euler"], default="zoh")
