@@ -230,6 +230,36 @@ def test_train_forward_checkpoints(kernel, mode, monkeypatch):
         assert err.max() <= 1e-4, f"checkpoint {j}: {err.max():.2e}"
 
 
+@pytest.mark.parametrize("kernel", [None, "tpar"])
+@pytest.mark.parametrize("N", [3, 8])
+def test_train_forward_checkpoints_small_state(kernel, N, monkeypatch):
+    """State sizes below 16 (padded state groups in the sequential kernel,
+    element loads in the time-parallel one), ZOH: checkpoints against the
+    oracle, and the backward from them against the oracle's backward."""
+    if kernel:
+        monkeypatch.setenv("SSM66_SCAN_KERNEL", kernel)
+    inp = W.scan_inputs(_cfg(2, 70, 20, N, "f32", True, seed=116 + N))
+    dy = _dy((2, 70, 20), "f32", 117)
+    args = (to_dev(inp["u"], "f32"), to_dev(inp["delta"], "f32"), to_dev(inp["A"], "f32"),
+            to_dev(inp["B"], "f32"), to_dev(inp["C"], "f32"))
+    kw = dict(D=to_dev(inp["D"], "f32"), z=to_dev(inp["z"], "f32"),
+              delta_bias=to_dev(inp["delta_bias"], "f32"))
+    _, _, ck = ssm.scan_fwd_train(*args, **kw)
+    g = ssm.scan_bwd(*args, to_dev(dy, "f32"), ckpt=ck, **kw)
+    torch.cuda.synchronize()
+    ckh = to_host64(ck)
+    for j in range(5):
+        t = 16 * j
+        _, lr = oracle.scan_fwd(inp["u"][:, :t], inp["delta"][:, :t], inp["A"], inp["B"][:, :t],
+                                inp["C"][:, :t], D=inp["D"], z=inp["z"][:, :t],
+                                delta_bias=inp["delta_bias"])
+        err = np.abs(ckh[:, j] - lr) / (1.0 + np.abs(lr))
+        assert err.max() <= 1e-4, f"N={N} checkpoint {j}: {err.max():.2e}"
+    r = oracle.scan_bwd(inp["u"], inp["delta"], inp["A"], inp["B"], inp["C"], dy, D=inp["D"],
+                        z=inp["z"], delta_bias=inp["delta_bias"])
+    _compare(g, r, "f32", f"small state N={N} {kernel}")
+
+
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 @pytest.mark.parametrize("mode", ["zoh", "euler"])
 def test_bwd_from_forward_checkpoints(io, mode):
