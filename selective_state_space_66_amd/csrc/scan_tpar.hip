@@ -43,33 +43,41 @@ constexpr int kTW = 4;        // waves per block
 constexpr int kTT = 64 * kTW; // tokens per chunk
 constexpr int kNMax = 16;     // largest state size
 
-// One combine step of the inclusive pair scan: the pair of the lane the DPP
-// control addresses (earlier tokens) is applied first,
+// The inclusive pair scan over the 64 lanes for four states at once: lane i
+// ends with the composition of the pairs of lanes 0..i (row shifts by 1, 2, 4,
+// 8, then the last lane of rows 0 and 2 into rows 1 and 3, and lane 31 into
+// rows 2 and 3).  One combine step applies the pair of the lane the DPP
+// control addresses (earlier tokens) first,
 //   b <- a * b_src + b,  a <- a * a_src,
 // as v_fmac_f32 and v_mul_f32 with a DPP source operand.  With bound_ctrl
 // off, a lane with no source lane (or in a row outside the row mask) is not
 // written, i.e. it keeps its pair: the identity (1, 0) is never materialised.
-// A VALU write followed by a DPP read of the same VGPR needs two wait states;
-// each block starts with them.
-#define SSM66_PAIR_STEP(CTRL)                                                     \
-  asm volatile("s_nop 1\n\t"                                                  \
-               "v_fmac_f32_dpp %0, %0, %1 " CTRL " bank_mask:0xf\n\t"          \
-               "s_nop 1\n\t"                                                  \
-               "v_mul_f32_dpp %1, %1, %1 " CTRL " bank_mask:0xf"                 \
-               : "+v"(b), "+v"(a))
+// A VALU write followed by a DPP read of the same VGPR needs two wait states:
+// the four states' instructions are interleaved so that three others separate
+// each write from the DPP read of its result, and only the block's first
+// read (of values the compiler has just written) waits.
+#define SSM66_STEP4(CTRL)                                         \
+  "v_fmac_f32_dpp %0, %0, %4 " CTRL " bank_mask:0xf\n\t"        \
+  "v_fmac_f32_dpp %1, %1, %5 " CTRL " bank_mask:0xf\n\t"        \
+  "v_fmac_f32_dpp %2, %2, %6 " CTRL " bank_mask:0xf\n\t"        \
+  "v_fmac_f32_dpp %3, %3, %7 " CTRL " bank_mask:0xf\n\t"        \
+  "v_mul_f32_dpp %4, %4, %4 " CTRL " bank_mask:0xf\n\t"         \
+  "v_mul_f32_dpp %5, %5, %5 " CTRL " bank_mask:0xf\n\t"         \
+  "v_mul_f32_dpp %6, %6, %6 " CTRL " bank_mask:0xf\n\t"         \
+  "v_mul_f32_dpp %7, %7, %7 " CTRL " bank_mask:0xf\n\t"
 
-// Inclusive scan over the 64 lanes: lane i ends with the composition of the
-// pairs of lanes 0..i (row shifts by 1, 2, 4, 8, then the last lane of rows 0
-// and 2 into rows 1 and 3, and lane 31 into rows 2 and 3).
-__device__ __forceinline__ void pair_scan(float& a, float& b) {
-  SSM66_PAIR_STEP("row_shr:1 row_mask:0xf");
-  SSM66_PAIR_STEP("row_shr:2 row_mask:0xf");
-  SSM66_PAIR_STEP("row_shr:4 row_mask:0xf");
-  SSM66_PAIR_STEP("row_shr:8 row_mask:0xf");
-  SSM66_PAIR_STEP("row_bcast:15 row_mask:0xa");
-  SSM66_PAIR_STEP("row_bcast:31 row_mask:0xc");
+__device__ __forceinline__ void pair_scan4(float (&a)[4], float (&b)[4]) {
+  asm volatile("s_nop 1\n\t"
+               SSM66_STEP4("row_shr:1 row_mask:0xf")
+               SSM66_STEP4("row_shr:2 row_mask:0xf")
+               SSM66_STEP4("row_shr:4 row_mask:0xf")
+               SSM66_STEP4("row_shr:8 row_mask:0xf")
+               SSM66_STEP4("row_bcast:15 row_mask:0xa")
+               SSM66_STEP4("row_bcast:31 row_mask:0xc")
+               : "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]),
+                 "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]));
 }
-#undef SSM66_PAIR_STEP
+#undef SSM66_STEP4
 
 __device__ __forceinline__ float lane_bcast(float v, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
@@ -204,26 +212,38 @@ __global__ __launch_bounds__(64 * kTW) void scan_tpar_kernel(
     // per-state form is chosen once per block when every state takes the
     // same one (FORM 0: Euler, 1: ZOH g form, 2: ZOH, per state).
     float pa[kNMax], pb[kNMax];
+    // the states are formed and scanned four at a time; with a state size
+    // below 16 the states of the last group past N are finite dummies (A = 0)
+    // that are never read out, and groups wholly past N are skipped
     auto pairs = [&](auto form_tag) {
       constexpr int FORM = decltype(form_tag)::value;
 #pragma unroll
-      for (int n = 0; n < kNMax; ++n) {
-        if (NF || n < N) {
-          const float apn = cst[0][n];
-          float a = exp2_hw(dl * apn);
-          float bu;
-          if (FORM == 0) {
-            bu = dl * Bv[n] * x;
-          } else if (FORM == 1 || ((fast_mask >> n) & 1)) {
-            const float wu = x * Bv[n];
-            bu = fmaf(a, wu, -wu);  // (abar - 1) u B, in g units
-          } else {
-            bu = dl * Bv[n] * zoh_phi(dl * apn * kLn2, a) * x;  // Delta A = Delta A log2(e) ln 2
+      for (int q = 0; q < kNMax / 4; ++q) {
+        if (NF || 4 * q < N) {
+          float a4[4], b4[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int n = 4 * q + i;
+            const float apn = cst[0][n];
+            const float a = exp2_hw(dl * apn);
+            float bu;
+            if (FORM == 0) {
+              bu = dl * Bv[n] * x;
+            } else if (FORM == 1 || ((fast_mask >> n) & 1)) {
+              const float wu = x * Bv[n];
+              bu = fmaf(a, wu, -wu);  // (abar - 1) u B, in g units
+            } else {
+              bu = dl * Bv[n] * zoh_phi(dl * apn * kLn2, a) * x;  // Delta A = Delta A log2(e) ln 2
+            }
+            a4[i] = rst ? 0.0f : a;
+            b4[i] = bu;
           }
-          if (rst) a = 0.0f;
-          pair_scan(a, bu);
-          pa[n] = a;
-          pb[n] = bu;
+          pair_scan4(a4, b4);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            pa[4 * q + i] = a4[i];
+            pb[4 * q + i] = b4[i];
+          }
         }
       }
     };
