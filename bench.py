@@ -12,7 +12,8 @@ one.  `value` is algorithmic bytes per step / measured step time.
 Also reported, outside `value`: the same scan under the exponential-Euler rule,
 the extended scan (initial state, lengths, document resets), the backward pass,
 the block's convolution (sequence and decoding step), the Mamba-2 / SSD layer
-on the matrix cores, the decode step (ssm_step) on its
+on the matrix cores, the scan on the Mamba-1.4B and long-sequence layers,
+the decode step (ssm_step) on its
 workload (batch 256, D 5120, N 16, 1000 consecutive tokens), the kernel
 roofline for the dominant kernel, and the fp64 CPU oracle timed on the host.
 
@@ -196,6 +197,73 @@ def time_narrow(dev, steps, warmup):
                      "alu_frac": round(FLOPS_PER_UPDATE * upd / (res["auto"] * 1e-3) / 1e12
                                        / ALU_PEAK_TFLOPS, 4)}
         del sets
+    return out
+
+
+def device_scan_inputs(cfg, dev):
+    """Timing inputs for a large scan workload, drawn on the device.
+
+    The (batch, L, D) tensors (u, raw delta, z) are N(0, 1) draws from torch's
+    seeded device generator, rounded to bf16; A, D, the dt bias, B, C, the
+    long-sequence filler vector and its 16 fresh positions per sequence follow
+    the workload recipe exactly.  The big tensors' values differ from the
+    parity tests' draws of the same recipe (generating those on the host takes
+    minutes at these sizes); the kernels' timing depends on the values only
+    through A, which picks the ZOH form."""
+    import torch
+    import workloads as W
+    b, L, dim, N = cfg.batch, cfg.L, cfg.dim, cfg.N
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(cfg.seed)
+
+    def big():
+        return torch.randn((b, L, dim), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+
+    A, D, bias = W.channel_params(cfg.seed, dim, N)
+    bc_idx = np.arange(b * L * N, dtype=np.int64).reshape(b, L, N)
+    if cfg.filler:
+        filler = torch.from_numpy(W.normal(cfg.seed, W.S_U, np.arange(dim))).to(dev)
+        u = filler.to(torch.bfloat16).expand(b, L, dim).contiguous()
+        pos = W.filler_positions(cfg.seed, b, L)
+        for bi in range(b):
+            for p in pos[bi]:
+                u[bi, int(p)] = torch.randn(dim, generator=gen, device=dev).to(torch.bfloat16)
+    else:
+        u = big()
+    return dict(u=u, delta=big(), A=to_dev(A, "f32", dev),
+                B=to_dev(W.to_bf16_bits(W.normal(cfg.seed, W.S_B, bc_idx)), "bf16", dev),
+                C=to_dev(W.to_bf16_bits(W.normal(cfg.seed, W.S_C, bc_idx)), "bf16", dev),
+                D=to_dev(D, "f32", dev), z=big() if cfg.gate else None,
+                delta_bias=to_dev(bias, "f32", dev))
+
+
+def time_layers(dev, steps, warmup):
+    """The scan forward (ZOH) on the two larger layers of the workload set: the
+    Mamba-1.4B-shaped layer (8 x 2048 x 4096, N 16, bf16, gate) and the
+    long-sequence selective-copying-like case (4 x 65536 x 2048, N 16, bf16, no
+    gate).  Each input set is far larger than the 256 MB Infinity Cache, so one
+    set is reused from launch to launch."""
+    import torch
+    import workloads as W
+    out = {}
+    for name, nsteps in (("mamba1p4b", steps), ("longseq", max(3, steps // 5))):
+        cfg = W.SCAN_CONFIGS[name]
+        sets = [device_scan_inputs(cfg, dev)]
+        torch.cuda.synchronize()
+        kern = time_scan(sets, nsteps, max(2, warmup // 5), "zoh")[1]
+        nbytes = scan_bytes(cfg.batch, cfg.L, cfg.dim, cfg.N, 2, cfg.gate)
+        upd = cfg.batch * cfg.L * cfg.dim * cfg.N
+        gbs = nbytes / (kern * 1e-3) / 1e9
+        out[name] = {"workload": f"ssm_scan_fwd: batch {cfg.batch}, L {cfg.L}, D {cfg.dim}, N {cfg.N}, "
+                                 f"bf16, {'gate' if cfg.gate else 'no gate'}, ZOH",
+                     "launches": nsteps, "kernel_ms": round(kern, 5), "GB/s": round(gbs, 2),
+                     "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+                     "elems_per_s": float(f"{cfg.batch * cfg.L * cfg.dim / (kern * 1e-3):.4g}"),
+                     "updates_per_s": float(f"{upd / (kern * 1e-3):.4g}"),
+                     "alu_frac": round(FLOPS_PER_UPDATE * upd / (kern * 1e-3) / 1e12 / ALU_PEAK_TFLOPS, 4),
+                     "algorithmic_bytes": nbytes}
+        del sets
+        torch.cuda.empty_cache()
     return out
 
 
@@ -611,6 +679,11 @@ def main():
     ssd = time_ssd(dev, args.steps, args.warmup)
     log(f"[bench] ssd: {ssd['kernel_ms']:.4f} ms")
     log(f"[bench] conv: {conv['kernel_ms']:.4f} ms, step {conv['step']['us_per_step']:.2f} us")
+    log("[bench] timing the scan on the Mamba-1.4B and long-sequence layers")
+    torch.cuda.empty_cache()
+    layers = time_layers(dev, args.steps, args.warmup)
+    log("[bench] layers: " + ", ".join(f"{k} {v['kernel_ms']:.4f} ms ({v['GB/s']:.0f} GB/s)"
+                                       for k, v in layers.items()))
     log("[bench] timing the scan on few, narrow rows")
     torch.cuda.empty_cache()
     narrow = time_narrow(dev, args.steps, args.warmup)
@@ -700,6 +773,7 @@ def main():
                              "step_ms_without_checkpoints": round(kern_ms + b_ms, 4)}},
         "conv": conv,
         "ssd": ssd,
+        "layers": layers,
         "time_parallel": narrow,
         "decode": {"workload": "ssm_step: batch 256, D 5120, N 16, bf16 io, fp32 state, gate, ZOH",
                    "steps": args.decode_steps,

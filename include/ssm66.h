@@ -111,7 +111,7 @@ extern "C" {
  * Two kernels compute it ("Mamba and selective state spaces",
  * "Selection breaks the convolution": the recurrence is an associative scan):
  * lanes holding (channel, state group) and running through time, and, for at
- * most 3072 (batch x channel) rows and 128 or more tokens, lanes holding
+ * most 4096 (batch x channel) rows and 128 or more tokens, lanes holding
  * tokens with the steps composed by a parallel scan.  Both give the same
  * result up to fp32 rounding.  The environment variable SSM66_SCAN_KERNEL
  * (read at each call) forces one: "tpar" the time-parallel kernel, "lds1",

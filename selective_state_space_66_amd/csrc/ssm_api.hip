@@ -36,9 +36,10 @@ int check_common(int64_t batch, int64_t len, int64_t dim, int64_t dstate, int io
 }
 
 // Crossover of the time-parallel scan, measured on MI355X (bf16, N 16, ZOH,
-// gate): it is faster up to 3072 (batch x channel) rows (159 against 195 us at
-// 2 x 2048 x 1536, even at 4096 rows, slower above) and from about 128 tokens.
-constexpr int64_t kTparMaxRows = 3072;
+// gate): it is faster up to 4096 (batch x channel) rows (178 against 196 us at
+// 4 x 2048 x 1024, 181 against 196 us at 2 x 2048 x 2048; about even at 4608
+// rows, slower at 6144: 261 against 221 us) and from about 128 tokens.
+constexpr int64_t kTparMaxRows = 4096;
 constexpr int64_t kTparMinLen = 128;
 
 // Scan kernel shape: G states per thread, NG state groups per channel

@@ -165,7 +165,7 @@ def _io(x: np.ndarray, io: str) -> np.ndarray:
     return to_bf16_bits(x) if io == "bf16" else np.ascontiguousarray(x, dtype=np.float32)
 
 
-def _filler_positions(seed: int, batch: int, L: int, count: int = 16) -> np.ndarray:
+def filler_positions(seed: int, batch: int, L: int, count: int = 16) -> np.ndarray:
     """(batch, count) distinct positions per sequence, sorted."""
     out = np.empty((batch, count), dtype=np.int64)
     for b in range(batch):
@@ -207,7 +207,7 @@ def scan_inputs(cfg: ScanConfig, channels: Optional[Sequence[int]] = None) -> di
         filler = normal(cfg.seed, S_U, ch)
         u = np.empty((b, L, k), dtype=np.uint16 if cfg.io == "bf16" else np.float32)
         u[...] = _io(filler, cfg.io)[None, None, :]
-        pos = _filler_positions(cfg.seed, b, L)
+        pos = filler_positions(cfg.seed, b, L)
         for bi in range(b):
             for j, p in enumerate(pos[bi]):
                 idx = (bi * 16 + j) * dim + ch
