@@ -26,7 +26,8 @@ one input set and prints no JSON:
     python bench.py --only conv [--launches 3]
     python bench.py --only ssd [--launches 3]
     python bench.py --only bwd [--dt-mode zoh|euler] [--launches 3]   # the backward, Mamba-130M layer
-    python bench.py --only tpar [--launches 3]   # the time-parallel scan, Mamba-130M layer at batch 1
+    python bench.py --only tpar [--launches 3]   # the time-parallel scan with four waves per row, forced, Mamba-130M layer at batch 1
+    python bench.py --only seq [--launches 3]    # the sequential scan (2 states per lane), forced, Mamba-130M layer
     python bench.py --only copy     # a plain 256 MiB device copy, for counter calibration
 """
 import argparse
@@ -78,7 +79,7 @@ def step_bytes(b, D, N, io_bytes, gate):
 # The sources each measured kernel is built from: its own file, plus the shared
 # device and launch headers and the C-ABI file that picks its launch shape.
 KERNEL_SOURCES = {
-    "scan_fwd_mamba130m_zoh": ["scan_fwd.hip"],
+    "scan_fwd_mamba130m_zoh": ["scan_fwd.hip", "scan_tpar.hip"],
     "step_decode_zoh": ["step.hip"],
     "conv1d_fwd_conv130m": ["conv1d.hip"],
     "ssd_fwd_ssd130m": ["ssd.hip"],
@@ -167,9 +168,10 @@ def time_narrow(dev, steps, warmup):
     leaves most of the GPU idle: the pages' speed-benchmark shape (batch 1,
     L 2048, D 1024, N 16), the Mamba-130M layer at batch 1 (1 x 2048 x 1536)
     and a long narrow sequence (1 x 65536 x 128), bf16, gate, ZOH.  Timed
-    with the library's own choice (the time-parallel scan) and with the
+    with the library's own choice (a time-parallel scan) and with the
     sequential kernel forced, for comparison."""
     import workloads as W
+    import selective_state_space_66_amd as ssm
     out = {}
     shapes = (("paper_speed_benchmark", (1, 2048, 1024)), ("mamba130m_batch1", (1, 2048, 1536)),
               ("long_narrow", (1, 65536, 128)))
@@ -190,7 +192,7 @@ def time_narrow(dev, steps, warmup):
             os.environ["SSM66_SCAN_KERNEL"] = old
         upd = b * L * D * 16
         out[name] = {"workload": f"ssm_scan_fwd: batch {b}, L {L}, D {D}, N 16, bf16, gate, ZOH",
-                     "kernel": "scan_tpar_kernel (lanes hold tokens)",
+                     "kernel": ssm.scan_kernel_name(b, L, D, 16),
                      "kernel_ms": round(res["auto"], 5),
                      "sequential_kernel_ms": round(res["sequential"], 5),
                      "speedup": round(res["sequential"] / res["auto"], 2),
@@ -245,6 +247,7 @@ def time_layers(dev, steps, warmup):
     set is reused from launch to launch."""
     import torch
     import workloads as W
+    import selective_state_space_66_amd as ssm
     out = {}
     for name, nsteps in (("mamba1p4b", steps), ("longseq", max(3, steps // 5))):
         cfg = W.SCAN_CONFIGS[name]
@@ -256,6 +259,7 @@ def time_layers(dev, steps, warmup):
         gbs = nbytes / (kern * 1e-3) / 1e9
         out[name] = {"workload": f"ssm_scan_fwd: batch {cfg.batch}, L {cfg.L}, D {cfg.dim}, N {cfg.N}, "
                                  f"bf16, {'gate' if cfg.gate else 'no gate'}, ZOH",
+                     "kernel": ssm.scan_kernel_name(cfg.batch, cfg.L, cfg.dim, cfg.N),
                      "launches": nsteps, "kernel_ms": round(kern, 5), "GB/s": round(gbs, 2),
                      "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
                      "elems_per_s": float(f"{cfg.batch * cfg.L * cfg.dim / (kern * 1e-3):.4g}"),
@@ -575,8 +579,13 @@ def profile_only(what, launches, dt_mode):
         for _ in range(launches):
             ssm.scan_bwd(s["u"], s["delta"], s["A"], s["B"], s["C"], dy, D=s["D"], z=s["z"],
                          delta_bias=s["delta_bias"], dt_mode=dt_mode, workspace=ws)
-    elif what == "tpar":
-        cfg = W.ScanConfig("mamba130m_batch1", 1, 2048, 1536, 16, "bf16", True, 7)
+    elif what in ("tpar", "seq"):
+        # the time-parallel kernel with four waves per row on the Mamba-130M
+        # layer at batch 1, or the sequential kernel (2 states per lane) on the
+        # Mamba-130M layer, forced
+        os.environ["SSM66_SCAN_KERNEL"] = "tpar" if what == "tpar" else "lds2"
+        cfg = (W.ScanConfig("mamba130m_batch1", 1, 2048, 1536, 16, "bf16", True, 7) if what == "tpar"
+               else W.SCAN_CONFIGS["mamba130m"])
         s = upload_scan(W.scan_inputs(cfg), dev)
         y = torch.empty_like(s["u"])
         last = torch.empty(cfg.batch, cfg.dim, cfg.N, device=dev)
@@ -611,7 +620,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--decode-steps", type=int, default=1000)
-    ap.add_argument("--only", choices=["scan", "bwd", "tpar", "decode", "conv", "ssd", "copy"],
+    ap.add_argument("--only", choices=["scan", "seq", "bwd", "tpar", "decode", "conv", "ssd", "copy"],
                     default=None,
                     help="profiling mode: a few launches of one kernel, no JSON")
     ap.add_argument("--launches", type=int, default=3)
@@ -643,9 +652,19 @@ def main():
     nbytes = scan_bytes(cfg.batch, cfg.L, cfg.dim, cfg.N, 2, cfg.gate)
     elems = cfg.batch * cfg.L * cfg.dim
 
-    log("[bench] timing ZOH scan")
+    scan_kernel = ssm.scan_kernel_name(cfg.batch, cfg.L, cfg.dim, cfg.N)
+    log(f"[bench] timing ZOH scan ({scan_kernel})")
     wall_ms, kern_ms = time_scan(sets, args.steps, args.warmup, "zoh")
     log(f"[bench] zoh: wall {wall_ms:.4f} ms/step, kernel {kern_ms:.4f} ms")
+    # the same scan with the sequential kernel forced, for comparison
+    old_env = os.environ.get("SSM66_SCAN_KERNEL")
+    os.environ["SSM66_SCAN_KERNEL"] = "lds2"
+    seq_kern_ms = time_scan(sets, args.steps, args.warmup, "zoh")[1]
+    if old_env is None:
+        os.environ.pop("SSM66_SCAN_KERNEL", None)
+    else:
+        os.environ["SSM66_SCAN_KERNEL"] = old_env
+    log(f"[bench] zoh, sequential kernel forced: {seq_kern_ms:.4f} ms")
     log("[bench] timing exponential-Euler scan")
     e_wall, e_kern = time_scan(sets, args.steps, args.warmup, "euler")
     log(f"[bench] euler: wall {e_wall:.4f} ms/step, kernel {e_kern:.4f} ms")
@@ -744,13 +763,17 @@ def main():
         "algorithmic_bytes_per_step": nbytes,
         "roofline": {"bound": "alu", "achieved": round(tflops, 3), "peak": round(ALU_PEAK_TFLOPS, 2),
                      "unit": "TFLOP/s", "frac": round(tflops / ALU_PEAK_TFLOPS, 4),
-                     "traffic": traffic, "kernel": "scan_fwd_kernel (ZOH, bf16, gate)",
+                     "traffic": traffic, "kernel": scan_kernel + " (ZOH, bf16, gate)",
                      "kernel_ms": round(kern_ms, 5),
                      "per_launch": {"updates": updates, "flops": FLOPS_PER_UPDATE * updates,
                                     "algorithmic_bytes": nbytes},
                      "hbm": {"achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                              "frac": round(achieved / HBM_PEAK_GBS, 4)}},
         "cpu_baseline": cpu,
+        "sequential_kernel": {"kernel": "scan_fwd_kernel (sequential, 2 states per lane), forced",
+                              "kernel_ms": round(seq_kern_ms, 5),
+                              "alu_frac": round(FLOPS_PER_UPDATE * updates / (seq_kern_ms * 1e-3) / 1e12
+                                                / ALU_PEAK_TFLOPS, 4)},
         "euler": {"ms_per_step": round(e_wall, 5), "GB/s": round(nbytes / (e_wall * 1e-3) / 1e9, 2),
                   "kernel_ms": round(e_kern, 5),
                   "alu_frac": round(FLOPS_PER_UPDATE * updates / (e_kern * 1e-3) / 1e12

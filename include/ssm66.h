@@ -80,7 +80,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 6
+#define SSM_ABI_VERSION 7
 
 /* status codes */
 #define SSM_OK 0
@@ -108,14 +108,20 @@ extern "C" {
  * h_t[b,c,n] = exp(Delta A[c,n]) h_{t-1}[b,c,n] + bbar(Delta, A[c,n], B[b,t,n]) u[b,t,c],
  * Delta = softplus?(delta[b,t,c] + delta_bias[c]), h_{-1} = 0.
  * last_state (optional) receives h after the last token.
- * Two kernels compute it ("Mamba and selective state spaces",
- * "Selection breaks the convolution": the recurrence is an associative scan):
- * lanes holding (channel, state group) and running through time, and, for at
- * most 4096 (batch x channel) rows and 128 or more tokens, lanes holding
- * tokens with the steps composed by a parallel scan.  Both give the same
- * result up to fp32 rounding.  The environment variable SSM66_SCAN_KERNEL
- * (read at each call) forces one: "tpar" the time-parallel kernel, "lds1",
- * "lds2" or "lds4" the sequential one with 1, 2 or 4 states per lane.
+ * Three kernels compute it ("Mamba and selective state spaces", "Selection
+ * breaks the convolution": the recurrence is an associative scan):
+ *   - sequential: lanes hold (channel, state group) and run through time;
+ *     for sequences under 256 tokens, and for 32768 or more (batch x
+ *     channel) rows;
+ *   - time-parallel, one wave per row: lanes hold four consecutive tokens,
+ *     composed in the lane and across the wave by a parallel scan; for
+ *     1024 to 32767 rows and 256 or more tokens;
+ *   - time-parallel, four waves per row: lanes hold one token each; for
+ *     fewer than 1024 rows and 128 or more tokens.
+ * All give the same result up to fp32 rounding; ssm_scan_kernel_name()
+ * names the one a call will run.  The environment variable SSM66_SCAN_KERNEL
+ * (read at each call) forces one: "wave" or "tpar" the time-parallel kernels,
+ * "lds1", "lds2" or "lds4" the sequential one with 1, 2 or 4 states per lane.
  * Returns SSM_OK or an error status (see above).
  */
 int ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
@@ -186,6 +192,15 @@ int ssm_scan_bwd(const void* u, const void* delta, const float* A, const void* B
  * dstate) float32, rounded up to 256 bytes.
  */
 size_t ssm_scan_ckpt_size(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate);
+
+/*
+ * The name of the kernel ssm_scan_fwd, ssm_scan_fwd_ex and ssm_scan_fwd_ckpt
+ * run for these sizes (with SSM66_SCAN_KERNEL as currently set), e.g.
+ * "scan_wave_kernel (time-parallel, one wave per row)".  A static string
+ * owned by the library; "invalid shape" for sizes the scan rejects.  Host
+ * only: no device work.
+ */
+const char* ssm_scan_kernel_name(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate);
 
 /*
  * The training forward: ssm_scan_fwd with an initial state (h0, nullable, as

@@ -55,6 +55,8 @@ def load_library():
     lib.ssm_scan_bwd_workspace_size.argtypes = [i64] * 4
     lib.ssm_scan_ckpt_size.restype = ctypes.c_size_t
     lib.ssm_scan_ckpt_size.argtypes = [i64] * 4
+    lib.ssm_scan_kernel_name.restype = ctypes.c_char_p
+    lib.ssm_scan_kernel_name.argtypes = [i64] * 4
     lib.ssm_scan_fwd_ckpt.restype = ci
     lib.ssm_scan_fwd_ckpt.argtypes = [vp] * 8 + [ci, ci] + [vp] * 4 + [i64] * 4 + [ci, vp]
     lib.ssm_scan_bwd_ex.restype = ci
@@ -337,6 +339,11 @@ def scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, softplus=Tr
     if st != 0:
         raise SsmError(st, "ssm_scan_bwd_ex")
     return g
+
+
+def scan_kernel_name(batch, L, dim, N):
+    """Name of the kernel ssm_scan_fwd runs for these sizes (host only)."""
+    return load_library().ssm_scan_kernel_name(batch, L, dim, N).decode()
 
 
 def scan_ckpt_size(batch, L, dim, N):

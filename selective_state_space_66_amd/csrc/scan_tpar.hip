@@ -86,8 +86,9 @@ __device__ __forceinline__ float lane_bcast(float v, int l) {
 // Pointers are separate __restrict__ arguments; y must not overlap any input,
 // and last_state none but h0 (read before the first chunk, written after the
 // last).
-// NF: N == 16, whose B and C rows are read as 16-byte vectors.  CKPT: also
-// write the state before every 16th token to ckpt (batch, ceil(L / 16), dim, N).
+// NF: N == 16 with 16-byte-aligned B and C, whose rows are read as 16-byte
+// vectors.  CKPT: also write the state before every 16th token to ckpt
+// (batch, ceil(L / 16), dim, N).
 template <typename IO, bool ZOH, bool GATE, bool NF, bool CKPT>
 __global__ __launch_bounds__(64 * kTW) void scan_tpar_kernel(
     const IO* __restrict__ u, const IO* __restrict__ dr, const float* __restrict__ Am,
@@ -293,14 +294,476 @@ __global__ __launch_bounds__(64 * kTW) void scan_tpar_kernel(
     last_state[(b * dim + c) * N + lane] = fast_l ? carry * ca_l : carry;
 }
 
+// ---------------------------------------------------------------------------
+// One wave per channel, four consecutive tokens per lane.
+//
+// For wide layers (many (batch, channel) rows) the time-parallel scan runs one
+// wave per row, so no carry crosses waves: a block owns kWW consecutive
+// channels of one batch entry, and each wave walks the sequence in chunks of
+// 256 tokens, lane l holding tokens 4l .. 4l + 3.  Per state:
+//   - the lane forms its four pairs and composes them in order (in-lane
+//     prefix: three combine steps);
+//   - the wave scans the 64 lane totals with DPP (pair_scan4), so the six
+//     scan levels are paid once per four tokens;
+//   - he = A_tot carry + B_tot is the state after the lane's last token, and
+//     a whole-wave shift by one lane (DPP wave_shr, lane 0 taking the carry)
+//     gives the state before its first token; each token's state is then one
+//     fma with its in-lane prefix, and lane 63's he is the next carry.
+// Each chunk's inputs are staged in LDS by the whole block: u, Delta (after
+// the softplus) and silu(z) as a (channel, token) tile read from global
+// memory in row segments of the block's channels (a lane reading its own
+// channel's four tokens would touch one cache line per element), and B and C
+// as fp32 in the order the lanes read them, so a lane's read of four states of
+// one of its tokens is one conflict-free 16-byte access.  Two barriers per
+// chunk: after staging, and after the chunk's last read.
+constexpr int kWW = 8;        // waves (channels) per block
+constexpr int kWT = 4;        // tokens per lane
+constexpr int kWC = 64 * kWT; // tokens per chunk
+
+// Slot swizzle of the staged B and C rows (16-byte slots, 4 banks each): the
+// writers of one lane slot l differ in the token offset i and the group pair
+// q / 2, and l ^ (4 i + 2 (q / 2)) puts them in 8 distinct bank groups.
+__device__ __forceinline__ int wave_swz(int i, int q) { return 4 * i + 2 * (q >> 1); }
+
+struct WaveSmem {
+  float4 b[kNMax / 4][kWT][64];  // [state group][token in lane][lane slot]
+  float4 c[kNMax / 4][kWT][64];
+  float2 xd[kWW][kWC];           // (x, Delta) per channel of the tile and token
+  float gz[kWW][kWC];            // silu(z)
+  float yt[kWW][kWC];            // y, stored by the block in row segments
+  // per wave (channel): A log2(e), the readout weight of the carry, and the
+  // carry itself, per state (read by all lanes as 16-byte broadcasts)
+  float4 a2[kWW][kNMax / 4];
+  float4 w1[kWW][kNMax / 4];
+  float4 carry[kWW][kNMax / 4];
+};
+
+// Arguments as for scan_tpar_kernel, plus ntiles = ceil(dim / kWW) channel
+// tiles per batch entry and vec_io: dim is a multiple of kWW and u, delta, z
+// are 16-byte aligned (the tile is read in row segments of 4 channels); NF
+// and CKPT likewise.  Four waves per SIMD (128 VGPRs) let two 8-wave blocks
+// share a CU.
+template <typename IO, bool ZOH, bool GATE, bool NF, bool CKPT>
+__global__ __launch_bounds__(64 * kWW, 4) void scan_wave_kernel(
+    const IO* __restrict__ u, const IO* __restrict__ dr, const float* __restrict__ Am,
+    const IO* __restrict__ Bm, const IO* __restrict__ Cm, const float* __restrict__ Dm,
+    const IO* __restrict__ zz, const float* __restrict__ bias_v, const float* h0,
+    const int32_t* __restrict__ seq_lens, const uint8_t* __restrict__ reset,
+    IO* __restrict__ y, float* last_state, float* __restrict__ ckpt, const int64_t L,
+    const int64_t dim, const int N, const int64_t ntiles, const int softplus, const int vec_io) {
+  __shared__ WaveSmem sm;
+
+  // XCD-aware order: each XCD gets a contiguous run of channel tiles, which
+  // share the 128-byte lines of u, Delta, z and y in its L2.
+  const int64_t nblk = (int64_t)gridDim.x, bid = blockIdx.x;
+  const int64_t logical = (nblk % 8 == 0) ? (bid % 8) * (nblk / 8) + bid / 8 : bid;
+  const int64_t b = logical / ntiles, tile = logical - b * ntiles;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t c0 = tile * kWW;             // first channel of the tile
+  const int64_t c = c0 + w;                  // this wave's channel
+  const bool cvalid = c < dim;               // wave-uniform; every wave stages and syncs
+  const int64_t cc = cvalid ? c : dim - 1;   // loads of a padding wave stay in bounds
+
+  // per-state constants, lane n holding state n's
+  const float a_l = lane < N ? Am[cc * N + lane] : 0.0f;
+  const bool fast_l = ZOH && fabsf(a_l) >= 0.5f;  // ZOH g form for this state
+  const float ca_l = fast_l ? 1.0f / a_l : 0.0f;
+  const uint64_t fast_mask = __ballot(fast_l);
+  const bool all_fast = ZOH && (~fast_mask & ((1ull << N) - 1)) == 0;  // uniform
+  const float dskip = Dm ? Dm[cc] : 0.0f;
+  // this wave's constants and carry (g units where fast) to LDS, lane n holding
+  // state n's; states past N are finite dummies (A = 0, carry 0), never read out
+  if (lane < kNMax) {
+    float hv = 0.0f;
+    if (h0 && lane < N) hv = h0[(b * dim + cc) * N + lane];
+    ((float*)sm.a2[w])[lane] = a_l * kLog2e;
+    ((float*)sm.w1[w])[lane] = fast_l ? ca_l : (ZOH ? 1.0f : 0.0f);
+    ((float*)sm.carry[w])[lane] = fast_l ? a_l * hv : hv;
+  }
+  const int64_t nck = (L + 15) / 16;  // checkpoints per sequence (CKPT)
+  int64_t Leff = L;
+  if (seq_lens) {
+    const int64_t sl = seq_lens[b];
+    Leff = sl < 0 ? 0 : (sl < L ? sl : L);
+  }
+  const int64_t row0 = b * L;
+
+  // ---- B and C staging: thread j stages token j / 2 of the chunk, states
+  // 8 (j % 2) .. + 7 (two groups of four): a wave reads 32 consecutive rows.
+  // Token t = 4 l + i of group q goes to slot l ^ swz(i, q) of row [q][i]; the
+  // XOR spreads the 8 writers of one l over distinct banks, and a reader's
+  // 64 lanes still cover the row's 64 slots.  Tokens past L are clamped to
+  // L - 1; padding tokens stage B = C = 0.
+  const int st_t = tid >> 1, st_h = tid & 1;
+  const int st_i = st_t & (kWT - 1), st_l = st_t / kWT;
+  // raw staging words: bf16 pairs (4 words) or fp32 values (8 words) per tensor
+  constexpr int SW = sizeof(IO) == 2 ? 4 : 8;
+  uint32_t sb[SW], sc[SW];
+  bool st_live = false;
+  auto stage_load = [&](int64_t t0) {
+    int64_t t = t0 + st_t;
+    st_live = t < Leff;
+    t = t < L ? t : L - 1;
+    if constexpr (NF) {
+      typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+#pragma unroll
+      for (int j = 0; j < SW / 4; ++j) {
+        const u32x4 vb = *(const u32x4*)(Bm + (row0 + t) * 16 + 8 * st_h + j * (16 / sizeof(IO)));
+        const u32x4 vc = *(const u32x4*)(Cm + (row0 + t) * 16 + 8 * st_h + j * (16 / sizeof(IO)));
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          sb[4 * j + k] = vb[k];
+          sc[4 * j + k] = vc[k];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < SW; ++j) {
+        sb[j] = 0u;
+        sc[j] = 0u;
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int n = 8 * st_h + j;
+        const int64_t e = (row0 + t) * N + (n < N ? n : N - 1);
+        uint32_t vb = 0u, vc = 0u;
+        if (n < N) {
+          if constexpr (sizeof(IO) == 2) {
+            vb = ((const uint16_t*)Bm)[e];
+            vc = ((const uint16_t*)Cm)[e];
+          } else {
+            vb = __float_as_uint(((const float*)Bm)[e]);
+            vc = __float_as_uint(((const float*)Cm)[e]);
+          }
+        }
+        if constexpr (sizeof(IO) == 2) {
+          sb[j / 2] |= vb << (16 * (j & 1));
+          sc[j / 2] |= vc << (16 * (j & 1));
+        } else {
+          sb[j] = vb;
+          sc[j] = vc;
+        }
+      }
+    }
+  };
+  // element j (0..7) of the staged words, as fp32; 0 for padding tokens
+  auto st_elem = [&](const uint32_t (&wv)[SW], int j) -> float {
+    float v;
+    if constexpr (sizeof(IO) == 2)
+      v = __uint_as_float((j & 1) ? (wv[j >> 1] & 0xffff0000u) : (wv[j >> 1] << 16));
+    else
+      v = __uint_as_float(wv[j]);
+    return st_live ? v : 0.0f;
+  };
+  auto stage_store = [&]() {
+#pragma unroll
+    for (int q2 = 0; q2 < 2; ++q2) {
+      const int q = 2 * st_h + q2;
+      const int slot = st_l ^ wave_swz(st_i, q);
+      sm.b[q][st_i][slot] = make_float4(st_elem(sb, 4 * q2), st_elem(sb, 4 * q2 + 1),
+                                        st_elem(sb, 4 * q2 + 2), st_elem(sb, 4 * q2 + 3));
+      sm.c[q][st_i][slot] = make_float4(st_elem(sc, 4 * q2), st_elem(sc, 4 * q2 + 1),
+                                        st_elem(sc, 4 * q2 + 2), st_elem(sc, 4 * q2 + 3));
+    }
+  };
+
+  // ---- the (channel, token) tile of u, raw Delta and z: thread j takes token
+  // j / 2 and channels 4 (j % 2) .. + 3 of the tile, one row segment per
+  // tensor (vec_io), else element by element with channels clamped to dim.
+  const int xt = tid >> 1, xh = tid & 1;
+  float xbias[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int64_t ch = c0 + 4 * xh + k;
+    xbias[k] = bias_v ? bias_v[ch < dim ? ch : dim - 1] : 0.0f;
+  }
+  constexpr int XW = sizeof(IO) == 2 ? 2 : 4;  // 32-bit words per 4 channels
+  uint32_t xu[XW], xr[XW], xz[XW];
+  bool x_live = false;
+  auto tile_load = [&](int64_t t0) {
+    int64_t t = t0 + xt;
+    x_live = t < Leff;
+    t = t < L ? t : L - 1;
+    const int64_t e0 = (row0 + t) * dim + c0 + 4 * xh;
+    if (vec_io) {
+      if constexpr (sizeof(IO) == 2) {
+        typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
+        const u32x2 a = *(const u32x2*)(u + e0), d = *(const u32x2*)(dr + e0);
+        xu[0] = a[0]; xu[1] = a[1]; xr[0] = d[0]; xr[1] = d[1];
+        if constexpr (GATE) {
+          const u32x2 g = *(const u32x2*)(zz + e0);
+          xz[0] = g[0]; xz[1] = g[1];
+        }
+      } else {
+        typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+        const u32x4 a = *(const u32x4*)(u + e0), d = *(const u32x4*)(dr + e0);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) { xu[k] = a[k]; xr[k] = d[k]; }
+        if constexpr (GATE) {
+          const u32x4 g = *(const u32x4*)(zz + e0);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) xz[k] = g[k];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < XW; ++k) { xu[k] = 0u; xr[k] = 0u; xz[k] = 0u; }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int64_t ch = c0 + 4 * xh + k;
+        const int64_t e = (row0 + t) * dim + (ch < dim ? ch : dim - 1);
+        uint32_t vu, vr, vz = 0u;
+        if constexpr (sizeof(IO) == 2) {
+          vu = ((const uint16_t*)u)[e];
+          vr = ((const uint16_t*)dr)[e];
+          if constexpr (GATE) vz = ((const uint16_t*)zz)[e];
+          xu[k / 2] |= vu << (16 * (k & 1));
+          xr[k / 2] |= vr << (16 * (k & 1));
+          xz[k / 2] |= vz << (16 * (k & 1));
+        } else {
+          vu = __float_as_uint(((const float*)u)[e]);
+          vr = __float_as_uint(((const float*)dr)[e]);
+          if constexpr (GATE) vz = __float_as_uint(((const float*)zz)[e]);
+          xu[k] = vu; xr[k] = vr; xz[k] = vz;
+        }
+      }
+    }
+  };
+  auto x_elem = [&](const uint32_t (&wv)[XW], int k) -> float {
+    if constexpr (sizeof(IO) == 2)
+      return __uint_as_float((k & 1) ? (wv[k >> 1] & 0xffff0000u) : (wv[k >> 1] << 16));
+    else
+      return __uint_as_float(wv[k]);
+  };
+  // Delta = softplus(raw + bias); padding tokens take x = Delta = 0, so their
+  // pair is the identity whatever their inputs hold
+  auto tile_store = [&]() {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float v = x_elem(xr, k) + xbias[k];
+      const float dlt = softplus ? softplus_f(v) : v;
+      const float xv = x_elem(xu, k);
+      sm.xd[4 * xh + k][xt] = x_live ? make_float2(xv, dlt) : make_float2(0.0f, 0.0f);
+      if constexpr (GATE) sm.gz[4 * xh + k][xt] = silu_f(x_elem(xz, k));
+    }
+  };
+
+  // y of the chunk: thread j stores token j / 2, channels 4 (j % 2) .. + 3 of
+  // the tile (one row segment with vec_io); tokens past L are not stored.
+  // Reads yt before the next chunk's barrier, which orders it before yt is
+  // written again.
+  auto y_store = [&](int64_t t0) {
+    const int64_t t = t0 + xt;
+    if (t >= L) return;
+    const int64_t e0 = (row0 + t) * dim + c0 + 4 * xh;
+    float v[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = sm.yt[4 * xh + k][xt];
+    if (vec_io) {
+      if constexpr (sizeof(IO) == 2) {
+        typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
+        u32x2 o;
+        o[0] = pack_bf16x2(v[0], v[1]);
+        o[1] = pack_bf16x2(v[2], v[3]);
+        *(u32x2*)(y + e0) = o;
+      } else {
+        *(float4*)(y + e0) = make_float4(v[0], v[1], v[2], v[3]);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (c0 + 4 * xh + k < dim) store_io(y + e0 + k, v[k]);
+    }
+  };
+
+  const int64_t nchunks = (L + kWC - 1) / kWC;
+  if (nchunks > 0) {
+    tile_load(0);
+    stage_load(0);
+  }
+
+  for (int64_t ck = 0; ck < nchunks; ++ck) {
+    const int64_t t0 = ck * kWC;
+    // staging (every wave finished reading the previous chunk before the
+    // barrier that ended it), then the next chunk's loads into the freed
+    // registers
+    tile_store();
+    stage_store();
+    if (ck + 1 < nchunks) {
+      tile_load(t0 + kWC);
+      stage_load(t0 + kWC);
+    }
+    lds_barrier();
+
+    const bool full = t0 + kWC <= Leff;  // every token of the chunk is real (uniform)
+    float x[kWT], dl[kWT], gz[kWT], acc[kWT];
+    bool live[kWT], rst[kWT];
+    {
+      const float4 v0 = *(const float4*)&sm.xd[w][kWT * lane];
+      const float4 v1 = *(const float4*)&sm.xd[w][kWT * lane + 2];
+      x[0] = v0.x; dl[0] = v0.y; x[1] = v0.z; dl[1] = v0.w;
+      x[2] = v1.x; dl[2] = v1.y; x[3] = v1.z; dl[3] = v1.w;
+      if constexpr (GATE) {
+        const float4 g = *(const float4*)&sm.gz[w][kWT * lane];
+        gz[0] = g.x; gz[1] = g.y; gz[2] = g.z; gz[3] = g.w;
+      } else {
+#pragma unroll
+        for (int i = 0; i < kWT; ++i) gz[i] = 1.0f;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kWT; ++i) {
+      live[i] = full || t0 + kWT * lane + i < Leff;
+      rst[i] = false;
+      acc[i] = 0.0f;
+    }
+    // document starts in this chunk (the same for every wave of the block)
+    bool any_rst = false;
+    if (reset) {
+#pragma unroll
+      for (int i = 0; i < kWT; ++i) {
+        const int64_t t = t0 + kWT * lane + i;
+        rst[i] = live[i] && reset[row0 + t] != 0;
+      }
+      any_rst = __ballot(rst[0] || rst[1] || rst[2] || rst[3]) != 0;
+    }
+    // the lane's first token starts a 16-token checkpoint group
+    const int64_t tl = t0 + kWT * lane;
+    const bool wck = CKPT && cvalid && (lane % 4 == 0) && tl < L;
+    float* ckp = ckpt + ((b * nck + (wck ? tl / 16 : 0)) * dim + cc) * N;
+
+    auto group = [&](auto form_tag, auto rst_tag, int q) {
+      constexpr int FORM = decltype(form_tag)::value;
+      constexpr bool RST = decltype(rst_tag)::value;
+      const float4 a24 = sm.a2[w][q], w14 = sm.w1[w][q], cin4 = sm.carry[w][q];
+      const float a2v[4] = {a24.x, a24.y, a24.z, a24.w};
+      const float w1v[4] = {w14.x, w14.y, w14.z, w14.w};
+      const float cinv[4] = {cin4.x, cin4.y, cin4.z, cin4.w};
+      float pa[kWT][4], pb[kWT][4];
+      float cv[kWT][4];
+#pragma unroll
+      for (int i = 0; i < kWT; ++i) {
+        const float4 bv4 = sm.b[q][i][lane ^ wave_swz(i, q)];
+        const float4 cv4 = sm.c[q][i][lane ^ wave_swz(i, q)];
+        const float bv[4] = {bv4.x, bv4.y, bv4.z, bv4.w};
+        cv[i][0] = cv4.x; cv[i][1] = cv4.y; cv[i][2] = cv4.z; cv[i][3] = cv4.w;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int n = 4 * q + k;
+          const float a = exp2_hw(dl[i] * a2v[k]);
+          float bu;
+          if (FORM == 0) {
+            bu = dl[i] * bv[k] * x[i];
+          } else if (FORM == 1 || ((fast_mask >> n) & 1)) {
+            const float wu = x[i] * bv[k];
+            bu = fmaf(a, wu, -wu);  // (abar - 1) u B, in g units
+          } else {
+            bu = dl[i] * bv[k] * zoh_phi(dl[i] * a2v[k] * kLn2, a) * x[i];
+          }
+          pa[i][k] = (RST && rst[i]) ? 0.0f : a;
+          pb[i][k] = bu;
+        }
+      }
+      // in-lane prefix: token i's pair becomes the composition of tokens 0..i
+#pragma unroll
+      for (int i = 1; i < kWT; ++i) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          pb[i][k] = fmaf(pa[i][k], pb[i - 1][k], pb[i][k]);
+          pa[i][k] *= pa[i - 1][k];
+        }
+      }
+      float ta[4] = {pa[kWT - 1][0], pa[kWT - 1][1], pa[kWT - 1][2], pa[kWT - 1][3]};
+      float tb[4] = {pb[kWT - 1][0], pb[kWT - 1][1], pb[kWT - 1][2], pb[kWT - 1][3]};
+      pair_scan4(ta, tb);
+      float he[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int n = 4 * q + k;
+        he[k] = fmaf(ta[k], cinv[k], tb[k]);  // after the lane's last token
+        const float hin = __int_as_float(__builtin_amdgcn_update_dpp(
+            __float_as_int(cinv[k]), __float_as_int(he[k]), 0x138 /* wave_shr:1 */, 0xf, 0xf, false));
+#pragma unroll
+        for (int i = 0; i < kWT; ++i) {
+          const float h = (i == kWT - 1) ? he[k] : fmaf(pa[i][k], hin, pb[i][k]);
+          acc[i] = fmaf(cv[i][k] * w1v[k] + (ZOH ? 0.0f : cv[i][k]), h, acc[i]);
+        }
+        if (CKPT && wck && (NF || n < N)) ckp[n] = ZOH ? hin * w1v[k] : hin;  // g / A where g is carried
+      }
+      // lane 63 holds the state after the chunk: the next chunk's carry
+      if (lane == 63) sm.carry[w][q] = make_float4(he[0], he[1], he[2], he[3]);
+    };
+    // one group of four states at a time (a rolled loop keeps one group's
+    // pairs live, not all sixteen states')
+    auto groups = [&](auto form_tag) {
+      const int ng = NF ? kNMax / 4 : (N + 3) / 4;
+      if (any_rst) {
+#pragma unroll 1
+        for (int q = 0; q < ng; ++q) group(form_tag, std::true_type(), q);
+      } else {
+#pragma unroll 1
+        for (int q = 0; q < ng; ++q) group(form_tag, std::false_type(), q);
+      }
+    };
+    if (!ZOH) groups(std::integral_constant<int, 0>());
+    else if (all_fast) groups(std::integral_constant<int, 1>());
+    else groups(std::integral_constant<int, 2>());
+
+    {
+      float yv[kWT];
+#pragma unroll
+      for (int i = 0; i < kWT; ++i) yv[i] = live[i] ? (acc[i] + dskip * x[i]) * gz[i] : 0.0f;
+      *(float4*)&sm.yt[w][kWT * lane] = make_float4(yv[0], yv[1], yv[2], yv[3]);
+    }
+    lds_barrier();  // the chunk's LDS is free for the next one, and y is staged
+    y_store(t0);
+  }
+
+  if (cvalid && last_state && lane < N) {
+    const float g = ((const float*)sm.carry[w])[lane];
+    last_state[(b * dim + c) * N + lane] = fast_l ? g * ca_l : g;
+  }
+}
+
+template <typename IO, bool ZOH, bool GATE>
+hipError_t wave_launch(const ScanParams& p, hipStream_t stream) {
+  const int64_t ntiles = (p.dim + kWW - 1) / kWW;
+  const int64_t nblk = ntiles * p.batch;
+  if (nblk > 0x7fffffff || kWC * p.dim >= 0x7fffffff) return hipErrorInvalidValue;  // 32-bit offsets
+  // the 16-state path reads B and C rows as 16-byte vectors
+  const bool vec = p.N == kNMax && (uintptr_t)p.B % 16 == 0 && (uintptr_t)p.C % 16 == 0;
+  auto kern = vec ? (p.ckpt ? scan_wave_kernel<IO, ZOH, GATE, true, true>
+                            : scan_wave_kernel<IO, ZOH, GATE, true, false>)
+                  : (p.ckpt ? scan_wave_kernel<IO, ZOH, GATE, false, true>
+                            : scan_wave_kernel<IO, ZOH, GATE, false, false>);
+  // the (channel, token) tile is read in row segments of 4 channels
+  const int vec_io = p.dim % kWW == 0 && (uintptr_t)p.u % 16 == 0 && (uintptr_t)p.delta % 16 == 0 &&
+                     (uintptr_t)p.z % 16 == 0;
+  hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(64 * kWW), 0, stream, (const IO*)p.u,
+                     (const IO*)p.delta, p.A, (const IO*)p.B, (const IO*)p.C, p.D,
+                     (const IO*)p.z, p.delta_bias, p.h0, p.seq_lens, p.reset, (IO*)p.y,
+                     p.last_state, p.ckpt, p.L, p.dim, (int)p.N, ntiles, p.softplus, vec_io);
+  return hipGetLastError();
+}
+
+template <typename IO>
+hipError_t wave_io(const ScanParams& p, bool zoh, bool gate, hipStream_t stream) {
+  if (zoh) return gate ? wave_launch<IO, true, true>(p, stream) : wave_launch<IO, true, false>(p, stream);
+  return gate ? wave_launch<IO, false, true>(p, stream) : wave_launch<IO, false, false>(p, stream);
+}
+
 template <typename IO, bool ZOH, bool GATE>
 hipError_t tpar_launch(const ScanParams& p, hipStream_t stream) {
   const int64_t nblk = p.batch * p.dim;
   if (nblk > 0x7fffffff || kTT * p.dim >= 0x7fffffff) return hipErrorInvalidValue;
-  auto kern = p.N == kNMax ? (p.ckpt ? scan_tpar_kernel<IO, ZOH, GATE, true, true>
-                                     : scan_tpar_kernel<IO, ZOH, GATE, true, false>)
-                           : (p.ckpt ? scan_tpar_kernel<IO, ZOH, GATE, false, true>
-                                     : scan_tpar_kernel<IO, ZOH, GATE, false, false>);
+  // the 16-state path reads B and C rows as 16-byte vectors
+  const bool vec = p.N == kNMax && (uintptr_t)p.B % 16 == 0 && (uintptr_t)p.C % 16 == 0;
+  auto kern = vec ? (p.ckpt ? scan_tpar_kernel<IO, ZOH, GATE, true, true>
+                            : scan_tpar_kernel<IO, ZOH, GATE, true, false>)
+                  : (p.ckpt ? scan_tpar_kernel<IO, ZOH, GATE, false, true>
+                            : scan_tpar_kernel<IO, ZOH, GATE, false, false>);
   hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(64 * kTW), 0, stream, (const IO*)p.u,
                      (const IO*)p.delta, p.A, (const IO*)p.B, (const IO*)p.C, p.D,
                      (const IO*)p.z, p.delta_bias, p.h0, p.seq_lens, p.reset, (IO*)p.y,
@@ -321,6 +784,13 @@ hipError_t launch_scan_tpar(const ScanParams& p, int io_dtype, bool zoh, bool ga
   if (p.N < 1 || p.N > kNMax) return hipErrorInvalidValue;
   if (io_dtype == 1) return tpar_io<bf16_bits>(p, zoh, gate, stream);
   return tpar_io<float>(p, zoh, gate, stream);
+}
+
+hipError_t launch_scan_wave(const ScanParams& p, int io_dtype, bool zoh, bool gate,
+                            hipStream_t stream) {
+  if (p.N < 1 || p.N > kNMax) return hipErrorInvalidValue;
+  if (io_dtype == 1) return wave_io<bf16_bits>(p, zoh, gate, stream);
+  return wave_io<float>(p, zoh, gate, stream);
 }
 
 }  // namespace ssm66

@@ -35,12 +35,22 @@ int check_common(int64_t batch, int64_t len, int64_t dim, int64_t dstate, int io
   return SSM_OK;
 }
 
-// Crossover of the time-parallel scan, measured on MI355X (bf16, N 16, ZOH,
-// gate): it is faster up to 4096 (batch x channel) rows (178 against 196 us at
-// 4 x 2048 x 1024, 181 against 196 us at 2 x 2048 x 2048; about even at 4608
-// rows, slower at 6144: 261 against 221 us) and from about 128 tokens.
-constexpr int64_t kTparMaxRows = 4096;
+// Kernel choice, from sweeps on MI355X (bf16, N 16, ZOH, gate):
+// - fewer than 1024 (batch x channel) rows and at least 128 tokens: the
+//   time-parallel kernel with four waves per row (88 against 153 us for one
+//   wave per row at 1 x 8192 x 256; slower from 1024 rows: 56 against 43 us
+//   at 1 x 2048 x 1024);
+// - sequences under 256 tokens: the sequential kernel (19 against 30 us at
+//   8 x 64 x 1536; 37 against 31 us at 8 x 256 x 1536);
+// - 32768 rows or more: the sequential kernel with 4 states per lane, whose
+//   2048 waves fill every SIMD twice (426 against 484 us at 8 x 2048 x 4096);
+// - everything between: the time-parallel kernel with one wave per row
+//   (205 against 235 us at 8 x 2048 x 1536, 3.5 against 6.9 ms at
+//   4 x 65536 x 2048, 370 against 415 us at 16 x 2048 x 1536).
+constexpr int64_t kTparMaxRows = 1023;
 constexpr int64_t kTparMinLen = 128;
+constexpr int64_t kWaveMinLen = 256;
+constexpr int64_t kSeqMinRows = 32768;
 
 // Scan kernel shape: G states per thread, NG state groups per channel
 // (G * NG >= dstate).  Up to 8 states one group shape covers them; for 9..16
@@ -62,18 +72,22 @@ void pick_scan_shape(int64_t batch, int64_t dim, int64_t dstate, int* G, int* NG
   *NG = 16 / g;
 }
 
-// Time-parallel scan (lanes hold tokens) or the sequential one.  The time-
-// parallel kernel spends about twice the arithmetic per update, so it only pays
-// where the sequential kernel leaves most of the GPU idle: few (batch, channel)
-// rows and a long sequence.  SSM66_SCAN_KERNEL = "tpar" forces it, "lds*" the
-// sequential one.
-bool use_time_parallel(int64_t batch, int64_t dim, int64_t L) {
-  if (256 * dim >= 0x7fffffff) return false;  // 32-bit lane offsets in a chunk
+// Which scan kernel runs (see the crossovers above).  SSM66_SCAN_KERNEL =
+// "tpar" forces the time-parallel kernel with four waves per row, "wave" the
+// one with one wave per row, "lds*" the sequential one.
+enum class ScanKernel { kSequential, kTpar, kWave };
+
+ScanKernel pick_scan_kernel(int64_t batch, int64_t dim, int64_t L, int64_t dstate) {
+  if (256 * dim >= 0x7fffffff || dstate > 16) return ScanKernel::kSequential;  // 32-bit lane offsets
   if (const char* e = getenv("SSM66_SCAN_KERNEL")) {
-    if (e[0] == 't') return true;
-    if (e[0] == 'l') return false;
+    if (e[0] == 't') return ScanKernel::kTpar;
+    if (e[0] == 'w') return ScanKernel::kWave;
+    if (e[0] == 'l') return ScanKernel::kSequential;
   }
-  return batch * dim <= kTparMaxRows && L >= kTparMinLen;
+  const int64_t rows = batch * dim;
+  if (rows <= kTparMaxRows) return L >= kTparMinLen ? ScanKernel::kTpar : ScanKernel::kSequential;
+  if (L < kWaveMinLen || rows >= kSeqMinRows) return ScanKernel::kSequential;
+  return ScanKernel::kWave;
 }
 
 }  // namespace
@@ -125,8 +139,13 @@ static int scan_fwd_impl(const void* u, const void* delta, const float* A, const
   p.y = y; p.last_state = last_state; p.ckpt = has_tokens ? ckpt : nullptr;
   p.batch = batch; p.L = seqlen; p.dim = dim; p.N = dstate; p.softplus = softplus;
   hipError_t e;
-  if (has_tokens && use_time_parallel(batch, dim, seqlen)) {
+  const ScanKernel kern =
+      has_tokens ? pick_scan_kernel(batch, dim, seqlen, dstate) : ScanKernel::kSequential;
+  if (kern == ScanKernel::kTpar) {
     e = ssm66::launch_scan_tpar(p, io_dtype, dt_mode == SSM_DT_ZOH, z != nullptr,
+                                (hipStream_t)stream);
+  } else if (kern == ScanKernel::kWave) {
+    e = ssm66::launch_scan_wave(p, io_dtype, dt_mode == SSM_DT_ZOH, z != nullptr,
                                 (hipStream_t)stream);
   } else {
     int G, NG;
@@ -144,6 +163,21 @@ int ssm_scan_fwd_ex(const void* u, const void* delta, const float* A, const void
                     int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype, void* stream) {
   return scan_fwd_impl(u, delta, A, B, C, D, z, delta_bias, softplus, dt_mode, h0, seq_lens, reset,
                        y, last_state, nullptr, batch, seqlen, dim, dstate, io_dtype, stream);
+}
+
+const char* ssm_scan_kernel_name(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate) {
+  if (check_common(batch, seqlen, dim, dstate, SSM_F32, 0, SSM_DT_ZOH) != SSM_OK) return "invalid shape";
+  if (batch == 0 || seqlen == 0 || dim == 0) return "none (no tokens)";
+  switch (pick_scan_kernel(batch, dim, seqlen, dstate)) {
+    case ScanKernel::kTpar: return "scan_tpar_kernel (time-parallel, four waves per row)";
+    case ScanKernel::kWave: return "scan_wave_kernel (time-parallel, one wave per row)";
+    default: break;
+  }
+  int G, NG;
+  pick_scan_shape(batch, dim, dstate, &G, &NG);
+  if (G == 4) return "scan_fwd_kernel (sequential, 4 states per lane)";
+  if (G == 2) return "scan_fwd_kernel (sequential, 2 states per lane)";
+  return "scan_fwd_kernel (sequential, 1 state per lane)";
 }
 
 size_t ssm_scan_ckpt_size(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate) {

@@ -89,6 +89,10 @@ hipError_t launch_scan_bwd(const ScanBwdParams& p, int io_dtype, bool zoh, bool 
 // The time-parallel scan (lanes hold tokens; associative pair scan).
 hipError_t launch_scan_tpar(const ScanParams& p, int io_dtype, bool zoh, bool gate,
                             hipStream_t stream);
+// The time-parallel scan with one wave per (batch, channel) row and four
+// consecutive tokens per lane (wide layers).
+hipError_t launch_scan_wave(const ScanParams& p, int io_dtype, bool zoh, bool gate,
+                            hipStream_t stream);
 hipError_t launch_ssd_fwd(const SSDParams& p, bool zoh, bool gate, hipStream_t stream);
 hipError_t launch_step(const StepParams& p, int io_dtype, bool zoh, bool gate, hipStream_t stream);
 

@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol(lib):
                           "ssm_scan_ckpt_size", "ssm_scan_bwd", "ssm_scan_bwd_ex",
                           "ssm_scan_bwd_workspace_size", "ssm_step", "ssm_ssd_fwd",
                           "ssm_conv1d_fwd", "ssm_conv1d_step", "ssm_status_string",
-                          "ssm_abi_version"}
+                          "ssm_abi_version", "ssm_scan_kernel_name"}
     raw = ctypes.CDLL(ssm.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), f"{n} not exported"
@@ -254,6 +254,30 @@ def test_ckpt_size(lib):
     assert f(2, 40, 70, 16) == (2 * 3 * 70 * 16 * 4 + 255) // 256 * 256  # states before 0, 16, 32
     assert f(1, 16, 8, 16) == 8 * 16 * 4 and f(1, 17, 8, 16) == 2 * 8 * 16 * 4
     assert f(-1, 4, 4, 4) == 0 and f(1, 4, 4, 17) == 0
+
+
+def test_scan_kernel_choice(lib, monkeypatch):
+    """The kernel the scan picks (host logic only): the crossovers measured on
+    MI355X, the environment override, and the degenerate sizes."""
+    monkeypatch.delenv("SSM66_SCAN_KERNEL", raising=False)
+    name = ssm.scan_kernel_name
+    assert name(8, 2048, 1536, 16).startswith("scan_wave_kernel")      # Mamba-130M layer
+    assert name(4, 65536, 2048, 16).startswith("scan_wave_kernel")     # long sequences
+    assert name(8, 2048, 1536, 8).startswith("scan_wave_kernel")       # fewer states
+    assert name(1, 2048, 1024, 16).startswith("scan_wave_kernel")      # 1024 rows
+    assert name(1, 8192, 1023, 16).startswith("scan_tpar_kernel")      # 1023 rows
+    assert name(1, 128, 256, 16).startswith("scan_tpar_kernel")
+    assert name(1, 127, 256, 16) == "scan_fwd_kernel (sequential, 1 state per lane)"
+    assert name(8, 255, 1536, 16) == "scan_fwd_kernel (sequential, 2 states per lane)"
+    assert name(8, 256, 1536, 16).startswith("scan_wave_kernel")
+    assert name(8, 2048, 4096, 16) == "scan_fwd_kernel (sequential, 4 states per lane)"
+    assert name(16, 2048, 2047, 16).startswith("scan_wave_kernel")     # 32752 rows
+    assert name(0, 16, 8, 16) == "none (no tokens)" and name(2, 0, 8, 16) == "none (no tokens)"
+    assert name(1, 4, 4, 17) == "invalid shape" and name(-1, 4, 4, 4) == "invalid shape"
+    for env, prefix in (("tpar", "scan_tpar_kernel"), ("wave", "scan_wave_kernel"),
+                        ("lds4", "scan_fwd_kernel (sequential, 4 states")):
+        monkeypatch.setenv("SSM66_SCAN_KERNEL", env)
+        assert name(8, 2048, 1536, 16).startswith(prefix), env
 
 
 ALIGN16 = ctypes.c_void_p(0x10000)

@@ -134,8 +134,9 @@ def test_long_sequence_fp32(mode):
     assert_close(to_host64(last), lr, "f32", "last_state")
 
 
-# sequential kernels with G = 1, 2, 4 states per thread, and the time-parallel one
-KERNELS = ["lds1", "lds2", "lds4", "tpar"]
+# sequential kernels with G = 1, 2, 4 states per thread, and the two
+# time-parallel ones (four waves per row; one wave per row, four tokens per lane)
+KERNELS = ["lds1", "lds2", "lds4", "tpar", "wave"]
 
 
 @pytest.mark.parametrize("kernel", KERNELS)
@@ -170,14 +171,16 @@ def test_each_kernel_short_sequences(kernel, L, monkeypatch):
     assert_close(to_host64(last), lr, "f32", "last_state")
 
 
+@pytest.mark.parametrize("kernel", ["tpar", "wave"])
 @pytest.mark.parametrize("N", [1, 5, 8, 16])
 @pytest.mark.parametrize("mode", ["zoh", "euler"])
-def test_time_parallel_state_sizes_and_chunks(N, mode, monkeypatch):
-    """The time-parallel kernel (lanes hold tokens, pairs combined by a wave
-    scan, waves through LDS, a carry between 256-token chunks): state sizes
-    below 16 (element loads), four chunks with a ragged last one, a zero and a
-    slow channel (the careful ZOH form beside the g form)."""
-    monkeypatch.setenv("SSM66_SCAN_KERNEL", "tpar")
+def test_time_parallel_state_sizes_and_chunks(kernel, N, mode, monkeypatch):
+    """The time-parallel kernels (lanes hold tokens, pairs combined by a wave
+    scan; across waves through LDS, or four tokens per lane composed in the
+    lane; a carry between 256-token chunks): state sizes below 16 (element
+    loads), several chunks with a ragged last one, a zero and a slow channel
+    (the careful ZOH form beside the g form)."""
+    monkeypatch.setenv("SSM66_SCAN_KERNEL", kernel)
     inp = W.scan_inputs(_cfg(2, 777, 5, N, "f32", True, seed=40 + N))
     A = inp["A"].copy()
     A[1, 0] = 0.0

@@ -192,7 +192,7 @@ def test_bwd_full_size_sampled():
 
 # ------------------------------------------------- the training forward's checkpoints
 
-@pytest.mark.parametrize("kernel", ["lds1", "lds2", "lds4", "tpar"])
+@pytest.mark.parametrize("kernel", ["lds1", "lds2", "lds4", "tpar", "wave"])
 @pytest.mark.parametrize("mode", ["zoh", "euler"])
 def test_train_forward_checkpoints(kernel, mode, monkeypatch):
     """scan_fwd_train gives scan_fwd's y and last_state bit for bit, and its
@@ -230,7 +230,7 @@ def test_train_forward_checkpoints(kernel, mode, monkeypatch):
         assert err.max() <= 1e-4, f"checkpoint {j}: {err.max():.2e}"
 
 
-@pytest.mark.parametrize("kernel", [None, "tpar"])
+@pytest.mark.parametrize("kernel", [None, "tpar", "wave"])
 @pytest.mark.parametrize("N", [3, 8])
 def test_train_forward_checkpoints_small_state(kernel, N, monkeypatch):
     """State sizes below 16 (padded state groups in the sequential kernel,
