@@ -320,14 +320,14 @@ constexpr int kWW = 8;        // waves (channels) per block
 constexpr int kWT = 4;        // tokens per lane
 constexpr int kWC = 64 * kWT; // tokens per chunk
 
-// Slot swizzle of the staged B and C rows (16-byte slots, 4 banks each): the
-// writers of one lane slot l differ in the token offset i and the group pair
-// q / 2, and l ^ (4 i + 2 (q / 2)) puts them in 8 distinct bank groups.
-__device__ __forceinline__ int wave_swz(int i, int q) { return 4 * i + 2 * (q >> 1); }
+// Staged B and C rows are padded by 2 slots (16 bytes, 4 banks each): the
+// writers of one lane slot differ in the token offset i, which then moves
+// them by 2 i bank groups, and a reader's address is a constant plus 16 lane.
+constexpr int kWRow = 64 + 2;
 
 struct WaveSmem {
-  float4 b[kNMax / 4][kWT][64];  // [state group][token in lane][lane slot]
-  float4 c[kNMax / 4][kWT][64];
+  float4 b[kNMax / 4][kWT][kWRow];  // [state group][token in lane][lane]
+  float4 c[kNMax / 4][kWT][kWRow];
   float2 xd[kWW][kWC];           // (x, Delta) per channel of the tile and token
   float gz[kWW][kWC];            // silu(z)
   float yt[kWW][kWC];            // y, stored by the block in row segments
@@ -392,10 +392,8 @@ __global__ __launch_bounds__(64 * kWW, 4) void scan_wave_kernel(
 
   // ---- B and C staging: thread j stages token j / 2 of the chunk, states
   // 8 (j % 2) .. + 7 (two groups of four): a wave reads 32 consecutive rows.
-  // Token t = 4 l + i of group q goes to slot l ^ swz(i, q) of row [q][i]; the
-  // XOR spreads the 8 writers of one l over distinct banks, and a reader's
-  // 64 lanes still cover the row's 64 slots.  Tokens past L are clamped to
-  // L - 1; padding tokens stage B = C = 0.
+  // Token t = 4 l + i of group q goes to slot l of row [q][i].  Tokens past L
+  // are clamped to L - 1; padding tokens stage B = C = 0.
   const int st_t = tid >> 1, st_h = tid & 1;
   const int st_i = st_t & (kWT - 1), st_l = st_t / kWT;
   // raw staging words: bf16 pairs (4 words) or fp32 values (8 words) per tensor
@@ -449,23 +447,25 @@ __global__ __launch_bounds__(64 * kWW, 4) void scan_wave_kernel(
     }
   };
   // element j (0..7) of the staged words, as fp32; 0 for padding tokens
-  auto st_elem = [&](const uint32_t (&wv)[SW], int j) -> float {
+  // (PAD: the chunk holds some)
+  auto st_elem = [&](auto pad_tag, const uint32_t (&wv)[SW], int j) -> float {
     float v;
     if constexpr (sizeof(IO) == 2)
       v = __uint_as_float((j & 1) ? (wv[j >> 1] & 0xffff0000u) : (wv[j >> 1] << 16));
     else
       v = __uint_as_float(wv[j]);
-    return st_live ? v : 0.0f;
+    if constexpr (decltype(pad_tag)::value) v = st_live ? v : 0.0f;
+    return v;
   };
-  auto stage_store = [&]() {
+  auto stage_store_as = [&](auto pad_tag) {
+    auto st_elem_p = [&](const uint32_t (&wv)[SW], int j) { return st_elem(pad_tag, wv, j); };
 #pragma unroll
     for (int q2 = 0; q2 < 2; ++q2) {
       const int q = 2 * st_h + q2;
-      const int slot = st_l ^ wave_swz(st_i, q);
-      sm.b[q][st_i][slot] = make_float4(st_elem(sb, 4 * q2), st_elem(sb, 4 * q2 + 1),
-                                        st_elem(sb, 4 * q2 + 2), st_elem(sb, 4 * q2 + 3));
-      sm.c[q][st_i][slot] = make_float4(st_elem(sc, 4 * q2), st_elem(sc, 4 * q2 + 1),
-                                        st_elem(sc, 4 * q2 + 2), st_elem(sc, 4 * q2 + 3));
+      sm.b[q][st_i][st_l] = make_float4(st_elem_p(sb, 4 * q2), st_elem_p(sb, 4 * q2 + 1),
+                                        st_elem_p(sb, 4 * q2 + 2), st_elem_p(sb, 4 * q2 + 3));
+      sm.c[q][st_i][st_l] = make_float4(st_elem_p(sc, 4 * q2), st_elem_p(sc, 4 * q2 + 1),
+                                        st_elem_p(sc, 4 * q2 + 2), st_elem_p(sc, 4 * q2 + 3));
     }
   };
 
@@ -538,14 +538,18 @@ __global__ __launch_bounds__(64 * kWW, 4) void scan_wave_kernel(
       return __uint_as_float(wv[k]);
   };
   // Delta = softplus(raw + bias); padding tokens take x = Delta = 0, so their
-  // pair is the identity whatever their inputs hold
-  auto tile_store = [&]() {
+  // pair is the identity whatever their inputs hold (PAD: the chunk holds some)
+  auto tile_store_as = [&](auto pad_tag) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const float v = x_elem(xr, k) + xbias[k];
-      const float dlt = softplus ? softplus_f(v) : v;
-      const float xv = x_elem(xu, k);
-      sm.xd[4 * xh + k][xt] = x_live ? make_float2(xv, dlt) : make_float2(0.0f, 0.0f);
+      float dlt = softplus ? softplus_f(v) : v;
+      float xv = x_elem(xu, k);
+      if constexpr (decltype(pad_tag)::value) {
+        dlt = x_live ? dlt : 0.0f;
+        xv = x_live ? xv : 0.0f;
+      }
+      sm.xd[4 * xh + k][xt] = make_float2(xv, dlt);
       if constexpr (GATE) sm.gz[4 * xh + k][xt] = silu_f(x_elem(xz, k));
     }
   };
@@ -589,8 +593,13 @@ __global__ __launch_bounds__(64 * kWW, 4) void scan_wave_kernel(
     // staging (every wave finished reading the previous chunk before the
     // barrier that ended it), then the next chunk's loads into the freed
     // registers
-    tile_store();
-    stage_store();
+    if (t0 + kWC <= Leff) {  // no padding token in the chunk (uniform)
+      tile_store_as(std::false_type());
+      stage_store_as(std::false_type());
+    } else {
+      tile_store_as(std::true_type());
+      stage_store_as(std::true_type());
+    }
     if (ck + 1 < nchunks) {
       tile_load(t0 + kWC);
       stage_load(t0 + kWC);
@@ -645,8 +654,8 @@ __global__ __launch_bounds__(64 * kWW, 4) void scan_wave_kernel(
       float cv[kWT][4];
 #pragma unroll
       for (int i = 0; i < kWT; ++i) {
-        const float4 bv4 = sm.b[q][i][lane ^ wave_swz(i, q)];
-        const float4 cv4 = sm.c[q][i][lane ^ wave_swz(i, q)];
+        const float4 bv4 = sm.b[q][i][lane];
+        const float4 cv4 = sm.c[q][i][lane];
         const float bv[4] = {bv4.x, bv4.y, bv4.z, bv4.w};
         cv[i][0] = cv4.x; cv[i][1] = cv4.y; cv[i][2] = cv4.z; cv[i][3] = cv4.w;
 #pragma unroll
