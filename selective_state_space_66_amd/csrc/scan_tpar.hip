@@ -340,7 +340,8 @@ struct WaveSmem {
 
 // Arguments as for scan_tpar_kernel, plus ntiles = ceil(dim / kWW) channel
 // tiles per batch entry and vec_io: dim is a multiple of kWW and u, delta, z
-// are 16-byte aligned (the tile is read in row segments of 4 channels); NF
+// and y are 16-byte aligned (tiles are read and y written in row segments of
+// 4 channels); NF
 // and CKPT likewise.  Four waves per SIMD (128 VGPRs) let two 8-wave blocks
 // share a CU.
 template <typename IO, bool ZOH, bool GATE, bool NF, bool CKPT>
@@ -747,9 +748,9 @@ hipError_t wave_launch(const ScanParams& p, hipStream_t stream) {
                             : scan_wave_kernel<IO, ZOH, GATE, true, false>)
                   : (p.ckpt ? scan_wave_kernel<IO, ZOH, GATE, false, true>
                             : scan_wave_kernel<IO, ZOH, GATE, false, false>);
-  // the (channel, token) tile is read in row segments of 4 channels
+  // the (channel, token) tiles are read and y written in row segments of 4 channels
   const int vec_io = p.dim % kWW == 0 && (uintptr_t)p.u % 16 == 0 && (uintptr_t)p.delta % 16 == 0 &&
-                     (uintptr_t)p.z % 16 == 0;
+                     (uintptr_t)p.z % 16 == 0 && (uintptr_t)p.y % 16 == 0;
   hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(64 * kWW), 0, stream, (const IO*)p.u,
                      (const IO*)p.delta, p.A, (const IO*)p.B, (const IO*)p.C, p.D,
                      (const IO*)p.z, p.delta_bias, p.h0, p.seq_lens, p.reset, (IO*)p.y,

@@ -160,6 +160,41 @@ def test_each_kernel_ragged(kernel, io, mode, gate, monkeypatch):
     assert_close(to_host64(last), lr, io, "last_state")
 
 
+def _offset_dev(x, io, off=1):
+    """A device tensor holding x that starts `off` elements past a 256-byte
+    aligned allocation: contiguous, aligned to its element size only."""
+    t = to_dev(x, io)
+    buf = torch.empty(t.numel() + off, dtype=t.dtype, device=t.device)
+    v = buf[off:].view(t.shape)
+    v.copy_(t)
+    assert v.data_ptr() % 16 != 0 and v.is_contiguous()
+    return v
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("which", ["all", "y"])
+def test_each_kernel_element_aligned_inputs(kernel, io, which, monkeypatch):
+    """Inputs and output (or y alone) one element past 16-byte alignment (the
+    C ABI asks only for element alignment): the kernels' vector loads and
+    stores are taken only for aligned rows, else element by element.
+    Dimensions keep the vector paths' other conditions (dim a multiple of 8,
+    N 16)."""
+    monkeypatch.setenv("SSM66_SCAN_KERNEL", kernel)
+    inp = W.scan_inputs(_cfg(2, 300, 48, 16, io, True, seed=19))
+    put = _offset_dev if which == "all" else to_dev
+    y = _offset_dev(np.zeros((2, 300, 48), dtype=np.uint16 if io == "bf16" else np.float32), io)
+    yo, last = ssm.scan_fwd(put(inp["u"], io), put(inp["delta"], io),
+                            to_dev(inp["A"], "f32"), put(inp["B"], io),
+                            put(inp["C"], io), D=to_dev(inp["D"], "f32"),
+                            z=put(inp["z"], io), delta_bias=to_dev(inp["delta_bias"], "f32"),
+                            dt_mode="zoh", y=y)
+    torch.cuda.synchronize()
+    yr, lr = scan_ref(inp, "zoh")
+    assert_close(to_host64(yo), yr, io, "y")
+    assert_close(to_host64(last), lr, io, "last_state")
+
+
 @pytest.mark.parametrize("kernel", KERNELS)
 @pytest.mark.parametrize("L", [0, 1, 3, 31, 32, 33, 65])
 def test_each_kernel_short_sequences(kernel, L, monkeypatch):
