@@ -130,9 +130,11 @@ def upload_scan(inp, dev):
 
 
 def time_scan(sets, steps, warmup, dt_mode, extras=None):
-    """Run warmup + timed steps rotating over the input sets.  Returns
-    (wall ms per step, mean per-launch kernel ms from HIP events).  `extras`
-    (h0, seq_lens, reset) selects the extended scan."""
+    """Run warmup steps, then `steps` timed by the wall clock (bracketed by
+    device synchronisations), then `steps` more with HIP events around each
+    launch, rotating over the input sets.  Returns (wall ms per step, mean
+    per-launch kernel ms from the events).  `extras` (h0, seq_lens, reset)
+    selects the extended scan."""
     import torch
     import selective_state_space_66_amd as ssm
     outs = [(torch.empty_like(s["u"]), torch.empty(s["u"].shape[0], s["u"].shape[2], s["A"].shape[1],
@@ -150,15 +152,20 @@ def time_scan(sets, steps, warmup, dt_mode, extras=None):
     for i in range(warmup):
         launch(i)
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
+    # wall time of `steps` back-to-back steps, nothing else on the stream
     t0 = time.perf_counter()
     for i in range(steps):
-        ev[i][0].record()
         launch(warmup + i)
-        ev[i][1].record()
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3 / steps
+    # then the same steps again with HIP events around each launch (kernel time)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record()
+        launch(warmup + steps + i)
+        ev[i][1].record()
+    torch.cuda.synchronize()
     kern = float(np.mean([a.elapsed_time(b) for a, b in ev]))
     return wall, kern
 
