@@ -77,6 +77,25 @@ __device__ __forceinline__ void pair_scan4(float (&a)[4], float (&b)[4]) {
                : "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]),
                  "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]));
 }
+
+// The same scan where only b is wanted afterwards: the last level updates b
+// alone (a is left at the previous level's values).  The trailing s_nop
+// gives a DPP read of b right after the block its two wait states.
+__device__ __forceinline__ void pair_scan4_b(float (&a)[4], float (&b)[4]) {
+  asm volatile("s_nop 1\n\t"
+               SSM66_STEP4("row_shr:1 row_mask:0xf")
+               SSM66_STEP4("row_shr:2 row_mask:0xf")
+               SSM66_STEP4("row_shr:4 row_mask:0xf")
+               SSM66_STEP4("row_shr:8 row_mask:0xf")
+               SSM66_STEP4("row_bcast:15 row_mask:0xa")
+               "v_fmac_f32_dpp %0, %0, %4 row_bcast:31 row_mask:0xc bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %1, %1, %5 row_bcast:31 row_mask:0xc bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %2, %2, %6 row_bcast:31 row_mask:0xc bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %3, %3, %7 row_bcast:31 row_mask:0xc bank_mask:0xf\n\t"
+               "s_nop 1"
+               : "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]),
+                 "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]));
+}
 #undef SSM66_STEP4
 
 __device__ __forceinline__ float lane_bcast(float v, int l) {
@@ -305,10 +324,12 @@ __global__ __launch_bounds__(64 * kTW) void scan_tpar_kernel(
 //     prefix: three combine steps);
 //   - the wave scans the 64 lane totals with DPP (pair_scan4), so the six
 //     scan levels are paid once per four tokens;
-//   - he = A_tot carry + B_tot is the state after the lane's last token, and
-//     a whole-wave shift by one lane (DPP wave_shr, lane 0 taking the carry)
-//     gives the state before its first token; each token's state is then one
-//     fma with its in-lane prefix, and lane 63's he is the next carry.
+//   - the carry enters through lane 0's total (b = A_tot carry + B_tot there;
+//     the other lanes read a zero carry), so after the scan each lane's b is
+//     the state after its last token, he; a whole-wave shift by one lane (DPP
+//     wave_shr, lane 0 keeping the carry) gives the state before its first
+//     token; each token's state is then one fma with its in-lane prefix, and
+//     lane 63's he is the next carry.
 // Each chunk's inputs are staged in LDS by the whole block: u, Delta (after
 // the softplus) and silu(z) as a (channel, token) tile read from global
 // memory in row segments of the block's channels (a lane reading its own
@@ -326,16 +347,17 @@ constexpr int kWC = 64 * kWT; // tokens per chunk
 constexpr int kWRow = 64 + 2;
 
 struct WaveSmem {
+  // per wave (channel) and group of four states: A log2(e), the readout
+  // weight, and the carry (g units where fast), as three float4.  Slot 0 is
+  // read by lane 0, slot 1 (the same constants, a zero carry) by the other
+  // lanes: one pointer per lane reaches all three with immediate offsets
+  // (first in the struct, so that the offsets fit the LDS instructions').
+  float4 kq[kWW][kNMax / 4][2][3];
   float4 b[kNMax / 4][kWT][kWRow];  // [state group][token in lane][lane]
   float4 c[kNMax / 4][kWT][kWRow];
   float2 xd[kWW][kWC];           // (x, Delta) per channel of the tile and token
   float gz[kWW][kWC];            // silu(z)
   float yt[kWW][kWC];            // y, stored by the block in row segments
-  // per wave (channel): A log2(e), the readout weight of the carry, and the
-  // carry itself, per state (read by all lanes as 16-byte broadcasts)
-  float4 a2[kWW][kNMax / 4];
-  float4 w1[kWW][kNMax / 4];
-  float4 carry[kWW][kNMax / 4];
 };
 
 // Arguments as for scan_tpar_kernel, plus ntiles = ceil(dim / kWW) channel
@@ -379,10 +401,15 @@ __global__ __launch_bounds__(64 * kWW, 4) void scan_wave_kernel(
   if (lane < kNMax) {
     float hv = 0.0f;
     if (h0 && lane < N) hv = h0[(b * dim + cc) * N + lane];
-    ((float*)sm.a2[w])[lane] = a_l * kLog2e;
-    ((float*)sm.w1[w])[lane] = fast_l ? ca_l : (ZOH ? 1.0f : 0.0f);
-    ((float*)sm.carry[w])[lane] = fast_l ? a_l * hv : hv;
+    float* s0 = (float*)&sm.kq[w][lane / 4][0][0] + (lane & 3);
+    float* s1 = (float*)&sm.kq[w][lane / 4][1][0] + (lane & 3);
+    const float a2 = a_l * kLog2e, w1 = fast_l ? ca_l : (ZOH ? 1.0f : 0.0f);
+    s0[0] = a2; s1[0] = a2;
+    s0[4] = w1; s1[4] = w1;
+    s0[8] = fast_l ? a_l * hv : hv;
+    s1[8] = 0.0f;
   }
+  const float4* kp = &sm.kq[w][0][lane == 0 ? 0 : 1][0];  // this lane's constants slot
   const int64_t nck = (L + 15) / 16;  // checkpoints per sequence (CKPT)
   int64_t Leff = L;
   if (seq_lens) {
@@ -647,7 +674,8 @@ __global__ __launch_bounds__(64 * kWW, 4) void scan_wave_kernel(
     auto group = [&](auto form_tag, auto rst_tag, int q) {
       constexpr int FORM = decltype(form_tag)::value;
       constexpr bool RST = decltype(rst_tag)::value;
-      const float4 a24 = sm.a2[w][q], w14 = sm.w1[w][q], cin4 = sm.carry[w][q];
+      const float4* kpq = kp + 6 * q;
+      const float4 a24 = kpq[0], w14 = kpq[1], cin4 = kpq[2];  // cin4: the carry in lane 0, else 0
       const float a2v[4] = {a24.x, a24.y, a24.z, a24.w};
       const float w1v[4] = {w14.x, w14.y, w14.z, w14.w};
       const float cinv[4] = {cin4.x, cin4.y, cin4.z, cin4.w};
@@ -686,13 +714,15 @@ __global__ __launch_bounds__(64 * kWW, 4) void scan_wave_kernel(
         }
       }
       float ta[4] = {pa[kWT - 1][0], pa[kWT - 1][1], pa[kWT - 1][2], pa[kWT - 1][3]};
-      float tb[4] = {pb[kWT - 1][0], pb[kWT - 1][1], pb[kWT - 1][2], pb[kWT - 1][3]};
-      pair_scan4(ta, tb);
+      float tb[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) tb[k] = fmaf(ta[k], cinv[k], pb[kWT - 1][k]);  // lane 0: the carry enters
+      pair_scan4_b(ta, tb);
       float he[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const int n = 4 * q + k;
-        he[k] = fmaf(ta[k], cinv[k], tb[k]);  // after the lane's last token
+        he[k] = tb[k];  // after the lane's last token
         const float hin = __int_as_float(__builtin_amdgcn_update_dpp(
             __float_as_int(cinv[k]), __float_as_int(he[k]), 0x138 /* wave_shr:1 */, 0xf, 0xf, false));
 #pragma unroll
@@ -703,7 +733,7 @@ __global__ __launch_bounds__(64 * kWW, 4) void scan_wave_kernel(
         if (CKPT && wck && (NF || n < N)) ckp[n] = ZOH ? hin * w1v[k] : hin;  // g / A where g is carried
       }
       // lane 63 holds the state after the chunk: the next chunk's carry
-      if (lane == 63) sm.carry[w][q] = make_float4(he[0], he[1], he[2], he[3]);
+      if (lane == 63) sm.kq[w][q][0][2] = make_float4(he[0], he[1], he[2], he[3]);
     };
     // one group of four states at a time (a rolled loop keeps one group's
     // pairs live, not all sixteen states')
@@ -732,7 +762,7 @@ __global__ __launch_bounds__(64 * kWW, 4) void scan_wave_kernel(
   }
 
   if (cvalid && last_state && lane < N) {
-    const float g = ((const float*)sm.carry[w])[lane];
+    const float g = ((const float*)&sm.kq[w][lane / 4][0][2])[lane & 3];
     last_state[(b * dim + c) * N + lane] = fast_l ? g * ca_l : g;
   }
 }
