@@ -433,11 +433,16 @@ __global__ __launch_bounds__(64 * kWW, 4) void scan_wave_kernel(
     st_live = t < Leff;
     t = t < L ? t : L - 1;
     if constexpr (NF) {
+      // the chunk's rows from a uniform base; this thread's byte offset in
+      // them (token t - t0, states 8 st_h ..) is the same every full chunk
       typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+      const char* bb = (const char*)(Bm + (row0 + t0) * 16);
+      const char* cb = (const char*)(Cm + (row0 + t0) * 16);
+      const uint32_t off = (uint32_t)((t - t0) * 16 + 8 * st_h) * (uint32_t)sizeof(IO);
 #pragma unroll
       for (int j = 0; j < SW / 4; ++j) {
-        const u32x4 vb = *(const u32x4*)(Bm + (row0 + t) * 16 + 8 * st_h + j * (16 / sizeof(IO)));
-        const u32x4 vc = *(const u32x4*)(Cm + (row0 + t) * 16 + 8 * st_h + j * (16 / sizeof(IO)));
+        const u32x4 vb = *(const u32x4*)(bb + off + 16 * j);
+        const u32x4 vc = *(const u32x4*)(cb + off + 16 * j);
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           sb[4 * j + k] = vb[k];
@@ -510,27 +515,38 @@ __global__ __launch_bounds__(64 * kWW, 4) void scan_wave_kernel(
   constexpr int XW = sizeof(IO) == 2 ? 2 : 4;  // 32-bit words per 4 channels
   uint32_t xu[XW], xr[XW], xz[XW];
   bool x_live = false;
+  // byte offset of this thread's row segment from the chunk's first element
+  // (c0 of token t0): token xt, channels 4 xh ..; the same every full chunk.
+  // The launch keeps 256 dim elements within 32 bits of bytes.
+  const uint32_t xoff = ((uint32_t)xt * (uint32_t)dim + 4u * (uint32_t)xh) * (uint32_t)sizeof(IO);
   auto tile_load = [&](int64_t t0) {
     int64_t t = t0 + xt;
     x_live = t < Leff;
     t = t < L ? t : L - 1;
     const int64_t e0 = (row0 + t) * dim + c0 + 4 * xh;
     if (vec_io) {
+      // uniform base, 32-bit per-thread byte offset (of the clamped token)
+      const int64_t cb0 = (row0 + t0) * dim + c0;
+      const uint32_t off =
+          ((uint32_t)(t - t0) * (uint32_t)dim + 4u * (uint32_t)xh) * (uint32_t)sizeof(IO);
+      const char* ub = (const char*)(u + cb0) + off;
+      const char* db = (const char*)(dr + cb0) + off;
+      const char* zb = (const char*)(zz + cb0) + off;
       if constexpr (sizeof(IO) == 2) {
         typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
-        const u32x2 a = *(const u32x2*)(u + e0), d = *(const u32x2*)(dr + e0);
+        const u32x2 a = *(const u32x2*)ub, d = *(const u32x2*)db;
         xu[0] = a[0]; xu[1] = a[1]; xr[0] = d[0]; xr[1] = d[1];
         if constexpr (GATE) {
-          const u32x2 g = *(const u32x2*)(zz + e0);
+          const u32x2 g = *(const u32x2*)zb;
           xz[0] = g[0]; xz[1] = g[1];
         }
       } else {
         typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
-        const u32x4 a = *(const u32x4*)(u + e0), d = *(const u32x4*)(dr + e0);
+        const u32x4 a = *(const u32x4*)ub, d = *(const u32x4*)db;
 #pragma unroll
         for (int k = 0; k < 4; ++k) { xu[k] = a[k]; xr[k] = d[k]; }
         if constexpr (GATE) {
-          const u32x4 g = *(const u32x4*)(zz + e0);
+          const u32x4 g = *(const u32x4*)zb;
 #pragma unroll
           for (int k = 0; k < 4; ++k) xz[k] = g[k];
         }
@@ -594,14 +610,15 @@ __global__ __launch_bounds__(64 * kWW, 4) void scan_wave_kernel(
 #pragma unroll
     for (int k = 0; k < 4; ++k) v[k] = sm.yt[4 * xh + k][xt];
     if (vec_io) {
+      char* yb = (char*)(y + (row0 + t0) * dim + c0) + xoff;  // uniform base + this thread's offset
       if constexpr (sizeof(IO) == 2) {
         typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
         u32x2 o;
         o[0] = pack_bf16x2(v[0], v[1]);
         o[1] = pack_bf16x2(v[2], v[3]);
-        *(u32x2*)(y + e0) = o;
+        *(u32x2*)yb = o;
       } else {
-        *(float4*)(y + e0) = make_float4(v[0], v[1], v[2], v[3]);
+        *(float4*)yb = make_float4(v[0], v[1], v[2], v[3]);
       }
     } else {
 #pragma unroll
@@ -771,7 +788,9 @@ template <typename IO, bool ZOH, bool GATE>
 hipError_t wave_launch(const ScanParams& p, hipStream_t stream) {
   const int64_t ntiles = (p.dim + kWW - 1) / kWW;
   const int64_t nblk = ntiles * p.batch;
-  if (nblk > 0x7fffffff || kWC * p.dim >= 0x7fffffff) return hipErrorInvalidValue;  // 32-bit offsets
+  // 32-bit offsets: lanes' element offsets, and the staging's byte offsets
+  // within a chunk of kWC tokens
+  if (nblk > 0x7fffffff || kWC * p.dim * (int64_t)sizeof(IO) >= 0xffffffffLL) return hipErrorInvalidValue;
   // the 16-state path reads B and C rows as 16-byte vectors
   const bool vec = p.N == kNMax && (uintptr_t)p.B % 16 == 0 && (uintptr_t)p.C % 16 == 0;
   auto kern = vec ? (p.ckpt ? scan_wave_kernel<IO, ZOH, GATE, true, true>

@@ -78,7 +78,8 @@ void pick_scan_shape(int64_t batch, int64_t dim, int64_t dstate, int* G, int* NG
 enum class ScanKernel { kSequential, kTpar, kWave };
 
 ScanKernel pick_scan_kernel(int64_t batch, int64_t dim, int64_t L, int64_t dstate) {
-  if (256 * dim >= 0x7fffffff || dstate > 16) return ScanKernel::kSequential;  // 32-bit lane offsets
+  // the time-parallel kernels address a 256-token chunk with 32-bit offsets
+  if (1024 * dim >= 0xffffffffLL || dstate > 16) return ScanKernel::kSequential;
   if (const char* e = getenv("SSM66_SCAN_KERNEL")) {
     if (e[0] == 't') return ScanKernel::kTpar;
     if (e[0] == 'w') return ScanKernel::kWave;
