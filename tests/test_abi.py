@@ -278,6 +278,12 @@ def test_scan_kernel_choice(lib, monkeypatch):
                         ("lds4", "scan_fwd_kernel (sequential, 4 states")):
         monkeypatch.setenv("SSM66_SCAN_KERNEL", env)
         assert name(8, 2048, 1536, 16).startswith(prefix), env
+    # the time-parallel kernels address a 256-token chunk of up to 4-byte
+    # elements with 32-bit offsets: wider layers take the sequential kernel
+    # even when one is forced
+    monkeypatch.setenv("SSM66_SCAN_KERNEL", "wave")
+    assert name(1, 2048, (1 << 22) - 1, 16).startswith("scan_wave_kernel")
+    assert name(1, 2048, 1 << 22, 16).startswith("scan_fwd_kernel")
 
 
 ALIGN16 = ctypes.c_void_p(0x10000)
