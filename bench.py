@@ -664,7 +664,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the scan shards by batch or channel with no communication; see DESIGN.md)",
+              "(the scan shards by batch or channel with no communication between GPUs)",
               file=sys.stderr)
         sys.exit(2)
 

@@ -23,7 +23,7 @@
  *   "Decoding with a constant-size cache": one step updates the state entrywise,
  *     reads it and gates it.
  *
- * Readings where the pages leave a step open (each is listed in the design doc):
+ * Readings where the pages leave a step open:
  *   - the bias is added once, inside the softplus; softplus may be switched off,
  *     in which case Delta = raw + bias as given;
  *   - A = 0 under ZOH takes the limit bbar = Delta * B;
