@@ -132,11 +132,12 @@ def upload_scan(inp, dev):
                 z=to_dev(inp["z"], io, dev), delta_bias=to_dev(inp["delta_bias"], "f32", dev))
 
 
-def time_scan(sets, steps, warmup, dt_mode, extras=None):
+def time_scan(sets, steps, warmup, dt_mode, extras=None, stats=False):
     """Run warmup steps, then `steps` timed by the wall clock (bracketed by
     device synchronisations), then `steps` more with HIP events around each
     launch, rotating over the input sets.  Returns (wall ms per step, mean
-    per-launch kernel ms from the events).  `extras` (h0, seq_lens, reset)
+    per-launch kernel ms from the events), and with `stats` also the median
+    and the minimum of the per-launch times.  `extras` (h0, seq_lens, reset)
     selects the extended scan."""
     import torch
     import selective_state_space_66_amd as ssm
@@ -169,7 +170,10 @@ def time_scan(sets, steps, warmup, dt_mode, extras=None):
         launch(warmup + steps + i)
         ev[i][1].record()
     torch.cuda.synchronize()
-    kern = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    times = [a.elapsed_time(b) for a, b in ev]
+    kern = float(np.mean(times))
+    if stats:
+        return wall, kern, float(np.median(times)), float(np.min(times))
     return wall, kern
 
 
@@ -276,11 +280,11 @@ def device_scan_inputs(cfg, dev):
 
 
 def time_layers(dev, steps, warmup):
-    """The scan forward (ZOH) on the two larger layers of the workload set: the
-    Mamba-1.4B-shaped layer (8 x 2048 x 4096, N 16, bf16, gate) and the
-    long-sequence selective-copying-like case (4 x 65536 x 2048, N 16, bf16, no
-    gate).  Each input set is far larger than the 256 MB Infinity Cache, so one
-    set is reused from launch to launch."""
+    """The scan forward on the two larger layers of the workload set, ZOH and
+    exponential-Euler: the Mamba-1.4B-shaped layer (8 x 2048 x 4096, N 16,
+    bf16, gate) and the long-sequence selective-copying-like case (4 x 65536 x
+    2048, N 16, bf16, no gate).  Each input set is far larger than the 256 MB
+    Infinity Cache, so one set is reused from launch to launch."""
     import torch
     import workloads as W
     import selective_state_space_66_amd as ssm
@@ -289,19 +293,28 @@ def time_layers(dev, steps, warmup):
         cfg = W.SCAN_CONFIGS[name]
         sets = [device_scan_inputs(cfg, dev)]
         torch.cuda.synchronize()
-        kern = time_scan(sets, nsteps, max(2, warmup // 5), "zoh")[1]
+        _, kern, kmed, kmin = time_scan(sets, nsteps, max(2, warmup // 5), "zoh", stats=True)
+        kern_e = time_scan(sets, nsteps, max(2, warmup // 5), "euler")[1]
         nbytes = scan_bytes(cfg.batch, cfg.L, cfg.dim, cfg.N, 2, cfg.gate)
         upd = cfg.batch * cfg.L * cfg.dim * cfg.N
         gbs = nbytes / (kern * 1e-3) / 1e9
         out[name] = {"workload": f"ssm_scan_fwd: batch {cfg.batch}, L {cfg.L}, D {cfg.dim}, N {cfg.N}, "
                                  f"bf16, {'gate' if cfg.gate else 'no gate'}, ZOH",
                      "kernel": ssm.scan_kernel_name(cfg.batch, cfg.L, cfg.dim, cfg.N),
-                     "launches": nsteps, "kernel_ms": round(kern, 5), "GB/s": round(gbs, 2),
+                     "launches": nsteps, "kernel_ms": round(kern, 5),
+                     "kernel_ms_median": round(kmed, 5), "kernel_ms_min": round(kmin, 5),
+                     "GB/s": round(gbs, 2),
                      "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
                      "elems_per_s": float(f"{cfg.batch * cfg.L * cfg.dim / (kern * 1e-3):.4g}"),
                      "updates_per_s": float(f"{upd / (kern * 1e-3):.4g}"),
                      "alu_frac": round(FLOPS_PER_UPDATE * upd / (kern * 1e-3) / 1e12 / ALU_PEAK_TFLOPS, 4),
-                     "algorithmic_bytes": nbytes}
+                     "algorithmic_bytes": nbytes,
+                     "euler": {"kernel_ms": round(kern_e, 5),
+                               "GB/s": round(nbytes / (kern_e * 1e-3) / 1e9, 2),
+                               "pct_hbm_peak": round(100.0 * nbytes / (kern_e * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+                               "updates_per_s": float(f"{upd / (kern_e * 1e-3):.4g}"),
+                               "alu_frac": round(FLOPS_PER_UPDATE * upd / (kern_e * 1e-3) / 1e12
+                                                 / ALU_PEAK_TFLOPS, 4)}}
         del sets
         torch.cuda.empty_cache()
     return out
@@ -692,7 +705,7 @@ def main():
     settle = settle_clock(sets)
     log(f"[bench] {settle} untimed launches while the clock settles")
     log(f"[bench] timing ZOH scan ({scan_kernel})")
-    wall_ms, kern_ms = time_scan(sets, args.steps, args.warmup, "zoh")
+    wall_ms, kern_ms, kern_med, kern_min = time_scan(sets, args.steps, args.warmup, "zoh", stats=True)
     log(f"[bench] zoh: wall {wall_ms:.4f} ms/step, kernel {kern_ms:.4f} ms")
     # the same scan with the sequential kernel forced, for comparison
     old_env = os.environ.get("SSM66_SCAN_KERNEL")
@@ -739,7 +752,8 @@ def main():
     log("[bench] timing the scan on the Mamba-1.4B and long-sequence layers")
     torch.cuda.empty_cache()
     layers = time_layers(dev, args.steps, args.warmup)
-    log("[bench] layers: " + ", ".join(f"{k} {v['kernel_ms']:.4f} ms ({v['GB/s']:.0f} GB/s)"
+    log("[bench] layers: " + ", ".join(f"{k} {v['kernel_ms']:.4f} ms ({v['GB/s']:.0f} GB/s), "
+                                       f"Euler {v['euler']['kernel_ms']:.4f} ms"
                                        for k, v in layers.items()))
     log("[bench] timing the scan on few, narrow rows")
     torch.cuda.empty_cache()
@@ -755,6 +769,9 @@ def main():
     d4_wall_s, d4_kern_ms = time_decode(dcfg, max(100, args.decode_steps // 5), dev, nstates=4)
     log("[bench] timing a plain device copy")
     copy_gbs = copy_bandwidth(dev)
+    for v in layers.values():
+        v["pct_copy_bw"] = round(100.0 * v["GB/s"] / copy_gbs, 2)
+        v["euler"]["pct_copy_bw"] = round(100.0 * v["euler"]["GB/s"] / copy_gbs, 2)
 
     cpu = None
     if not args.no_cpu:
@@ -803,7 +820,8 @@ def main():
         "roofline": {"bound": "alu", "achieved": round(tflops, 3), "peak": round(ALU_PEAK_TFLOPS, 2),
                      "unit": "TFLOP/s", "frac": round(tflops / ALU_PEAK_TFLOPS, 4),
                      "traffic": traffic, "kernel": scan_kernel + " (ZOH, bf16, gate)",
-                     "kernel_ms": round(kern_ms, 5),
+                     "kernel_ms": round(kern_ms, 5), "kernel_ms_median": round(kern_med, 5),
+                     "kernel_ms_min": round(kern_min, 5),
                      "per_launch": {"updates": updates, "flops": FLOPS_PER_UPDATE * updates,
                                     "algorithmic_bytes": nbytes},
                      "hbm": {"achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
