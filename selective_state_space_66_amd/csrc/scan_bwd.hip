@@ -58,32 +58,32 @@ struct BSmem {
   float chan[2][S::NG][S::CW];              // dD, d bias per (group, channel), at the end
 };
 
-// phi(k) = (e^k - 1)/k from a = e^k.  Below |k| = 1/2: 1 + k psi(k), psi a
-// degree-4 polynomial fitted to (phi(k) - 1)/k on [-1/2, 1/2] (Chebyshev
-// interpolation; phi within 3e-7 relative in fp32, and phi(0) = 1 exactly).
-// Above: the closed form (a - 1)/k, whose rounding error relative to phi is
-// about 2 ulp / |k|.
-__device__ __forceinline__ float phi_of(float k, float a) {
+// phi(k) = (e^k - 1)/k from a = e^k, and rk = 1/k (from 1/Delta and 1/A:
+// a product of two reciprocals instead of one per state).  Below |k| = 1/2:
+// 1 + k psi(k), psi a degree-4 polynomial fitted to (phi(k) - 1)/k on
+// [-1/2, 1/2] (Chebyshev interpolation; phi within 3e-7 relative in fp32, and
+// phi(0) = 1 exactly).  Above: the closed form (a - 1)/k, whose rounding
+// error relative to phi is about 2 ulp / |k|.
+__device__ __forceinline__ float phi_of(float k, float a, float rk) {
   float p = fmaf(0.0013966609258204699f, k, 0.008395552635192871f);
   p = fmaf(p, k, 0.041666179895401f);
   p = fmaf(p, k, 0.1666627675294876f);
   p = fmaf(p, k, 0.5f);
   p = fmaf(p, k, 1.0f);
-  const float pl = (a - 1.0f) * rcp_hw(k);  // 1 ulp; an IEEE division costs ~10 instructions
-  return fabsf(k) < 0.5f ? p : pl;
+  return fabsf(k) < 0.5f ? p : (a - 1.0f) * rk;
 }
 
-// phi'(k) given a = e^k and phi = phi(k).  Below |k| = 1/2: 1/2 + k chi(k),
-// chi a degree-4 polynomial fitted to (phi'(k) - 1/2)/k on [-1/2, 1/2]
-// (within 6e-7 relative in fp32, phi'(0) = 1/2 exactly).  Above: the closed
-// form (a - phi)/k.
-__device__ __forceinline__ float phi_prime(float k, float a, float phi) {
+// phi'(k) given a = e^k, phi = phi(k) and rk = 1/k.  Below |k| = 1/2:
+// 1/2 + k chi(k), chi a degree-4 polynomial fitted to (phi'(k) - 1/2)/k on
+// [-1/2, 1/2] (within 6e-7 relative in fp32, phi'(0) = 1/2 exactly).  Above:
+// the closed form (a - phi)/k.
+__device__ __forceinline__ float phi_prime(float k, float a, float phi, float rk) {
   float d = fmaf(0.001197385136038065f, k, 0.006998891942203045f);
   d = fmaf(d, k, 0.03333290293812752f);
   d = fmaf(d, k, 0.1249965950846672f);
   d = fmaf(d, k, 0.3333333432674408f);
   d = fmaf(d, k, 0.5f);
-  return fabsf(k) < 0.5f ? d : (a - phi) * rcp_hw(k);
+  return fabsf(k) < 0.5f ? d : (a - phi) * rk;
 }
 
 struct BwdArgs {
@@ -205,7 +205,9 @@ __global__ __launch_bounds__((BShape<G, NG>::THREADS)) void scan_bwd_kernel(cons
         // d softplus / dv = sigma(v)
         e_sv[i] = p.softplus ? rcp_hw(1.0f + exp2_hw(-v * kLog2e)) : 1.0f;
       }
-      sm.dd[r][cl] = make_float4(dl, x, ds, 0.0f);
+      // 1/Delta for the closed forms of phi and phi' (unused where Delta = 0:
+      // the polynomial branch is taken there)
+      sm.dd[r][cl] = make_float4(dl, x, ds, rcp_hw(dl));
     }
     const bool live = t0 + btt < L;
 #pragma unroll
@@ -244,7 +246,7 @@ __global__ __launch_bounds__((BShape<G, NG>::THREADS)) void scan_bwd_kernel(cons
             const float ub = d4.y * Bv;
             h[k] = fmaf(a, h[k] + ub, -ub);
           } else {
-            const float phi = ZOH ? phi_of(d4.x * Aa[k], a) : 1.0f;
+            const float phi = ZOH ? phi_of(d4.x * Aa[k], a, d4.w * CA[k]) : 1.0f;
             update_state(h[k], a, phi, d4.x, d4.y, Bv);
           }
         }
@@ -323,7 +325,7 @@ __global__ __launch_bounds__((BShape<G, NG>::THREADS)) void scan_bwd_kernel(cons
 #pragma unroll
           for (int k = 0; k < G; ++k) {
             const float a = exp2_hw(d4.x * Ap[k]);
-            const float phi = ZOH ? phi_of(d4.x * Aa[k], a) : 1.0f;
+            const float phi = ZOH ? phi_of(d4.x * Aa[k], a, d4.w * CA[k]) : 1.0f;
             update_state(h[k], a, phi, d4.x, d4.y, sm.bc[t][g][k]);
             hs[t][k] = h[k];
             as[t][k] = a;
@@ -364,7 +366,8 @@ __global__ __launch_bounds__((BShape<G, NG>::THREADS)) void scan_bwd_kernel(cons
           const int t = half * HALF + tt;
           if (FULL || t < nt) {
             const float4 d4 = sm.dd[t][cl];
-            const float dl = d4.x, x = d4.y, ds = d4.z;
+            const float dl = d4.x, x = d4.y, ds = d4.z, rdl = d4.w;
+            const float xdl = x * dl;
             float ddt = 0.0f, dx = 0.0f;
 #pragma unroll
             for (int k = 0; k < G; ++k) {
@@ -379,19 +382,19 @@ __global__ __launch_bounds__((BShape<G, NG>::THREADS)) void scan_bwd_kernel(cons
               const float xB = x * Bv;
               if constexpr (ZOH) {
                 const float phi = ps[t][k];
-                const float dphi = phi_prime(dl * Aa[k], a, phi);
+                const float dphi = phi_prime(dl * Aa[k], a, phi, rdl * CA[k]);
                 // dDelta: q (h_{t-1} A + u B) abar (d bbar/dDelta = abar B);
                 // dA: q (h_{t-1} Delta abar + u B Delta^2 phi'); dB: q u Delta
                 // phi; du: q Delta B phi
                 ddt = fmaf(qa, fmaf(hp, Aa[k], xB), ddt);
                 dA[k] = fmaf(dl, fmaf(q * xB * dl, dphi, qa * hp), dA[k]);
                 const float qp = q * phi;
-                sm.red[0][tt][n0 + k][cl] = qp * x * dl;
+                sm.red[0][tt][n0 + k][cl] = qp * xdl;
                 dx = fmaf(qp, dl * Bv, dx);
               } else {
                 ddt = fmaf(qa * hp, Aa[k], fmaf(q, xB, ddt));
                 dA[k] = fmaf(qa * hp, dl, dA[k]);
-                sm.red[0][tt][n0 + k][cl] = q * x * dl;
+                sm.red[0][tt][n0 + k][cl] = q * xdl;
                 dx = fmaf(q * dl, Bv, dx);
               }
               sm.red[1][tt][n0 + k][cl] = ds * hs[t][k];
