@@ -704,13 +704,14 @@ __global__ __launch_bounds__(64 * kWW, 4) void scan_wave_kernel(
         const float4 cv4 = sm.c[q][i][lane];
         const float bv[4] = {bv4.x, bv4.y, bv4.z, bv4.w};
         cv[i][0] = cv4.x; cv[i][1] = cv4.y; cv[i][2] = cv4.z; cv[i][3] = cv4.w;
+        const float dx = FORM == 0 ? dl[i] * x[i] : 0.0f;  // Euler: Delta u, once per token
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           const int n = 4 * q + k;
           const float a = exp2_hw(dl[i] * a2v[k]);
           float bu;
           if (FORM == 0) {
-            bu = dl[i] * bv[k] * x[i];
+            bu = dx * bv[k];
           } else if (FORM == 1 || ((fast_mask >> n) & 1)) {
             const float wu = x[i] * bv[k];
             bu = fmaf(a, wu, -wu);  // (abar - 1) u B, in g units
@@ -745,7 +746,7 @@ __global__ __launch_bounds__(64 * kWW, 4) void scan_wave_kernel(
 #pragma unroll
         for (int i = 0; i < kWT; ++i) {
           const float h = (i == kWT - 1) ? he[k] : fmaf(pa[i][k], hin, pb[i][k]);
-          acc[i] = fmaf(cv[i][k] * w1v[k] + (ZOH ? 0.0f : cv[i][k]), h, acc[i]);
+          acc[i] = fmaf(ZOH ? cv[i][k] * w1v[k] : cv[i][k], h, acc[i]);  // Euler reads out h itself
         }
         if (CKPT && wck && (NF || n < N)) ckp[n] = ZOH ? hin * w1v[k] : hin;  // g / A where g is carried
       }
