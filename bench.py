@@ -48,14 +48,18 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 # ALU roofline of the scan.  Per state update the method does 2 multiplies and
 # 2 FMAs (6 flops: Delta A, (Delta u) B, the state FMA, the readout FMA) and one
-# exponential.  MI355X issues 256 CU x 4 SIMD x 16 lanes x 2.4 GHz = 39.3e12
-# non-packed fp32 lane instructions per second (packed fp32 is not used), and
-# v_exp_f32 takes two issue slots (half rate): 4 + 2 = 6 slots for 6 flops, so
-# the mix peaks at 39.3 TFLOP/s, i.e. 6.55e12 state updates per second.
+# exponential.  MI355X has 256 CUs of 4 SIMDs x 16 fp32 lanes at 2.4 GHz:
+# 39.3e12 fp32 lane-instructions per second, i.e. 78.6 TFLOP/s counting an FMA
+# as 2 flops.  The published 157.3 TFLOP/s needs packed fp32 (two FMAs per
+# lane-instruction), which this build turns off, so the roofline's peak is 78.6.
 VALU_LANE_OPS = 256 * 4 * 16 * 2.4e9
+FP32_TFLOPS = 2 * VALU_LANE_OPS / 1e12
+FP32_PUBLISHED_TFLOPS = 157.3
 FLOPS_PER_UPDATE = 6
-SLOTS_PER_UPDATE = 6
-ALU_PEAK_TFLOPS = VALU_LANE_OPS / SLOTS_PER_UPDATE * FLOPS_PER_UPDATE / 1e12
+# The fewest VALU instructions a state update needs besides its exponential:
+# Euler: Delta*A', (Delta u)*B, the state FMA, the readout FMA; ZOH adds the
+# (abar - 1) factor (an FMA) and the 1/A weight (a multiply) of the input term.
+VALU_PER_UPDATE = {"zoh": 6, "euler": 4}
 METRIC = "selective-scan fwd achieved HBM GB/s (% of peak) and B·L·D elems/s; decode tok/s"
 
 
@@ -77,6 +81,57 @@ def step_bytes(b, D, N, io_bytes, gate):
     delta, [z] read and y written (b D), B, C (b N), A (D N), D and bias (D)."""
     streamed = 3 if gate else 2
     return 8 * b * D * N + (streamed + 1) * b * D * io_bytes + 2 * b * N * io_bytes + 4 * D * N + 8 * D
+
+
+def alu_rates(dev, blocks=2048, iters=4096, reps=7):
+    """Measured issue rates of the chip (the library's probe kernels): fp32 FMA
+    and v_exp_f32 lane-operations per second, and the issue slots one
+    exponential takes inside a stream of FMAs (8 exponentials and 32 FMAs per
+    iteration, against the FMA-only rate).  blocks x 256 lanes fill every
+    SIMD with 8 waves; each probe is timed with HIP events on torch's current
+    stream (where the library launches), median of `reps` launches."""
+    import torch
+    import selective_state_space_66_amd as ssm
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    lanes = blocks * 256
+    ms = {}
+    for op in ("fma", "exp", "mix"):
+        ssm.alu_probe(op, sink, blocks, iters)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        for a, b in ev:
+            a.record()
+            ssm.alu_probe(op, sink, blocks, iters)
+            b.record()
+        torch.cuda.synchronize()
+        ms[op] = float(np.median([a.elapsed_time(b) for a, b in ev]))
+    n = lanes * iters
+    fma = 8 * n / (ms["fma"] * 1e-3)
+    exp = 8 * n / (ms["exp"] * 1e-3)
+    exp_slots = (ms["mix"] * 1e-3 * fma / n - 32) / 8
+    return {"fma_lane_ops_per_s": float(f"{fma:.4g}"), "exp_lane_ops_per_s": float(f"{exp:.4g}"),
+            "exp_slots_in_fma_stream": round(exp_slots, 3),
+            "fma_frac_of_nominal": round(fma / VALU_LANE_OPS, 4),
+            "probe_ms": {k: round(v, 4) for k, v in ms.items()},
+            "probe": f"{blocks} blocks x 256 lanes x {iters} iterations of 8 FMAs, 8 exponentials, "
+                     "or 8 x (exponential + 4 FMAs); 8 independent chains per lane"}
+
+
+def alu_figures(updates, ms, mode, rates):
+    """The scan's compute position: the method's flops per second against the
+    fp32 FMA peak (and the published packed-fp32 peak), and the kernel time
+    against the measured ALU floor -- the fewest VALU instructions per update
+    plus one exponential at its measured cost, issued at the measured FMA rate."""
+    tflops = FLOPS_PER_UPDATE * updates / (ms * 1e-3) / 1e12
+    out = {"TFLOPs": round(tflops, 3), "frac_fp32": round(tflops / FP32_TFLOPS, 4),
+           "frac_published_fp32": round(tflops / FP32_PUBLISHED_TFLOPS, 4)}
+    if rates:
+        slots = VALU_PER_UPDATE[mode] + rates["exp_slots_in_fma_stream"]
+        floor_ms = updates * slots / rates["fma_lane_ops_per_s"] * 1e3
+        out["floor"] = {"slots_per_update": round(slots, 3), "floor_ms": round(floor_ms, 5),
+                        "frac": round(floor_ms / ms, 4)}
+    return out
 
 
 # The sources each measured kernel is built from: its own file, plus the shared
@@ -132,7 +187,7 @@ def upload_scan(inp, dev):
                 z=to_dev(inp["z"], io, dev), delta_bias=to_dev(inp["delta_bias"], "f32", dev))
 
 
-def time_scan(sets, steps, warmup, dt_mode, extras=None, stats=False):
+def time_scan(sets, steps, warmup, dt_mode, extras=None, stats=False, kernel=None):
     """Run warmup steps, then `steps` timed by the wall clock (bracketed by
     device synchronisations), then `steps` more with HIP events around each
     launch, rotating over the input sets.  Returns (wall ms per step, mean
@@ -151,7 +206,7 @@ def time_scan(sets, steps, warmup, dt_mode, extras=None, stats=False):
         y, last = outs[i % len(sets)]
         ssm.scan_fwd(s["u"], s["delta"], s["A"], s["B"], s["C"], D=s["D"], z=s["z"],
                      delta_bias=s["delta_bias"], softplus=True, dt_mode=dt_mode, y=y,
-                     last_state=last, **ex)
+                     last_state=last, kernel=kernel, **ex)
 
     for i in range(warmup):
         launch(i)
@@ -203,7 +258,7 @@ def settle_clock(sets, ms=100.0):
     return n
 
 
-def time_narrow(dev, steps, warmup):
+def time_narrow(dev, steps, warmup, rates=None):
     """The scan where (batch x channel) rows are few, so the sequential kernel
     leaves most of the GPU idle: the pages' speed-benchmark shape (batch 1,
     L 2048, D 1024, N 16), the Mamba-130M layer at batch 1 (1 x 2048 x 1536)
@@ -219,80 +274,36 @@ def time_narrow(dev, steps, warmup):
         cfg = W.ScanConfig(name, b, L, D, 16, "bf16", True, 7)
         sets = [upload_scan(W.scan_inputs(cfg), dev)]
         res = {}
-        old = os.environ.get("SSM66_SCAN_KERNEL")
-        for label, env in (("auto", None), ("sequential", "lds1")):
-            if env is None:
-                os.environ.pop("SSM66_SCAN_KERNEL", None)
-            else:
-                os.environ["SSM66_SCAN_KERNEL"] = env
-            res[label] = time_scan(sets, steps, warmup, "zoh")[1]
-        if old is None:
-            os.environ.pop("SSM66_SCAN_KERNEL", None)
-        else:
-            os.environ["SSM66_SCAN_KERNEL"] = old
+        for label, kern in (("auto", None), ("sequential", "seq1")):
+            res[label] = time_scan(sets, steps, warmup, "zoh", kernel=kern)[1]
         upd = b * L * D * 16
         out[name] = {"workload": f"ssm_scan_fwd: batch {b}, L {L}, D {D}, N 16, bf16, gate, ZOH",
                      "kernel": ssm.scan_kernel_name(b, L, D, 16),
                      "kernel_ms": round(res["auto"], 5),
                      "sequential_kernel_ms": round(res["sequential"], 5),
                      "speedup": round(res["sequential"] / res["auto"], 2),
-                     "alu_frac": round(FLOPS_PER_UPDATE * upd / (res["auto"] * 1e-3) / 1e12
-                                       / ALU_PEAK_TFLOPS, 4)}
+                     "alu": alu_figures(upd, res["auto"], "zoh", rates)}
         del sets
     return out
 
 
-def device_scan_inputs(cfg, dev):
-    """Timing inputs for a large scan workload, drawn on the device.
-
-    The (batch, L, D) tensors (u, raw delta, z) are N(0, 1) draws from torch's
-    seeded device generator, rounded to bf16; A, D, the dt bias, B, C, the
-    long-sequence filler vector and its 16 fresh positions per sequence follow
-    the workload recipe exactly.  The big tensors' values differ from the
-    parity tests' draws of the same recipe (generating those on the host takes
-    minutes at these sizes); the kernels' timing depends on the values only
-    through A, which picks the ZOH form."""
-    import torch
-    import workloads as W
-    b, L, dim, N = cfg.batch, cfg.L, cfg.dim, cfg.N
-    gen = torch.Generator(device=dev)
-    gen.manual_seed(cfg.seed)
-
-    def big():
-        return torch.randn((b, L, dim), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
-
-    A, D, bias = W.channel_params(cfg.seed, dim, N)
-    bc_idx = np.arange(b * L * N, dtype=np.int64).reshape(b, L, N)
-    if cfg.filler:
-        filler = torch.from_numpy(W.normal(cfg.seed, W.S_U, np.arange(dim))).to(dev)
-        u = filler.to(torch.bfloat16).expand(b, L, dim).contiguous()
-        pos = W.filler_positions(cfg.seed, b, L)
-        for bi in range(b):
-            for p in pos[bi]:
-                u[bi, int(p)] = torch.randn(dim, generator=gen, device=dev).to(torch.bfloat16)
-    else:
-        u = big()
-    return dict(u=u, delta=big(), A=to_dev(A, "f32", dev),
-                B=to_dev(W.to_bf16_bits(W.normal(cfg.seed, W.S_B, bc_idx)), "bf16", dev),
-                C=to_dev(W.to_bf16_bits(W.normal(cfg.seed, W.S_C, bc_idx)), "bf16", dev),
-                D=to_dev(D, "f32", dev), z=big() if cfg.gate else None,
-                delta_bias=to_dev(bias, "f32", dev))
-
-
-def time_layers(dev, steps, warmup):
+def time_layers(dev, steps, warmup, rates=None):
     """The scan forward on the two larger layers of the workload set, ZOH and
     exponential-Euler: the Mamba-1.4B-shaped layer (8 x 2048 x 4096, N 16,
     bf16, gate) and the long-sequence selective-copying-like case (4 x 65536 x
-    2048, N 16, bf16, no gate).  Each input set is far larger than the 256 MB
-    Infinity Cache, so one set is reused from launch to launch."""
+    2048, N 16, bf16, no gate), on the seeded inputs the parity tests check.
+    Each input set is far larger than the 256 MB Infinity Cache, so one set is
+    reused from launch to launch."""
     import torch
     import workloads as W
     import selective_state_space_66_amd as ssm
     out = {}
-    for name, nsteps in (("mamba1p4b", steps), ("longseq", max(3, steps // 5))):
+    for name, nsteps in (("mamba1p4b", steps), ("longseq", max(10, steps // 4))):
         cfg = W.SCAN_CONFIGS[name]
-        sets = [device_scan_inputs(cfg, dev)]
+        t0 = time.perf_counter()
+        sets = [upload_scan(W.scan_inputs(cfg), dev)]
         torch.cuda.synchronize()
+        log(f"[bench] {name}: inputs generated and uploaded in {time.perf_counter() - t0:.1f} s")
         _, kern, kmed, kmin = time_scan(sets, nsteps, max(2, warmup // 5), "zoh", stats=True)
         kern_e = time_scan(sets, nsteps, max(2, warmup // 5), "euler")[1]
         nbytes = scan_bytes(cfg.batch, cfg.L, cfg.dim, cfg.N, 2, cfg.gate)
@@ -307,16 +318,32 @@ def time_layers(dev, steps, warmup):
                      "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
                      "elems_per_s": float(f"{cfg.batch * cfg.L * cfg.dim / (kern * 1e-3):.4g}"),
                      "updates_per_s": float(f"{upd / (kern * 1e-3):.4g}"),
-                     "alu_frac": round(FLOPS_PER_UPDATE * upd / (kern * 1e-3) / 1e12 / ALU_PEAK_TFLOPS, 4),
+                     "alu": alu_figures(upd, kern, "zoh", rates),
                      "algorithmic_bytes": nbytes,
                      "euler": {"kernel_ms": round(kern_e, 5),
                                "GB/s": round(nbytes / (kern_e * 1e-3) / 1e9, 2),
                                "pct_hbm_peak": round(100.0 * nbytes / (kern_e * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
                                "updates_per_s": float(f"{upd / (kern_e * 1e-3):.4g}"),
-                               "alu_frac": round(FLOPS_PER_UPDATE * upd / (kern_e * 1e-3) / 1e12
-                                                 / ALU_PEAK_TFLOPS, 4)}}
+                               "alu": alu_figures(upd, kern_e, "euler", rates)}}
         del sets
         torch.cuda.empty_cache()
+    return out
+
+
+def time_tiny(dev, steps=200):
+    """The tiny fp32 workload (batch 1, L 256, D 64, N 16, no gate): launch-bound
+    on the GPU; timed per launch with events, both rules."""
+    import torch
+    import workloads as W
+    import selective_state_space_66_amd as ssm
+    cfg = W.SCAN_CONFIGS["tiny"]
+    inp = W.scan_inputs(cfg)
+    s = upload_scan(inp, dev)
+    out = {"workload": "ssm_scan_fwd: batch 1, L 256, D 64, N 16, fp32 io, no gate, D skip, "
+                       "softplus(delta + bias)",
+           "kernel": ssm.scan_kernel_name(cfg.batch, cfg.L, cfg.dim, cfg.N)}
+    for mode in ("zoh", "euler"):
+        out[mode] = {"kernel_us": round(time_scan([s], steps, 20, mode)[1] * 1e3, 2)}
     return out
 
 
@@ -587,16 +614,107 @@ def copy_bandwidth(dev, nbytes=256 << 20, reps=20):
     return 2 * nbytes / (ms * 1e-3) / 1e9
 
 
-def cpu_baseline(cfg, inp, threads):
-    """The fp64 oracle, as it stands, on the same workload on the host cores."""
+def host_facts():
+    """The host the oracle runs on: CPU model, CPUs online, CPUs this process
+    may use, and the threads the oracle takes (that share)."""
+    import oracle
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        affinity = None
+    return {"cpu_model": model, "nproc": os.cpu_count(), "affinity_cpus": affinity,
+            "omp_num_threads": os.environ.get("OMP_NUM_THREADS"),
+            "oracle_threads": oracle.host_threads()}
+
+
+def _oracle_scan_seconds(inp, io, threads, mode="zoh"):
     import oracle
     import workloads as W
-    f = lambda k: W.as_f64(inp[k], cfg.io)
+    f = lambda k: W.as_f64(inp[k], io)
     args = [f("u"), f("delta"), inp["A"], f("B"), f("C")]
     t0 = time.perf_counter()
-    oracle.scan_fwd(*args, D=inp["D"], z=f("z"), delta_bias=inp["delta_bias"], softplus=True,
-                    dt_mode="zoh", nthreads=threads)
+    oracle.scan_fwd(*args, D=inp["D"], z=f("z") if inp["z"] is not None else None,
+                    delta_bias=inp["delta_bias"], softplus=True, dt_mode=mode, nthreads=threads)
     return time.perf_counter() - t0
+
+
+def cpu_baselines(inp1, threads):
+    """The fp64 oracle, as it stands, timed on the host for every workload:
+    whole where that takes seconds (the tiny case, the Mamba-130M layer), on a
+    stated channel subset or a run of steps otherwise (extrapolated by the
+    subset's share of the updates, which the oracle's cost is linear in).
+    On `threads` host threads, and on one core for the first three."""
+    import oracle
+    import workloads as W
+    out = {}
+
+    def rec(name, seconds, updates, frac, sample, one_core=None):
+        full = seconds / frac
+        r = {"sample": sample, "seconds": round(seconds, 3), "updates": updates,
+             "updates_per_s": float(f"{updates / seconds:.4g}"),
+             "full_seconds" + ("" if frac == 1 else "_extrapolated"): round(full, 2)}
+        if one_core is not None:  # (seconds, updates) of the one-core run
+            r["one_core_seconds"] = round(one_core[0], 3)
+            r["one_core_updates_per_s"] = float(f"{one_core[1] / one_core[0]:.4g}")
+            r["one_core_full_seconds" + ("" if frac == 1 else "_extrapolated")] = \
+                round(one_core[0] * updates / frac / one_core[1], 2)
+        out[name] = r
+
+    cfg = W.SCAN_CONFIGS["tiny"]
+    inp = W.scan_inputs(cfg)
+    upd = cfg.batch * cfg.L * cfg.dim * cfg.N
+    rec("tiny", _oracle_scan_seconds(inp, cfg.io, threads), upd, 1.0, "whole (1 x 256 x 64, N 16)",
+        (_oracle_scan_seconds(inp, cfg.io, 1), upd))
+
+    cfg = W.SCAN_CONFIGS["mamba130m"]
+    upd = cfg.batch * cfg.L * cfg.dim * cfg.N
+    rec("mamba130m", _oracle_scan_seconds(inp1, cfg.io, threads), upd, 1.0,
+        "whole (8 x 2048 x 1536, N 16, gate)", (_oracle_scan_seconds(inp1, cfg.io, 1), upd))
+
+    cfg = W.SCAN_CONFIGS["mamba1p4b"]
+    ch = np.arange(1024)
+    inp = W.scan_inputs(cfg, channels=ch)
+    upd = cfg.batch * cfg.L * len(ch) * cfg.N
+    one = W.scan_inputs(cfg, channels=np.arange(256))
+    rec("mamba1p4b", _oracle_scan_seconds(inp, cfg.io, threads), upd, len(ch) / cfg.dim,
+        "channels 0-1023 of 4096 (8 x 2048, N 16, gate); one core on channels 0-255",
+        (_oracle_scan_seconds(one, cfg.io, 1), upd // 4))
+    del inp, one
+
+    cfg = W.SCAN_CONFIGS["longseq"]
+    ch = np.arange(128)
+    inp = W.scan_inputs(cfg, channels=ch)
+    upd = cfg.batch * cfg.L * len(ch) * cfg.N
+    rec("longseq", _oracle_scan_seconds(inp, cfg.io, threads), upd, len(ch) / cfg.dim,
+        "channels 0-127 of 2048 (4 x 65536, N 16)")
+    del inp
+
+    cfg = W.STEP_CONFIGS["decode"]
+    A, D, bias = W.channel_params(cfg.seed, cfg.dim, cfg.N)
+    st = W.step_state0(cfg).astype(np.float64)
+    nsteps = 10
+    toks = W.step_inputs_range(cfg, 0, nsteps)
+    f = lambda x: W.as_f64(x, cfg.io)
+    toks = [{k: f(t[k]) for k in ("u", "delta", "B", "C", "z")} for t in toks]
+    t0 = time.perf_counter()
+    for t in toks:
+        _, st = oracle.step(st, t["u"], t["delta"], A, t["B"], t["C"], D=D, z=t["z"],
+                            delta_bias=bias, nthreads=threads, inplace=True)
+    sec = time.perf_counter() - t0
+    upd = nsteps * cfg.batch * cfg.dim * cfg.N
+    rec("decode", sec, upd, nsteps / cfg.steps, f"{nsteps} of the 1000 steps on the whole "
+        "256 x 5120 x 16 state")
+    out["decode"]["tok_per_s"] = round(nsteps * cfg.batch / sec, 1)
+    return out
 
 
 def profile_only(what, launches, dt_mode):
@@ -632,7 +750,7 @@ def profile_only(what, launches, dt_mode):
         # the time-parallel kernel with four waves per row on the Mamba-130M
         # layer at batch 1, or the sequential kernel (2 states per lane) on the
         # Mamba-130M layer, forced
-        os.environ["SSM66_SCAN_KERNEL"] = "tpar" if what == "tpar" else "lds2"
+        kern = "tpar" if what == "tpar" else "seq2"
         cfg = (W.ScanConfig("mamba130m_batch1", 1, 2048, 1536, 16, "bf16", True, 7) if what == "tpar"
                else W.SCAN_CONFIGS["mamba130m"])
         s = upload_scan(W.scan_inputs(cfg), dev)
@@ -640,7 +758,8 @@ def profile_only(what, launches, dt_mode):
         last = torch.empty(cfg.batch, cfg.dim, cfg.N, device=dev)
         for _ in range(launches):
             ssm.scan_fwd(s["u"], s["delta"], s["A"], s["B"], s["C"], D=s["D"], z=s["z"],
-                         delta_bias=s["delta_bias"], dt_mode=dt_mode, y=y, last_state=last)
+                         delta_bias=s["delta_bias"], dt_mode=dt_mode, y=y, last_state=last,
+                         kernel=kern)
     elif what == "decode":
         time_decode(W.STEP_CONFIGS["decode"], launches, dev, npool=2)
     elif what == "ssd":
@@ -704,17 +823,15 @@ def main():
     scan_kernel = ssm.scan_kernel_name(cfg.batch, cfg.L, cfg.dim, cfg.N)
     settle = settle_clock(sets)
     log(f"[bench] {settle} untimed launches while the clock settles")
+    rates = alu_rates(dev)
+    log(f"[bench] ALU rates: FMA {rates['fma_lane_ops_per_s']:.4g}/s, exp {rates['exp_lane_ops_per_s']:.4g}/s, "
+        f"{rates['exp_slots_in_fma_stream']} FMA slots per exponential in an FMA stream")
+    settle_clock(sets, ms=30.0)
     log(f"[bench] timing ZOH scan ({scan_kernel})")
     wall_ms, kern_ms, kern_med, kern_min = time_scan(sets, args.steps, args.warmup, "zoh", stats=True)
     log(f"[bench] zoh: wall {wall_ms:.4f} ms/step, kernel {kern_ms:.4f} ms")
     # the same scan with the sequential kernel forced, for comparison
-    old_env = os.environ.get("SSM66_SCAN_KERNEL")
-    os.environ["SSM66_SCAN_KERNEL"] = "lds2"
-    seq_kern_ms = time_scan(sets, args.steps, args.warmup, "zoh")[1]
-    if old_env is None:
-        os.environ.pop("SSM66_SCAN_KERNEL", None)
-    else:
-        os.environ["SSM66_SCAN_KERNEL"] = old_env
+    seq_kern_ms = time_scan(sets, args.steps, args.warmup, "zoh", kernel="seq2")[1]
     log(f"[bench] zoh, sequential kernel forced: {seq_kern_ms:.4f} ms")
     log("[bench] timing exponential-Euler scan")
     e_wall, e_kern = time_scan(sets, args.steps, args.warmup, "euler")
@@ -751,13 +868,15 @@ def main():
     log(f"[bench] conv: {conv['kernel_ms']:.4f} ms, step {conv['step']['us_per_step']:.2f} us")
     log("[bench] timing the scan on the Mamba-1.4B and long-sequence layers")
     torch.cuda.empty_cache()
-    layers = time_layers(dev, args.steps, args.warmup)
+    layers = time_layers(dev, args.steps, args.warmup, rates)
     log("[bench] layers: " + ", ".join(f"{k} {v['kernel_ms']:.4f} ms ({v['GB/s']:.0f} GB/s), "
                                        f"Euler {v['euler']['kernel_ms']:.4f} ms"
                                        for k, v in layers.items()))
     log("[bench] timing the scan on few, narrow rows")
     torch.cuda.empty_cache()
-    narrow = time_narrow(dev, args.steps, args.warmup)
+    narrow = time_narrow(dev, args.steps, args.warmup, rates)
+    log("[bench] timing the tiny workload")
+    tiny = time_tiny(dev)
     log("[bench] narrow: " + ", ".join(f"{k} {v['kernel_ms']:.4f} ms (sequential {v['sequential_kernel_ms']:.4f})"
                                        for k, v in narrow.items()))
 
@@ -775,18 +894,20 @@ def main():
 
     cpu = None
     if not args.no_cpu:
-        threads = min(16, os.cpu_count() or 1)
-        log(f"[bench] timing the fp64 oracle on {threads} host threads (whole workload)")
-        cpu_s = cpu_baseline(cfg, inp0, threads)
-        cpu = {"value": round(nbytes / cpu_s / 1e9, 4), "unit": "GB/s", "cores": threads,
+        facts = host_facts()
+        threads = facts["oracle_threads"]
+        log(f"[bench] timing the fp64 oracle on {threads} host threads ({facts})")
+        per = cpu_baselines(inp0, threads)
+        c1 = per["mamba130m"]
+        cpu = {"value": round(nbytes / c1["seconds"] / 1e9, 4), "unit": "GB/s", "cores": threads,
                "kind": "oracle",
                "sample": f"the whole workload ({cfg.batch}x{cfg.L}x{cfg.dim}, N {cfg.N}, ZOH, "
-                         f"gate): {cpu_s:.2f} s wall, {elems / cpu_s:.4g} elems/s"}
-        log(f"[bench] oracle: {cpu_s:.2f} s; now on one core")
-        cpu_1 = cpu_baseline(cfg, inp0, 1)
-        cpu["one_core"] = {"value": round(nbytes / cpu_1 / 1e9, 4), "unit": "GB/s",
-                           "seconds": round(cpu_1, 2)}
-        log(f"[bench] oracle on one core: {cpu_1:.2f} s")
+                         f"gate): {c1['seconds']:.2f} s wall on {threads} threads, "
+                         f"{elems / c1['seconds']:.4g} elems/s",
+               "host": facts, "one_core": {"value": round(nbytes / c1["one_core_seconds"] / 1e9, 4),
+                                           "unit": "GB/s", "seconds": c1["one_core_seconds"]},
+               "workloads": per}
+        log(f"[bench] oracle: " + ", ".join(f"{k} {v['seconds']:.2f} s" for k, v in per.items()))
 
     gbs = nbytes / (wall_ms * 1e-3) / 1e9
     achieved = nbytes / (kern_ms * 1e-3) / 1e9
@@ -817,30 +938,34 @@ def main():
         "elems_per_s": float(f"{elems / (wall_ms * 1e-3):.4g}"),
         "updates_per_s": float(f"{elems * cfg.N / (wall_ms * 1e-3):.4g}"),
         "algorithmic_bytes_per_step": nbytes,
-        "roofline": {"bound": "alu", "achieved": round(tflops, 3), "peak": round(ALU_PEAK_TFLOPS, 2),
-                     "unit": "TFLOP/s", "frac": round(tflops / ALU_PEAK_TFLOPS, 4),
-                     "traffic": traffic, "kernel": scan_kernel + " (ZOH, bf16, gate)",
+        "roofline": {"bound": "alu", "achieved": round(tflops, 3), "peak": round(FP32_TFLOPS, 2),
+                     "unit": "TFLOP/s", "frac": round(tflops / FP32_TFLOPS, 4),
+                     "traffic": traffic,
+                     "peak_basis": "256 CU x 4 SIMD x 16 lanes x 2.4 GHz x 2 flops per fp32 FMA "
+                                   "(packed fp32 off in this build)",
+                     "published_fp32_peak": FP32_PUBLISHED_TFLOPS,
+                     "frac_published_fp32": round(tflops / FP32_PUBLISHED_TFLOPS, 4),
+                     "kernel": scan_kernel + " (ZOH, bf16, gate)",
                      "kernel_ms": round(kern_ms, 5), "kernel_ms_median": round(kern_med, 5),
                      "kernel_ms_min": round(kern_min, 5),
                      "per_launch": {"updates": updates, "flops": FLOPS_PER_UPDATE * updates,
                                     "algorithmic_bytes": nbytes},
                      "hbm": {"achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                             "frac": round(achieved / HBM_PEAK_GBS, 4)}},
+                             "frac": round(achieved / HBM_PEAK_GBS, 4)},
+                     "alu_floor": alu_figures(updates, kern_ms, "zoh", rates)["floor"],
+                     "alu_rates": rates},
         "cpu_baseline": cpu,
         "sequential_kernel": {"kernel": "scan_fwd_kernel (sequential, 2 states per lane), forced",
                               "kernel_ms": round(seq_kern_ms, 5),
-                              "alu_frac": round(FLOPS_PER_UPDATE * updates / (seq_kern_ms * 1e-3) / 1e12
-                                                / ALU_PEAK_TFLOPS, 4)},
+                              "alu": alu_figures(updates, seq_kern_ms, "zoh", rates)},
         "euler": {"ms_per_step": round(e_wall, 5), "GB/s": round(nbytes / (e_wall * 1e-3) / 1e9, 2),
                   "kernel_ms": round(e_kern, 5),
-                  "alu_frac": round(FLOPS_PER_UPDATE * updates / (e_kern * 1e-3) / 1e12
-                                    / ALU_PEAK_TFLOPS, 4)},
+                  "alu": alu_figures(updates, e_kern, "euler", rates)},
         "scan_ex": {"workload": "ssm_scan_fwd_ex on the same layer, ZOH: h0 given, lengths "
                                 f"{lens}, a document start every 512 tokens",
                     "kernel_ms": round(x_kern, 5),
                     "GB/s": round(x_bytes / (x_kern * 1e-3) / 1e9, 2),
-                    "alu_frac": round(FLOPS_PER_UPDATE * x_updates / (x_kern * 1e-3) / 1e12
-                                      / ALU_PEAK_TFLOPS, 4)},
+                    "alu": alu_figures(x_updates, x_kern, "zoh", rates)},
         "bwd": {"workload": "ssm_scan_bwd on the same layer, ZOH, gate, D, bias: du, d delta, dz, "
                             "dA, dB, dC, dD, d bias (states recomputed from the inputs)",
                 "ms": round(b_ms, 4), "x_forward": round(b_ms / kern_ms, 2),
@@ -854,6 +979,7 @@ def main():
         "conv": conv,
         "ssd": ssd,
         "layers": layers,
+        "tiny": tiny,
         "time_parallel": narrow,
         "decode": {"workload": "ssm_step: batch 256, D 5120, N 16, bf16 io, fp32 state, gate, ZOH",
                    "steps": args.decode_steps,

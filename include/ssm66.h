@@ -1,7 +1,8 @@
 /*
  * ssm66.h -- C ABI of the MI355X (gfx950) selective-scan library.
  *
- * Seven operations, defined on "Mamba and selective state spaces"
+ * Seven operations (and one measurement aid, ssm_alu_probe), defined on
+ * "Mamba and selective state spaces"
  * (zerotofrontier.app/ssm/mamba):
  *
  *   ssm_scan_fwd : the selective state-space layer (S6) over whole sequences --
@@ -80,7 +81,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 7
+#define SSM_ABI_VERSION 8
 
 /* status codes */
 #define SSM_OK 0
@@ -101,6 +102,14 @@ extern "C" {
 #define SSM_DT_ZOH 0
 #define SSM_DT_EULER 1
 
+/* scan kernel choices for ssm_scan_fwd_kernel */
+#define SSM_SCAN_KERNEL_AUTO 0 /* the library's choice by shape (what ssm_scan_fwd runs) */
+#define SSM_SCAN_KERNEL_SEQ1 1 /* sequential; 1 state per lane for 9..16 states */
+#define SSM_SCAN_KERNEL_SEQ2 2 /* sequential; 2 states per lane for 9..16 states */
+#define SSM_SCAN_KERNEL_SEQ4 3 /* sequential; 4 states per lane for 9..16 states */
+#define SSM_SCAN_KERNEL_TPAR 4 /* time-parallel, four waves per (batch, channel) row */
+#define SSM_SCAN_KERNEL_WAVE 5 /* time-parallel, one wave per row */
+
 /*
  * The selective scan over whole sequences.
  *
@@ -119,9 +128,7 @@ extern "C" {
  *   - time-parallel, four waves per row: lanes hold one token each; for
  *     fewer than 1024 rows and 128 or more tokens.
  * All give the same result up to fp32 rounding; ssm_scan_kernel_name()
- * names the one a call will run.  The environment variable SSM66_SCAN_KERNEL
- * (read at each call) forces one: "wave" or "tpar" the time-parallel kernels,
- * "lds1", "lds2" or "lds4" the sequential one with 1, 2 or 4 states per lane.
+ * names the one a call will run, and ssm_scan_fwd_kernel forces one.
  * Returns SSM_OK or an error status (see above).
  */
 int ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
@@ -151,6 +158,27 @@ int ssm_scan_fwd_ex(const void* u, const void* delta, const float* A, const void
                     int softplus, int dt_mode, const float* h0, const int32_t* seq_lens,
                     const uint8_t* reset, void* y, float* last_state, int64_t batch,
                     int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype, void* stream);
+
+/*
+ * ssm_scan_fwd_ex and ssm_scan_fwd_ckpt in one call, on a kernel chosen by the
+ * caller: kernel is one of SSM_SCAN_KERNEL_* (SSM_SCAN_KERNEL_AUTO is the
+ * library's own choice).  For tests that run every kernel on the same inputs,
+ * and for measuring one kernel against another; every kernel computes the
+ * same layer ("The selective state-space model"; the three compositions of
+ * its recurrence are described at ssm_scan_fwd).  h0, seq_lens, reset and
+ * ckpt are nullable and mean what they mean for ssm_scan_fwd_ex and
+ * ssm_scan_fwd_ckpt.  The SEQ choices fix the states per lane only for 9..16
+ * states (fewer states have one shape).  Returns SSM_ERR_FLAG for an unknown
+ * kernel, SSM_ERR_UNSUPPORTED where the forced kernel cannot address the
+ * shape (the time-parallel kernels need 1024 * dim < 2^32), else as
+ * ssm_scan_fwd_ex.
+ */
+int ssm_scan_fwd_kernel(int kernel, const void* u, const void* delta, const float* A,
+                        const void* B, const void* C, const float* D, const void* z,
+                        const float* delta_bias, int softplus, int dt_mode, const float* h0,
+                        const int32_t* seq_lens, const uint8_t* reset, void* y,
+                        float* last_state, float* ckpt, int64_t batch, int64_t seqlen,
+                        int64_t dim, int64_t dstate, int io_dtype, void* stream);
 
 /*
  * Bytes of device workspace ssm_scan_bwd needs for these sizes (0 for invalid
@@ -195,7 +223,7 @@ size_t ssm_scan_ckpt_size(int64_t batch, int64_t seqlen, int64_t dim, int64_t ds
 
 /*
  * The name of the kernel ssm_scan_fwd, ssm_scan_fwd_ex and ssm_scan_fwd_ckpt
- * run for these sizes (with SSM66_SCAN_KERNEL as currently set), e.g.
+ * run for these sizes, e.g.
  * "scan_wave_kernel (time-parallel, one wave per row)".  A static string
  * owned by the library; "invalid shape" for sizes the scan rejects.  Host
  * only: no device work.
@@ -302,6 +330,25 @@ int ssm_conv1d_fwd(const void* x, const float* weight, const float* bias, int si
 int ssm_conv1d_step(void* window, const void* x, const float* weight, const float* bias,
                     int silu, void* out, int64_t batch, int64_t dim, int64_t width, int io_dtype,
                     void* stream);
+
+/* issue-rate probes of ssm_alu_probe */
+#define SSM_PROBE_FMA 0 /* per iteration 8 x v_fma_f32 per lane */
+#define SSM_PROBE_EXP 1 /* per iteration 8 x v_exp_f32 per lane */
+#define SSM_PROBE_MIX 2 /* per iteration 8 x (v_exp_f32 + 4 x v_fma_f32) per lane */
+
+/*
+ * A measurement aid, not part of the layer: the chip's fp32 FMA and v_exp_f32
+ * issue rates, which bound the scan ("Mamba and selective state spaces", "Why
+ * the scan must be fused": one exponential per state update, and a few
+ * multiply-adds, set the scan's compute floor).  Launches blocks x 256 lanes
+ * that each run iters iterations of the chosen body over 8 independent
+ * chains and write one float per lane to sink (blocks * 256 floats, device
+ * memory, 4-byte aligned, owned by the caller; the values have no meaning).
+ * Time the launch on `stream` to get lane-operations per second.
+ * Returns SSM_ERR_FLAG for an unknown op, SSM_ERR_SHAPE for blocks outside
+ * [1, 2^31 - 1] or iters outside [0, 2^31 - 1], else as the other calls.
+ */
+int ssm_alu_probe(int op, float* sink, int64_t blocks, int64_t iters, void* stream);
 
 /* A static, human-readable string for a status code. */
 const char* ssm_status_string(int status);

@@ -68,6 +68,10 @@ def _load():
     lib.oracle_step.restype = None
     lib.oracle_step.argtypes = [ctypes.c_void_p] * 9 + [ctypes.c_int, ctypes.c_int,
                                                         ctypes.c_void_p] + [ctypes.c_int64] * 3
+    lib.oracle_step_mt.restype = None
+    lib.oracle_step_mt.argtypes = [ctypes.c_void_p] * 9 + [ctypes.c_int, ctypes.c_int,
+                                                           ctypes.c_void_p] + \
+        [ctypes.c_int64] * 3 + [ctypes.c_int]
     lib.oracle_scan_bwd.restype = None
     lib.oracle_scan_bwd.argtypes = [ctypes.c_void_p] * 9 + [ctypes.c_int, ctypes.c_int] + \
         [ctypes.c_void_p] * 11 + [ctypes.c_int64] * 4
@@ -83,6 +87,28 @@ def _load():
         [ctypes.c_int64] * 3
     _lib = lib
     return lib
+
+
+def host_threads() -> int:
+    """Host threads the oracle uses by default: the CPUs this process may run
+    on (its affinity mask), capped by a cgroup CPU quota and by OMP_NUM_THREADS
+    where those are set (a machine that shares its cores between jobs grants
+    each its share that way)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    try:
+        with open("/sys/fs/cgroup/cpu.max") as f:
+            quota, period = f.read().split()[:2]
+        if quota != "max":
+            n = min(n, max(1, -(-int(quota) // int(period))))
+    except (OSError, ValueError):
+        pass
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    if omp.isdigit() and int(omp) > 0:
+        n = min(n, int(omp))
+    return max(1, n)
 
 
 def _f64(a):
@@ -158,7 +184,7 @@ def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True,
     y = np.empty((batch, L, dim), dtype=np.float64)
     last = np.empty((batch, dim, N), dtype=np.float64)
     if nthreads is None:
-        nthreads = os.cpu_count() or 1
+        nthreads = host_threads()
     lib = _load()
     if seq_lens is None and reset is None:
         lib.oracle_scan_fwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
@@ -173,14 +199,21 @@ def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True,
 
 
 def step(state, u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True,
-         dt_mode="zoh"):
+         dt_mode="zoh", nthreads=None, inplace=False):
     """One fp64 decode step.
 
-    state: (batch, dim, N) -- not modified; the updated state is returned.
-    u, delta, z: (batch, dim); B, C: (batch, N).
+    state: (batch, dim, N) -- not modified (unless inplace: then it must be a
+    C-contiguous float64 array, updated and returned); the updated state is returned.
+    u, delta, z: (batch, dim); B, C: (batch, N).  Rows (b, c) are split over
+    nthreads host threads (default: host_threads()).
     Returns (y (batch, dim), new_state (batch, dim, N)).
     """
-    st = np.array(state, dtype=np.float64, copy=True, order="C")
+    if inplace:
+        assert isinstance(state, np.ndarray) and state.dtype == np.float64 \
+            and state.flags.c_contiguous
+        st = state
+    else:
+        st = np.array(state, dtype=np.float64, copy=True, order="C")
     u = _f64(u)
     delta = _f64(delta)
     A = _f64(A)
@@ -193,9 +226,11 @@ def step(state, u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=Tru
     N = A.shape[1]
     assert st.shape == (batch, dim, N) and B.shape == (batch, N) and C.shape == (batch, N)
     y = np.empty((batch, dim), dtype=np.float64)
-    _load().oracle_step(_ptr(st), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
-                        _ptr(z), _ptr(delta_bias), int(bool(softplus)), _MODES[dt_mode],
-                        _ptr(y), batch, dim, N)
+    if nthreads is None:
+        nthreads = host_threads()
+    _load().oracle_step_mt(_ptr(st), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                           _ptr(z), _ptr(delta_bias), int(bool(softplus)), _MODES[dt_mode],
+                           _ptr(y), batch, dim, N, int(nthreads))
     return y, st
 
 

@@ -213,28 +213,71 @@ void oracle_scan_fwd(const double* u, const double* delta, const double* A,
 /* One decode step: the same body as the scan for a single token, with the
  * state read from and written back to `state` (batch, dim, N).
  * u, delta, z, y : (batch, dim); B, C : (batch, N). */
+typedef struct {
+  double* state;
+  const double *u, *delta, *A, *B, *C, *D, *z, *bias;
+  double* y;
+  int64_t dim, N;
+  int softplus, dt_mode;
+  int64_t row_begin, row_end; /* rows are (b, c) pairs, b-major */
+} step_job;
+
+static void* step_worker(void* arg) {
+  const step_job* j = (const step_job*)arg;
+  const int64_t dim = j->dim, N = j->N;
+  for (int64_t r = j->row_begin; r < j->row_end; ++r) {
+    const int64_t b = r / dim, c = r % dim;
+    const int64_t xi = b * dim + c;
+    const double x = j->u[xi];
+    const double dt = step_size(j->delta[xi], j->bias ? j->bias[c] : 0.0, j->softplus);
+    double* h = j->state + xi * N;
+    double acc = 0.0;
+    for (int64_t n = 0; n < N; ++n) {
+      double abar, bbar;
+      oracle_discretize(dt, j->A[c * N + n], j->B[b * N + n], j->dt_mode, &abar, &bbar);
+      h[n] = abar * h[n] + bbar * x;
+      acc += j->C[b * N + n] * h[n];
+    }
+    double out = acc + (j->D ? j->D[c] : 0.0) * x;
+    if (j->z) out *= j->z[xi] * oracle_sigmoid(j->z[xi]);
+    j->y[xi] = out;
+  }
+  return NULL;
+}
+
+/* The step over all rows, split over `nthreads` host threads (rows are
+ * independent; each is computed exactly as written above). */
+void oracle_step_mt(double* state, const double* u, const double* delta, const double* A,
+                    const double* B, const double* C, const double* D, const double* z,
+                    const double* delta_bias, int softplus, int dt_mode, double* y,
+                    int64_t batch, int64_t dim, int64_t N, int nthreads) {
+  const int64_t rows = batch * dim;
+  if (rows <= 0) return;
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > rows) nthreads = (int)rows;
+  step_job* jobs = (step_job*)calloc((size_t)nthreads, sizeof(step_job));
+  pthread_t* tids = (pthread_t*)calloc((size_t)nthreads, sizeof(pthread_t));
+  for (int i = 0; i < nthreads; ++i) {
+    step_job* j = &jobs[i];
+    j->state = state; j->u = u; j->delta = delta; j->A = A; j->B = B; j->C = C; j->D = D;
+    j->z = z; j->bias = delta_bias; j->y = y; j->dim = dim; j->N = N;
+    j->softplus = softplus; j->dt_mode = dt_mode;
+    j->row_begin = rows * i / nthreads;
+    j->row_end = rows * (i + 1) / nthreads;
+  }
+  for (int i = 1; i < nthreads; ++i) pthread_create(&tids[i], NULL, step_worker, &jobs[i]);
+  step_worker(&jobs[0]);
+  for (int i = 1; i < nthreads; ++i) pthread_join(tids[i], NULL);
+  free(jobs);
+  free(tids);
+}
+
 void oracle_step(double* state, const double* u, const double* delta, const double* A,
                  const double* B, const double* C, const double* D, const double* z,
                  const double* delta_bias, int softplus, int dt_mode, double* y,
                  int64_t batch, int64_t dim, int64_t N) {
-  for (int64_t b = 0; b < batch; ++b) {
-    for (int64_t c = 0; c < dim; ++c) {
-      const int64_t xi = b * dim + c;
-      const double x = u[xi];
-      const double dt = step_size(delta[xi], delta_bias ? delta_bias[c] : 0.0, softplus);
-      double* h = state + xi * N;
-      double acc = 0.0;
-      for (int64_t n = 0; n < N; ++n) {
-        double abar, bbar;
-        oracle_discretize(dt, A[c * N + n], B[b * N + n], dt_mode, &abar, &bbar);
-        h[n] = abar * h[n] + bbar * x;
-        acc += C[b * N + n] * h[n];
-      }
-      double out = acc + (D ? D[c] : 0.0) * x;
-      if (z) out *= z[xi] * oracle_sigmoid(z[xi]);
-      y[xi] = out;
-    }
-  }
+  oracle_step_mt(state, u, delta, A, B, C, D, z, delta_bias, softplus, dt_mode, y, batch, dim, N,
+                 1);
 }
 
 /* ------------------------------------------------------------------------

@@ -27,6 +27,10 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libssm66_hi
 SSM_F32, SSM_BF16 = 0, 1
 SSM_DT_ZOH, SSM_DT_EULER = 0, 1
 _MODES = {"zoh": SSM_DT_ZOH, "euler": SSM_DT_EULER}
+# scan kernel choices (SSM_SCAN_KERNEL_*): the library's own, the sequential
+# kernel with 1, 2 or 4 states per lane, the time-parallel kernels with four
+# waves or one wave per (batch, channel) row
+SCAN_KERNELS = {"auto": 0, "seq1": 1, "seq2": 2, "seq4": 3, "tpar": 4, "wave": 5}
 
 _lib = None
 
@@ -57,6 +61,8 @@ def load_library():
     lib.ssm_scan_ckpt_size.argtypes = [i64] * 4
     lib.ssm_scan_kernel_name.restype = ctypes.c_char_p
     lib.ssm_scan_kernel_name.argtypes = [i64] * 4
+    lib.ssm_scan_fwd_kernel.restype = ci
+    lib.ssm_scan_fwd_kernel.argtypes = [ci] + [vp] * 8 + [ci, ci] + [vp] * 6 + [i64] * 4 + [ci, vp]
     lib.ssm_scan_fwd_ckpt.restype = ci
     lib.ssm_scan_fwd_ckpt.argtypes = [vp] * 8 + [ci, ci] + [vp] * 4 + [i64] * 4 + [ci, vp]
     lib.ssm_scan_bwd_ex.restype = ci
@@ -73,6 +79,8 @@ def load_library():
     lib.ssm_conv1d_step.argtypes = [vp] * 4 + [ci, vp] + [i64] * 3 + [ci, vp]
     lib.ssm_step.restype = ci
     lib.ssm_step.argtypes = [vp] * 9 + [ci, ci, vp, i64, i64, i64, ci, vp]
+    lib.ssm_alu_probe.restype = ci
+    lib.ssm_alu_probe.argtypes = [ci, vp, i64, i64, vp]
     lib.ssm_status_string.restype = ctypes.c_char_p
     lib.ssm_status_string.argtypes = [ci]
     lib.ssm_abi_version.restype = ci
@@ -121,7 +129,8 @@ def _stream(device):
 
 
 def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True, dt_mode="zoh",
-             y=None, last_state=None, return_last_state=True, h0=None, seq_lens=None, reset=None):
+             y=None, last_state=None, return_last_state=True, h0=None, seq_lens=None, reset=None,
+             kernel=None):
     """Selective scan over whole sequences on the GPU.
 
     u, delta, z: (batch, L, dim); B, C: (batch, L, N) -- all float32 or all bfloat16.
@@ -129,6 +138,7 @@ def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True, 
     h0: optional (batch, dim, N) float32 initial state (last_state may be h0: in place);
     seq_lens: optional (batch,) int32 real lengths (padding after them: y = 0, state kept);
     reset: optional (batch, L) bool or uint8, state zeroed before each flagged token.
+    kernel: None (the library's choice) or a key of SCAN_KERNELS to force one kernel.
     Returns (y, last_state): y like u; last_state (batch, dim, N) float32 (None if not requested).
     """
     import torch
@@ -156,7 +166,7 @@ def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True, 
     if last_state is None and return_last_state:
         last_state = torch.empty((batch, dim, N), dtype=torch.float32, device=dev)
     _check(last_state, "last_state", (batch, dim, N), torch.float32, dev)
-    if h0 is None and seq_lens is None and reset is None:
+    if h0 is None and seq_lens is None and reset is None and kernel is None:
         st = lib.ssm_scan_fwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
                               _ptr(delta_bias), int(bool(softplus)), _MODES[dt_mode], _ptr(y),
                               _ptr(last_state), batch, L, dim, N, _io_code(u), _stream(dev))
@@ -168,6 +178,15 @@ def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True, 
     if reset is not None and reset.dtype == torch.bool:
         reset = reset.view(torch.uint8)
     _check(reset, "reset", (batch, L), torch.uint8, dev)
+    if kernel is not None:
+        st = lib.ssm_scan_fwd_kernel(SCAN_KERNELS[kernel], _ptr(u), _ptr(delta), _ptr(A), _ptr(B),
+                                     _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+                                     int(bool(softplus)), _MODES[dt_mode], _ptr(h0),
+                                     _ptr(seq_lens), _ptr(reset), _ptr(y), _ptr(last_state), None,
+                                     batch, L, dim, N, _io_code(u), _stream(dev))
+        if st != 0:
+            raise SsmError(st, "ssm_scan_fwd_kernel")
+        return y, last_state
     st = lib.ssm_scan_fwd_ex(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
                              _ptr(delta_bias), int(bool(softplus)), _MODES[dt_mode], _ptr(h0),
                              _ptr(seq_lens), _ptr(reset), _ptr(y), _ptr(last_state), batch, L,
@@ -341,6 +360,24 @@ def scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, softplus=Tr
     return g
 
 
+ALU_PROBES = {"fma": 0, "exp": 1, "mix": 2}
+
+
+def alu_probe(op, sink, blocks, iters):
+    """Launch the issue-rate probe `op` ("fma", "exp" or "mix") on the current
+    stream: blocks x 256 lanes, iters iterations each; sink is a float32 device
+    tensor of at least blocks * 256 elements.  Time it with events on the
+    current stream."""
+    import torch
+    lib = load_library()
+    if sink.dtype != torch.float32 or sink.device.type != "cuda" or sink.numel() < blocks * 256:
+        raise ValueError("sink: float32 device tensor of at least blocks * 256 elements")
+    st = lib.ssm_alu_probe(ALU_PROBES[op], _ptr(sink), int(blocks), int(iters),
+                           _stream(sink.device))
+    if st != 0:
+        raise SsmError(st, "ssm_alu_probe")
+
+
 def scan_kernel_name(batch, L, dim, N):
     """Name of the kernel ssm_scan_fwd runs for these sizes (host only)."""
     return load_library().ssm_scan_kernel_name(batch, L, dim, N).decode()
@@ -352,9 +389,9 @@ def scan_ckpt_size(batch, L, dim, N):
 
 
 def scan_fwd_train(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True,
-                   dt_mode="zoh", h0=None, y=None, last_state=None, ckpt=None):
+                   dt_mode="zoh", h0=None, y=None, last_state=None, ckpt=None, kernel=None):
     """The training forward: scan_fwd (with an optional h0) that also keeps the
-    state before every 16th token for scan_bwd.
+    state before every 16th token for scan_bwd.  kernel as for scan_fwd.
 
     Returns (y, last_state, ckpt); ckpt is (batch, ceil(L/16), dim, N) float32.
     """
@@ -386,6 +423,15 @@ def scan_fwd_train(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=
     if ckpt is None:
         ckpt = torch.empty((batch, (L + 15) // 16, dim, N), dtype=torch.float32, device=dev)
     _check(ckpt, "ckpt", (batch, (L + 15) // 16, dim, N), torch.float32, dev)
+    if kernel is not None:
+        st = lib.ssm_scan_fwd_kernel(SCAN_KERNELS[kernel], _ptr(u), _ptr(delta), _ptr(A), _ptr(B),
+                                     _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+                                     int(bool(softplus)), _MODES[dt_mode], _ptr(h0), None, None,
+                                     _ptr(y), _ptr(last_state), _ptr(ckpt), batch, L, dim, N,
+                                     _io_code(u), _stream(dev))
+        if st != 0:
+            raise SsmError(st, "ssm_scan_fwd_kernel")
+        return y, last_state, ckpt
     st = lib.ssm_scan_fwd_ckpt(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
                                _ptr(delta_bias), int(bool(softplus)), _MODES[dt_mode], _ptr(h0),
                                _ptr(y), _ptr(last_state), _ptr(ckpt), batch, L, dim, N,

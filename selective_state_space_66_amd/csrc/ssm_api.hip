@@ -4,7 +4,6 @@
 // status without touching a device and with nothing enqueued.  A valid call
 // chooses a kernel instance and enqueues one launch on the caller's stream.
 #include <stdint.h>
-#include <stdlib.h>
 
 #include "../../include/ssm66.h"
 #include "ssm_launch.h"
@@ -56,14 +55,11 @@ constexpr int64_t kSeqMinRows = 32768;
 // (G * NG >= dstate).  Up to 8 states one group shape covers them; for 9..16
 // the choice trades per-thread work against the number of waves: a wave is
 // 16 channels x 4 groups (64 lanes), so b * dim * NG / 64 waves share the 1024
-// SIMDs.  SSM66_SCAN_KERNEL = "lds1", "lds2" or "lds4" forces G for 9..16
-// states (tuning, and tests that cover every instance).
-void pick_scan_shape(int64_t batch, int64_t dim, int64_t dstate, int* G, int* NG) {
+// SIMDs.  forced_g (1, 2 or 4; 0 = choose) fixes G for 9..16 states.
+void pick_scan_shape(int64_t batch, int64_t dim, int64_t dstate, int forced_g, int* G, int* NG) {
   if (dstate <= 4) { *G = 1; *NG = 4; return; }
   if (dstate <= 8) { *G = 2; *NG = 4; return; }
-  int g = 0;
-  if (const char* e = getenv("SSM66_SCAN_KERNEL"))
-    if (e[0] == 'l' && e[1] == 'd' && e[2] == 's') g = atoi(e + 3);
+  int g = forced_g;
   if (g != 1 && g != 2 && g != 4) {
     const int64_t waves4 = batch * dim * 4 / 64;  // waves with G = 4
     g = waves4 >= 2048 ? 4 : (waves4 >= 512 ? 2 : 1);
@@ -72,23 +68,27 @@ void pick_scan_shape(int64_t batch, int64_t dim, int64_t dstate, int* G, int* NG
   *NG = 16 / g;
 }
 
-// Which scan kernel runs (see the crossovers above).  SSM66_SCAN_KERNEL =
-// "tpar" forces the time-parallel kernel with four waves per row, "wave" the
-// one with one wave per row, "lds*" the sequential one.
+// Which scan kernel runs (see the crossovers above).
 enum class ScanKernel { kSequential, kTpar, kWave };
 
+// the time-parallel kernels address a 256-token chunk with 32-bit offsets
+bool tpar_fits(int64_t dim) { return 1024 * dim < 0xffffffffLL; }
+
 ScanKernel pick_scan_kernel(int64_t batch, int64_t dim, int64_t L, int64_t dstate) {
-  // the time-parallel kernels address a 256-token chunk with 32-bit offsets
-  if (1024 * dim >= 0xffffffffLL || dstate > 16) return ScanKernel::kSequential;
-  if (const char* e = getenv("SSM66_SCAN_KERNEL")) {
-    if (e[0] == 't') return ScanKernel::kTpar;
-    if (e[0] == 'w') return ScanKernel::kWave;
-    if (e[0] == 'l') return ScanKernel::kSequential;
-  }
+  if (!tpar_fits(dim) || dstate > 16) return ScanKernel::kSequential;
   const int64_t rows = batch * dim;
   if (rows <= kTparMaxRows) return L >= kTparMinLen ? ScanKernel::kTpar : ScanKernel::kSequential;
   if (L < kWaveMinLen || rows >= kSeqMinRows) return ScanKernel::kSequential;
   return ScanKernel::kWave;
+}
+
+// Grid of the chosen kernel within the launch limit (one block per 16
+// channels for the sequential kernel, per 8 for one wave per row, per row for
+// four waves per row).
+bool grid_fits(ScanKernel k, int64_t batch, int64_t dim) {
+  const int64_t per = k == ScanKernel::kWave ? 8 : (k == ScanKernel::kTpar ? 1 : 16);
+  const __int128 blocks = (__int128)batch * ((dim + per - 1) / per);
+  return blocks <= 0x7fffffff;
 }
 
 }  // namespace
@@ -111,11 +111,14 @@ const char* ssm_status_string(int status) {
   }
 }
 
-static int scan_fwd_impl(const void* u, const void* delta, const float* A, const void* B,
-                    const void* C, const float* D, const void* z, const float* delta_bias,
-                    int softplus, int dt_mode, const float* h0, const int32_t* seq_lens,
-                    const uint8_t* reset, void* y, float* last_state, float* ckpt, int64_t batch,
-                    int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype, void* stream) {
+// kernel: SSM_SCAN_KERNEL_AUTO, or one of the forced choices of
+// ssm_scan_fwd_kernel (validated by the caller).
+static int scan_fwd_impl(int kernel, const void* u, const void* delta, const float* A,
+                         const void* B, const void* C, const float* D, const void* z,
+                         const float* delta_bias, int softplus, int dt_mode, const float* h0,
+                         const int32_t* seq_lens, const uint8_t* reset, void* y,
+                         float* last_state, float* ckpt, int64_t batch, int64_t seqlen,
+                         int64_t dim, int64_t dstate, int io_dtype, void* stream) {
   int st = check_common(batch, seqlen, dim, dstate, io_dtype, softplus, dt_mode);
   if (st != SSM_OK) return st;
   const bool has_tokens = batch > 0 && seqlen > 0 && dim > 0;
@@ -131,8 +134,22 @@ static int scan_fwd_impl(const void* u, const void* delta, const float* A, const
   const void* f32_ptrs[6] = {A, D, delta_bias, last_state, h0, seq_lens};
   for (const void* q : f32_ptrs)
     if (q && !aligned(q, 4)) return SSM_ERR_ALIGN;
-  // grid size, and 32-bit lane offsets within a chunk (16 groups x dim)
-  if (batch * ((dim + 15) / 16) > 0x7fffffff || 16 * dim > 0x7fffffff) return SSM_ERR_UNSUPPORTED;
+  // the sequential kernel's 32-bit lane offsets within a chunk (16 groups x dim)
+  if (16 * dim > 0x7fffffff) return SSM_ERR_UNSUPPORTED;
+
+  ScanKernel kern = ScanKernel::kSequential;
+  int forced_g = 0;
+  if (!has_tokens) {
+    kern = ScanKernel::kSequential;  // writes the initial state only
+  } else if (kernel == SSM_SCAN_KERNEL_AUTO) {
+    kern = pick_scan_kernel(batch, dim, seqlen, dstate);
+  } else if (kernel == SSM_SCAN_KERNEL_TPAR || kernel == SSM_SCAN_KERNEL_WAVE) {
+    if (!tpar_fits(dim)) return SSM_ERR_UNSUPPORTED;
+    kern = kernel == SSM_SCAN_KERNEL_TPAR ? ScanKernel::kTpar : ScanKernel::kWave;
+  } else {
+    forced_g = kernel == SSM_SCAN_KERNEL_SEQ1 ? 1 : (kernel == SSM_SCAN_KERNEL_SEQ2 ? 2 : 4);
+  }
+  if (!grid_fits(kern, batch, dim)) return SSM_ERR_UNSUPPORTED;
 
   ssm66::ScanParams p;
   p.u = u; p.delta = delta; p.A = A; p.B = B; p.C = C; p.D = D; p.z = z;
@@ -140,8 +157,6 @@ static int scan_fwd_impl(const void* u, const void* delta, const float* A, const
   p.y = y; p.last_state = last_state; p.ckpt = has_tokens ? ckpt : nullptr;
   p.batch = batch; p.L = seqlen; p.dim = dim; p.N = dstate; p.softplus = softplus;
   hipError_t e;
-  const ScanKernel kern =
-      has_tokens ? pick_scan_kernel(batch, dim, seqlen, dstate) : ScanKernel::kSequential;
   if (kern == ScanKernel::kTpar) {
     e = ssm66::launch_scan_tpar(p, io_dtype, dt_mode == SSM_DT_ZOH, z != nullptr,
                                 (hipStream_t)stream);
@@ -150,11 +165,23 @@ static int scan_fwd_impl(const void* u, const void* delta, const float* A, const
                                 (hipStream_t)stream);
   } else {
     int G, NG;
-    pick_scan_shape(batch, dim, dstate, &G, &NG);
+    pick_scan_shape(batch, dim, dstate, forced_g, &G, &NG);
     e = ssm66::launch_scan_fwd(p, io_dtype, G, NG, dt_mode == SSM_DT_ZOH, z != nullptr,
                                (hipStream_t)stream);
   }
   return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
+int ssm_scan_fwd_kernel(int kernel, const void* u, const void* delta, const float* A,
+                        const void* B, const void* C, const float* D, const void* z,
+                        const float* delta_bias, int softplus, int dt_mode, const float* h0,
+                        const int32_t* seq_lens, const uint8_t* reset, void* y,
+                        float* last_state, float* ckpt, int64_t batch, int64_t seqlen,
+                        int64_t dim, int64_t dstate, int io_dtype, void* stream) {
+  if (kernel < SSM_SCAN_KERNEL_AUTO || kernel > SSM_SCAN_KERNEL_WAVE) return SSM_ERR_FLAG;
+  return scan_fwd_impl(kernel, u, delta, A, B, C, D, z, delta_bias, softplus, dt_mode, h0,
+                       seq_lens, reset, y, last_state, ckpt, batch, seqlen, dim, dstate, io_dtype,
+                       stream);
 }
 
 int ssm_scan_fwd_ex(const void* u, const void* delta, const float* A, const void* B,
@@ -162,8 +189,9 @@ int ssm_scan_fwd_ex(const void* u, const void* delta, const float* A, const void
                     int softplus, int dt_mode, const float* h0, const int32_t* seq_lens,
                     const uint8_t* reset, void* y, float* last_state, int64_t batch,
                     int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype, void* stream) {
-  return scan_fwd_impl(u, delta, A, B, C, D, z, delta_bias, softplus, dt_mode, h0, seq_lens, reset,
-                       y, last_state, nullptr, batch, seqlen, dim, dstate, io_dtype, stream);
+  return scan_fwd_impl(SSM_SCAN_KERNEL_AUTO, u, delta, A, B, C, D, z, delta_bias, softplus,
+                       dt_mode, h0, seq_lens, reset, y, last_state, nullptr, batch, seqlen, dim,
+                       dstate, io_dtype, stream);
 }
 
 const char* ssm_scan_kernel_name(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate) {
@@ -175,7 +203,7 @@ const char* ssm_scan_kernel_name(int64_t batch, int64_t seqlen, int64_t dim, int
     default: break;
   }
   int G, NG;
-  pick_scan_shape(batch, dim, dstate, &G, &NG);
+  pick_scan_shape(batch, dim, dstate, 0, &G, &NG);
   if (G == 4) return "scan_fwd_kernel (sequential, 4 states per lane)";
   if (G == 2) return "scan_fwd_kernel (sequential, 2 states per lane)";
   return "scan_fwd_kernel (sequential, 1 state per lane)";
@@ -192,8 +220,9 @@ int ssm_scan_fwd_ckpt(const void* u, const void* delta, const float* A, const vo
                       float* ckpt, int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
                       int io_dtype, void* stream) {
   if (seqlen > 0 && batch > 0 && dim > 0 && !ckpt) return SSM_ERR_NULL;
-  return scan_fwd_impl(u, delta, A, B, C, D, z, delta_bias, softplus, dt_mode, h0, nullptr,
-                       nullptr, y, last_state, ckpt, batch, seqlen, dim, dstate, io_dtype, stream);
+  return scan_fwd_impl(SSM_SCAN_KERNEL_AUTO, u, delta, A, B, C, D, z, delta_bias, softplus,
+                       dt_mode, h0, nullptr, nullptr, y, last_state, ckpt, batch, seqlen, dim,
+                       dstate, io_dtype, stream);
 }
 
 int ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
@@ -388,6 +417,15 @@ int ssm_conv1d_step(void* window, const void* x, const float* weight, const floa
   p.reset = nullptr; p.out = out; p.state_out = window;
   p.batch = batch; p.L = 1; p.dim = dim; p.k = width; p.silu = silu;
   const hipError_t e = ssm66::launch_conv1d(p, io_dtype, vec4, true, (hipStream_t)stream);
+  return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
+int ssm_alu_probe(int op, float* sink, int64_t blocks, int64_t iters, void* stream) {
+  if (op != SSM_PROBE_FMA && op != SSM_PROBE_EXP && op != SSM_PROBE_MIX) return SSM_ERR_FLAG;
+  if (blocks < 1 || blocks > 0x7fffffff || iters < 0 || iters > 0x7fffffff) return SSM_ERR_SHAPE;
+  if (!sink) return SSM_ERR_NULL;
+  if (!aligned(sink, 4)) return SSM_ERR_ALIGN;
+  const hipError_t e = ssm66::launch_alu_probe(op, sink, blocks, (int)iters, (hipStream_t)stream);
   return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 

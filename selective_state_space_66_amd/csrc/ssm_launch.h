@@ -96,4 +96,12 @@ hipError_t launch_scan_wave(const ScanParams& p, int io_dtype, bool zoh, bool ga
 hipError_t launch_ssd_fwd(const SSDParams& p, bool zoh, bool gate, hipStream_t stream);
 hipError_t launch_step(const StepParams& p, int io_dtype, bool zoh, bool gate, hipStream_t stream);
 
+// Issue-rate probes (probe.hip): blocks x 256 lanes, iters iterations of 8
+// FMAs, 8 exponentials, or 8 x (exponential + 4 FMAs); sink holds one float
+// per lane.
+constexpr int kAluProbeFma = 0;
+constexpr int kAluProbeExp = 1;
+constexpr int kAluProbeMix = 2;
+hipError_t launch_alu_probe(int op, float* sink, int64_t blocks, int iters, hipStream_t stream);
+
 }  // namespace ssm66

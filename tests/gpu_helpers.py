@@ -27,7 +27,9 @@ def f64(x, io):
     return W.as_f64(x, io)
 
 
-def scan_gpu(inp, dt_mode="zoh", softplus=True, use_D=True, use_bias=True, use_z=True):
+def scan_gpu(inp, dt_mode="zoh", softplus=True, use_D=True, use_bias=True, use_z=True,
+             kernel=None):
+    """The HIP scan on inp; kernel forces one scan kernel (see ssm.SCAN_KERNELS)."""
     io = inp["io"]
     y, last = ssm.scan_fwd(
         to_dev(inp["u"], io), to_dev(inp["delta"], io), to_dev(inp["A"], "f32"),
@@ -35,7 +37,7 @@ def scan_gpu(inp, dt_mode="zoh", softplus=True, use_D=True, use_bias=True, use_z
         D=to_dev(inp["D"], "f32") if use_D else None,
         z=to_dev(inp["z"], io) if (use_z and inp["z"] is not None) else None,
         delta_bias=to_dev(inp["delta_bias"], "f32") if use_bias else None,
-        softplus=softplus, dt_mode=dt_mode)
+        softplus=softplus, dt_mode=dt_mode, kernel=kernel)
     torch.cuda.synchronize()
     return y, last
 

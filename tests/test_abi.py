@@ -38,7 +38,8 @@ def test_exports_every_declared_symbol(lib):
                           "ssm_scan_ckpt_size", "ssm_scan_bwd", "ssm_scan_bwd_ex",
                           "ssm_scan_bwd_workspace_size", "ssm_step", "ssm_ssd_fwd",
                           "ssm_conv1d_fwd", "ssm_conv1d_step", "ssm_status_string",
-                          "ssm_abi_version", "ssm_scan_kernel_name"}
+                          "ssm_abi_version", "ssm_scan_kernel_name", "ssm_scan_fwd_kernel",
+                          "ssm_alu_probe"}
     raw = ctypes.CDLL(ssm.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), f"{n} not exported"
@@ -256,10 +257,9 @@ def test_ckpt_size(lib):
     assert f(-1, 4, 4, 4) == 0 and f(1, 4, 4, 17) == 0
 
 
-def test_scan_kernel_choice(lib, monkeypatch):
+def test_scan_kernel_choice(lib):
     """The kernel the scan picks (host logic only): the crossovers measured on
-    MI355X, the environment override, and the degenerate sizes."""
-    monkeypatch.delenv("SSM66_SCAN_KERNEL", raising=False)
+    MI355X and the degenerate sizes."""
     name = ssm.scan_kernel_name
     assert name(8, 2048, 1536, 16).startswith("scan_wave_kernel")      # Mamba-130M layer
     assert name(4, 65536, 2048, 16).startswith("scan_wave_kernel")     # long sequences
@@ -274,16 +274,43 @@ def test_scan_kernel_choice(lib, monkeypatch):
     assert name(16, 2048, 2047, 16).startswith("scan_wave_kernel")     # 32752 rows
     assert name(0, 16, 8, 16) == "none (no tokens)" and name(2, 0, 8, 16) == "none (no tokens)"
     assert name(1, 4, 4, 17) == "invalid shape" and name(-1, 4, 4, 4) == "invalid shape"
-    for env, prefix in (("tpar", "scan_tpar_kernel"), ("wave", "scan_wave_kernel"),
-                        ("lds4", "scan_fwd_kernel (sequential, 4 states")):
-        monkeypatch.setenv("SSM66_SCAN_KERNEL", env)
-        assert name(8, 2048, 1536, 16).startswith(prefix), env
-    # the time-parallel kernels address a 256-token chunk of up to 4-byte
-    # elements with 32-bit offsets: wider layers take the sequential kernel
-    # even when one is forced
-    monkeypatch.setenv("SSM66_SCAN_KERNEL", "wave")
-    assert name(1, 2048, (1 << 22) - 1, 16).startswith("scan_wave_kernel")
     assert name(1, 2048, 1 << 22, 16).startswith("scan_fwd_kernel")
+
+
+def _scan_kernel(lib, kernel, **kw):
+    """ssm_scan_fwd_kernel with fake (never dereferenced) pointers: every case
+    here is rejected before any HIP call."""
+    a = dict(u=FAKE, d=FAKE, A=FAKE, B=FAKE, C=FAKE, y=FAKE, batch=2, L=300, dim=48, N=16,
+             io=0, ckpt=None)
+    a.update(kw)
+    return lib.ssm_scan_fwd_kernel(kernel, a["u"], a["d"], a["A"], a["B"], a["C"], None, None,
+                                   None, 1, 0, None, None, None, a["y"], None, a["ckpt"],
+                                   a["batch"], a["L"], a["dim"], a["N"], a["io"], None)
+
+
+def test_forced_kernel_validation(lib):
+    """ssm_scan_fwd_kernel: unknown kernels are flagged; a forced time-parallel
+    kernel on a layer too wide for its 32-bit chunk offsets, and grids past the
+    launch limit of the chosen kernel, are unsupported -- all before any HIP
+    call."""
+    c = _header_constants()
+    assert c["SSM_SCAN_KERNEL_AUTO"] == 0 and c["SSM_SCAN_KERNEL_WAVE"] == 5
+    assert _scan_kernel(lib, -1) == c["SSM_ERR_FLAG"]
+    assert _scan_kernel(lib, 6) == c["SSM_ERR_FLAG"]
+    assert _scan_kernel(lib, c["SSM_SCAN_KERNEL_WAVE"], dim=1 << 22) == c["SSM_ERR_UNSUPPORTED"]
+    assert _scan_kernel(lib, c["SSM_SCAN_KERNEL_TPAR"], dim=1 << 22) == c["SSM_ERR_UNSUPPORTED"]
+    # four waves per row: one block per (batch, channel) row
+    assert _scan_kernel(lib, c["SSM_SCAN_KERNEL_TPAR"], batch=1 << 20, dim=1 << 12, L=1) \
+        == c["SSM_ERR_UNSUPPORTED"]
+    # one wave per row: one block per 8 channels of a batch entry
+    assert _scan_kernel(lib, c["SSM_SCAN_KERNEL_WAVE"], batch=1 << 23, dim=1 << 11, L=1) \
+        == c["SSM_ERR_UNSUPPORTED"]
+    # the automatic choice for the same shape is the sequential kernel, whose
+    # blocks of 16 channels still fit
+    assert ssm.scan_kernel_name(1 << 23, 1, 1 << 11, 16).startswith("scan_fwd_kernel")
+    assert _scan_kernel(lib, c["SSM_SCAN_KERNEL_AUTO"], batch=1 << 23, dim=1 << 11, L=1,
+                        u=MISALIGNED) == c["SSM_ERR_ALIGN"]
+    assert _scan_kernel(lib, c["SSM_SCAN_KERNEL_SEQ4"], y=None) == c["SSM_ERR_NULL"]
 
 
 ALIGN16 = ctypes.c_void_p(0x10000)

@@ -101,11 +101,17 @@ def _readout_scale(inp, mode):
 
 
 def test_extreme_step_sizes_finite():
-    """softplus of +-1000 stays finite; Delta = 0 tokens leave the state alone.
-    Under exponential-Euler a step of ~1000 writes ~1000 u B into the state
-    (the write "keeps growing like Delta B"), so the readout sums terms of
-    magnitude ~1e3 that may cancel: the bound here is 1e-4 (1 + term scale)
-    elementwise, the fp32 summation bound with a wide margin."""
+    """Raw step sizes of +-1000: softplus stays finite, Delta = 0 tokens leave
+    the state alone, and a step of 1000 forgets the state ("Mamba and selective
+    state spaces", "The discretization the code actually uses").
+
+    Under ZOH the input weight saturates at B / |A| as Delta grows, so every
+    readout term stays of the size of the inputs and the acceptance bound
+    1e-4 (1 + |y_ref|) holds elementwise.  Under exponential-Euler the weight
+    is Delta B itself: a step of 1000 puts about 1000 u B into the state, and
+    the readout sums terms of magnitude ~1e3 that can cancel.  An fp32 sum of
+    n terms is accurate to about n eps times the sum of their magnitudes, not
+    times |y|, so for Euler the bound is 1e-4 (1 + term scale) elementwise."""
     inp = W.scan_inputs(_cfg(1, 64, 64, 16, "f32", True, seed=8))
     d = inp["delta"].copy()
     d[0, ::7, :] = 1000.0
@@ -116,8 +122,10 @@ def test_extreme_step_sizes_finite():
         yr, lr = scan_ref(inp, mode)
         yg = to_host64(y)
         assert np.all(np.isfinite(yg))
-        scale = _readout_scale(inp, mode)
-        err = np.abs(yg - yr) / (1.0 + scale)
+        if mode == "zoh":
+            err = np.abs(yg - yr) / (1.0 + np.abs(yr))
+        else:
+            err = np.abs(yg - yr) / (1.0 + _readout_scale(inp, mode))
         assert float(err.max()) <= 1e-4, f"y {mode}: {float(err.max()):.3e}"
         ls = to_host64(last)
         assert float(np.max(np.abs(ls - lr) / (1.0 + np.abs(lr)))) <= 1e-4, f"last {mode}"
@@ -136,25 +144,24 @@ def test_long_sequence_fp32(mode):
 
 # sequential kernels with G = 1, 2, 4 states per thread, and the two
 # time-parallel ones (four waves per row; one wave per row, four tokens per lane)
-KERNELS = ["lds1", "lds2", "lds4", "tpar", "wave"]
+KERNELS = ["seq1", "seq2", "seq4", "tpar", "wave"]
 
 
 @pytest.mark.parametrize("kernel", KERNELS)
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 @pytest.mark.parametrize("mode", ["zoh", "euler"])
 @pytest.mark.parametrize("gate", [True, False])
-def test_each_kernel_ragged(kernel, io, mode, gate, monkeypatch):
+def test_each_kernel_ragged(kernel, io, mode, gate):
     """Every scan kernel instance for 16 states (G = 1, 2, 4 states per thread),
-    forced through SSM66_SCAN_KERNEL: a ragged channel tile and last chunk, and
+    forced through the kernel choice: a ragged channel tile and last chunk, and
     one channel with a zero and one with slow rates (the careful ZOH form)
     beside fast-path channels."""
-    monkeypatch.setenv("SSM66_SCAN_KERNEL", kernel)
     inp = W.scan_inputs(_cfg(2, 100, 130, 16, io, gate, seed=12))
     A = inp["A"].copy()
     A[70, 3] = 0.0
     A[71, :] = -0.2
     inp["A"] = A
-    y, last = scan_gpu(inp, mode)
+    y, last = scan_gpu(inp, mode, kernel=kernel)
     yr, lr = scan_ref(inp, mode)
     assert_close(to_host64(y), yr, io, "y")
     assert_close(to_host64(last), lr, io, "last_state")
@@ -174,13 +181,12 @@ def _offset_dev(x, io, off=1):
 @pytest.mark.parametrize("kernel", KERNELS)
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 @pytest.mark.parametrize("which", ["all", "y"])
-def test_each_kernel_element_aligned_inputs(kernel, io, which, monkeypatch):
+def test_each_kernel_element_aligned_inputs(kernel, io, which):
     """Inputs and output (or y alone) one element past 16-byte alignment (the
     C ABI asks only for element alignment): the kernels' vector loads and
     stores are taken only for aligned rows, else element by element.
     Dimensions keep the vector paths' other conditions (dim a multiple of 8,
     N 16)."""
-    monkeypatch.setenv("SSM66_SCAN_KERNEL", kernel)
     inp = W.scan_inputs(_cfg(2, 300, 48, 16, io, True, seed=19))
     put = _offset_dev if which == "all" else to_dev
     y = _offset_dev(np.zeros((2, 300, 48), dtype=np.uint16 if io == "bf16" else np.float32), io)
@@ -188,7 +194,7 @@ def test_each_kernel_element_aligned_inputs(kernel, io, which, monkeypatch):
                             to_dev(inp["A"], "f32"), put(inp["B"], io),
                             put(inp["C"], io), D=to_dev(inp["D"], "f32"),
                             z=put(inp["z"], io), delta_bias=to_dev(inp["delta_bias"], "f32"),
-                            dt_mode="zoh", y=y)
+                            dt_mode="zoh", y=y, kernel=kernel)
     torch.cuda.synchronize()
     yr, lr = scan_ref(inp, "zoh")
     assert_close(to_host64(yo), yr, io, "y")
@@ -197,10 +203,9 @@ def test_each_kernel_element_aligned_inputs(kernel, io, which, monkeypatch):
 
 @pytest.mark.parametrize("kernel", KERNELS)
 @pytest.mark.parametrize("L", [0, 1, 3, 31, 32, 33, 65])
-def test_each_kernel_short_sequences(kernel, L, monkeypatch):
-    monkeypatch.setenv("SSM66_SCAN_KERNEL", kernel)
+def test_each_kernel_short_sequences(kernel, L):
     inp = W.scan_inputs(_cfg(3, L, 70, 16, "f32", True, seed=13))
-    y, last = scan_gpu(inp, "zoh")
+    y, last = scan_gpu(inp, "zoh", kernel=kernel)
     yr, lr = scan_ref(inp, "zoh")
     assert_close(to_host64(y), yr, "f32", "y")
     assert_close(to_host64(last), lr, "f32", "last_state")
@@ -209,19 +214,18 @@ def test_each_kernel_short_sequences(kernel, L, monkeypatch):
 @pytest.mark.parametrize("kernel", ["tpar", "wave"])
 @pytest.mark.parametrize("N", [1, 5, 8, 16])
 @pytest.mark.parametrize("mode", ["zoh", "euler"])
-def test_time_parallel_state_sizes_and_chunks(kernel, N, mode, monkeypatch):
+def test_time_parallel_state_sizes_and_chunks(kernel, N, mode):
     """The time-parallel kernels (lanes hold tokens, pairs combined by a wave
     scan; across waves through LDS, or four tokens per lane composed in the
     lane; a carry between 256-token chunks): state sizes below 16 (element
     loads), several chunks with a ragged last one, a zero and a slow channel
     (the careful ZOH form beside the g form)."""
-    monkeypatch.setenv("SSM66_SCAN_KERNEL", kernel)
     inp = W.scan_inputs(_cfg(2, 777, 5, N, "f32", True, seed=40 + N))
     A = inp["A"].copy()
     A[1, 0] = 0.0
     A[3, :] = -0.2
     inp["A"] = A
-    y, last = scan_gpu(inp, mode)
+    y, last = scan_gpu(inp, mode, kernel=kernel)
     yr, lr = scan_ref(inp, mode)
     assert_close(to_host64(y), yr, "f32", "y")
     assert_close(to_host64(last), lr, "f32", "last_state")
@@ -286,59 +290,3 @@ def test_tiny_config_full():
         yr, lr = scan_ref(inp, mode)
         assert_close(to_host64(y), yr, "f32", f"y {mode}")
         assert_close(to_host64(last), lr, "f32", f"last {mode}")
-
-
-def _sample_channels(dim, seed, k=12):
-    rng = np.random.default_rng(seed)
-    ch = {0, 1, 63, 64, dim // 2, dim - 65, dim - 1}
-    ch.update(int(c) for c in rng.choice(dim, size=k, replace=False))
-    return np.array(sorted(ch), dtype=np.int64)
-
-
-@pytest.mark.parametrize("name", ["mamba130m", "mamba1p4b", "longseq"])
-def test_full_size_sampled(name):
-    """Full-size launch (the benchmark's configuration); the oracle checks a sample
-    of channels over every batch entry and token, plus their final states."""
-    cfg = W.SCAN_CONFIGS[name]
-    print(f"[{name}] generating inputs", flush=True)
-    inp = W.scan_inputs(cfg)
-    ch = _sample_channels(cfg.dim, cfg.seed, k=6 if name == "longseq" else 12)
-    for mode in ("zoh", "euler"):
-        print(f"[{name}] launch {mode}", flush=True)
-        y, last = scan_gpu(inp, mode)
-        chd = torch.from_numpy(ch).to(DEV)
-        ys = to_host64(y.index_select(2, chd))
-        ls = to_host64(last.index_select(1, chd))
-        del y, last
-        sub = W.scan_inputs(cfg, channels=ch)
-        for k in ("u", "delta", "z"):
-            if sub[k] is not None:
-                assert np.array_equal(sub[k], inp[k][:, :, ch])
-        yr, lr = scan_ref(sub, mode)
-        e1 = assert_close(ys, yr, "bf16", f"{name} y {mode}")
-        e2 = assert_close(ls, lr, "bf16", f"{name} last_state {mode}")
-        print(f"[{name}] {mode}: rel-rms y {e1:.2e}, last_state {e2:.2e}", flush=True)
-        torch.cuda.empty_cache()
-
-
-@pytest.mark.parametrize("shape", [(1, 2048, 1024), (1, 2048, 1536), (1, 65536, 128)])
-def test_full_size_time_parallel_sampled(shape):
-    """The benchmark's time-parallel shapes at full size, with the library's own
-    kernel choice (the time-parallel scan for these few rows): sampled channels
-    over every token, and their final states, against the oracle."""
-    b, L, dim = shape
-    cfg = W.ScanConfig(f"narrow{b}x{L}x{dim}", b, L, dim, 16, "bf16", True, 7)
-    inp = W.scan_inputs(cfg)
-    ch = _sample_channels(dim, 7, k=6)
-    for mode in ("zoh", "euler"):
-        print(f"[{cfg.name}] launch {mode}", flush=True)
-        y, last = scan_gpu(inp, mode)
-        chd = torch.from_numpy(ch).to(DEV)
-        ys = to_host64(y.index_select(2, chd))
-        ls = to_host64(last.index_select(1, chd))
-        del y, last
-        sub = W.scan_inputs(cfg, channels=ch)
-        yr, lr = scan_ref(sub, mode)
-        e1 = assert_close(ys, yr, "bf16", f"{cfg.name} y {mode}")
-        e2 = assert_close(ls, lr, "bf16", f"{cfg.name} last_state {mode}")
-        print(f"[{cfg.name}] {mode}: rel-rms y {e1:.2e}, last_state {e2:.2e}", flush=True)

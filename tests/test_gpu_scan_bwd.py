@@ -192,14 +192,13 @@ def test_bwd_full_size_sampled():
 
 # ------------------------------------------------- the training forward's checkpoints
 
-@pytest.mark.parametrize("kernel", ["lds1", "lds2", "lds4", "tpar", "wave"])
+@pytest.mark.parametrize("kernel", ["seq1", "seq2", "seq4", "tpar", "wave"])
 @pytest.mark.parametrize("mode", ["zoh", "euler"])
-def test_train_forward_checkpoints(kernel, mode, monkeypatch):
+def test_train_forward_checkpoints(kernel, mode):
     """scan_fwd_train gives scan_fwd's y and last_state bit for bit, and its
     checkpoint j is the state before token 16 j: the oracle's final state of
     the sequence cut there (j = 0: h0).  A ragged channel tile, a ragged last
     chunk, a zero and a slow channel (both ZOH forms)."""
-    monkeypatch.setenv("SSM66_SCAN_KERNEL", kernel)
     inp = W.scan_inputs(_cfg(2, 99, 34, 16, "f32", True, seed=110))
     A = inp["A"].copy()
     A[5, 2] = 0.0
@@ -210,8 +209,8 @@ def test_train_forward_checkpoints(kernel, mode, monkeypatch):
             to_dev(inp["B"], "f32"), to_dev(inp["C"], "f32"))
     kw = dict(D=to_dev(inp["D"], "f32"), z=to_dev(inp["z"], "f32"),
               delta_bias=to_dev(inp["delta_bias"], "f32"), dt_mode=mode, h0=to_dev(h0, "f32"))
-    y, last, ck = ssm.scan_fwd_train(*args, **kw)
-    y2, last2 = ssm.scan_fwd(*args, **kw)
+    y, last, ck = ssm.scan_fwd_train(*args, kernel=kernel, **kw)
+    y2, last2 = ssm.scan_fwd(*args, kernel=kernel, **kw)
     torch.cuda.synchronize()
     assert torch.equal(y, y2) and torch.equal(last, last2)
     ckh = to_host64(ck)
@@ -232,19 +231,17 @@ def test_train_forward_checkpoints(kernel, mode, monkeypatch):
 
 @pytest.mark.parametrize("kernel", [None, "tpar", "wave"])
 @pytest.mark.parametrize("N", [3, 8])
-def test_train_forward_checkpoints_small_state(kernel, N, monkeypatch):
+def test_train_forward_checkpoints_small_state(kernel, N):
     """State sizes below 16 (padded state groups in the sequential kernel,
     element loads in the time-parallel one), ZOH: checkpoints against the
     oracle, and the backward from them against the oracle's backward."""
-    if kernel:
-        monkeypatch.setenv("SSM66_SCAN_KERNEL", kernel)
     inp = W.scan_inputs(_cfg(2, 70, 20, N, "f32", True, seed=116 + N))
     dy = _dy((2, 70, 20), "f32", 117)
     args = (to_dev(inp["u"], "f32"), to_dev(inp["delta"], "f32"), to_dev(inp["A"], "f32"),
             to_dev(inp["B"], "f32"), to_dev(inp["C"], "f32"))
     kw = dict(D=to_dev(inp["D"], "f32"), z=to_dev(inp["z"], "f32"),
               delta_bias=to_dev(inp["delta_bias"], "f32"))
-    _, _, ck = ssm.scan_fwd_train(*args, **kw)
+    _, _, ck = ssm.scan_fwd_train(*args, kernel=kernel, **kw)
     g = ssm.scan_bwd(*args, to_dev(dy, "f32"), ckpt=ck, **kw)
     torch.cuda.synchronize()
     ckh = to_host64(ck)

@@ -12,7 +12,7 @@ import selective_state_space_66_amd as ssm
 pytestmark = pytest.mark.gpu
 
 # sequential kernels with G = 1, 2, 4 states per thread, and the time-parallel one
-KERNELS = ["lds1", "lds2", "lds4", "tpar", "wave"]
+KERNELS = ["seq1", "seq2", "seq4", "tpar", "wave"]
 BF16_NAN = np.uint16(0x7FC0)
 
 
@@ -20,13 +20,13 @@ def _cfg(batch, L, dim, N, io, gate, seed):
     return W.ScanConfig(f"x{batch}x{L}x{dim}x{N}", batch, L, dim, N, io, gate, seed)
 
 
-def _gpu(inp, mode, h0=None, seq_lens=None, reset=None, last_state=None):
+def _gpu(inp, mode, h0=None, seq_lens=None, reset=None, last_state=None, kernel=None):
     io = inp["io"]
     y, last = ssm.scan_fwd(
         to_dev(inp["u"], io), to_dev(inp["delta"], io), to_dev(inp["A"], "f32"),
         to_dev(inp["B"], io), to_dev(inp["C"], io), D=to_dev(inp["D"], "f32"),
         z=to_dev(inp["z"], io), delta_bias=to_dev(inp["delta_bias"], "f32"), dt_mode=mode,
-        h0=h0, seq_lens=seq_lens, reset=reset, last_state=last_state)
+        h0=h0, seq_lens=seq_lens, reset=reset, last_state=last_state, kernel=kernel)
     torch.cuda.synchronize()
     return y, last
 
@@ -64,21 +64,20 @@ def _poison_padding(inp, lens):
 @pytest.mark.parametrize("kernel", KERNELS)
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 @pytest.mark.parametrize("mode", ["zoh", "euler"])
-def test_chunked_prefill_with_initial_state(kernel, io, mode, monkeypatch):
+def test_chunked_prefill_with_initial_state(kernel, io, mode):
     """Prefill in two chunks, the second from the state the first returned,
     equals one scan over the whole sequence (the oracle's)."""
-    monkeypatch.setenv("SSM66_SCAN_KERNEL", kernel)
     inp = W.scan_inputs(_cfg(2, 150, 70, 16, io, True, seed=31))
     yr, lr = _ref(inp, mode)
     cut = 77  # inside a chunk for every chunk length
-    y1, l1 = _gpu(_cut(inp, 0, cut), mode)
-    y2, l2 = _gpu(_cut(inp, cut, 150), mode, h0=l1)
+    y1, l1 = _gpu(_cut(inp, 0, cut), mode, kernel=kernel)
+    y2, l2 = _gpu(_cut(inp, cut, 150), mode, h0=l1, kernel=kernel)
     y = torch.cat([y1, y2], dim=1)
     assert_close(to_host64(y), yr, io, "y")
     assert_close(to_host64(l2), lr, io, "last_state")
     # the same with the state advanced in place (last_state is h0)
-    _, st = _gpu(_cut(inp, 0, cut), mode)
-    y3, st2 = _gpu(_cut(inp, cut, 150), mode, h0=st, last_state=st)
+    _, st = _gpu(_cut(inp, 0, cut), mode, kernel=kernel)
+    y3, st2 = _gpu(_cut(inp, cut, 150), mode, h0=st, last_state=st, kernel=kernel)
     assert st2.data_ptr() == st.data_ptr()
     assert torch.equal(y3, y2) and torch.equal(st, l2)
 
@@ -101,16 +100,15 @@ def test_initial_state_small_A(mode):
 @pytest.mark.parametrize("kernel", KERNELS)
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 @pytest.mark.parametrize("mode", ["zoh", "euler"])
-def test_sequence_lengths(kernel, io, mode, monkeypatch):
+def test_sequence_lengths(kernel, io, mode):
     """Right padding: lengths at 0, 1, chunk boundaries, inside chunks and the
     full length; NaN in every padded input; y = 0 exactly on padding."""
-    monkeypatch.setenv("SSM66_SCAN_KERNEL", kernel)
     lens = [0, 1, 31, 32, 64, 97, 130, 130]
     inp = W.scan_inputs(_cfg(len(lens), 130, 70, 16, io, True, seed=33))
     inp = _poison_padding(inp, lens)
     h0 = np.random.default_rng(4).normal(size=(len(lens), 70, 16)).astype(np.float32)
     sl = torch.tensor(lens, dtype=torch.int32, device=DEV)
-    y, last = _gpu(inp, mode, h0=to_dev(h0, "f32"), seq_lens=sl)
+    y, last = _gpu(inp, mode, h0=to_dev(h0, "f32"), seq_lens=sl, kernel=kernel)
     yr, lr = _ref(inp, mode, h0=h0.astype(np.float64), seq_lens=lens)
     yg = to_host64(y)
     for b, l in enumerate(lens):
@@ -122,10 +120,9 @@ def test_sequence_lengths(kernel, io, mode, monkeypatch):
 @pytest.mark.parametrize("kernel", KERNELS)
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 @pytest.mark.parametrize("mode", ["zoh", "euler"])
-def test_document_resets(kernel, io, mode, monkeypatch):
+def test_document_resets(kernel, io, mode):
     """Resets at t = 0, inside full chunks, at chunk starts and in the ragged
     last chunk, with a non-zero h0 (discarded where t = 0 is flagged)."""
-    monkeypatch.setenv("SSM66_SCAN_KERNEL", kernel)
     L = 150
     inp = W.scan_inputs(_cfg(3, L, 70, 16, io, True, seed=34))
     reset = np.zeros((3, L), dtype=np.uint8)
@@ -133,7 +130,7 @@ def test_document_resets(kernel, io, mode, monkeypatch):
     reset[1, [7, 128, 140]] = 1
     h0 = np.random.default_rng(5).normal(size=(3, 70, 16)).astype(np.float32)
     y, last = _gpu(inp, mode, h0=to_dev(h0, "f32"),
-                   reset=torch.from_numpy(reset).to(DEV).bool())
+                   reset=torch.from_numpy(reset).to(DEV).bool(), kernel=kernel)
     yr, lr = _ref(inp, mode, h0=h0.astype(np.float64), reset=reset)
     assert_close(to_host64(y), yr, io, "y")
     assert_close(to_host64(last), lr, io, "last_state")

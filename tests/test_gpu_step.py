@@ -108,36 +108,3 @@ def test_prefill_then_decode_on_gpu(mode):
             z=to_dev(inp["z"][:, t], "bf16"), delta_bias=bd, dt_mode=mode)))
     assert_close(np.stack(ys, axis=1), yr[:, L1:], "bf16", "decoded y")
     assert_close(to_host64(st), lr, "bf16", "final state")
-
-
-def _sample(dim, seed):
-    rng = np.random.default_rng(seed)
-    return np.array(sorted({0, 63, 64, dim - 1, *rng.choice(dim, 8, replace=False).tolist()}),
-                    dtype=np.int64)
-
-
-def test_decode_config_full_size():
-    """The decode workload at full size (256 x 5120, N = 16) for 100 steps."""
-    cfg = W.STEP_CONFIGS["decode"]
-    ch = _sample(cfg.dim, 4)
-    checks = {1, 10, 100}
-    print("[decode] full size, 100 steps", flush=True)
-    got, gst = _run_steps_gpu(cfg, 100, checks, ch)
-    ref, rst = _run_steps_ref(cfg, 100, checks, ch)
-    for s in sorted(checks):
-        assert_close(got[s], ref[s], "bf16", f"y step {s}")
-    assert_close(gst, rst, "bf16", "state")
-
-
-def test_decode_thousand_steps():
-    """1000 consecutive steps (the decode workload's length) on 16 of its 256 sequences."""
-    full = W.STEP_CONFIGS["decode"]
-    cfg = W.StepConfig("decode16", 16, full.dim, full.N, full.io, True, full.seed, 1000)
-    ch = _sample(cfg.dim, 5)
-    checks = {1, 10, 100, 1000}
-    print("[decode] 16 sequences, 1000 steps", flush=True)
-    got, gst = _run_steps_gpu(cfg, 1000, checks, ch)
-    ref, rst = _run_steps_ref(cfg, 1000, checks, ch)
-    for s in sorted(checks):
-        assert_close(got[s], ref[s], "bf16", f"y step {s}")
-    assert_close(gst, rst, "bf16", "state")

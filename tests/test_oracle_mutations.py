@@ -31,7 +31,8 @@ MUTATIONS = {
                          "    double out = acc;\n    if (j->z) {\n      const double zz = j->z[xi];\n      out *= zz * oracle_sigmoid(zz);\n    }\n    out += dskip * x;"),
     "decay_sign": ("  *abar = exp(kappa);", "  *abar = exp(-kappa);"),
     "sigmoid_sign": ("if (v >= 0.0) return 1.0 / (1.0 + exp(-v));", "if (v >= 0.0) return 1.0 / (1.0 + exp(v));"),
-    "step_drops_state": ("        h[n] = abar * h[n] + bbar * x;", "        h[n] = bbar * x;"),
+    "step_drops_state": ("      h[n] = abar * h[n] + bbar * x;\n      acc += j->C[b * N + n] * h[n];",
+                         "      h[n] = bbar * x;\n      acc += j->C[b * N + n] * h[n];"),
     "padding_off_by_one": ("    if (t >= len) { /* padding: no output, state kept */",
                            "    if (t > len) { /* padding: no output, state kept */"),
     "padding_updates_state": ("      j->y[xi] = 0.0;\n      continue;", "      j->y[xi] = 0.0;"),

@@ -80,8 +80,14 @@ def _pool():
     if _POOL is None:
         import concurrent.futures
         import os
-        n = min(16, os.cpu_count() or 1)
-        _POOL = concurrent.futures.ThreadPoolExecutor(max_workers=n)
+        try:
+            n = len(os.sched_getaffinity(0))
+        except (AttributeError, OSError):
+            n = os.cpu_count() or 1
+        omp = os.environ.get("OMP_NUM_THREADS", "")
+        if omp.isdigit() and int(omp) > 0:
+            n = min(n, int(omp))
+        _POOL = concurrent.futures.ThreadPoolExecutor(max_workers=max(1, min(16, n)))
     return _POOL
 
 
@@ -243,6 +249,12 @@ def step_inputs(cfg: StepConfig, step: int, channels: Optional[Sequence[int]] = 
         C=_io(normal(cfg.seed, base + S_C, bn), cfg.io),
         z=_io(normal(cfg.seed, base + S_Z, idx), cfg.io) if cfg.gate else None,
         channels=ch, io=cfg.io)
+
+
+def step_inputs_range(cfg: StepConfig, s0: int, s1: int) -> list:
+    """step_inputs for steps s0 .. s1 - 1 (all channels), generated in parallel
+    on the host threads; the same values as one call per step."""
+    return list(_pool().map(lambda s: step_inputs(cfg, s), range(s0, s1)))
 
 
 def as_f64(x: Optional[np.ndarray], io: str) -> Optional[np.ndarray]:
