@@ -69,7 +69,8 @@
  *     work and return; nothing is synchronised.  On any error status nothing
  *     has been enqueued, except SSM_ERR_HIP, which reports a failed launch.
  *     Faults inside a kernel surface at the caller's next synchronisation.
- *   - Thread-safe: no mutable global state.
+ *   - Thread-safe.  The only mutable global state is the per-device address
+ *     of ssm_scan_bwd_noalloc's static scratch, set once under a lock.
  */
 #ifndef SSM66_H
 #define SSM66_H
@@ -259,6 +260,33 @@ int ssm_scan_bwd_ex(const void* u, const void* delta, const float* A, const void
                     void* dC, float* dD, void* dz, float* ddelta_bias, float* dh0,
                     const float* ckpt, void* workspace, size_t workspace_bytes, int64_t batch,
                     int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype, void* stream);
+
+/* size of the static device scratch behind ssm_scan_bwd_noalloc (64 MiB) */
+#define SSM_NOALLOC_SCRATCH_BYTES 67108864
+
+/*
+ * ssm_scan_bwd_ex for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments without workspace and workspace_bytes, the same kernels
+ * and the same results, with the workspace taken from a static array in
+ * device memory of SSM_NOALLOC_SCRATCH_BYTES.  The library calls no allocator
+ * for it: the array exists once per GPU it runs on and stays until the
+ * process ends.  Sizes whose ssm_scan_bwd_workspace_size exceeds the array
+ * return SSM_ERR_UNSUPPORTED before any HIP call.  Every call on one GPU
+ * shares that GPU's array (nothing in it needs to start at zero; it keeps the
+ * last call's partial sums): calls that overlap on one GPU -- on different
+ * streams, or from different threads without ordering -- race and give wrong
+ * results.  The first call on a device looks the array's address up on that
+ * device (SSM_ERR_HIP if the runtime cannot).  Returns SSM_OK or an error
+ * status as ssm_scan_bwd_ex.
+ */
+int ssm_scan_bwd_noalloc(const void* u, const void* delta, const float* A, const void* B,
+                         const void* C, const float* D, const void* z, const float* delta_bias,
+                         int softplus, int dt_mode, const float* h0, const void* dy,
+                         const float* dlast_state, void* du, void* ddelta, float* dA, void* dB,
+                         void* dC, float* dD, void* dz, float* ddelta_bias, float* dh0,
+                         const float* ckpt, int64_t batch, int64_t seqlen, int64_t dim,
+                         int64_t dstate, int io_dtype, void* stream);
 
 /*
  * One decode step against the state cache `state` (batch, dim, dstate),

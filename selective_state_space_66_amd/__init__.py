@@ -68,6 +68,8 @@ def load_library():
     lib.ssm_scan_bwd_ex.restype = ci
     lib.ssm_scan_bwd_ex.argtypes = [vp] * 8 + [ci, ci] + [vp] * 14 + [ctypes.c_size_t] + \
         [i64] * 4 + [ci, vp]
+    lib.ssm_scan_bwd_noalloc.restype = ci
+    lib.ssm_scan_bwd_noalloc.argtypes = [vp] * 8 + [ci, ci] + [vp] * 13 + [i64] * 4 + [ci, vp]
     lib.ssm_scan_bwd.restype = ci
     lib.ssm_scan_bwd.argtypes = [vp] * 8 + [ci, ci] + [vp] * 13 + [ctypes.c_size_t] + \
         [i64] * 4 + [ci, vp]
@@ -305,7 +307,7 @@ def conv1d_step(window, x, weight, bias=None, silu=True, out=None):
 
 
 def scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, softplus=True,
-             dt_mode="zoh", h0=None, dlast=None, workspace=None, ckpt=None):
+             dt_mode="zoh", h0=None, dlast=None, workspace=None, ckpt=None, noalloc=False):
     """Gradients of scan_fwd on the GPU (states recomputed, not stored).
 
     dy: like u; dlast: optional (batch, dim, N) float32, the gradient of last_state.
@@ -314,6 +316,8 @@ def scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, softplus=Tr
     workspace: optional uint8 device tensor of at least scan_bwd_workspace_size() bytes.
     ckpt: optional checkpoints from scan_fwd_train on the same inputs and h0; the
     states are then recomputed from them, without a forward sweep.
+    noalloc: run ssm_scan_bwd_noalloc, whose workspace is the library's static
+    device scratch (no workspace tensor; sizes within its limit only).
     """
     import torch
     lib = load_library()
@@ -335,10 +339,14 @@ def scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, softplus=Tr
     _check(dlast, "dlast", (batch, dim, N), torch.float32, dev)
     _check(ckpt, "ckpt", (batch, (L + 15) // 16, dim, N), torch.float32, dev)
     need = scan_bwd_workspace_size(batch, L, dim, N)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-    if workspace.numel() < need:
-        raise ValueError(f"workspace: need {need} bytes, got {workspace.numel()}")
+    if noalloc:
+        if workspace is not None:
+            raise ValueError("noalloc takes no workspace")
+    else:
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        if workspace.numel() < need:
+            raise ValueError(f"workspace: need {need} bytes, got {workspace.numel()}")
     f32 = dict(dtype=torch.float32, device=dev)
     g = dict(du=torch.empty_like(u), ddelta=torch.empty_like(u),
              dB=torch.empty((batch, L, N), dtype=io, device=dev),
@@ -348,6 +356,17 @@ def scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, softplus=Tr
              dD=torch.empty((dim,), **f32) if D is not None else None,
              ddelta_bias=torch.empty((dim,), **f32) if delta_bias is not None else None,
              dh0=torch.empty((batch, dim, N), **f32) if h0 is not None else None)
+    if noalloc:
+        st = lib.ssm_scan_bwd_noalloc(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                                      _ptr(z), _ptr(delta_bias), int(bool(softplus)),
+                                      _MODES[dt_mode], _ptr(h0), _ptr(dy), _ptr(dlast),
+                                      _ptr(g["du"]), _ptr(g["ddelta"]), _ptr(g["dA"]),
+                                      _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dD"]), _ptr(g["dz"]),
+                                      _ptr(g["ddelta_bias"]), _ptr(g["dh0"]), _ptr(ckpt), batch,
+                                      L, dim, N, _io_code(u), _stream(dev))
+        if st != 0:
+            raise SsmError(st, "ssm_scan_bwd_noalloc")
+        return g
     st = lib.ssm_scan_bwd_ex(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
                              _ptr(delta_bias), int(bool(softplus)), _MODES[dt_mode], _ptr(h0),
                              _ptr(dy), _ptr(dlast), _ptr(g["du"]), _ptr(g["ddelta"]),

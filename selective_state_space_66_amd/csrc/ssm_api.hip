@@ -5,6 +5,8 @@
 // chooses a kernel instance and enqueues one launch on the caller's stream.
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/ssm66.h"
 #include "ssm_launch.h"
 
@@ -89,6 +91,36 @@ bool grid_fits(ScanKernel k, int64_t batch, int64_t dim) {
   const int64_t per = k == ScanKernel::kWave ? 8 : (k == ScanKernel::kTpar ? 1 : 16);
   const __int128 blocks = (__int128)batch * ((dim + per - 1) / per);
   return blocks <= 0x7fffffff;
+}
+
+// The backward pass's workspace for callers that cannot allocate
+// (ssm_scan_bwd_noalloc): a fixed array in device memory, one copy per GPU the
+// library runs on, held until the process ends.  Host code never passes the
+// array's name to a kernel (on the host it only stands for the symbol): each
+// device's address comes from hipGetSymbolAddress, once, with that device
+// current, and is kept here.
+constexpr size_t kScratchBytes = (size_t)SSM_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // per device; set once under g_scratch_mu
+
+// The current device's address of `scratch`: SSM_OK, or SSM_ERR_HIP if the
+// runtime cannot name the device or the symbol, SSM_ERR_UNSUPPORTED for a
+// device index past the table.
+int scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return SSM_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return SSM_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return SSM_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return SSM_OK;
 }
 
 }  // namespace
@@ -266,13 +298,16 @@ size_t ssm_scan_bwd_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, i
   return ssm66::scan_bwd_workspace_bytes(batch, seqlen, dim, dstate);
 }
 
-int ssm_scan_bwd_ex(const void* u, const void* delta, const float* A, const void* B,
-                    const void* C, const float* D, const void* z, const float* delta_bias,
-                    int softplus, int dt_mode, const float* h0, const void* dy,
-                    const float* dlast_state, void* du, void* ddelta, float* dA, void* dB,
-                    void* dC, float* dD, void* dz, float* ddelta_bias, float* dh0,
-                    const float* ckpt, void* workspace, size_t workspace_bytes, int64_t batch,
-                    int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype, void* stream) {
+// workspace == NULL with use_scratch: the library's static scratch (checked
+// against its size before any HIP call).
+static int scan_bwd_impl(const void* u, const void* delta, const float* A, const void* B,
+                         const void* C, const float* D, const void* z, const float* delta_bias,
+                         int softplus, int dt_mode, const float* h0, const void* dy,
+                         const float* dlast_state, void* du, void* ddelta, float* dA, void* dB,
+                         void* dC, float* dD, void* dz, float* ddelta_bias, float* dh0,
+                         const float* ckpt, void* workspace, size_t workspace_bytes,
+                         bool use_scratch, int64_t batch, int64_t seqlen, int64_t dim,
+                         int64_t dstate, int io_dtype, void* stream) {
   int st = check_common(batch, seqlen, dim, dstate, io_dtype, softplus, dt_mode);
   if (st != SSM_OK) return st;
   if (batch == 0 || dim == 0) return SSM_OK;
@@ -281,9 +316,13 @@ int ssm_scan_bwd_ex(const void* u, const void* delta, const float* A, const void
   if (has_tokens && (!u || !delta || !B || !C || !dy || !du || !ddelta || !dB || !dC))
     return SSM_ERR_NULL;
   if (z && !dz) return SSM_ERR_NULL;  // the gate's gradient is part of the result
-  if (!workspace) return SSM_ERR_NULL;
-  if (workspace_bytes < ssm66::scan_bwd_workspace_bytes(batch, seqlen, dim, dstate))
-    return SSM_ERR_SHAPE;
+  const size_t need = ssm66::scan_bwd_workspace_bytes(batch, seqlen, dim, dstate);
+  if (use_scratch) {
+    if (need > kScratchBytes) return SSM_ERR_UNSUPPORTED;
+  } else {
+    if (!workspace) return SSM_ERR_NULL;
+    if (workspace_bytes < need) return SSM_ERR_SHAPE;
+  }
   const size_t es = io_dtype == SSM_BF16 ? 2 : 4;
   const void* io_ptrs[11] = {u, delta, B, C, z, dy, du, ddelta, dB, dC, dz};
   for (const void* q : io_ptrs)
@@ -292,8 +331,12 @@ int ssm_scan_bwd_ex(const void* u, const void* delta, const float* A, const void
                               ckpt, workspace};
   for (const void* q : f32_ptrs)
     if (q && !aligned(q, 4)) return SSM_ERR_ALIGN;
-  if (!aligned(workspace, 256)) return SSM_ERR_ALIGN;
+  if (workspace && !aligned(workspace, 256)) return SSM_ERR_ALIGN;
   if (batch * ((dim + 15) / 16) > 0x7fffffff) return SSM_ERR_UNSUPPORTED;
+  if (use_scratch) {  // validation is done: the first HIP call
+    st = scratch_address(&workspace);
+    if (st != SSM_OK) return st;
+  }
 
   ssm66::ScanBwdParams p;
   p.u = u; p.delta = delta; p.B = B; p.C = C; p.z = z; p.dy = dy;
@@ -306,6 +349,31 @@ int ssm_scan_bwd_ex(const void* u, const void* delta, const float* A, const void
   const hipError_t e = ssm66::launch_scan_bwd(p, io_dtype, dt_mode == SSM_DT_ZOH, z != nullptr,
                                               (hipStream_t)stream);
   return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
+int ssm_scan_bwd_ex(const void* u, const void* delta, const float* A, const void* B,
+                    const void* C, const float* D, const void* z, const float* delta_bias,
+                    int softplus, int dt_mode, const float* h0, const void* dy,
+                    const float* dlast_state, void* du, void* ddelta, float* dA, void* dB,
+                    void* dC, float* dD, void* dz, float* ddelta_bias, float* dh0,
+                    const float* ckpt, void* workspace, size_t workspace_bytes, int64_t batch,
+                    int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype, void* stream) {
+  return scan_bwd_impl(u, delta, A, B, C, D, z, delta_bias, softplus, dt_mode, h0, dy,
+                       dlast_state, du, ddelta, dA, dB, dC, dD, dz, ddelta_bias, dh0, ckpt,
+                       workspace, workspace_bytes, false, batch, seqlen, dim, dstate, io_dtype,
+                       stream);
+}
+
+int ssm_scan_bwd_noalloc(const void* u, const void* delta, const float* A, const void* B,
+                         const void* C, const float* D, const void* z, const float* delta_bias,
+                         int softplus, int dt_mode, const float* h0, const void* dy,
+                         const float* dlast_state, void* du, void* ddelta, float* dA, void* dB,
+                         void* dC, float* dD, void* dz, float* ddelta_bias, float* dh0,
+                         const float* ckpt, int64_t batch, int64_t seqlen, int64_t dim,
+                         int64_t dstate, int io_dtype, void* stream) {
+  return scan_bwd_impl(u, delta, A, B, C, D, z, delta_bias, softplus, dt_mode, h0, dy,
+                       dlast_state, du, ddelta, dA, dB, dC, dD, dz, ddelta_bias, dh0, ckpt,
+                       nullptr, 0, true, batch, seqlen, dim, dstate, io_dtype, stream);
 }
 
 int ssm_scan_bwd(const void* u, const void* delta, const float* A, const void* B, const void* C,

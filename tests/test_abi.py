@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol(lib):
                           "ssm_scan_bwd_workspace_size", "ssm_step", "ssm_ssd_fwd",
                           "ssm_conv1d_fwd", "ssm_conv1d_step", "ssm_status_string",
                           "ssm_abi_version", "ssm_scan_kernel_name", "ssm_scan_fwd_kernel",
-                          "ssm_alu_probe"}
+                          "ssm_alu_probe", "ssm_scan_bwd_noalloc"}
     raw = ctypes.CDLL(ssm.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), f"{n} not exported"
@@ -341,3 +341,27 @@ def test_ssd_invalid_arguments_are_rejected(lib):
     assert _ssd(lib, x=OFF8) == c["SSM_ERR_ALIGN"]        # 16-byte vectors
     assert _ssd(lib, B=OFF8) == c["SSM_ERR_ALIGN"]
     assert _ssd(lib, batch=0) == c["SSM_OK"]
+
+
+def test_noalloc_backward_validation(lib):
+    """ssm_scan_bwd_noalloc refuses, before any HIP call, sizes whose workspace
+    exceeds its static scratch, and checks its arguments like ssm_scan_bwd_ex."""
+    c = _header_constants()
+    limit = c["SSM_NOALLOC_SCRATCH_BYTES"]
+    assert limit == 64 << 20
+
+    def call(batch, L, dim, N, **kw):
+        a = dict(u=FAKE, A=FAKE, dy=FAKE, out=FAKE, dA=FAKE, io=1)
+        a.update(kw)
+        return lib.ssm_scan_bwd_noalloc(a["u"], a["u"], a["A"], a["u"], a["u"], None, None, None,
+                                        1, 0, None, a["dy"], None, a["out"], a["out"], a["dA"],
+                                        a["out"], a["out"], None, None, None, None, None, batch,
+                                        L, dim, N, a["io"], None)
+
+    assert ssm.scan_bwd_workspace_size(4, 2048, 1536, 16) > limit
+    assert call(4, 2048, 1536, 16) == c["SSM_ERR_UNSUPPORTED"]
+    assert ssm.scan_bwd_workspace_size(1, 2048, 1536, 16) <= limit
+    assert call(1, 2048, 1536, 16, dy=None) == c["SSM_ERR_NULL"]
+    assert call(1, 2048, 1536, 16, u=MISALIGNED) == c["SSM_ERR_ALIGN"]
+    assert call(1, 2048, 1536, 17) == c["SSM_ERR_SHAPE"]
+    assert call(0, 2048, 1536, 16) == c["SSM_OK"]  # no rows: nothing to do, no HIP call
