@@ -24,7 +24,7 @@ roofline for the dominant kernel, and the fp64 CPU oracle timed on the host.
 
 For profilers (rocprofv3) a reduced mode runs a few launches of one kernel on
 one input set and prints no JSON:
-    python bench.py --only scan [--dt-mode zoh|euler] [--launches 3]
+    python bench.py --only scan [--dt-mode zoh|euler] [--launches 3] [--kernel wave]
     python bench.py --only decode [--launches 3]
     python bench.py --only conv [--launches 3]
     python bench.py --only ssd [--launches 3]
@@ -717,8 +717,9 @@ def cpu_baselines(inp1, threads):
     return out
 
 
-def profile_only(what, launches, dt_mode):
-    """A few launches of one kernel for an external profiler (no timing, no JSON)."""
+def profile_only(what, launches, dt_mode, kernel=None):
+    """A few launches of one kernel for an external profiler (no timing, no JSON);
+    kernel forces one scan kernel for `scan`."""
     import torch
     import selective_state_space_66_amd as ssm
     import workloads as W
@@ -735,7 +736,8 @@ def profile_only(what, launches, dt_mode):
         last = torch.empty(cfg.batch, cfg.dim, cfg.N, device=dev)
         for _ in range(launches):
             ssm.scan_fwd(s["u"], s["delta"], s["A"], s["B"], s["C"], D=s["D"], z=s["z"],
-                         delta_bias=s["delta_bias"], dt_mode=dt_mode, y=y, last_state=last)
+                         delta_bias=s["delta_bias"], dt_mode=dt_mode, y=y, last_state=last,
+                         kernel=kernel)
     elif what == "bwd":
         cfg = W.SCAN_CONFIGS["mamba130m"]
         s = upload_scan(W.scan_inputs(cfg), dev)
@@ -793,6 +795,8 @@ def main():
                     help="profiling mode: a few launches of one kernel, no JSON")
     ap.add_argument("--launches", type=int, default=3)
     ap.add_argument("--dt-mode", choices=["zoh", "euler"], default="zoh")
+    ap.add_argument("--kernel", default=None,
+                    help="profiling mode, scan: force one scan kernel (seq1, seq2, seq4, tpar, wave, wave8)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -805,7 +809,7 @@ def main():
     import workloads as W
     ssm.load_library()  # fail loudly if the HIP library is missing
     if args.only:
-        profile_only(args.only, args.launches, args.dt_mode)
+        profile_only(args.only, args.launches, args.dt_mode, args.kernel)
         return
     dev = torch.device("cuda:0")
 
