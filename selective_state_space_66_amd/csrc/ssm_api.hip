@@ -14,9 +14,12 @@ namespace {
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
-// a * b * c without int64 overflow; false on overflow
+// a * b * c for non-negative a, b, c without int64 overflow; false on
+// overflow (each partial product fits in 128 bits)
 bool mul3(int64_t a, int64_t b, int64_t c, int64_t* out) {
-  __int128 r = (__int128)a * b * c;
+  const __int128 ab = (__int128)a * b;
+  if (ab > INT64_MAX) return false;
+  const __int128 r = ab * c;
   if (r > INT64_MAX) return false;
   *out = (int64_t)r;
   return true;
@@ -73,8 +76,9 @@ void pick_scan_shape(int64_t batch, int64_t dim, int64_t dstate, int forced_g, i
 // Which scan kernel runs (see the crossovers above).
 enum class ScanKernel { kSequential, kTpar, kWave };
 
-// the time-parallel kernels address a 256-token chunk with 32-bit offsets
-bool tpar_fits(int64_t dim) { return 1024 * dim < 0xffffffffLL; }
+// the time-parallel kernels address a 256-token chunk of up to 4-byte
+// elements with 32-bit offsets: 1024 dim < 2^32 - 1
+bool tpar_fits(int64_t dim) { return dim < ((int64_t)1 << 22); }
 
 ScanKernel pick_scan_kernel(int64_t batch, int64_t dim, int64_t L, int64_t dstate) {
   if (!tpar_fits(dim) || dstate > 16) return ScanKernel::kSequential;
@@ -167,7 +171,7 @@ static int scan_fwd_impl(int kernel, const void* u, const void* delta, const flo
   for (const void* q : f32_ptrs)
     if (q && !aligned(q, 4)) return SSM_ERR_ALIGN;
   // the sequential kernel's 32-bit lane offsets within a chunk (16 groups x dim)
-  if (16 * dim > 0x7fffffff) return SSM_ERR_UNSUPPORTED;
+  if (dim > 0x7fffffff / 16) return SSM_ERR_UNSUPPORTED;
 
   ScanKernel kern = ScanKernel::kSequential;
   int forced_g = 0;
@@ -396,9 +400,9 @@ int ssm_ssd_fwd(const void* x, const float* dt, const float* A, const void* B, c
   if (io_dtype != SSM_F32 && io_dtype != SSM_BF16) return SSM_ERR_DTYPE;
   if (softplus != 0 && softplus != 1) return SSM_ERR_FLAG;
   if (dt_mode != SSM_DT_ZOH && dt_mode != SSM_DT_EULER) return SSM_ERR_FLAG;
-  int64_t tmp;
-  if (!mul3(batch, seqlen, nheads * headdim, &tmp) || !mul3(batch, seqlen, dstate, &tmp) ||
-      !mul3(batch, nheads * headdim, dstate, &tmp))
+  int64_t dim, tmp;
+  if (!mul3(nheads, headdim, 1, &dim) || !mul3(batch, seqlen, dim, &tmp) ||
+      !mul3(batch, seqlen, dstate, &tmp) || !mul3(batch, dim, dstate, &tmp))
     return SSM_ERR_SHAPE;
   if (batch == 0 || nheads == 0) return SSM_OK;
   if (!A) return SSM_ERR_NULL;
@@ -475,7 +479,7 @@ int ssm_conv1d_step(void* window, const void* x, const float* weight, const floa
   for (const void* q : io_ptrs)
     if (q && !aligned(q, es)) return SSM_ERR_ALIGN;
   if (!aligned(weight, 4) || (bias && !aligned(bias, 4))) return SSM_ERR_ALIGN;
-  if ((batch * dim + 255) / 256 > 0x7fffffff) return SSM_ERR_UNSUPPORTED;
+  if (batch * dim > (int64_t)0x7fffffff * 256) return SSM_ERR_UNSUPPORTED;
   bool vec4 = dim % 4 == 0;
   for (const void* q : io_ptrs)
     if (q && !aligned(q, 4 * es)) vec4 = false;
