@@ -697,13 +697,10 @@ __global__ __launch_bounds__(64 * kWW, 4) void scan_wave_kernel(
       const float w1v[4] = {w14.x, w14.y, w14.z, w14.w};
       const float cinv[4] = {cin4.x, cin4.y, cin4.z, cin4.w};
       float pa[kWT][4], pb[kWT][4];
-      float cv[kWT][4];
 #pragma unroll
       for (int i = 0; i < kWT; ++i) {
         const float4 bv4 = sm.b[q][i][lane];
-        const float4 cv4 = sm.c[q][i][lane];
         const float bv[4] = {bv4.x, bv4.y, bv4.z, bv4.w};
-        cv[i][0] = cv4.x; cv[i][1] = cv4.y; cv[i][2] = cv4.z; cv[i][3] = cv4.w;
         const float dx = FORM == 0 ? dl[i] * x[i] : 0.0f;  // Euler: Delta u, once per token
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -736,6 +733,13 @@ __global__ __launch_bounds__(64 * kWW, 4) void scan_wave_kernel(
 #pragma unroll
       for (int k = 0; k < 4; ++k) tb[k] = fmaf(ta[k], cinv[k], pb[kWT - 1][k]);  // lane 0: the carry enters
       pair_scan4_b(ta, tb);
+      // C is read after the scan, not held through it
+      float cv[kWT][4];
+#pragma unroll
+      for (int i = 0; i < kWT; ++i) {
+        const float4 cv4 = sm.c[q][i][lane];
+        cv[i][0] = cv4.x; cv[i][1] = cv4.y; cv[i][2] = cv4.z; cv[i][3] = cv4.w;
+      }
       float he[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -779,9 +783,12 @@ __global__ __launch_bounds__(64 * kWW, 4) void scan_wave_kernel(
     y_store(t0);
   }
 
+  // the carried value and its readout weight from LDS (1/A where g = A h is
+  // carried), so that no per-lane constant has to live through the loop
   if (cvalid && last_state && lane < N) {
     const float g = ((const float*)&sm.kq[w][lane / 4][0][2])[lane & 3];
-    last_state[(b * dim + c) * N + lane] = fast_l ? g * ca_l : g;
+    const float w1 = ((const float*)&sm.kq[w][lane / 4][0][1])[lane & 3];
+    last_state[(b * dim + c) * N + lane] = ((fast_mask >> lane) & 1) ? g * w1 : g;
   }
 }
 
