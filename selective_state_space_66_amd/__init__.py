@@ -471,7 +471,7 @@ def ssd_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, softplus=True, dt_mode
 
     x, z: (batch, L, nheads, headdim) bfloat16; dt: (batch, L, nheads) float32;
     A, D, dt_bias: (nheads,) float32; B, C: (batch, L, N) bfloat16;
-    h0: optional (batch, nheads, headdim, N) float32.  headdim 64, N 64 or 128.
+    h0: optional (batch, nheads, headdim, N) float32.  headdim a multiple of 16, N 64 or 128.
     Returns (y like x, last_state (batch, nheads, headdim, N) float32 or None).
     """
     import torch

@@ -19,9 +19,9 @@
 // accumulation on v_mfma_f32_16x16x32_bf16: lane l holds A[l%16][8(l/16)+j],
 // B[8(l/16)+j][l%16] (j = 0..7) and D[4(l/16)+i][l%16] (i = 0..3).
 //
-// Work split: a block owns 16 of a head's 64 channels (one MFMA tile) for one
-// batch entry and walks the chunks in order, so b * H * 4 blocks run at once
-// (768 for 8 x 24 heads: three per CU).  The block recomputes the chunk's
+// Work split: a block owns 16 of a head's P channels (one MFMA tile) for one
+// batch entry and walks the chunks in order, so b * H * P / 16 blocks run at
+// once (768 for 8 x 24 heads of 64: three per CU).  The block recomputes the chunk's
 // scores C B^T (they do not depend on the channel), and its 4 waves each take
 // one 16-token row block of them, of Y, and a quarter of the state's columns,
 // which stay in MFMA accumulators (fp32) for the whole sequence.
@@ -36,7 +36,7 @@
 // enters LDS: each wave reads the 16 C rows of its token block straight into
 // the operand registers (the same fragment serves C B^T and H C^T).
 //
-// Only P = 64 and N in {64, 128} with bf16 io are instantiated.
+// P may be any multiple of 16; N is 64 or 128; io is bf16.
 #include "ssm_device.h"
 #include "ssm_launch.h"
 
@@ -53,9 +53,7 @@ typedef __attribute__((ext_vector_type(8))) short i16x8;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr int kQ = 64;               // tokens per chunk
-constexpr int kP = 64;               // channels per head
-constexpr int kPS = 16;              // channels per block
-constexpr int kSlices = kP / kPS;    // blocks per (batch entry, head)
+constexpr int kPS = 16;              // channels per block (a head's P is a multiple of it)
 constexpr int kWaves = 4;
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -128,7 +126,7 @@ struct SSDArgs {
   const float *dt, *A, *D, *dt_bias, *h0;
   bf16_bits* y;
   float* last_state;
-  int64_t batch, L, nheads;
+  int64_t batch, L, nheads, P;
   int softplus;
 };
 
@@ -211,15 +209,16 @@ __global__ __launch_bounds__(256, 3) void ssd_fwd_kernel(const SSDArgs p) {
   constexpr int NTW = N / 16 / kWaves;     // state column tiles per wave
   constexpr int RB = kQ * N / 8 / 256;     // 16-byte pieces of B per thread
   static_assert(NTW >= 1 && RB >= 1, "N is 64 or 128");
-  const int64_t H = p.nheads, L = p.L, HP = H * kP;
+  const int64_t H = p.nheads, L = p.L, P = p.P, HP = H * P;
+  const int64_t nsl = P / kPS;  // blocks per (batch entry, head)
 
   // XCD-aware order: consecutive block ids go round-robin to the 8 XCDs, so
   // each XCD gets a contiguous run of (batch entry, head, slice) -- the blocks
   // of one batch entry share its B and C rows in that XCD's L2.
   const int64_t nblk = (int64_t)gridDim.x, bid = blockIdx.x;
   const int64_t logical = (nblk % 8 == 0) ? (bid % 8) * (nblk / 8) + bid / 8 : bid;
-  const int64_t bh = logical / kSlices;
-  const int q = (int)(logical - bh * kSlices);
+  const int64_t bh = logical / nsl;
+  const int64_t q = logical - bh * nsl;
   const int64_t b = bh / H, h = bh - b * H;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -228,11 +227,11 @@ __global__ __launch_bounds__(256, 3) void ssd_fwd_kernel(const SSDArgs p) {
   const float A = p.A[h];
   const float Dh = p.D ? p.D[h] : 0.0f;
   const float bias = p.dt_bias ? p.dt_bias[h] : 0.0f;
-  const int64_t ch0 = h * kP + q * kPS;      // first channel of the block in a row of x, z, y
+  const int64_t ch0 = h * P + q * kPS;      // first channel of the block in a row of x, z, y
 
   // ---- the state, as H^T tiles: wave w holds column tiles nt = w + 4 j;
   // lane value i is H[p = lr][n = 16 nt + 4 lk + i]
-  const int64_t hrow = ((b * H + h) * kP + q * kPS + lr) * N;
+  const int64_t hrow = ((b * H + h) * P + q * kPS + lr) * N;
   f32x4 Hacc[NTW];
 #pragma unroll
   for (int j = 0; j < NTW; ++j) {
@@ -420,7 +419,7 @@ __global__ __launch_bounds__(256, 3) void ssd_fwd_kernel(const SSDArgs p) {
 
 template <int N, bool ZOH, bool GATE>
 hipError_t ssd_launch(const SSDArgs& a, hipStream_t stream) {
-  const int64_t nblk = a.batch * a.nheads * kSlices;
+  const int64_t nblk = a.batch * a.nheads * (a.P / kPS);
   if (nblk > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL((ssd_fwd_kernel<N, ZOH, GATE>), dim3((unsigned)nblk), dim3(64 * kWaves), 0,
                      stream, a);
@@ -440,8 +439,8 @@ hipError_t launch_ssd_fwd(const SSDParams& q, bool zoh, bool gate, hipStream_t s
   a.x = (const bf16_bits*)q.x; a.B = (const bf16_bits*)q.B; a.C = (const bf16_bits*)q.C;
   a.z = (const bf16_bits*)q.z; a.dt = q.dt; a.A = q.A; a.D = q.D; a.dt_bias = q.dt_bias;
   a.h0 = q.h0; a.y = (bf16_bits*)q.y; a.last_state = q.last_state;
-  a.batch = q.batch; a.L = q.L; a.nheads = q.nheads; a.softplus = q.softplus;
-  if (q.P != kP) return hipErrorInvalidValue;
+  a.batch = q.batch; a.L = q.L; a.nheads = q.nheads; a.P = q.P; a.softplus = q.softplus;
+  if (q.P < kPS || q.P % kPS != 0) return hipErrorInvalidValue;
   if (q.N == 128) return ssd_modes<128>(a, zoh, gate, stream);
   if (q.N == 64) return ssd_modes<64>(a, zoh, gate, stream);
   return hipErrorInvalidValue;

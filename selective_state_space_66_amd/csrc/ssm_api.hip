@@ -407,8 +407,9 @@ int ssm_ssd_fwd(const void* x, const float* dt, const float* A, const void* B, c
   if (batch == 0 || nheads == 0) return SSM_OK;
   if (!A) return SSM_ERR_NULL;
   if (seqlen > 0 && (!x || !dt || !B || !C || !y)) return SSM_ERR_NULL;
-  // the MFMA kernel: bf16 operands, 64 channels per head, 64 or 128 states
-  if (io_dtype != SSM_BF16 || headdim != 64 || (dstate != 64 && dstate != 128))
+  // the MFMA kernel: bf16 operands, a multiple of 16 channels per head, 64 or
+  // 128 states
+  if (io_dtype != SSM_BF16 || headdim % 16 != 0 || (dstate != 64 && dstate != 128))
     return SSM_ERR_UNSUPPORTED;
   const void* v16[5] = {x, z, y, B, C};
   for (const void* q : v16)
@@ -416,7 +417,7 @@ int ssm_ssd_fwd(const void* x, const float* dt, const float* A, const void* B, c
   const void* f32_ptrs[7] = {dt, A, D, dt_bias, h0, last_state, nullptr};
   for (const void* q : f32_ptrs)
     if (q && !aligned(q, 4)) return SSM_ERR_ALIGN;
-  if (batch * nheads > 0x7fffffff / 4) return SSM_ERR_UNSUPPORTED;  // 4 blocks per head
+  if (batch * nheads > 0x7fffffff / (headdim / 16)) return SSM_ERR_UNSUPPORTED;  // P / 16 blocks per head
 
   ssm66::SSDParams p;
   p.x = x; p.B = B; p.C = C; p.z = z; p.dt = dt; p.A = A; p.D = D; p.dt_bias = dt_bias;

@@ -85,7 +85,7 @@ size_t scan_bwd_ckpt_bytes(int64_t batch, int64_t L, int64_t dim, int64_t N);
 size_t scan_bwd_workspace_bytes(int64_t batch, int64_t L, int64_t dim, int64_t N);
 hipError_t launch_scan_bwd(const ScanBwdParams& p, int io_dtype, bool zoh, bool gate,
                            hipStream_t stream);
-// P == 64, N in {64, 128}, bf16 io; 16-byte aligned x, z, y, B, C.
+// P a multiple of 16, N in {64, 128}, bf16 io; 16-byte aligned x, z, y, B, C.
 // The time-parallel scan (lanes hold tokens; associative pair scan).
 hipError_t launch_scan_tpar(const ScanParams& p, int io_dtype, bool zoh, bool gate,
                             hipStream_t stream);

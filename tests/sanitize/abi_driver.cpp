@@ -124,7 +124,7 @@ int main() {
   EXPECT(ssd(P, -2, 8, 4, 64, 128, SSM_BF16), SSM_ERR_SHAPE);
   EXPECT(ssd(P, 2, 8, big, 64, 128, SSM_BF16), SSM_ERR_SHAPE);
   EXPECT(ssd(P, 2, 8, big / 32, 64, 128, SSM_BF16), SSM_ERR_SHAPE);
-  EXPECT(ssd(P, 2, 8, 4, 32, 128, SSM_BF16), SSM_ERR_UNSUPPORTED);
+  EXPECT(ssd(P, 2, 8, 4, 24, 128, SSM_BF16), SSM_ERR_UNSUPPORTED);
   EXPECT(ssd(M, 2, 8, 4, 64, 128, SSM_BF16), SSM_ERR_ALIGN);
   EXPECT(ssd(P, (int64_t)1 << 30, 1, 1 << 10, 64, 64, SSM_BF16), SSM_ERR_UNSUPPORTED);
 

@@ -15,8 +15,8 @@ import selective_state_space_66_amd as ssm
 pytestmark = pytest.mark.gpu
 
 
-def _cfg(batch, L, H, N, gate, seed):
-    return W.SSDConfig(f"s{batch}x{L}x{H}x{N}", batch, L, H, 64, N, "bf16", gate, seed)
+def _cfg(batch, L, H, N, gate, seed, P=64):
+    return W.SSDConfig(f"s{batch}x{L}x{H}x{P}x{N}", batch, L, H, P, N, "bf16", gate, seed)
 
 
 def _gpu(inp, mode, softplus=True, h0=None, use_D=True):
@@ -51,6 +51,21 @@ def test_ssd_ragged(N, mode, gate):
     e1 = assert_close(to_host64(y), yr, "bf16", "y")
     e2 = assert_close(to_host64(last), lr, "bf16", "last_state")
     print(f"N={N} {mode} gate={gate}: y {e1:.2e} last {e2:.2e}", flush=True)
+
+
+@pytest.mark.parametrize("P", [16, 32, 48, 128])
+@pytest.mark.parametrize("N", [64, 128])
+@pytest.mark.parametrize("mode", ["euler", "zoh"])
+def test_ssd_head_sizes(P, N, mode):
+    """Heads of 16, 32, 48 and 128 channels (one to eight 16-channel blocks per
+    head), three chunks with a ragged last one, an initial state, the gate."""
+    inp = W.ssd_inputs(_cfg(2, 150, 3, N, True, seed=120 + P, P=P))
+    h0 = np.random.default_rng(121 + P).normal(size=(2, 3, P, N)).astype(np.float32)
+    y, last = _gpu(inp, mode, h0=h0)
+    yr, lr = _ref(inp, mode, h0=h0)
+    assert y.shape == (2, 150, 3, P) and last.shape == (2, 3, P, N)
+    assert_close(to_host64(y), yr, "bf16", f"y P={P}")
+    assert_close(to_host64(last), lr, "bf16", f"last_state P={P}")
 
 
 @pytest.mark.parametrize("L", [1, 17, 64, 65, 200])
