@@ -313,8 +313,9 @@ int ssm_step(float* state, const void* u, const void* delta, const float* A, con
  * dstate) float32 (the scan's state layout).  D, z, dt_bias, h0, last_state
  * may be NULL.  The kernel runs on the matrix cores with bf16 operands and
  * fp32 accumulation and state: io_dtype must be SSM_BF16, headdim a multiple
- * of 16 and dstate 64 or 128 (else SSM_ERR_UNSUPPORTED); x, z, y, B, C must be
- * 16-byte aligned.  Returns SSM_OK or an error status.
+ * of 16, nheads * headdim at most 2^23 and dstate 64 or 128 (else
+ * SSM_ERR_UNSUPPORTED); x, z, y, B, C must be 16-byte aligned.  Returns SSM_OK
+ * or an error status.
  */
 int ssm_ssd_fwd(const void* x, const float* dt, const float* A, const void* B, const void* C,
                 const float* D, const void* z, const float* dt_bias, int softplus, int dt_mode,

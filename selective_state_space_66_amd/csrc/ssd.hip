@@ -33,8 +33,15 @@
 // each lane's four results are consecutive in the row-major layout the next
 // product reads, and every LDS write is 8 bytes; Y comes out as Y^T, four
 // consecutive channels of one token per lane, stored as 8 bytes.  C never
-// enters LDS: each wave reads the 16 C rows of its token block straight into
-// the operand registers (the same fragment serves C B^T and H C^T).
+// enters LDS: each wave reads the 16 C rows of its token block in whole
+// 128-byte row pieces and moves them into the operand registers with DPP row
+// shifts (the same fragment serves C B^T and H C^T).
+//
+// Memory operations: every chunk issues the same loads and the same store
+// (past the end the last chunk is read again; the output is a buffer store
+// whose range ends at row L), so each wait for the loads of a chunk, issued a
+// chunk ahead, counts a fixed number of later operations and waits for those
+// loads only.
 //
 // P may be any multiple of 16; N is 64 or 128; io is bf16.
 #include "ssm_device.h"
@@ -46,6 +53,7 @@ namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(8))) float f32x8;
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
 typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
 typedef __attribute__((ext_vector_type(4))) short i16x4;
@@ -55,6 +63,9 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 constexpr int kQ = 64;               // tokens per chunk
 constexpr int kPS = 16;              // channels per block (a head's P is a multiple of it)
 constexpr int kWaves = 4;
+// Word 3 of a raw buffer resource (no stride, no swizzle, 32-bit data format):
+// accesses at or past the range in word 2 read 0 and write nothing.
+constexpr int kBufferFlags = 0x00020000;
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -80,6 +91,13 @@ __device__ __forceinline__ bf16x8 tr_frag(const __bf16* base, int lane) {
   const i16x8 v = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
   return __builtin_bit_cast(bf16x8, v);
 }
+
+// The contractions over the states (C B^T and C H^T) take the N states in
+// k-steps of 32; within a k-step, lane group lk (lanes 16 lk .. 16 lk + 15)
+// holds the 8 states starting at kn(k, lk) = 64 (k / 2) + 16 lk + 8 (k % 2).
+// Any split that is the same for both operands gives the same sums; this one
+// lets C be read by whole 128-byte rows (see load_chunk).
+__device__ __forceinline__ constexpr int kn(int k, int lk) { return 64 * (k / 2) + 16 * lk + 8 * (k % 2); }
 
 // Per-token constants of one chunk, from its step sizes.
 struct ChunkConsts {
@@ -173,7 +191,7 @@ __device__ __forceinline__ void scores_times_x(const Sm& sm, int cur, const Chun
   for (int k = 0; k < N / 32; ++k)
 #pragma unroll
     for (int sb = 0; sb <= W; ++sb)
-      g[sb] = mfma16(*(const bf16x8*)&sm.Bs[cur][16 * sb + lr][32 * k + 8 * lk], as_bf16x8(cC[k]),
+      g[sb] = mfma16(*(const bf16x8*)&sm.Bs[cur][16 * sb + lr][kn(k, lk)], as_bf16x8(cC[k]),
                      g[sb]);
   const float ct = kc.cuml[16 * W + lr];
 #pragma unroll
@@ -246,39 +264,66 @@ __global__ __launch_bounds__(256, 3) void ssd_fwd_kernel(const SSDArgs p) {
   }
 
   // ---- global reads of one chunk into registers, addressed as a uniform
-  // chunk base plus 32-bit byte offsets; rows past L are clamped to the last
-  // row (finite data that the zero weights of padding tokens cancel).  Issued
-  // two chunks ahead of use, one chunk ahead of staging.
+  // chunk base plus 32-bit byte offsets that are the same for every full
+  // chunk; in a partial last chunk rows past L are clamped to the last row
+  // (finite data that the zero weights of padding tokens cancel).  Issued two
+  // chunks ahead of use, one chunk ahead of staging (C too: its registers
+  // are copied into the operand registers when the chunk is staged).
   u32x4 rB[RB], rC[NK];
   u32x2 rX, rZ = u32x2{0u, 0u};
   float rdt;
   const int tz = 16 * w + lr;   // token of this lane's C row, z and output
   const int tx = tid >> 2;      // token of this thread's x piece
+  const int sB = tid / (N / 8), cB8 = (tid % (N / 8)) * 8;  // first B piece: row, column
+  constexpr int kRowsPerPiece = 256 / (N / 8);                // B rows between pieces
+  const uint32_t offB = (uint32_t)(sB * N + cB8) * 2u;
+  // C: wave w reads the 16 rows of its token block as whole 128-byte pieces
+  // of rows: load j covers rows 16 w + 8 (j % 2) .. + 7, bytes 128 (j / 2) ..
+  // + 127 of each; lane (lk, m) takes row + m % 8, 16 bytes at 16 (2 lk + m / 8).
+  const int crow = 16 * w + (lr & 7), cpiece = 2 * lk + (lr >> 3);
+  const uint32_t offC = (uint32_t)(crow * N + 8 * cpiece) * 2u;
+  const uint32_t offZ = ((uint32_t)tz * (uint32_t)HP + 4 * lk) * 2u;
+  const uint32_t offX = ((uint32_t)tx * (uint32_t)HP + 4 * (tid & 3)) * 2u;
+  // dt is used by wave 0 only (one token per lane, 64 cache lines); the
+  // other waves issue the same load on one address, so that every wave keeps
+  // the same count of memory operations in flight
+  const uint32_t offD = w == 0 ? (uint32_t)lane * (uint32_t)H * 4u : 0u;
   auto load_chunk = [&](int64_t t0) {
-    const int lim = (int)(L - 1 - t0 < kQ - 1 ? L - 1 - t0 : kQ - 1);  // last row of the chunk
     const char* Bc = (const char*)(p.B + (b * L + t0) * N);
     const char* Cc = (const char*)(p.C + (b * L + t0) * N);
     const char* Xc = (const char*)(p.x + (b * L + t0) * HP + ch0);
     const char* Zc = (const char*)(p.z + (b * L + t0) * HP + ch0);
     const char* Dc = (const char*)(p.dt + (b * L + t0) * H + h);
-    {  // first, so that waiting for it does not wait for the rest
-      const uint32_t rd = (uint32_t)(lane < lim ? lane : lim);
-      rdt = *(const float*)(Dc + rd * (uint32_t)H * 4u);
-    }
+    if (t0 + kQ <= L) {
+      rdt = *(const float*)(Dc + offD);  // first, so that waiting for it does not wait for the rest
 #pragma unroll
-    for (int r = 0; r < RB; ++r) {
-      const int e = tid + 256 * r;
-      const int s = e / (N / 8), c8 = (e % (N / 8)) * 8;
-      const uint32_t off = (uint32_t)((s < lim ? s : lim) * N + c8) * 2u;
-      rB[r] = *(const u32x4*)(Bc + off);
-    }
-    const uint32_t rz = (uint32_t)(tz < lim ? tz : lim);
-    const uint32_t offc = (rz * N + 8 * lk) * 2u;
+      for (int r = 0; r < RB; ++r) {
+        const char* Bcr = Bc + r * kRowsPerPiece * N * 2;  // uniform: the offset stays 32-bit
+        rB[r] = *(const u32x4*)(Bcr + offB);
+      }
 #pragma unroll
-    for (int k = 0; k < NK; ++k) rC[k] = *(const u32x4*)(Cc + offc + 64 * k);
-    if constexpr (GATE) rZ = *(const u32x2*)(Zc + (rz * (uint32_t)HP + 4 * lk) * 2u);
-    const uint32_t rx = (uint32_t)(tx < lim ? tx : lim);
-    rX = *(const u32x2*)(Xc + (rx * (uint32_t)HP + 4 * (tid & 3)) * 2u);
+      for (int j = 0; j < NK; ++j)
+        rC[j] = *(const u32x4*)(Cc + (offC + (uint32_t)((8 * (j % 2) * N + 64 * (j / 2)) * 2)));
+      if constexpr (GATE) rZ = *(const u32x2*)(Zc + offZ);
+      rX = *(const u32x2*)(Xc + offX);
+    } else {
+      const int lim = (int)(L - 1 - t0);  // last row of the chunk, < kQ - 1
+      rdt = *(const float*)(Dc + (w == 0 ? (uint32_t)(lane < lim ? lane : lim) * (uint32_t)H * 4u : 0u));
+#pragma unroll
+      for (int r = 0; r < RB; ++r) {
+        const int sr = sB + r * kRowsPerPiece;
+        rB[r] = *(const u32x4*)(Bc + (uint32_t)((sr < lim ? sr : lim) * N + cB8) * 2u);
+      }
+      const uint32_t rz = (uint32_t)(tz < lim ? tz : lim);
+#pragma unroll
+      for (int j = 0; j < NK; ++j) {
+        const int cr = crow + 8 * (j % 2);
+        rC[j] = *(const u32x4*)(Cc + (uint32_t)((cr < lim ? cr : lim) * N + 8 * cpiece + 64 * (j / 2)) * 2u);
+      }
+      if constexpr (GATE) rZ = *(const u32x2*)(Zc + (rz * (uint32_t)HP + 4 * lk) * 2u);
+      const uint32_t rx = (uint32_t)(tx < lim ? tx : lim);
+      rX = *(const u32x2*)(Xc + (rx * (uint32_t)HP + 4 * (tid & 3)) * 2u);
+    }
   };
 
   // ---- step sizes, decays and weights of a chunk (wave 0, lane = token)
@@ -307,13 +352,26 @@ __global__ __launch_bounds__(256, 3) void ssd_fwd_kernel(const SSDArgs p) {
   auto stage = [&](int buf, int64_t t0) {
     const int nlive = (int)(L - t0 < kQ ? L - t0 : kQ);
 #pragma unroll
-    for (int r = 0; r < RB; ++r) {
-      const int e = tid + 256 * r;
-      *(u32x4*)&sm.Bs[buf][e / (N / 8)][(e % (N / 8)) * 8] = rB[r];
-    }
+    for (int r = 0; r < RB; ++r) *(u32x4*)&sm.Bs[buf][sB + r * kRowsPerPiece][cB8] = rB[r];
     *(u32x2*)&sm.Xs[buf][tx][4 * (tid & 3)] = tx < nlive ? rX : u32x2{0u, 0u};
+    // C into the operand layout (lane group lk, lane m = token 16 w + m,
+    // states kn(k, lk) ..): within each 16-lane row, the 8 lanes m >= 8 of the
+    // rows-0..7 load and the 8 lanes m < 8 of the rows-8..15 load trade places
+    // (DPP row shifts by 8 that write only half of each row).  The halves kept
+    // are first copied into new registers: were the shifts written over the
+    // loaded registers, the next chunk's loads would need other registers and
+    // the loop would end by moving them back, waiting there for those loads.
 #pragma unroll
-    for (int k = 0; k < NK; ++k) cC[k] = rC[k];
+    for (int h = 0; h < NK / 2; ++h)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r0 = (int)rC[2 * h][i], r1 = (int)rC[2 * h + 1][i];
+        int k0, k1;
+        asm("v_mov_b32 %0, %1" : "=v"(k0) : "v"(r0));
+        asm("v_mov_b32 %0, %1" : "=v"(k1) : "v"(r1));
+        cC[2 * h][i] = (uint32_t)__builtin_amdgcn_update_dpp(k0, r1, 0x118, 0xf, 0xc, false);
+        cC[2 * h + 1][i] = (uint32_t)__builtin_amdgcn_update_dpp(k1, r0, 0x108, 0xf, 0x3, false);
+      }
     if constexpr (GATE) {
       gz[0] = silu_f(lo_bf(rZ.x));
       gz[1] = silu_f(hi_bf(rZ.x));
@@ -323,16 +381,24 @@ __global__ __launch_bounds__(256, 3) void ssd_fwd_kernel(const SSDArgs p) {
     if (w == 0) chunk_consts(sm.cc[buf], rdt, nlive);
   };
 
-  // Per chunk, after the barrier that publishes its staging: Y^T from the
-  // state, the scores times x, the epilogue, the state update; then the next
-  // chunk is staged into the other buffers and the one after it is read.
   const int64_t nchunks = (L + kQ - 1) / kQ;
+  const int64_t tlast = (nchunks - 1) * kQ;  // first token of the last chunk
   if (nchunks > 0) {
     load_chunk(0);
     stage(0, 0);
-    if (nchunks > 1) load_chunk(kQ);
+    load_chunk(nchunks > 1 ? kQ : 0);
+    // a store that writes nothing (empty range), so that the loop is entered
+    // with the same memory operations in flight as each chunk leaves it
+    const __amdgpu_buffer_rsrc_t none =
+        __builtin_amdgcn_make_buffer_rsrc((void*)p.y, (short)0, 0, kBufferFlags);
+    __builtin_amdgcn_raw_buffer_store_b64(u32x2{0u, 0u}, none, (int)offZ, 0, 0);
   }
   lds_barrier();
+
+  // One chunk, after the barrier that publishes its staging: Y^T from the
+  // state, the scores times x, the epilogue, the state update; then the next
+  // chunk is staged into the other buffers, the one after it is read, and the
+  // chunk's output is stored.
   for (int64_t ck = 0; ck < nchunks; ++ck) {
     const int64_t t0 = ck * kQ;
     const int nlive = (int)(L - t0 < kQ ? L - t0 : kQ);
@@ -344,7 +410,7 @@ __global__ __launch_bounds__(256, 3) void ssd_fwd_kernel(const SSDArgs p) {
     f32x4 y = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int k = 0; k < NK; ++k)
-      y = mfma16(*(const bf16x8*)&sm.Hs[cur][lr][32 * k + 8 * lk], as_bf16x8(cC[k]), y);
+      y = mfma16(*(const bf16x8*)&sm.Hs[cur][lr][kn(k, lk)], as_bf16x8(cC[k]), y);
     {
       const float e = kc.et[tz];
 #pragma unroll
@@ -356,16 +422,16 @@ __global__ __launch_bounds__(256, 3) void ssd_fwd_kernel(const SSDArgs p) {
       case 2: scores_times_x<2, N>(sm, cur, kc, cC, lane, y); break;
       default: scores_times_x<3, N>(sm, cur, kc, cC, lane, y); break;
     }
-    // ---- epilogue: skip, gate, store 4 channels of token tz
-    if (tz < nlive) {
+    // ---- epilogue: skip, gate; 4 channels of token tz, stored at the end
+    // of the chunk
+    u32x2 yout;
+    {
       const u32x2 xv = *(const u32x2*)&sm.Xs[cur][tz][4 * lk];
       const float o0 = fmaf(Dh, lo_bf(xv.x), y[0]) * gz[0];
       const float o1 = fmaf(Dh, hi_bf(xv.x), y[1]) * gz[1];
       const float o2 = fmaf(Dh, lo_bf(xv.y), y[2]) * gz[2];
       const float o3 = fmaf(Dh, hi_bf(xv.y), y[3]) * gz[3];
-      char* Yc = (char*)(p.y + (b * L + t0) * HP + ch0);
-      *(u32x2*)(Yc + ((uint32_t)tz * (uint32_t)HP + 4 * lk) * 2u) =
-          u32x2{pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)};
+      yout = u32x2{pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)};
     }
 
     // ---- state update, H^T tiles: D[n][p] = exp(cum_Q) H^T[n][p]
@@ -379,12 +445,8 @@ __global__ __launch_bounds__(256, 3) void ssd_fwd_kernel(const SSDArgs p) {
 #pragma unroll
       for (int s0 = 0; s0 < kQ; s0 += 32) {
         const bf16x8 xt = tr_frag<kPS>(&sm.Xs[cur][s0][0], lane);  // x[s0 + 8 lk + j][lr]
-        const float4 e0 = *(const float4*)&kc.eend[s0 + 8 * lk];
-        const float4 e1 = *(const float4*)&kc.eend[s0 + 8 * lk + 4];
-        const float ev[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
-        bf16x8 xw;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) xw[j] = (__bf16)((float)xt[j] * ev[j]);
+        const f32x8 ev = *(const f32x8*)&kc.eend[s0 + 8 * lk];
+        const bf16x8 xw = __builtin_convertvector(__builtin_convertvector(xt, f32x8) * ev, bf16x8);
 #pragma unroll
         for (int j = 0; j < NTW; ++j) {
           const bf16x8 bt = tr_frag<Sm::BS>(&sm.Bs[cur][s0][16 * (w + kWaves * j)], lane);
@@ -399,10 +461,17 @@ __global__ __launch_bounds__(256, 3) void ssd_fwd_kernel(const SSDArgs p) {
     }
 
     // ---- the next chunk into the other buffers (last read in the previous
-    // chunk), and the reads of the one after it
-    if (ck + 1 < nchunks) {
-      stage(nxt, t0 + kQ);
-      if (ck + 2 < nchunks) load_chunk(t0 + 2 * kQ);
+    // chunk), the reads of the one after it, then this chunk's output.  All of
+    // it is issued on every chunk, so that each wait for a load counts a fixed
+    // number of later memory operations: past the end the staged buffers are
+    // never read and the last chunk is read again; the store is a buffer store
+    // whose range ends at row L, so the hardware drops the rows past it.
+    stage(nxt, t0 + kQ);
+    load_chunk(t0 + 2 * kQ < L ? t0 + 2 * kQ : tlast);
+    {
+      const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(p.y + (b * L + t0) * HP + ch0), (short)0, nlive * (int)HP * 2, kBufferFlags);
+      __builtin_amdgcn_raw_buffer_store_b64(yout, yr, (int)offZ, 0, 0);
     }
     lds_barrier();
   }

@@ -418,6 +418,7 @@ int ssm_ssd_fwd(const void* x, const float* dt, const float* A, const void* B, c
   for (const void* q : f32_ptrs)
     if (q && !aligned(q, 4)) return SSM_ERR_ALIGN;
   if (batch * nheads > 0x7fffffff / (headdim / 16)) return SSM_ERR_UNSUPPORTED;  // P / 16 blocks per head
+  if (dim > ((int64_t)1 << 23)) return SSM_ERR_UNSUPPORTED;  // a chunk's rows addressed in 32 bits
 
   ssm66::SSDParams p;
   p.x = x; p.B = B; p.C = C; p.z = z; p.dt = dt; p.A = A; p.D = D; p.dt_bias = dt_bias;

@@ -27,10 +27,12 @@ __device__ __forceinline__ void store_io(bf16_bits* p, float v) {
 }
 
 // two floats -> two bf16 (round to nearest even) in one word, a in the low half
+// (a two-element vector conversion: one v_cvt_pk_bf16_f32 instead of two
+// conversions, a shift and an or)
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  const uint32_t lo = __builtin_bit_cast(uint16_t, (__bf16)a);
-  const uint32_t hi = __builtin_bit_cast(uint16_t, (__bf16)b);
-  return lo | (hi << 16);
+  typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
 
 // Barrier for data exchanged through LDS only.  __syncthreads() also fences
