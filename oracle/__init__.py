@@ -73,7 +73,7 @@ def _load():
                                                            ctypes.c_void_p] + \
         [ctypes.c_int64] * 3 + [ctypes.c_int]
     lib.oracle_scan_bwd.restype = None
-    lib.oracle_scan_bwd.argtypes = [ctypes.c_void_p] * 9 + [ctypes.c_int, ctypes.c_int] + \
+    lib.oracle_scan_bwd.argtypes = [ctypes.c_void_p] * 11 + [ctypes.c_int, ctypes.c_int] + \
         [ctypes.c_void_p] * 11 + [ctypes.c_int64] * 4
     lib.oracle_ssd_fwd.restype = None
     lib.oracle_ssd_fwd.argtypes = [ctypes.c_void_p] * 9 + [ctypes.c_int, ctypes.c_int,
@@ -284,11 +284,13 @@ def conv1d_step(window, x, weight, bias=None, silu=True):
 
 
 def scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, softplus=True,
-             dt_mode="zoh", h0=None, dlast=None):
-    """Gradients of the fp64 scan: given dy (batch, L, dim) and optionally dlast
-    (batch, dim, N), the gradient of last_state, returns a dict with du, ddelta
-    (of the raw delta), dA, dB, dC and, where their inputs are given, dD, dz,
-    ddelta_bias and dh0 -- all float64.  Every state is kept (small cases only).
+             dt_mode="zoh", h0=None, dlast=None, seq_lens=None, reset=None):
+    """Gradients of the fp64 scan (scan_fwd, with h0, seq_lens and reset as
+    there): given dy (batch, L, dim) and optionally dlast (batch, dim, N), the
+    gradient of last_state, returns a dict with du, ddelta (of the raw delta),
+    dA, dB, dC and, where their inputs are given, dD, dz, ddelta_bias and dh0
+    -- all float64.  Padding tokens get zero gradients.  Every state is kept
+    (small cases only).
     """
     u, delta, A, B, C = _f64(u), _f64(delta), _f64(A), _f64(B), _f64(C)
     dy, D, z, delta_bias, h0, dlast = _f64(dy), _f64(D), _f64(z), _f64(delta_bias), _f64(h0), \
@@ -298,6 +300,10 @@ def scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, softplus=Tr
     assert dy.shape == u.shape and B.shape == (batch, L, N) and C.shape == (batch, L, N)
     assert dlast is None or dlast.shape == (batch, dim, N)
     assert h0 is None or h0.shape == (batch, dim, N)
+    sl = None if seq_lens is None else np.ascontiguousarray(seq_lens, dtype=np.int64)
+    rs = None if reset is None else np.ascontiguousarray(np.asarray(reset) != 0, dtype=np.uint8)
+    assert sl is None or sl.shape == (batch,)
+    assert rs is None or rs.shape == (batch, L)
     out = dict(du=np.empty_like(u), ddelta=np.empty_like(u), dA=np.empty((dim, N)),
                dB=np.empty((batch, L, N)), dC=np.empty((batch, L, N)))
     out["dD"] = np.empty(dim) if D is not None else None
@@ -305,8 +311,9 @@ def scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, softplus=Tr
     out["ddelta_bias"] = np.empty(dim) if delta_bias is not None else None
     out["dh0"] = np.empty((batch, dim, N)) if h0 is not None else None
     _load().oracle_scan_bwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
-                            _ptr(delta_bias), _ptr(h0), int(bool(softplus)), _MODES[dt_mode],
-                            _ptr(dy), _ptr(dlast), _ptr(out["du"]), _ptr(out["ddelta"]),
+                            _ptr(delta_bias), _ptr(h0), _ptr(sl), _ptr(rs), int(bool(softplus)),
+                            _MODES[dt_mode], _ptr(dy), _ptr(dlast), _ptr(out["du"]),
+                            _ptr(out["ddelta"]),
                             _ptr(out["dA"]), _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dD"]),
                             _ptr(out["dz"]), _ptr(out["ddelta_bias"]), _ptr(out["dh0"]),
                             batch, L, dim, N)

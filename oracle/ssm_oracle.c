@@ -389,6 +389,11 @@ void oracle_conv1d_step(double* window, const double* x, const double* w, const 
  *     draw_t = dDelta_t sigma(v_t) with softplus (the derivative of softplus),
  *              dDelta_t without;  dbias = sum_t draw_t
  *     dh0 = abar_0 g_0.
+ *   lengths and document starts (the forward of oracle_scan_fwd_ex): tokens
+ *   at or past len are padding -- no output, the state passes unchanged -- so
+ *   their gradients are zero and g passes through them unchanged; a document
+ *   starting at t computes h_t = bbar_t u_t (h_{t-1} taken as zero), so
+ *   dabar_t = 0 there and nothing of g reaches t - 1 (nor h0 before it).
  * phi' is taken from its series below |kappa| = 0.1 and from
  * (kappa e^kappa - expm1(kappa)) / kappa^2 above it.
  * ------------------------------------------------------------------------ */
@@ -409,7 +414,8 @@ static double phi_prime(double k) {
 
 void oracle_scan_bwd(const double* u, const double* delta, const double* A, const double* B,
                      const double* C, const double* D, const double* z,
-                     const double* delta_bias, const double* h0, int softplus, int dt_mode,
+                     const double* delta_bias, const double* h0, const int64_t* seq_lens,
+                     const uint8_t* reset, int softplus, int dt_mode,
                      const double* dy, const double* dlast, double* du, double* ddelta,
                      double* dA, double* dB, double* dC, double* dD, double* dz,
                      double* ddelta_bias, double* dh0, int64_t batch, int64_t L, int64_t dim,
@@ -427,28 +433,44 @@ void oracle_scan_bwd(const double* u, const double* delta, const double* A, cons
     for (int64_t c = 0; c < dim; ++c) {
       const double bias = delta_bias ? delta_bias[c] : 0.0;
       const double dskip = D ? D[c] : 0.0;
+      int64_t len = seq_lens ? seq_lens[b] : L; /* real tokens of this sequence */
+      if (len < 0) len = 0;
+      if (len > L) len = L;
       /* forward, keeping every state: hs[(t + 1) * N + n] = h_t */
       for (int64_t n = 0; n < N; ++n) hs[n] = h0 ? h0[(b * dim + c) * N + n] : 0.0;
       for (int64_t t = 0; t < L; ++t) {
         const int64_t xi = (b * L + t) * dim + c;
+        if (t >= len) { /* padding: the state passes unchanged */
+          for (int64_t n = 0; n < N; ++n) hs[(t + 1) * N + n] = hs[t * N + n];
+          continue;
+        }
+        const int doc_start = reset && reset[b * L + t];
         const double dt = step_size(delta[xi], bias, softplus);
         for (int64_t n = 0; n < N; ++n) {
           double abar, bbar;
           oracle_discretize(dt, A[c * N + n], B[(b * L + t) * N + n], dt_mode, &abar, &bbar);
-          hs[(t + 1) * N + n] = abar * hs[t * N + n] + bbar * u[xi];
+          const double prev = doc_start ? 0.0 : hs[t * N + n];
+          hs[(t + 1) * N + n] = abar * prev + bbar * u[xi];
         }
       }
       /* reverse */
       for (int64_t n = 0; n < N; ++n) g[n] = dlast ? dlast[(b * dim + c) * N + n] : 0.0;
       for (int64_t t = L - 1; t >= 0; --t) {
         const int64_t xi = (b * L + t) * dim + c;
+        if (t >= len) { /* padding: zero gradients, g passes through */
+          du[xi] = 0.0;
+          ddelta[xi] = 0.0;
+          if (z && dz) dz[xi] = 0.0;
+          continue;
+        }
+        const int doc_start = reset && reset[b * L + t];
         const double x = u[xi];
         const double v = delta[xi] + bias;
         const double dt = softplus ? oracle_softplus(v) : v;
         const double* Bt = B + (b * L + t) * N;
         const double* Ct = C + (b * L + t) * N;
         const double* ht = hs + (t + 1) * N;
-        const double* hp = hs + t * N;
+        const double* hp = hs + t * N; /* read as zero at a document start */
         double s = dskip * x;
         for (int64_t n = 0; n < N; ++n) s += Ct[n] * ht[n];
         double ds = dy[xi];
@@ -464,7 +486,7 @@ void oracle_scan_bwd(const double* u, const double* delta, const double* A, cons
           oracle_discretize(dt, a, Bt[n], dt_mode, &abar, &bbar);
           g[n] += ds * Ct[n];
           dC[(b * L + t) * N + n] += ds * ht[n];
-          const double dabar = g[n] * hp[n];
+          const double dabar = doc_start ? 0.0 : g[n] * hp[n];
           const double dbbar = g[n] * x;
           dx += g[n] * bbar;
           if (dt_mode == ORACLE_DT_ZOH) {
@@ -477,7 +499,7 @@ void oracle_scan_bwd(const double* u, const double* delta, const double* A, cons
             dA[c * N + n] += dabar * dt * abar;
             dB[(b * L + t) * N + n] += dbbar * dt;
           }
-          g[n] *= abar; /* carry to t - 1 */
+          g[n] = doc_start ? 0.0 : g[n] * abar; /* carry to t - 1 */
         }
         du[xi] = dx;
         if (dD) dD[c] += ds * x;

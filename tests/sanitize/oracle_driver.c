@@ -38,7 +38,8 @@ void oracle_conv1d_step(double* window, const double* x, const double* w, const 
                         int silu, double* out, int64_t batch, int64_t dim, int64_t k);
 void oracle_scan_bwd(const double* u, const double* delta, const double* A, const double* B,
                      const double* C, const double* D, const double* z,
-                     const double* delta_bias, const double* h0, int softplus, int dt_mode,
+                     const double* delta_bias, const double* h0, const int64_t* seq_lens,
+                     const uint8_t* reset, int softplus, int dt_mode,
                      const double* dy, const double* dlast, double* du, double* ddelta,
                      double* dA, double* dB, double* dC, double* dD, double* dz,
                      double* ddelta_bias, double* dh0, int64_t batch, int64_t L, int64_t dim,
@@ -100,8 +101,9 @@ int main(void) {
       double *dB = arr(batch * L * N), *dC = arr(batch * L * N), *dD = arr(dim);
       double *dz = arr(batch * L * dim), *dbias = arr(dim), *dh0 = arr(batch * dim * N);
       oracle_scan_bwd(u, dl, A, B, C, o ? D : NULL, o ? z : NULL, o ? bias : NULL, o ? h0 : NULL,
-                      1, mode, dy, o ? dlast : NULL, du, ddl, dA, dB, dC, o ? dD : NULL,
-                      o ? dz : NULL, o ? dbias : NULL, o ? dh0 : NULL, batch, L, dim, N);
+                      o ? lens : NULL, o ? reset : NULL, 1, mode, dy, o ? dlast : NULL, du, ddl,
+                      dA, dB, dC, o ? dD : NULL, o ? dz : NULL, o ? dbias : NULL,
+                      o ? dh0 : NULL, batch, L, dim, N);
 
       const int64_t k = 4;
       double *w = arr(dim * k), *win = arr(batch * (k - 1) * dim), *wout = arr(batch * (k - 1) * dim);

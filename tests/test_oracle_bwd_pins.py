@@ -84,6 +84,61 @@ def test_gradients_match_finite_differences(mode, gate, softplus, small_a):
         assert err < 1e-7, f"{out}: {err:.2e}"
 
 
+# lengths and document starts: (seq_lens, reset positions per sequence)
+VARLEN = [
+    ([7, 4], [[3], [2]]),        # a short sequence; one document start in each
+    ([7, 7], [[0, 5], []]),      # a start at token 0 discards h0
+    ([5, 0], [[1, 2], [0]]),     # two starts in a row; an empty sequence
+]
+
+
+@pytest.mark.parametrize("mode", ["zoh", "euler"])
+@pytest.mark.parametrize("lens,starts", VARLEN)
+def test_lengths_and_resets_match_finite_differences(mode, lens, starts):
+    """The loss through the forward with lengths and document starts (padding
+    outputs are the constant 0; a start forgets the state): every gradient,
+    h0's included, against central differences of that forward."""
+    p = _problem(gate=True)
+    batch, L, dim = p["u"].shape
+    N = p["A"].shape[1]
+    reset = np.zeros((batch, L), dtype=np.uint8)
+    for b, ts in enumerate(starts):
+        reset[b, ts] = 1
+    h0 = RNG.normal(size=(batch, dim, N))
+    dy = RNG.normal(size=(batch, L, dim))
+    dlast = RNG.normal(size=(batch, dim, N))
+    kw = dict(dt_mode=mode, seq_lens=np.array(lens), reset=reset)
+    g = oracle.scan_bwd(**p, dy=dy, h0=h0, dlast=dlast, **kw)
+    q = dict(p, h0=h0)
+    for inp, out in [("u", "du"), ("delta", "ddelta"), ("A", "dA"), ("B", "dB"), ("C", "dC"),
+                     ("D", "dD"), ("delta_bias", "ddelta_bias"), ("h0", "dh0"), ("z", "dz")]:
+        fd = _fd(q, inp, dy, dlast, **kw)
+        scale = 1.0 + np.abs(fd).max()
+        err = np.abs(g[out] - fd).max() / scale
+        assert err < 1e-7, f"{out}: {err:.2e}"
+    for b, n in enumerate(lens):  # padding tokens: exactly zero
+        for name in ("du", "ddelta", "dz"):
+            assert np.all(g[name][b, n:] == 0.0)
+        assert np.all(g["dB"][b, n:] == 0.0) and np.all(g["dC"][b, n:] == 0.0)
+
+
+def test_padding_equals_the_truncated_sequence():
+    """A sequence of length n padded to L has the gradients of the same
+    sequence cut to n tokens (the padding only passes dlast through)."""
+    p = _problem(gate=True, batch=1, L=9)
+    n = 5
+    h0 = RNG.normal(size=(1, 3, 4))
+    dy = RNG.normal(size=(1, 9, 3))
+    dlast = RNG.normal(size=(1, 3, 4))
+    g = oracle.scan_bwd(**p, dy=dy, h0=h0, dlast=dlast, seq_lens=np.array([n]))
+    cut = {k: (v[:, :n] if k in ("u", "delta", "B", "C", "z") else v) for k, v in p.items()}
+    gc = oracle.scan_bwd(**cut, dy=dy[:, :n], h0=h0, dlast=dlast)
+    for k in ("du", "ddelta", "dB", "dC", "dz"):
+        np.testing.assert_array_equal(g[k][:, :n], gc[k])
+    for k in ("dA", "dD", "ddelta_bias", "dh0"):
+        np.testing.assert_array_equal(g[k], gc[k])
+
+
 def test_gradient_of_last_state_alone():
     """With dy = 0 only the final state carries gradient: dC = 0, and du at the
     last token is B-weighted through bbar only."""

@@ -51,7 +51,16 @@ MUTATIONS = {
                                  "          const int64_t s = len - 1 - j;"),
     "conv_reset_ignored": ("        if (reset && reset[b * L + t]) start = t;", "        (void)reset;"),
     "conv_bias_dropped": ("        double pre = bias ? bias[c] : 0.0;", "        double pre = 0.0;"),
-    "bwd_no_carry": ("          g[n] *= abar; /* carry to t - 1 */", "          (void)0;"),
+    "bwd_no_carry": ("          g[n] = doc_start ? 0.0 : g[n] * abar; /* carry to t - 1 */",
+                     "          g[n] = doc_start ? 0.0 : g[n]; /* carry to t - 1 */"),
+    "bwd_carry_crosses_reset": ("          g[n] = doc_start ? 0.0 : g[n] * abar; /* carry to t - 1 */",
+                                "          g[n] *= abar; /* carry to t - 1 */"),
+    "bwd_reset_keeps_previous_state": ("          const double dabar = doc_start ? 0.0 : g[n] * hp[n];",
+                                       "          const double dabar = g[n] * hp[n];"),
+    "bwd_padding_has_gradients": ("        if (t >= len) { /* padding: zero gradients, g passes through */",
+                                  "        if (t >= L) { /* padding: zero gradients, g passes through */"),
+    "bwd_forward_ignores_reset": ("          const double prev = doc_start ? 0.0 : hs[t * N + n];",
+                                  "          const double prev = hs[t * N + n];"),
     "bwd_softplus_derivative": ("        const double dv = softplus ? ddt * oracle_sigmoid(v) : ddt;",
                                 "        const double dv = softplus ? ddt * oracle_sigmoid(-v) : ddt;"),
     "bwd_zoh_ddelta_as_euler": ("            ddt += dabar * a * abar + dbbar * abar * Bt[n];",
