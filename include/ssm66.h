@@ -82,7 +82,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 8
+#define SSM_ABI_VERSION 9
 
 /* status codes */
 #define SSM_OK 0
@@ -189,7 +189,8 @@ int ssm_scan_fwd_kernel(int kernel, const void* u, const void* delta, const floa
 size_t ssm_scan_bwd_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate);
 
 /*
- * Backward pass of ssm_scan_fwd / ssm_scan_fwd_ex without lengths or resets.
+ * Backward pass of ssm_scan_fwd / ssm_scan_fwd_ex without lengths or resets
+ * (ssm_scan_bwd_ex takes those).
  * Inputs: the forward's inputs (u, delta, A, B, C, D, z, delta_bias, softplus,
  * dt_mode, h0 -- D, z, delta_bias, h0 nullable), dy (batch, seqlen, dim) io
  * dtype, and dlast_state (batch, dim, dstate) float32, the gradient of
@@ -248,18 +249,29 @@ int ssm_scan_fwd_ckpt(const void* u, const void* delta, const float* A, const vo
                       int io_dtype, void* stream);
 
 /*
- * ssm_scan_bwd with the forward's checkpoints: ckpt (nullable) is what
- * ssm_scan_fwd_ckpt wrote for the same inputs and h0; with it the backward
- * skips its own forward sweep (the checkpoint part of the workspace is then
- * unused).  NULL makes it ssm_scan_bwd.  Returns SSM_OK or an error status.
+ * ssm_scan_bwd for the whole ssm_scan_fwd_ex: seq_lens (batch) int32 and
+ * reset (batch, seqlen) uint8, both nullable, mean what they mean there --
+ * tokens at or past a length are padding (their du, ddelta, dz and their rows
+ * of dB, dC come out zero; dlast_state reaches the last real token), and a
+ * document starting at t sees a zero state, so no gradient flows from t back
+ * to earlier tokens or to h0 ("Mamba and selective state spaces", "Why the
+ * scan must be fused": the backward pass is the forward's linear recurrence
+ * run in reverse, here with the forward's breaks).  ckpt (nullable) is what
+ * the forward wrote for the same inputs, h0, lengths and resets
+ * (ssm_scan_fwd_ckpt, or ssm_scan_fwd_kernel with a ckpt); with it the
+ * backward skips its own forward sweep (the checkpoint part of the workspace
+ * is then unused; checkpoints of chunks wholly in the padding are not read).
+ * With all three NULL it is ssm_scan_bwd.  seq_lens must be 4-byte aligned.
+ * Returns SSM_OK or an error status.
  */
 int ssm_scan_bwd_ex(const void* u, const void* delta, const float* A, const void* B,
                     const void* C, const float* D, const void* z, const float* delta_bias,
-                    int softplus, int dt_mode, const float* h0, const void* dy,
-                    const float* dlast_state, void* du, void* ddelta, float* dA, void* dB,
-                    void* dC, float* dD, void* dz, float* ddelta_bias, float* dh0,
-                    const float* ckpt, void* workspace, size_t workspace_bytes, int64_t batch,
-                    int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype, void* stream);
+                    int softplus, int dt_mode, const float* h0, const int32_t* seq_lens,
+                    const uint8_t* reset, const void* dy, const float* dlast_state, void* du,
+                    void* ddelta, float* dA, void* dB, void* dC, float* dD, void* dz,
+                    float* ddelta_bias, float* dh0, const float* ckpt, void* workspace,
+                    size_t workspace_bytes, int64_t batch, int64_t seqlen, int64_t dim,
+                    int64_t dstate, int io_dtype, void* stream);
 
 /* size of the static device scratch behind ssm_scan_bwd_noalloc (64 MiB) */
 #define SSM_NOALLOC_SCRATCH_BYTES 67108864
@@ -282,11 +294,12 @@ int ssm_scan_bwd_ex(const void* u, const void* delta, const float* A, const void
  */
 int ssm_scan_bwd_noalloc(const void* u, const void* delta, const float* A, const void* B,
                          const void* C, const float* D, const void* z, const float* delta_bias,
-                         int softplus, int dt_mode, const float* h0, const void* dy,
-                         const float* dlast_state, void* du, void* ddelta, float* dA, void* dB,
-                         void* dC, float* dD, void* dz, float* ddelta_bias, float* dh0,
-                         const float* ckpt, int64_t batch, int64_t seqlen, int64_t dim,
-                         int64_t dstate, int io_dtype, void* stream);
+                         int softplus, int dt_mode, const float* h0, const int32_t* seq_lens,
+                         const uint8_t* reset, const void* dy, const float* dlast_state,
+                         void* du, void* ddelta, float* dA, void* dB, void* dC, float* dD,
+                         void* dz, float* ddelta_bias, float* dh0, const float* ckpt,
+                         int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                         int io_dtype, void* stream);
 
 /*
  * One decode step against the state cache `state` (batch, dim, dstate),

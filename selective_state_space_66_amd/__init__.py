@@ -66,10 +66,10 @@ def load_library():
     lib.ssm_scan_fwd_ckpt.restype = ci
     lib.ssm_scan_fwd_ckpt.argtypes = [vp] * 8 + [ci, ci] + [vp] * 4 + [i64] * 4 + [ci, vp]
     lib.ssm_scan_bwd_ex.restype = ci
-    lib.ssm_scan_bwd_ex.argtypes = [vp] * 8 + [ci, ci] + [vp] * 14 + [ctypes.c_size_t] + \
+    lib.ssm_scan_bwd_ex.argtypes = [vp] * 8 + [ci, ci] + [vp] * 16 + [ctypes.c_size_t] + \
         [i64] * 4 + [ci, vp]
     lib.ssm_scan_bwd_noalloc.restype = ci
-    lib.ssm_scan_bwd_noalloc.argtypes = [vp] * 8 + [ci, ci] + [vp] * 13 + [i64] * 4 + [ci, vp]
+    lib.ssm_scan_bwd_noalloc.argtypes = [vp] * 8 + [ci, ci] + [vp] * 15 + [i64] * 4 + [ci, vp]
     lib.ssm_scan_bwd.restype = ci
     lib.ssm_scan_bwd.argtypes = [vp] * 8 + [ci, ci] + [vp] * 13 + [ctypes.c_size_t] + \
         [i64] * 4 + [ci, vp]
@@ -307,15 +307,19 @@ def conv1d_step(window, x, weight, bias=None, silu=True, out=None):
 
 
 def scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, softplus=True,
-             dt_mode="zoh", h0=None, dlast=None, workspace=None, ckpt=None, noalloc=False):
-    """Gradients of scan_fwd on the GPU (states recomputed, not stored).
+             dt_mode="zoh", h0=None, dlast=None, workspace=None, ckpt=None, noalloc=False,
+             seq_lens=None, reset=None):
+    """Gradients of scan_fwd / scan_fwd_ex on the GPU (states recomputed, not stored).
 
     dy: like u; dlast: optional (batch, dim, N) float32, the gradient of last_state.
+    seq_lens (batch,) int32 and reset (batch, L) uint8 or bool: as for scan_fwd_ex
+    (padding tokens get zero gradients; no gradient crosses a document start).
     Returns a dict: du, ddelta (of the raw delta), dB, dC (io dtype), dA (float32),
     and, where their inputs were given, dz (io dtype), dD, ddelta_bias, dh0 (float32).
     workspace: optional uint8 device tensor of at least scan_bwd_workspace_size() bytes.
-    ckpt: optional checkpoints from scan_fwd_train on the same inputs and h0; the
-    states are then recomputed from them, without a forward sweep.
+    ckpt: optional checkpoints from scan_fwd_train (or scan_fwd with kernel and
+    ckpt) on the same inputs, h0, lengths and resets; the states are then
+    recomputed from them, without a forward sweep.
     noalloc: run ssm_scan_bwd_noalloc, whose workspace is the library's static
     device scratch (no workspace tensor; sizes within its limit only).
     """
@@ -338,6 +342,11 @@ def scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, softplus=Tr
     _check(h0, "h0", (batch, dim, N), torch.float32, dev)
     _check(dlast, "dlast", (batch, dim, N), torch.float32, dev)
     _check(ckpt, "ckpt", (batch, (L + 15) // 16, dim, N), torch.float32, dev)
+    _check(seq_lens, "seq_lens", (batch,), torch.int32, dev)
+    if reset is not None:
+        if reset.dtype == torch.bool:
+            reset = reset.to(torch.uint8)
+        _check(reset, "reset", (batch, L), torch.uint8, dev)
     need = scan_bwd_workspace_size(batch, L, dim, N)
     if noalloc:
         if workspace is not None:
@@ -359,7 +368,8 @@ def scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, softplus=Tr
     if noalloc:
         st = lib.ssm_scan_bwd_noalloc(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
                                       _ptr(z), _ptr(delta_bias), int(bool(softplus)),
-                                      _MODES[dt_mode], _ptr(h0), _ptr(dy), _ptr(dlast),
+                                      _MODES[dt_mode], _ptr(h0), _ptr(seq_lens), _ptr(reset),
+                                      _ptr(dy), _ptr(dlast),
                                       _ptr(g["du"]), _ptr(g["ddelta"]), _ptr(g["dA"]),
                                       _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dD"]), _ptr(g["dz"]),
                                       _ptr(g["ddelta_bias"]), _ptr(g["dh0"]), _ptr(ckpt), batch,
@@ -369,7 +379,8 @@ def scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, softplus=Tr
         return g
     st = lib.ssm_scan_bwd_ex(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
                              _ptr(delta_bias), int(bool(softplus)), _MODES[dt_mode], _ptr(h0),
-                             _ptr(dy), _ptr(dlast), _ptr(g["du"]), _ptr(g["ddelta"]),
+                             _ptr(seq_lens), _ptr(reset), _ptr(dy), _ptr(dlast), _ptr(g["du"]),
+                             _ptr(g["ddelta"]),
                              _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dD"]),
                              _ptr(g["dz"]), _ptr(g["ddelta_bias"]), _ptr(g["dh0"]), _ptr(ckpt),
                              _ptr(workspace), workspace.numel(), batch, L, dim, N, _io_code(u),
@@ -408,9 +419,11 @@ def scan_ckpt_size(batch, L, dim, N):
 
 
 def scan_fwd_train(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True,
-                   dt_mode="zoh", h0=None, y=None, last_state=None, ckpt=None, kernel=None):
-    """The training forward: scan_fwd (with an optional h0) that also keeps the
-    state before every 16th token for scan_bwd.  kernel as for scan_fwd.
+                   dt_mode="zoh", h0=None, y=None, last_state=None, ckpt=None, kernel=None,
+                   seq_lens=None, reset=None):
+    """The training forward: scan_fwd (with optional h0, seq_lens and reset, as
+    there) that also keeps the state before every 16th token for scan_bwd.
+    kernel as for scan_fwd.
 
     Returns (y, last_state, ckpt); ckpt is (batch, ceil(L/16), dim, N) float32.
     """
@@ -442,10 +455,16 @@ def scan_fwd_train(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=
     if ckpt is None:
         ckpt = torch.empty((batch, (L + 15) // 16, dim, N), dtype=torch.float32, device=dev)
     _check(ckpt, "ckpt", (batch, (L + 15) // 16, dim, N), torch.float32, dev)
-    if kernel is not None:
-        st = lib.ssm_scan_fwd_kernel(SCAN_KERNELS[kernel], _ptr(u), _ptr(delta), _ptr(A), _ptr(B),
-                                     _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
-                                     int(bool(softplus)), _MODES[dt_mode], _ptr(h0), None, None,
+    _check(seq_lens, "seq_lens", (batch,), torch.int32, dev)
+    if reset is not None:
+        if reset.dtype == torch.bool:
+            reset = reset.to(torch.uint8)
+        _check(reset, "reset", (batch, L), torch.uint8, dev)
+    if kernel is not None or seq_lens is not None or reset is not None:
+        st = lib.ssm_scan_fwd_kernel(SCAN_KERNELS[kernel or "auto"], _ptr(u), _ptr(delta), _ptr(A),
+                                     _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+                                     int(bool(softplus)), _MODES[dt_mode], _ptr(h0),
+                                     _ptr(seq_lens), _ptr(reset),
                                      _ptr(y), _ptr(last_state), _ptr(ckpt), batch, L, dim, N,
                                      _io_code(u), _stream(dev))
         if st != 0:

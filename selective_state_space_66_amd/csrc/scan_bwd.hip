@@ -24,6 +24,12 @@
 // across the block's channels and leave as one partial per channel tile.  A
 // second kernel adds the partials (channel tiles for dB, dC; batch entries for
 // dA, dD, d bias) in a fixed order: the result does not depend on timing.
+//
+// Lengths and document starts (the forward of ssm_scan_fwd_ex): tokens at or
+// past a sequence's length are staged as Delta = u = dy = 0, so the state and
+// the adjoint pass them unchanged (abar = 1, bbar u = 0) and their outputs
+// are written as zeros; at a document start the recomputed state restarts
+// from zero, the update sees h_{t-1} = 0 and no adjoint is carried to t - 1.
 #include <type_traits>
 
 #include "ssm_device.h"
@@ -52,6 +58,7 @@ struct BShape {
 template <class S>
 struct BSmem {
   float4 dd[S::TC][S::CW];                  // (Delta, u, ds, -) per token and channel
+  int rst[S::TC];                           // document starts within the chunk
   float bc[S::TC][S::NG][2 * S::G];         // B then C of each group, per token
   float part[2][S::NG][S::PST];             // per-group partial sums per (token, channel)
   float red[2][S::HALF][S::NPAD][S::CW + 1];  // dB, dC contributions per (token, state, channel)
@@ -89,6 +96,8 @@ __device__ __forceinline__ float phi_prime(float k, float a, float phi, float rk
 struct BwdArgs {
   const void *u, *delta, *B, *C, *z, *dy;
   const float *A, *D, *bias, *h0, *dlast;
+  const int32_t* seq_lens;  // nullable: real tokens per sequence
+  const uint8_t* reset;     // nullable: document starts (batch, L)
   void *du, *ddelta, *dz;
   float* dh0;
   float* ckpt;    // (batch, nchunks, dim, N)
@@ -126,6 +135,11 @@ __global__ __launch_bounds__((BShape<G, NG>::THREADS)) void scan_bwd_kernel(cons
   const int64_t cc = cvalid ? c : dim - 1;
   const int n0 = g * G;
   const int64_t row0 = b * L;
+  int64_t Lb = L;  // real tokens of this sequence; the rest is padding
+  if (p.seq_lens) {
+    const int64_t sl = p.seq_lens[b];
+    Lb = sl < 0 ? 0 : (sl < L ? sl : L);
+  }
 
   float Aa[G], Ap[G], CA[G];
   bool small_a = false;
@@ -150,13 +164,16 @@ __global__ __launch_bounds__((BShape<G, NG>::THREADS)) void scan_bwd_kernel(cons
   static_assert(TC * NG == S::THREADS, "one (token, group) of B and C per thread");
   const int btt = tid / NG, bgg = tid % NG;
   IO ru[RPT], rdl[RPT], rdy[RPT], rz[RPT], rb[G], rc[G];
+  int rrs[RPT];
   auto load_raw = [&](int64_t t0, bool bwd) {
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
       const int64_t t = t0 + g + NG * i;
-      const int64_t idx = (row0 + (t < L ? t : L - 1)) * dim + cc;
+      const int64_t tr = t < L ? t : L - 1;
+      const int64_t idx = (row0 + tr) * dim + cc;
       ru[i] = u[idx];
       rdl[i] = dr[idx];
+      rrs[i] = p.reset ? (int)p.reset[row0 + tr] : 0;
       if (bwd) {
         rdy[i] = dyp[idx];
         if constexpr (GATE) rz[i] = zz[idx];
@@ -178,11 +195,19 @@ __global__ __launch_bounds__((BShape<G, NG>::THREADS)) void scan_bwd_kernel(cons
   // thread's tokens stay in registers.  Tokens past L get zeros, and so do u
   // and dy of channels past dim.
   float e_dy[RPT], e_sv[RPT], e_gz[RPT], e_dg[RPT], e_u[RPT], e_ds[RPT];
-  auto stage = [&](int64_t t0, bool bwd) {
+  // returns whether this thread staged a document start (cl == 0 threads
+  // stage the chunk's flags)
+  auto stage = [&](int64_t t0, bool bwd) -> int {
+    int starts = 0;
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
       const int r = g + NG * i;
-      const bool live = t0 + r < L;
+      const bool live = t0 + r < Lb;
+      if (cl == 0) {
+        const int f = (live && rrs[i] != 0) ? 1 : 0;
+        sm.rst[r] = f;
+        starts |= f;
+      }
       const float x = (live && cvalid) ? to_f32(ru[i]) : 0.0f;
       const float v = to_f32(rdl[i]) + bias;
       const float dl = live ? (p.softplus ? softplus_f(v) : v) : 0.0f;
@@ -209,13 +234,21 @@ __global__ __launch_bounds__((BShape<G, NG>::THREADS)) void scan_bwd_kernel(cons
       // the polynomial branch is taken there)
       sm.dd[r][cl] = make_float4(dl, x, ds, rcp_hw(dl));
     }
-    const bool live = t0 + btt < L;
+    const bool live = t0 + btt < Lb;
 #pragma unroll
     for (int k = 0; k < G; ++k) {
       const bool ok = live && bgg * G + k < N;
       sm.bc[btt][bgg][k] = ok ? to_f32(rb[k]) : 0.0f;
       if (bwd) sm.bc[btt][bgg][G + k] = ok ? to_f32(rc[k]) : 0.0f;
     }
+    return starts;
+  };
+  // the barrier after staging; with document starts it also tells every
+  // thread whether the chunk has one (block-uniform)
+  auto staged = [&](int starts) -> bool {
+    if (p.reset) return __syncthreads_or(starts) != 0;
+    lds_barrier();
+    return false;
   };
 
   auto update_state = [&](float& h, float a, float bw, float dl, float x, float Bv) {
@@ -237,6 +270,10 @@ __global__ __launch_bounds__((BShape<G, NG>::THREADS)) void scan_bwd_kernel(cons
 #pragma unroll
     for (int t = 0; t < TC; ++t) {
       if (FULL || t < nt) {
+        if (!FULL && sm.rst[t]) {  // a document starts here: forget the state
+#pragma unroll
+          for (int k = 0; k < G; ++k) h[k] = 0.0f;
+        }
         const float4 d4 = sm.dd[t][cl];
 #pragma unroll
         for (int k = 0; k < G; ++k) {
@@ -263,11 +300,11 @@ __global__ __launch_bounds__((BShape<G, NG>::THREADS)) void scan_bwd_kernel(cons
         if (n0 + k < N)
           p.ckpt[((b * p.nchunks + ck) * dim + c) * N + n0 + k] = fast ? h[k] * CA[k] : h[k];
     }
-    stage(t0, false);
+    const int starts = stage(t0, false);
     if (ck + 1 < p.nchunks) load_raw(t0 + TC, false);
-    lds_barrier();
+    const bool rst = staged(starts);
     const int nt = (int)(L - t0 < TC ? L - t0 : TC);
-    if (nt == TC) {
+    if (nt == TC && !rst) {
       if (fast) p1_tokens(std::true_type(), std::true_type(), nt);
       else p1_tokens(std::true_type(), std::false_type(), nt);
     } else {
@@ -299,15 +336,17 @@ __global__ __launch_bounds__((BShape<G, NG>::THREADS)) void scan_bwd_kernel(cons
   for (int64_t ck = p.nchunks - 1; ck >= 0; --ck) {
     const int64_t t0 = ck * TC;
     const int nt = (int)(L - t0 < TC ? L - t0 : TC);
-    stage(t0, true);
+    const int starts = stage(t0, true);
+    // a chunk wholly in the padding starts from zero (a forward with lengths
+    // need not have written its checkpoint); its tokens change nothing
     float hst[G];
 #pragma unroll
-    for (int k = 0; k < G; ++k) hst[k] = (cvalid && n0 + k < N) ? hnext[k] : 0.0f;
+    for (int k = 0; k < G; ++k) hst[k] = (cvalid && n0 + k < N && t0 < Lb) ? hnext[k] : 0.0f;
     if (ck > 0) {
       load_raw(t0 - TC, true);
       load_ckpt(ck - 1);
     }
-    lds_barrier();
+    const bool rst = staged(starts);
 
     // recompute: states, abar and phi of the chunk; partial pre-gate readout
     // (for dz).  Full chunks run unguarded.
@@ -320,6 +359,10 @@ __global__ __launch_bounds__((BShape<G, NG>::THREADS)) void scan_bwd_kernel(cons
 #pragma unroll
       for (int t = 0; t < TC; ++t) {
         if (FULL || t < nt) {
+          if (!FULL && sm.rst[t]) {
+#pragma unroll
+            for (int k = 0; k < G; ++k) h[k] = 0.0f;
+          }
           const float4 d4 = sm.dd[t][cl];
           float acc = 0.0f;
 #pragma unroll
@@ -336,7 +379,7 @@ __global__ __launch_bounds__((BShape<G, NG>::THREADS)) void scan_bwd_kernel(cons
         }
       }
     };
-    if (nt == TC) recompute(std::true_type());
+    if (nt == TC && !rst) recompute(std::true_type());
     else recompute(std::false_type());
     lds_barrier();
     // dz = dy s silu'(z), s = C.h + D u (this thread's tokens)
@@ -368,12 +411,14 @@ __global__ __launch_bounds__((BShape<G, NG>::THREADS)) void scan_bwd_kernel(cons
             const float4 d4 = sm.dd[t][cl];
             const float dl = d4.x, x = d4.y, ds = d4.z, rdl = d4.w;
             const float xdl = x * dl;
+            // a document start: the update saw h_{t-1} = 0 and carries nothing back
+            const bool start = !FULL && sm.rst[t] != 0;
             float ddt = 0.0f, dx = 0.0f;
 #pragma unroll
             for (int k = 0; k < G; ++k) {
               const float Bv = sm.bc[t][g][k], Cv = sm.bc[t][g][G + k];
               const float a = as[t][k];
-              const float hp = t > 0 ? hs[t > 0 ? t - 1 : 0][k] : hst[k];
+              const float hp = start ? 0.0f : (t > 0 ? hs[t > 0 ? t - 1 : 0][k] : hst[k]);
               // q is the adjoint of h_t (q abar carries it to t - 1); the
               // adjoints of abar and bbar u are q h_{t-1} and q.  Channels
               // past dim stage u = ds = 0, so their dB, dC terms are zero.
@@ -398,14 +443,14 @@ __global__ __launch_bounds__((BShape<G, NG>::THREADS)) void scan_bwd_kernel(cons
                 dx = fmaf(q * dl, Bv, dx);
               }
               sm.red[1][tt][n0 + k][cl] = ds * hs[t][k];
-              gad[k] = qa;
+              gad[k] = start ? 0.0f : qa;
             }
             sm.part[0][g][t * CW + cl] = ddt;
             sm.part[1][g][t * CW + cl] = dx;
           }
         }
       };
-      if (nt == TC) reverse(std::true_type());
+      if (nt == TC && !rst) reverse(std::true_type());
       else reverse(std::false_type());
       lds_barrier();
       // dB, dC of these HALF tokens: sum over the block's channels
@@ -435,7 +480,7 @@ __global__ __launch_bounds__((BShape<G, NG>::THREADS)) void scan_bwd_kernel(cons
           ddt += sm.part[0][j][r * CW + cl];
           dx += sm.part[1][j][r * CW + cl];
         }
-        const float dv = ddt * e_sv[i];
+        const float dv = t < Lb ? ddt * e_sv[i] : 0.0f;  // padding: no step size
         accB += dv;
         accD = fmaf(e_ds[i], e_u[i], accD);
         if (cvalid) {
@@ -533,6 +578,7 @@ hipError_t bwd_io(const ScanBwdParams& q, bool zoh, bool gate, hipStream_t strea
   BwdArgs a;
   a.u = q.u; a.delta = q.delta; a.B = q.B; a.C = q.C; a.z = q.z; a.dy = q.dy;
   a.A = q.A; a.D = q.D; a.bias = q.delta_bias; a.h0 = q.h0; a.dlast = q.dlast;
+  a.seq_lens = q.seq_lens; a.reset = q.reset;
   a.du = q.du; a.ddelta = q.ddelta; a.dz = q.dz; a.dh0 = q.dh0;
   a.batch = q.batch; a.L = q.L; a.dim = q.dim; a.N = q.N;
   a.ntiles = (q.dim + 15) / 16;

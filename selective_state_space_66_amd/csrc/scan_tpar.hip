@@ -523,7 +523,6 @@ __global__ __launch_bounds__(64 * kWW, 4) void scan_wave_kernel(
     int64_t t = t0 + xt;
     x_live = t < Leff;
     t = t < L ? t : L - 1;
-    const int64_t e0 = (row0 + t) * dim + c0 + 4 * xh;
     if (vec_io) {
       // uniform base, 32-bit per-thread byte offset (of the clamped token)
       const int64_t cb0 = (row0 + t0) * dim + c0;

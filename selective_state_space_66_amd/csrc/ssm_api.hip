@@ -306,7 +306,8 @@ size_t ssm_scan_bwd_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, i
 // against its size before any HIP call).
 static int scan_bwd_impl(const void* u, const void* delta, const float* A, const void* B,
                          const void* C, const float* D, const void* z, const float* delta_bias,
-                         int softplus, int dt_mode, const float* h0, const void* dy,
+                         int softplus, int dt_mode, const float* h0, const int32_t* seq_lens,
+                         const uint8_t* reset, const void* dy,
                          const float* dlast_state, void* du, void* ddelta, float* dA, void* dB,
                          void* dC, float* dD, void* dz, float* ddelta_bias, float* dh0,
                          const float* ckpt, void* workspace, size_t workspace_bytes,
@@ -331,8 +332,8 @@ static int scan_bwd_impl(const void* u, const void* delta, const float* A, const
   const void* io_ptrs[11] = {u, delta, B, C, z, dy, du, ddelta, dB, dC, dz};
   for (const void* q : io_ptrs)
     if (q && !aligned(q, es)) return SSM_ERR_ALIGN;
-  const void* f32_ptrs[11] = {A, D, delta_bias, h0, dlast_state, dA, dD, ddelta_bias, dh0,
-                              ckpt, workspace};
+  const void* f32_ptrs[12] = {A, D, delta_bias, h0, dlast_state, dA, dD, ddelta_bias, dh0,
+                              ckpt, workspace, seq_lens};
   for (const void* q : f32_ptrs)
     if (q && !aligned(q, 4)) return SSM_ERR_ALIGN;
   if (workspace && !aligned(workspace, 256)) return SSM_ERR_ALIGN;
@@ -345,6 +346,7 @@ static int scan_bwd_impl(const void* u, const void* delta, const float* A, const
   ssm66::ScanBwdParams p;
   p.u = u; p.delta = delta; p.B = B; p.C = C; p.z = z; p.dy = dy;
   p.A = A; p.D = D; p.delta_bias = delta_bias; p.h0 = h0; p.dlast = dlast_state;
+  p.seq_lens = seq_lens; p.reset = reset;
   p.du = du; p.ddelta = ddelta; p.dB = dB; p.dC = dC; p.dz = dz;
   p.dA = dA; p.dD = dD; p.ddelta_bias = ddelta_bias; p.dh0 = dh0;
   p.workspace = workspace;
@@ -357,12 +359,14 @@ static int scan_bwd_impl(const void* u, const void* delta, const float* A, const
 
 int ssm_scan_bwd_ex(const void* u, const void* delta, const float* A, const void* B,
                     const void* C, const float* D, const void* z, const float* delta_bias,
-                    int softplus, int dt_mode, const float* h0, const void* dy,
-                    const float* dlast_state, void* du, void* ddelta, float* dA, void* dB,
-                    void* dC, float* dD, void* dz, float* ddelta_bias, float* dh0,
-                    const float* ckpt, void* workspace, size_t workspace_bytes, int64_t batch,
-                    int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype, void* stream) {
-  return scan_bwd_impl(u, delta, A, B, C, D, z, delta_bias, softplus, dt_mode, h0, dy,
+                    int softplus, int dt_mode, const float* h0, const int32_t* seq_lens,
+                    const uint8_t* reset, const void* dy, const float* dlast_state, void* du,
+                    void* ddelta, float* dA, void* dB, void* dC, float* dD, void* dz,
+                    float* ddelta_bias, float* dh0, const float* ckpt, void* workspace,
+                    size_t workspace_bytes, int64_t batch, int64_t seqlen, int64_t dim,
+                    int64_t dstate, int io_dtype, void* stream) {
+  return scan_bwd_impl(u, delta, A, B, C, D, z, delta_bias, softplus, dt_mode, h0, seq_lens,
+                       reset, dy,
                        dlast_state, du, ddelta, dA, dB, dC, dD, dz, ddelta_bias, dh0, ckpt,
                        workspace, workspace_bytes, false, batch, seqlen, dim, dstate, io_dtype,
                        stream);
@@ -370,12 +374,14 @@ int ssm_scan_bwd_ex(const void* u, const void* delta, const float* A, const void
 
 int ssm_scan_bwd_noalloc(const void* u, const void* delta, const float* A, const void* B,
                          const void* C, const float* D, const void* z, const float* delta_bias,
-                         int softplus, int dt_mode, const float* h0, const void* dy,
-                         const float* dlast_state, void* du, void* ddelta, float* dA, void* dB,
-                         void* dC, float* dD, void* dz, float* ddelta_bias, float* dh0,
-                         const float* ckpt, int64_t batch, int64_t seqlen, int64_t dim,
-                         int64_t dstate, int io_dtype, void* stream) {
-  return scan_bwd_impl(u, delta, A, B, C, D, z, delta_bias, softplus, dt_mode, h0, dy,
+                         int softplus, int dt_mode, const float* h0, const int32_t* seq_lens,
+                         const uint8_t* reset, const void* dy, const float* dlast_state,
+                         void* du, void* ddelta, float* dA, void* dB, void* dC, float* dD,
+                         void* dz, float* ddelta_bias, float* dh0, const float* ckpt,
+                         int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                         int io_dtype, void* stream) {
+  return scan_bwd_impl(u, delta, A, B, C, D, z, delta_bias, softplus, dt_mode, h0, seq_lens,
+                       reset, dy,
                        dlast_state, du, ddelta, dA, dB, dC, dD, dz, ddelta_bias, dh0, ckpt,
                        nullptr, 0, true, batch, seqlen, dim, dstate, io_dtype, stream);
 }
@@ -387,7 +393,8 @@ int ssm_scan_bwd(const void* u, const void* delta, const float* A, const void* B
                  float* ddelta_bias, float* dh0, void* workspace, size_t workspace_bytes,
                  int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype,
                  void* stream) {
-  return ssm_scan_bwd_ex(u, delta, A, B, C, D, z, delta_bias, softplus, dt_mode, h0, dy,
+  return ssm_scan_bwd_ex(u, delta, A, B, C, D, z, delta_bias, softplus, dt_mode, h0, nullptr,
+                         nullptr, dy,
                          dlast_state, du, ddelta, dA, dB, dC, dD, dz, ddelta_bias, dh0, nullptr,
                          workspace, workspace_bytes, batch, seqlen, dim, dstate, io_dtype, stream);
 }

@@ -43,6 +43,8 @@ struct StepParams {
 struct ScanBwdParams {
   const void *u, *delta, *B, *C, *z, *dy;     // io dtype; z nullable
   const float *A, *D, *delta_bias, *h0, *dlast;  // D, delta_bias, h0, dlast nullable
+  const int32_t* seq_lens;                     // nullable: real tokens per sequence
+  const uint8_t* reset;                        // nullable: document starts (batch, L)
   void *du, *ddelta, *dB, *dC, *dz;           // io dtype; dz nullable
   float *dA, *dD, *ddelta_bias, *dh0;          // dD, ddelta_bias, dh0 nullable
   void* workspace;                             // scan_bwd_workspace_bytes(...) bytes

@@ -106,14 +106,21 @@ int main() {
   EXPECT(bwd(P, 1, 2, 5, 8, 16), SSM_ERR_SHAPE);
   EXPECT(bwd(M, (size_t)1 << 40, 2, 5, 8, 16), SSM_ERR_ALIGN);
   EXPECT(bwd(P, (size_t)1 << 40, big, 5, 8, 16), SSM_ERR_SHAPE);
-  EXPECT(ssm_scan_bwd_noalloc(P, P, F, P, P, nullptr, nullptr, nullptr, 1, 0, nullptr, P,
-                              nullptr, P, P, F, P, P, nullptr, nullptr, nullptr, nullptr, nullptr,
-                              8, 2048, 1536, 16, SSM_BF16, nullptr),
+  EXPECT(ssm_scan_bwd_noalloc(P, P, F, P, P, nullptr, nullptr, nullptr, 1, 0, nullptr, nullptr,
+                              nullptr, P, nullptr, P, P, F, P, P, nullptr, nullptr, nullptr,
+                              nullptr, nullptr, 8, 2048, 1536, 16, SSM_BF16, nullptr),
          SSM_ERR_UNSUPPORTED);
-  EXPECT(ssm_scan_bwd_noalloc(P, P, F, P, P, nullptr, P, nullptr, 1, 0, nullptr, P, nullptr, P,
-                              P, F, P, P, nullptr, nullptr, nullptr, nullptr, nullptr, 1, 64, 64,
-                              16, SSM_BF16, nullptr),
+  EXPECT(ssm_scan_bwd_noalloc(P, P, F, P, P, nullptr, P, nullptr, 1, 0, nullptr, nullptr,
+                              nullptr, P, nullptr, P, P, F, P, P, nullptr, nullptr, nullptr,
+                              nullptr, nullptr, 1, 64, 64, 16, SSM_BF16, nullptr),
          SSM_ERR_NULL);  // a gate without its gradient
+  {  // lengths and resets: seq_lens must be 4-byte aligned
+    const int32_t* lens_m = (const int32_t*)((const char*)F + 2);
+    EXPECT(ssm_scan_bwd_ex(P, P, F, P, P, nullptr, nullptr, nullptr, 1, 0, nullptr, lens_m,
+                           nullptr, P, nullptr, P, P, F, P, P, nullptr, nullptr, nullptr,
+                           nullptr, nullptr, P, (size_t)1 << 40, 2, 5, 8, 16, SSM_BF16, nullptr),
+           SSM_ERR_ALIGN);
+  }
 
   // Mamba-2 / SSD
   auto ssd = [&](const void* x, int64_t b, int64_t L, int64_t h, int64_t pd, int64_t n, int io) {

@@ -215,12 +215,14 @@ def test_bwd_workspace_size(lib):
 
 def _bwd_ex(lib, ckpt, **kw):
     a = dict(u=FAKE, delta=FAKE, A=FAKE, B=FAKE, C=FAKE, D=None, z=None, bias=None, softplus=1,
-             dt_mode=0, h0=None, dy=FAKE, dlast=None, du=FAKE, ddelta=FAKE, dA=FAKE, dB=FAKE,
-             dC=FAKE, dD=None, dz=None, dbias=None, dh0=None, ws=ctypes.c_void_p(0x100000),
-             wsb=1 << 40, batch=2, L=8, dim=64, N=16, io=1, stream=None)
+             dt_mode=0, h0=None, lens=None, reset=None, dy=FAKE, dlast=None, du=FAKE,
+             ddelta=FAKE, dA=FAKE, dB=FAKE, dC=FAKE, dD=None, dz=None, dbias=None, dh0=None,
+             ws=ctypes.c_void_p(0x100000), wsb=1 << 40, batch=2, L=8, dim=64, N=16, io=1,
+             stream=None)
     a.update(kw)
     return lib.ssm_scan_bwd_ex(a["u"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"],
-                               a["bias"], a["softplus"], a["dt_mode"], a["h0"], a["dy"],
+                               a["bias"], a["softplus"], a["dt_mode"], a["h0"], a["lens"],
+                               a["reset"], a["dy"],
                                a["dlast"], a["du"], a["ddelta"], a["dA"], a["dB"], a["dC"],
                                a["dD"], a["dz"], a["dbias"], a["dh0"], ckpt, a["ws"], a["wsb"],
                                a["batch"], a["L"], a["dim"], a["N"], a["io"], a["stream"])
@@ -248,6 +250,7 @@ def test_training_entry_points_reject_invalid_arguments(lib):
     assert _bwd_ex(lib, MISALIGNED) == c["SSM_ERR_ALIGN"]
     assert _bwd_ex(lib, FAKE, dy=None) == c["SSM_ERR_NULL"]
     assert _bwd_ex(lib, FAKE, batch=0) == c["SSM_OK"]
+    assert _bwd_ex(lib, FAKE, lens=MISALIGNED) == c["SSM_ERR_ALIGN"]  # int32 lengths
 
 
 def test_ckpt_size(lib):
@@ -354,7 +357,8 @@ def test_noalloc_backward_validation(lib):
         a = dict(u=FAKE, A=FAKE, dy=FAKE, out=FAKE, dA=FAKE, io=1)
         a.update(kw)
         return lib.ssm_scan_bwd_noalloc(a["u"], a["u"], a["A"], a["u"], a["u"], None, None, None,
-                                        1, 0, None, a["dy"], None, a["out"], a["out"], a["dA"],
+                                        1, 0, None, None, None, a["dy"], None, a["out"], a["out"],
+                                        a["dA"],
                                         a["out"], a["out"], None, None, None, None, None, batch,
                                         L, dim, N, a["io"], None)
 

@@ -309,3 +309,99 @@ def test_bwd_from_forward_checkpoints_full_size_sampled():
            "dD": g["dD"].index_select(0, chd), "ddelta_bias": g["ddelta_bias"].index_select(0, chd),
            "dB": g["dB"], "dC": g["dC"], "dh0": None}
     _compare(got, r, "bf16", "full from checkpoints")
+
+
+# ------------------------------------------------- lengths and document starts
+
+def _varlen(batch, L, seed):
+    """Lengths (one full, one short, one empty where batch > 2) and document
+    starts (at token 0 of the first sequence, mid-chunk, on a chunk boundary,
+    two in a row, one past a length, which is ignored)."""
+    lens = np.array([L, L - 37, 0][:batch], dtype=np.int32)
+    reset = np.zeros((batch, L), dtype=np.uint8)
+    reset[0, [0, 21, 48, 49]] = 1
+    if batch > 1:
+        reset[1, [5, 32, L - 10]] = 1
+    return lens, reset
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("mode", ["zoh", "euler"])
+@pytest.mark.parametrize("from_ckpt", [False, True])
+def test_bwd_lengths_and_resets(io, mode, from_ckpt):
+    """ssm_scan_bwd_ex with lengths and document starts, h0 and dlast, with
+    its own forward sweep or from the training forward's checkpoints (taken
+    with the same lengths and starts), against the oracle's backward."""
+    inp = W.scan_inputs(_cfg(3, 99, 34, 16, io, True, seed=130))
+    dy = _dy((3, 99, 34), io, 131)
+    rng = np.random.default_rng(132)
+    h0 = rng.normal(size=(3, 34, 16)).astype(np.float32)
+    dlast = rng.normal(size=(3, 34, 16)).astype(np.float32)
+    lens, reset = _varlen(3, 99, 133)
+    args = (to_dev(inp["u"], io), to_dev(inp["delta"], io), to_dev(inp["A"], "f32"),
+            to_dev(inp["B"], io), to_dev(inp["C"], io))
+    kw = dict(D=to_dev(inp["D"], "f32"), z=to_dev(inp["z"], io),
+              delta_bias=to_dev(inp["delta_bias"], "f32"), dt_mode=mode, h0=to_dev(h0, "f32"),
+              seq_lens=torch.from_numpy(lens).to(DEV), reset=torch.from_numpy(reset).to(DEV))
+    ck = ssm.scan_fwd_train(*args, **kw)[2] if from_ckpt else None
+    g = ssm.scan_bwd(*args, to_dev(dy, io), dlast=to_dev(dlast, "f32"), ckpt=ck, **kw)
+    torch.cuda.synchronize()
+    r = oracle.scan_bwd(f64(inp["u"], io), f64(inp["delta"], io), inp["A"], f64(inp["B"], io),
+                        f64(inp["C"], io), f64(dy, io), D=inp["D"], z=f64(inp["z"], io),
+                        delta_bias=inp["delta_bias"], dt_mode=mode, h0=h0.astype(np.float64),
+                        dlast=dlast.astype(np.float64), seq_lens=lens, reset=reset)
+    _compare(g, r, io, f"varlen {io} {mode} ckpt={from_ckpt}")
+    for b, n in enumerate(lens):  # padding rows are exactly zero
+        for k in ("du", "ddelta", "dz", "dB", "dC"):
+            assert torch.all(g[k][b, n:] == 0), f"{k} past length {n}"
+
+
+@pytest.mark.parametrize("kernel", ["seq1", "seq2", "seq4", "tpar", "wave"])
+def test_bwd_lengths_and_resets_from_every_forward(kernel):
+    """The checkpoints of every forward kernel, taken with lengths and
+    document starts, give the backward the oracle's gradients."""
+    inp = W.scan_inputs(_cfg(2, 80, 20, 16, "f32", True, seed=134))
+    dy = _dy((2, 80, 20), "f32", 135)
+    lens, reset = _varlen(2, 80, 136)
+    args = (to_dev(inp["u"], "f32"), to_dev(inp["delta"], "f32"), to_dev(inp["A"], "f32"),
+            to_dev(inp["B"], "f32"), to_dev(inp["C"], "f32"))
+    kw = dict(D=to_dev(inp["D"], "f32"), z=to_dev(inp["z"], "f32"),
+              delta_bias=to_dev(inp["delta_bias"], "f32"),
+              seq_lens=torch.from_numpy(lens).to(DEV), reset=torch.from_numpy(reset).to(DEV))
+    _, _, ck = ssm.scan_fwd_train(*args, kernel=kernel, **kw)
+    g = ssm.scan_bwd(*args, to_dev(dy, "f32"), ckpt=ck, **kw)
+    torch.cuda.synchronize()
+    r = oracle.scan_bwd(inp["u"], inp["delta"], inp["A"], inp["B"], inp["C"], dy, D=inp["D"],
+                        z=inp["z"], delta_bias=inp["delta_bias"], seq_lens=lens, reset=reset)
+    _compare(g, r, "f32", f"varlen from {kernel}")
+
+
+def test_bwd_lengths_all_padding_and_state_sizes():
+    """Every sequence empty (only dlast reaches dh0), and state sizes below 16
+    with lengths and starts."""
+    inp = W.scan_inputs(_cfg(2, 40, 12, 16, "f32", True, seed=137))
+    dy = _dy((2, 40, 12), "f32", 138)
+    dlast = np.random.default_rng(139).normal(size=(2, 12, 16)).astype(np.float32)
+    h0 = np.zeros((2, 12, 16), dtype=np.float32)
+    lens = np.zeros(2, dtype=np.int32)
+    g = ssm.scan_bwd(to_dev(inp["u"], "f32"), to_dev(inp["delta"], "f32"), to_dev(inp["A"], "f32"),
+                     to_dev(inp["B"], "f32"), to_dev(inp["C"], "f32"), to_dev(dy, "f32"),
+                     D=to_dev(inp["D"], "f32"), z=to_dev(inp["z"], "f32"), h0=to_dev(h0, "f32"),
+                     dlast=to_dev(dlast, "f32"), seq_lens=torch.from_numpy(lens).to(DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(g["dh0"], to_dev(dlast, "f32"))
+    for k in ("du", "ddelta", "dz", "dB", "dC", "dA", "dD"):
+        assert torch.all(g[k] == 0), k
+    for N in (3, 8):
+        inp = W.scan_inputs(_cfg(2, 60, 20, N, "f32", True, seed=140 + N))
+        dy = _dy((2, 60, 20), "f32", 141)
+        lens, reset = _varlen(2, 60, 142)
+        g = ssm.scan_bwd(to_dev(inp["u"], "f32"), to_dev(inp["delta"], "f32"),
+                         to_dev(inp["A"], "f32"), to_dev(inp["B"], "f32"), to_dev(inp["C"], "f32"),
+                         to_dev(dy, "f32"), D=to_dev(inp["D"], "f32"), z=to_dev(inp["z"], "f32"),
+                         seq_lens=torch.from_numpy(lens).to(DEV),
+                         reset=torch.from_numpy(reset).to(DEV))
+        torch.cuda.synchronize()
+        r = oracle.scan_bwd(inp["u"], inp["delta"], inp["A"], inp["B"], inp["C"], dy, D=inp["D"],
+                            z=inp["z"], seq_lens=lens, reset=reset)
+        _compare(g, r, "f32", f"varlen N={N}")
