@@ -85,6 +85,9 @@ def _load():
     lib.oracle_conv1d_step.restype = None
     lib.oracle_conv1d_step.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int, ctypes.c_void_p] + \
         [ctypes.c_int64] * 3
+    lib.oracle_conv1d_bwd.restype = None
+    lib.oracle_conv1d_bwd.argtypes = [ctypes.c_void_p] * 6 + [ctypes.c_int] + \
+        [ctypes.c_void_p] * 6 + [ctypes.c_int64] * 4
     _lib = lib
     return lib
 
@@ -281,6 +284,35 @@ def conv1d_step(window, x, weight, bias=None, silu=True):
     _load().oracle_conv1d_step(_ptr(win), _ptr(x), _ptr(w), _ptr(bias), int(bool(silu)),
                                _ptr(out), batch, dim, k)
     return out, win
+
+
+def conv1d_bwd(x, weight, dout, bias=None, silu=True, state_in=None, seq_lens=None, reset=None,
+               dstate_out=None):
+    """Gradients of conv1d_fwd (same arguments), fp64: given dout (batch, L, dim)
+    and optionally dstate_out (batch, k - 1, dim), the gradient of state_out,
+    returns a dict with dx, dweight (dim, k) and, where their inputs are
+    given, dbias and dstate_in."""
+    x, w, dout = _f64(x), _f64(weight), _f64(dout)
+    bias, state_in, dstate_out = _f64(bias), _f64(state_in), _f64(dstate_out)
+    batch, L, dim = x.shape
+    k = w.shape[1]
+    assert w.shape == (dim, k) and dout.shape == x.shape
+    assert state_in is None or state_in.shape == (batch, k - 1, dim)
+    assert dstate_out is None or dstate_out.shape == (batch, k - 1, dim)
+    if seq_lens is not None:
+        seq_lens = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int64))
+        assert seq_lens.shape == (batch,)
+    if reset is not None:
+        reset = np.ascontiguousarray(np.asarray(reset) != 0, dtype=np.uint8)
+        assert reset.shape == (batch, L)
+    out = dict(dx=np.empty_like(x), dweight=np.empty((dim, k)),
+               dbias=np.empty(dim) if bias is not None else None,
+               dstate_in=np.empty((batch, k - 1, dim)) if state_in is not None else None)
+    _load().oracle_conv1d_bwd(_ptr(x), _ptr(w), _ptr(bias), _ptr(state_in), _ptr(seq_lens),
+                              _ptr(reset), int(bool(silu)), _ptr(dout), _ptr(dstate_out),
+                              _ptr(out["dx"]), _ptr(out["dweight"]), _ptr(out["dbias"]),
+                              _ptr(out["dstate_in"]), batch, L, dim, k)
+    return out
 
 
 def scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, softplus=True,

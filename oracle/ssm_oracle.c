@@ -341,6 +341,77 @@ void oracle_conv1d_fwd(const double* x, const double* w, const double* bias,
   }
 }
 
+/* Backward pass of oracle_conv1d_fwd, by the chain rule through the forward
+ * exactly as written above (the pages define the forward only): with
+ * dpre_t = dout_t act'(pre_t), act'(p) = sigma(p) (1 + p (1 - sigma(p))) for
+ * SiLU and 1 without, every real token t adds
+ *   dbias += dpre_t,   dw_i += dpre_t XT(t - i),
+ * and w_i dpre_t to the gradient of the input it read at t - i (an x, a
+ * carried-in window entry, or nothing where the forward read a zero); the
+ * gradient of state_out (dstate_out, nullable) goes to the inputs the window
+ * holds.  Outputs past a length are constants, so nothing flows from them.
+ * dx, dw (dim, k), dbias and dstate_in are overwritten; dbias and dstate_in
+ * may be NULL. */
+static double act_prime(double v, int silu) {
+  if (!silu) return 1.0;
+  const double s = oracle_sigmoid(v);
+  return s * (1.0 + v * (1.0 - s));
+}
+
+void oracle_conv1d_bwd(const double* x, const double* w, const double* bias,
+                       const double* state_in, const int64_t* seq_lens, const uint8_t* reset,
+                       int silu, const double* dout, const double* dstate_out, double* dx,
+                       double* dw, double* dbias, double* dstate_in, int64_t batch, int64_t L,
+                       int64_t dim, int64_t k) {
+  for (int64_t i = 0; i < batch * L * dim; ++i) dx[i] = 0.0;
+  for (int64_t i = 0; i < dim * k; ++i) dw[i] = 0.0;
+  if (dbias)
+    for (int64_t c = 0; c < dim; ++c) dbias[c] = 0.0;
+  if (dstate_in)
+    for (int64_t i = 0; i < batch * (k - 1) * dim; ++i) dstate_in[i] = 0.0;
+  for (int64_t b = 0; b < batch; ++b) {
+    int64_t len = seq_lens ? seq_lens[b] : L;
+    if (len < 0) len = 0;
+    if (len > L) len = L;
+    for (int64_t c = 0; c < dim; ++c) {
+#define XT(s, start)                                                                   \
+  (((s) < (start)) ? 0.0                                                               \
+   : ((s) >= 0)    ? x[(b * L + (s)) * dim + c]                                        \
+   : (state_in && (s) >= -(k - 1)) ? state_in[(b * (k - 1) + (k - 1 + (s))) * dim + c] \
+                                   : 0.0)
+      /* add v to the gradient of the input the forward read at s */
+#define ROUTE(s, start, v)                                                      \
+  do {                                                                          \
+    if ((s) >= (start)) {                                                       \
+      if ((s) >= 0)                                                             \
+        dx[(b * L + (s)) * dim + c] += (v);                                     \
+      else if (state_in && dstate_in && (s) >= -(k - 1))                        \
+        dstate_in[(b * (k - 1) + (k - 1 + (s))) * dim + c] += (v);              \
+    }                                                                           \
+  } while (0)
+      int64_t start = -(k - 1);
+      for (int64_t t = 0; t < len; ++t) {
+        if (reset && reset[b * L + t]) start = t;
+        double pre = bias ? bias[c] : 0.0;
+        for (int64_t i = 0; i < k; ++i) pre += w[c * k + i] * XT(t - i, start);
+        const double dpre = dout[(b * L + t) * dim + c] * act_prime(pre, silu);
+        if (dbias) dbias[c] += dpre;
+        for (int64_t i = 0; i < k; ++i) {
+          dw[c * k + i] += dpre * XT(t - i, start);
+          ROUTE(t - i, start, w[c * k + i] * dpre);
+        }
+      }
+      if (dstate_out)
+        for (int64_t j = 0; j < k - 1; ++j) {
+          const int64_t s = len - (k - 1) + j; /* oldest first, as state_out */
+          ROUTE(s, start, dstate_out[(b * (k - 1) + j) * dim + c]);
+        }
+#undef ROUTE
+#undef XT
+    }
+  }
+}
+
 /* One decoding step: append x to the window, convolve, shift. */
 void oracle_conv1d_step(double* window, const double* x, const double* w, const double* bias,
                         int silu, double* out, int64_t batch, int64_t dim, int64_t k) {

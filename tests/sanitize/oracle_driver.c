@@ -36,6 +36,11 @@ void oracle_conv1d_fwd(const double* x, const double* w, const double* bias,
                        int64_t dim, int64_t k);
 void oracle_conv1d_step(double* window, const double* x, const double* w, const double* bias,
                         int silu, double* out, int64_t batch, int64_t dim, int64_t k);
+void oracle_conv1d_bwd(const double* x, const double* w, const double* bias,
+                       const double* state_in, const int64_t* seq_lens, const uint8_t* reset,
+                       int silu, const double* dout, const double* dstate_out, double* dx,
+                       double* dw, double* dbias, double* dstate_in, int64_t batch, int64_t L,
+                       int64_t dim, int64_t k);
 void oracle_scan_bwd(const double* u, const double* delta, const double* A, const double* B,
                      const double* C, const double* D, const double* z,
                      const double* delta_bias, const double* h0, const int64_t* seq_lens,
@@ -110,6 +115,10 @@ int main(void) {
       oracle_conv1d_fwd(u, w, o ? bias : NULL, o ? win : NULL, o ? lens : NULL, o ? reset : NULL,
                         o, y, o ? wout : NULL, batch, L, dim, k);
       oracle_conv1d_step(win, u, w, o ? bias : NULL, o, y, batch, dim, k);
+      double *dw = arr(dim * k), *dwin = arr(batch * (k - 1) * dim);
+      oracle_conv1d_bwd(u, w, o ? bias : NULL, o ? win : NULL, o ? lens : NULL, o ? reset : NULL,
+                        o, dy, o ? wout : NULL, du, dw, o ? dbias : NULL, o ? dwin : NULL, batch,
+                        L, dim, k);
 
       const int64_t nh = 2, P = 3, Ns = 4, dims = nh * P;
       double *x = arr(batch * L * dims), *dtr = arr(batch * L * nh), *Ah = arr(nh);
@@ -121,7 +130,7 @@ int main(void) {
 
       double* all[] = {u, dl, A, B, C, D, z, bias, h0, y, last, st, dy, dlast, du, ddl, dA, dB,
                        dC, dD, dz, dbias, dh0, w, win, wout, x, dtr, Ah, Bs, Cs, Dh, zs, dtb,
-                       h0s, ys, ls};
+                       h0s, ys, ls, dw, dwin};
       for (size_t i = 0; i < sizeof(all) / sizeof(all[0]); ++i) free(all[i]);
       free(reset);
     }

@@ -72,6 +72,15 @@ MUTATIONS = {
     "bwd_silu_derivative": ("          if (dz) dz[xi] = dy[xi] * s * sg * (1.0 + zz * (1.0 - sg));",
                             "          if (dz) dz[xi] = dy[xi] * s * sg;"),
     "bwd_phi_prime_series": ("      s += (double)j * kp / term_f;", "      s += kp / term_f;"),
+    "conv_bwd_silu_derivative": ("  return s * (1.0 + v * (1.0 - s));", "  return s;"),
+    "conv_bwd_taps_reversed": ("          ROUTE(t - i, start, w[c * k + i] * dpre);",
+                               "          ROUTE(t - i, start, w[c * k + (k - 1 - i)] * dpre);"),
+    "conv_bwd_crosses_reset": ("        if (reset && reset[b * L + t]) start = t;\n        double pre = bias ? bias[c] : 0.0;\n        for (int64_t i = 0; i < k; ++i) pre += w[c * k + i] * XT(t - i, start);\n        const double dpre",
+                               "        double pre = bias ? bias[c] : 0.0;\n        for (int64_t i = 0; i < k; ++i) pre += w[c * k + i] * XT(t - i, start);\n        const double dpre"),
+    "conv_bwd_window_grad_dropped": ("          ROUTE(s, start, dstate_out[(b * (k - 1) + j) * dim + c]);",
+                                     "          (void)s;"),
+    "conv_bwd_dw_lag": ("          dw[c * k + i] += dpre * XT(t - i, start);",
+                        "          dw[c * k + i] += dpre * XT(t - i + 1, start);"),
     "ssd_wrong_head_decay": ("      const double a = A[hd];", "      const double a = A[0];"),
     "ssd_weight_missing": ("            h[n] = alpha * h[n] + w * B[(b * L + t) * N + n] * xv;",
                            "            h[n] = alpha * h[n] + B[(b * L + t) * N + n] * xv;"),
@@ -95,6 +104,7 @@ def test_planted_mistake_is_caught(name, tmp_path):
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
                         os.path.join(ROOT, "tests", "test_oracle_pins.py"),
                         os.path.join(ROOT, "tests", "test_oracle_conv_pins.py"),
+                        os.path.join(ROOT, "tests", "test_oracle_conv_bwd_pins.py"),
                         os.path.join(ROOT, "tests", "test_oracle_bwd_pins.py"),
                         os.path.join(ROOT, "tests", "test_oracle_ssd_pins.py")],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
