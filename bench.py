@@ -523,6 +523,12 @@ def time_ssd(dev, steps, warmup, nsets=3):
                      "flops": fl}}
 
 
+def conv_bwd_bytes(b, L, D, k, io_bytes):
+    """Algorithmic bytes of the convolution's backward pass: x and dout read,
+    dx written once; weights and bias read, their gradients written."""
+    return 3 * b * L * D * io_bytes + 4 * D * (k + 1) * 2
+
+
 def conv_bytes(b, L, D, k, io_bytes):
     """Algorithmic bytes of the sequence convolution: x read and out written once,
     the decoding window written, weights and bias read."""
@@ -564,6 +570,27 @@ def time_conv(dev, steps, warmup, nsets=4):
     torch.cuda.synchronize()
     fwd_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
 
+    # the backward pass on the same layer: dout per set, one workspace
+    gen = torch.Generator(device="cpu").manual_seed(14)
+    douts = [torch.randn(x.shape, generator=gen).to(x.dtype).to(dev) for x, _, _ in sets]
+    ws = torch.empty(ssm.conv1d_bwd_workspace_size(cfg.batch, cfg.L, cfg.dim, cfg.k),
+                     dtype=torch.uint8, device=dev)
+
+    def launch_bwd(i):
+        x, w, b = sets[i % nsets]
+        ssm.conv1d_bwd(x, w, douts[i % nsets], bias=b, workspace=ws)
+
+    for i in range(warmup):
+        launch_bwd(i)
+    torch.cuda.synchronize()
+    for i in range(steps):
+        ev[i][0].record()
+        launch_bwd(warmup + i)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    bwd_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    bwd_b = conv_bwd_bytes(cfg.batch, cfg.L, cfg.dim, cfg.k, 2)
+
     dcfg = W.CONV_CONFIGS["conv_decode"]
     w, b = W.conv_params(dcfg.seed, dcfg.dim, dcfg.k)
     wd, bd = to_dev(w, "f32", dev), to_dev(b, "f32", dev)
@@ -591,7 +618,13 @@ def time_conv(dev, steps, warmup, nsets=4):
             "traffic": measured_traffic("conv1d_fwd_conv130m"),
             "step": {"workload": f"ssm_conv1d_step: batch {dcfg.batch}, D {dcfg.dim}, k {dcfg.k}, "
                                  "bf16, SiLU", "us_per_step": round(step_us, 3),
-                     "GB/s": round(step_b / (step_us * 1e-6) / 1e9, 2)}}
+                     "GB/s": round(step_b / (step_us * 1e-6) / 1e9, 2)},
+            "backward": {"workload": "ssm_conv1d_bwd on the same layer: dx, dweight, dbias "
+                                     "(its finalize kernel included)",
+                         "kernel_ms": round(bwd_ms, 5),
+                         "GB/s": round(bwd_b / (bwd_ms * 1e-3) / 1e9, 2),
+                         "hbm_frac": round(bwd_b / (bwd_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                         "algorithmic_bytes": bwd_b}}
 
 
 def copy_bandwidth(dev, nbytes=256 << 20, reps=20):
@@ -779,6 +812,15 @@ def profile_only(what, launches, dt_mode, kernel=None):
         w, b = to_dev(inp["w"], "f32", dev), to_dev(inp["bias"], "f32", dev)
         for _ in range(launches):
             ssm.conv1d_fwd(x, w, bias=b)
+    elif what == "conv_bwd":
+        cfg = W.CONV_CONFIGS["conv130m"]
+        inp = W.conv_inputs(cfg)
+        x = to_dev(inp["x"], cfg.io, dev)
+        w, b = to_dev(inp["w"], "f32", dev), to_dev(inp["bias"], "f32", dev)
+        gen = torch.Generator(device="cpu").manual_seed(14)
+        dout = torch.randn(x.shape, generator=gen).to(x.dtype).to(dev)
+        for _ in range(launches):
+            ssm.conv1d_bwd(x, w, dout, bias=b)
     torch.cuda.synchronize()
     log(f"[bench] profile-only {what}: {launches} launches done")
 
@@ -790,7 +832,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--decode-steps", type=int, default=1000)
-    ap.add_argument("--only", choices=["scan", "seq", "bwd", "tpar", "decode", "conv", "ssd", "copy"],
+    ap.add_argument("--only", choices=["scan", "seq", "bwd", "tpar", "decode", "conv", "conv_bwd",
+                                       "ssd", "copy"],
                     default=None,
                     help="profiling mode: a few launches of one kernel, no JSON")
     ap.add_argument("--launches", type=int, default=3)

@@ -39,7 +39,7 @@
  *   ssm_conv1d_fwd, ssm_conv1d_step : the short causal depthwise convolution
  *                  (+ SiLU) that feeds the scan in "The Mamba block", over
  *                  whole sequences and as one decoding step with its window of
- *                  the last k - 1 inputs.
+ *                  the last k - 1 inputs; ssm_conv1d_bwd is its backward pass.
  *
  * Conventions shared by all calls
  *   - Every pointer is caller-owned DEVICE memory (HBM).  The library keeps no
@@ -372,6 +372,40 @@ int ssm_conv1d_fwd(const void* x, const float* weight, const float* bias, int si
 int ssm_conv1d_step(void* window, const void* x, const float* weight, const float* bias,
                     int silu, void* out, int64_t batch, int64_t dim, int64_t width, int io_dtype,
                     void* stream);
+
+/*
+ * Bytes of device workspace ssm_conv1d_bwd needs for these sizes (0 for
+ * invalid sizes): (width + 1) partial sums per channel for every 128 tokens
+ * of every sequence.
+ */
+size_t ssm_conv1d_bwd_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int64_t width);
+
+/*
+ * Backward pass of ssm_conv1d_fwd (the same x, weight, bias, silu, window_in,
+ * seq_lens, reset): the chain rule through "The Mamba block"'s convolution
+ * x_t = SiLU(sum_{i<k} w_i * xt_{t-i} + b_conv).  Given dout (batch, seqlen,
+ * dim) io dtype and dwindow_out (batch, width - 1, dim) io dtype or NULL, the
+ * gradient of window_out, it writes
+ *   dx          : (batch, seqlen, dim) io dtype (zero past a length);
+ *   dweight     : (dim, width) float32;  dbias : (dim) float32, or NULL;
+ *   dwindow_in  : (batch, width - 1, dim) io dtype, the gradient of
+ *                 window_in -- written only when window_in is given, and not
+ *                 the same memory.
+ * An input feeds the outputs of its document only (no gradient crosses a
+ * document start) and of real tokens only.  workspace: device memory of at
+ * least ssm_conv1d_bwd_workspace_size(...) bytes, 16-byte aligned, owned by
+ * the caller; the sums over tokens and batch entries behind dweight and
+ * dbias are added in a fixed order (repeated calls give identical bits).
+ * 1 <= width <= 4; one sequence (seqlen * dim elements) must stay below
+ * 2^31 bytes (else SSM_ERR_UNSUPPORTED).  Returns SSM_OK or an error status
+ * (SSM_ERR_SHAPE also when workspace_bytes is too small).
+ */
+int ssm_conv1d_bwd(const void* x, const float* weight, const float* bias, int silu,
+                   const void* window_in, const int32_t* seq_lens, const uint8_t* reset,
+                   const void* dout, const void* dwindow_out, void* dx, float* dweight,
+                   float* dbias, void* dwindow_in, void* workspace, size_t workspace_bytes,
+                   int64_t batch, int64_t seqlen, int64_t dim, int64_t width, int io_dtype,
+                   void* stream);
 
 /* issue-rate probes of ssm_alu_probe */
 #define SSM_PROBE_FMA 0 /* per iteration 8 x v_fma_f32 per lane */

@@ -70,6 +70,11 @@ def load_library():
         [i64] * 4 + [ci, vp]
     lib.ssm_scan_bwd_noalloc.restype = ci
     lib.ssm_scan_bwd_noalloc.argtypes = [vp] * 8 + [ci, ci] + [vp] * 15 + [i64] * 4 + [ci, vp]
+    lib.ssm_conv1d_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.ssm_conv1d_bwd_workspace_size.argtypes = [i64] * 4
+    lib.ssm_conv1d_bwd.restype = ci
+    lib.ssm_conv1d_bwd.argtypes = [vp] * 3 + [ci] + [vp] * 10 + [ctypes.c_size_t] + [i64] * 4 + \
+        [ci, vp]
     lib.ssm_scan_bwd.restype = ci
     lib.ssm_scan_bwd.argtypes = [vp] * 8 + [ci, ci] + [vp] * 13 + [ctypes.c_size_t] + \
         [i64] * 4 + [ci, vp]
@@ -304,6 +309,57 @@ def conv1d_step(window, x, weight, bias=None, silu=True, out=None):
     if st != 0:
         raise SsmError(st, "ssm_conv1d_step")
     return out
+
+
+def conv1d_bwd_workspace_size(batch, L, dim, width):
+    """Bytes of workspace ssm_conv1d_bwd needs for these sizes."""
+    return int(load_library().ssm_conv1d_bwd_workspace_size(batch, L, dim, width))
+
+
+def conv1d_bwd(x, weight, dout, bias=None, silu=True, window_in=None, seq_lens=None, reset=None,
+               dwindow_out=None, workspace=None):
+    """Gradients of conv1d_fwd on the GPU (same arguments): given dout like x
+    and optionally dwindow_out (batch, k - 1, dim), the gradient of the window
+    handed to decoding, returns a dict with dx (io dtype), dweight (dim, k)
+    float32 and, where their inputs were given, dbias (float32) and dwindow_in
+    (io dtype).  workspace: optional uint8 device tensor of at least
+    conv1d_bwd_workspace_size() bytes."""
+    import torch
+    lib = load_library()
+    batch, L, dim = x.shape
+    k = weight.shape[1]
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on the GPU")
+    io = x.dtype
+    _io_code(x)
+    _check(x, "x", (batch, L, dim), io, dev)
+    _check(dout, "dout", (batch, L, dim), io, dev)
+    _check(weight, "weight", (dim, k), torch.float32, dev)
+    _check(bias, "bias", (dim,), torch.float32, dev)
+    _check(window_in, "window_in", (batch, k - 1, dim), io, dev)
+    _check(dwindow_out, "dwindow_out", (batch, k - 1, dim), io, dev)
+    _check(seq_lens, "seq_lens", (batch,), torch.int32, dev)
+    if reset is not None:
+        if reset.dtype == torch.bool:
+            reset = reset.to(torch.uint8)
+        _check(reset, "reset", (batch, L), torch.uint8, dev)
+    need = conv1d_bwd_workspace_size(batch, L, dim, k)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    if workspace.numel() < need:
+        raise ValueError(f"workspace: need {need} bytes, got {workspace.numel()}")
+    g = dict(dx=torch.empty_like(x), dweight=torch.empty((dim, k), dtype=torch.float32, device=dev),
+             dbias=torch.empty((dim,), dtype=torch.float32, device=dev) if bias is not None else None,
+             dwindow_in=torch.empty_like(window_in) if window_in is not None else None)
+    st = lib.ssm_conv1d_bwd(_ptr(x), _ptr(weight), _ptr(bias), int(bool(silu)), _ptr(window_in),
+                            _ptr(seq_lens), _ptr(reset), _ptr(dout), _ptr(dwindow_out),
+                            _ptr(g["dx"]), _ptr(g["dweight"]), _ptr(g["dbias"]),
+                            _ptr(g["dwindow_in"]), _ptr(workspace), workspace.numel(), batch, L,
+                            dim, k, _io_code(x), _stream(dev))
+    if st != 0:
+        raise SsmError(st, "ssm_conv1d_bwd")
+    return g
 
 
 def scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, softplus=True,

@@ -36,6 +36,9 @@ template <>
 struct VecIO<float, 1> {
   using Raw = float;
   static __device__ __forceinline__ Raw load_raw(const float* p) { return *p; }
+  static __device__ __forceinline__ Raw bload(__amdgpu_buffer_rsrc_t r, uint32_t vo, uint32_t so) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)vo, (int)so, 0));
+  }
   static __device__ __forceinline__ void unpack(Raw r, float (&v)[1]) { v[0] = r; }
   static __device__ __forceinline__ void store(float* p, const float (&v)[1]) { *p = v[0]; }
 };
@@ -43,6 +46,12 @@ template <>
 struct VecIO<float, 4> {
   using Raw = float4;
   static __device__ __forceinline__ Raw load_raw(const float* p) { return *(const float4*)p; }
+  static __device__ __forceinline__ Raw bload(__amdgpu_buffer_rsrc_t r, uint32_t vo, uint32_t so) {
+    typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_t;
+    const u32x4_t q = __builtin_amdgcn_raw_buffer_load_b128(r, (int)vo, (int)so, 0);
+    return make_float4(__uint_as_float(q[0]), __uint_as_float(q[1]), __uint_as_float(q[2]),
+                       __uint_as_float(q[3]));
+  }
   static __device__ __forceinline__ void unpack(Raw q, float (&v)[4]) {
     v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
   }
@@ -54,6 +63,9 @@ template <>
 struct VecIO<bf16_bits, 1> {
   using Raw = uint32_t;
   static __device__ __forceinline__ Raw load_raw(const bf16_bits* p) { return *p; }
+  static __device__ __forceinline__ Raw bload(__amdgpu_buffer_rsrc_t r, uint32_t vo, uint32_t so) {
+    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)vo, (int)so, 0);
+  }
   static __device__ __forceinline__ void unpack(Raw r, float (&v)[1]) {
     v[0] = __uint_as_float(r << 16);
   }
@@ -65,6 +77,11 @@ template <>
 struct VecIO<bf16_bits, 4> {
   using Raw = uint2;
   static __device__ __forceinline__ Raw load_raw(const bf16_bits* p) { return *(const uint2*)p; }
+  static __device__ __forceinline__ Raw bload(__amdgpu_buffer_rsrc_t r, uint32_t vo, uint32_t so) {
+    typedef __attribute__((ext_vector_type(2))) unsigned int u32x2_t;
+    const u32x2_t q = __builtin_amdgcn_raw_buffer_load_b64(r, (int)vo, (int)so, 0);
+    return make_uint2(q[0], q[1]);
+  }
   static __device__ __forceinline__ void unpack(Raw q, float (&v)[4]) {
     v[0] = __uint_as_float(q.x << 16);
     v[1] = __uint_as_float(q.x & 0xffff0000u);
@@ -256,6 +273,346 @@ __global__ __launch_bounds__(256) void conv1d_step_kernel(
   if constexpr (K > 1) V::store(window + (b * (K - 1) + (K - 2)) * dim + c0, xt);
 }
 
+// ---- backward pass.  The chain rule through the forward above, in gather
+// form: with dpre_t = dout_t act'(pre_t) for the real tokens (0 past a length),
+//   dx_s  = sum_i w_i dpre_{s+i} [s visible from s + i] (+ the gradient of the
+//           window handed to decoding, where s is one of its inputs),
+//   dw_i  = sum_t dpre_t xt_{t-i} [visible],   dbias = sum_t dpre_t,
+// and the carried-in window's gradient from the first K - 1 tokens; "s
+// visible from t" means no document starts in (s, t].  A thread owns VEC
+// channels and runs of kBwdT tokens; for a run it reads x from K - 1 tokens
+// before to K - 1 after, dout to K - 1 after (the halos mostly come from L2),
+// recomputes pre and dpre over the run and its halo, and writes dx of the run.
+// dw and dbias are summed over a thread's runs, then over the block's waves
+// through LDS, into one partial row per block; a second kernel adds the rows
+// in a fixed order.
+constexpr int kBwdT = 8;       // tokens per run
+// word 3 of a raw buffer resource (no stride, 32-bit data format)
+constexpr int kConvBufferFlags = 0x00020000;
+constexpr int kBwdRuns = 4;    // runs per thread
+constexpr int kBwdSpan = kConvWaves * kBwdRuns * kBwdT;  // tokens per block (128)
+
+struct ConvBwdArgs {
+  const void *x, *state_in, *dout, *dstate_out;
+  const float *w, *bias;
+  const int32_t* seq_lens;
+  const uint8_t* reset;
+  void *dx, *dstate_in;
+  float* partial;  // (batch * nspans, K + 1, dim)
+  int64_t L, dim, nspans;
+  int silu;
+};
+
+__device__ __forceinline__ float act_prime(float v, bool silu) {
+  if (!silu) return 1.0f;
+  const float sg = rcp_hw(1.0f + exp2_hw(-v * kLog2e));
+  return sg * fmaf(v, 1.0f - sg, 1.0f);
+}
+
+template <typename IO, int K, int VEC>
+__global__ __launch_bounds__(64 * kConvWaves) void conv1d_bwd_kernel(const ConvBwdArgs p) {
+  using V = VecIO<IO, VEC>;
+  constexpr int NX = kBwdT + 2 * (K - 1);  // x at t0 - (K - 1) .. t0 + kBwdT + K - 2
+  constexpr int ND = kBwdT + K - 1;        // dout, dpre at t0 .. t0 + kBwdT + K - 2
+  static_assert(NX <= 32, "reset flags of a run fit one word");
+  __shared__ float red[kConvWaves][VEC * (K + 1)][64];
+
+  const IO* __restrict__ x = (const IO*)p.x;
+  const IO* __restrict__ dout = (const IO*)p.dout;
+  const IO* __restrict__ sin = (const IO*)p.state_in;
+  const IO* __restrict__ dso = (const IO*)p.dstate_out;
+  const int64_t L = p.L, dim = p.dim, nvec = dim / VEC;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar run bounds
+  const int64_t cv = (int64_t)blockIdx.x * 64 + lane;
+  const bool cok = cv < nvec;
+  const int64_t c0 = (cok ? cv : nvec - 1) * VEC;  // loads of idle lanes stay in bounds
+  const int64_t span = blockIdx.y, b = blockIdx.z;
+  int64_t len = L;
+  if (p.seq_lens) {
+    const int64_t sl = p.seq_lens[b];
+    len = sl < 0 ? 0 : (sl < L ? sl : L);
+  }
+  // one buffer resource per tensor and sequence (the launch keeps a
+  // sequence's bytes below 2^32): rows at scalar offsets, channels at the
+  // lane's offset
+  const uint32_t loff = (uint32_t)c0 * (uint32_t)sizeof(IO);
+  const uint32_t rowb = (uint32_t)dim * (uint32_t)sizeof(IO);
+  const __amdgpu_buffer_rsrc_t rx =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(x + b * L * dim), (short)0, -1, kConvBufferFlags);
+  const __amdgpu_buffer_rsrc_t rd =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(dout + b * L * dim), (short)0, -1, kConvBufferFlags);
+  const __amdgpu_buffer_rsrc_t rwin = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(sin ? sin + b * (K - 1) * dim : x), (short)0, -1, kConvBufferFlags);
+  const bool silu = p.silu != 0;
+
+  float wt[VEC][K], bs[VEC];
+#pragma unroll
+  for (int v = 0; v < VEC; ++v) {
+#pragma unroll
+    for (int i = 0; i < K; ++i) wt[v][i] = p.w[(c0 + v) * K + i];
+    bs[v] = p.bias ? p.bias[c0 + v] : 0.0f;
+  }
+  float dw[VEC][K], db[VEC];
+#pragma unroll
+  for (int v = 0; v < VEC; ++v) {
+    db[v] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < K; ++i) dw[v][i] = 0.0f;
+  }
+  // the gradient of the window handed to decoding: entry j is the input at
+  // len - (K - 1) + j
+  auto dwo = [&](int64_t j, float (&o)[VEC]) {
+    vload<IO, VEC>(dso + (b * (K - 1) + j) * dim + c0, o);
+  };
+
+  for (int r = 0; r < kBwdRuns; ++r) {
+    const int64_t t0 = span * kBwdSpan + (int64_t)(wave * kBwdRuns + r) * kBwdT;
+    if (t0 >= L) break;  // wave-uniform
+    // ---- loads first: x (window entries before token 0), dout, document starts
+    // buffer loads: the row's byte offset is scalar (rows clamped into the
+    // sequence), the lane's channels its 32-bit vector offset
+    typename V::Raw xr[NX], dr[ND];
+    const int32_t tl = (int32_t)(L - 1);
+#pragma unroll
+    for (int q = 0; q < NX; ++q) {
+      const int32_t pos = (int32_t)t0 - (K - 1) + q;
+      if (pos < 0 && sin)  // the carried-in window (first run only)
+        xr[q] = V::bload(rwin, loff, (uint32_t)(K - 1 + pos) * rowb);
+      else
+        xr[q] = V::bload(rx, loff, (uint32_t)(pos < 0 ? 0 : (pos < tl ? pos : tl)) * rowb);
+    }
+#pragma unroll
+    for (int q = 0; q < ND; ++q) {
+      const int32_t pos = (int32_t)t0 + q;
+      dr[q] = V::bload(rd, loff, (uint32_t)(pos < tl ? pos : tl) * rowb);
+    }
+    uint32_t starts = 0;  // bit q: a document starts at t0 - (K - 1) + q (real tokens only)
+    if (p.reset) {
+#pragma unroll
+      for (int q = 0; q < NX; ++q) {
+        const int64_t pos = t0 - (K - 1) + q;
+        if (pos >= 0 && pos < len && p.reset[b * L + pos]) starts |= 1u << q;
+      }
+      starts = __builtin_amdgcn_readfirstlane(starts);  // the same for every lane
+    }
+    // no document starts at positions qa + 1 .. qb (window indices)
+    auto visible = [&](int qa, int qb) -> bool {
+      const uint32_t m = (qb >= 31 ? 0xffffffffu : ((1u << (qb + 1)) - 1u)) & ~((1u << (qa + 1)) - 1u);
+      return (starts & m) == 0;
+    };
+    // x at window index q, or 0 where the forward read a zero (before token 0
+    // with no window given)
+    auto xin = [&](int q, float (&o)[VEC]) {
+      V::unpack(xr[q], o);
+      if (t0 - (K - 1) + q < 0 && !sin) {
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) o[v] = 0.0f;
+      }
+    };
+
+    // ---- one pass over the positions t0 - (K - 1) .. t0 + kBwdT + K - 2 with
+    // sliding windows: xw[i] is x i positions back, dpw[i] dpre i positions
+    // back.  At position p: dpre_p (p >= t0; zero past the length), the dw and
+    // dbias terms of p (p in the run), and dx of s = p - (K - 1) (s in the run).
+    float xw[K][VEC], dpw[K][VEC];
+#pragma unroll
+    for (int i = 0; i < K; ++i)
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) xw[i][v] = dpw[i][v] = 0.0f;
+#pragma unroll
+    for (int q = 0; q < NX; ++q) {
+      // one position at a time: unpacking every loaded bf16 row at once would
+      // hold them all as fp32
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = K - 1; i >= 1; --i)
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) xw[i][v] = xw[i - 1][v];
+      xin(q, xw[0]);
+      if (q >= K - 1) {  // p = t0 + j
+        const int j = q - (K - 1);
+        const int64_t pp = t0 + j;
+        float pre[VEC];
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) pre[v] = bs[v];
+#pragma unroll
+        for (int i = 0; i < K; ++i) {
+          const bool vis = visible(q - i, q);
+#pragma unroll
+          for (int v = 0; v < VEC; ++v) pre[v] = fmaf(wt[v][i], vis ? xw[i][v] : 0.0f, pre[v]);
+        }
+        float dov[VEC];
+        V::unpack(dr[j], dov);
+#pragma unroll
+        for (int i = K - 1; i >= 1; --i)
+#pragma unroll
+          for (int v = 0; v < VEC; ++v) dpw[i][v] = dpw[i - 1][v];
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) dpw[0][v] = pp < len ? dov[v] * act_prime(pre[v], silu) : 0.0f;
+        if (j < kBwdT && pp < len) {
+#pragma unroll
+          for (int i = 0; i < K; ++i) {
+            const bool vis = visible(q - i, q);
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) dw[v][i] = fmaf(dpw[0][v], vis ? xw[i][v] : 0.0f, dw[v][i]);
+          }
+#pragma unroll
+          for (int v = 0; v < VEC; ++v) db[v] += dpw[0][v];
+        }
+      }
+      if (q >= 2 * (K - 1)) {  // dx of s = t0 + m
+        const int m = q - 2 * (K - 1);
+        const int qs = q - (K - 1);
+        const int64_t s = t0 + m;
+        float acc[VEC];
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) acc[v] = 0.0f;
+#pragma unroll
+        for (int i = 0; i < K; ++i) {  // dpre at s + i is dpw[K - 1 - i]
+          const bool vis = visible(qs, qs + i);
+#pragma unroll
+          for (int v = 0; v < VEC; ++v) acc[v] = fmaf(wt[v][i], vis ? dpw[K - 1 - i][v] : 0.0f, acc[v]);
+        }
+        if (dso && s < len && s >= len - (K - 1) && visible(qs, (int)(len - 1 - t0) + K - 1)) {
+          float o[VEC];
+          dwo(s - (len - (K - 1)), o);
+#pragma unroll
+          for (int v = 0; v < VEC; ++v) acc[v] += o[v];
+        }
+        if (cok && s < L) V::store((IO*)p.dx + (b * L + s) * dim + c0, acc);
+      }
+      // the carried-in window's gradient, in the first run of the sequence,
+      // once dpre at positions 0 .. K - 2 is known (dpre at P is dpw[K - 2 - P])
+      if (K > 1 && q == 2 * K - 3 && t0 == 0 && sin && p.dstate_in && cok) {
+#pragma unroll
+        for (int jw = 0; jw < K - 1; ++jw) {
+          const int sw = -(K - 1) + jw;  // the window entry's position
+          float acc[VEC];
+#pragma unroll
+          for (int v = 0; v < VEC; ++v) acc[v] = 0.0f;
+#pragma unroll
+          for (int i = 0; i < K; ++i) {
+            if (sw + i >= 0) {
+              const bool vis = visible(jw, jw + i);
+#pragma unroll
+              for (int v = 0; v < VEC; ++v)
+                acc[v] = fmaf(wt[v][i], vis ? dpw[K - 2 - (sw + i)][v] : 0.0f, acc[v]);
+            }
+          }
+          // a sequence shorter than the window hands on entries of this one
+          if (dso && sw >= len - (K - 1) && (len == 0 || visible(jw, (int)(len - 1) + K - 1))) {
+            float o[VEC];
+            dwo(sw - (len - (K - 1)), o);
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) acc[v] += o[v];
+          }
+          V::store((IO*)p.dstate_in + (b * (K - 1) + jw) * dim + c0, acc);
+        }
+      }
+    }
+  }
+
+  // no tokens at all: the window passes through
+  if (L == 0 && wave == 0 && sin && p.dstate_in && cok) {
+#pragma unroll
+    for (int j = 0; j < K - 1; ++j) {
+      float o[VEC];
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) o[v] = 0.0f;
+      if (dso) dwo(j, o);
+      V::store((IO*)p.dstate_in + (b * (K - 1) + j) * dim + c0, o);
+    }
+  }
+
+  // ---- dw, dbias: the block's waves through LDS, one partial row per block
+#pragma unroll
+  for (int v = 0; v < VEC; ++v) {
+#pragma unroll
+    for (int i = 0; i < K; ++i) red[wave][v * (K + 1) + i][lane] = dw[v][i];
+    red[wave][v * (K + 1) + K][lane] = db[v];
+  }
+  __syncthreads();
+  if (wave == 0 && cok) {
+    float* row = p.partial + (b * p.nspans + span) * (K + 1) * dim;
+#pragma unroll
+    for (int i = 0; i <= K; ++i) {
+      float o[VEC];
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) {
+        float sum = 0.0f;
+#pragma unroll
+        for (int wv = 0; wv < kConvWaves; ++wv) sum += red[wv][v * (K + 1) + i][lane];
+        o[v] = sum;
+      }
+      VecIO<float, VEC>::store(row + i * dim + c0, o);
+    }
+  }
+}
+
+// dw (dim, K) and dbias from the partial rows.  A block takes 32 consecutive
+// sums; its 8 thread groups add every 8th row each (group g: rows g, g + 8,
+// ...), and the 8 group sums are added in group order: a fixed order.
+constexpr int kFinOut = 32, kFinGroups = 8;
+__global__ __launch_bounds__(kFinOut * kFinGroups) void conv1d_bwd_finalize(
+    const float* __restrict__ partial, float* __restrict__ dw, float* __restrict__ dbias,
+    const int64_t rows, const int64_t dim, const int K) {
+  __shared__ float part[kFinGroups][kFinOut];
+  const int o = threadIdx.x % kFinOut, g = threadIdx.x / kFinOut;
+  const int64_t e = (int64_t)blockIdx.x * kFinOut + o;  // (i, c) with i = e / dim
+  const int64_t n = (int64_t)(K + 1) * dim;
+  float sum = 0.0f;
+  if (e < n) {
+    const int i = (int)(e / dim);
+    const int64_t c = e - (int64_t)i * dim;
+    for (int64_t r = g; r < rows; r += kFinGroups) sum += partial[(r * (K + 1) + i) * dim + c];
+  }
+  part[g][o] = sum;
+  __syncthreads();
+  if (g == 0 && e < n) {
+    float tot = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kFinGroups; ++j) tot += part[j][o];
+    const int i = (int)(e / dim);
+    const int64_t c = e - (int64_t)i * dim;
+    if (i < K) dw[c * K + i] = tot;
+    else if (dbias) dbias[c] = tot;
+  }
+}
+
+template <typename IO, int K, int VEC>
+hipError_t bwd_launch(const ConvBwdParams& q, hipStream_t stream) {
+  ConvBwdArgs a;
+  a.x = q.x; a.state_in = q.state_in; a.dout = q.dout; a.dstate_out = q.dstate_out;
+  a.w = q.w; a.bias = q.bias; a.seq_lens = q.seq_lens; a.reset = q.reset;
+  a.dx = q.dx; a.dstate_in = q.dstate_in; a.partial = (float*)q.workspace;
+  a.L = q.L; a.dim = q.dim; a.nspans = conv1d_bwd_spans(q.L); a.silu = q.silu;
+  const int64_t nvec = q.dim / VEC;
+  if (q.batch > 0) {  // no batch entries: the sums below are zero
+    const dim3 grid((unsigned)((nvec + 63) / 64), (unsigned)a.nspans, (unsigned)q.batch);
+    hipLaunchKernelGGL((conv1d_bwd_kernel<IO, K, VEC>), grid, dim3(64 * kConvWaves), 0, stream,
+                       a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int64_t n = (int64_t)(K + 1) * q.dim;
+  hipLaunchKernelGGL(conv1d_bwd_finalize, dim3((unsigned)((n + kFinOut - 1) / kFinOut)),
+                     dim3(kFinOut * kFinGroups), 0, stream, (const float*)a.partial, q.dw,
+                     q.dbias, q.batch * a.nspans, q.dim, K);
+  return hipGetLastError();
+}
+
+template <typename IO, int VEC>
+hipError_t bwd_by_width(const ConvBwdParams& q, hipStream_t stream) {
+  switch (q.k) {
+    case 1: return bwd_launch<IO, 1, VEC>(q, stream);
+    case 2: return bwd_launch<IO, 2, VEC>(q, stream);
+    case 3: return bwd_launch<IO, 3, VEC>(q, stream);
+    case 4: return bwd_launch<IO, 4, VEC>(q, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 template <typename IO, int K, int VEC>
 hipError_t fwd_launch(const ConvParams& p, hipStream_t stream) {
   const int64_t nvec = p.dim / VEC;
@@ -305,6 +662,18 @@ hipError_t launch_conv1d(const ConvParams& p, int io_dtype, bool vec4, bool step
                          hipStream_t stream) {
   if (io_dtype == 1) return by_vec<bf16_bits>(p, vec4, step, stream);
   return by_vec<float>(p, vec4, step, stream);
+}
+
+int64_t conv1d_bwd_spans(int64_t L) { return L > 0 ? (L + kBwdSpan - 1) / kBwdSpan : 1; }
+
+size_t conv1d_bwd_workspace_bytes(int64_t batch, int64_t L, int64_t dim, int64_t k) {
+  return (size_t)batch * (size_t)conv1d_bwd_spans(L) * (size_t)(k + 1) * (size_t)dim * sizeof(float);
+}
+
+hipError_t launch_conv1d_bwd(const ConvBwdParams& q, int io_dtype, bool vec4, hipStream_t stream) {
+  if (io_dtype == 1)
+    return vec4 ? bwd_by_width<bf16_bits, 4>(q, stream) : bwd_by_width<bf16_bits, 1>(q, stream);
+  return vec4 ? bwd_by_width<float, 4>(q, stream) : bwd_by_width<float, 1>(q, stream);
 }
 
 }  // namespace ssm66

@@ -472,6 +472,64 @@ int ssm_conv1d_fwd(const void* x, const float* weight, const float* bias, int si
   return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 
+static int conv_bwd_shape(int64_t batch, int64_t seqlen, int64_t dim, int64_t width) {
+  if (batch < 0 || seqlen < 0 || dim < 0) return SSM_ERR_SHAPE;
+  if (width < 1 || width > 4) return SSM_ERR_SHAPE;
+  int64_t tmp;
+  if (!mul3(batch, seqlen, dim, &tmp) || !mul3(batch, width, dim, &tmp) ||
+      !mul3(batch, (seqlen + 127) / 128 + 1, (width + 1) * dim, &tmp))
+    return SSM_ERR_SHAPE;
+  return SSM_OK;
+}
+
+size_t ssm_conv1d_bwd_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int64_t width) {
+  if (conv_bwd_shape(batch, seqlen, dim, width) != SSM_OK) return 0;
+  return ssm66::conv1d_bwd_workspace_bytes(batch, seqlen, dim, width);
+}
+
+int ssm_conv1d_bwd(const void* x, const float* weight, const float* bias, int silu,
+                   const void* window_in, const int32_t* seq_lens, const uint8_t* reset,
+                   const void* dout, const void* dwindow_out, void* dx, float* dweight,
+                   float* dbias, void* dwindow_in, void* workspace, size_t workspace_bytes,
+                   int64_t batch, int64_t seqlen, int64_t dim, int64_t width, int io_dtype,
+                   void* stream) {
+  int st = conv_bwd_shape(batch, seqlen, dim, width);
+  if (st != SSM_OK) return st;
+  if (io_dtype != SSM_F32 && io_dtype != SSM_BF16) return SSM_ERR_DTYPE;
+  if (silu != 0 && silu != 1) return SSM_ERR_FLAG;
+  if (dim == 0) return SSM_OK;
+  if (!weight || !dweight) return SSM_ERR_NULL;
+  if (seqlen > 0 && (!x || !dout || !dx)) return SSM_ERR_NULL;
+  if (width > 1 && window_in && dwindow_in == window_in) return SSM_ERR_FLAG;  // no in-place
+  const size_t need = ssm66::conv1d_bwd_workspace_bytes(batch, seqlen, dim, width);
+  if (!workspace) return SSM_ERR_NULL;
+  if (workspace_bytes < need) return SSM_ERR_SHAPE;
+  const size_t es = io_dtype == SSM_BF16 ? 2 : 4;
+  const void* io_ptrs[6] = {x, dout, dx, window_in, dwindow_out, dwindow_in};
+  for (const void* q : io_ptrs)
+    if (q && !aligned(q, es)) return SSM_ERR_ALIGN;
+  const void* f32_ptrs[5] = {weight, bias, seq_lens, dweight, dbias};
+  for (const void* q : f32_ptrs)
+    if (q && !aligned(q, 4)) return SSM_ERR_ALIGN;
+  if (!aligned(workspace, 16)) return SSM_ERR_ALIGN;
+  // grid: 64 channel vectors in x, 128-token spans in y, batch in z; one
+  // sequence's bytes within 32-bit buffer offsets
+  if ((seqlen + 127) / 128 > 65535 || batch > 65535 || dim / 64 + 1 > 0x7fffffff)
+    return SSM_ERR_UNSUPPORTED;
+  if (seqlen * dim > (int64_t)0x7fffffff / (int64_t)es) return SSM_ERR_UNSUPPORTED;
+  bool vec4 = dim % 4 == 0;
+  for (const void* q : io_ptrs)
+    if (q && !aligned(q, 4 * es)) vec4 = false;
+
+  ssm66::ConvBwdParams p;
+  p.x = x; p.w = weight; p.bias = bias; p.state_in = window_in; p.seq_lens = seq_lens;
+  p.reset = reset; p.dout = dout; p.dstate_out = dwindow_out; p.dx = dx; p.dw = dweight;
+  p.dbias = dbias; p.dstate_in = dwindow_in; p.workspace = workspace;
+  p.batch = batch; p.L = seqlen; p.dim = dim; p.k = width; p.silu = silu;
+  const hipError_t e = ssm66::launch_conv1d_bwd(p, io_dtype, vec4, (hipStream_t)stream);
+  return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
 int ssm_conv1d_step(void* window, const void* x, const float* weight, const float* bias,
                     int silu, void* out, int64_t batch, int64_t dim, int64_t width, int io_dtype,
                     void* stream) {

@@ -81,6 +81,29 @@ hipError_t launch_scan_fwd(const ScanParams& p, int io_dtype, int G, int NG, boo
                            hipStream_t stream);
 // step = false: the sequence kernel; true: one decoding step.  vec4: dim is a
 // multiple of 4 and the io pointers are aligned to 4 elements.
+// The convolution's backward pass: gradients of x, w, bias and the
+// carried-in window given dout and the gradient of the window handed on.
+struct ConvBwdParams {
+  const void* x;            // (batch, L, dim) io dtype
+  const float* w;           // (dim, k)
+  const float* bias;        // nullable (dim)
+  const void* state_in;     // nullable (batch, k - 1, dim)
+  const int32_t* seq_lens;  // nullable (batch)
+  const uint8_t* reset;     // nullable (batch, L)
+  const void* dout;         // (batch, L, dim) io dtype
+  const void* dstate_out;   // nullable (batch, k - 1, dim) io dtype
+  void* dx;                 // (batch, L, dim) io dtype
+  float* dw;                // (dim, k)
+  float* dbias;             // nullable (dim)
+  void* dstate_in;          // nullable (batch, k - 1, dim) io dtype; written when state_in is given
+  void* workspace;          // conv1d_bwd_workspace_bytes(...) bytes
+  int64_t batch, L, dim, k;
+  int silu;
+};
+int64_t conv1d_bwd_spans(int64_t L);
+size_t conv1d_bwd_workspace_bytes(int64_t batch, int64_t L, int64_t dim, int64_t k);
+hipError_t launch_conv1d_bwd(const ConvBwdParams& q, int io_dtype, bool vec4, hipStream_t stream);
+
 hipError_t launch_conv1d(const ConvParams& p, int io_dtype, bool vec4, bool step,
                          hipStream_t stream);
 size_t scan_bwd_ckpt_bytes(int64_t batch, int64_t L, int64_t dim, int64_t N);

@@ -39,7 +39,8 @@ def test_exports_every_declared_symbol(lib):
                           "ssm_scan_bwd_workspace_size", "ssm_step", "ssm_ssd_fwd",
                           "ssm_conv1d_fwd", "ssm_conv1d_step", "ssm_status_string",
                           "ssm_abi_version", "ssm_scan_kernel_name", "ssm_scan_fwd_kernel",
-                          "ssm_alu_probe", "ssm_scan_bwd_noalloc"}
+                          "ssm_alu_probe", "ssm_scan_bwd_noalloc", "ssm_conv1d_bwd",
+                          "ssm_conv1d_bwd_workspace_size"}
     raw = ctypes.CDLL(ssm.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), f"{n} not exported"
@@ -369,3 +370,33 @@ def test_noalloc_backward_validation(lib):
     assert call(1, 2048, 1536, 16, u=MISALIGNED) == c["SSM_ERR_ALIGN"]
     assert call(1, 2048, 1536, 17) == c["SSM_ERR_SHAPE"]
     assert call(0, 2048, 1536, 16) == c["SSM_OK"]  # no rows: nothing to do, no HIP call
+
+
+def test_conv_backward_validation(lib):
+    """ssm_conv1d_bwd checks its arguments before any HIP call."""
+    c = _header_constants()
+    ws = lib.ssm_conv1d_bwd_workspace_size
+    assert ws(2, 300, 64, 4) == 2 * 3 * 5 * 64 * 4   # (width + 1) sums per channel per 128 tokens
+    assert ws(2, 0, 64, 4) == 2 * 1 * 5 * 64 * 4
+    assert ws(2, 10, 64, 5) == 0 and ws(-1, 10, 64, 4) == 0
+
+    def call(**kw):
+        a = dict(x=FAKE, w=FAKE, bias=None, silu=1, win=None, lens=None, reset=None, dout=FAKE,
+                 dwo=None, dx=FAKE, dw=FAKE, db=None, dwin=None, ws=FAKE, wsb=1 << 40, batch=2,
+                 L=10, dim=64, k=4, io=1)
+        a.update(kw)
+        return lib.ssm_conv1d_bwd(a["x"], a["w"], a["bias"], a["silu"], a["win"], a["lens"],
+                                  a["reset"], a["dout"], a["dwo"], a["dx"], a["dw"], a["db"],
+                                  a["dwin"], a["ws"], a["wsb"], a["batch"], a["L"], a["dim"],
+                                  a["k"], a["io"], None)
+
+    assert call(k=0) == c["SSM_ERR_SHAPE"] and call(k=5) == c["SSM_ERR_SHAPE"]
+    assert call(io=2) == c["SSM_ERR_DTYPE"]
+    assert call(silu=2) == c["SSM_ERR_FLAG"]
+    assert call(dw=None) == c["SSM_ERR_NULL"] and call(dout=None) == c["SSM_ERR_NULL"]
+    assert call(ws=None) == c["SSM_ERR_NULL"]
+    assert call(wsb=16) == c["SSM_ERR_SHAPE"]
+    assert call(dx=MISALIGNED) == c["SSM_ERR_ALIGN"]
+    assert call(lens=MISALIGNED) == c["SSM_ERR_ALIGN"]
+    assert call(win=FAKE, dwin=FAKE) == c["SSM_ERR_FLAG"]  # not in place
+    assert call(dim=0) == c["SSM_OK"]

@@ -143,3 +143,132 @@ def test_conv_full_size_sampled():
     chd = torch.from_numpy(ch).to(DEV)
     assert_close(to_host64(out.index_select(2, chd)), ro, "bf16", "out")
     np.testing.assert_array_equal(to_host64(win.index_select(2, chd)), rw)
+
+
+# ------------------------------------------------------------- backward pass
+
+def _dout(shape, io, seed):
+    x = np.random.default_rng(seed).normal(size=shape).astype(np.float32)
+    return W.to_bf16_bits(x) if io == "bf16" else x
+
+
+def _bwd_compare(g, r, io, what):
+    """dx, dwindow_in: fp32 within 1e-4 (1 + |ref|) elementwise (a sum of at
+    most k products); dweight, dbias (sums over every token of every sequence)
+    within 2e-5 (1 + max |ref|) of the tensor's scale; bf16 io: relative RMS
+    1e-2 for everything (inputs and dout are the same bf16 bits on both sides,
+    dx is rounded to bf16 once)."""
+    for k, ref in r.items():
+        if ref is None:
+            assert g[k] is None, k
+            continue
+        got = to_host64(g[k])
+        assert got.shape == ref.shape, k
+        assert np.all(np.isfinite(got)), f"{what} {k}"
+        if io == "bf16":
+            assert_close(got, ref, "bf16", f"{what} {k}")
+        elif k in ("dweight", "dbias"):
+            err = np.abs(got - ref).max() / (1.0 + np.abs(ref).max())
+            assert err <= 2e-5, f"{what} {k}: {err:.2e}"
+        else:
+            assert_close(got, ref, "f32", f"{what} {k}")
+
+
+def _bwd_run(inp, dout, silu=True, window_in=None, seq_lens=None, reset=None, dwo=None):
+    io = inp["io"]
+    g = ssm.conv1d_bwd(to_dev(inp["x"], io), to_dev(inp["w"], "f32"), to_dev(dout, io),
+                       bias=to_dev(inp["bias"], "f32"), silu=silu,
+                       window_in=None if window_in is None else to_dev(window_in, io),
+                       seq_lens=None if seq_lens is None else torch.from_numpy(seq_lens).to(DEV),
+                       reset=None if reset is None else torch.from_numpy(reset).to(DEV),
+                       dwindow_out=None if dwo is None else to_dev(dwo, io))
+    torch.cuda.synchronize()
+    r = oracle.conv1d_bwd(f64(inp["x"], io), inp["w"], f64(dout, io), bias=inp["bias"], silu=silu,
+                          state_in=None if window_in is None else f64(window_in, io),
+                          seq_lens=seq_lens, reset=reset,
+                          dstate_out=None if dwo is None else f64(dwo, io))
+    r = dict(dx=r["dx"], dweight=r["dweight"], dbias=r["dbias"], dwindow_in=r["dstate_in"])
+    return g, r
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("k", [1, 2, 3, 4])
+@pytest.mark.parametrize("dim", [64, 70])
+@pytest.mark.parametrize("silu", [True, False])
+def test_conv_bwd(io, k, dim, silu):
+    """Three sequences of 300 tokens (three 128-token spans, the last ragged),
+    a carried-in window and the gradient of the window handed on."""
+    inp = _inputs(3, 300, dim, k, io, seed=60 + k)
+    win0 = _window(3, k, dim, io, seed=61 + k)
+    dout = _dout((3, 300, dim), io, 62 + k)
+    dwo = _dout((3, k - 1, dim), io, 63 + k)
+    g, r = _bwd_run(inp, dout, silu=silu, window_in=win0, dwo=dwo)
+    _bwd_compare(g, r, io, f"bwd k={k} dim={dim} silu={silu}")
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("k", [2, 4])
+@pytest.mark.parametrize("dim", [64, 70])
+def test_conv_bwd_lengths_and_resets(io, k, dim):
+    """Lengths (full, one inside a span, one shorter than the window, empty)
+    and document starts (at token 0, mid-run, on a run edge, two in a row,
+    one past a length), with and without a carried-in window."""
+    batch, L = 4, 300
+    inp = _inputs(batch, L, dim, k, io, seed=70 + k)
+    dout = _dout((batch, L, dim), io, 71)
+    dwo = _dout((batch, k - 1, dim), io, 72)
+    lens = np.array([300, 133, 2, 0], dtype=np.int32)
+    reset = np.zeros((batch, L), dtype=np.uint8)
+    reset[0, [0, 5, 8, 9, 128, 250]] = 1
+    reset[1, [7, 64, 200]] = 1
+    reset[2, [1]] = 1
+    for win0 in (None, _window(batch, k, dim, io, seed=73)):
+        g, r = _bwd_run(inp, dout, window_in=win0, seq_lens=lens, reset=reset, dwo=dwo)
+        _bwd_compare(g, r, io, f"varlen k={k} dim={dim} window={win0 is not None}")
+        dx = to_host64(g["dx"])
+        for b, n in enumerate(lens):
+            assert np.all(dx[b, n:] == 0.0)
+
+
+def test_conv_bwd_no_tokens_and_deterministic():
+    """No tokens: the window's gradient passes through, dw and dbias are zero;
+    two calls give the same bits."""
+    k, dim = 4, 64
+    x = torch.zeros((2, 0, dim), dtype=torch.float32, device=DEV)
+    w = torch.randn((dim, k), device=DEV)
+    win0 = torch.randn((2, k - 1, dim), device=DEV)
+    dwo = torch.randn((2, k - 1, dim), device=DEV)
+    g = ssm.conv1d_bwd(x, w, x, bias=torch.zeros(dim, device=DEV), window_in=win0,
+                       dwindow_out=dwo)
+    torch.cuda.synchronize()
+    assert torch.equal(g["dwindow_in"], dwo)
+    assert torch.all(g["dweight"] == 0) and torch.all(g["dbias"] == 0)
+    inp = _inputs(2, 500, 96, 4, "bf16", seed=74)
+    dout = _dout((2, 500, 96), "bf16", 75)
+    args = (to_dev(inp["x"], "bf16"), to_dev(inp["w"], "f32"), to_dev(dout, "bf16"))
+    g1 = ssm.conv1d_bwd(*args, bias=to_dev(inp["bias"], "f32"))
+    g2 = ssm.conv1d_bwd(*args, bias=to_dev(inp["bias"], "f32"))
+    torch.cuda.synchronize()
+    for key in ("dx", "dweight", "dbias"):
+        assert torch.equal(g1[key], g2[key]), key
+
+
+def test_conv_bwd_full_size_sampled():
+    """The Mamba-130M layer's convolution (batch 8, L 2048, D 1536, k 4, bf16)
+    at full size: channels are independent, so the oracle on sampled channels
+    is the exact reference for their dx, dweight and dbias."""
+    cfg = W.CONV_CONFIGS["conv130m"]
+    inp = W.conv_inputs(cfg)
+    dout = _dout((cfg.batch, cfg.L, cfg.dim), "bf16", 76)
+    g = ssm.conv1d_bwd(to_dev(inp["x"], "bf16"), to_dev(inp["w"], "f32"), to_dev(dout, "bf16"),
+                       bias=to_dev(inp["bias"], "f32"))
+    torch.cuda.synchronize()
+    ch = np.array([0, 1, 5, 700, 1535])
+    sub = W.conv_inputs(cfg, channels=ch)
+    r = oracle.conv1d_bwd(f64(sub["x"], "bf16"), sub["w"], f64(dout[:, :, ch], "bf16"),
+                          bias=sub["bias"])
+    chd = torch.from_numpy(ch).to(DEV)
+    got = dict(dx=g["dx"].index_select(2, chd), dweight=g["dweight"].index_select(0, chd),
+               dbias=g["dbias"].index_select(0, chd), dwindow_in=None)
+    _bwd_compare(got, dict(dx=r["dx"], dweight=r["dweight"], dbias=r["dbias"], dwindow_in=None),
+                 "bf16", "full size")
