@@ -180,8 +180,9 @@ __device__ __forceinline__ float lane_value(float v, int l) {
 // block it is taken directly.  A tile's lane values (s = 16 sb + 4 lk + i,
 // t = 16 W + lr) are, rounded to bf16, exactly the B operand of the K = 16
 // MFMA (4 consecutive k per lane), so Y^T += x^T S^T takes them from registers.
-template <int W, int N, class Sm>
-__device__ __forceinline__ void scores_times_x(const Sm& sm, int cur, const ChunkConsts& kc,
+template <int W, int N, int BS>
+__device__ __forceinline__ void scores_times_x(const __bf16 (*Bs)[BS], const __bf16 (*Xs)[kPS],
+                                               const ChunkConsts& kc,
                                                const u32x4 (&cC)[N / 32], int lane, f32x4& y) {
   const int lr = lane & 15, lk = lane >> 4;
   f32x4 g[W + 1];
@@ -191,7 +192,7 @@ __device__ __forceinline__ void scores_times_x(const Sm& sm, int cur, const Chun
   for (int k = 0; k < N / 32; ++k)
 #pragma unroll
     for (int sb = 0; sb <= W; ++sb)
-      g[sb] = mfma16(*(const bf16x8*)&sm.Bs[cur][16 * sb + lr][kn(k, lk)], as_bf16x8(cC[k]),
+      g[sb] = mfma16(*(const bf16x8*)&Bs[16 * sb + lr][kn(k, lk)], as_bf16x8(cC[k]),
                      g[sb]);
   const float ct = kc.cuml[16 * W + lr];
 #pragma unroll
@@ -215,7 +216,7 @@ __device__ __forceinline__ void scores_times_x(const Sm& sm, int cur, const Chun
       }
     }
     const i16x4 sf = __builtin_bit_cast(i16x4, u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])});
-    y = mfma16k16(tr_frag4<kPS>(&sm.Xs[cur][16 * sb][0], lane), sf, y);
+    y = mfma16k16(tr_frag4<kPS>(&Xs[16 * sb][0], lane), sf, y);
   }
 }
 
@@ -417,10 +418,10 @@ __global__ __launch_bounds__(256, 3) void ssd_fwd_kernel(const SSDArgs p) {
       for (int i = 0; i < 4; ++i) y[i] *= e;
     }
     switch (w) {
-      case 0: scores_times_x<0, N>(sm, cur, kc, cC, lane, y); break;
-      case 1: scores_times_x<1, N>(sm, cur, kc, cC, lane, y); break;
-      case 2: scores_times_x<2, N>(sm, cur, kc, cC, lane, y); break;
-      default: scores_times_x<3, N>(sm, cur, kc, cC, lane, y); break;
+      case 0: scores_times_x<0, N, Sm::BS>(sm.Bs[cur], sm.Xs[cur], kc, cC, lane, y); break;
+      case 1: scores_times_x<1, N, Sm::BS>(sm.Bs[cur], sm.Xs[cur], kc, cC, lane, y); break;
+      case 2: scores_times_x<2, N, Sm::BS>(sm.Bs[cur], sm.Xs[cur], kc, cC, lane, y); break;
+      default: scores_times_x<3, N, Sm::BS>(sm.Bs[cur], sm.Xs[cur], kc, cC, lane, y); break;
     }
     // ---- epilogue: skip, gate; 4 channels of token tz, stored at the end
     // of the chunk
@@ -486,9 +487,269 @@ __global__ __launch_bounds__(256, 3) void ssd_fwd_kernel(const SSDArgs p) {
   }
 }
 
+// ---- the grouped form, for shapes with enough slices to give every CU a
+// block: a block of kGroups x 4 waves takes kGroups slices (16 channels each)
+// of one batch entry.  The chunk's B and C rows -- the same for every head --
+// are read from memory once per block into LDS and shared by the groups,
+// which cuts the block's reads of them kGroups-fold; each group keeps its own
+// x columns, state, constants and output, exactly as the one-slice kernel
+// above (the same products, in the same order, so the same results).  Where a
+// batch entry's slices do not fill its last block, the spare groups compute
+// on the last slice and store nothing.
+constexpr int kGroups = 3;
+
+template <int N>
+struct alignas(16) SSDGroupSmem {
+  static constexpr int BS = N + 8;
+  __bf16 Bs[2][kQ][BS];                  // B rows of a chunk (shared)
+  __bf16 Cs[2][kQ][BS];                  // C rows of a chunk (shared)
+  __bf16 Xs[kGroups][2][kQ][kPS];        // each group's x columns
+  __bf16 Hs[kGroups][2][kPS][BS];        // each group's state, bf16
+  ChunkConsts cc[kGroups][2];            // each group's per-token constants
+};
+
+template <int N, bool ZOH, bool GATE>
+__global__ __launch_bounds__(64 * kWaves * kGroups, 1) void ssd_fwd_grouped_kernel(
+    const SSDArgs p) {
+  using Sm = SSDGroupSmem<N>;
+  __shared__ Sm sm;
+  constexpr int NK = N / 32;
+  constexpr int NTW = N / 16 / kWaves;
+  constexpr int NT = 64 * kWaves * kGroups;   // threads
+  constexpr int PIECES = kQ * N / 8;          // 16-byte pieces of B (and of C) per chunk
+  constexpr int RBC = (2 * PIECES + NT - 1) / NT;
+  static_assert(NTW >= 1, "N is 64 or 128");
+  const int64_t H = p.nheads, L = p.L, P = p.P, HP = H * P;
+  const int64_t nsl = P / kPS;                         // slices per head
+  const int64_t SB = H * nsl;                          // slices per batch entry
+  const int64_t nbb = (SB + kGroups - 1) / kGroups;    // blocks per batch entry
+
+  // XCD-aware order, as the one-slice kernel: an XCD's blocks are consecutive
+  // logical blocks, i.e. mostly one batch entry, whose B and C stay in its L2
+  const int64_t nblk = (int64_t)gridDim.x, bid = blockIdx.x;
+  const int64_t logical = (nblk % 8 == 0) ? (bid % 8) * (nblk / 8) + bid / 8 : bid;
+  const int64_t b = logical / nbb, slot = logical - b * nbb;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = wv / kWaves, w = wv % kWaves;          // group; token block 16 w ..
+  const int tg = tid - g * 64 * kWaves;                // thread within the group
+  const int lr = lane & 15, lk = lane >> 4;
+  const int64_t sl0 = slot * kGroups + g;
+  const bool live_group = sl0 < SB;
+  const int64_t slc = live_group ? sl0 : SB - 1;
+  const int64_t h = slc / nsl, q = slc - h * nsl;
+  const float A = p.A[h];
+  const float Dh = p.D ? p.D[h] : 0.0f;
+  const float bias = p.dt_bias ? p.dt_bias[h] : 0.0f;
+  const int64_t ch0 = h * P + q * kPS;
+
+  const int64_t hrow = ((b * H + h) * P + q * kPS + lr) * N;
+  f32x4 Hacc[NTW];
+#pragma unroll
+  for (int j = 0; j < NTW; ++j) {
+    const int n = 16 * (w + kWaves * j) + 4 * lk;
+    Hacc[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    if (p.h0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Hacc[j][i] = p.h0[hrow + n + i];
+    }
+    *(u32x2*)&sm.Hs[g][0][lr][n] =
+        u32x2{pack_bf16x2(Hacc[j][0], Hacc[j][1]), pack_bf16x2(Hacc[j][2], Hacc[j][3])};
+  }
+
+  // ---- global reads of one chunk, issued two chunks ahead of use: the block
+  // reads B and C (piece e = tid + NT r: B for e < PIECES, then C; pieces
+  // past the end load the last one again and are not staged), each group its
+  // x columns, each wave the gate of its tokens, wave 0 of a group its step
+  // sizes (the group's other waves load one address, as in the one-slice
+  // kernel).  Rows past L are clamped to the last row.
+  u32x4 rBC[RBC];
+  u32x2 rX, rZ = u32x2{0u, 0u};
+  float rdt;
+  const int tz = 16 * w + lr;
+  const int tx = tg >> 2;
+  const uint32_t offZ = ((uint32_t)tz * (uint32_t)HP + 4 * lk) * 2u;
+  const uint32_t offX = ((uint32_t)tx * (uint32_t)HP + 4 * (tg & 3)) * 2u;
+  const uint32_t offD = w == 0 ? (uint32_t)lane * (uint32_t)H * 4u : 0u;
+  auto piece = [&](int r, int& row, int& col, bool& isC, bool& staged) {
+    const int e0 = tid + NT * r;
+    staged = e0 < 2 * PIECES;
+    const int e = staged ? e0 : 2 * PIECES - 1;
+    isC = e >= PIECES;
+    const int ep = isC ? e - PIECES : e;
+    row = ep / (N / 8);
+    col = (ep % (N / 8)) * 8;
+  };
+  auto load_chunk = [&](int64_t t0) {
+    const int lim = (int)(L - 1 - t0 < kQ - 1 ? L - 1 - t0 : kQ - 1);  // last row of the chunk
+    const char* Bc = (const char*)(p.B + (b * L + t0) * N);
+    const char* Cc = (const char*)(p.C + (b * L + t0) * N);
+    const char* Xc = (const char*)(p.x + (b * L + t0) * HP + ch0);
+    const char* Zc = (const char*)(p.z + (b * L + t0) * HP + ch0);
+    const char* Dc = (const char*)(p.dt + (b * L + t0) * H + h);
+    const int ld = lane < lim ? lane : lim;
+    rdt = *(const float*)(Dc + (w == 0 ? (uint32_t)ld * (uint32_t)H * 4u : 0u));
+#pragma unroll
+    for (int r = 0; r < RBC; ++r) {
+      int row, col;
+      bool isC, staged;
+      piece(r, row, col, isC, staged);
+      const uint32_t off = (uint32_t)((row < lim ? row : lim) * N + col) * 2u;
+      rBC[r] = *(const u32x4*)((isC ? Cc : Bc) + off);
+    }
+    const uint32_t rz = (uint32_t)(tz < lim ? tz : lim);
+    if constexpr (GATE) rZ = *(const u32x2*)(Zc + (rz * (uint32_t)HP + 4 * lk) * 2u);
+    const uint32_t rx = (uint32_t)(tx < lim ? tx : lim);
+    rX = *(const u32x2*)(Xc + (rx * (uint32_t)HP + 4 * (tg & 3)) * 2u);
+    (void)offD;
+  };
+
+  auto chunk_consts = [&](ChunkConsts& kc, float raw, int nlive) {
+    const float v = raw + bias;
+    float dl = p.softplus ? softplus_f(v) : v;
+    if (lane >= nlive) dl = 0.0f;
+    const float a = dl * A;
+    float wt = dl;
+    if constexpr (ZOH) wt = dl * zoh_phi(a, exp2_hw(a * kLog2e));
+    const float c = wave_inclusive_sum(a * kLog2e);
+    const float cb0 = lane_value(c, 15), cb1 = lane_value(c, 31), cb2 = lane_value(c, 47);
+    const float cend = lane_value(c, 63);
+    const float cblk = lane < 16 ? cb0 : (lane < 32 ? cb1 : (lane < 48 ? cb2 : cend));
+    kc.cuml[lane] = c;
+    kc.wv[lane] = wt;
+    kc.fw[lane] = exp2_hw(cblk - c) * wt;
+    kc.eend[lane] = exp2_hw(cend - c) * wt;
+    kc.et[lane] = exp2_hw(c);
+  };
+
+  float gz[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+  auto stage = [&](int buf, int64_t t0) {
+    const int nlive = (int)(L - t0 < kQ ? L - t0 : kQ);
+#pragma unroll
+    for (int r = 0; r < RBC; ++r) {
+      int row, col;
+      bool isC, staged;
+      piece(r, row, col, isC, staged);
+      if (staged) *(u32x4*)(isC ? &sm.Cs[buf][row][col] : &sm.Bs[buf][row][col]) = rBC[r];
+    }
+    *(u32x2*)&sm.Xs[g][buf][tx][4 * (tg & 3)] = tx < nlive ? rX : u32x2{0u, 0u};
+    if constexpr (GATE) {
+      gz[0] = silu_f(lo_bf(rZ.x));
+      gz[1] = silu_f(hi_bf(rZ.x));
+      gz[2] = silu_f(lo_bf(rZ.y));
+      gz[3] = silu_f(hi_bf(rZ.y));
+    }
+    if (w == 0) chunk_consts(sm.cc[g][buf], rdt, nlive);
+  };
+
+  const int64_t nchunks = (L + kQ - 1) / kQ;
+  const int64_t tlast = (nchunks - 1) * kQ;
+  if (nchunks > 0) {
+    load_chunk(0);
+    stage(0, 0);
+    load_chunk(nchunks > 1 ? kQ : 0);
+    // a store that writes nothing, so that every chunk starts with the same
+    // memory operations in flight (as in the one-slice kernel)
+    const __amdgpu_buffer_rsrc_t none =
+        __builtin_amdgcn_make_buffer_rsrc((void*)p.y, (short)0, 0, kBufferFlags);
+    __builtin_amdgcn_raw_buffer_store_b64(u32x2{0u, 0u}, none, (int)offZ, 0, 0);
+  }
+  lds_barrier();
+
+  for (int64_t ck = 0; ck < nchunks; ++ck) {
+    const int64_t t0 = ck * kQ;
+    const int nlive = (int)(L - t0 < kQ ? L - t0 : kQ);
+    const int cur = (int)(ck & 1), nxt = cur ^ 1;
+    const ChunkConsts& kc = sm.cc[g][cur];
+
+    u32x4 cC[NK];
+#pragma unroll
+    for (int k = 0; k < NK; ++k) cC[k] = *(const u32x4*)&sm.Cs[cur][tz][kn(k, lk)];
+
+    f32x4 y = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int k = 0; k < NK; ++k)
+      y = mfma16(*(const bf16x8*)&sm.Hs[g][cur][lr][kn(k, lk)], as_bf16x8(cC[k]), y);
+    {
+      const float e = kc.et[tz];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) y[i] *= e;
+    }
+    switch (w) {
+      case 0: scores_times_x<0, N, Sm::BS>(sm.Bs[cur], sm.Xs[g][cur], kc, cC, lane, y); break;
+      case 1: scores_times_x<1, N, Sm::BS>(sm.Bs[cur], sm.Xs[g][cur], kc, cC, lane, y); break;
+      case 2: scores_times_x<2, N, Sm::BS>(sm.Bs[cur], sm.Xs[g][cur], kc, cC, lane, y); break;
+      default: scores_times_x<3, N, Sm::BS>(sm.Bs[cur], sm.Xs[g][cur], kc, cC, lane, y); break;
+    }
+    u32x2 yout;
+    {
+      const u32x2 xv = *(const u32x2*)&sm.Xs[g][cur][tz][4 * lk];
+      const float o0 = fmaf(Dh, lo_bf(xv.x), y[0]) * gz[0];
+      const float o1 = fmaf(Dh, hi_bf(xv.x), y[1]) * gz[1];
+      const float o2 = fmaf(Dh, lo_bf(xv.y), y[2]) * gz[2];
+      const float o3 = fmaf(Dh, hi_bf(xv.y), y[3]) * gz[3];
+      yout = u32x2{pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)};
+    }
+    {
+      const float etot = exp2_hw(kc.cuml[kQ - 1]);
+#pragma unroll
+      for (int j = 0; j < NTW; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Hacc[j][i] *= etot;
+#pragma unroll
+      for (int s0 = 0; s0 < kQ; s0 += 32) {
+        const bf16x8 xt = tr_frag<kPS>(&sm.Xs[g][cur][s0][0], lane);
+        const f32x8 ev = *(const f32x8*)&kc.eend[s0 + 8 * lk];
+        const bf16x8 xw = __builtin_convertvector(__builtin_convertvector(xt, f32x8) * ev, bf16x8);
+#pragma unroll
+        for (int j = 0; j < NTW; ++j) {
+          const bf16x8 bt = tr_frag<Sm::BS>(&sm.Bs[cur][s0][16 * (w + kWaves * j)], lane);
+          Hacc[j] = mfma16(bt, xw, Hacc[j]);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < NTW; ++j)
+        *(u32x2*)&sm.Hs[g][nxt][lr][16 * (w + kWaves * j) + 4 * lk] =
+            u32x2{pack_bf16x2(Hacc[j][0], Hacc[j][1]), pack_bf16x2(Hacc[j][2], Hacc[j][3])};
+    }
+    stage(nxt, t0 + kQ);
+    load_chunk(t0 + 2 * kQ < L ? t0 + 2 * kQ : tlast);
+    {
+      // a spare group's range is empty: its rows are not stored
+      const int rows = live_group ? nlive : 0;
+      const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(p.y + (b * L + t0) * HP + ch0), (short)0, rows * (int)HP * 2, kBufferFlags);
+      __builtin_amdgcn_raw_buffer_store_b64(yout, yr, (int)offZ, 0, 0);
+    }
+    lds_barrier();
+  }
+
+  if (p.last_state && live_group) {
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) {
+      const int n = 16 * (w + kWaves * j) + 4 * lk;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p.last_state[hrow + n + i] = Hacc[j][i];
+    }
+  }
+}
+
+// The grouped kernel where it gives every CU at least one block (256 CUs),
+// else the one-slice kernel (three blocks per CU, more blocks in flight).
+constexpr int64_t kGroupedMinBlocks = 256;
+
 template <int N, bool ZOH, bool GATE>
 hipError_t ssd_launch(const SSDArgs& a, hipStream_t stream) {
-  const int64_t nblk = a.batch * a.nheads * (a.P / kPS);
+  const int64_t slices = a.nheads * (a.P / kPS);
+  const int64_t grouped = a.batch * ((slices + kGroups - 1) / kGroups);
+  if (grouped >= kGroupedMinBlocks) {
+    if (grouped > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((ssd_fwd_grouped_kernel<N, ZOH, GATE>), dim3((unsigned)grouped),
+                       dim3(64 * kWaves * kGroups), 0, stream, a);
+    return hipGetLastError();
+  }
+  const int64_t nblk = a.batch * slices;
   if (nblk > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL((ssd_fwd_kernel<N, ZOH, GATE>), dim3((unsigned)nblk), dim3(64 * kWaves), 0,
                      stream, a);

@@ -123,3 +123,33 @@ def test_ssd_full_size_sampled():
         e1 = assert_close(to_host64(y.index_select(2, hd)), yr, "bf16", f"y {mode}")
         e2 = assert_close(to_host64(last.index_select(1, hd)), lr, "bf16", f"last {mode}")
         print(f"full {mode}: y {e1:.2e} last {e2:.2e}", flush=True)
+
+
+# -------------------------------------------- the grouped kernel (three slices per block)
+
+@pytest.mark.parametrize("N", [64, 128])
+@pytest.mark.parametrize("mode", ["euler", "zoh"])
+def test_ssd_grouped_ragged(N, mode):
+    """128 sequences of 2 heads x 32 channels: 4 slices per batch entry, so
+    256 blocks of three slices take the grouped kernel, and the second block
+    of each entry has two spare groups.  Two chunks (the last ragged), h0."""
+    inp = W.ssd_inputs(_cfg(128, 100, 2, N, True, seed=140 + N, P=32))
+    h0 = np.random.default_rng(141).normal(size=(128, 2, 32, N)).astype(np.float32)
+    y, last = _gpu(inp, mode, h0=h0)
+    yr, lr = _ref(inp, mode, h0=h0)
+    assert_close(to_host64(y), yr, "bf16", f"grouped y N={N} {mode}")
+    assert_close(to_host64(last), lr, "bf16", f"grouped last N={N} {mode}")
+
+
+def test_ssd_grouped_equals_one_slice():
+    """Every batch entry is independent, and the grouped kernel runs each
+    slice's arithmetic exactly as the one-slice kernel: entry 5 of a 96-entry
+    run (grouped: 96 x 4 blocks) equals the same entry run alone (one-slice:
+    12 blocks), bit for bit."""
+    inp = W.ssd_inputs(_cfg(96, 150, 3, 128, True, seed=142, P=64))
+    h0 = np.random.default_rng(143).normal(size=(96, 3, 64, 128)).astype(np.float32)
+    y, last = _gpu(inp, "zoh", h0=h0)
+    one = {k: (v[5:6] if isinstance(v, np.ndarray) and v.ndim >= 2 and v.shape[0] == 96 else v)
+           for k, v in inp.items()}
+    y1, last1 = _gpu(one, "zoh", h0=h0[5:6])
+    assert torch.equal(y[5:6], y1) and torch.equal(last[5:6], last1)
