@@ -141,6 +141,7 @@ KERNEL_SOURCES = {
     "step_decode_zoh": ["step.hip"],
     "conv1d_fwd_conv130m": ["conv1d.hip"],
     "ssd_fwd_ssd130m": ["ssd.hip"],
+    "conv1d_bwd_conv130m": ["conv1d.hip"],
 }
 COMMON_SOURCES = ["ssm_device.h", "ssm_launch.h", "ssm_api.hip"]
 
@@ -624,7 +625,8 @@ def time_conv(dev, steps, warmup, nsets=4):
                          "kernel_ms": round(bwd_ms, 5),
                          "GB/s": round(bwd_b / (bwd_ms * 1e-3) / 1e9, 2),
                          "hbm_frac": round(bwd_b / (bwd_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                         "algorithmic_bytes": bwd_b}}
+                         "algorithmic_bytes": bwd_b,
+                         "traffic": measured_traffic("conv1d_bwd_conv130m")}}
 
 
 def copy_bandwidth(dev, nbytes=256 << 20, reps=20):
