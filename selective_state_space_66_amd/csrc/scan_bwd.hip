@@ -109,7 +109,9 @@ struct BwdArgs {
   int softplus, want_dz;
 };
 
-template <typename IO, int G, int NG, bool ZOH, bool GATE>
+// RST: document starts are given (a separate instance, so that the common
+// case carries none of their registers)
+template <typename IO, int G, int NG, bool ZOH, bool GATE, bool RST>
 __global__ __launch_bounds__((BShape<G, NG>::THREADS)) void scan_bwd_kernel(const BwdArgs p) {
   using S = BShape<G, NG>;
   constexpr int CW = S::CW, TC = S::TC, RPT = S::RPT, NPAD = S::NPAD, HALF = S::HALF;
@@ -173,7 +175,7 @@ __global__ __launch_bounds__((BShape<G, NG>::THREADS)) void scan_bwd_kernel(cons
       const int64_t idx = (row0 + tr) * dim + cc;
       ru[i] = u[idx];
       rdl[i] = dr[idx];
-      rrs[i] = p.reset ? (int)p.reset[row0 + tr] : 0;
+      if constexpr (RST) rrs[i] = (int)p.reset[row0 + tr];
       if (bwd) {
         rdy[i] = dyp[idx];
         if constexpr (GATE) rz[i] = zz[idx];
@@ -203,10 +205,12 @@ __global__ __launch_bounds__((BShape<G, NG>::THREADS)) void scan_bwd_kernel(cons
     for (int i = 0; i < RPT; ++i) {
       const int r = g + NG * i;
       const bool live = t0 + r < Lb;
-      if (cl == 0) {
-        const int f = (live && rrs[i] != 0) ? 1 : 0;
-        sm.rst[r] = f;
-        starts |= f;
+      if constexpr (RST) {
+        if (cl == 0) {
+          const int f = (live && rrs[i] != 0) ? 1 : 0;
+          sm.rst[r] = f;
+          starts |= f;
+        }
       }
       const float x = (live && cvalid) ? to_f32(ru[i]) : 0.0f;
       const float v = to_f32(rdl[i]) + bias;
@@ -246,7 +250,7 @@ __global__ __launch_bounds__((BShape<G, NG>::THREADS)) void scan_bwd_kernel(cons
   // the barrier after staging; with document starts it also tells every
   // thread whether the chunk has one (block-uniform)
   auto staged = [&](int starts) -> bool {
-    if (p.reset) return __syncthreads_or(starts) != 0;
+    if constexpr (RST) return __syncthreads_or(starts) != 0;
     lds_barrier();
     return false;
   };
@@ -270,7 +274,7 @@ __global__ __launch_bounds__((BShape<G, NG>::THREADS)) void scan_bwd_kernel(cons
 #pragma unroll
     for (int t = 0; t < TC; ++t) {
       if (FULL || t < nt) {
-        if (!FULL && sm.rst[t]) {  // a document starts here: forget the state
+        if (RST && !FULL && sm.rst[t]) {  // a document starts here: forget the state
 #pragma unroll
           for (int k = 0; k < G; ++k) h[k] = 0.0f;
         }
@@ -359,7 +363,7 @@ __global__ __launch_bounds__((BShape<G, NG>::THREADS)) void scan_bwd_kernel(cons
 #pragma unroll
       for (int t = 0; t < TC; ++t) {
         if (FULL || t < nt) {
-          if (!FULL && sm.rst[t]) {
+          if (RST && !FULL && sm.rst[t]) {
 #pragma unroll
             for (int k = 0; k < G; ++k) h[k] = 0.0f;
           }
@@ -412,7 +416,7 @@ __global__ __launch_bounds__((BShape<G, NG>::THREADS)) void scan_bwd_kernel(cons
             const float dl = d4.x, x = d4.y, ds = d4.z, rdl = d4.w;
             const float xdl = x * dl;
             // a document start: the update saw h_{t-1} = 0 and carries nothing back
-            const bool start = !FULL && sm.rst[t] != 0;
+            const bool start = RST && !FULL && sm.rst[t] != 0;
             float ddt = 0.0f, dx = 0.0f;
 #pragma unroll
             for (int k = 0; k < G; ++k) {
@@ -560,8 +564,12 @@ hipError_t bwd_launch_one(const BwdArgs& a, hipStream_t stream) {
   using S = BShape<G, NG>;
   const int64_t nblk = a.ntiles * a.batch;
   if (nblk > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((scan_bwd_kernel<IO, G, NG, ZOH, GATE>), dim3((unsigned)nblk),
-                     dim3(S::THREADS), 0, stream, a);
+  if (a.reset)
+    hipLaunchKernelGGL((scan_bwd_kernel<IO, G, NG, ZOH, GATE, true>), dim3((unsigned)nblk),
+                       dim3(S::THREADS), 0, stream, a);
+  else
+    hipLaunchKernelGGL((scan_bwd_kernel<IO, G, NG, ZOH, GATE, false>), dim3((unsigned)nblk),
+                       dim3(S::THREADS), 0, stream, a);
   return hipGetLastError();
 }
 
