@@ -82,7 +82,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 9
+#define SSM_ABI_VERSION 10
 
 /* status codes */
 #define SSM_OK 0
@@ -110,6 +110,7 @@ extern "C" {
 #define SSM_SCAN_KERNEL_SEQ4 3 /* sequential; 4 states per lane for 9..16 states */
 #define SSM_SCAN_KERNEL_TPAR 4 /* time-parallel, four waves per (batch, channel) row */
 #define SSM_SCAN_KERNEL_WAVE 5 /* time-parallel, one wave per row */
+#define SSM_SCAN_KERNEL_WAVE4 6 /* time-parallel, 16 lanes per row (four rows per wave) */
 
 /*
  * The selective scan over whole sequences.

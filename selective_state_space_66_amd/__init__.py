@@ -29,8 +29,8 @@ SSM_DT_ZOH, SSM_DT_EULER = 0, 1
 _MODES = {"zoh": SSM_DT_ZOH, "euler": SSM_DT_EULER}
 # scan kernel choices (SSM_SCAN_KERNEL_*): the library's own, the sequential
 # kernel with 1, 2 or 4 states per lane, the time-parallel kernels with four
-# waves or one wave per (batch, channel) row
-SCAN_KERNELS = {"auto": 0, "seq1": 1, "seq2": 2, "seq4": 3, "tpar": 4, "wave": 5}
+# waves, one wave or 16 lanes per (batch, channel) row
+SCAN_KERNELS = {"auto": 0, "seq1": 1, "seq2": 2, "seq4": 3, "tpar": 4, "wave": 5, "wave4": 6}
 
 _lib = None
 

@@ -314,22 +314,31 @@ __global__ __launch_bounds__(64 * kTW) void scan_tpar_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// One wave per channel, four consecutive tokens per lane.
+// One wave per channel, or four channels per wave; four consecutive tokens
+// per lane.
 //
-// For wide layers (many (batch, channel) rows) the time-parallel scan runs one
-// wave per row, so no carry crosses waves: a block owns kWW consecutive
-// channels of one batch entry, and each wave walks the sequence in chunks of
-// 256 tokens, lane l holding tokens 4l .. 4l + 3.  Per state:
+// For wide layers (many (batch, channel) rows) the time-parallel scan gives
+// each row a segment of LPC lanes within one wave, so no carry crosses waves:
+// LPC = 64 (one channel per wave) or 16 (four channels per wave, one per row
+// of 16 lanes).  A block owns CPB consecutive channels of one batch entry, and
+// each segment walks its channel's sequence in chunks of 4 LPC tokens, lane l
+// of the segment holding tokens 4l .. 4l + 3.  Per state:
 //   - the lane forms its four pairs and composes them in order (in-lane
 //     prefix: three combine steps);
-//   - the wave scans the 64 lane totals with DPP (pair_scan4), so the six
-//     scan levels are paid once per four tokens;
-//   - the carry enters through lane 0's total (b = A_tot carry + B_tot there;
-//     the other lanes read a zero carry), so after the scan each lane's b is
-//     the state after its last token, he; a whole-wave shift by one lane (DPP
-//     wave_shr, lane 0 keeping the carry) gives the state before its first
-//     token; each token's state is then one fma with its in-lane prefix, and
-//     lane 63's he is the next carry.
+//   - the segment scans its LPC lane totals with DPP (pair_scan4 over the
+//     wave, or its four in-row levels over rows of 16 lanes), so the scan
+//     levels are paid once per four tokens;
+//   - the carry enters through the segment's first lane (b = A_tot carry +
+//     B_tot there; the other lanes read a zero carry), so after the scan each
+//     lane's b is the state after its last token, he; a shift by one lane (DPP
+//     wave_shr, or row_shr within rows; the segment's first lane keeping the
+//     carry) gives the state before its first token; each token's state is
+//     then one fma with its in-lane prefix, and the segment's last lane's he is
+//     the next carry.
+// Sixteen-lane segments skip the two scan levels that cross rows (one VALU
+// instruction per update) and share each staged B and C row among twice as
+// many channels, but make a quarter as many waves: the host takes them where
+// the rows still give every SIMD three waves.
 // Each chunk's inputs are staged in LDS by the whole block: u, Delta (after
 // the softplus) and silu(z) as a (channel, token) tile read from global
 // memory in row segments of the block's channels (a lane reading its own
@@ -337,44 +346,101 @@ __global__ __launch_bounds__(64 * kTW) void scan_tpar_kernel(
 // as fp32 in the order the lanes read them, so a lane's read of four states of
 // one of its tokens is one conflict-free 16-byte access.  Two barriers per
 // chunk: after staging, and after the chunk's last read.
-constexpr int kWW = 8;        // waves (channels) per block
-constexpr int kWT = 4;        // tokens per lane
-constexpr int kWC = 64 * kWT; // tokens per chunk
+constexpr int kWT = 4;  // tokens per lane
 
-// Staged B and C rows are padded by 2 slots (16 bytes, 4 banks each): the
-// writers of one lane slot differ in the token offset i, which then moves
-// them by 2 i bank groups, and a reader's address is a constant plus 16 lane.
-constexpr int kWRow = 64 + 2;
-
-struct WaveSmem {
-  // per wave (channel) and group of four states: A log2(e), the readout
-  // weight, and the carry (g units where fast), as three float4.  Slot 0 is
-  // read by lane 0, slot 1 (the same constants, a zero carry) by the other
-  // lanes: one pointer per lane reaches all three with immediate offsets
-  // (first in the struct, so that the offsets fit the LDS instructions').
-  float4 kq[kWW][kNMax / 4][2][3];
-  float4 b[kNMax / 4][kWT][kWRow];  // [state group][token in lane][lane]
-  float4 c[kNMax / 4][kWT][kWRow];
-  float2 xd[kWW][kWC];           // (x, Delta) per channel of the tile and token
-  float gz[kWW][kWC];            // silu(z)
-  float yt[kWW][kWC];            // y, stored by the block in row segments
+template <int CPW>  // channels per wave: 1 or 4
+struct WaveShape {
+  static constexpr int LPC = 64 / CPW;          // lanes per channel
+  static constexpr int WPB = CPW == 1 ? 8 : 4;  // waves per block
+  static constexpr int CPB = WPB * CPW;         // channels per block
+  static constexpr int TCK = LPC * kWT;         // tokens per chunk
+  static constexpr int NT = 64 * WPB;           // threads per block
+  static constexpr int TPT = CPB / 4;           // tile-staging threads per token (4 channels each)
+  static constexpr int SPT = 16 * TCK / NT;     // B and C states per staging thread
+  // waves per SIMD the registers are sized for: four (128 VGPRs) with one
+  // channel per wave; three (168) with four, which the host picks only where
+  // the layer has about three such waves per SIMD
+  static constexpr int WPS = CPW == 1 ? 4 : 3;
+  // Staged B and C: a reader's address is a constant plus 16 bytes times its
+  // lane, and the writers in one pass of the LDS (16 lanes of 16 bytes) must
+  // reach 16 different groups of 4 banks.  Rows are padded by ROW - LPC slots
+  // and each state group's rows by QPAD: with one wave per channel a pass
+  // holds tokens 0..7 (row offset i, slot l) of two groups two apart, at
+  // group 2 i + l + 8 (q / 2); with four channels per wave, tokens 0..3 of
+  // all four groups, at 4 i + q.
+  static constexpr int ROW = LPC + (CPW == 1 ? 2 : 4);
+  static constexpr int QPAD = CPW == 1 ? 4 : 1;
+  // The (channel, token) tiles' rows are padded so that the staging threads of
+  // one token, whose channel rows are 4 apart, write different banks: by 32
+  // bytes (1 wave per channel: 2 threads per token) or 16 (4 channels per
+  // wave: 4 threads per token).  Rows stay 16-byte aligned.
+  static constexpr int XPAD = CPW == 1 ? 4 : 2;  // float2 slots
+  static constexpr int GPAD = CPW == 1 ? 8 : 4;  // float slots
+  static_assert(CPW == 1 || CPW == 4, "one or four channels per wave");
+  static_assert(TCK * TPT == NT && TCK * (16 / SPT) == NT, "the staging threads cover the chunk");
 };
 
-// Arguments as for scan_tpar_kernel, plus ntiles = ceil(dim / kWW) channel
-// tiles per batch entry and vec_io: dim is a multiple of kWW and u, delta, z
+template <int CPW>
+struct WaveSmem {
+  using S = WaveShape<CPW>;
+  // per channel and group of four states: A log2(e), the readout weight, and
+  // the carry (g units where fast), as three float4.  Slot 0 is read by the
+  // segment's first lane, slot 1 (the same constants, a zero carry) by the
+  // others: one pointer per lane reaches all three with immediate offsets
+  // (first in the struct, so that the offsets fit the LDS instructions').
+  float4 kq[S::CPB][kNMax / 4][2][3];
+  // [state group][token in lane * ROW + lane in segment], QPAD spare slots
+  // after each group's rows
+  float4 b[kNMax / 4][kWT * S::ROW + S::QPAD];
+  float4 c[kNMax / 4][kWT * S::ROW + S::QPAD];
+  // per channel of the tile, one token per slot (rows padded: XPAD, GPAD)
+  float2 xd[S::CPB][S::TCK + S::XPAD];  // (x, Delta)
+  float gz[S::CPB][S::TCK + S::GPAD];   // silu(z)
+  float yt[S::CPB][S::TCK + S::GPAD];   // y, stored by the block in row segments
+};
+
+// The scan of pair_scan4_b within rows of 16 lanes (its first four levels):
+// lane i of a row ends with the composition of lanes 0..i of that row.
+#define SSM66_STEP4(CTRL)                                         \
+  "v_fmac_f32_dpp %0, %0, %4 " CTRL " bank_mask:0xf\n\t"        \
+  "v_fmac_f32_dpp %1, %1, %5 " CTRL " bank_mask:0xf\n\t"        \
+  "v_fmac_f32_dpp %2, %2, %6 " CTRL " bank_mask:0xf\n\t"        \
+  "v_fmac_f32_dpp %3, %3, %7 " CTRL " bank_mask:0xf\n\t"        \
+  "v_mul_f32_dpp %4, %4, %4 " CTRL " bank_mask:0xf\n\t"         \
+  "v_mul_f32_dpp %5, %5, %5 " CTRL " bank_mask:0xf\n\t"         \
+  "v_mul_f32_dpp %6, %6, %6 " CTRL " bank_mask:0xf\n\t"         \
+  "v_mul_f32_dpp %7, %7, %7 " CTRL " bank_mask:0xf\n\t"
+__device__ __forceinline__ void pair_scan4_b_rows(float (&a)[4], float (&b)[4]) {
+  asm volatile("s_nop 1\n\t"
+               SSM66_STEP4("row_shr:1 row_mask:0xf")
+               SSM66_STEP4("row_shr:2 row_mask:0xf")
+               SSM66_STEP4("row_shr:4 row_mask:0xf")
+               "v_fmac_f32_dpp %0, %0, %4 row_shr:8 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %1, %1, %5 row_shr:8 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %2, %2, %6 row_shr:8 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %3, %3, %7 row_shr:8 row_mask:0xf bank_mask:0xf\n\t"
+               "s_nop 1"
+               : "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]),
+                 "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]));
+}
+#undef SSM66_STEP4
+
+// Arguments as for scan_tpar_kernel, plus ntiles = ceil(dim / CPB) channel
+// tiles per batch entry and vec_io: dim is a multiple of CPB and u, delta, z
 // and y are 16-byte aligned (tiles are read and y written in row segments of
-// 4 channels); NF
-// and CKPT likewise.  Four waves per SIMD (128 VGPRs) let two 8-wave blocks
-// share a CU.
-template <typename IO, bool ZOH, bool GATE, bool NF, bool CKPT>
-__global__ __launch_bounds__(64 * kWW, 4) void scan_wave_kernel(
+// 4 channels); NF and CKPT likewise.  Four waves per SIMD (128 VGPRs) let
+// blocks share a CU.
+template <typename IO, bool ZOH, bool GATE, bool NF, bool CKPT, int CPW>
+__global__ __launch_bounds__(WaveShape<CPW>::NT, WaveShape<CPW>::WPS) void scan_wave_kernel(
     const IO* __restrict__ u, const IO* __restrict__ dr, const float* __restrict__ Am,
     const IO* __restrict__ Bm, const IO* __restrict__ Cm, const float* __restrict__ Dm,
     const IO* __restrict__ zz, const float* __restrict__ bias_v, const float* h0,
     const int32_t* __restrict__ seq_lens, const uint8_t* __restrict__ reset,
     IO* __restrict__ y, float* last_state, float* __restrict__ ckpt, const int64_t L,
     const int64_t dim, const int N, const int64_t ntiles, const int softplus, const int vec_io) {
-  __shared__ WaveSmem sm;
+  using S = WaveShape<CPW>;
+  constexpr int LPC = S::LPC, CPB = S::CPB, TCK = S::TCK;
+  __shared__ WaveSmem<CPW> sm;
 
   // XCD-aware order: each XCD gets a contiguous run of channel tiles, which
   // share the 128-byte lines of u, Delta, z and y in its L2.
@@ -384,48 +450,56 @@ __global__ __launch_bounds__(64 * kWW, 4) void scan_wave_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t c0 = tile * kWW;             // first channel of the tile
-  const int64_t c = c0 + w;                  // this wave's channel
-  const bool cvalid = c < dim;               // wave-uniform; every wave stages and syncs
-  const int64_t cc = cvalid ? c : dim - 1;   // loads of a padding wave stay in bounds
+  const int sl = CPW == 1 ? lane : (lane & (LPC - 1));  // lane within its channel's segment
+  const int ch = CPW == 1 ? w : w * CPW + lane / LPC;   // channel within the tile
+  const int64_t c0 = tile * CPB;             // first channel of the tile
+  const int64_t c = c0 + ch;                 // this segment's channel
+  const bool cvalid = c < dim;               // uniform per segment; every wave stages and syncs
+  const int64_t cc = cvalid ? c : dim - 1;   // loads of a padding segment stay in bounds
 
-  // per-state constants, lane n holding state n's
-  const float a_l = lane < N ? Am[cc * N + lane] : 0.0f;
+  // per-state constants, lane n of the segment holding state n's
+  const float a_l = sl < N ? Am[cc * N + sl] : 0.0f;
   const bool fast_l = ZOH && fabsf(a_l) >= 0.5f;  // ZOH g form for this state
   const float ca_l = fast_l ? 1.0f / a_l : 0.0f;
-  const uint64_t fast_mask = __ballot(fast_l);
-  const bool all_fast = ZOH && (~fast_mask & ((1ull << N) - 1)) == 0;  // uniform
+  // the fast states of this lane's channel, bit n for state n
+  const uint32_t fast_bits = (uint32_t)(__ballot(fast_l) >> (CPW == 1 ? 0 : lane - sl)) & 0xffffu;
+  // every state of every channel of the wave takes the g form (uniform)
+  const bool all_fast = ZOH && __ballot(sl < N && cvalid && !fast_l) == 0;
   const float dskip = Dm ? Dm[cc] : 0.0f;
-  // this wave's constants and carry (g units where fast) to LDS, lane n holding
-  // state n's; states past N are finite dummies (A = 0, carry 0), never read out
-  if (lane < kNMax) {
+  // this channel's constants and carry (g units where fast) to LDS, lane n of
+  // the segment holding state n's; states past N are finite dummies (A = 0,
+  // carry 0), never read out
+  if (sl < kNMax) {
     float hv = 0.0f;
-    if (h0 && lane < N) hv = h0[(b * dim + cc) * N + lane];
-    float* s0 = (float*)&sm.kq[w][lane / 4][0][0] + (lane & 3);
-    float* s1 = (float*)&sm.kq[w][lane / 4][1][0] + (lane & 3);
+    if (h0 && sl < N) hv = h0[(b * dim + cc) * N + sl];
+    float* s0 = (float*)&sm.kq[ch][sl / 4][0][0] + (sl & 3);
+    float* s1 = (float*)&sm.kq[ch][sl / 4][1][0] + (sl & 3);
     const float a2 = a_l * kLog2e, w1 = fast_l ? ca_l : (ZOH ? 1.0f : 0.0f);
     s0[0] = a2; s1[0] = a2;
     s0[4] = w1; s1[4] = w1;
     s0[8] = fast_l ? a_l * hv : hv;
     s1[8] = 0.0f;
   }
-  const float4* kp = &sm.kq[w][0][lane == 0 ? 0 : 1][0];  // this lane's constants slot
+  const float4* kp = &sm.kq[ch][0][sl == 0 ? 0 : 1][0];  // this lane's constants slot
   const int64_t nck = (L + 15) / 16;  // checkpoints per sequence (CKPT)
   int64_t Leff = L;
   if (seq_lens) {
-    const int64_t sl = seq_lens[b];
-    Leff = sl < 0 ? 0 : (sl < L ? sl : L);
+    const int64_t sl_b = seq_lens[b];
+    Leff = sl_b < 0 ? 0 : (sl_b < L ? sl_b : L);
   }
   const int64_t row0 = b * L;
 
-  // ---- B and C staging: thread j stages token j / 2 of the chunk, states
-  // 8 (j % 2) .. + 7 (two groups of four): a wave reads 32 consecutive rows.
-  // Token t = 4 l + i of group q goes to slot l of row [q][i].  Tokens past L
-  // are clamped to L - 1; padding tokens stage B = C = 0.
-  const int st_t = tid >> 1, st_h = tid & 1;
+  // ---- B and C staging: thread j stages token j / TPK of the chunk, states
+  // SPT (j % TPK) .. + SPT - 1 (SPT / 4 groups of four): a wave reads
+  // consecutive rows.  Token t = 4 l + i of group q goes to slot l of row
+  // [q][i].  Tokens past L are clamped to L - 1; padding tokens stage
+  // B = C = 0.
+  constexpr int SPT = S::SPT;
+  constexpr int TPK = 16 / SPT;
+  const int st_t = tid / TPK, st_h = tid % TPK;
   const int st_i = st_t & (kWT - 1), st_l = st_t / kWT;
-  // raw staging words: bf16 pairs (4 words) or fp32 values (8 words) per tensor
-  constexpr int SW = sizeof(IO) == 2 ? 4 : 8;
+  // raw staging words: bf16 pairs (SPT / 2 words) or fp32 values (SPT words) per tensor
+  constexpr int SW = sizeof(IO) == 2 ? SPT / 2 : SPT;
   uint32_t sb[SW], sc[SW];
   bool st_live = false;
   auto stage_load = [&](int64_t t0) {
@@ -434,20 +508,29 @@ __global__ __launch_bounds__(64 * kWW, 4) void scan_wave_kernel(
     t = t < L ? t : L - 1;
     if constexpr (NF) {
       // the chunk's rows from a uniform base; this thread's byte offset in
-      // them (token t - t0, states 8 st_h ..) is the same every full chunk
+      // them (token t - t0, states SPT st_h ..) is the same every full chunk
       typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+      typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
       const char* bb = (const char*)(Bm + (row0 + t0) * 16);
       const char* cb = (const char*)(Cm + (row0 + t0) * 16);
-      const uint32_t off = (uint32_t)((t - t0) * 16 + 8 * st_h) * (uint32_t)sizeof(IO);
+      const uint32_t off = (uint32_t)((t - t0) * 16 + SPT * st_h) * (uint32_t)sizeof(IO);
+      if constexpr (SW % 4 == 0) {
 #pragma unroll
-      for (int j = 0; j < SW / 4; ++j) {
-        const u32x4 vb = *(const u32x4*)(bb + off + 16 * j);
-        const u32x4 vc = *(const u32x4*)(cb + off + 16 * j);
+        for (int j = 0; j < SW / 4; ++j) {
+          const u32x4 vb = *(const u32x4*)(bb + off + 16 * j);
+          const u32x4 vc = *(const u32x4*)(cb + off + 16 * j);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          sb[4 * j + k] = vb[k];
-          sc[4 * j + k] = vc[k];
+          for (int k = 0; k < 4; ++k) {
+            sb[4 * j + k] = vb[k];
+            sc[4 * j + k] = vc[k];
+          }
         }
+      } else {
+        static_assert(SW == 2, "8-byte pieces");
+        const u32x2 vb = *(const u32x2*)(bb + off);
+        const u32x2 vc = *(const u32x2*)(cb + off);
+        sb[0] = vb[0]; sb[1] = vb[1];
+        sc[0] = vc[0]; sc[1] = vc[1];
       }
     } else {
 #pragma unroll
@@ -456,8 +539,8 @@ __global__ __launch_bounds__(64 * kWW, 4) void scan_wave_kernel(
         sc[j] = 0u;
       }
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int n = 8 * st_h + j;
+      for (int j = 0; j < SPT; ++j) {
+        const int n = SPT * st_h + j;
         const int64_t e = (row0 + t) * N + (n < N ? n : N - 1);
         uint32_t vb = 0u, vc = 0u;
         if (n < N) {
@@ -479,7 +562,7 @@ __global__ __launch_bounds__(64 * kWW, 4) void scan_wave_kernel(
       }
     }
   };
-  // element j (0..7) of the staged words, as fp32; 0 for padding tokens
+  // element j (0..SPT-1) of the staged words, as fp32; 0 for padding tokens
   // (PAD: the chunk holds some)
   auto st_elem = [&](auto pad_tag, const uint32_t (&wv)[SW], int j) -> float {
     float v;
@@ -493,31 +576,32 @@ __global__ __launch_bounds__(64 * kWW, 4) void scan_wave_kernel(
   auto stage_store_as = [&](auto pad_tag) {
     auto st_elem_p = [&](const uint32_t (&wv)[SW], int j) { return st_elem(pad_tag, wv, j); };
 #pragma unroll
-    for (int q2 = 0; q2 < 2; ++q2) {
-      const int q = 2 * st_h + q2;
-      sm.b[q][st_i][st_l] = make_float4(st_elem_p(sb, 4 * q2), st_elem_p(sb, 4 * q2 + 1),
+    for (int q2 = 0; q2 < SPT / 4; ++q2) {
+      const int q = (SPT / 4) * st_h + q2;
+      sm.b[q][st_i * S::ROW + st_l] = make_float4(st_elem_p(sb, 4 * q2), st_elem_p(sb, 4 * q2 + 1),
                                         st_elem_p(sb, 4 * q2 + 2), st_elem_p(sb, 4 * q2 + 3));
-      sm.c[q][st_i][st_l] = make_float4(st_elem_p(sc, 4 * q2), st_elem_p(sc, 4 * q2 + 1),
+      sm.c[q][st_i * S::ROW + st_l] = make_float4(st_elem_p(sc, 4 * q2), st_elem_p(sc, 4 * q2 + 1),
                                         st_elem_p(sc, 4 * q2 + 2), st_elem_p(sc, 4 * q2 + 3));
     }
   };
 
   // ---- the (channel, token) tile of u, raw Delta and z: thread j takes token
-  // j / 2 and channels 4 (j % 2) .. + 3 of the tile, one row segment per
+  // j / TPT and channels 4 (j % TPT) .. + 3 of the tile, one row segment per
   // tensor (vec_io), else element by element with channels clamped to dim.
-  const int xt = tid >> 1, xh = tid & 1;
+  constexpr int TPT = S::TPT;
+  const int xt = tid / TPT, xh = tid % TPT;
   float xbias[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const int64_t ch = c0 + 4 * xh + k;
-    xbias[k] = bias_v ? bias_v[ch < dim ? ch : dim - 1] : 0.0f;
+    const int64_t chk = c0 + 4 * xh + k;
+    xbias[k] = bias_v ? bias_v[chk < dim ? chk : dim - 1] : 0.0f;
   }
   constexpr int XW = sizeof(IO) == 2 ? 2 : 4;  // 32-bit words per 4 channels
   uint32_t xu[XW], xr[XW], xz[XW];
   bool x_live = false;
   // byte offset of this thread's row segment from the chunk's first element
   // (c0 of token t0): token xt, channels 4 xh ..; the same every full chunk.
-  // The launch keeps 256 dim elements within 32 bits of bytes.
+  // The launch keeps TCK dim elements within 32 bits of bytes.
   const uint32_t xoff = ((uint32_t)xt * (uint32_t)dim + 4u * (uint32_t)xh) * (uint32_t)sizeof(IO);
   auto tile_load = [&](int64_t t0) {
     int64_t t = t0 + xt;
@@ -555,8 +639,8 @@ __global__ __launch_bounds__(64 * kWW, 4) void scan_wave_kernel(
       for (int k = 0; k < XW; ++k) { xu[k] = 0u; xr[k] = 0u; xz[k] = 0u; }
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const int64_t ch = c0 + 4 * xh + k;
-        const int64_t e = (row0 + t) * dim + (ch < dim ? ch : dim - 1);
+        const int64_t chk = c0 + 4 * xh + k;
+        const int64_t e = (row0 + t) * dim + (chk < dim ? chk : dim - 1);
         uint32_t vu, vr, vz = 0u;
         if constexpr (sizeof(IO) == 2) {
           vu = ((const uint16_t*)u)[e];
@@ -597,8 +681,8 @@ __global__ __launch_bounds__(64 * kWW, 4) void scan_wave_kernel(
     }
   };
 
-  // y of the chunk: thread j stores token j / 2, channels 4 (j % 2) .. + 3 of
-  // the tile (one row segment with vec_io); tokens past L are not stored.
+  // y of the chunk: thread j stores token j / TPT, channels 4 (j % TPT) .. + 3
+  // of the tile (one row segment with vec_io); tokens past L are not stored.
   // Reads yt before the next chunk's barrier, which orders it before yt is
   // written again.
   auto y_store = [&](int64_t t0) {
@@ -626,18 +710,18 @@ __global__ __launch_bounds__(64 * kWW, 4) void scan_wave_kernel(
     }
   };
 
-  const int64_t nchunks = (L + kWC - 1) / kWC;
+  const int64_t nchunks = (L + TCK - 1) / TCK;
   if (nchunks > 0) {
     tile_load(0);
     stage_load(0);
   }
 
   for (int64_t ck = 0; ck < nchunks; ++ck) {
-    const int64_t t0 = ck * kWC;
+    const int64_t t0 = ck * TCK;
     // staging (every wave finished reading the previous chunk before the
     // barrier that ended it), then the next chunk's loads into the freed
     // registers
-    if (t0 + kWC <= Leff) {  // no padding token in the chunk (uniform)
+    if (t0 + TCK <= Leff) {  // no padding token in the chunk (uniform)
       tile_store_as(std::false_type());
       stage_store_as(std::false_type());
     } else {
@@ -645,21 +729,21 @@ __global__ __launch_bounds__(64 * kWW, 4) void scan_wave_kernel(
       stage_store_as(std::true_type());
     }
     if (ck + 1 < nchunks) {
-      tile_load(t0 + kWC);
-      stage_load(t0 + kWC);
+      tile_load(t0 + TCK);
+      stage_load(t0 + TCK);
     }
     lds_barrier();
 
-    const bool full = t0 + kWC <= Leff;  // every token of the chunk is real (uniform)
+    const bool full = t0 + TCK <= Leff;  // every token of the chunk is real (uniform)
     float x[kWT], dl[kWT], gz[kWT], acc[kWT];
     bool live[kWT], rst[kWT];
     {
-      const float4 v0 = *(const float4*)&sm.xd[w][kWT * lane];
-      const float4 v1 = *(const float4*)&sm.xd[w][kWT * lane + 2];
+      const float4 v0 = *(const float4*)&sm.xd[ch][kWT * sl];
+      const float4 v1 = *(const float4*)&sm.xd[ch][kWT * sl + 2];
       x[0] = v0.x; dl[0] = v0.y; x[1] = v0.z; dl[1] = v0.w;
       x[2] = v1.x; dl[2] = v1.y; x[3] = v1.z; dl[3] = v1.w;
       if constexpr (GATE) {
-        const float4 g = *(const float4*)&sm.gz[w][kWT * lane];
+        const float4 g = *(const float4*)&sm.gz[ch][kWT * sl];
         gz[0] = g.x; gz[1] = g.y; gz[2] = g.z; gz[3] = g.w;
       } else {
 #pragma unroll
@@ -668,37 +752,37 @@ __global__ __launch_bounds__(64 * kWW, 4) void scan_wave_kernel(
     }
 #pragma unroll
     for (int i = 0; i < kWT; ++i) {
-      live[i] = full || t0 + kWT * lane + i < Leff;
+      live[i] = full || t0 + kWT * sl + i < Leff;
       rst[i] = false;
       acc[i] = 0.0f;
     }
-    // document starts in this chunk (the same for every wave of the block)
+    // document starts in this chunk (the same for every channel of the block)
     bool any_rst = false;
     if (reset) {
 #pragma unroll
       for (int i = 0; i < kWT; ++i) {
-        const int64_t t = t0 + kWT * lane + i;
+        const int64_t t = t0 + kWT * sl + i;
         rst[i] = live[i] && reset[row0 + t] != 0;
       }
       any_rst = __ballot(rst[0] || rst[1] || rst[2] || rst[3]) != 0;
     }
     // the lane's first token starts a 16-token checkpoint group
-    const int64_t tl = t0 + kWT * lane;
-    const bool wck = CKPT && cvalid && (lane % 4 == 0) && tl < L;
+    const int64_t tl = t0 + kWT * sl;
+    const bool wck = CKPT && cvalid && (sl % 4 == 0) && tl < L;
     float* ckp = ckpt + ((b * nck + (wck ? tl / 16 : 0)) * dim + cc) * N;
 
     auto group = [&](auto form_tag, auto rst_tag, int q) {
       constexpr int FORM = decltype(form_tag)::value;
       constexpr bool RST = decltype(rst_tag)::value;
       const float4* kpq = kp + 6 * q;
-      const float4 a24 = kpq[0], w14 = kpq[1], cin4 = kpq[2];  // cin4: the carry in lane 0, else 0
+      const float4 a24 = kpq[0], w14 = kpq[1], cin4 = kpq[2];  // cin4: the carry in the first lane, else 0
       const float a2v[4] = {a24.x, a24.y, a24.z, a24.w};
       const float w1v[4] = {w14.x, w14.y, w14.z, w14.w};
       const float cinv[4] = {cin4.x, cin4.y, cin4.z, cin4.w};
       float pa[kWT][4], pb[kWT][4];
 #pragma unroll
       for (int i = 0; i < kWT; ++i) {
-        const float4 bv4 = sm.b[q][i][lane];
+        const float4 bv4 = sm.b[q][i * S::ROW + sl];
         const float bv[4] = {bv4.x, bv4.y, bv4.z, bv4.w};
         const float dx = FORM == 0 ? dl[i] * x[i] : 0.0f;  // Euler: Delta u, once per token
 #pragma unroll
@@ -708,7 +792,7 @@ __global__ __launch_bounds__(64 * kWW, 4) void scan_wave_kernel(
           float bu;
           if (FORM == 0) {
             bu = dx * bv[k];
-          } else if (FORM == 1 || ((fast_mask >> n) & 1)) {
+          } else if (FORM == 1 || ((fast_bits >> n) & 1)) {
             const float wu = x[i] * bv[k];
             bu = fmaf(a, wu, -wu);  // (abar - 1) u B, in g units
           } else {
@@ -718,6 +802,17 @@ __global__ __launch_bounds__(64 * kWW, 4) void scan_wave_kernel(
           pb[i][k] = bu;
         }
       }
+      // C: read after the scan where registers are short (128), else before the
+      // prefix, so that the prefix and the scan cover the read's latency
+      float cv[kWT][4];
+      auto read_c = [&]() {
+#pragma unroll
+        for (int i = 0; i < kWT; ++i) {
+          const float4 cv4 = sm.c[q][i * S::ROW + sl];
+          cv[i][0] = cv4.x; cv[i][1] = cv4.y; cv[i][2] = cv4.z; cv[i][3] = cv4.w;
+        }
+      };
+      if constexpr (S::WPS != 4) read_c();
       // in-lane prefix: token i's pair becomes the composition of tokens 0..i
 #pragma unroll
       for (int i = 1; i < kWT; ++i) {
@@ -730,22 +825,22 @@ __global__ __launch_bounds__(64 * kWW, 4) void scan_wave_kernel(
       float ta[4] = {pa[kWT - 1][0], pa[kWT - 1][1], pa[kWT - 1][2], pa[kWT - 1][3]};
       float tb[4];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) tb[k] = fmaf(ta[k], cinv[k], pb[kWT - 1][k]);  // lane 0: the carry enters
-      pair_scan4_b(ta, tb);
-      // C is read after the scan, not held through it
-      float cv[kWT][4];
-#pragma unroll
-      for (int i = 0; i < kWT; ++i) {
-        const float4 cv4 = sm.c[q][i][lane];
-        cv[i][0] = cv4.x; cv[i][1] = cv4.y; cv[i][2] = cv4.z; cv[i][3] = cv4.w;
-      }
+      for (int k = 0; k < 4; ++k) tb[k] = fmaf(ta[k], cinv[k], pb[kWT - 1][k]);  // first lane: the carry enters
+      if constexpr (LPC == 64)
+        pair_scan4_b(ta, tb);
+      else
+        pair_scan4_b_rows(ta, tb);
+      if constexpr (S::WPS == 4) read_c();
       float he[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const int n = 4 * q + k;
         he[k] = tb[k];  // after the lane's last token
+        // the state before the lane's first token: the previous lane's he; the
+        // segment's first lane (no source lane) keeps the carry
+        constexpr int kShr1 = LPC == 64 ? 0x138 /* wave_shr:1 */ : 0x111 /* row_shr:1 */;
         const float hin = __int_as_float(__builtin_amdgcn_update_dpp(
-            __float_as_int(cinv[k]), __float_as_int(he[k]), 0x138 /* wave_shr:1 */, 0xf, 0xf, false));
+            __float_as_int(cinv[k]), __float_as_int(he[k]), kShr1, 0xf, 0xf, false));
 #pragma unroll
         for (int i = 0; i < kWT; ++i) {
           const float h = (i == kWT - 1) ? he[k] : fmaf(pa[i][k], hin, pb[i][k]);
@@ -753,8 +848,8 @@ __global__ __launch_bounds__(64 * kWW, 4) void scan_wave_kernel(
         }
         if (CKPT && wck && (NF || n < N)) ckp[n] = ZOH ? hin * w1v[k] : hin;  // g / A where g is carried
       }
-      // lane 63 holds the state after the chunk: the next chunk's carry
-      if (lane == 63) sm.kq[w][q][0][2] = make_float4(he[0], he[1], he[2], he[3]);
+      // the segment's last lane holds the state after the chunk: the next carry
+      if (sl == LPC - 1) sm.kq[ch][q][0][2] = make_float4(he[0], he[1], he[2], he[3]);
     };
     // one group of four states at a time (a rolled loop keeps one group's
     // pairs live, not all sixteen states')
@@ -776,7 +871,7 @@ __global__ __launch_bounds__(64 * kWW, 4) void scan_wave_kernel(
       float yv[kWT];
 #pragma unroll
       for (int i = 0; i < kWT; ++i) yv[i] = live[i] ? (acc[i] + dskip * x[i]) * gz[i] : 0.0f;
-      *(float4*)&sm.yt[w][kWT * lane] = make_float4(yv[0], yv[1], yv[2], yv[3]);
+      *(float4*)&sm.yt[ch][kWT * sl] = make_float4(yv[0], yv[1], yv[2], yv[3]);
     }
     lds_barrier();  // the chunk's LDS is free for the next one, and y is staged
     y_store(t0);
@@ -784,40 +879,42 @@ __global__ __launch_bounds__(64 * kWW, 4) void scan_wave_kernel(
 
   // the carried value and its readout weight from LDS (1/A where g = A h is
   // carried), so that no per-lane constant has to live through the loop
-  if (cvalid && last_state && lane < N) {
-    const float g = ((const float*)&sm.kq[w][lane / 4][0][2])[lane & 3];
-    const float w1 = ((const float*)&sm.kq[w][lane / 4][0][1])[lane & 3];
-    last_state[(b * dim + c) * N + lane] = ((fast_mask >> lane) & 1) ? g * w1 : g;
+  if (cvalid && last_state && sl < N) {
+    const float g = ((const float*)&sm.kq[ch][sl / 4][0][2])[sl & 3];
+    const float w1 = ((const float*)&sm.kq[ch][sl / 4][0][1])[sl & 3];
+    last_state[(b * dim + c) * N + sl] = ((fast_bits >> sl) & 1) ? g * w1 : g;
   }
 }
 
-template <typename IO, bool ZOH, bool GATE>
+template <typename IO, bool ZOH, bool GATE, int CPW>
 hipError_t wave_launch(const ScanParams& p, hipStream_t stream) {
-  const int64_t ntiles = (p.dim + kWW - 1) / kWW;
+  using S = WaveShape<CPW>;
+  const int64_t ntiles = (p.dim + S::CPB - 1) / S::CPB;
   const int64_t nblk = ntiles * p.batch;
   // 32-bit offsets: lanes' element offsets, and the staging's byte offsets
-  // within a chunk of kWC tokens
-  if (nblk > 0x7fffffff || kWC * p.dim * (int64_t)sizeof(IO) >= 0xffffffffLL) return hipErrorInvalidValue;
+  // within a chunk of TCK tokens
+  if (nblk > 0x7fffffff || S::TCK * p.dim * (int64_t)sizeof(IO) >= 0xffffffffLL) return hipErrorInvalidValue;
   // the 16-state path reads B and C rows as 16-byte vectors
   const bool vec = p.N == kNMax && (uintptr_t)p.B % 16 == 0 && (uintptr_t)p.C % 16 == 0;
-  auto kern = vec ? (p.ckpt ? scan_wave_kernel<IO, ZOH, GATE, true, true>
-                            : scan_wave_kernel<IO, ZOH, GATE, true, false>)
-                  : (p.ckpt ? scan_wave_kernel<IO, ZOH, GATE, false, true>
-                            : scan_wave_kernel<IO, ZOH, GATE, false, false>);
+  auto kern = vec ? (p.ckpt ? scan_wave_kernel<IO, ZOH, GATE, true, true, CPW>
+                            : scan_wave_kernel<IO, ZOH, GATE, true, false, CPW>)
+                  : (p.ckpt ? scan_wave_kernel<IO, ZOH, GATE, false, true, CPW>
+                            : scan_wave_kernel<IO, ZOH, GATE, false, false, CPW>);
   // the (channel, token) tiles are read and y written in row segments of 4 channels
-  const int vec_io = p.dim % kWW == 0 && (uintptr_t)p.u % 16 == 0 && (uintptr_t)p.delta % 16 == 0 &&
+  const int vec_io = p.dim % S::CPB == 0 && (uintptr_t)p.u % 16 == 0 && (uintptr_t)p.delta % 16 == 0 &&
                      (uintptr_t)p.z % 16 == 0 && (uintptr_t)p.y % 16 == 0;
-  hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(64 * kWW), 0, stream, (const IO*)p.u,
+  hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(S::NT), 0, stream, (const IO*)p.u,
                      (const IO*)p.delta, p.A, (const IO*)p.B, (const IO*)p.C, p.D,
                      (const IO*)p.z, p.delta_bias, p.h0, p.seq_lens, p.reset, (IO*)p.y,
                      p.last_state, p.ckpt, p.L, p.dim, (int)p.N, ntiles, p.softplus, vec_io);
   return hipGetLastError();
 }
 
-template <typename IO>
+template <typename IO, int CPW>
 hipError_t wave_io(const ScanParams& p, bool zoh, bool gate, hipStream_t stream) {
-  if (zoh) return gate ? wave_launch<IO, true, true>(p, stream) : wave_launch<IO, true, false>(p, stream);
-  return gate ? wave_launch<IO, false, true>(p, stream) : wave_launch<IO, false, false>(p, stream);
+  if (zoh)
+    return gate ? wave_launch<IO, true, true, CPW>(p, stream) : wave_launch<IO, true, false, CPW>(p, stream);
+  return gate ? wave_launch<IO, false, true, CPW>(p, stream) : wave_launch<IO, false, false, CPW>(p, stream);
 }
 
 template <typename IO, bool ZOH, bool GATE>
@@ -853,10 +950,12 @@ hipError_t launch_scan_tpar(const ScanParams& p, int io_dtype, bool zoh, bool ga
 }
 
 hipError_t launch_scan_wave(const ScanParams& p, int io_dtype, bool zoh, bool gate,
-                            hipStream_t stream) {
+                            int channels_per_wave, hipStream_t stream) {
   if (p.N < 1 || p.N > kNMax) return hipErrorInvalidValue;
-  if (io_dtype == 1) return wave_io<bf16_bits>(p, zoh, gate, stream);
-  return wave_io<float>(p, zoh, gate, stream);
+  if (channels_per_wave == 4)
+    return io_dtype == 1 ? wave_io<bf16_bits, 4>(p, zoh, gate, stream) : wave_io<float, 4>(p, zoh, gate, stream);
+  if (channels_per_wave != 1) return hipErrorInvalidValue;
+  return io_dtype == 1 ? wave_io<bf16_bits, 1>(p, zoh, gate, stream) : wave_io<float, 1>(p, zoh, gate, stream);
 }
 
 }  // namespace ssm66

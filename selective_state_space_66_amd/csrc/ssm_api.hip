@@ -39,22 +39,28 @@ int check_common(int64_t batch, int64_t len, int64_t dim, int64_t dstate, int io
   return SSM_OK;
 }
 
-// Kernel choice, from sweeps on MI355X (bf16, N 16, ZOH, gate):
+// Kernel choice, from sweeps on MI355X (bf16, N 16, ZOH, gate; kernel times):
 // - fewer than 1024 (batch x channel) rows and at least 128 tokens: the
 //   time-parallel kernel with four waves per row (88 against 153 us for one
-//   wave per row at 1 x 8192 x 256; slower from 1024 rows: 56 against 43 us
+//   wave per row at 1 x 8192 x 256; slower from 1024 rows: 52 against 39 us
 //   at 1 x 2048 x 1024);
-// - sequences under 256 tokens: the sequential kernel (19 against 30 us at
-//   8 x 64 x 1536; 37 against 31 us at 8 x 256 x 1536);
-// - 32768 rows or more: the sequential kernel with 4 states per lane, whose
-//   2048 waves fill every SIMD twice (426 against 484 us at 8 x 2048 x 4096);
-// - everything between: the time-parallel kernel with one wave per row
-//   (205 against 235 us at 8 x 2048 x 1536, 3.5 against 6.9 ms at
-//   4 x 65536 x 2048, 370 against 415 us at 16 x 2048 x 1536).
+// - 12288 rows or more (three waves per SIMD with four rows per wave) and at
+//   least 128 tokens: the time-parallel kernel with 16 lanes per row (161
+//   against 167 us for one wave per row at 8 x 2048 x 1536; 391 against 448,
+//   and 425 for the sequential kernel, at 8 x 2048 x 4096; 760 against 821
+//   for the sequential kernel at 16 x 2048 x 4096; 17 against 22 us for the
+//   sequential kernel at 8 x 128 x 1536, even at 8 x 64 x 1536);
+// - between 1024 and 12288 rows and at least 256 tokens: the time-parallel
+//   kernel with one wave per row (146 against 160 us for 16 lanes per row at
+//   2 x 2048 x 5120; 3.5 against 6.9 ms for the sequential kernel at
+//   4 x 65536 x 2048);
+// - shorter sequences: the sequential kernel (19 against 30 us for one wave
+//   per row at 8 x 64 x 1536).
 constexpr int64_t kTparMaxRows = 1023;
 constexpr int64_t kTparMinLen = 128;
 constexpr int64_t kWaveMinLen = 256;
-constexpr int64_t kSeqMinRows = 32768;
+constexpr int64_t kWave4MinRows = 12288;
+constexpr int64_t kWave4MinLen = 128;
 
 // Scan kernel shape: G states per thread, NG state groups per channel
 // (G * NG >= dstate).  Up to 8 states one group shape covers them; for 9..16
@@ -74,7 +80,7 @@ void pick_scan_shape(int64_t batch, int64_t dim, int64_t dstate, int forced_g, i
 }
 
 // Which scan kernel runs (see the crossovers above).
-enum class ScanKernel { kSequential, kTpar, kWave };
+enum class ScanKernel { kSequential, kTpar, kWave, kWave4 };
 
 // the time-parallel kernels address a 256-token chunk of up to 4-byte
 // elements with 32-bit offsets: 1024 dim < 2^32 - 1
@@ -84,13 +90,13 @@ ScanKernel pick_scan_kernel(int64_t batch, int64_t dim, int64_t L, int64_t dstat
   if (!tpar_fits(dim) || dstate > 16) return ScanKernel::kSequential;
   const int64_t rows = batch * dim;
   if (rows <= kTparMaxRows) return L >= kTparMinLen ? ScanKernel::kTpar : ScanKernel::kSequential;
-  if (L < kWaveMinLen || rows >= kSeqMinRows) return ScanKernel::kSequential;
-  return ScanKernel::kWave;
+  if (rows >= kWave4MinRows) return L >= kWave4MinLen ? ScanKernel::kWave4 : ScanKernel::kSequential;
+  return L >= kWaveMinLen ? ScanKernel::kWave : ScanKernel::kSequential;
 }
 
 // Grid of the chosen kernel within the launch limit (one block per 16
-// channels for the sequential kernel, per 8 for one wave per row, per row for
-// four waves per row).
+// channels for the sequential kernel and for 16 lanes per row, per 8 for one
+// wave per row, per row for four waves per row).
 bool grid_fits(ScanKernel k, int64_t batch, int64_t dim) {
   const int64_t per = k == ScanKernel::kWave ? 8 : (k == ScanKernel::kTpar ? 1 : 16);
   const __int128 blocks = (__int128)batch * ((dim + per - 1) / per);
@@ -179,9 +185,11 @@ static int scan_fwd_impl(int kernel, const void* u, const void* delta, const flo
     kern = ScanKernel::kSequential;  // writes the initial state only
   } else if (kernel == SSM_SCAN_KERNEL_AUTO) {
     kern = pick_scan_kernel(batch, dim, seqlen, dstate);
-  } else if (kernel == SSM_SCAN_KERNEL_TPAR || kernel == SSM_SCAN_KERNEL_WAVE) {
+  } else if (kernel == SSM_SCAN_KERNEL_TPAR || kernel == SSM_SCAN_KERNEL_WAVE ||
+             kernel == SSM_SCAN_KERNEL_WAVE4) {
     if (!tpar_fits(dim)) return SSM_ERR_UNSUPPORTED;
-    kern = kernel == SSM_SCAN_KERNEL_TPAR ? ScanKernel::kTpar : ScanKernel::kWave;
+    kern = kernel == SSM_SCAN_KERNEL_TPAR ? ScanKernel::kTpar
+                                          : (kernel == SSM_SCAN_KERNEL_WAVE ? ScanKernel::kWave : ScanKernel::kWave4);
   } else {
     forced_g = kernel == SSM_SCAN_KERNEL_SEQ1 ? 1 : (kernel == SSM_SCAN_KERNEL_SEQ2 ? 2 : 4);
   }
@@ -196,9 +204,9 @@ static int scan_fwd_impl(int kernel, const void* u, const void* delta, const flo
   if (kern == ScanKernel::kTpar) {
     e = ssm66::launch_scan_tpar(p, io_dtype, dt_mode == SSM_DT_ZOH, z != nullptr,
                                 (hipStream_t)stream);
-  } else if (kern == ScanKernel::kWave) {
+  } else if (kern == ScanKernel::kWave || kern == ScanKernel::kWave4) {
     e = ssm66::launch_scan_wave(p, io_dtype, dt_mode == SSM_DT_ZOH, z != nullptr,
-                                (hipStream_t)stream);
+                                kern == ScanKernel::kWave4 ? 4 : 1, (hipStream_t)stream);
   } else {
     int G, NG;
     pick_scan_shape(batch, dim, dstate, forced_g, &G, &NG);
@@ -214,7 +222,7 @@ int ssm_scan_fwd_kernel(int kernel, const void* u, const void* delta, const floa
                         const int32_t* seq_lens, const uint8_t* reset, void* y,
                         float* last_state, float* ckpt, int64_t batch, int64_t seqlen,
                         int64_t dim, int64_t dstate, int io_dtype, void* stream) {
-  if (kernel < SSM_SCAN_KERNEL_AUTO || kernel > SSM_SCAN_KERNEL_WAVE) return SSM_ERR_FLAG;
+  if (kernel < SSM_SCAN_KERNEL_AUTO || kernel > SSM_SCAN_KERNEL_WAVE4) return SSM_ERR_FLAG;
   return scan_fwd_impl(kernel, u, delta, A, B, C, D, z, delta_bias, softplus, dt_mode, h0,
                        seq_lens, reset, y, last_state, ckpt, batch, seqlen, dim, dstate, io_dtype,
                        stream);
@@ -236,6 +244,7 @@ const char* ssm_scan_kernel_name(int64_t batch, int64_t seqlen, int64_t dim, int
   switch (pick_scan_kernel(batch, dim, seqlen, dstate)) {
     case ScanKernel::kTpar: return "scan_tpar_kernel (time-parallel, four waves per row)";
     case ScanKernel::kWave: return "scan_wave_kernel (time-parallel, one wave per row)";
+    case ScanKernel::kWave4: return "scan_wave_kernel (time-parallel, 16 lanes per row)";
     default: break;
   }
   int G, NG;

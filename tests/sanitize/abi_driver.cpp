@@ -67,12 +67,12 @@ int main() {
   EXPECT(scan(P, F, P, 1, 2, (int64_t)1 << 40, 1, SSM_F32, 1, 0), SSM_ERR_UNSUPPORTED);
   EXPECT(scan(P, F, P, (int64_t)1 << 36, 1, 1 << 10, 16, SSM_BF16, 1, 0), SSM_ERR_UNSUPPORTED);
   // forced kernels
-  for (int k : {-1, SSM_SCAN_KERNEL_WAVE + 1, 1000})
+  for (int k : {-1, SSM_SCAN_KERNEL_WAVE4 + 1, 1000})
     EXPECT(ssm_scan_fwd_kernel(k, P, P, F, P, P, nullptr, nullptr, nullptr, 1, 0, nullptr,
                                nullptr, nullptr, P, nullptr, nullptr, 2, 5, 8, 16, SSM_BF16,
                                nullptr),
            SSM_ERR_FLAG);
-  for (int k = SSM_SCAN_KERNEL_AUTO; k <= SSM_SCAN_KERNEL_WAVE; ++k)
+  for (int k = SSM_SCAN_KERNEL_AUTO; k <= SSM_SCAN_KERNEL_WAVE4; ++k)
     EXPECT(ssm_scan_fwd_kernel(k, P, P, F, P, P, nullptr, nullptr, nullptr, 1, 0, nullptr,
                                nullptr, nullptr, P, nullptr, nullptr, 1, 2, (int64_t)1 << 50, 1,
                                SSM_BF16, nullptr),

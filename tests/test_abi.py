@@ -265,17 +265,23 @@ def test_scan_kernel_choice(lib):
     """The kernel the scan picks (host logic only): the crossovers measured on
     MI355X and the degenerate sizes."""
     name = ssm.scan_kernel_name
-    assert name(8, 2048, 1536, 16).startswith("scan_wave_kernel")      # Mamba-130M layer
-    assert name(4, 65536, 2048, 16).startswith("scan_wave_kernel")     # long sequences
-    assert name(8, 2048, 1536, 8).startswith("scan_wave_kernel")       # fewer states
-    assert name(1, 2048, 1024, 16).startswith("scan_wave_kernel")      # 1024 rows
+    sixteen = "scan_wave_kernel (time-parallel, 16 lanes per row)"
+    one = "scan_wave_kernel (time-parallel, one wave per row)"
+    assert name(8, 2048, 1536, 16) == sixteen                          # Mamba-130M layer: 12288 rows
+    assert name(8, 2048, 1535, 16) == one                              # 12280 rows
+    assert name(4, 65536, 2048, 16) == one                             # long sequences
+    assert name(8, 2048, 1536, 8) == sixteen                           # fewer states
+    assert name(8, 2048, 4096, 16) == sixteen                          # Mamba-1.4B layer
+    assert name(16, 2048, 2047, 16) == sixteen
+    assert name(1, 2048, 1024, 16) == one                              # 1024 rows
     assert name(1, 8192, 1023, 16).startswith("scan_tpar_kernel")      # 1023 rows
     assert name(1, 128, 256, 16).startswith("scan_tpar_kernel")
     assert name(1, 127, 256, 16) == "scan_fwd_kernel (sequential, 1 state per lane)"
-    assert name(8, 255, 1536, 16) == "scan_fwd_kernel (sequential, 2 states per lane)"
-    assert name(8, 256, 1536, 16).startswith("scan_wave_kernel")
-    assert name(8, 2048, 4096, 16) == "scan_fwd_kernel (sequential, 4 states per lane)"
-    assert name(16, 2048, 2047, 16).startswith("scan_wave_kernel")     # 32752 rows
+    assert name(8, 128, 1536, 16) == sixteen
+    assert name(8, 127, 1536, 16) == "scan_fwd_kernel (sequential, 2 states per lane)"
+    assert name(4, 255, 1536, 16) == "scan_fwd_kernel (sequential, 1 state per lane)"
+    assert name(4, 256, 1536, 16) == one
+    assert name(32, 127, 4096, 16) == "scan_fwd_kernel (sequential, 4 states per lane)"
     assert name(0, 16, 8, 16) == "none (no tokens)" and name(2, 0, 8, 16) == "none (no tokens)"
     assert name(1, 4, 4, 17) == "invalid shape" and name(-1, 4, 4, 4) == "invalid shape"
     assert name(1, 2048, 1 << 22, 16).startswith("scan_fwd_kernel")
@@ -298,16 +304,20 @@ def test_forced_kernel_validation(lib):
     launch limit of the chosen kernel, are unsupported -- all before any HIP
     call."""
     c = _header_constants()
-    assert c["SSM_SCAN_KERNEL_AUTO"] == 0 and c["SSM_SCAN_KERNEL_WAVE"] == 5
+    assert c["SSM_SCAN_KERNEL_AUTO"] == 0 and c["SSM_SCAN_KERNEL_WAVE4"] == 6
     assert _scan_kernel(lib, -1) == c["SSM_ERR_FLAG"]
-    assert _scan_kernel(lib, 6) == c["SSM_ERR_FLAG"]
+    assert _scan_kernel(lib, 7) == c["SSM_ERR_FLAG"]
     assert _scan_kernel(lib, c["SSM_SCAN_KERNEL_WAVE"], dim=1 << 22) == c["SSM_ERR_UNSUPPORTED"]
+    assert _scan_kernel(lib, c["SSM_SCAN_KERNEL_WAVE4"], dim=1 << 22) == c["SSM_ERR_UNSUPPORTED"]
     assert _scan_kernel(lib, c["SSM_SCAN_KERNEL_TPAR"], dim=1 << 22) == c["SSM_ERR_UNSUPPORTED"]
     # four waves per row: one block per (batch, channel) row
     assert _scan_kernel(lib, c["SSM_SCAN_KERNEL_TPAR"], batch=1 << 20, dim=1 << 12, L=1) \
         == c["SSM_ERR_UNSUPPORTED"]
     # one wave per row: one block per 8 channels of a batch entry
     assert _scan_kernel(lib, c["SSM_SCAN_KERNEL_WAVE"], batch=1 << 23, dim=1 << 11, L=1) \
+        == c["SSM_ERR_UNSUPPORTED"]
+    # 16 lanes per row: one block per 16 channels
+    assert _scan_kernel(lib, c["SSM_SCAN_KERNEL_WAVE4"], batch=1 << 24, dim=1 << 11, L=1) \
         == c["SSM_ERR_UNSUPPORTED"]
     # the automatic choice for the same shape is the sequential kernel, whose
     # blocks of 16 channels still fit

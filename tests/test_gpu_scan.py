@@ -144,7 +144,7 @@ def test_long_sequence_fp32(mode):
 
 # sequential kernels with G = 1, 2, 4 states per thread, and the two
 # time-parallel ones (four waves per row; one wave per row, four tokens per lane)
-KERNELS = ["seq1", "seq2", "seq4", "tpar", "wave"]
+KERNELS = ["seq1", "seq2", "seq4", "tpar", "wave", "wave4"]
 
 
 @pytest.mark.parametrize("kernel", KERNELS)
@@ -211,7 +211,7 @@ def test_each_kernel_short_sequences(kernel, L):
     assert_close(to_host64(last), lr, "f32", "last_state")
 
 
-@pytest.mark.parametrize("kernel", ["tpar", "wave"])
+@pytest.mark.parametrize("kernel", ["tpar", "wave", "wave4"])
 @pytest.mark.parametrize("N", [1, 5, 8, 16])
 @pytest.mark.parametrize("mode", ["zoh", "euler"])
 def test_time_parallel_state_sizes_and_chunks(kernel, N, mode):

@@ -192,7 +192,7 @@ def test_bwd_full_size_sampled():
 
 # ------------------------------------------------- the training forward's checkpoints
 
-@pytest.mark.parametrize("kernel", ["seq1", "seq2", "seq4", "tpar", "wave"])
+@pytest.mark.parametrize("kernel", ["seq1", "seq2", "seq4", "tpar", "wave", "wave4"])
 @pytest.mark.parametrize("mode", ["zoh", "euler"])
 def test_train_forward_checkpoints(kernel, mode):
     """scan_fwd_train gives scan_fwd's y and last_state bit for bit, and its
@@ -229,7 +229,7 @@ def test_train_forward_checkpoints(kernel, mode):
         assert err.max() <= 1e-4, f"checkpoint {j}: {err.max():.2e}"
 
 
-@pytest.mark.parametrize("kernel", [None, "tpar", "wave"])
+@pytest.mark.parametrize("kernel", [None, "tpar", "wave", "wave4"])
 @pytest.mark.parametrize("N", [3, 8])
 def test_train_forward_checkpoints_small_state(kernel, N):
     """State sizes below 16 (padded state groups in the sequential kernel,
@@ -356,7 +356,7 @@ def test_bwd_lengths_and_resets(io, mode, from_ckpt):
             assert torch.all(g[k][b, n:] == 0), f"{k} past length {n}"
 
 
-@pytest.mark.parametrize("kernel", ["seq1", "seq2", "seq4", "tpar", "wave"])
+@pytest.mark.parametrize("kernel", ["seq1", "seq2", "seq4", "tpar", "wave", "wave4"])
 def test_bwd_lengths_and_resets_from_every_forward(kernel):
     """The checkpoints of every forward kernel, taken with lengths and
     document starts, give the backward the oracle's gradients."""

@@ -12,7 +12,7 @@ import selective_state_space_66_amd as ssm
 pytestmark = pytest.mark.gpu
 
 # sequential kernels with G = 1, 2, 4 states per thread, and the time-parallel one
-KERNELS = ["seq1", "seq2", "seq4", "tpar", "wave"]
+KERNELS = ["seq1", "seq2", "seq4", "tpar", "wave", "wave4"]
 BF16_NAN = np.uint16(0x7FC0)
 
 
