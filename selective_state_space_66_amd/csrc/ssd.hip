@@ -124,18 +124,48 @@ __device__ __forceinline__ i16x4 tr_frag4(const __bf16* base, int lane) {
       (lds_i16x4*)(void*)(base + (4 * g + kk) * STRIDE + 4 * qq));
 }
 
-// Row strides (bf16 elements).  Bs and Hs rows are read 16 bytes per lane,
-// rows l % 16: a stride of 4 dwords mod 32 puts 8 consecutive rows on distinct
-// banks.  Xs rows are 32 bytes, so the 16 lanes of a transposing read (4 rows
-// x 4 column quads) cover the 32 banks once.  Everything a chunk reads is
+// B, C and the state sit in LDS in rows of N bf16 with the 16-byte pieces of
+// row r permuted: piece c is stored at c ^ swz(r).  Two access patterns meet
+// in these rows: 16-byte reads of one piece by 16 lanes on rows r .. r + 15
+// (the operands of the contractions over the states), and transposing reads
+// in which each group of 16 lanes takes 32 bytes from each of rows r .. r + 3
+// (the B operand of the state update); the staging writes whole rows.  swz
+// rotates the low three bits of r by one (and folds in bit 3), which gives
+// each lane of a pass its own banks in all three, with 32 banks as with 64,
+// where no plain row padding serves both of the first two.
+template <int N>
+__device__ __forceinline__ constexpr int swz(int r) {
+  return (((r << 1) & 6) | ((r >> 2) & 1)) ^ (((r >> 3) & 1) * (N == 128 ? 8 : 2));
+}
+// the element offset of column col within row r (col % 8 is kept)
+template <int N>
+__device__ __forceinline__ constexpr int sw(int r, int col) {
+  return (((col >> 3) ^ swz<N>(r)) << 3) | (col & 7);
+}
+
+// tr_frag on rows stored with the permutation: the fragment of the 16 x 32
+// (row x column) block at rows r0 .., columns col0 .., where rows points at
+// row r0, a multiple of 16 (so swz of its rows depends on the offset only).
+template <int N>
+__device__ __forceinline__ bf16x8 tr_frag_sw(const __bf16* rows, int col0, int lane) {
+  const int g = lane >> 4, kk = (lane & 15) >> 2, qq = lane & 3;
+  const int ra = 8 * g + kk, rb = ra + 4, col = col0 + 4 * qq;
+  const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(void*)(rows + ra * N + sw<N>(ra, col)));
+  const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(void*)(rows + rb * N + sw<N>(rb, col)));
+  const i16x8 v = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// Xs rows are 32 bytes, so the 16 lanes of a transposing read (4 rows x 4
+// column quads) cover 32 banks once.  Everything a chunk reads is
 // double-buffered by chunk parity, so staging the next chunk does not wait for
 // the current one: one barrier per chunk.
 template <int N>
 struct alignas(16) SSDSmem {
-  static constexpr int BS = N + 8;
-  __bf16 Bs[2][kQ][BS];         // B rows of a chunk (n contiguous)
+  static constexpr int BS = N;
+  __bf16 Bs[2][kQ][BS];         // B rows of a chunk (pieces permuted by swz)
   __bf16 Xs[2][kQ][kPS];        // this block's x columns (p contiguous)
-  __bf16 Hs[2][kPS][BS];        // the state entering a chunk, bf16
+  __bf16 Hs[2][kPS][BS];        // the state entering a chunk, bf16 (pieces permuted)
   ChunkConsts cc[2];            // per-token constants
 };
 
@@ -192,7 +222,7 @@ __device__ __forceinline__ void scores_times_x(const __bf16 (*Bs)[BS], const __b
   for (int k = 0; k < N / 32; ++k)
 #pragma unroll
     for (int sb = 0; sb <= W; ++sb)
-      g[sb] = mfma16(*(const bf16x8*)&Bs[16 * sb + lr][kn(k, lk)], as_bf16x8(cC[k]),
+      g[sb] = mfma16(*(const bf16x8*)&Bs[16 * sb + lr][sw<N>(lr, kn(k, lk))], as_bf16x8(cC[k]),
                      g[sb]);
   const float ct = kc.cuml[16 * W + lr];
 #pragma unroll
@@ -260,7 +290,7 @@ __global__ __launch_bounds__(256, 3) void ssd_fwd_kernel(const SSDArgs p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) Hacc[j][i] = p.h0[hrow + n + i];
     }
-    *(u32x2*)&sm.Hs[0][lr][n] =
+    *(u32x2*)&sm.Hs[0][lr][sw<N>(lr, n)] =
         u32x2{pack_bf16x2(Hacc[j][0], Hacc[j][1]), pack_bf16x2(Hacc[j][2], Hacc[j][3])};
   }
 
@@ -353,7 +383,10 @@ __global__ __launch_bounds__(256, 3) void ssd_fwd_kernel(const SSDArgs p) {
   auto stage = [&](int buf, int64_t t0) {
     const int nlive = (int)(L - t0 < kQ ? L - t0 : kQ);
 #pragma unroll
-    for (int r = 0; r < RB; ++r) *(u32x4*)&sm.Bs[buf][sB + r * kRowsPerPiece][cB8] = rB[r];
+    for (int r = 0; r < RB; ++r) {
+      const int row = sB + r * kRowsPerPiece;
+      *(u32x4*)&sm.Bs[buf][row][sw<N>(row, cB8)] = rB[r];
+    }
     *(u32x2*)&sm.Xs[buf][tx][4 * (tid & 3)] = tx < nlive ? rX : u32x2{0u, 0u};
     // C into the operand layout (lane group lk, lane m = token 16 w + m,
     // states kn(k, lk) ..): within each 16-lane row, the 8 lanes m >= 8 of the
@@ -411,7 +444,7 @@ __global__ __launch_bounds__(256, 3) void ssd_fwd_kernel(const SSDArgs p) {
     f32x4 y = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int k = 0; k < NK; ++k)
-      y = mfma16(*(const bf16x8*)&sm.Hs[cur][lr][kn(k, lk)], as_bf16x8(cC[k]), y);
+      y = mfma16(*(const bf16x8*)&sm.Hs[cur][lr][sw<N>(lr, kn(k, lk))], as_bf16x8(cC[k]), y);
     {
       const float e = kc.et[tz];
 #pragma unroll
@@ -450,14 +483,14 @@ __global__ __launch_bounds__(256, 3) void ssd_fwd_kernel(const SSDArgs p) {
         const bf16x8 xw = __builtin_convertvector(__builtin_convertvector(xt, f32x8) * ev, bf16x8);
 #pragma unroll
         for (int j = 0; j < NTW; ++j) {
-          const bf16x8 bt = tr_frag<Sm::BS>(&sm.Bs[cur][s0][16 * (w + kWaves * j)], lane);
+          const bf16x8 bt = tr_frag_sw<N>(&sm.Bs[cur][s0][0], 16 * (w + kWaves * j), lane);
           Hacc[j] = mfma16(bt, xw, Hacc[j]);
         }
       }
       // Hs[nxt] was last read in the previous chunk, before this chunk's barrier
 #pragma unroll
       for (int j = 0; j < NTW; ++j)
-        *(u32x2*)&sm.Hs[nxt][lr][16 * (w + kWaves * j) + 4 * lk] =
+        *(u32x2*)&sm.Hs[nxt][lr][sw<N>(lr, 16 * (w + kWaves * j) + 4 * lk)] =
             u32x2{pack_bf16x2(Hacc[j][0], Hacc[j][1]), pack_bf16x2(Hacc[j][2], Hacc[j][3])};
     }
 
@@ -500,11 +533,11 @@ constexpr int kGroups = 3;
 
 template <int N>
 struct alignas(16) SSDGroupSmem {
-  static constexpr int BS = N + 8;
-  __bf16 Bs[2][kQ][BS];                  // B rows of a chunk (shared)
-  __bf16 Cs[2][kQ][BS];                  // C rows of a chunk (shared)
+  static constexpr int BS = N;
+  __bf16 Bs[2][kQ][BS];                  // B rows of a chunk (shared; pieces permuted by swz)
+  __bf16 Cs[2][kQ][BS];                  // C rows of a chunk (shared; pieces permuted)
   __bf16 Xs[kGroups][2][kQ][kPS];        // each group's x columns
-  __bf16 Hs[kGroups][2][kPS][BS];        // each group's state, bf16
+  __bf16 Hs[kGroups][2][kPS][BS];        // each group's state, bf16 (pieces permuted)
   ChunkConsts cc[kGroups][2];            // each group's per-token constants
 };
 
@@ -554,7 +587,7 @@ __global__ __launch_bounds__(64 * kWaves * kGroups, 1) void ssd_fwd_grouped_kern
 #pragma unroll
       for (int i = 0; i < 4; ++i) Hacc[j][i] = p.h0[hrow + n + i];
     }
-    *(u32x2*)&sm.Hs[g][0][lr][n] =
+    *(u32x2*)&sm.Hs[g][0][lr][sw<N>(lr, n)] =
         u32x2{pack_bf16x2(Hacc[j][0], Hacc[j][1]), pack_bf16x2(Hacc[j][2], Hacc[j][3])};
   }
 
@@ -631,7 +664,7 @@ __global__ __launch_bounds__(64 * kWaves * kGroups, 1) void ssd_fwd_grouped_kern
       int row, col;
       bool isC, staged;
       piece(r, row, col, isC, staged);
-      if (staged) *(u32x4*)(isC ? &sm.Cs[buf][row][col] : &sm.Bs[buf][row][col]) = rBC[r];
+      if (staged) *(u32x4*)(isC ? &sm.Cs[buf][row][sw<N>(row, col)] : &sm.Bs[buf][row][sw<N>(row, col)]) = rBC[r];
     }
     *(u32x2*)&sm.Xs[g][buf][tx][4 * (tg & 3)] = tx < nlive ? rX : u32x2{0u, 0u};
     if constexpr (GATE) {
@@ -665,12 +698,12 @@ __global__ __launch_bounds__(64 * kWaves * kGroups, 1) void ssd_fwd_grouped_kern
 
     u32x4 cC[NK];
 #pragma unroll
-    for (int k = 0; k < NK; ++k) cC[k] = *(const u32x4*)&sm.Cs[cur][tz][kn(k, lk)];
+    for (int k = 0; k < NK; ++k) cC[k] = *(const u32x4*)&sm.Cs[cur][tz][sw<N>(tz, kn(k, lk))];
 
     f32x4 y = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int k = 0; k < NK; ++k)
-      y = mfma16(*(const bf16x8*)&sm.Hs[g][cur][lr][kn(k, lk)], as_bf16x8(cC[k]), y);
+      y = mfma16(*(const bf16x8*)&sm.Hs[g][cur][lr][sw<N>(lr, kn(k, lk))], as_bf16x8(cC[k]), y);
     {
       const float e = kc.et[tz];
 #pragma unroll
@@ -704,13 +737,13 @@ __global__ __launch_bounds__(64 * kWaves * kGroups, 1) void ssd_fwd_grouped_kern
         const bf16x8 xw = __builtin_convertvector(__builtin_convertvector(xt, f32x8) * ev, bf16x8);
 #pragma unroll
         for (int j = 0; j < NTW; ++j) {
-          const bf16x8 bt = tr_frag<Sm::BS>(&sm.Bs[cur][s0][16 * (w + kWaves * j)], lane);
+          const bf16x8 bt = tr_frag_sw<N>(&sm.Bs[cur][s0][0], 16 * (w + kWaves * j), lane);
           Hacc[j] = mfma16(bt, xw, Hacc[j]);
         }
       }
 #pragma unroll
       for (int j = 0; j < NTW; ++j)
-        *(u32x2*)&sm.Hs[g][nxt][lr][16 * (w + kWaves * j) + 4 * lk] =
+        *(u32x2*)&sm.Hs[g][nxt][lr][sw<N>(lr, 16 * (w + kWaves * j) + 4 * lk)] =
             u32x2{pack_bf16x2(Hacc[j][0], Hacc[j][1]), pack_bf16x2(Hacc[j][2], Hacc[j][3])};
     }
     stage(nxt, t0 + kQ);
