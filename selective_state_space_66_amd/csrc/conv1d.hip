@@ -280,16 +280,16 @@ __global__ __launch_bounds__(256) void conv1d_step_kernel(
 //   dw_i  = sum_t dpre_t xt_{t-i} [visible],   dbias = sum_t dpre_t,
 // and the carried-in window's gradient from the first K - 1 tokens; "s
 // visible from t" means no document starts in (s, t].  A thread owns VEC
-// channels and runs of kBwdT tokens; for a run it reads x from K - 1 tokens
-// before to K - 1 after, dout to K - 1 after (the halos mostly come from L2),
-// recomputes pre and dpre over the run and its halo, and writes dx of the run.
-// dw and dbias are summed over a thread's runs, then over the block's waves
-// through LDS, into one partial row per block; a second kernel adds the rows
-// in a fixed order.
-constexpr int kBwdT = 8;       // tokens per run
+// channels and kBwdRuns * kBwdT consecutive tokens, which it streams through
+// one pass with sliding windows: it reads x from K - 1 tokens before them to
+// K - 1 after, dout to K - 1 after, each row once, recomputes pre and dpre
+// over them and the K - 1 after, and writes their dx.  dw and dbias are summed
+// over a thread's tokens, then over the block's waves through LDS, into one
+// partial row per block; a second kernel adds the rows in a fixed order.
+constexpr int kBwdT = 8;       // positions per load block
 // word 3 of a raw buffer resource (no stride, 32-bit data format)
 constexpr int kConvBufferFlags = 0x00020000;
-constexpr int kBwdRuns = 4;    // runs per thread
+constexpr int kBwdRuns = 4;    // load blocks of tokens per thread
 constexpr int kBwdSpan = kConvWaves * kBwdRuns * kBwdT;  // tokens per block (128)
 
 struct ConvBwdArgs {
@@ -312,9 +312,6 @@ __device__ __forceinline__ float act_prime(float v, bool silu) {
 template <typename IO, int K, int VEC>
 __global__ __launch_bounds__(64 * kConvWaves) void conv1d_bwd_kernel(const ConvBwdArgs p) {
   using V = VecIO<IO, VEC>;
-  constexpr int NX = kBwdT + 2 * (K - 1);  // x at t0 - (K - 1) .. t0 + kBwdT + K - 2
-  constexpr int ND = kBwdT + K - 1;        // dout, dpre at t0 .. t0 + kBwdT + K - 2
-  static_assert(NX <= 32, "reset flags of a run fit one word");
   __shared__ float red[kConvWaves][VEC * (K + 1)][64];
 
   const IO* __restrict__ x = (const IO*)p.x;
@@ -366,73 +363,91 @@ __global__ __launch_bounds__(64 * kConvWaves) void conv1d_bwd_kernel(const ConvB
     vload<IO, VEC>(dso + (b * (K - 1) + j) * dim + c0, o);
   };
 
-  for (int r = 0; r < kBwdRuns; ++r) {
-    const int64_t t0 = span * kBwdSpan + (int64_t)(wave * kBwdRuns + r) * kBwdT;
-    if (t0 >= L) break;  // wave-uniform
-    // ---- loads first: x (window entries before token 0), dout, document starts
+  // ---- this thread's tokens: NT consecutive positions from s0 (the wave's
+  // part of the block's span), streamed through one pass with sliding
+  // windows.  At x-window index q (position s0 - (K - 1) + q):
+  //   - x enters the window (xw[i] is x i positions back);
+  //   - from q = K - 1 on, p = s0 + q - (K - 1): pre_p and dpre_p (zero past
+  //     the length; dpw[i] is dpre i positions back), and the dw and dbias
+  //     terms of p while p is one of this thread's tokens;
+  //   - from q = 2 (K - 1) on, dx of s = p - (K - 1), one of its tokens.
+  // The last K - 1 positions only complete dpre for the dx of the last
+  // tokens.  Every row is loaded once, kBwdT positions ahead of its first use.
+  constexpr int NT = kBwdRuns * kBwdT;             // tokens of a thread
+  constexpr int NXT = NT + 2 * (K - 1);            // x positions
+  constexpr int NDT = NT + (K - 1);                // dout positions
+  static_assert(NXT <= 64, "document starts of a thread fit one 64-bit word");
+  const int64_t s0 = span * kBwdSpan + (int64_t)wave * NT;
+  if (s0 < L) {  // wave-uniform
+    typename V::Raw xr[NXT], dr[NDT];
+    const int32_t tl = (int32_t)(L - 1);
     // buffer loads: the row's byte offset is scalar (rows clamped into the
     // sequence), the lane's channels its 32-bit vector offset
-    typename V::Raw xr[NX], dr[ND];
-    const int32_t tl = (int32_t)(L - 1);
-#pragma unroll
-    for (int q = 0; q < NX; ++q) {
-      const int32_t pos = (int32_t)t0 - (K - 1) + q;
-      if (pos < 0 && sin)  // the carried-in window (first run only)
+    auto load_x = [&](int q) {
+      const int32_t pos = (int32_t)s0 - (K - 1) + q;
+      if (pos < 0 && sin)  // the carried-in window (the sequence's first tokens only)
         xr[q] = V::bload(rwin, loff, (uint32_t)(K - 1 + pos) * rowb);
       else
         xr[q] = V::bload(rx, loff, (uint32_t)(pos < 0 ? 0 : (pos < tl ? pos : tl)) * rowb);
-    }
-#pragma unroll
-    for (int q = 0; q < ND; ++q) {
-      const int32_t pos = (int32_t)t0 + q;
-      dr[q] = V::bload(rd, loff, (uint32_t)(pos < tl ? pos : tl) * rowb);
-    }
-    uint32_t starts = 0;  // bit q: a document starts at t0 - (K - 1) + q (real tokens only)
+    };
+    auto load_d = [&](int j) {
+      const int32_t pos = (int32_t)s0 + j;
+      dr[j] = V::bload(rd, loff, (uint32_t)(pos < tl ? pos : tl) * rowb);
+    };
+    uint64_t starts = 0;  // bit q: a document starts at s0 - (K - 1) + q (real tokens only)
     if (p.reset) {
 #pragma unroll
-      for (int q = 0; q < NX; ++q) {
-        const int64_t pos = t0 - (K - 1) + q;
-        if (pos >= 0 && pos < len && p.reset[b * L + pos]) starts |= 1u << q;
+      for (int q = 0; q < NXT; ++q) {
+        const int64_t pos = s0 - (K - 1) + q;
+        if (pos >= 0 && pos < len && p.reset[b * L + pos]) starts |= 1ull << q;
       }
-      starts = __builtin_amdgcn_readfirstlane(starts);  // the same for every lane
+      // the same for every lane
+      const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)starts);
+      const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(starts >> 32));
+      starts = (uint64_t)lo | ((uint64_t)hi << 32);
     }
     // no document starts at positions qa + 1 .. qb (window indices)
     auto visible = [&](int qa, int qb) -> bool {
-      const uint32_t m = (qb >= 31 ? 0xffffffffu : ((1u << (qb + 1)) - 1u)) & ~((1u << (qa + 1)) - 1u);
-      return (starts & m) == 0;
+      const uint64_t upto = qb >= 63 ? ~0ull : ((1ull << (qb + 1)) - 1ull);
+      return (starts & upto & ~((1ull << (qa + 1)) - 1ull)) == 0;
     };
     // x at window index q, or 0 where the forward read a zero (before token 0
     // with no window given)
     auto xin = [&](int q, float (&o)[VEC]) {
       V::unpack(xr[q], o);
-      if (t0 - (K - 1) + q < 0 && !sin) {
+      if (s0 - (K - 1) + q < 0 && !sin) {
 #pragma unroll
         for (int v = 0; v < VEC; ++v) o[v] = 0.0f;
       }
     };
 
-    // ---- one pass over the positions t0 - (K - 1) .. t0 + kBwdT + K - 2 with
-    // sliding windows: xw[i] is x i positions back, dpw[i] dpre i positions
-    // back.  At position p: dpre_p (p >= t0; zero past the length), the dw and
-    // dbias terms of p (p in the run), and dx of s = p - (K - 1) (s in the run).
+    // the first kBwdT x positions (and the dout positions read with them); then
+    // each position issues the loads kBwdT positions ahead (dout at j is first
+    // read at x position j + K - 1)
+#pragma unroll
+    for (int q = 0; q < kBwdT; ++q) load_x(q);
+#pragma unroll
+    for (int j = 0; j < kBwdT - (K - 1); ++j) load_d(j);
     float xw[K][VEC], dpw[K][VEC];
 #pragma unroll
     for (int i = 0; i < K; ++i)
 #pragma unroll
       for (int v = 0; v < VEC; ++v) xw[i][v] = dpw[i][v] = 0.0f;
 #pragma unroll
-    for (int q = 0; q < NX; ++q) {
+    for (int q = 0; q < NXT; ++q) {
+      if (q + kBwdT < NXT) load_x(q + kBwdT);
+      if (q + kBwdT - (K - 1) >= 0 && q + kBwdT - (K - 1) < NDT) load_d(q + kBwdT - (K - 1));
       // one position at a time: unpacking every loaded bf16 row at once would
-      // hold them all as fp32
+      // hold them all as fp32, and the loads stay where they are issued
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = K - 1; i >= 1; --i)
 #pragma unroll
         for (int v = 0; v < VEC; ++v) xw[i][v] = xw[i - 1][v];
       xin(q, xw[0]);
-      if (q >= K - 1) {  // p = t0 + j
+      if (q >= K - 1) {  // p = s0 + j
         const int j = q - (K - 1);
-        const int64_t pp = t0 + j;
+        const int64_t pp = s0 + j;
         float pre[VEC];
 #pragma unroll
         for (int v = 0; v < VEC; ++v) pre[v] = bs[v];
@@ -450,7 +465,7 @@ __global__ __launch_bounds__(64 * kConvWaves) void conv1d_bwd_kernel(const ConvB
           for (int v = 0; v < VEC; ++v) dpw[i][v] = dpw[i - 1][v];
 #pragma unroll
         for (int v = 0; v < VEC; ++v) dpw[0][v] = pp < len ? dov[v] * act_prime(pre[v], silu) : 0.0f;
-        if (j < kBwdT && pp < len) {
+        if (j < NT && pp < len) {
 #pragma unroll
           for (int i = 0; i < K; ++i) {
             const bool vis = visible(q - i, q);
@@ -461,10 +476,10 @@ __global__ __launch_bounds__(64 * kConvWaves) void conv1d_bwd_kernel(const ConvB
           for (int v = 0; v < VEC; ++v) db[v] += dpw[0][v];
         }
       }
-      if (q >= 2 * (K - 1)) {  // dx of s = t0 + m
+      if (q >= 2 * (K - 1)) {  // dx of s = s0 + m
         const int m = q - 2 * (K - 1);
         const int qs = q - (K - 1);
-        const int64_t s = t0 + m;
+        const int64_t s = s0 + m;
         float acc[VEC];
 #pragma unroll
         for (int v = 0; v < VEC; ++v) acc[v] = 0.0f;
@@ -474,7 +489,7 @@ __global__ __launch_bounds__(64 * kConvWaves) void conv1d_bwd_kernel(const ConvB
 #pragma unroll
           for (int v = 0; v < VEC; ++v) acc[v] = fmaf(wt[v][i], vis ? dpw[K - 1 - i][v] : 0.0f, acc[v]);
         }
-        if (dso && s < len && s >= len - (K - 1) && visible(qs, (int)(len - 1 - t0) + K - 1)) {
+        if (dso && s < len && s >= len - (K - 1) && visible(qs, (int)(len - 1 - s0) + K - 1)) {
           float o[VEC];
           dwo(s - (len - (K - 1)), o);
 #pragma unroll
@@ -482,9 +497,10 @@ __global__ __launch_bounds__(64 * kConvWaves) void conv1d_bwd_kernel(const ConvB
         }
         if (cok && s < L) V::store((IO*)p.dx + (b * L + s) * dim + c0, acc);
       }
-      // the carried-in window's gradient, in the first run of the sequence,
-      // once dpre at positions 0 .. K - 2 is known (dpre at P is dpw[K - 2 - P])
-      if (K > 1 && q == 2 * K - 3 && t0 == 0 && sin && p.dstate_in && cok) {
+      // the carried-in window's gradient, by the thread that starts the
+      // sequence, once dpre at positions 0 .. K - 2 is known (dpre at P is
+      // dpw[K - 2 - P])
+      if (K > 1 && q == 2 * K - 3 && s0 == 0 && sin && p.dstate_in && cok) {
 #pragma unroll
         for (int jw = 0; jw < K - 1; ++jw) {
           const int sw = -(K - 1) + jw;  // the window entry's position
