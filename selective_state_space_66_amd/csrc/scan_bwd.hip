@@ -60,7 +60,7 @@ struct BSmem {
   float4 dd[S::TC][S::CW];                  // (Delta, u, ds, -) per token and channel
   int rst[S::TC];                           // document starts within the chunk
   float bc[S::TC][S::NG][2 * S::G];         // B then C of each group, per token
-  float part[2][S::NG][S::PST];             // per-group partial sums per (token, channel)
+  float part[3][S::NG][S::PST];             // per-group partial sums per (token, channel)
   float red[2][S::HALF][S::NPAD][S::CW + 1];  // dB, dC contributions per (token, state, channel)
   float chan[2][S::NG][S::CW];              // dD, d bias per (group, channel), at the end
 };
@@ -102,6 +102,7 @@ struct BwdArgs {
   float* dh0;
   float* ckpt;    // (batch, nchunks, dim, N)
   int have_ckpt;  // ckpt was written by the forward: no pass 1
+  int split_fast; // the FAST instance is launched too: each block runs in one
   float* pbc;     // (ntiles, 2, batch, L, N)
   float* pA;      // (batch, dim, N)
   float* pDb;     // (2, batch, dim)
@@ -110,11 +111,14 @@ struct BwdArgs {
 };
 
 // RST: document starts are given (a separate instance, so that the common
-// case carries none of their registers)
-template <typename IO, int G, int NG, bool ZOH, bool GATE, bool RST>
+// case carries none of their registers).  FAST: the instance for blocks whose
+// states all have |A| >= 1/2 (ZOH); with split_fast set, the two instances
+// are launched over the same grid and each block runs in the one that fits.
+template <typename IO, int G, int NG, bool ZOH, bool GATE, bool RST, bool FAST>
 __global__ __launch_bounds__((BShape<G, NG>::THREADS)) void scan_bwd_kernel(const BwdArgs p) {
   using S = BShape<G, NG>;
   constexpr int CW = S::CW, TC = S::TC, RPT = S::RPT, NPAD = S::NPAD, HALF = S::HALF;
+  static_assert(ZOH || !FAST, "the fast form is a ZOH form");
   __shared__ BSmem<S> sm;
 
   const IO* __restrict__ u = (const IO*)p.u;
@@ -153,9 +157,16 @@ __global__ __launch_bounds__((BShape<G, NG>::THREADS)) void scan_bwd_kernel(cons
     CA[k] = Aa[k] != 0.0f ? 1.0f / Aa[k] : 0.0f;
     if (real && !(fabsf(Aa[k]) >= 0.5f)) small_a = true;
   }
+  // pass 2 takes the g form (g = A h) in the FAST instance: every state of
+  // the block has |A| >= 1/2, where abar - 1 and 1/A are accurate enough
+  // (block-uniform choice; the other blocks leave)
+  if (p.split_fast) {
+    const bool block_fast = ZOH && !__syncthreads_or(small_a);
+    if (block_fast != FAST) return;
+  }
   // pass 1 under ZOH keeps g = A h, as the forward's fast form, unless a lane
   // of the wave has a small |A| (wave-uniform choice)
-  const bool fast = ZOH && !__any(small_a);
+  const bool fast = FAST || (ZOH && !__any(small_a));
   const float bias = p.bias ? p.bias[cc] : 0.0f;
   const float dskip = p.D ? p.D[cc] : 0.0f;
 
@@ -196,7 +207,7 @@ __global__ __launch_bounds__((BShape<G, NG>::THREADS)) void scan_bwd_kernel(cons
   // channel), B and C per (token, state); the epilogue values of this
   // thread's tokens stay in registers.  Tokens past L get zeros, and so do u
   // and dy of channels past dim.
-  float e_dy[RPT], e_sv[RPT], e_gz[RPT], e_dg[RPT], e_u[RPT], e_ds[RPT];
+  float e_dy[RPT], e_sv[RPT], e_dg[RPT], e_u[RPT], e_ds[RPT];
   // returns whether this thread staged a document start (cl == 0 threads
   // stage the chunk's flags)
   auto stage = [&](int64_t t0, bool bwd) -> int {
@@ -227,7 +238,6 @@ __global__ __launch_bounds__((BShape<G, NG>::THREADS)) void scan_bwd_kernel(cons
         }
         ds = dyv * gz;
         e_dy[i] = dyv;
-        e_gz[i] = gz;
         e_dg[i] = dg;
         e_u[i] = x;
         e_ds[i] = ds;
@@ -270,7 +280,7 @@ __global__ __launch_bounds__((BShape<G, NG>::THREADS)) void scan_bwd_kernel(cons
     if (fast) h[k] *= Aa[k];
   }
   auto p1_tokens = [&](auto full_tag, auto fast_tag, int nt) {
-    constexpr bool FULL = decltype(full_tag)::value, FAST = decltype(fast_tag)::value;
+    constexpr bool FULL = decltype(full_tag)::value, P1F = decltype(fast_tag)::value;
 #pragma unroll
     for (int t = 0; t < TC; ++t) {
       if (FULL || t < nt) {
@@ -283,7 +293,7 @@ __global__ __launch_bounds__((BShape<G, NG>::THREADS)) void scan_bwd_kernel(cons
         for (int k = 0; k < G; ++k) {
           const float Bv = sm.bc[t][g][k];
           const float a = exp2_hw(d4.x * Ap[k]);
-          if constexpr (FAST) {
+          if constexpr (P1F) {
             const float ub = d4.y * Bv;
             h[k] = fmaf(a, h[k] + ub, -ub);
           } else {
@@ -352,12 +362,16 @@ __global__ __launch_bounds__((BShape<G, NG>::THREADS)) void scan_bwd_kernel(cons
     }
     const bool rst = staged(starts);
 
-    // recompute: states, abar and phi of the chunk; partial pre-gate readout
-    // (for dz).  Full chunks run unguarded.
-    float hs[TC][G], as[TC][G], ps[TC][G];
+    // recompute: the chunk's states and abar (and phi, off the fast form).
+    // On the fast form the registers hold g = A h; gst is the chunk start's.
+    float hs[TC][G], as[TC][G], ps[TC][G], gst[G];
 #pragma unroll
-    for (int k = 0; k < G; ++k) h[k] = hst[k];
+    for (int k = 0; k < G; ++k) {
+      gst[k] = FAST ? hst[k] * Aa[k] : hst[k];
+      h[k] = gst[k];
+    }
     const bool want_s = GATE && p.want_dz;
+    // off the fast form the partial pre-gate readout s (for dz) is taken here
     auto recompute = [&](auto full_tag) {
       constexpr bool FULL = decltype(full_tag)::value;
 #pragma unroll
@@ -371,37 +385,53 @@ __global__ __launch_bounds__((BShape<G, NG>::THREADS)) void scan_bwd_kernel(cons
           float acc = 0.0f;
 #pragma unroll
           for (int k = 0; k < G; ++k) {
+            const float Bv = sm.bc[t][g][k];
             const float a = exp2_hw(d4.x * Ap[k]);
-            const float phi = ZOH ? phi_of(d4.x * Aa[k], a, d4.w * CA[k]) : 1.0f;
-            update_state(h[k], a, phi, d4.x, d4.y, sm.bc[t][g][k]);
+            if constexpr (FAST) {
+              const float ub = d4.y * Bv;
+              h[k] = fmaf(a, h[k] + ub, -ub);
+            } else {
+              const float phi = ZOH ? phi_of(d4.x * Aa[k], a, d4.w * CA[k]) : 1.0f;
+              update_state(h[k], a, phi, d4.x, d4.y, Bv);
+              ps[t][k] = phi;
+              acc = fmaf(sm.bc[t][g][G + k], h[k], acc);
+            }
             hs[t][k] = h[k];
             as[t][k] = a;
-            ps[t][k] = phi;
-            acc = fmaf(sm.bc[t][g][G + k], h[k], acc);
           }
-          if (want_s) sm.part[0][g][t * CW + cl] = acc;
+          if (!FAST && want_s) sm.part[0][g][t * CW + cl] = acc;
         }
       }
     };
-    if (nt == TC && !rst) recompute(std::true_type());
+    const bool full = nt == TC && !rst;
+    if (full) recompute(std::true_type());
     else recompute(std::false_type());
-    lds_barrier();
-    // dz = dy s silu'(z), s = C.h + D u (this thread's tokens)
-    if constexpr (GATE) {
-      if (p.want_dz) {
+    if constexpr (FAST) {
+      // the final state h_T (the state after the last real token: padding
+      // tokens leave it unchanged) enters dA on the fast form
+      if (t0 < Lb && Lb <= t0 + TC) {
 #pragma unroll
-        for (int i = 0; i < RPT; ++i) {
-          const int r = g + NG * i;
-          const int64_t t = t0 + r;
-          if (cvalid && r < nt) {
-            float s = fmaf(dskip, e_u[i], 0.0f);
-            for (int j = 0; j < NG; ++j) s += sm.part[0][j][r * CW + cl];
-            store_io((IO*)p.dz + (row0 + t) * dim + c, e_dy[i] * s * e_dg[i]);
+        for (int k = 0; k < G; ++k) dA[k] = fmaf(-gad[k], h[k] * CA[k], dA[k]);
+      }
+    } else {
+      lds_barrier();
+      // dz = dy s silu'(z), s = C.h + D u (this thread's tokens)
+      if constexpr (GATE) {
+        if (p.want_dz) {
+#pragma unroll
+          for (int i = 0; i < RPT; ++i) {
+            const int r = g + NG * i;
+            const int64_t t = t0 + r;
+            if (cvalid && r < nt) {
+              float sv = fmaf(dskip, e_u[i], 0.0f);
+              for (int j = 0; j < NG; ++j) sv += sm.part[0][j][r * CW + cl];
+              store_io((IO*)p.dz + (row0 + t) * dim + c, e_dy[i] * sv * e_dg[i]);
+            }
           }
         }
       }
+      lds_barrier();
     }
-    lds_barrier();
 
     // the adjoint backwards through the chunk, in two rounds of HALF tokens
 #pragma unroll
@@ -417,44 +447,62 @@ __global__ __launch_bounds__((BShape<G, NG>::THREADS)) void scan_bwd_kernel(cons
             const float xdl = x * dl;
             // a document start: the update saw h_{t-1} = 0 and carries nothing back
             const bool start = RST && !FULL && sm.rst[t] != 0;
-            float ddt = 0.0f, dx = 0.0f;
+            float ddt = 0.0f, dx = 0.0f, sacc = 0.0f;
 #pragma unroll
             for (int k = 0; k < G; ++k) {
               const float Bv = sm.bc[t][g][k], Cv = sm.bc[t][g][G + k];
               const float a = as[t][k];
-              const float hp = start ? 0.0f : (t > 0 ? hs[t > 0 ? t - 1 : 0][k] : hst[k]);
+              const float hp = start ? 0.0f : (t > 0 ? hs[t > 0 ? t - 1 : 0][k] : gst[k]);
               // q is the adjoint of h_t (q abar carries it to t - 1); the
               // adjoints of abar and bbar u are q h_{t-1} and q.  Channels
               // past dim stage u = ds = 0, so their dB, dC terms are zero.
               const float q = fmaf(ds, Cv, gad[k]);
               const float qa = q * a;
-              const float xB = x * Bv;
-              if constexpr (ZOH) {
-                const float phi = ps[t][k];
-                const float dphi = phi_prime(dl * Aa[k], a, phi, rdl * CA[k]);
-                // dDelta: q (h_{t-1} A + u B) abar (d bbar/dDelta = abar B);
-                // dA: q (h_{t-1} Delta abar + u B Delta^2 phi'); dB: q u Delta
-                // phi; du: q Delta B phi
-                ddt = fmaf(qa, fmaf(hp, Aa[k], xB), ddt);
-                dA[k] = fmaf(dl, fmaf(q * xB * dl, dphi, qa * hp), dA[k]);
-                const float qp = q * phi;
-                sm.red[0][tt][n0 + k][cl] = qp * xdl;
-                dx = fmaf(qp, dl * Bv, dx);
+              if constexpr (FAST) {
+                // g form (hp, hs hold g = A h; bbar u = (abar - 1) u B / A):
+                // dDelta: q abar (g_{t-1} + u B); dB, du: w u, w B with
+                // w = q (abar - 1) / A; dA collects Delta q abar (g_{t-1} +
+                // u B) - ds C h here (times 1/A at the end)
+                const float hv = hs[t][k] * CA[k];
+                const float Ch = Cv * hv;
+                if (want_s) sacc += Ch;
+                const float m = qa * fmaf(x, Bv, hp);
+                ddt += m;
+                dA[k] = fmaf(-ds, Ch, fmaf(dl, m, dA[k]));
+                const float w = (qa - q) * CA[k];
+                sm.red[0][tt][n0 + k][cl] = w * x;
+                sm.red[1][tt][n0 + k][cl] = ds * hv;
+                dx = fmaf(w, Bv, dx);
               } else {
-                ddt = fmaf(qa * hp, Aa[k], fmaf(q, xB, ddt));
-                dA[k] = fmaf(qa * hp, dl, dA[k]);
-                sm.red[0][tt][n0 + k][cl] = q * xdl;
-                dx = fmaf(q * dl, Bv, dx);
+                const float xB = x * Bv;
+                if constexpr (ZOH) {
+                  const float phi = ps[t][k];
+                  const float dphi = phi_prime(dl * Aa[k], a, phi, rdl * CA[k]);
+                  // dDelta: q (h_{t-1} A + u B) abar (d bbar/dDelta = abar B);
+                  // dA: q (h_{t-1} Delta abar + u B Delta^2 phi'); dB: q u Delta
+                  // phi; du: q Delta B phi
+                  ddt = fmaf(qa, fmaf(hp, Aa[k], xB), ddt);
+                  dA[k] = fmaf(dl, fmaf(q * xB * dl, dphi, qa * hp), dA[k]);
+                  const float qp = q * phi;
+                  sm.red[0][tt][n0 + k][cl] = qp * xdl;
+                  dx = fmaf(qp, dl * Bv, dx);
+                } else {
+                  ddt = fmaf(qa * hp, Aa[k], fmaf(q, xB, ddt));
+                  dA[k] = fmaf(qa * hp, dl, dA[k]);
+                  sm.red[0][tt][n0 + k][cl] = q * xdl;
+                  dx = fmaf(q * dl, Bv, dx);
+                }
+                sm.red[1][tt][n0 + k][cl] = ds * hs[t][k];
               }
-              sm.red[1][tt][n0 + k][cl] = ds * hs[t][k];
               gad[k] = start ? 0.0f : qa;
             }
             sm.part[0][g][t * CW + cl] = ddt;
             sm.part[1][g][t * CW + cl] = dx;
+            if (FAST && want_s) sm.part[2][g][t * CW + cl] = sacc;
           }
         }
       };
-      if (nt == TC && !rst) reverse(std::true_type());
+      if (full) reverse(std::true_type());
       else reverse(std::false_type());
       lds_barrier();
       // dB, dC of these HALF tokens: sum over the block's channels
@@ -473,16 +521,18 @@ __global__ __launch_bounds__((BShape<G, NG>::THREADS)) void scan_bwd_kernel(cons
       lds_barrier();
     }
 
-    // epilogue: d(raw delta), du; sums for dD and d bias
+    // epilogue: d(raw delta), du (and on the fast form dz = dy s silu'(z),
+    // s = C.h + D u); sums for dD and d bias
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
       const int r = g + NG * i;
       const int64_t t = t0 + r;
       if (r < nt) {
-        float ddt = 0.0f, dx = e_ds[i] * dskip;
+        float ddt = 0.0f, dx = e_ds[i] * dskip, sv = dskip * e_u[i];
         for (int j = 0; j < NG; ++j) {
           ddt += sm.part[0][j][r * CW + cl];
           dx += sm.part[1][j][r * CW + cl];
+          if (FAST && want_s) sv += sm.part[2][j][r * CW + cl];
         }
         const float dv = t < Lb ? ddt * e_sv[i] : 0.0f;  // padding: no step size
         accB += dv;
@@ -490,6 +540,9 @@ __global__ __launch_bounds__((BShape<G, NG>::THREADS)) void scan_bwd_kernel(cons
         if (cvalid) {
           store_io((IO*)p.ddelta + (row0 + t) * dim + c, dv);
           store_io((IO*)p.du + (row0 + t) * dim + c, dx);
+          if constexpr (GATE && FAST) {
+            if (want_s) store_io((IO*)p.dz + (row0 + t) * dim + c, e_dy[i] * sv * e_dg[i]);
+          }
         }
       }
     }
@@ -497,13 +550,21 @@ __global__ __launch_bounds__((BShape<G, NG>::THREADS)) void scan_bwd_kernel(cons
   }
 
   // ---- per-block results: dh0 (the carried adjoint is abar_0 g_0), dA,
-  // dD and d bias partials for this batch entry
+  // dD and d bias partials for this batch entry.  On the fast form dA holds
+  // A dA - h0 dh0 (the sum over the updates of q dbbar/dA u, which it lacks,
+  // equals sum ds C h + dlast h_T - h0 dh0: the adjoint identity of a linear
+  // recurrence); with no real token there is nothing to add.
   if (cvalid) {
 #pragma unroll
     for (int k = 0; k < G; ++k) {
       if (n0 + k < N) {
+        float dAk = dA[k];
+        if constexpr (FAST) {
+          if (p.h0 && Lb > 0) dAk = fmaf(p.h0[(b * dim + c) * N + n0 + k], gad[k], dAk);
+          dAk *= CA[k];
+        }
         if (p.dh0) p.dh0[(b * dim + c) * N + n0 + k] = gad[k];
-        p.pA[(b * dim + c) * N + n0 + k] = dA[k];
+        p.pA[(b * dim + c) * N + n0 + k] = dAk;
       }
     }
   }
@@ -559,18 +620,30 @@ __global__ __launch_bounds__(256) void bwd_finalize_params(
   }
 }
 
-template <typename IO, int G, int NG, bool ZOH, bool GATE>
-hipError_t bwd_launch_one(const BwdArgs& a, hipStream_t stream) {
+template <typename IO, int G, int NG, bool ZOH, bool GATE, bool FAST>
+hipError_t bwd_launch_rst(const BwdArgs& a, hipStream_t stream) {
   using S = BShape<G, NG>;
   const int64_t nblk = a.ntiles * a.batch;
-  if (nblk > 0x7fffffff) return hipErrorInvalidValue;
   if (a.reset)
-    hipLaunchKernelGGL((scan_bwd_kernel<IO, G, NG, ZOH, GATE, true>), dim3((unsigned)nblk),
+    hipLaunchKernelGGL((scan_bwd_kernel<IO, G, NG, ZOH, GATE, true, FAST>), dim3((unsigned)nblk),
                        dim3(S::THREADS), 0, stream, a);
   else
-    hipLaunchKernelGGL((scan_bwd_kernel<IO, G, NG, ZOH, GATE, false>), dim3((unsigned)nblk),
+    hipLaunchKernelGGL((scan_bwd_kernel<IO, G, NG, ZOH, GATE, false, FAST>), dim3((unsigned)nblk),
                        dim3(S::THREADS), 0, stream, a);
   return hipGetLastError();
+}
+
+// ZOH with N > 8 launches the exact instance and the fast one over the same
+// grid; each block runs in one of them.  Other shapes and Euler run the exact
+// instance alone.
+template <typename IO, int G, int NG, bool ZOH, bool GATE>
+hipError_t bwd_launch_one(BwdArgs a, hipStream_t stream) {
+  if (a.ntiles * a.batch > 0x7fffffff) return hipErrorInvalidValue;
+  constexpr bool kSplit = ZOH && G == 2 && NG == 8;
+  a.split_fast = kSplit ? 1 : 0;
+  const hipError_t e = bwd_launch_rst<IO, G, NG, ZOH, GATE, false>(a, stream);
+  if (e != hipSuccess || !kSplit) return e;
+  return bwd_launch_rst<IO, G, NG, ZOH, GATE, kSplit>(a, stream);
 }
 
 template <typename IO, int G, int NG>
