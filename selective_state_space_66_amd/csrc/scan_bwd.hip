@@ -32,6 +32,7 @@
 // from zero, the update sees h_{t-1} = 0 and no adjoint is carried to t - 1.
 #include <type_traits>
 
+#include "ssm_bwd.h"
 #include "ssm_device.h"
 #include "ssm_launch.h"
 
@@ -93,22 +94,6 @@ __device__ __forceinline__ float phi_prime(float k, float a, float phi, float rk
   return fabsf(k) < 0.5f ? d : (a - phi) * rk;
 }
 
-struct BwdArgs {
-  const void *u, *delta, *B, *C, *z, *dy;
-  const float *A, *D, *bias, *h0, *dlast;
-  const int32_t* seq_lens;  // nullable: real tokens per sequence
-  const uint8_t* reset;     // nullable: document starts (batch, L)
-  void *du, *ddelta, *dz;
-  float* dh0;
-  float* ckpt;    // (batch, nchunks, dim, N)
-  int have_ckpt;  // ckpt was written by the forward: no pass 1
-  int split_fast; // the FAST instance is launched too: each block runs in one
-  float* pbc;     // (ntiles, 2, batch, L, N)
-  float* pA;      // (batch, dim, N)
-  float* pDb;     // (2, batch, dim)
-  int64_t batch, L, dim, N, ntiles, nchunks;
-  int softplus, want_dz;
-};
 
 // RST: document starts are given (a separate instance, so that the common
 // case carries none of their registers).  FAST: the instance for blocks whose
@@ -677,7 +662,18 @@ hipError_t bwd_io(const ScanBwdParams& q, bool zoh, bool gate, hipStream_t strea
   w += (size_t)q.batch * q.dim * q.N * sizeof(float);
   a.pDb = (float*)w;
   hipError_t e;
-  if (q.N <= 4) e = bwd_modes<IO, 1, 4>(a, zoh, gate, stream);
+  // ZOH, N = 16, no document starts, aligned rows: the fast tiles go to the
+  // time-parallel kernel, the others to this file's exact instance
+  auto al16 = [](const void* ptr) { return ptr == nullptr || (uintptr_t)ptr % 16 == 0; };
+  const bool wave = zoh && q.N == 16 && !q.reset && q.dim % 16 == 0 && al16(q.u) && al16(q.delta) &&
+                    al16(q.z) && al16(q.dy) && al16(q.du) && al16(q.ddelta) && al16(q.dz) && al16(q.B) &&
+                    al16(q.C);
+  if (wave) {
+    a.split_fast = 1;
+    e = gate ? bwd_launch_rst<IO, 2, 8, true, true, false>(a, stream)
+             : bwd_launch_rst<IO, 2, 8, true, false, false>(a, stream);
+    if (e == hipSuccess) e = launch_scan_bwd_wave(a, sizeof(IO) == 2, gate, stream);
+  } else if (q.N <= 4) e = bwd_modes<IO, 1, 4>(a, zoh, gate, stream);
   else if (q.N <= 8) e = bwd_modes<IO, 2, 4>(a, zoh, gate, stream);
   else e = bwd_modes<IO, 2, 8>(a, zoh, gate, stream);
   if (e != hipSuccess) return e;
