@@ -308,6 +308,13 @@ __global__ __launch_bounds__(kNT, 3) void scan_bwd_wave_kernel(const BwdArgs p) 
       load4(at(dyp + cb, off), xy);
     }
   };
+  // Staging the backward's chunk also takes what its epilogue needs for the
+  // same (token, 4 channels) -- the thread that stages them finishes them --
+  // so that the raw inputs are read and the transcendentals taken once:
+  // softplus'(v), ds D, dy silu'(z) and dy silu'(z) D u; and it adds ds u
+  // into the sums for dD.
+  float ep_sg[4], ep_dsD[4], ep_dyg[4], ep_dyx[4];
+  float accD[4] = {0.0f, 0.0f, 0.0f, 0.0f}, accB[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   auto tile_store = [&](int64_t t0, auto bwd_tag) {
     constexpr bool BWD = decltype(bwd_tag)::value;
     const bool live = t0 + xt < Lb;
@@ -315,13 +322,39 @@ __global__ __launch_bounds__(kNT, 3) void scan_bwd_wave_kernel(const BwdArgs p) 
     for (int k = 0; k < 4; ++k) {
       const int cl = 4 * xh + k;
       const float v = elem(xr, k) + sm.cst[1][cl];
-      const float dl = live ? (p.softplus ? softplus_f(v) : v) : 0.0f;
       const float xv = live ? elem(xu, k) : 0.0f;
-      sm.io.in.xd[cl][xt] = make_float2(xv, dl);
-      if constexpr (BWD) {
-        float d = live ? elem(xy, k) : 0.0f;
-        if constexpr (GATE) d *= silu_f(elem(xz, k));
+      if constexpr (!BWD) {
+        const float dl = live ? (p.softplus ? softplus_f(v) : v) : 0.0f;
+        sm.io.in.xd[cl][xt] = make_float2(xv, dl);
+      } else {
+        // softplus(v) = max(v, 0) + log(1 + e^-|v|) (as softplus_f) and its
+        // derivative sigma(v) = (v >= 0 ? 1 : e^-|v|) / (1 + e^-|v|), from
+        // one exponential
+        float dl = v, sgv = 1.0f;
+        if (p.softplus) {
+          const float e = exp2_hw(-fabsf(v) * kLog2e);
+          const float wv = 1.0f + e;
+          const float r = (wv - 1.0f) - e;
+          dl = fmaf(log2_hw(wv), kLn2, fmaxf(v, 0.0f) - r);
+          sgv = (v >= 0.0f ? 1.0f : e) * rcp_hw(wv);
+        }
+        sm.io.in.xd[cl][xt] = make_float2(xv, live ? dl : 0.0f);
+        const float dyv = live ? elem(xy, k) : 0.0f;
+        float gz = 1.0f, dg = 0.0f;
+        if constexpr (GATE) {
+          const float zv = elem(xz, k);
+          const float sz = rcp_hw(1.0f + exp2_hw(-zv * kLog2e));  // sigma(z)
+          gz = zv * sz;                                          // silu(z)
+          dg = sz * fmaf(zv, 1.0f - sz, 1.0f);                   // silu'(z)
+        }
+        const float d = dyv * gz;
+        const float dskip = sm.cst[0][cl];
         sm.ds[cl][xt] = d;
+        ep_sg[k] = live ? sgv : 0.0f;  // padding: no step size
+        ep_dsD[k] = d * dskip;
+        ep_dyg[k] = dyv * dg;
+        ep_dyx[k] = ep_dyg[k] * dskip * xv;
+        accD[k] = fmaf(d, xv, accD[k]);
       }
     }
   };
@@ -432,7 +465,6 @@ __global__ __launch_bounds__(kNT, 3) void scan_bwd_wave_kernel(const BwdArgs p) 
 
   // ---- the chunks backwards
   sm.dacc[ch][sl] = 0.0f;  // thread (ch, n); first read after the first chunk's barrier
-  float accD[4] = {0.0f, 0.0f, 0.0f, 0.0f}, accB[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   const bool want_s = GATE && p.want_dz;
   const int row = lane >> 4;  // the channel's row in the wave
   float hck = 0.0f;           // this thread's (channel, state) checkpoint, a chunk ahead
@@ -604,43 +636,22 @@ __global__ __launch_bounds__(kNT, 3) void scan_bwd_wave_kernel(const BwdArgs p) 
     if (want_s) *(float4*)&sm.io.out.sv[ch][kTPL * sl] = make_float4(svs[0], svs[1], svs[2], svs[3]);
     lds_barrier();
 
-    // epilogue per (token, 4 channels): d(raw delta), du, dz from the raw
-    // inputs (read again; the same lines were read a chunk ago), and the sums
-    // for dD and d bias
+    // epilogue per (token, 4 channels): d(raw delta), du, dz = dy silu'(z)
+    // (C.h + D u), and the sums for d bias
     {
       const int64_t t = t0 + xt;
       if (t < L) {
-        const bool live = t < Lb;
         const int64_t cb = (row0 + t0) * dim + c0;
         const uint32_t off = xoff(t0);
-        uint32_t ru[XW], rr[XW], rz[XW], ry[XW];
-        load4(at(u + cb, off), ru);
-        load4(at(dr + cb, off), rr);
-        if constexpr (GATE) load4(at(zz + cb, off), rz);
-        load4(at(dyp + cb, off), ry);
         float o_dt[4], o_du[4], o_dz[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           const int cl = 4 * xh + k;
-          const float dskip = sm.cst[0][cl];
-          const float xv = live ? elem(ru, k) : 0.0f;
-          const float v = elem(rr, k) + sm.cst[1][cl];
-          const float sgv = p.softplus ? rcp_hw(1.0f + exp2_hw(-v * kLog2e)) : 1.0f;  // softplus'
-          const float dyv = live ? elem(ry, k) : 0.0f;
-          float gz = 1.0f, dg = 0.0f;
-          if constexpr (GATE) {
-            const float zv = elem(rz, k);
-            const float sg = rcp_hw(1.0f + exp2_hw(-zv * kLog2e));  // sigma(z)
-            gz = zv * sg;                                          // silu(z)
-            dg = sg * fmaf(zv, 1.0f - sg, 1.0f);                   // silu'(z)
-          }
-          const float dsk = dyv * gz;
-          const float dv = live ? sm.io.out.ddt[cl][xt] * sgv : 0.0f;
+          const float dv = sm.io.out.ddt[cl][xt] * ep_sg[k];
           o_dt[k] = dv;
-          o_du[k] = fmaf(dsk, dskip, sm.io.out.dx[cl][xt]);
-          o_dz[k] = want_s ? dyv * fmaf(dskip, xv, sm.io.out.sv[cl][xt]) * dg : 0.0f;
+          o_du[k] = sm.io.out.dx[cl][xt] + ep_dsD[k];
+          o_dz[k] = want_s ? fmaf(ep_dyg[k], sm.io.out.sv[cl][xt], ep_dyx[k]) : 0.0f;
           accB[k] += dv;
-          accD[k] = fmaf(dsk, xv, accD[k]);
         }
         store4((IO*)at((const IO*)p.ddelta + cb, off), o_dt);
         store4((IO*)at((const IO*)p.du + cb, off), o_du);
