@@ -568,19 +568,35 @@ __global__ __launch_bounds__((BShape<G, NG>::THREADS)) void scan_bwd_kernel(cons
 }
 
 // dB, dC: add the channel tiles' partials in tile order, round to the io dtype.
-template <typename IO>
+// A thread takes four consecutive elements (16-byte reads; n is a multiple of
+// 4 when every row of B holds a multiple of 4 states, else one element).
+template <typename IO, int V>
 __global__ __launch_bounds__(256) void bwd_finalize_bc(const float* __restrict__ pbc,
                                                        IO* __restrict__ dB, IO* __restrict__ dC,
                                                        const int64_t ntiles, const int64_t n) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * V;
   if (i >= n) return;
-  float sb = 0.0f, sc = 0.0f;
+  float sb[V], sc[V];
+#pragma unroll
+  for (int k = 0; k < V; ++k) sb[k] = sc[k] = 0.0f;
+#pragma unroll 4
   for (int64_t tl = 0; tl < ntiles; ++tl) {
-    sb += pbc[(tl * 2 + 0) * n + i];
-    sc += pbc[(tl * 2 + 1) * n + i];
+    const float* pb = pbc + (tl * 2) * n + i;
+    const float* pc = pb + n;
+    if constexpr (V == 4) {
+      const float4 b4 = *(const float4*)pb, c4 = *(const float4*)pc;
+      sb[0] += b4.x; sb[1] += b4.y; sb[2] += b4.z; sb[3] += b4.w;
+      sc[0] += c4.x; sc[1] += c4.y; sc[2] += c4.z; sc[3] += c4.w;
+    } else {
+      sb[0] += pb[0];
+      sc[0] += pc[0];
+    }
   }
-  store_io(dB + i, sb);
-  store_io(dC + i, sc);
+#pragma unroll
+  for (int k = 0; k < V; ++k) {
+    store_io(dB + i + k, sb[k]);
+    store_io(dC + i + k, sc[k]);
+  }
 }
 
 // dA (dim * N), dD and d bias (dim): add the batch entries' partials in order.
@@ -679,8 +695,14 @@ hipError_t bwd_io(const ScanBwdParams& q, bool zoh, bool gate, hipStream_t strea
   if (e != hipSuccess) return e;
   const int64_t nbc = q.batch * q.L * q.N;
   if (nbc > 0) {
-    hipLaunchKernelGGL((bwd_finalize_bc<IO>), dim3((unsigned)((nbc + 255) / 256)), dim3(256), 0,
-                       stream, a.pbc, (IO*)q.dB, (IO*)q.dC, a.ntiles, nbc);
+    // the partials are 256-byte aligned sections; 4 elements per thread
+    // where n (and so each section's offset in elements) is a multiple of 4
+    if (nbc % 4 == 0)
+      hipLaunchKernelGGL((bwd_finalize_bc<IO, 4>), dim3((unsigned)((nbc / 4 + 255) / 256)), dim3(256), 0,
+                         stream, a.pbc, (IO*)q.dB, (IO*)q.dC, a.ntiles, nbc);
+    else
+      hipLaunchKernelGGL((bwd_finalize_bc<IO, 1>), dim3((unsigned)((nbc + 255) / 256)), dim3(256), 0,
+                         stream, a.pbc, (IO*)q.dB, (IO*)q.dC, a.ntiles, nbc);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
