@@ -831,10 +831,9 @@ __global__ __launch_bounds__(WaveShape<CPW>::NT, WaveShape<CPW>::WPS) void scan_
       else
         pair_scan4_b_rows(ta, tb);
       if constexpr (S::WPS == 4) read_c();
-      float he[4];
+      float he[4], hck[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const int n = 4 * q + k;
         he[k] = tb[k];  // after the lane's last token
         // the state before the lane's first token: the previous lane's he; the
         // segment's first lane (no source lane) keeps the carry
@@ -846,7 +845,18 @@ __global__ __launch_bounds__(WaveShape<CPW>::NT, WaveShape<CPW>::WPS) void scan_
           const float h = (i == kWT - 1) ? he[k] : fmaf(pa[i][k], hin, pb[i][k]);
           acc[i] = fmaf(ZOH ? cv[i][k] * w1v[k] : cv[i][k], h, acc[i]);  // Euler reads out h itself
         }
-        if (CKPT && wck && (NF || n < N)) ckp[n] = ZOH ? hin * w1v[k] : hin;  // g / A where g is carried
+        hck[k] = ZOH ? hin * w1v[k] : hin;  // g / A where g is carried
+      }
+      // the checkpoint: one 16-byte store of the group's four states (the
+      // 16-state path's rows are 64-byte aligned), else state by state
+      if (CKPT && wck) {
+        if constexpr (NF) {
+          *(float4*)(ckp + 4 * q) = make_float4(hck[0], hck[1], hck[2], hck[3]);
+        } else {
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            if (4 * q + k < N) ckp[4 * q + k] = hck[k];
+        }
       }
       // the segment's last lane holds the state after the chunk: the next carry
       if (sl == LPC - 1) sm.kq[ch][q][0][2] = make_float4(he[0], he[1], he[2], he[3]);
@@ -894,8 +904,10 @@ hipError_t wave_launch(const ScanParams& p, hipStream_t stream) {
   // 32-bit offsets: lanes' element offsets, and the staging's byte offsets
   // within a chunk of TCK tokens
   if (nblk > 0x7fffffff || S::TCK * p.dim * (int64_t)sizeof(IO) >= 0xffffffffLL) return hipErrorInvalidValue;
-  // the 16-state path reads B and C rows as 16-byte vectors
-  const bool vec = p.N == kNMax && (uintptr_t)p.B % 16 == 0 && (uintptr_t)p.C % 16 == 0;
+  // the 16-state path reads B and C rows and writes checkpoint rows as
+  // 16-byte vectors
+  const bool vec = p.N == kNMax && (uintptr_t)p.B % 16 == 0 && (uintptr_t)p.C % 16 == 0 &&
+                   (uintptr_t)p.ckpt % 16 == 0;
   auto kern = vec ? (p.ckpt ? scan_wave_kernel<IO, ZOH, GATE, true, true, CPW>
                             : scan_wave_kernel<IO, ZOH, GATE, true, false, CPW>)
                   : (p.ckpt ? scan_wave_kernel<IO, ZOH, GATE, false, true, CPW>
