@@ -29,6 +29,7 @@ one input set and prints no JSON:
     python bench.py --only conv [--launches 3]
     python bench.py --only ssd [--launches 3]
     python bench.py --only bwd [--dt-mode zoh|euler] [--launches 3]   # the backward, Mamba-130M layer
+    python bench.py --only train [--launches 3]  # the forward keeping checkpoints, then the backward from them
     python bench.py --only tpar [--launches 3]   # the time-parallel scan with four waves per row, forced, Mamba-130M layer at batch 1
     python bench.py --only seq [--launches 3]    # the sequential scan (2 states per lane), forced, Mamba-130M layer
     python bench.py --only copy     # a plain 256 MiB device copy, for counter calibration
@@ -802,6 +803,22 @@ def profile_only(what, launches, dt_mode, kernel=None):
         for _ in range(launches):
             ssm.scan_bwd(s["u"], s["delta"], s["A"], s["B"], s["C"], dy, D=s["D"], z=s["z"],
                          delta_bias=s["delta_bias"], dt_mode=dt_mode, workspace=ws)
+    elif what == "train":
+        # the training path: the forward that keeps the state every 16 tokens,
+        # then the backward from those checkpoints
+        cfg = W.SCAN_CONFIGS["mamba130m"]
+        s = upload_scan(W.scan_inputs(cfg), dev)
+        ws = torch.empty(ssm.scan_bwd_workspace_size(cfg.batch, cfg.L, cfg.dim, cfg.N),
+                         dtype=torch.uint8, device=dev)
+        gen = torch.Generator(device="cpu").manual_seed(13)
+        dy = torch.randn((cfg.batch, cfg.L, cfg.dim), generator=gen).to(torch.bfloat16).to(dev)
+        y, last, ck = ssm.scan_fwd_train(s["u"], s["delta"], s["A"], s["B"], s["C"], D=s["D"], z=s["z"],
+                                         delta_bias=s["delta_bias"], dt_mode=dt_mode)
+        for _ in range(launches):
+            ssm.scan_fwd_train(s["u"], s["delta"], s["A"], s["B"], s["C"], D=s["D"], z=s["z"],
+                               delta_bias=s["delta_bias"], dt_mode=dt_mode, y=y, last_state=last, ckpt=ck)
+            ssm.scan_bwd(s["u"], s["delta"], s["A"], s["B"], s["C"], dy, D=s["D"], z=s["z"],
+                         delta_bias=s["delta_bias"], dt_mode=dt_mode, workspace=ws, ckpt=ck)
     elif what in ("tpar", "seq"):
         # the time-parallel kernel with four waves per row on the Mamba-130M
         # layer at batch 1, or the sequential kernel (2 states per lane) on the
@@ -853,7 +870,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--decode-steps", type=int, default=1000)
-    ap.add_argument("--only", choices=["scan", "seq", "bwd", "tpar", "decode", "conv", "conv_bwd",
+    ap.add_argument("--only", choices=["scan", "seq", "bwd", "train", "tpar", "decode", "conv", "conv_bwd",
                                        "ssd", "copy"],
                     default=None,
                     help="profiling mode: a few launches of one kernel, no JSON")
@@ -1039,6 +1056,8 @@ def main():
                     "alu": alu_figures(x_updates, x_kern, "zoh", rates)},
         "bwd": {"workload": "ssm_scan_bwd on the same layer, ZOH, gate, D, bias: du, d delta, dz, "
                             "dA, dB, dC, dD, d bias (states recomputed from the inputs)",
+                "kernels": "scan_bwd_wave_kernel (time-parallel, rows of 16 lanes; every tile here has "
+                           "|A| >= 1/2), then the dB/dC and dA/dD/dbias finalize kernels",
                 "ms": round(b_ms, 4), "x_forward": round(b_ms / kern_ms, 2),
                 "updates_per_s": float(f"{elems * cfg.N / (b_ms * 1e-3):.4g}"),
                 "workspace_MB": round(b_ws / 1e6, 1),
