@@ -143,6 +143,7 @@ KERNEL_SOURCES = {
     "conv1d_fwd_conv130m": ["conv1d.hip"],
     "ssd_fwd_ssd130m": ["ssd.hip"],
     "conv1d_bwd_conv130m": ["conv1d.hip"],
+    "scan_bwd_mamba130m_zoh": ["scan_bwd.hip", "scan_bwd_wave.hip", "ssm_bwd.h"],
 }
 COMMON_SOURCES = ["ssm_device.h", "ssm_launch.h", "ssm_api.hip"]
 
@@ -1059,6 +1060,7 @@ def main():
                 "kernels": "scan_bwd_wave_kernel (time-parallel, rows of 16 lanes; every tile here has "
                            "|A| >= 1/2), then the dB/dC and dA/dD/dbias finalize kernels",
                 "ms": round(b_ms, 4), "x_forward": round(b_ms / kern_ms, 2),
+                "traffic": measured_traffic("scan_bwd_mamba130m_zoh"),
                 "updates_per_s": float(f"{elems * cfg.N / (b_ms * 1e-3):.4g}"),
                 "workspace_MB": round(b_ws / 1e6, 1),
                 "training": {"workload": "ssm_scan_fwd_ckpt (keeps the state every 16 tokens) then "
