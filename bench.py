@@ -138,7 +138,7 @@ def alu_figures(updates, ms, mode, rates):
 # The sources each measured kernel is built from: its own file, plus the shared
 # device and launch headers and the C-ABI file that picks its launch shape.
 KERNEL_SOURCES = {
-    "scan_fwd_mamba130m_zoh": ["scan_fwd.hip", "scan_tpar.hip"],
+    "scan_fwd_mamba130m_zoh": ["scan_fwd.hip", "scan_tpar.hip", "scan_wave8.hip", "ssm_wave8.h"],
     "step_decode_zoh": ["step.hip"],
     "conv1d_fwd_conv130m": ["conv1d.hip"],
     "ssd_fwd_ssd130m": ["ssd.hip"],

@@ -9,7 +9,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libssm66_hip.so")
-SOURCES = ["ssm_api.hip", "scan_fwd.hip", "scan_tpar.hip", "scan_bwd.hip", "scan_bwd_wave.hip", "step.hip", "conv1d.hip", "ssd.hip",
+SOURCES = ["ssm_api.hip", "scan_fwd.hip", "scan_tpar.hip", "scan_wave8.hip", "scan_bwd.hip", "scan_bwd_wave.hip", "step.hip", "conv1d.hip", "ssd.hip",
            "probe.hip"]
 
 HIPCC_FLAGS = [

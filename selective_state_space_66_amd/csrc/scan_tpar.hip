@@ -34,6 +34,7 @@
 
 #include "ssm_device.h"
 #include "ssm_launch.h"
+#include "ssm_wave8.h"
 
 namespace ssm66 {
 
@@ -964,6 +965,8 @@ hipError_t launch_scan_tpar(const ScanParams& p, int io_dtype, bool zoh, bool ga
 hipError_t launch_scan_wave(const ScanParams& p, int io_dtype, bool zoh, bool gate,
                             int channels_per_wave, hipStream_t stream) {
   if (p.N < 1 || p.N > kNMax) return hipErrorInvalidValue;
+  // the common case of the 16-lane layout: eight tokens per lane (scan_wave8.hip)
+  if (channels_per_wave == 4 && scan_wave8_fits(p, io_dtype)) return launch_scan_wave8(p, zoh, gate, stream);
   if (channels_per_wave == 4)
     return io_dtype == 1 ? wave_io<bf16_bits, 4>(p, zoh, gate, stream) : wave_io<float, 4>(p, zoh, gate, stream);
   if (channels_per_wave != 1) return hipErrorInvalidValue;
