@@ -182,6 +182,18 @@ def to_dev(x, io, dev):
     return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(dev)
 
 
+def launched_scan_kernel(name, io):
+    """The one kernel a forward call without lengths, document starts or
+    checkpoints runs, from the library's name for its layout and the call's io
+    type: the 16-lane layout takes eight tokens per lane for bf16 io, four
+    otherwise."""
+    if name.startswith("scan_wave8_kernel / scan_wave_kernel"):
+        tpl = 8 if io == "bf16" else 4
+        return (f"{'scan_wave8_kernel' if tpl == 8 else 'scan_wave_kernel'} "
+                f"(time-parallel, 16 lanes per row, {tpl} tokens per lane)")
+    return name
+
+
 def upload_scan(inp, dev):
     io = inp["io"]
     return dict(u=to_dev(inp["u"], io, dev), delta=to_dev(inp["delta"], io, dev),
@@ -281,7 +293,7 @@ def time_narrow(dev, steps, warmup, rates=None):
             res[label] = time_scan(sets, steps, warmup, "zoh", kernel=kern)[1]
         upd = b * L * D * 16
         out[name] = {"workload": f"ssm_scan_fwd: batch {b}, L {L}, D {D}, N 16, bf16, gate, ZOH",
-                     "kernel": ssm.scan_kernel_name(b, L, D, 16),
+                     "kernel": launched_scan_kernel(ssm.scan_kernel_name(b, L, D, 16), "bf16"),
                      "kernel_ms": round(res["auto"], 5),
                      "sequential_kernel_ms": round(res["sequential"], 5),
                      "speedup": round(res["sequential"] / res["auto"], 2),
@@ -314,7 +326,8 @@ def time_layers(dev, steps, warmup, rates=None):
         gbs = nbytes / (kern * 1e-3) / 1e9
         out[name] = {"workload": f"ssm_scan_fwd: batch {cfg.batch}, L {cfg.L}, D {cfg.dim}, N {cfg.N}, "
                                  f"bf16, {'gate' if cfg.gate else 'no gate'}, ZOH",
-                     "kernel": ssm.scan_kernel_name(cfg.batch, cfg.L, cfg.dim, cfg.N),
+                     "kernel": launched_scan_kernel(ssm.scan_kernel_name(cfg.batch, cfg.L, cfg.dim, cfg.N),
+                                                    cfg.io),
                      "launches": nsteps, "kernel_ms": round(kern, 5),
                      "kernel_ms_median": round(kmed, 5), "kernel_ms_min": round(kmin, 5),
                      "GB/s": round(gbs, 2),
@@ -344,7 +357,7 @@ def time_tiny(dev, steps=200):
     s = upload_scan(inp, dev)
     out = {"workload": "ssm_scan_fwd: batch 1, L 256, D 64, N 16, fp32 io, no gate, D skip, "
                        "softplus(delta + bias)",
-           "kernel": ssm.scan_kernel_name(cfg.batch, cfg.L, cfg.dim, cfg.N)}
+           "kernel": launched_scan_kernel(ssm.scan_kernel_name(cfg.batch, cfg.L, cfg.dim, cfg.N), cfg.io)}
     for mode in ("zoh", "euler"):
         out[mode] = {"kernel_us": round(time_scan([s], steps, 20, mode)[1] * 1e3, 2)}
     return out
@@ -878,7 +891,7 @@ def main():
     ap.add_argument("--launches", type=int, default=3)
     ap.add_argument("--dt-mode", choices=["zoh", "euler"], default="zoh")
     ap.add_argument("--kernel", default=None,
-                    help="profiling mode, scan: force one scan kernel (seq1, seq2, seq4, tpar, wave, wave8)")
+                    help="profiling mode, scan: force one scan kernel (seq1, seq2, seq4, tpar, wave, wave4)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -906,7 +919,7 @@ def main():
     nbytes = scan_bytes(cfg.batch, cfg.L, cfg.dim, cfg.N, 2, cfg.gate)
     elems = cfg.batch * cfg.L * cfg.dim
 
-    scan_kernel = ssm.scan_kernel_name(cfg.batch, cfg.L, cfg.dim, cfg.N)
+    scan_kernel = launched_scan_kernel(ssm.scan_kernel_name(cfg.batch, cfg.L, cfg.dim, cfg.N), cfg.io)
     settle = settle_clock(sets)
     log(f"[bench] {settle} untimed launches while the clock settles")
     rates = alu_rates(dev)
@@ -1034,7 +1047,7 @@ def main():
                                    "(packed fp32 off in this build)",
                      "published_fp32_peak": FP32_PUBLISHED_TFLOPS,
                      "frac_published_fp32": round(tflops / FP32_PUBLISHED_TFLOPS, 4),
-                     "kernel": scan_kernel + " (ZOH, bf16, gate)",
+                     "kernel": scan_kernel, "instance": "ZOH, bf16 io, gate",
                      "kernel_ms": round(kern_ms, 5), "kernel_ms_median": round(kern_med, 5),
                      "kernel_ms_min": round(kern_min, 5),
                      "per_launch": {"updates": updates, "flops": FLOPS_PER_UPDATE * updates,

@@ -45,11 +45,14 @@ int check_common(int64_t batch, int64_t len, int64_t dim, int64_t dstate, int io
 //   wave per row at 1 x 8192 x 256; slower from 1024 rows: 52 against 39 us
 //   at 1 x 2048 x 1024);
 // - 12288 rows or more (three waves per SIMD with four rows per wave) and at
-//   least 128 tokens: the time-parallel kernel with 16 lanes per row (161
-//   against 167 us for one wave per row at 8 x 2048 x 1536; 391 against 448,
-//   and 425 for the sequential kernel, at 8 x 2048 x 4096; 760 against 821
-//   for the sequential kernel at 16 x 2048 x 4096; 17 against 22 us for the
-//   sequential kernel at 8 x 128 x 1536, even at 8 x 64 x 1536);
+//   least 128 tokens: the time-parallel kernel with 16 lanes per row, eight
+//   tokens per lane with bf16 io and no lengths, starts or checkpoints, four
+//   otherwise (with four: 161 against 167 us for one wave per row at
+//   8 x 2048 x 1536; 391 against 448, and 425 for the sequential kernel, at
+//   8 x 2048 x 4096; 760 against 821 for the sequential kernel at
+//   16 x 2048 x 4096; 17 against 22 us for the sequential kernel at
+//   8 x 128 x 1536, even at 8 x 64 x 1536; with eight: 146.5 and 357 us at
+//   8 x 2048 x 1536 and 8 x 2048 x 4096);
 // - between 1024 and 12288 rows and at least 256 tokens: the time-parallel
 //   kernel with one wave per row (146 against 160 us for 16 lanes per row at
 //   2 x 2048 x 5120; 3.5 against 6.9 ms for the sequential kernel at
@@ -244,7 +247,9 @@ const char* ssm_scan_kernel_name(int64_t batch, int64_t seqlen, int64_t dim, int
   switch (pick_scan_kernel(batch, dim, seqlen, dstate)) {
     case ScanKernel::kTpar: return "scan_tpar_kernel (time-parallel, four waves per row)";
     case ScanKernel::kWave: return "scan_wave_kernel (time-parallel, one wave per row)";
-    case ScanKernel::kWave4: return "scan_wave_kernel (time-parallel, 16 lanes per row)";
+    case ScanKernel::kWave4:
+      return "scan_wave8_kernel / scan_wave_kernel (time-parallel, 16 lanes per row; 8 tokens per lane for bf16 "
+             "io without lengths, starts or checkpoints, else 4)";
     default: break;
   }
   int G, NG;
