@@ -13,10 +13,13 @@
 // four: the four DPP levels of the row scan and the state entering each lane
 // are paid once per eight tokens, and a chunk is 128 tokens.  The states are
 // taken four at a time (a rolled loop over the four state groups: one group's
-// 8 x 4 pairs live, three waves per SIMD).  Per group: each lane composes its tokens' (abar, bbar u)
-// pairs into prefixes, the row scans the 16 lane totals (the chunk's carry
-// entering at the first lane), and each lane recovers the state after each of
-// its tokens and adds C.h into the token's output.
+// 8 x 4 pairs live, three waves per SIMD).  Per group: each lane composes its
+// tokens' (abar, bbar u) pairs into its total (the b part token by token, the
+// a part as one exponential of the lane's summed step, since the abar of one
+// state are exponentials of the same A), the row scans the 16 lane totals (the
+// chunk's carry entering at the first lane), and each lane walks its tokens
+// again from the state before its first one, adding C.h into each token's
+// output.
 //
 // This kernel takes the common case of the Mamba layers: bf16 io, N = 16, no
 // lengths, document starts or checkpoints, a width that is a multiple of 16
@@ -238,6 +241,11 @@ __global__ __launch_bounds__(kNT8, 3) void scan_wave8_kernel(
     }
 #pragma unroll
     for (int i = 0; i < kTPL8; ++i) acc[i] = 0.0f;
+    // the lane's summed step: exp2(A log2(e) * dsum) is the product of its
+    // eight abar, for every state
+    float dsum = dl[0];
+#pragma unroll
+    for (int i = 1; i < kTPL8; ++i) dsum += dl[i];
 
     // one group of four states at a time (a rolled loop)
     auto groups = [&](auto form_tag) {
@@ -269,20 +277,20 @@ __global__ __launch_bounds__(kNT8, 3) void scan_wave8_kernel(
             pb[i][k] = bu;
           }
         }
-        // in-lane prefix: token i's pair becomes the composition of tokens 0..i
+        // the lane's total pair: the b part composed token by token from a
+        // zero state, the a part as one exponential of the summed step
+        float ta[4], tb[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) tb[k] = pb[0][k];
 #pragma unroll
         for (int i = 1; i < kTPL8; ++i) {
 #pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            pb[i][k] = fmaf(pa[i][k], pb[i - 1][k], pb[i][k]);
-            pa[i][k] *= pa[i - 1][k];
-          }
+          for (int k = 0; k < 4; ++k) tb[k] = fmaf(pa[i][k], tb[k], pb[i][k]);
         }
-        float ta[4], tb[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          ta[k] = pa[kTPL8 - 1][k];
-          tb[k] = fmaf(ta[k], cinv[k], pb[kTPL8 - 1][k]);  // first lane: the carry enters
+          ta[k] = exp2_hw(dsum * a2v[k]);
+          tb[k] = fmaf(ta[k], cinv[k], tb[k]);  // first lane: the carry enters
         }
         row_scan4(ta, tb);
         float hin[4];
@@ -292,14 +300,15 @@ __global__ __launch_bounds__(kNT8, 3) void scan_wave8_kernel(
           // total; the row's first lane (no source lane) keeps the carry
           hin[k] = __int_as_float(__builtin_amdgcn_update_dpp(
               __float_as_int(cinv[k]), __float_as_int(tb[k]), 0x111 /* row_shr:1 */, 0xf, 0xf, false));
+        // the states after each token, from the state before the lane's first
 #pragma unroll
         for (int i = 0; i < kTPL8; ++i) {
           const float4 cv4 = sm.c[q][i * kROW8 + sl];
           const float cv[4] = {cv4.x, cv4.y, cv4.z, cv4.w};
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
-            const float h = (i == kTPL8 - 1) ? tb[k] : fmaf(pa[i][k], hin[k], pb[i][k]);
-            acc[i] = fmaf(ZOH ? cv[k] * w1v[k] : cv[k], h, acc[i]);  // Euler reads out h itself
+            hin[k] = (i == kTPL8 - 1) ? tb[k] : fmaf(pa[i][k], hin[k], pb[i][k]);
+            acc[i] = fmaf(ZOH ? cv[k] * w1v[k] : cv[k], hin[k], acc[i]);  // Euler reads out h itself
           }
         }
         // the row's last lane holds the state after the chunk: the next carry
