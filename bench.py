@@ -183,10 +183,9 @@ def to_dev(x, io, dev):
 
 
 def launched_scan_kernel(name, io):
-    """The one kernel a forward call without lengths, document starts or
-    checkpoints runs, from the library's name for its layout and the call's io
-    type: the 16-lane layout takes eight tokens per lane for bf16 io, four
-    otherwise."""
+    """The one kernel a forward call without lengths or document starts runs,
+    from the library's name for its layout and the call's io type: the 16-lane
+    layout takes eight tokens per lane for bf16 io, four otherwise."""
     if name.startswith("scan_wave8_kernel / scan_wave_kernel"):
         tpl = 8 if io == "bf16" else 4
         return (f"{'scan_wave8_kernel' if tpl == 8 else 'scan_wave_kernel'} "

@@ -22,9 +22,13 @@
 // output.
 //
 // This kernel takes the common case of the Mamba layers: bf16 io, N = 16, no
-// lengths, document starts or checkpoints, a width that is a multiple of 16
-// and 16-byte aligned rows; scan_tpar.hip's kernel takes the rest.  Its
-// per-state forms are that kernel's: exponential-Euler bbar u = Delta u B;
+// lengths or document starts, a width that is a multiple of 16 and 16-byte
+// aligned rows; scan_tpar.hip's kernel takes the rest.  CKPT (the training
+// forward): the lanes whose first token is a multiple of 16 (the even lanes of
+// a row) also write the state before it, in h units, as the backward reads it:
+// ckpt[((b * ceil(L / 16) + t / 16) * dim + c) * 16 + n].
+//
+// The per-state forms are scan_tpar.hip's: exponential-Euler bbar u = Delta u B;
 // ZOH on g = A h where |A| >= 1/2 (bbar u = (abar - 1) u B in g units, read
 // out with weight 1/A), else bbar = Delta B phi(Delta A).
 //
@@ -107,12 +111,12 @@ __device__ __forceinline__ void row_scan4(float (&a)[4], float (&b)[4]) {
 
 // Arguments as scan_tpar.hip's wave kernel (bf16 io, N = 16, dim a multiple of
 // 16, the row tensors and B, C 16-byte aligned); ntiles = dim / 16.
-template <bool ZOH, bool GATE>
+template <bool ZOH, bool GATE, bool CKPT>
 __global__ __launch_bounds__(kNT8, 3) void scan_wave8_kernel(
     const bf16_bits* __restrict__ u, const bf16_bits* __restrict__ dr, const float* __restrict__ Am,
     const bf16_bits* __restrict__ Bm, const bf16_bits* __restrict__ Cm, const float* __restrict__ Dm,
     const bf16_bits* __restrict__ zz, const float* __restrict__ bias_v, const float* h0,
-    bf16_bits* __restrict__ y, float* last_state, const int64_t L, const int64_t dim,
+    bf16_bits* __restrict__ y, float* last_state, float* __restrict__ ckpt, const int64_t L, const int64_t dim,
     const int64_t ntiles, const int softplus) {
   __shared__ Wave8Smem sm;
 
@@ -233,6 +237,11 @@ __global__ __launch_bounds__(kNT8, 3) void scan_wave8_kernel(
     }
     lds_barrier();
 
+    // the lane's first token starts a 16-token checkpoint group (CKPT)
+    const int64_t tl = t0 + kTPL8 * sl;
+    const bool wck = CKPT && (sl % 2 == 0) && tl < L;
+    float* ckp = CKPT ? ckpt + ((b * ((L + 15) / 16) + (wck ? tl / 16 : 0)) * dim + c0 + ch) * kN8 : nullptr;
+
     float x[kTPL8], dl[kTPL8], acc[kTPL8];
 #pragma unroll
     for (int j = 0; j < kTPL8 / 2; ++j) {
@@ -300,6 +309,10 @@ __global__ __launch_bounds__(kNT8, 3) void scan_wave8_kernel(
           // total; the row's first lane (no source lane) keeps the carry
           hin[k] = __int_as_float(__builtin_amdgcn_update_dpp(
               __float_as_int(cinv[k]), __float_as_int(tb[k]), 0x111 /* row_shr:1 */, 0xf, 0xf, false));
+        // the checkpoint: g / A where g is carried, one 16-byte store
+        if (CKPT && wck)
+          *(float4*)(ckp + 4 * q) = ZOH ? make_float4(hin[0] * w1v[0], hin[1] * w1v[1], hin[2] * w1v[2], hin[3] * w1v[3])
+                                        : make_float4(hin[0], hin[1], hin[2], hin[3]);
         // the states after each token, from the state before the lane's first
 #pragma unroll
         for (int i = 0; i < kTPL8; ++i) {
@@ -339,14 +352,14 @@ __global__ __launch_bounds__(kNT8, 3) void scan_wave8_kernel(
   }
 }
 
-template <bool ZOH, bool GATE>
+template <bool ZOH, bool GATE, bool CKPT>
 hipError_t wave8_launch(const ScanParams& p, hipStream_t stream) {
   const int64_t ntiles = p.dim / kCPB8;
   const int64_t nblk = ntiles * p.batch;
-  hipLaunchKernelGGL((scan_wave8_kernel<ZOH, GATE>), dim3((unsigned)nblk), dim3(kNT8), 0, stream,
+  hipLaunchKernelGGL((scan_wave8_kernel<ZOH, GATE, CKPT>), dim3((unsigned)nblk), dim3(kNT8), 0, stream,
                      (const bf16_bits*)p.u, (const bf16_bits*)p.delta, p.A, (const bf16_bits*)p.B,
                      (const bf16_bits*)p.C, p.D, (const bf16_bits*)p.z, p.delta_bias, p.h0, (bf16_bits*)p.y,
-                     p.last_state, p.L, p.dim, ntiles, p.softplus);
+                     p.last_state, p.ckpt, p.L, p.dim, ntiles, p.softplus);
   return hipGetLastError();
 }
 
@@ -354,14 +367,18 @@ hipError_t wave8_launch(const ScanParams& p, hipStream_t stream) {
 
 bool scan_wave8_fits(const ScanParams& p, int io_dtype) {
   auto al16 = [](const void* ptr) { return ptr == nullptr || (uintptr_t)ptr % 16 == 0; };
-  return io_dtype == 1 && p.N == kN8 && p.dim % kCPB8 == 0 && !p.seq_lens && !p.reset && !p.ckpt &&
+  return io_dtype == 1 && p.N == kN8 && p.dim % kCPB8 == 0 && !p.seq_lens && !p.reset && al16(p.ckpt) &&
          al16(p.u) && al16(p.delta) && al16(p.z) && al16(p.y) && al16(p.B) && al16(p.C) &&
          p.batch * (p.dim / kCPB8) <= 0x7fffffff && kTCK8 * p.dim * 2 < 0xffffffffLL;
 }
 
 hipError_t launch_scan_wave8(const ScanParams& p, bool zoh, bool gate, hipStream_t stream) {
-  if (zoh) return gate ? wave8_launch<true, true>(p, stream) : wave8_launch<true, false>(p, stream);
-  return gate ? wave8_launch<false, true>(p, stream) : wave8_launch<false, false>(p, stream);
+  if (p.ckpt) {
+    if (zoh) return gate ? wave8_launch<true, true, true>(p, stream) : wave8_launch<true, false, true>(p, stream);
+    return gate ? wave8_launch<false, true, true>(p, stream) : wave8_launch<false, false, true>(p, stream);
+  }
+  if (zoh) return gate ? wave8_launch<true, true, false>(p, stream) : wave8_launch<true, false, false>(p, stream);
+  return gate ? wave8_launch<false, true, false>(p, stream) : wave8_launch<false, false, false>(p, stream);
 }
 
 }  // namespace ssm66

@@ -46,7 +46,7 @@ int check_common(int64_t batch, int64_t len, int64_t dim, int64_t dstate, int io
 //   at 1 x 2048 x 1024);
 // - 12288 rows or more (three waves per SIMD with four rows per wave) and at
 //   least 128 tokens: the time-parallel kernel with 16 lanes per row, eight
-//   tokens per lane with bf16 io and no lengths, starts or checkpoints, four
+//   tokens per lane with bf16 io and no lengths or document starts, four
 //   otherwise (with four: 161 against 167 us for one wave per row at
 //   8 x 2048 x 1536; 391 against 448, and 425 for the sequential kernel, at
 //   8 x 2048 x 4096; 760 against 821 for the sequential kernel at
@@ -249,7 +249,7 @@ const char* ssm_scan_kernel_name(int64_t batch, int64_t seqlen, int64_t dim, int
     case ScanKernel::kWave: return "scan_wave_kernel (time-parallel, one wave per row)";
     case ScanKernel::kWave4:
       return "scan_wave8_kernel / scan_wave_kernel (time-parallel, 16 lanes per row; 8 tokens per lane for bf16 "
-             "io without lengths, starts or checkpoints, else 4)";
+             "io without lengths or document starts, else 4)";
     default: break;
   }
   int G, NG;

@@ -8,9 +8,9 @@
 
 namespace ssm66 {
 
-// bf16 io (io_dtype 1), N = 16, no lengths, document starts or checkpoints,
-// dim a multiple of 16, the row tensors and B, C 16-byte aligned, and a grid
-// and chunk offsets within 32 bits
+// bf16 io (io_dtype 1), N = 16, no lengths or document starts, dim a
+// multiple of 16, the row tensors, B, C and the checkpoints (if any) 16-byte
+// aligned, and a grid and chunk offsets within 32 bits
 bool scan_wave8_fits(const ScanParams& p, int io_dtype);
 
 // the scan of p (which scan_wave8_fits accepts) on stream

@@ -266,7 +266,7 @@ def test_scan_kernel_choice(lib):
     MI355X and the degenerate sizes."""
     name = ssm.scan_kernel_name
     sixteen = ("scan_wave8_kernel / scan_wave_kernel (time-parallel, 16 lanes per row; 8 tokens per lane for bf16 "
-               "io without lengths, starts or checkpoints, else 4)")
+               "io without lengths or document starts, else 4)")
     one = "scan_wave_kernel (time-parallel, one wave per row)"
     assert name(8, 2048, 1536, 16) == sixteen                          # Mamba-130M layer: 12288 rows
     assert name(8, 2048, 1535, 16) == one                              # 12280 rows
