@@ -126,6 +126,7 @@ __global__ __launch_bounds__(kNT8, 3) void scan_wave8_kernel(
   const int64_t logical = (nblk % 8 == 0) ? (bid % 8) * (nblk / 8) + bid / 8 : bid;
   const int64_t b = logical / ntiles, tile = logical - b * ntiles;
   const int tid = threadIdx.x, lane = tid & 63;
+  const int wave_id = __builtin_amdgcn_readfirstlane(tid >> 6);
   // the row's channel in the tile and the lane in the row; for per-(channel,
   // state) work the same thread stands for (channel ch, state sl)
   const int ch = tid >> 4, sl = tid & (kLPC8 - 1);
@@ -152,7 +153,6 @@ __global__ __launch_bounds__(kNT8, 3) void scan_wave8_kernel(
   }
   if (tid < kCPB8) sm.bias[tid] = bias_v ? bias_v[c0 + tid] : 0.0f;
   lds_barrier();  // the constants and the bias, before the first staging reads them
-  const float4* kp = &sm.kq[ch][0][sl == 0 ? 0 : 1][0];  // + 6 q: group q
 
   // ---- staging.  Addresses: a uniform base per chunk and a 32-bit byte
   // offset per thread (the launch keeps a chunk's rows within 32 bits).
@@ -237,10 +237,12 @@ __global__ __launch_bounds__(kNT8, 3) void scan_wave8_kernel(
     }
     lds_barrier();
 
-    // the lane's first token starts a 16-token checkpoint group (CKPT)
-    const int64_t tl = t0 + kTPL8 * sl;
-    const bool wck = CKPT && (sl % 2 == 0) && tl < L;
-    float* ckp = CKPT ? ckpt + ((b * ((L + 15) / 16) + (wck ? tl / 16 : 0)) * dim + c0 + ch) * kN8 : nullptr;
+    // the lane's first token starts a 16-token checkpoint group (CKPT): its
+    // row is the chunk's first (a uniform base) plus sl / 2 groups and the
+    // channel (a 32-bit offset)
+    const bool wck = CKPT && (sl % 2 == 0) && t0 + kTPL8 * sl < L;
+    float* ckb = CKPT ? ckpt + ((b * ((L + 15) / 16) + t0 / 16) * dim + c0) * kN8 : nullptr;
+    const uint32_t cko = ((uint32_t)(sl >> 1) * (uint32_t)dim + (uint32_t)ch) * kN8;
 
     float x[kTPL8], dl[kTPL8], acc[kTPL8];
 #pragma unroll
@@ -255,6 +257,14 @@ __global__ __launch_bounds__(kNT8, 3) void scan_wave8_kernel(
     float dsum = dl[0];
 #pragma unroll
     for (int i = 1; i < kTPL8; ++i) dsum += dl[i];
+
+    // this lane's constants slot (+ 6 q: group q), and its channel's carry
+    // slots: formed here from the wave's index and the lane's (mbcnt), not
+    // kept in registers through the staging
+    const int lid = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    const int chk = wave_id * 4 + (lid >> 4);
+    const float4* kp = &sm.kq[chk][0][(lid & 15) == 0 ? 0 : 1][0];
+    float4* kcarry = &sm.kq[chk][0][0][2];  // + 6 q: group q
 
     // one group of four states at a time (a rolled loop)
     auto groups = [&](auto form_tag) {
@@ -311,7 +321,7 @@ __global__ __launch_bounds__(kNT8, 3) void scan_wave8_kernel(
               __float_as_int(cinv[k]), __float_as_int(tb[k]), 0x111 /* row_shr:1 */, 0xf, 0xf, false));
         // the checkpoint: g / A where g is carried, one 16-byte store
         if (CKPT && wck)
-          *(float4*)(ckp + 4 * q) = ZOH ? make_float4(hin[0] * w1v[0], hin[1] * w1v[1], hin[2] * w1v[2], hin[3] * w1v[3])
+          *(float4*)(ckb + cko + 4 * q) = ZOH ? make_float4(hin[0] * w1v[0], hin[1] * w1v[1], hin[2] * w1v[2], hin[3] * w1v[3])
                                         : make_float4(hin[0], hin[1], hin[2], hin[3]);
         // the states after each token, from the state before the lane's first
 #pragma unroll
@@ -325,7 +335,7 @@ __global__ __launch_bounds__(kNT8, 3) void scan_wave8_kernel(
           }
         }
         // the row's last lane holds the state after the chunk: the next carry
-        if (sl == kLPC8 - 1) sm.kq[ch][q][0][2] = make_float4(tb[0], tb[1], tb[2], tb[3]);
+        if (sl == kLPC8 - 1) kcarry[6 * q] = make_float4(tb[0], tb[1], tb[2], tb[3]);
       }
     };
     if (!ZOH) groups(std::integral_constant<int, 0>());
@@ -343,12 +353,16 @@ __global__ __launch_bounds__(kNT8, 3) void scan_wave8_kernel(
     y_store(t0);
   }
 
-  // the carried value and its readout weight (1/A where g = A h is carried)
+  // the carried value and its readout weight (1/A where g = A h is carried).
+  // The thread index is formed again from the wave's index (a scalar) and the
+  // lane's, so that no address for this step is kept in registers (or
+  // scratch) across the chunk loop.
   if (last_state) {
-    const float g = ((const float*)&sm.kq[ch][sl >> 2][0][2])[sl & 3];
-    const float w1 = ((const float*)&sm.kq[ch][sl >> 2][0][1])[sl & 3];
-    const bool fast = ZOH && fabsf(Am[c0 * kN8 + tid]) >= 0.5f;
-    last_state[cs0 + tid] = fast ? g * w1 : g;
+    const int t = wave_id * 64 + (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    const float* kqs = (const float*)&sm.kq[t >> 4][(t & 15) >> 2][0][0] + (t & 3);
+    const float g = kqs[8], w1 = kqs[4];
+    const bool fast = ZOH && fabsf(Am[c0 * kN8 + t]) >= 0.5f;
+    last_state[cs0 + t] = fast ? g * w1 : g;
   }
 }
 
