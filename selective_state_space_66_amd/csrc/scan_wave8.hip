@@ -56,12 +56,13 @@ constexpr int kCPB8 = 16;          // channels per block (4 waves x 4 rows)
 constexpr int kNT8 = 256;          // threads per block
 // LDS padding (chosen with a bank model of these accesses): the B and C rows
 // of one token-in-lane hold 16 lanes in 17 float4 slots, and each state group
-// 4 more; the (channel, token) rows of u and Delta 2 more float2 slots; the
-// token rows of z and y 2 more bf16 (9 words a row: the lanes of a row, 8 tokens
-// apart, then reach 8 different banks; the rows are written and read in words).
+// 4 more; the (u, Delta) row of a channel holds the pairs of tokens 2p, 2p + 1
+// of lane l in float4 slot p * 17 + l, so the 16 lanes of a row read 64
+// consecutive words for each p; the token rows of z and
+// y 2 more bf16 (9 words a row: the lanes of a row, 8 tokens apart, then reach
+// 8 different banks; the rows are written and read in words).
 constexpr int kROW8 = kLPC8 + 1;
 constexpr int kQPAD8 = 4;
-constexpr int kXPAD8 = 2;
 constexpr int kZPAD8 = 2;
 
 struct Wave8Smem {
@@ -71,7 +72,7 @@ struct Wave8Smem {
   float4 kq[kCPB8][kN8 / 4][2][3];
   float4 b[kN8 / 4][kTPL8 * kROW8 + kQPAD8];  // [group][token in lane * kROW8 + lane]
   float4 c[kN8 / 4][kTPL8 * kROW8 + kQPAD8];
-  float2 xd[kCPB8][kTCK8 + kXPAD8];           // (u, Delta) per channel and token
+  float2 xd[kCPB8][kTPL8 * kROW8];            // (u, Delta): [channel][(pair * kROW8 + lane) * 2 + token & 1]
   uint16_t zt[kTCK8][kCPB8 + kZPAD8];         // z, raw bf16, per token and channel
   uint16_t yt[kTCK8][kCPB8 + kZPAD8];         // y, bf16, per token and channel
   float bias[kCPB8];                          // delta bias per channel
@@ -176,11 +177,12 @@ __global__ __launch_bounds__(kNT8, 3) void scan_wave8_kernel(
   // padding tokens (past L) take u = Delta = 0: their pair is the identity
   auto tile_store = [&](int64_t t0) {
     const bool live = t0 + xt < L;
+    const int xslot = (((xt & (kTPL8 - 1)) >> 1) * kROW8 + (xt >> 3)) * 2 + (xt & 1);
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const float v = bf(xr[k >> 1], k & 1) + sm.bias[8 * xh + k];
       const float dl = softplus ? softplus_f(v) : v;
-      sm.xd[8 * xh + k][xt] = live ? make_float2(bf(xu[k >> 1], k & 1), dl) : make_float2(0.0f, 0.0f);
+      sm.xd[8 * xh + k][xslot] = live ? make_float2(bf(xu[k >> 1], k & 1), dl) : make_float2(0.0f, 0.0f);
     }
     if constexpr (GATE) {
       uint32_t* zw = (uint32_t*)&sm.zt[xt][8 * xh];
@@ -247,7 +249,7 @@ __global__ __launch_bounds__(kNT8, 3) void scan_wave8_kernel(
     float x[kTPL8], dl[kTPL8], acc[kTPL8];
 #pragma unroll
     for (int j = 0; j < kTPL8 / 2; ++j) {
-      const float4 v = *(const float4*)&sm.xd[ch][kTPL8 * sl + 2 * j];
+      const float4 v = *(const float4*)&sm.xd[ch][(j * kROW8 + sl) * 2];
       x[2 * j] = v.x; dl[2 * j] = v.y; x[2 * j + 1] = v.z; dl[2 * j + 1] = v.w;
     }
 #pragma unroll
