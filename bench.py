@@ -185,7 +185,11 @@ def to_dev(x, io, dev):
 def launched_scan_kernel(name, io):
     """The one kernel a forward call without lengths or document starts runs,
     from the library's name for its layout and the call's io type: the 16-lane
-    layout takes eight tokens per lane for bf16 io, four otherwise."""
+    layout takes eight tokens per lane for bf16 io, four otherwise; from 8192
+    rows the eight-token kernel takes the bf16 calls it fits."""
+    split = "scan_wave8_kernel (time-parallel, 16 lanes per row, 8 tokens per lane) for bf16 io"
+    if name.startswith(split):
+        return name[:name.index(" for bf16 io")] if io == "bf16" else name.split(", else ", 1)[1]
     if name.startswith("scan_wave8_kernel / scan_wave_kernel"):
         tpl = 8 if io == "bf16" else 4
         return (f"{'scan_wave8_kernel' if tpl == 8 else 'scan_wave_kernel'} "

@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include <mutex>
+#include <string>
 
 #include "../../include/ssm66.h"
 #include "ssm_launch.h"
@@ -53,6 +54,10 @@ int check_common(int64_t batch, int64_t len, int64_t dim, int64_t dstate, int io
 //   16 x 2048 x 4096; 17 against 22 us for the sequential kernel at
 //   8 x 128 x 1536, even at 8 x 64 x 1536; with eight: 146.5 and 357 us at
 //   8 x 2048 x 1536 and 8 x 2048 x 4096);
+// - from 8192 rows when the eight-token kernel takes the call (bf16 io, 16
+//   states, a width that is a multiple of 16, no lengths or document starts)
+//   and at least 128 tokens: that kernel (3.01 against 3.32 ms for one wave per
+//   row under ZOH, 2.61 against 2.96 ms under Euler, at 4 x 65536 x 2048);
 // - between 1024 and 12288 rows and at least 256 tokens: the time-parallel
 //   kernel with one wave per row (146 against 160 us for 16 lanes per row at
 //   2 x 2048 x 5120; 3.5 against 6.9 ms for the sequential kernel at
@@ -63,6 +68,7 @@ constexpr int64_t kTparMaxRows = 1023;
 constexpr int64_t kTparMinLen = 128;
 constexpr int64_t kWaveMinLen = 256;
 constexpr int64_t kWave4MinRows = 12288;
+constexpr int64_t kWave8MinRows = 8192;
 constexpr int64_t kWave4MinLen = 128;
 
 // Scan kernel shape: G states per thread, NG state groups per channel
@@ -89,11 +95,14 @@ enum class ScanKernel { kSequential, kTpar, kWave, kWave4 };
 // elements with 32-bit offsets: 1024 dim < 2^32 - 1
 bool tpar_fits(int64_t dim) { return dim < ((int64_t)1 << 22); }
 
-ScanKernel pick_scan_kernel(int64_t batch, int64_t dim, int64_t L, int64_t dstate) {
+// eight: the call is one the eight-token kernel takes (bf16 io, 16 states, a
+// width that is a multiple of 16, no lengths or document starts).
+ScanKernel pick_scan_kernel(int64_t batch, int64_t dim, int64_t L, int64_t dstate, bool eight) {
   if (!tpar_fits(dim) || dstate > 16) return ScanKernel::kSequential;
   const int64_t rows = batch * dim;
   if (rows <= kTparMaxRows) return L >= kTparMinLen ? ScanKernel::kTpar : ScanKernel::kSequential;
-  if (rows >= kWave4MinRows) return L >= kWave4MinLen ? ScanKernel::kWave4 : ScanKernel::kSequential;
+  if (rows >= (eight ? kWave8MinRows : kWave4MinRows))
+    return L >= kWave4MinLen ? ScanKernel::kWave4 : ScanKernel::kSequential;
   return L >= kWaveMinLen ? ScanKernel::kWave : ScanKernel::kSequential;
 }
 
@@ -187,7 +196,8 @@ static int scan_fwd_impl(int kernel, const void* u, const void* delta, const flo
   if (!has_tokens) {
     kern = ScanKernel::kSequential;  // writes the initial state only
   } else if (kernel == SSM_SCAN_KERNEL_AUTO) {
-    kern = pick_scan_kernel(batch, dim, seqlen, dstate);
+    const bool eight = io_dtype == SSM_BF16 && dstate == 16 && dim % 16 == 0 && !seq_lens && !reset;
+    kern = pick_scan_kernel(batch, dim, seqlen, dstate, eight);
   } else if (kernel == SSM_SCAN_KERNEL_TPAR || kernel == SSM_SCAN_KERNEL_WAVE ||
              kernel == SSM_SCAN_KERNEL_WAVE4) {
     if (!tpar_fits(dim)) return SSM_ERR_UNSUPPORTED;
@@ -241,10 +251,9 @@ int ssm_scan_fwd_ex(const void* u, const void* delta, const float* A, const void
                        dstate, io_dtype, stream);
 }
 
-const char* ssm_scan_kernel_name(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate) {
-  if (check_common(batch, seqlen, dim, dstate, SSM_F32, 0, SSM_DT_ZOH) != SSM_OK) return "invalid shape";
-  if (batch == 0 || seqlen == 0 || dim == 0) return "none (no tokens)";
-  switch (pick_scan_kernel(batch, dim, seqlen, dstate)) {
+// The name of a kernel choice other than the eight-token split below.
+static const char* scan_kernel_label(ScanKernel k, int64_t batch, int64_t dim, int64_t dstate) {
+  switch (k) {
     case ScanKernel::kTpar: return "scan_tpar_kernel (time-parallel, four waves per row)";
     case ScanKernel::kWave: return "scan_wave_kernel (time-parallel, one wave per row)";
     case ScanKernel::kWave4:
@@ -257,6 +266,31 @@ const char* ssm_scan_kernel_name(int64_t batch, int64_t seqlen, int64_t dim, int
   if (G == 4) return "scan_fwd_kernel (sequential, 4 states per lane)";
   if (G == 2) return "scan_fwd_kernel (sequential, 2 states per lane)";
   return "scan_fwd_kernel (sequential, 1 state per lane)";
+}
+
+const char* ssm_scan_kernel_name(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate) {
+  if (check_common(batch, seqlen, dim, dstate, SSM_F32, 0, SSM_DT_ZOH) != SSM_OK) return "invalid shape";
+  if (batch == 0 || seqlen == 0 || dim == 0) return "none (no tokens)";
+  const bool eight_ok = dstate == 16 && dim % 16 == 0;
+  const ScanKernel k = pick_scan_kernel(batch, dim, seqlen, dstate, false);
+  const ScanKernel k8 = pick_scan_kernel(batch, dim, seqlen, dstate, eight_ok);
+  if (k8 == k) return scan_kernel_label(k, batch, dim, dstate);
+  // rows where the choice depends on the call: the eight-token kernel for the
+  // calls it takes, the other choice for the rest (C++ initialises these
+  // function-local statics once, thread-safely)
+  static const std::string prefix =
+      "scan_wave8_kernel (time-parallel, 16 lanes per row, 8 tokens per lane) for bf16 io without lengths or "
+      "document starts, else ";
+  static const std::string one = prefix + scan_kernel_label(ScanKernel::kWave, 0, 0, 0);
+  static const std::string seq1 = prefix + "scan_fwd_kernel (sequential, 1 state per lane)";
+  static const std::string seq2 = prefix + "scan_fwd_kernel (sequential, 2 states per lane)";
+  static const std::string seq4 = prefix + "scan_fwd_kernel (sequential, 4 states per lane)";
+  if (k == ScanKernel::kWave) return one.c_str();
+  // otherwise the sequential kernel (the eight-token kernel needs 8192 rows,
+  // past the four-waves-per-row range)
+  int G, NG;
+  pick_scan_shape(batch, dim, dstate, 0, &G, &NG);
+  return G == 4 ? seq4.c_str() : (G == 2 ? seq2.c_str() : seq1.c_str());
 }
 
 size_t ssm_scan_ckpt_size(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate) {

@@ -270,7 +270,15 @@ def test_scan_kernel_choice(lib):
     one = "scan_wave_kernel (time-parallel, one wave per row)"
     assert name(8, 2048, 1536, 16) == sixteen                          # Mamba-130M layer: 12288 rows
     assert name(8, 2048, 1535, 16) == one                              # 12280 rows
-    assert name(4, 65536, 2048, 16) == one                             # long sequences
+    split = ("scan_wave8_kernel (time-parallel, 16 lanes per row, 8 tokens per lane) for bf16 io without "
+             "lengths or document starts, else ")
+    assert name(4, 65536, 2048, 16) == split + one                     # long sequences: 8192 rows
+    assert name(4, 2048, 2048, 16) == split + one
+    assert name(4, 2048, 2032, 16) == one                              # 8128 rows
+    assert name(4, 2048, 2047, 16) == one                              # width not a multiple of 16
+    assert name(4, 2048, 2048, 8) == one                               # fewer states
+    assert name(4, 200, 2048, 16) == split + "scan_fwd_kernel (sequential, 2 states per lane)"
+    assert name(4, 127, 2048, 16).startswith("scan_fwd_kernel")
     assert name(8, 2048, 1536, 8) == sixteen                           # fewer states
     assert name(8, 2048, 4096, 16) == sixteen                          # Mamba-1.4B layer
     assert name(16, 2048, 2047, 16) == sixteen
